@@ -1,0 +1,87 @@
+"""Parity metrics between a GPU result and the oracle.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+* Final output y (bf16): relative error of the whole tensor against the float64
+  oracle, max_rel = max|y - r| / max|r| and mean_rel = sum|y - r| / sum|r|.
+  Elementwise ratios are not used: they blow up where r is near zero. Rounding
+  y to bf16 alone already gives mean_rel near 1.4e-3 on these workloads.
+* SwiGLU-output FP8 codes: the GPU evaluates the W13 GEMM in fp32 and silu with
+  its own exp, so a code may land one grid step away from the oracle's, and a
+  block whose amax sits right at a scale boundary (1.75 * 2^p) may take the
+  neighbouring scale. ``h_code_mismatch`` counts the elements that differ by
+  more than that.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from .formats import E4M3_VALUES, bf16_to_f64, f64_to_bf16_rne
+
+
+def y_metrics(y_bits: np.ndarray, y_ref: np.ndarray) -> dict:
+    """y_bits: bf16 bit patterns [n, H]; y_ref float64 [n, H]."""
+    y = bf16_to_f64(y_bits)
+    r = np.asarray(y_ref, dtype=np.float64)
+    d = np.abs(y - r)
+    eq = (np.asarray(y_bits, dtype=np.uint16) == f64_to_bf16_rne(r))
+    return {
+        "max_rel": float(d.max() / max(np.abs(r).max(), 1e-300)) if d.size else 0.0,
+        "mean_rel": float(d.sum() / max(np.abs(r).sum(), 1e-300)) if d.size else 0.0,
+        "frac_equal_bf16": float(eq.mean()) if eq.size else 1.0,
+        "finite": bool(np.isfinite(y).all()),
+    }
+
+
+def _signed_index(codes: np.ndarray) -> np.ndarray:
+    """E4M3 code -> signed position on the grid (+-0 -> 0); adjacent grid points
+    differ by 1, across zero too."""
+    c = codes.astype(np.int64)
+    mag = c & 0x7F
+    return np.where(c & 0x80, -mag, mag)
+
+
+def h_code_mismatch(hq, hs, hq_ref, hs_ref, amax_ref, block: int = 128) -> dict:
+    """Count SwiGLU-output code mismatches under the tolerance rule.
+
+    hq, hq_ref uint8 [R, C]; hs, hs_ref uint8 [R, C/block]; amax_ref float64
+    [R, C/block] (the oracle's block amax).
+
+    * Same scale code: an element matches if its grid positions differ by <= 1.
+    * Scale codes differ: allowed only for blocks whose oracle amax is within
+      2^-16 (relative) of a boundary 1.75 * 2^p; an element there matches if the
+      decoded values differ by at most one grid step of the coarser scale. In any
+      other block every element counts as a mismatch.
+    Returns counts and the fraction of mismatching elements.
+    """
+    hq = np.asarray(hq).reshape(-1, np.asarray(hq).shape[-1])
+    hq_ref = np.asarray(hq_ref).reshape(hq.shape)
+    R, C = hq.shape
+    nb = C // block
+    hs = np.asarray(hs).reshape(R, nb).astype(np.int64)
+    hs_ref = np.asarray(hs_ref).reshape(R, nb).astype(np.int64)
+    amax = np.asarray(amax_ref, dtype=np.float64).reshape(R, nb)
+
+    a = hq.reshape(R, nb, block)
+    b = hq_ref.reshape(R, nb, block)
+    same = (hs == hs_ref)[..., None]
+    close_same = np.abs(_signed_index(a) - _signed_index(b)) <= 1
+
+    m, ex = np.frexp(amax)               # amax = 2m * 2^(ex-1)
+    boundary = 1.75 * np.ldexp(1.0, ex - 1)
+    near = np.abs(amax - boundary) <= amax * 2.0 ** -16
+    va = E4M3_VALUES[a] * np.ldexp(1.0, hs - 127)[..., None]
+    vb = E4M3_VALUES[b] * np.ldexp(1.0, hs_ref - 127)[..., None]
+    coarse = np.maximum(hs, hs_ref) - 127
+    # one grid step of the coarser lattice at this magnitude
+    mag = np.maximum(np.abs(va), np.abs(vb)) / np.ldexp(1.0, coarse)[..., None]
+    _, mex = np.frexp(np.maximum(mag, 2.0 ** -6))
+    step = np.ldexp(1.0, (mex - 1 - 3)) * np.ldexp(1.0, coarse)[..., None]
+    close_diff = near[..., None] & (np.abs(va - vb) <= step)
+
+    ok = np.where(same, close_same, close_diff)
+    bad = int((~ok).sum())
+    return {"elements": int(a.size), "mismatch": bad, "frac": bad / max(a.size, 1),
+            "scale_diff_blocks": int((~same[..., 0]).sum()),
+            "max_code_dist_same_scale": int(np.where(same, np.abs(_signed_index(a) - _signed_index(b)), 0).max()) if a.size else 0}

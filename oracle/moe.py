@@ -1,0 +1,203 @@
+"""Oracle for the routed MoE FFN (plain CPU, float64, exact dequantization).
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+Definition followed (per token t, with e = topk_ids[t, j]):
+
+    y_t = sum_j w[t, j] * W2[e] . Q( silu(W1[e] . Q(x_t)) * (W3[e] . Q(x_t)) )
+          (+ the shared expert's output, weight 1)
+
+* Q(.) quantizes a vector to E4M3 with one power-of-two scale per 128
+  consecutive elements and dequantizes it again (``formats.quantize_blocks``).
+  For x this is the online FP8 activation quantization ("Pushing the Limits of
+  Serving DeepSeek-V4-Pro", §2.2); for the SwiGLU output it is the quantization
+  fused with SwiGLU that hands W2 its FP8 data and scales (same blog, §4.3). The
+  routing weight is applied after W2, in the top-k reduction (same blog, §3.2),
+  so the SwiGLU output is quantized unweighted.
+* W1 = W13 rows [0, I) (gate), W3 = W13 rows [I, 2I) (up), W2 the down
+  projection; all MXFP4, dequantized exactly (E2M1 value * 2^(scale-127)).
+* silu(g) = g / (1 + exp(-g)), evaluated in float64, no clamp.
+
+Exactness: a product of an E4M3 value (4 significant bits) and an E2M1 value
+(2 significant bits) times power-of-two scales has at most 6 significant bits,
+and a dot product over 7168 such terms spans far fewer than float64's 53 bits
+for realistic scales, so the float64 GEMMs below are exact whatever order the
+BLAS library sums in (tests/test_oracle_ffn.py checks this against math.fsum).
+The oracle therefore fixes the GEMM results exactly; only exp and the final
+combine carry float64 rounding.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from .formats import (E2M1_VALUES, E4M3_VALUES, E8M0_VALUES, bf16_to_f64,
+                      dequantize_blocks, quantize_blocks)
+
+# ----------------------------------------------------------------------------- plan
+
+
+def plan_ref(topk_ids, E: int) -> dict:
+    """Route plan: pack the (token, pick) pairs by expert ahead of the expert GEMMs
+    without changing the token-to-expert mapping ("Optimization progress report",
+    Optimization 14).
+
+    Pair p = t*K + j. Reading (the pages give no order): pairs are ordered by
+    expert and, within an expert, by p (a stable sort). Ids outside [0, E) are
+    dropped and counted. Returns
+      expert_offsets [E+1] int32  -- exclusive scan of per-expert counts
+      sorted_pairs   [P]   int32  -- pair ids in plan order, -1 past the valid ones
+      pair_rows      [P]   int32  -- position of pair p in sorted_pairs, -1 if dropped
+      dropped        int
+    """
+    ids = np.asarray(topk_ids).reshape(-1).astype(np.int64)
+    P = ids.size
+    valid = (ids >= 0) & (ids < E)
+    counts = np.bincount(ids[valid], minlength=E)
+    offsets = np.zeros(E + 1, dtype=np.int32)
+    offsets[1:] = np.cumsum(counts)
+    order = np.argsort(np.where(valid, ids, E), kind="stable")
+    n = int(valid.sum())
+    sorted_pairs = np.full(P, -1, dtype=np.int32)
+    sorted_pairs[:n] = order[:n]
+    pair_rows = np.full(P, -1, dtype=np.int32)
+    pair_rows[order[:n]] = np.arange(n, dtype=np.int32)
+    return {"expert_offsets": offsets, "sorted_pairs": sorted_pairs,
+            "pair_rows": pair_rows, "dropped": P - n}
+
+
+# ----------------------------------------------------------------------------- quant
+
+
+def _u16(x) -> np.ndarray:
+    if isinstance(x, torch.Tensor):
+        return x.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+    return np.asarray(x, dtype=np.uint16)
+
+
+def quant_act_ref(x) -> tuple:
+    """Online FP8 activation quantization ("Pushing the Limits of Serving
+    DeepSeek-V4-Pro", §2.2): bf16 x [T, H] -> E4M3 codes [T, H] and one E8M0
+    scale per token per 128 columns [T, H/128]."""
+    codes, scales, _ = quantize_blocks(bf16_to_f64(_u16(x)), 128)
+    return codes, scales
+
+
+# ----------------------------------------------------------------------------- dequant
+
+_E2M1_T = torch.from_numpy(E2M1_VALUES)
+_E4M3_T = torch.from_numpy(E4M3_VALUES)
+_E8M0_T = torch.from_numpy(E8M0_VALUES)
+# value pair of one packed byte: (element 2i from the low nibble, element 2i+1 from the high)
+_BYTE_PAIR = torch.stack([_E2M1_T[torch.arange(256) & 15], _E2M1_T[torch.arange(256) >> 4]], -1)
+
+
+def dequant_mxfp4(codes, scales) -> torch.Tensor:
+    """MXFP4 [N, K/2] codes + [N, K/32] E8M0 scales -> exact float64 [N, K]."""
+    codes = torch.as_tensor(codes).cpu()
+    scales = torch.as_tensor(scales).cpu()
+    N, half = codes.shape
+    Kd = 2 * half
+    w = _BYTE_PAIR[codes.long()].reshape(N, Kd // 32, 32)
+    return (w * _E8M0_T[scales.long()].unsqueeze(-1)).reshape(N, Kd)
+
+
+def dequant_fp8_block(codes, scales) -> torch.Tensor:
+    """FP8 E4M3 [N, K] codes + [N/128, K/128] E8M0 block scales -> float64 [N, K]."""
+    codes = torch.as_tensor(codes).cpu()
+    scales = torch.as_tensor(scales).cpu()
+    N, Kd = codes.shape
+    v = _E4M3_T[codes.long()].reshape(N // 128, 128, Kd // 128, 128)
+    return (v * _E8M0_T[scales.long()][:, None, :, None]).reshape(N, Kd)
+
+
+def _silu_mul(g: np.ndarray, u: np.ndarray) -> np.ndarray:
+    with np.errstate(over="ignore"):
+        return g / (1.0 + np.exp(-g)) * u
+
+
+def _expert_ffn(xh: torch.Tensor, W13: torch.Tensor, W2: torch.Tensor, I: int):
+    """One expert on the dequantized rows xh [m, H] (float64): W13 GEMM, SwiGLU,
+    requantization of the SwiGLU output, W2 GEMM. Returns (out [m, H] float64,
+    h codes, h scale codes, h block amax)."""
+    acc = (xh @ W13.T).numpy()
+    h = _silu_mul(acc[:, :I], acc[:, I:])
+    hq, hs, amax = quantize_blocks(h, 128)
+    hh = torch.from_numpy(dequantize_blocks(hq, hs, 128))
+    return (hh @ W2.T).numpy(), hq, hs, amax
+
+
+# ----------------------------------------------------------------------------- FFN
+
+
+def ffn_ref(x, topk_ids, topk_weights, w13, w13_s, w2, w2_s, shared=None, tokens=None) -> dict:
+    """The routed MoE FFN in float64 for all tokens or for a subset ``tokens``.
+
+    x bf16 [T, H]; topk_ids int [T, K]; topk_weights float32 [T, K]; w13 [E, 2I, H/2],
+    w13_s [E, 2I, H/32], w2 [E, H, I/2], w2_s [E, H, I/32] (uint8, any device; the
+    experts needed are copied to the host one at a time); ``shared`` = optional dict
+    w13s [2Is, H], w13s_s [2Is/128, H/128], w2s [H, Is], w2s_s [H/128, Is/128].
+
+    Returns dict with, for the selected tokens in the given order:
+      y      float64 [n, H]
+      x_q, x_s   activation codes / scales of those tokens
+      h_q    uint8 [n, K, I]   SwiGLU-output codes per (token, pick)
+      h_s    uint8 [n, K, I/128]
+      h_amax float64 [n, K, I/128]
+      valid  bool [n, K]       pick has an id in [0, E)
+      shared_h_q / shared_h_s / shared_h_amax (when a shared expert is given)
+    """
+    xb = _u16(x)
+    ids = np.asarray(torch.as_tensor(topk_ids).cpu()).astype(np.int64)
+    wts = np.asarray(torch.as_tensor(topk_weights).cpu()).astype(np.float64)
+    T, H = xb.shape
+    K = ids.shape[1]
+    E = w13.shape[0]
+    I = w2.shape[2] * 2
+    sel = np.arange(T) if tokens is None else np.asarray(tokens, dtype=np.int64)
+    n = sel.size
+
+    x_q, x_s = quant_act_ref(xb[sel])
+    xh = torch.from_numpy(dequantize_blocks(x_q, x_s, 128))
+
+    y = np.zeros((n, H), dtype=np.float64)
+    h_q = np.zeros((n, K, I), dtype=np.uint8)
+    h_s = np.zeros((n, K, I // 128), dtype=np.uint8)
+    h_amax = np.zeros((n, K, I // 128), dtype=np.float64)
+    sid = ids[sel]
+    valid = (sid >= 0) & (sid < E)
+    outs = np.zeros((n, K, H), dtype=np.float64)
+    for e in np.unique(sid[valid]):
+        rows, picks = np.nonzero(sid == e)
+        W13 = dequant_mxfp4(w13[int(e)], w13_s[int(e)])
+        W2 = dequant_mxfp4(w2[int(e)], w2_s[int(e)])
+        o, hq, hs, am = _expert_ffn(xh[torch.from_numpy(rows)], W13, W2, I)
+        outs[rows, picks] = o
+        h_q[rows, picks] = hq
+        h_s[rows, picks] = hs
+        h_amax[rows, picks] = am
+    # top-k weighted reduction, picks in order, dropped picks contribute nothing
+    for j in range(K):
+        y += np.where(valid[:, j:j + 1], wts[sel, j:j + 1] * outs[:, j], 0.0)
+    res = {"y": y, "x_q": x_q, "x_s": x_s, "h_q": h_q, "h_s": h_s, "h_amax": h_amax,
+           "valid": valid}
+    if shared is not None:
+        Is = shared["w2s"].shape[1]
+        W13s = dequant_fp8_block(shared["w13s"], shared["w13s_s"])
+        W2s = dequant_fp8_block(shared["w2s"], shared["w2s_s"])
+        o, hq, hs, am = _expert_ffn(xh, W13s, W2s, Is)
+        y += o
+        res.update(shared_h_q=hq, shared_h_s=hs, shared_h_amax=am)
+    return res
+
+
+def ffn_ref_dense_single(x, w13, w13_s, w2, w2_s) -> np.ndarray:
+    """A single MXFP4 SwiGLU expert applied densely to every token (no routing):
+    the special case K = 1 / E = 1 of ``ffn_ref`` with weight 1. Written as plain
+    matrix products over all tokens at once."""
+    xq, xs = quant_act_ref(x)
+    xh = torch.from_numpy(dequantize_blocks(xq, xs, 128))
+    I = w2.shape[1] * 2
+    o, _, _, _ = _expert_ffn(xh, dequant_mxfp4(w13, w13_s), dequant_mxfp4(w2, w2_s), I)
+    return o
