@@ -1,0 +1,222 @@
+"""Routed MoE FFN with MXFP4 expert weights and online FP8 activations on MI355X.
+
+Thin Python binding over the C-ABI library ``libmoe_mxfp4.so`` (declared in
+``include/moe_mxfp4.h``). This module only marshals arguments: torch supplies
+device memory and the current HIP stream, every step of the path runs in the
+library's HIP kernels. There is no fallback: if the library is missing or a
+call fails, an exception is raised.
+
+    plan(topk_ids, E)                     -> Plan          (moe_plan)
+    quant_act(x)                          -> (x_q, x_s)    (moe_quant_act)
+    ffn(x, topk_weights, plan, weights)   -> y             (moe_ffn)
+"""
+
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe_mxfp4.so")
+
+MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP = 0, -1, -2, -3, -4
+EV_START, EV_QUANT_DONE, EV_W13_DONE, EV_W2_DONE, EV_SHARED_DONE, EV_END = range(6)
+NUM_EVENTS = 6
+
+
+class MoEError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        super().__init__(f"{what}: {status_string(code)} ({code})")
+        self.code = code
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("H", ctypes.c_int32), ("I", ctypes.c_int32), ("E", ctypes.c_int32),
+                ("K", ctypes.c_int32), ("Is", ctypes.c_int32), ("small_max", ctypes.c_int32)]
+
+
+class Shared(ctypes.Structure):
+    _fields_ = [("w13s", ctypes.c_void_p), ("w13s_s", ctypes.c_void_p), ("w2s", ctypes.c_void_p),
+                ("w2s_s", ctypes.c_void_p)]
+
+
+class Debug(ctypes.Structure):
+    _fields_ = [("x_q", ctypes.c_void_p), ("x_s", ctypes.c_void_p), ("h_q", ctypes.c_void_p),
+                ("h_s", ctypes.c_void_p), ("sh_q", ctypes.c_void_p), ("sh_s", ctypes.c_void_p),
+                ("events", ctypes.POINTER(ctypes.c_void_p))]
+
+
+_lib = None
+
+#: every symbol the header declares, with its ctypes signature
+_SIGNATURES = {
+    "moe_validate": (ctypes.c_int, [ctypes.POINTER(Dims)]),
+    "moe_plan_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(Dims)]),
+    "moe_plan": (ctypes.c_int, [ctypes.POINTER(Dims)] + [ctypes.c_void_p] * 6 + [ctypes.c_size_t, ctypes.c_void_p]),
+    "moe_quant_act": (ctypes.c_int, [ctypes.POINTER(Dims)] + [ctypes.c_void_p] * 4),
+    "moe_ffn_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(Dims)]),
+    "moe_ffn": (ctypes.c_int, [ctypes.POINTER(Dims)] + [ctypes.c_void_p] * 10 + [ctypes.POINTER(Shared),
+                ctypes.c_void_p, ctypes.POINTER(Debug), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+}
+
+
+def lib() -> ctypes.CDLL:
+    """Load the C-ABI library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m mxfp4_weights_fp8_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def status_string(code: int) -> str:
+    return lib().moe_status_string(code).decode()
+
+
+def make_dims(T, H, I, E, K, Is=0, small_max=0) -> Dims:
+    return Dims(int(T), int(H), int(I), int(E), int(K), int(Is), int(small_max))
+
+
+def validate(d: Dims) -> int:
+    return lib().moe_validate(ctypes.byref(d))
+
+
+def plan_workspace_bytes(d: Dims) -> int:
+    return lib().moe_plan_workspace_bytes(ctypes.byref(d))
+
+
+def ffn_workspace_bytes(d: Dims) -> int:
+    return lib().moe_ffn_workspace_bytes(ctypes.byref(d))
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _check(rc: int, what: str):
+    if rc != MOE_OK:
+        raise MoEError(rc, what)
+
+
+def _require(t: torch.Tensor, dtype, shape, name):
+    if t.dtype != dtype or tuple(t.shape) != tuple(shape) or not t.is_contiguous() or not t.is_cuda:
+        raise ValueError(f"{name}: expected contiguous cuda {dtype} {tuple(shape)}, got {t.dtype} "
+                         f"{tuple(t.shape)} contiguous={t.is_contiguous()} device={t.device}")
+
+
+@dataclasses.dataclass
+class Plan:
+    dims: Dims
+    expert_offsets: torch.Tensor   # [E+1] int32
+    sorted_pairs: torch.Tensor     # [P] int32
+    pair_rows: torch.Tensor        # [P] int32
+    status: torch.Tensor           # [1] int32 (dropped pairs)
+    ws: torch.Tensor               # plan workspace (uint8)
+
+
+def plan(topk_ids: torch.Tensor, E: int, H: int, I: int, small_max: int = 0, Is: int = 0,
+         out: Optional[Plan] = None) -> Plan:
+    """moe_plan on the current stream. topk_ids: cuda int32 [T, K]. H, I (and Is)
+    complete the dims that moe_ffn will use with this plan."""
+    T, K = topk_ids.shape
+    d = make_dims(T, H, I, E, K, Is, small_max)
+    _check(validate(d), "moe_plan dims")
+    _require(topk_ids, torch.int32, (T, K), "topk_ids")
+    dev = topk_ids.device
+    if out is None:
+        P = T * K
+        out = Plan(d, torch.empty(E + 1, dtype=torch.int32, device=dev),
+                   torch.empty(max(P, 1), dtype=torch.int32, device=dev),
+                   torch.empty(max(P, 1), dtype=torch.int32, device=dev),
+                   torch.zeros(1, dtype=torch.int32, device=dev),
+                   torch.empty(plan_workspace_bytes(d), dtype=torch.uint8, device=dev))
+    rc = lib().moe_plan(ctypes.byref(d), _ptr(topk_ids), _ptr(out.expert_offsets), _ptr(out.sorted_pairs),
+                        _ptr(out.pair_rows), _ptr(out.status), _ptr(out.ws), out.ws.numel(), _stream(dev))
+    _check(rc, "moe_plan")
+    out.dims = d
+    return out
+
+
+def quant_act(x: torch.Tensor):
+    """moe_quant_act: bf16 [T, H] -> (E4M3 codes uint8 [T, H], E8M0 scales uint8 [T, H/128])."""
+    T, H = x.shape
+    d = make_dims(T, H, 128, 1, 1)
+    _check(validate(d), "moe_quant_act dims")
+    _require(x, torch.bfloat16, (T, H), "x")
+    x_q = torch.empty((T, H), dtype=torch.uint8, device=x.device)
+    x_s = torch.empty((T, H // 128), dtype=torch.uint8, device=x.device)
+    _check(lib().moe_quant_act(ctypes.byref(d), _ptr(x), _ptr(x_q), _ptr(x_s), _stream(x.device)), "moe_quant_act")
+    return x_q, x_s
+
+
+def ffn(x: torch.Tensor, topk_weights: torch.Tensor, p: Plan, weights: dict, shared: Optional[dict] = None,
+        debug: bool = False, ws: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None,
+        events=None):
+    """moe_ffn on the current stream. weights: dict w13, w13_s, w2, w2_s (uint8
+    cuda, layouts as in the header); shared: optional dict w13s, w13s_s, w2s, w2s_s.
+    Returns y (bf16 [T, H]); with debug=True returns (y, dict of x_q, x_s, h_q, h_s,
+    sh_q, sh_s). ``events``: optional list of NUM_EVENTS torch.cuda.Event recorded
+    at the stage boundaries."""
+    d = p.dims
+    T, H, I, E, K, Is = d.T, d.H, d.I, d.E, d.K, d.Is
+    dev = x.device
+    _require(x, torch.bfloat16, (T, H), "x")
+    _require(topk_weights, torch.float32, (T, K), "topk_weights")
+    _require(weights["w13"], torch.uint8, (E, 2 * I, H // 2), "w13")
+    _require(weights["w13_s"], torch.uint8, (E, 2 * I, H // 32), "w13_s")
+    _require(weights["w2"], torch.uint8, (E, H, I // 2), "w2")
+    _require(weights["w2_s"], torch.uint8, (E, H, I // 32), "w2_s")
+    sh = None
+    if shared is not None and Is > 0:
+        _require(shared["w13s"], torch.uint8, (2 * Is, H), "w13s")
+        _require(shared["w13s_s"], torch.uint8, (2 * Is // 128, H // 128), "w13s_s")
+        _require(shared["w2s"], torch.uint8, (H, Is), "w2s")
+        _require(shared["w2s_s"], torch.uint8, (H // 128, Is // 128), "w2s_s")
+        sh = Shared(shared["w13s"].data_ptr(), shared["w13s_s"].data_ptr(), shared["w2s"].data_ptr(),
+                    shared["w2s_s"].data_ptr())
+    if y is None:
+        y = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    if ws is None:
+        ws = torch.empty(ffn_workspace_bytes(d), dtype=torch.uint8, device=dev)
+    dbg_t = None
+    dbg = None
+    ev_arr = None
+    if debug or events is not None:
+        dbg = Debug()
+        if debug:
+            P = T * K
+            dbg_t = {"x_q": torch.empty((T, H), dtype=torch.uint8, device=dev),
+                     "x_s": torch.empty((T, H // 128), dtype=torch.uint8, device=dev),
+                     "h_q": torch.zeros((max(P, 1), I), dtype=torch.uint8, device=dev),
+                     "h_s": torch.zeros((max(P, 1), I // 128), dtype=torch.uint8, device=dev),
+                     "sh_q": torch.zeros((T, max(Is, 128)), dtype=torch.uint8, device=dev),
+                     "sh_s": torch.zeros((T, max(Is, 128) // 128), dtype=torch.uint8, device=dev)}
+            for k, v in dbg_t.items():
+                setattr(dbg, k, v.data_ptr())
+        if events is not None:
+            ev_arr = (ctypes.c_void_p * NUM_EVENTS)(*[ctypes.c_void_p(e.cuda_event) if e is not None else None
+                                                      for e in events])
+            dbg.events = ctypes.cast(ev_arr, ctypes.POINTER(ctypes.c_void_p))
+    rc = lib().moe_ffn(ctypes.byref(d), _ptr(x), _ptr(topk_weights), _ptr(p.expert_offsets), _ptr(p.sorted_pairs),
+                       _ptr(p.pair_rows), _ptr(p.ws), _ptr(weights["w13"]), _ptr(weights["w13_s"]),
+                       _ptr(weights["w2"]), _ptr(weights["w2_s"]), ctypes.byref(sh) if sh is not None else None,
+                       _ptr(y), ctypes.byref(dbg) if dbg is not None else None, _ptr(ws), ws.numel(), _stream(dev))
+    _check(rc, "moe_ffn")
+    if debug:
+        return y, dbg_t
+    return y

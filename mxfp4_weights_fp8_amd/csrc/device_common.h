@@ -1,0 +1,78 @@
+// Device-side helpers shared by the gfx950 kernels: block-scaled MFMA operand
+// types, FP8 E4M3 encoding, the E8M0 block-scale rule, bf16 rounding.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+// Operand format selectors of v_mfma_scale_f32_*_f8f6f4 (cbsz / blgp fields).
+constexpr int kFmtE4M3 = 0;
+constexpr int kFmtE2M1 = 4;
+
+// Lane layout of v_mfma_scale_f32_16x16x128_f8f6f4 on gfx950, lane l, q = l / 16:
+//   A (16 x 128): row l % 16.  B (128 x 16): column l % 16.
+//   8-bit operand: register bytes 0..15 hold K = 16q + i, bytes 16..31 hold
+//     K = 64 + 16q + i (two 16-byte halves of the 128-long K step).
+//   4-bit operand: the low 16 bytes hold K = 32q .. 32q+31, low nibble first.
+//   scale operand (E8M0 in the low byte with op_sel 0): row/column l % 16,
+//     K block q (K = 32q .. 32q+31).
+//   D (16 x 16 fp32): column l % 16, rows 4q .. 4q+3.
+template <int FMT_A, int FMT_B>
+__device__ __forceinline__ v4f mfma_scale_16x16x128(v8i a, v8i b, v4f c, int scale_a, int scale_b) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, FMT_A, FMT_B, 0, scale_a, 0, scale_b);
+}
+
+// Smallest e with amax <= 448 * 2^e, from the fp32 bit pattern of amax >= 0:
+// with amax = m * 2^p, m in [1, 2), e = p - 8 if m <= 1.75 else p - 7; zero and
+// fp32 subnormals take the smallest E8M0 exponent, -127.
+__device__ __forceinline__ int e8m0_exponent(float amax) {
+  uint32_t b = __float_as_uint(amax) & 0x7FFFFFFFu;
+  int be = (int)(b >> 23);
+  int e = be - 127 - 8 + ((b & 0x7FFFFFu) > 0x600000u ? 1 : 0);
+  e = be == 0 ? -127 : e;
+  return e < -127 ? -127 : e;
+}
+
+// 2^-e as a float, for e in [-127, 126].
+__device__ __forceinline__ float exp2_neg(int e) { return __uint_as_float((uint32_t)(127 - e) << 23); }
+
+// Round v to an E4M3FN code: nearest, ties to even, saturating at 448, sign
+// kept for values that round to zero. Normal range (|v| >= 2^-6): keep three
+// mantissa bits of the fp32 pattern with a round-half-even carry (a carry out of
+// the mantissa moves the exponent up, which is the right code). Subnormal range:
+// the grid is k * 2^-9, k = rint(|v| * 512) in 0..8 (8 is the smallest normal).
+__device__ __forceinline__ uint32_t e4m3_encode(float v) {
+  uint32_t b = __float_as_uint(v);
+  uint32_t s = (b >> 24) & 0x80u;
+  uint32_t a = b & 0x7FFFFFFFu;
+  uint32_t code;
+  if (a >= 0x3C800000u) {
+    uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);
+    code = (r >> 20) - (120u << 3);
+    code = code > 0x7Eu ? 0x7Eu : code;
+  } else {
+    code = (uint32_t)rintf(__uint_as_float(a) * 512.0f);
+  }
+  return s | code;
+}
+
+// fp32 -> bf16 bit pattern, round to nearest even (finite inputs).
+__device__ __forceinline__ uint16_t bf16_rne(float f) {
+  uint32_t b = __float_as_uint(f);
+  b += 0x7FFFu + ((b >> 16) & 1u);
+  return (uint16_t)(b >> 16);
+}
+
+__device__ __forceinline__ float bf16_to_float(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
+
+__device__ __forceinline__ v4i load16(const void* p) { return *reinterpret_cast<const v4i*>(p); }
+
+}  // namespace moe

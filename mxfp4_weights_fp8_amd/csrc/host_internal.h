@@ -1,0 +1,85 @@
+// Host-side internals shared by the C-ABI layer and the kernel launchers:
+// tiling constants, workspace layouts and launcher declarations.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/moe_mxfp4.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------- constants
+constexpr int kSmallRows = 16;       // rows per small-M tile (MFMA N side)
+constexpr int kDefaultSmallMax = 16; // experts with <= this many pairs take the small-M path
+constexpr int kLargeRows = 128;      // rows per large-M tile
+constexpr int kPlanChunk = 2048;     // pairs per route-planner block
+constexpr int kMaxExperts = 4096;
+constexpr int kMaxTopK = 64;
+
+inline int small_max_of(const moe_dims& d) { return d.small_max > 0 ? d.small_max : kDefaultSmallMax; }
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Upper bounds on the tile work lists the planner builds (host-side, from dims
+// only, so grids can be sized without reading device data).
+inline int64_t small_items_bound(const moe_dims& d) {
+  int64_t P = (int64_t)d.T * d.K;
+  int64_t sm = small_max_of(d);
+  int64_t experts = P < d.E ? P : d.E;
+  // each small expert (1 <= M <= sm) yields ceil(M / kSmallRows) tiles
+  return sm <= kSmallRows ? experts : experts + P / kSmallRows;
+}
+inline int64_t large_items_bound(const moe_dims& d) {
+  int64_t P = (int64_t)d.T * d.K;
+  int64_t sm = small_max_of(d);
+  int64_t big = P / (sm + 1);            // experts with more than sm pairs
+  if (big > d.E) big = d.E;
+  return P / kLargeRows + big;
+}
+
+// ---------------------------------------------------------------- plan workspace
+// int32 header, then the two tile lists (int2 = {expert, first row}), then the
+// planner's per-block scratch.
+struct PlanWs {
+  int32_t* hdr;           // [0] small item count, [1] large item count
+  int2* small_items;
+  int2* large_items;
+  int32_t* local_rank;    // [P]
+  int32_t* block_counts;  // [NB * E]
+  int32_t* block_base;    // [NB * E]
+  int64_t small_cap, large_cap, nb;
+};
+size_t plan_ws_layout(const moe_dims& d, void* base, PlanWs* out);
+
+// ---------------------------------------------------------------- ffn workspace
+struct FfnWs {
+  uint8_t* x_q;   // [T, H]
+  uint8_t* x_s;   // [T, H/128]
+  uint8_t* h_q;   // [P, I]
+  uint8_t* h_s;   // [P, I/128]
+  float* o;       // [P, H] per-pair W2 outputs, slot p = t*K + j
+  uint8_t* sh_q;  // [T, Is]
+  uint8_t* sh_s;  // [T, Is/128]
+  float* so;      // [T, H] shared-expert output
+};
+size_t ffn_ws_layout(const moe_dims& d, void* base, FfnWs* out);
+
+// ---------------------------------------------------------------- launchers
+// Each returns hipSuccess or the launch error.
+hipError_t launch_plan(const moe_dims& d, const int32_t* ids, int32_t* offsets, int32_t* sorted_pairs,
+                       int32_t* pair_rows, int32_t* status, const PlanWs& ws, hipStream_t s);
+hipError_t launch_quant_act(const uint16_t* x, uint8_t* x_q, uint8_t* x_s, int T, int H, hipStream_t s);
+hipError_t launch_w13_small(const moe_dims& d, const int2* items, const int32_t* n_items, int64_t max_items,
+                            int item_rows, const int32_t* offsets, const int32_t* sorted_pairs,
+                            const uint8_t* x_q, const uint8_t* x_s, const uint8_t* w13, const uint8_t* w13_s,
+                            uint8_t* h_q, uint8_t* h_s, hipStream_t s);
+hipError_t launch_w2_small(const moe_dims& d, const int2* items, const int32_t* n_items, int64_t max_items,
+                           int item_rows, const int32_t* offsets, const int32_t* sorted_pairs,
+                           const uint8_t* h_q, const uint8_t* h_s, const uint8_t* w2, const uint8_t* w2_s,
+                           float* o, hipStream_t s);
+hipError_t launch_combine(const float* o, const float* topk_weights, const int32_t* pair_rows, const float* so,
+                          uint16_t* y, int T, int H, int K, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,159 @@
+// C ABI of the routed MoE FFN (declared in include/moe_mxfp4.h): argument checks,
+// workspace carving and the launch sequence. Nothing here allocates, synchronizes
+// or reads device memory, so every call is an enqueue on the caller's stream.
+#include "host_internal.h"
+
+namespace moe {
+
+size_t ffn_ws_layout(const moe_dims& d, void* base, FfnWs* out) {
+  const int64_t T = d.T, H = d.H, I = d.I, P = (int64_t)d.T * d.K, Is = d.Is;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = align_up(off + (bytes ? bytes : 1), 256);
+    return o;
+  };
+  const size_t o_xq = take((size_t)(T * H));
+  const size_t o_xs = take((size_t)(T * H / 128));
+  const size_t o_hq = take((size_t)(P * I));
+  const size_t o_hs = take((size_t)(P * I / 128));
+  const size_t o_o = take(sizeof(float) * (size_t)(P * H));
+  const size_t o_shq = take((size_t)(T * Is));
+  const size_t o_shs = take((size_t)(T * Is / 128));
+  const size_t o_so = take(Is ? sizeof(float) * (size_t)(T * H) : 0);
+  if (out) {
+    char* b = static_cast<char*>(base);
+    out->x_q = reinterpret_cast<uint8_t*>(b + o_xq);
+    out->x_s = reinterpret_cast<uint8_t*>(b + o_xs);
+    out->h_q = reinterpret_cast<uint8_t*>(b + o_hq);
+    out->h_s = reinterpret_cast<uint8_t*>(b + o_hs);
+    out->o = reinterpret_cast<float*>(b + o_o);
+    out->sh_q = reinterpret_cast<uint8_t*>(b + o_shq);
+    out->sh_s = reinterpret_cast<uint8_t*>(b + o_shs);
+    out->so = reinterpret_cast<float*>(b + o_so);
+  }
+  return off;
+}
+
+namespace {
+
+int validate(const moe_dims* d) {
+  if (!d) return MOE_EINVAL;
+  if (d->T < 0 || d->H <= 0 || d->I <= 0 || d->E < 1 || d->E > kMaxExperts || d->K < 1 || d->K > kMaxTopK ||
+      d->Is < 0 || d->small_max < 0)
+    return MOE_EINVAL;
+  if (d->H % 128 || d->I % 128 || d->Is % 128) return MOE_EUNSUPPORTED;
+  if ((int64_t)d->T * d->K > (int64_t)1 << 30) return MOE_EUNSUPPORTED;
+  if (d->H > (1 << 20) || d->I > (1 << 20) || d->Is > (1 << 20)) return MOE_EUNSUPPORTED;
+  return MOE_OK;
+}
+
+inline int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
+
+inline void record(const moe_debug* dbg, int which, hipStream_t s) {
+  if (dbg && dbg->events && dbg->events[which]) hipEventRecord((hipEvent_t)dbg->events[which], s);
+}
+
+}  // namespace
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+int moe_validate(const moe_dims* dims) { return validate(dims); }
+
+size_t moe_plan_workspace_bytes(const moe_dims* dims) {
+  if (validate(dims) != MOE_OK) return 0;
+  return plan_ws_layout(*dims, nullptr, nullptr);
+}
+
+size_t moe_ffn_workspace_bytes(const moe_dims* dims) {
+  if (validate(dims) != MOE_OK) return 0;
+  return ffn_ws_layout(*dims, nullptr, nullptr);
+}
+
+int moe_plan(const moe_dims* dims, const int32_t* topk_ids, int32_t* expert_offsets, int32_t* sorted_pairs,
+             int32_t* pair_rows, int32_t* status, void* ws, size_t ws_bytes, void* stream) {
+  int rc = validate(dims);
+  if (rc != MOE_OK) return rc;
+  const bool any = dims->T > 0;
+  if (!expert_offsets || !status || !ws || (any && (!topk_ids || !sorted_pairs || !pair_rows))) return MOE_EINVAL;
+  PlanWs pw;
+  if (ws_bytes < plan_ws_layout(*dims, ws, &pw)) return MOE_EWORKSPACE;
+  return hip_status(launch_plan(*dims, topk_ids, expert_offsets, sorted_pairs, pair_rows, status, pw,
+                                (hipStream_t)stream));
+}
+
+int moe_quant_act(const moe_dims* dims, const uint16_t* x, uint8_t* x_q, uint8_t* x_s, void* stream) {
+  int rc = validate(dims);
+  if (rc != MOE_OK) return rc;
+  if (dims->T == 0) return MOE_OK;
+  if (!x || !x_q || !x_s) return MOE_EINVAL;
+  return hip_status(launch_quant_act(x, x_q, x_s, dims->T, dims->H, (hipStream_t)stream));
+}
+
+int moe_ffn(const moe_dims* dims, const uint16_t* x, const float* topk_weights, const int32_t* expert_offsets,
+            const int32_t* sorted_pairs, const int32_t* pair_rows, const void* plan_ws, const uint8_t* w13,
+            const uint8_t* w13_s, const uint8_t* w2, const uint8_t* w2_s, const moe_shared* shared, uint16_t* y,
+            const moe_debug* dbg, void* ws, size_t ws_bytes, void* stream) {
+  int rc = validate(dims);
+  if (rc != MOE_OK) return rc;
+  const moe_dims& d = *dims;
+  hipStream_t s = (hipStream_t)stream;
+  const bool use_shared = shared != nullptr && d.Is > 0;
+  if (d.T == 0) return MOE_OK;
+  if (!x || !topk_weights || !expert_offsets || !sorted_pairs || !pair_rows || !plan_ws || !w13 || !w13_s || !w2 ||
+      !w2_s || !y || !ws)
+    return MOE_EINVAL;
+  if (use_shared && (!shared->w13s || !shared->w13s_s || !shared->w2s || !shared->w2s_s)) return MOE_EINVAL;
+  if (use_shared) return MOE_EUNSUPPORTED;
+  FfnWs fw;
+  if (ws_bytes < ffn_ws_layout(d, ws, &fw)) return MOE_EWORKSPACE;
+  PlanWs pw;
+  plan_ws_layout(d, const_cast<void*>(plan_ws), &pw);
+  uint8_t* x_q = dbg && dbg->x_q ? dbg->x_q : fw.x_q;
+  uint8_t* x_s = dbg && dbg->x_s ? dbg->x_s : fw.x_s;
+  uint8_t* h_q = dbg && dbg->h_q ? dbg->h_q : fw.h_q;
+  uint8_t* h_s = dbg && dbg->h_s ? dbg->h_s : fw.h_s;
+
+  record(dbg, MOE_EV_START, s);
+  hipError_t err = launch_quant_act(x, x_q, x_s, d.T, d.H, s);
+  if (err != hipSuccess) return MOE_EHIP;
+  record(dbg, MOE_EV_QUANT_DONE, s);
+
+  err = launch_w13_small(d, pw.small_items, pw.hdr + 0, pw.small_cap, kSmallRows, expert_offsets, sorted_pairs,
+                         x_q, x_s, w13, w13_s, h_q, h_s, s);
+  if (err != hipSuccess) return MOE_EHIP;
+  err = launch_w13_small(d, pw.large_items, pw.hdr + 1, pw.large_cap, kLargeRows, expert_offsets, sorted_pairs,
+                         x_q, x_s, w13, w13_s, h_q, h_s, s);
+  if (err != hipSuccess) return MOE_EHIP;
+  record(dbg, MOE_EV_W13_DONE, s);
+
+  err = launch_w2_small(d, pw.small_items, pw.hdr + 0, pw.small_cap, kSmallRows, expert_offsets, sorted_pairs, h_q,
+                        h_s, w2, w2_s, fw.o, s);
+  if (err != hipSuccess) return MOE_EHIP;
+  err = launch_w2_small(d, pw.large_items, pw.hdr + 1, pw.large_cap, kLargeRows, expert_offsets, sorted_pairs, h_q,
+                        h_s, w2, w2_s, fw.o, s);
+  if (err != hipSuccess) return MOE_EHIP;
+  record(dbg, MOE_EV_W2_DONE, s);
+  record(dbg, MOE_EV_SHARED_DONE, s);
+
+  err = launch_combine(fw.o, topk_weights, pair_rows, nullptr, y, d.T, d.H, d.K, s);
+  if (err != hipSuccess) return MOE_EHIP;
+  record(dbg, MOE_EV_END, s);
+  return MOE_OK;
+}
+
+const char* moe_status_string(int code) {
+  switch (code) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_EINVAL: return "MOE_EINVAL: null pointer or dimension out of range";
+    case MOE_EUNSUPPORTED: return "MOE_EUNSUPPORTED: shape outside what the kernels support";
+    case MOE_EWORKSPACE: return "MOE_EWORKSPACE: workspace too small";
+    case MOE_EHIP: return "MOE_EHIP: a HIP launch failed";
+    default: return "unknown moe status code";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,351 @@
+// Route planner: pack the (token, pick) pairs by expert ahead of the expert GEMMs
+// without changing the token-to-expert mapping ("Optimization progress report",
+// Optimization 14), and build the device-side tile work lists the grouped GEMMs
+// drain, so no host readback is needed between planning and the FFN.
+//
+// Pair p = t*K + j. Output order: by expert, then by p (stable counting sort).
+//   1. local ranks: each block takes kPlanChunk consecutive pairs; every wave
+//      takes 64 of them at a time and finds, per lane, the lanes holding the same
+//      expert with one ballot per key bit ("peer mask"); the rank inside the wave
+//      is the popcount of the lower peers; waves of the same round are ordered
+//      through a small LDS table; a per-expert LDS cursor carries the count across
+//      rounds. No atomics decide an order, so the result is deterministic.
+//   2. scan: per expert, an exclusive scan over blocks, then over experts ->
+//      expert_offsets; the work lists are built from the per-expert counts.
+//   3. scatter: position = block base of the pair's expert + local rank.
+// One block (P <= kPlanChunk, the decode shapes) runs all three phases in a
+// single fused launch; larger P uses three launches.
+#include "device_common.h"
+#include "host_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kPlanThreads = 256;
+constexpr int kPlanWaves = kPlanThreads / 64;
+constexpr int kScanThreads = 1024;
+
+// Exclusive scan of a[0..n) in LDS with all threads of the block; returns the total.
+__device__ int block_exclusive_scan(int32_t* a, int n, int32_t* part) {
+  const int t = threadIdx.x, nt = blockDim.x;
+  const int per = (n + nt - 1) / nt;
+  const int lo = min(n, t * per), hi = min(n, lo + per);
+  int s = 0;
+  for (int i = lo; i < hi; ++i) s += a[i];
+  part[t] = s;
+  __syncthreads();
+  for (int off = 1; off < nt; off <<= 1) {
+    int v = t >= off ? part[t - off] : 0;
+    __syncthreads();
+    part[t] += v;
+    __syncthreads();
+  }
+  int run = part[t] - s;
+  for (int i = lo; i < hi; ++i) {
+    int v = a[i];
+    a[i] = run;
+    run += v;
+  }
+  const int total = part[nt - 1];
+  __syncthreads();
+  return total;
+}
+
+// Phase 1 for pairs [begin, end): local_rank[p] = number of earlier pairs of the
+// same expert inside [begin, end). cursor[E] must start at zero and ends holding
+// the per-expert counts of the range; wcnt[kPlanWaves * E] must start at zero and
+// ends at zero.
+__device__ void local_ranks(const int32_t* __restrict__ ids, int begin, int end, int E, int nbits,
+                            int32_t* __restrict__ local_rank, int32_t* cursor, int32_t* wcnt) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const uint64_t lower = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int base = begin; base < end; base += kPlanThreads) {
+    const int p = base + tid;
+    int key = -1;
+    if (p < end) {
+      const int v = ids[p];
+      key = (v >= 0 && v < E) ? v : -1;
+    }
+    const bool valid = key >= 0;
+    uint64_t peer = __ballot(valid);
+    for (int bit = 0; bit < nbits; ++bit) {
+      const bool b = valid && ((key >> bit) & 1);
+      const uint64_t m = __ballot(b);
+      peer &= b ? m : ~m;
+    }
+    const int rank = __popcll(peer & lower);
+    const int cnt = __popcll(peer);
+    const bool leader = valid && rank == 0;
+    if (leader) wcnt[wave * E + key] = cnt;
+    __syncthreads();
+    if (valid) {
+      int r = cursor[key] + rank;
+      for (int w = 0; w < wave; ++w) r += wcnt[w * E + key];
+      local_rank[p] = r;
+    }
+    __syncthreads();
+    if (leader) {
+      atomicAdd(&cursor[key], cnt);   // integer adds commute: order-independent
+      wcnt[wave * E + key] = 0;
+    }
+    __syncthreads();
+  }
+}
+
+// Work lists from per-expert counts cnt[E] (LDS): small-M tiles of kSmallRows rows
+// for experts with 1..small_max pairs (expert order), large-M tiles of kLargeRows
+// rows for the rest, heaviest expert first (ties: lower id first).
+__device__ void build_worklists(const int32_t* cnt, int E, int small_max, int2* __restrict__ small_items,
+                                int64_t small_cap, int2* __restrict__ large_items, int64_t large_cap,
+                                int32_t* __restrict__ hdr, int32_t* a1, int32_t* a2, int32_t* part) {
+  const int t = threadIdx.x, nt = blockDim.x;
+  for (int e = t; e < E; e += nt) {
+    const int m = cnt[e];
+    a1[e] = (m >= 1 && m <= small_max) ? (m + kSmallRows - 1) / kSmallRows : 0;
+  }
+  __syncthreads();
+  const int n_small = block_exclusive_scan(a1, E, part);
+  for (int e = t; e < E; e += nt) {
+    const int m = cnt[e];
+    if (m >= 1 && m <= small_max) {
+      const int s = a1[e];
+      for (int i = 0; i * kSmallRows < m; ++i)
+        if (s + i < small_cap) small_items[s + i] = make_int2(e, i * kSmallRows);
+    }
+  }
+  __syncthreads();
+  // heavy-first order of the large experts: a2[rank] = expert
+  for (int e = t; e < E; e += nt) {
+    const int m = cnt[e];
+    if (m > small_max) {
+      int r = 0;
+      for (int f = 0; f < E; ++f) {
+        const int mf = cnt[f];
+        r += (mf > small_max) && (mf > m || (mf == m && f < e));
+      }
+      a2[r] = e;
+    }
+  }
+  for (int e = t; e < E; e += nt) a1[e] = cnt[e] > small_max ? 1 : 0;
+  __syncthreads();
+  const int n_big = block_exclusive_scan(a1, E, part);
+  for (int r = t; r < E; r += nt) a1[r] = r < n_big ? (cnt[a2[r]] + kLargeRows - 1) / kLargeRows : 0;
+  __syncthreads();
+  const int n_large = block_exclusive_scan(a1, E, part);
+  for (int r = t; r < n_big; r += nt) {
+    const int e = a2[r], m = cnt[e], s = a1[r];
+    for (int i = 0; i * kLargeRows < m; ++i)
+      if (s + i < large_cap) large_items[s + i] = make_int2(e, i * kLargeRows);
+  }
+  if (t == 0) {
+    hdr[0] = n_small < small_cap ? n_small : (int)small_cap;
+    hdr[1] = n_large < large_cap ? n_large : (int)large_cap;
+  }
+}
+
+struct PlanArgs {
+  const int32_t* ids;
+  int32_t* offsets;
+  int32_t* sorted_pairs;
+  int32_t* pair_rows;
+  int32_t* status;
+  int32_t* hdr;
+  int2* small_items;
+  int2* large_items;
+  int32_t* local_rank;
+  int32_t* block_counts;
+  int32_t* block_base;
+  int64_t small_cap, large_cap;
+  int P, E, nbits, small_max, nb;
+};
+
+// Single-block plan: all three phases in one launch (P <= kPlanChunk).
+__global__ __launch_bounds__(kPlanThreads) void k_plan_fused(PlanArgs a) {
+  extern __shared__ int32_t lds[];
+  const int E = a.E;
+  int32_t* cnt = lds;                         // [E]
+  int32_t* wcnt = cnt + E;                    // [kPlanWaves * E]
+  int32_t* off = wcnt + kPlanWaves * E;       // [E + 1]
+  int32_t* a1 = off + E + 1;                  // [E]
+  int32_t* a2 = a1 + E;                       // [E]
+  int32_t* part = a2 + E;                     // [kPlanThreads]
+  const int t = threadIdx.x;
+  for (int i = t; i < (kPlanWaves + 1) * E; i += kPlanThreads) lds[i] = 0;
+  __syncthreads();
+  local_ranks(a.ids, 0, a.P, E, a.nbits, a.local_rank, cnt, wcnt);
+  for (int e = t; e < E; e += kPlanThreads) off[e] = cnt[e];
+  __syncthreads();
+  const int n_valid = block_exclusive_scan(off, E, part);
+  if (t == 0) {
+    off[E] = n_valid;
+    a.status[0] = a.P - n_valid;
+  }
+  __syncthreads();
+  for (int e = t; e <= E; e += kPlanThreads) a.offsets[e] = off[e];
+  for (int p = t; p < a.P; p += kPlanThreads) {
+    const int v = a.ids[p];
+    if (v >= 0 && v < E) {
+      const int pos = off[v] + a.local_rank[p];
+      a.sorted_pairs[pos] = p;
+      a.pair_rows[p] = pos;
+    } else {
+      a.pair_rows[p] = -1;
+    }
+    if (p >= n_valid) a.sorted_pairs[p] = -1;
+  }
+  build_worklists(cnt, E, a.small_max, a.small_items, a.small_cap, a.large_items, a.large_cap, a.hdr, a1, a2,
+                  part);
+}
+
+// Multi-block phase 1.
+__global__ __launch_bounds__(kPlanThreads) void k_plan_local(PlanArgs a) {
+  extern __shared__ int32_t lds[];
+  const int E = a.E;
+  int32_t* cnt = lds;
+  int32_t* wcnt = cnt + E;
+  const int t = threadIdx.x, b = blockIdx.x;
+  for (int i = t; i < (kPlanWaves + 1) * E; i += kPlanThreads) lds[i] = 0;
+  __syncthreads();
+  const int begin = b * kPlanChunk;
+  const int end = min(a.P, begin + kPlanChunk);
+  local_ranks(a.ids, begin, end, E, a.nbits, a.local_rank, cnt, wcnt);
+  for (int e = t; e < E; e += kPlanThreads) a.block_counts[(int64_t)b * E + e] = cnt[e];
+}
+
+// Multi-block phase 2 (one block of kScanThreads).
+__global__ __launch_bounds__(kScanThreads) void k_plan_scan(PlanArgs a) {
+  extern __shared__ int32_t lds[];
+  const int E = a.E, nb = a.nb;
+  int32_t* cnt = lds;               // [E]
+  int32_t* off = cnt + E;           // [E + 1]
+  int32_t* a1 = off + E + 1;        // [E]
+  int32_t* a2 = a1 + E;             // [E]
+  int32_t* part = a2 + E;           // [kScanThreads]
+  const int t = threadIdx.x;
+  for (int e = t; e < E; e += kScanThreads) {
+    int run = 0;
+    for (int b = 0; b < nb; ++b) {
+      const int c = a.block_counts[(int64_t)b * E + e];
+      a.block_base[(int64_t)b * E + e] = run;
+      run += c;
+    }
+    cnt[e] = run;
+    off[e] = run;
+  }
+  __syncthreads();
+  const int n_valid = block_exclusive_scan(off, E, part);
+  if (t == 0) {
+    off[E] = n_valid;
+    a.status[0] = a.P - n_valid;
+  }
+  __syncthreads();
+  for (int e = t; e <= E; e += kScanThreads) a.offsets[e] = off[e];
+  for (int e = t; e < E; e += kScanThreads)
+    for (int b = 0; b < nb; ++b) a.block_base[(int64_t)b * E + e] += off[e];
+  build_worklists(cnt, E, a.small_max, a.small_items, a.small_cap, a.large_items, a.large_cap, a.hdr, a1, a2,
+                  part);
+}
+
+// Multi-block phase 3.
+__global__ __launch_bounds__(256) void k_plan_scatter(PlanArgs a) {
+  const int p = blockIdx.x * 256 + threadIdx.x;
+  if (p >= a.P) return;
+  const int v = a.ids[p];
+  if (v >= 0 && v < a.E) {
+    const int pos = a.block_base[(int64_t)(p / kPlanChunk) * a.E + v] + a.local_rank[p];
+    a.sorted_pairs[pos] = p;
+    a.pair_rows[p] = pos;
+  } else {
+    a.pair_rows[p] = -1;
+  }
+  if (p >= a.offsets[a.E]) a.sorted_pairs[p] = -1;
+}
+
+}  // namespace
+
+size_t plan_ws_layout(const moe_dims& d, void* base, PlanWs* out) {
+  const int64_t P = (int64_t)d.T * d.K;
+  const int64_t nb = ceil_div(P, kPlanChunk) < 1 ? 1 : ceil_div(P, kPlanChunk);
+  const int64_t sc = small_items_bound(d), lc = large_items_bound(d);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = align_up(off + bytes, 256);
+    return o;
+  };
+  const size_t o_hdr = take(64);
+  const size_t o_small = take(sizeof(int2) * (size_t)(sc > 0 ? sc : 1));
+  const size_t o_large = take(sizeof(int2) * (size_t)(lc > 0 ? lc : 1));
+  const size_t o_rank = take(sizeof(int32_t) * (size_t)(P > 0 ? P : 1));
+  const size_t o_bc = take(sizeof(int32_t) * (size_t)(nb * d.E));
+  const size_t o_bb = take(sizeof(int32_t) * (size_t)(nb * d.E));
+  if (out) {
+    char* b = static_cast<char*>(base);
+    out->hdr = reinterpret_cast<int32_t*>(b + o_hdr);
+    out->small_items = reinterpret_cast<int2*>(b + o_small);
+    out->large_items = reinterpret_cast<int2*>(b + o_large);
+    out->local_rank = reinterpret_cast<int32_t*>(b + o_rank);
+    out->block_counts = reinterpret_cast<int32_t*>(b + o_bc);
+    out->block_base = reinterpret_cast<int32_t*>(b + o_bb);
+    out->small_cap = sc;
+    out->large_cap = lc;
+    out->nb = nb;
+  }
+  return off;
+}
+
+hipError_t launch_plan(const moe_dims& d, const int32_t* ids, int32_t* offsets, int32_t* sorted_pairs,
+                       int32_t* pair_rows, int32_t* status, const PlanWs& ws, hipStream_t s) {
+  PlanArgs a;
+  a.ids = ids;
+  a.offsets = offsets;
+  a.sorted_pairs = sorted_pairs;
+  a.pair_rows = pair_rows;
+  a.status = status;
+  a.hdr = ws.hdr;
+  a.small_items = ws.small_items;
+  a.large_items = ws.large_items;
+  a.local_rank = ws.local_rank;
+  a.block_counts = ws.block_counts;
+  a.block_base = ws.block_base;
+  a.small_cap = ws.small_cap;
+  a.large_cap = ws.large_cap;
+  a.P = d.T * d.K;
+  a.E = d.E;
+  int nbits = 0;
+  while ((1 << nbits) < d.E) ++nbits;
+  a.nbits = nbits;
+  a.small_max = small_max_of(d);
+  a.nb = (int)ws.nb;
+  if (a.P <= kPlanChunk) {
+    const size_t lds = sizeof(int32_t) * ((size_t)(kPlanWaves + 4) * d.E + 1 + kPlanThreads);
+    if (lds > 65536) {
+      hipError_t e = hipFuncSetAttribute((const void*)k_plan_fused, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                         (int)lds);
+      if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(k_plan_fused, dim3(1), dim3(kPlanThreads), lds, s, a);
+    return hipGetLastError();
+  }
+  const size_t lds_local = sizeof(int32_t) * (size_t)(kPlanWaves + 1) * d.E;
+  hipError_t err = hipSuccess;
+  if (lds_local > 65536) {
+    err = hipFuncSetAttribute((const void*)k_plan_local, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_local);
+    if (err != hipSuccess) return err;
+  }
+  hipLaunchKernelGGL(k_plan_local, dim3(a.nb), dim3(kPlanThreads), lds_local, s, a);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const size_t lds_scan = sizeof(int32_t) * ((size_t)4 * d.E + 1 + kScanThreads);
+  if (lds_scan > 65536) {
+    err = hipFuncSetAttribute((const void*)k_plan_scan, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_scan);
+    if (err != hipSuccess) return err;
+  }
+  hipLaunchKernelGGL(k_plan_scan, dim3(1), dim3(kScanThreads), lds_scan, s, a);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(k_plan_scatter, dim3((unsigned)ceil_div(a.P, 256)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -43,17 +43,18 @@ def _signed_index(codes: np.ndarray) -> np.ndarray:
 
 
 def h_code_mismatch(hq, hs, hq_ref, hs_ref, amax_ref, block: int = 128) -> dict:
-    """Count SwiGLU-output code mismatches under the tolerance rule.
+    """Compare SwiGLU-output codes element by element.
 
     hq, hq_ref uint8 [R, C]; hs, hs_ref uint8 [R, C/block]; amax_ref float64
-    [R, C/block] (the oracle's block amax).
-
-    * Same scale code: an element matches if its grid positions differ by <= 1.
-    * Scale codes differ: allowed only for blocks whose oracle amax is within
-      2^-16 (relative) of a boundary 1.75 * 2^p; an element there matches if the
-      decoded values differ by at most one grid step of the coarser scale. In any
-      other block every element counts as a mismatch.
-    Returns counts and the fraction of mismatching elements.
+    [R, C/block] (the oracle's block amax). Each element is
+      equal  -- same decoded value (+0 and -0 are equal);
+      close  -- the two values are neighbours: same scale and grid positions one
+                apart, or, in a block whose scale differs, a block whose oracle
+                amax is within 2^-16 (relative) of a scale boundary 1.75 * 2^p and
+                values at most one grid step of the coarser scale apart;
+      bad    -- anything else (a scale that differs away from a boundary counts
+                every element of its block as bad).
+    The bar: no bad element, and at most 0.1% of elements close-but-unequal.
     """
     hq = np.asarray(hq).reshape(-1, np.asarray(hq).shape[-1])
     hq_ref = np.asarray(hq_ref).reshape(hq.shape)
@@ -65,23 +66,25 @@ def h_code_mismatch(hq, hs, hq_ref, hs_ref, amax_ref, block: int = 128) -> dict:
 
     a = hq.reshape(R, nb, block)
     b = hq_ref.reshape(R, nb, block)
-    same = (hs == hs_ref)[..., None]
-    close_same = np.abs(_signed_index(a) - _signed_index(b)) <= 1
-
-    m, ex = np.frexp(amax)               # amax = 2m * 2^(ex-1)
-    boundary = 1.75 * np.ldexp(1.0, ex - 1)
-    near = np.abs(amax - boundary) <= amax * 2.0 ** -16
     va = E4M3_VALUES[a] * np.ldexp(1.0, hs - 127)[..., None]
     vb = E4M3_VALUES[b] * np.ldexp(1.0, hs_ref - 127)[..., None]
-    coarse = np.maximum(hs, hs_ref) - 127
-    # one grid step of the coarser lattice at this magnitude
-    mag = np.maximum(np.abs(va), np.abs(vb)) / np.ldexp(1.0, coarse)[..., None]
+    equal = va == vb
+    same = (hs == hs_ref)[..., None]
+    dist = np.abs(_signed_index(a) - _signed_index(b))
+
+    _, ex = np.frexp(amax)               # amax = 2m * 2^(ex-1)
+    boundary = 1.75 * np.ldexp(1.0, ex - 1)
+    near = np.abs(amax - boundary) <= amax * 2.0 ** -16
+    coarse = np.ldexp(1.0, np.maximum(hs, hs_ref) - 127)[..., None]
+    mag = np.maximum(np.abs(va), np.abs(vb)) / coarse
     _, mex = np.frexp(np.maximum(mag, 2.0 ** -6))
-    step = np.ldexp(1.0, (mex - 1 - 3)) * np.ldexp(1.0, coarse)[..., None]
+    step = np.ldexp(1.0, mex - 1 - 3) * coarse
     close_diff = near[..., None] & (np.abs(va - vb) <= step)
 
-    ok = np.where(same, close_same, close_diff)
-    bad = int((~ok).sum())
-    return {"elements": int(a.size), "mismatch": bad, "frac": bad / max(a.size, 1),
+    close = ~equal & np.where(same, dist <= 1, close_diff)
+    bad = ~equal & ~close
+    n = int(a.size)
+    return {"elements": n, "differ": int((~equal).sum()), "bad": int(bad.sum()),
+            "frac_differ": float((~equal).sum()) / max(n, 1),
             "scale_diff_blocks": int((~same[..., 0]).sum()),
-            "max_code_dist_same_scale": int(np.where(same, np.abs(_signed_index(a) - _signed_index(b)), 0).max()) if a.size else 0}
+            "max_code_dist_same_scale": int(np.where(same, dist, 0).max()) if n else 0}

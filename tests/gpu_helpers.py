@@ -1,0 +1,82 @@
+"""Helpers shared by the GPU parity tests: run the HIP path through the C-ABI
+binding, run the oracle on the same seeded inputs, compare."""
+
+from __future__ import annotations
+
+import sys
+import time
+
+import numpy as np
+import torch
+
+import mxfp4_weights_fp8_amd as moe
+from oracle.compare import h_code_mismatch, y_metrics
+from oracle.moe import ffn_ref, plan_ref
+
+#: the parity bar for the final output (vs the float64 oracle)
+MAX_REL = 2e-2
+MEAN_REL = 2e-3
+#: SwiGLU-output codes: at most this fraction may differ (each by at most one grid step)
+H_DIFFER = 1e-3
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def u16(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def run_path(inp, small_max=0, debug=True):
+    """plan + ffn on the GPU for MoEInputs already on the device."""
+    w = inp.wl
+    p = moe.plan(inp.topk_ids, w.E, w.H, w.I, small_max=small_max, Is=w.Is if inp.shared else 0)
+    out = moe.ffn(inp.x, inp.topk_weights, p, inp.weights, shared=inp.shared, debug=debug)
+    torch.cuda.synchronize()
+    return p, out
+
+
+def check_plan(p, ids_np, E):
+    ref = plan_ref(ids_np, E)
+    P = ids_np.size
+    assert np.array_equal(p.expert_offsets.cpu().numpy(), ref["expert_offsets"])
+    assert np.array_equal(p.sorted_pairs.cpu().numpy()[:P], ref["sorted_pairs"])
+    assert np.array_equal(p.pair_rows.cpu().numpy()[:P], ref["pair_rows"])
+    assert int(p.status.cpu()[0]) == ref["dropped"]
+
+
+def check_ffn(inp, p, y, dbg, tokens=None, label=""):
+    """Oracle on the selected tokens; compare y, x codes, SwiGLU codes. Returns metrics."""
+    t0 = time.time()
+    ref = ffn_ref(inp.x, inp.topk_ids, inp.topk_weights, **inp.weights, shared=inp.shared, tokens=tokens)
+    t_oracle = time.time() - t0
+    sel = np.arange(inp.wl.T) if tokens is None else np.asarray(tokens)
+    yb = u16(y)[sel]
+    m = y_metrics(yb, ref["y"])
+    # activation codes: bit-exact
+    assert np.array_equal(dbg["x_q"].cpu().numpy()[sel], ref["x_q"]), "x_q differs"
+    assert np.array_equal(dbg["x_s"].cpu().numpy()[sel], ref["x_s"]), "x_s differs"
+    # SwiGLU codes of every valid pick of the selected tokens, rows in plan order
+    K = inp.wl.K
+    rows = p.pair_rows.cpu().numpy()
+    valid = ref["valid"]
+    prow = np.array([[rows[t * K + j] for j in range(K)] for t in sel])
+    hq = dbg["h_q"].cpu().numpy()[prow[valid]]
+    hs = dbg["h_s"].cpu().numpy()[prow[valid]]
+    hm = h_code_mismatch(hq, hs, ref["h_q"][valid], ref["h_s"][valid], ref["h_amax"][valid])
+    m.update({"h_" + k: v for k, v in hm.items()}, oracle_s=round(t_oracle, 2), label=label)
+    if inp.shared is not None:
+        shm = h_code_mismatch(dbg["sh_q"].cpu().numpy()[sel][:, :inp.wl.Is], dbg["sh_s"].cpu().numpy()[sel][:, :inp.wl.Is // 128],
+                              ref["shared_h_q"], ref["shared_h_s"], ref["shared_h_amax"])
+        m.update({"sh_" + k: v for k, v in shm.items()})
+    say(f"[parity {label}] {m}")
+    assert m["finite"], m
+    assert m["max_rel"] <= MAX_REL, m
+    assert m["mean_rel"] <= MEAN_REL, m
+    assert m["h_bad"] == 0, m
+    assert m["h_frac_differ"] <= H_DIFFER, m
+    if inp.shared is not None:
+        assert m["sh_bad"] == 0 and m["sh_frac_differ"] <= H_DIFFER, m
+    return m

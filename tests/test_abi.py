@@ -1,0 +1,93 @@
+"""The C-ABI library loads and exports every entry point the header declares, and
+its host-side argument checks behave as documented. Nothing here launches GPU work."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import mxfp4_weights_fp8_amd as moe
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "moe_mxfp4.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_symbols():
+    assert declared_functions() == sorted(moe._SIGNATURES)
+
+
+def test_library_exports_every_declared_symbol():
+    L = ctypes.CDLL(moe.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_status_strings():
+    for c in (0, -1, -2, -3, -4):
+        assert moe.status_string(c).startswith("MOE_")
+    assert "unknown" in moe.status_string(7)
+
+
+@pytest.mark.parametrize("dims,code", [
+    ((64, 256, 512, 8, 2), moe.MOE_OK),
+    ((0, 7168, 3072, 384, 8), moe.MOE_OK),
+    ((-1, 256, 512, 8, 2), moe.MOE_EINVAL),
+    ((4, 256, 512, 0, 2), moe.MOE_EINVAL),
+    ((4, 256, 512, 8, 0), moe.MOE_EINVAL),
+    ((4, 256, 512, 4097, 2), moe.MOE_EINVAL),
+    ((4, 200, 512, 8, 2), moe.MOE_EUNSUPPORTED),
+    ((4, 256, 500, 8, 2), moe.MOE_EUNSUPPORTED),
+])
+def test_validate(dims, code):
+    assert moe.validate(moe.make_dims(*dims)) == code
+
+
+def test_validate_null_and_shared():
+    assert moe.lib().moe_validate(None) == moe.MOE_EINVAL
+    assert moe.validate(moe.make_dims(4, 256, 512, 8, 2, Is=100)) == moe.MOE_EUNSUPPORTED
+    assert moe.validate(moe.make_dims(4, 256, 512, 8, 2, Is=128)) == moe.MOE_OK
+
+
+def test_workspace_sizes():
+    d = moe.make_dims(32768, 7168, 3072, 384, 8)
+    ffn = moe.ffn_workspace_bytes(d)
+    P = 32768 * 8
+    assert ffn >= 32768 * 7168 + P * 3072 + 4 * P * 7168       # x_q + h_q + fp32 per-pair rows
+    assert moe.plan_workspace_bytes(d) >= 4 * P
+    assert moe.ffn_workspace_bytes(moe.make_dims(4, 200, 512, 8, 2)) == 0   # invalid dims -> 0
+    small = moe.make_dims(7, 7168, 3072, 384, 8)
+    assert 0 < moe.ffn_workspace_bytes(small) < ffn
+
+
+def test_host_checks_reject_before_enqueue():
+    L = moe.lib()
+    d = moe.make_dims(4, 256, 512, 8, 2)
+    fake = ctypes.c_void_p(0x1000)   # never dereferenced: every check below fails first
+    # null outputs
+    assert L.moe_plan(ctypes.byref(d), fake, None, fake, fake, fake, fake, 1 << 20, None) == moe.MOE_EINVAL
+    # workspace too small
+    assert L.moe_plan(ctypes.byref(d), fake, fake, fake, fake, fake, fake, 1, None) == moe.MOE_EWORKSPACE
+    args = [fake] * 10
+    assert L.moe_ffn(ctypes.byref(d), *args, None, fake, None, fake, 1, None) == moe.MOE_EWORKSPACE
+    args[0] = None
+    assert L.moe_ffn(ctypes.byref(d), *args, None, fake, None, fake, 1 << 30, None) == moe.MOE_EINVAL
+    assert L.moe_quant_act(ctypes.byref(d), None, fake, fake, None) == moe.MOE_EINVAL
+    # T == 0 is a no-op for the FFN and the quantizer
+    z = moe.make_dims(0, 256, 512, 8, 2)
+    assert L.moe_ffn(ctypes.byref(z), *([None] * 10), None, None, None, None, 0, None) == moe.MOE_OK
+    assert L.moe_quant_act(ctypes.byref(z), None, None, None, None) == moe.MOE_OK
+
+
+def test_product_path_has_no_cpu_fallback():
+    """The binding raises when the library is absent instead of computing anything."""
+    import importlib
+    src = open(moe.__file__).read()
+    assert "oracle" not in src and "synth" not in src
+    assert "raise RuntimeError" in src
+    importlib.reload(moe)

@@ -1,0 +1,192 @@
+"""GPU parity: the HIP path (through the C-ABI) against the CPU oracle on the same
+seeded inputs. Plans and activation codes bit-exact; SwiGLU codes within one grid
+step on at most 0.1% of elements; y within max-rel 2e-2 / mean-rel 2e-3."""
+
+import numpy as np
+import pytest
+import torch
+
+import mxfp4_weights_fp8_amd as moe
+from gpu_helpers import check_ffn, check_plan, run_path, say, u16
+from oracle.formats import bf16_to_f64
+from oracle.moe import quant_act_ref
+from synth import WORKLOADS, make_expert_weights, make_inputs, make_routing, scaled
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev(gpu):
+    moe.lib()
+    return gpu
+
+
+# ----------------------------------------------------------------------------- quantizer
+
+def test_quant_act_every_bf16_value(dev):
+    """Every finite bf16 pattern, shuffled into 128-column blocks (so block scales
+    span the whole exponent range), plus zero blocks and blocks whose amax sits on
+    and next to a scale boundary 1.75 * 2^p: codes and scales bit-exact."""
+    allv = np.arange(65536, dtype=np.uint16)
+    fin = allv[np.isfinite(bf16_to_f64(allv))]
+    rows = []
+    for seed in range(3):
+        perm = np.random.default_rng(seed).permutation(fin)
+        n = perm.size // 128 * 128
+        rows.append(perm[:n].reshape(-1, 128))
+    sorted_rows = np.sort(fin)[: fin.size // 128 * 128].reshape(-1, 128)   # narrow-range blocks
+    rows.append(sorted_rows)
+    special = np.zeros((8, 128), dtype=np.uint16)                          # zeros, -0, boundaries
+    special[1, :] = 0x8000
+    b175 = np.float32(1.75).view(np.uint32) >> 16                          # bf16 1.75
+    special[2, 0] = b175
+    special[3, 0] = b175 + 1
+    special[4, 5] = b175 | 0x8000
+    special[5, :] = np.random.default_rng(9).integers(0, 0x80, 128)        # subnormals only
+    special[6, 7] = 0x7F7F                                                  # largest finite
+    special[7, :] = 0x3F80
+    rows.append(special)
+    X = np.concatenate(rows)
+    T = X.shape[0] // 8 * 8
+    X = X[:T].reshape(T // 8, 8 * 128)            # H = 1024
+    x = torch.from_numpy(X.view(np.int16)).view(torch.bfloat16).to(dev)
+    xq, xs = moe.quant_act(x)
+    torch.cuda.synchronize()
+    rq, rs = quant_act_ref(X)
+    assert np.array_equal(xs.cpu().numpy(), rs)
+    assert np.array_equal(xq.cpu().numpy(), rq)
+
+
+# ----------------------------------------------------------------------------- planner
+
+@pytest.mark.parametrize("T,K,E,seed", [(1, 1, 1, 0), (7, 8, 384, 1), (64, 2, 8, 2), (256, 8, 384, 3),
+                                        (255, 3, 5, 4), (300, 8, 4096, 5), (4096, 8, 384, 6), (5000, 7, 64, 7)])
+def test_plan_random(dev, T, K, E, seed):
+    ids = np.random.default_rng(seed).integers(0, E, (T, K)).astype(np.int32)
+    p = moe.plan(torch.from_numpy(ids).to(dev), E, 256, 256)
+    torch.cuda.synchronize()
+    check_plan(p, ids, E)
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode7", "decode256", "prefill32k"])
+def test_plan_workloads(dev, name):
+    w = WORKLOADS[name]
+    ids, _ = make_routing(w)
+    p = moe.plan(torch.from_numpy(ids).to(dev), w.E, w.H, w.I)
+    torch.cuda.synchronize()
+    check_plan(p, ids, w.E)
+
+
+@pytest.mark.parametrize("T", [100, 3000])
+def test_plan_invalid_ids_dropped(dev, T):
+    rng = np.random.default_rng(T)
+    ids = rng.integers(0, 16, (T, 4)).astype(np.int32)
+    bad = rng.random(ids.shape) < 0.1
+    ids[bad] = rng.choice([-1, 16, 1 << 30, -(1 << 30)], bad.sum())
+    p = moe.plan(torch.from_numpy(ids).to(dev), 16, 256, 256)
+    torch.cuda.synchronize()
+    check_plan(p, ids, 16)
+
+
+def test_plan_empty(dev):
+    p = moe.plan(torch.zeros((0, 8), dtype=torch.int32, device=dev), 32, 256, 256)
+    torch.cuda.synchronize()
+    assert not p.expert_offsets.cpu().numpy().any() and int(p.status.cpu()[0]) == 0
+
+
+# ----------------------------------------------------------------------------- FFN, small shapes
+
+@pytest.mark.parametrize("small_max", [0, 1, 10 ** 6])
+def test_ffn_tiny(dev, small_max):
+    """Tiny config (64 tokens, H 256, 8 experts, I 512, top-2) in full, with the
+    default small/large split, everything on the large-M path, everything small."""
+    inp = make_inputs("tiny").to(dev)
+    p, (y, dbg) = run_path(inp, small_max=small_max)
+    check_plan(p, inp.topk_ids.cpu().numpy(), inp.wl.E)
+    check_ffn(inp, p, y, dbg, label=f"tiny small_max={small_max}")
+
+
+@pytest.mark.parametrize("T,H,I,E,K,seed", [
+    (1, 128, 128, 1, 1, 41),        # degenerate: one token, one expert
+    (33, 384, 384, 5, 3, 42),       # ragged: odd T, H and I not multiples of 256
+    (130, 640, 256, 3, 2, 43),      # experts with > 128 rows (several large tiles + a tail)
+    (17, 256, 1152, 40, 8, 44),     # many experts, I = 9 * 128
+])
+def test_ffn_shapes(dev, T, H, I, E, K, seed):
+    wl = scaled("tiny", T=T, H=H, I=I, E=E, K=K, seed=seed, weight_seed=seed, name=f"s{seed}")
+    inp = make_inputs(wl).to(dev)
+    p, (y, dbg) = run_path(inp)
+    check_ffn(inp, p, y, dbg, label=f"shape {T}x{H} I{I} E{E} K{K}")
+
+
+def test_ffn_invalid_ids(dev):
+    inp = make_inputs("tiny").to(dev)
+    ids = inp.topk_ids.clone()
+    ids[::5, 1] = -3
+    ids[3, 0] = 99
+    inp.topk_ids = ids
+    p, (y, dbg) = run_path(inp)
+    assert int(p.status.cpu()[0]) == int((ids < 0).sum() + (ids >= inp.wl.E).sum())
+    check_ffn(inp, p, y, dbg, label="tiny with dropped ids")
+
+
+def test_ffn_deterministic_and_token_permutation(dev):
+    inp = make_inputs(scaled("tiny", T=200, E=16, K=4, name="perm")).to(dev)
+    _, (y1, _) = run_path(inp)
+    _, (y2, _) = run_path(inp)
+    assert torch.equal(y1, y2)
+    perm = torch.from_numpy(np.random.default_rng(3).permutation(200)).to(dev)
+    inp.x, inp.topk_ids, inp.topk_weights = inp.x[perm].contiguous(), inp.topk_ids[perm].contiguous(), \
+        inp.topk_weights[perm].contiguous()
+    _, (y3, _) = run_path(inp)
+    assert torch.equal(y3, y1[perm])
+
+
+# ----------------------------------------------------------------------------- FFN, full sizes
+
+@pytest.fixture(scope="module")
+def full_weights(dev):
+    """The 384-expert MXFP4 weight set of the H 7168 / I 3072 workloads (13.5 GB),
+    generated on the GPU once for this module."""
+    import time
+    t = time.time()
+    W = make_expert_weights(WORKLOADS["decode7"], dev)
+    torch.cuda.synchronize()
+    say(f"[full weights] generated in {time.time() - t:.1f}s")
+    return W
+
+
+def _full_inputs(name, dev, W):
+    inp = make_inputs(name, weights=False).to(dev)
+    inp.weights = W
+    return inp
+
+
+def test_ffn_decode7_full(dev, full_weights):
+    """7-token verify at full size, every token checked against the oracle."""
+    inp = _full_inputs("decode7", dev, full_weights)
+    p, (y, dbg) = run_path(inp)
+    check_plan(p, inp.topk_ids.cpu().numpy(), inp.wl.E)
+    check_ffn(inp, p, y, dbg, label="decode7 full")
+
+
+def test_ffn_decode256_sampled(dev, full_weights):
+    inp = _full_inputs("decode256", dev, full_weights)
+    p, (y, dbg) = run_path(inp)
+    toks = np.random.default_rng(1).choice(inp.wl.T, 12, replace=False)
+    check_ffn(inp, p, y, dbg, tokens=toks, label="decode256 sampled")
+    assert torch.isfinite(y.float()).all()
+
+
+def test_ffn_prefill32k_sampled(dev, full_weights):
+    inp = _full_inputs("prefill32k", dev, full_weights)
+    p, (y, dbg) = run_path(inp)
+    # tokens routed to the hottest expert, to a median one, and random ones
+    counts = np.bincount(inp.topk_ids.cpu().numpy().ravel(), minlength=384)
+    hot = int(np.argmax(counts))
+    ids = inp.topk_ids.cpu().numpy()
+    toks = list(np.nonzero((ids == hot).any(1))[0][[0, -1]])
+    toks += list(np.random.default_rng(2).choice(inp.wl.T, 4, replace=False))
+    toks += [inp.wl.T - 1]
+    check_ffn(inp, p, y, dbg, tokens=toks, label="prefill32k sampled")
+    assert torch.isfinite(y.float()).all()
