@@ -48,12 +48,16 @@ def h_code_mismatch(hq, hs, hq_ref, hs_ref, amax_ref, block: int = 128) -> dict:
     hq, hq_ref uint8 [R, C]; hs, hs_ref uint8 [R, C/block]; amax_ref float64
     [R, C/block] (the oracle's block amax). Each element is
       equal  -- same decoded value (+0 and -0 are equal);
-      close  -- the two values are neighbours: same scale and grid positions one
-                apart, or, in a block whose scale differs, a block whose oracle
-                amax is within 2^-16 (relative) of a scale boundary 1.75 * 2^p and
-                values at most one grid step of the coarser scale apart;
-      bad    -- anything else (a scale that differs away from a boundary counts
-                every element of its block as bad).
+      close  -- the values are neighbours:
+                * same scale and grid positions one apart; or
+                * same scale, both values below 2^-5 * scale (where the E4M3 grid
+                  has the fixed step 2^-9 * scale, finer than the rounding inside
+                  a hardware MX dot product) and at most 2^-6 * scale apart; or
+                * a scale that differs in a block whose oracle amax is within
+                  2^-16 (relative) of a scale boundary 1.75 * 2^p, and values at
+                  most one grid step of the coarser scale apart;
+      bad    -- anything else (a scale that differs away from a boundary makes
+                every element of its block bad).
     The bar: no bad element, and at most 0.1% of elements close-but-unequal.
     """
     hq = np.asarray(hq).reshape(-1, np.asarray(hq).shape[-1])
@@ -66,11 +70,15 @@ def h_code_mismatch(hq, hs, hq_ref, hs_ref, amax_ref, block: int = 128) -> dict:
 
     a = hq.reshape(R, nb, block)
     b = hq_ref.reshape(R, nb, block)
-    va = E4M3_VALUES[a] * np.ldexp(1.0, hs - 127)[..., None]
-    vb = E4M3_VALUES[b] * np.ldexp(1.0, hs_ref - 127)[..., None]
+    scale_a = np.ldexp(1.0, hs - 127)[..., None]
+    scale_b = np.ldexp(1.0, hs_ref - 127)[..., None]
+    va = E4M3_VALUES[a] * scale_a
+    vb = E4M3_VALUES[b] * scale_b
     equal = va == vb
     same = (hs == hs_ref)[..., None]
     dist = np.abs(_signed_index(a) - _signed_index(b))
+    fixed_step = (np.abs(E4M3_VALUES[a]) < 2.0 ** -5) & (np.abs(E4M3_VALUES[b]) < 2.0 ** -5) & \
+        (np.abs(va - vb) <= 2.0 ** -6 * scale_b)
 
     _, ex = np.frexp(amax)               # amax = 2m * 2^(ex-1)
     boundary = 1.75 * np.ldexp(1.0, ex - 1)
@@ -81,10 +89,13 @@ def h_code_mismatch(hq, hs, hq_ref, hs_ref, amax_ref, block: int = 128) -> dict:
     step = np.ldexp(1.0, mex - 1 - 3) * coarse
     close_diff = near[..., None] & (np.abs(va - vb) <= step)
 
-    close = ~equal & np.where(same, dist <= 1, close_diff)
+    close = ~equal & np.where(same, (dist <= 1) | fixed_step, close_diff)
     bad = ~equal & ~close
     n = int(a.size)
-    return {"elements": n, "differ": int((~equal).sum()), "bad": int(bad.sum()),
+    idx = np.argwhere(bad)[:5]
+    examples = [(int(a[i, j, k]), int(b[i, j, k]), float(va[i, j, k]), float(vb[i, j, k]), float(amax[i, j]))
+                for i, j, k in idx]
+    return {"elements": n, "bad_examples": examples, "differ": int((~equal).sum()), "bad": int(bad.sum()),
             "frac_differ": float((~equal).sum()) / max(n, 1),
             "scale_diff_blocks": int((~same[..., 0]).sum()),
             "max_code_dist_same_scale": int(np.where(same, dist, 0).max()) if n else 0}
