@@ -1,0 +1,199 @@
+"""Benchmark of the routed MoE FFN (MXFP4 weights, FP8 activations) on one MI355X.
+
+A step is one pass of the whole hot path over one batch resident in HBM: route
+plan (moe_plan) + activation quantization, W13 GEMM with the fused SwiGLU + FP8
+requantization, W2 GEMM and the top-k combine (moe_ffn).
+
+The headline line is the 7-token decode verify (H 7168, 384 experts, I 3072,
+top-8, Zipf 1.0 routing): tokens/s, with the roofline of its dominant kernel
+(the W13 weight stream, HBM-bound). The same JSON line carries the 32K-token
+prefill chunk (Zipf 1.2) as "prefill32k", with the MFMA roofline of its W13
+GEMM, because the metric names both. Kernel durations come from HIP events the
+library records on the stream it launches on; the oracle's CPU time on a
+bounded sample is reported as cpu_baseline.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-prefill] [--no-cpu]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import mxfp4_weights_fp8_amd as moe  # noqa: E402
+from synth import WORKLOADS, make_expert_weights, make_inputs  # noqa: E402
+
+METRIC = "MoE FFN tokens/s + % MFMA peak (32K prefill) + HBM GB/s (decode M=7)"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_PEAK_FP8_TFLOPS = 5000.0  # dense FP8 rate; a block-scaled MFMA with one 8-bit operand issues at it
+MFMA_PEAK_FP4_TFLOPS = 10100.0 # dense FP4/FP6 rate (both operands <= 6 bits)
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def expert_bytes(w) -> dict:
+    """Algorithmic bytes of one expert's MXFP4 weights (codes + E8M0 scales)."""
+    H, I = w.H, w.I
+    w13 = 2 * I * H // 2 + 2 * I * H // 32
+    w2 = H * I // 2 + H * I // 32
+    return {"w13": w13, "w2": w2}
+
+
+class Runner:
+    """Holds one workload resident on the GPU and runs steps of the hot path."""
+
+    def __init__(self, name: str, dev, weights=None):
+        self.w = WORKLOADS[name]
+        w = self.w
+        inp = make_inputs(name, weights=False).to(dev)
+        inp.weights = weights if weights is not None else make_expert_weights(w, dev)
+        self.inp = inp
+        self.dev = dev
+        self.plan = moe.plan(inp.topk_ids, w.E, w.H, w.I, Is=w.Is)
+        d = self.plan.dims
+        self.ws = torch.empty(moe.ffn_workspace_bytes(d), dtype=torch.uint8, device=dev)
+        self.y = torch.empty((w.T, w.H), dtype=torch.bfloat16, device=dev)
+        ids = inp.topk_ids.cpu().numpy()
+        self.distinct = int(len(np.unique(ids[(ids >= 0) & (ids < w.E)])))
+
+    def step(self, events=None):
+        w = self.w
+        moe.plan(self.inp.topk_ids, w.E, w.H, w.I, Is=w.Is, out=self.plan)
+        moe.ffn(self.inp.x, self.inp.topk_weights, self.plan, self.inp.weights, shared=self.inp.shared,
+                ws=self.ws, y=self.y, events=events)
+
+    def run(self, steps: int, warmup: int):
+        for _ in range(warmup):
+            self.step()
+        torch.cuda.synchronize()
+        evs = [moe.StageEvents() for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            self.step(evs[i])
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        stages = {"quant": (moe.EV_START, moe.EV_QUANT_DONE), "w13": (moe.EV_QUANT_DONE, moe.EV_W13_DONE),
+                  "w2": (moe.EV_W13_DONE, moe.EV_W2_DONE), "shared": (moe.EV_W2_DONE, moe.EV_SHARED_DONE),
+                  "combine": (moe.EV_SHARED_DONE, moe.EV_END), "ffn": (moe.EV_START, moe.EV_END)}
+        ms = {k: float(np.mean([e.elapsed_ms(a, b) for e in evs])) for k, (a, b) in stages.items()}
+        return (t1 - t0) * 1e3 / steps, ms
+
+
+def cpu_baseline(name: str, weights_dev, tokens) -> dict:
+    """The oracle, as it stands, on a bounded sample of the workload's tokens.
+    The experts those tokens use are copied to host memory before the clock starts."""
+    from oracle.moe import ffn_ref
+
+    inp = make_inputs(name, weights=False)
+    ids = inp.topk_ids.numpy()[tokens]
+    used = sorted(set(int(e) for e in ids.ravel() if 0 <= e < inp.wl.E))
+    host = {k: torch.empty(v.shape, dtype=v.dtype) for k, v in weights_dev.items()}   # untouched rows unused
+    for k, v in weights_dev.items():
+        host[k][used] = v[used].cpu()
+    t0 = time.perf_counter()
+    ffn_ref(inp.x, inp.topk_ids, inp.topk_weights, **host, tokens=tokens)
+    dt = time.perf_counter() - t0
+    return {"value": len(tokens) / dt, "unit": "tokens/s", "cores": torch.get_num_threads(), "kind": "oracle",
+            "sample": f"{len(tokens)} of {inp.wl.T} tokens of {name} (float64 oracle incl. expert dequant), "
+                      f"{dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--prefill-steps", type=int, default=5)
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on one GPU; multi-GPU runs are not part of it "
+              f"(asked for --gpus {args.gpus})", file=sys.stderr)
+        sys.exit(2)
+
+    dev = torch.device("cuda:0")
+    moe.lib()
+    t = time.time()
+    W = make_expert_weights(WORKLOADS["decode7"], dev)     # one 384-expert set, shared by both workloads
+    torch.cuda.synchronize()
+    log(f"[bench] weights generated in {time.time() - t:.1f}s")
+
+    # ---- decode verify, 7 tokens (headline)
+    dec = Runner("decode7", dev, W)
+    ms_step, ms = dec.run(args.steps, args.warmup)
+    w = dec.w
+    eb = expert_bytes(w)
+    # W13 stage: every touched expert's W13 codes + scales once, the routed activation
+    # rows (codes + scales) and the SwiGLU output (codes + scales) of every pair
+    P = w.T * w.K
+    w13_bytes = dec.distinct * eb["w13"] + w.T * (w.H + w.H // 128) + P * (w.I + w.I // 128)
+    w13_gbs = w13_bytes / (ms["w13"] * 1e-3) / 1e9
+    step_bytes = dec.distinct * (eb["w13"] + eb["w2"]) + w.T * w.H * 2 * 2
+    log(f"[bench] decode7: {ms_step:.3f} ms/step, stages {ms}, distinct experts {dec.distinct}")
+    out = {
+        "metric": METRIC,
+        "value": w.T / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8e4m3 x fp4e2m1 (E8M0 block scales), fp32 accumulate",
+        "data": "synthetic (seeded: x N(0,1) bf16, Zipf routing, N(0,0.02) weights packed to MXFP4)",
+        "config": {"workload": "decode7", "tokens": w.T, "hidden": w.H, "experts": w.E, "intermediate": w.I,
+                   "top_k": w.K, "routing": f"zipf s={w.zipf_s}", "distinct_experts": dec.distinct},
+        "roofline": {"bound": "hbm", "kernel": "W13 grouped GEMM + SwiGLU/requant (k_w13_small)",
+                     "achieved": w13_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": w13_gbs / HBM_PEAK_GBS,
+                     "traffic": None, "algorithmic_bytes_per_launch": w13_bytes, "avg_launch_ms": ms["w13"]},
+        "step_hbm_gbs": step_bytes / (ms_step * 1e-3) / 1e9,
+        "stage_ms": ms,
+    }
+
+    # ---- prefill chunk, 32K tokens
+    if not args.no_prefill:
+        pre = Runner("prefill32k", dev, W)
+        ps, pms = pre.run(args.prefill_steps, 1)
+        pw = pre.w
+        Pp = pw.T * pw.K
+        f13 = 2.0 * Pp * (2 * pw.I) * pw.H
+        f2 = 2.0 * Pp * pw.H * pw.I
+        t13 = f13 / (pms["w13"] * 1e-3) / 1e12
+        out["prefill32k"] = {
+            "value": pw.T / (ps * 1e-3), "unit": "tokens/s", "ms_per_step": ps, "steps": args.prefill_steps,
+            "config": {"workload": "prefill32k", "tokens": pw.T, "routing": f"zipf s={pw.zipf_s}"},
+            "effective_tflops": (f13 + f2) / (ps * 1e-3) / 1e12,
+            "mfma_frac_fp8_peak": (f13 + f2) / (ps * 1e-3) / 1e12 / MFMA_PEAK_FP8_TFLOPS,
+            "roofline": {"bound": "mfma", "kernel": "W13 grouped GEMM + SwiGLU/requant", "achieved": t13,
+                         "peak": MFMA_PEAK_FP8_TFLOPS, "unit": "TFLOP/s", "frac": t13 / MFMA_PEAK_FP8_TFLOPS,
+                         "frac_of_fp4_peak": t13 / MFMA_PEAK_FP4_TFLOPS, "traffic": None,
+                         "algorithmic_flops_per_launch": f13, "avg_launch_ms": pms["w13"]},
+            "stage_ms": pms,
+        }
+        log(f"[bench] prefill32k: {ps:.3f} ms/step, stages {pms}")
+        del pre
+
+    # ---- oracle on the host cores (bounded sample)
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline("decode7", W, list(range(WORKLOADS["decode7"].T)))
+        log(f"[bench] cpu_baseline {out['cpu_baseline']}")
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

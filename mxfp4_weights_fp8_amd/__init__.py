@@ -164,14 +164,55 @@ def quant_act(x: torch.Tensor):
     return x_q, x_s
 
 
+_hip = None
+
+
+def _hip_rt() -> ctypes.CDLL:
+    global _hip
+    if _hip is None:
+        _hip = ctypes.CDLL("libamdhip64.so")
+        _hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        _hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        _hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+    return _hip
+
+
+class StageEvents:
+    """NUM_EVENTS raw HIP events for moe_ffn's stage boundaries (recorded by the
+    library on the stream it launches on)."""
+
+    def __init__(self):
+        h = _hip_rt()
+        self.handles = []
+        for _ in range(NUM_EVENTS):
+            e = ctypes.c_void_p()
+            if h.hipEventCreate(ctypes.byref(e)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.handles.append(e)
+        self.array = (ctypes.c_void_p * NUM_EVENTS)(*[e.value for e in self.handles])
+
+    def elapsed_ms(self, a: int, b: int) -> float:
+        out = ctypes.c_float()
+        rc = _hip_rt().hipEventElapsedTime(ctypes.byref(out), self.handles[a], self.handles[b])
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return float(out.value)
+
+    def __del__(self):
+        try:
+            for e in self.handles:
+                _hip_rt().hipEventDestroy(e)
+        except Exception:
+            pass
+
+
 def ffn(x: torch.Tensor, topk_weights: torch.Tensor, p: Plan, weights: dict, shared: Optional[dict] = None,
         debug: bool = False, ws: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None,
         events=None):
     """moe_ffn on the current stream. weights: dict w13, w13_s, w2, w2_s (uint8
     cuda, layouts as in the header); shared: optional dict w13s, w13s_s, w2s, w2s_s.
     Returns y (bf16 [T, H]); with debug=True returns (y, dict of x_q, x_s, h_q, h_s,
-    sh_q, sh_s). ``events``: optional list of NUM_EVENTS torch.cuda.Event recorded
-    at the stage boundaries."""
+    sh_q, sh_s). ``events``: optional StageEvents recorded at the stage boundaries."""
     d = p.dims
     T, H, I, E, K, Is = d.T, d.H, d.I, d.E, d.K, d.Is
     dev = x.device
@@ -209,8 +250,7 @@ def ffn(x: torch.Tensor, topk_weights: torch.Tensor, p: Plan, weights: dict, sha
             for k, v in dbg_t.items():
                 setattr(dbg, k, v.data_ptr())
         if events is not None:
-            ev_arr = (ctypes.c_void_p * NUM_EVENTS)(*[ctypes.c_void_p(e.cuda_event) if e is not None else None
-                                                      for e in events])
+            ev_arr = events.array
             dbg.events = ctypes.cast(ev_arr, ctypes.POINTER(ctypes.c_void_p))
     rc = lib().moe_ffn(ctypes.byref(d), _ptr(x), _ptr(topk_weights), _ptr(p.expert_offsets), _ptr(p.sorted_pairs),
                        _ptr(p.pair_rows), _ptr(p.ws), _ptr(weights["w13"]), _ptr(weights["w13_s"]),
