@@ -75,4 +75,22 @@ __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f +
 
 __device__ __forceinline__ v4i load16(const void* p) { return *reinterpret_cast<const v4i*>(p); }
 
+// Buffer loads: a wave-uniform resource (base, size in bytes, kept in SGPRs), a
+// 32-bit per-lane offset and a wave-uniform offset. Reads past `bytes` return 0.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kRsrcWord3 = 0x00020000;   // raw (untyped) buffer access on gfx9-family
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcWord3);
+}
+__device__ __forceinline__ v4i buf_load16(rsrc_t r, int voff, int soff) {
+  return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+__device__ __forceinline__ int buf_load4(rsrc_t r, int voff, int soff) {
+  return (int)__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+}
+__device__ __forceinline__ int buf_load1(rsrc_t r, int voff, int soff) {
+  return (int)__builtin_amdgcn_raw_buffer_load_b8(r, voff, soff, 0);
+}
+
 }  // namespace moe
