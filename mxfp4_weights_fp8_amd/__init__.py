@@ -181,13 +181,15 @@ class StageEvents:
     """NUM_EVENTS raw HIP events for moe_ffn's stage boundaries (recorded by the
     library on the stream it launches on)."""
 
-    def __init__(self):
+    def __init__(self, only=None):
+        """only: optional subset of stage indices to record (the others stay NULL)."""
         h = _hip_rt()
         self.handles = []
-        for _ in range(NUM_EVENTS):
+        for i in range(NUM_EVENTS):
             e = ctypes.c_void_p()
-            if h.hipEventCreate(ctypes.byref(e)) != 0:
-                raise RuntimeError("hipEventCreate failed")
+            if only is None or i in only:
+                if h.hipEventCreate(ctypes.byref(e)) != 0:
+                    raise RuntimeError("hipEventCreate failed")
             self.handles.append(e)
         self.array = (ctypes.c_void_p * NUM_EVENTS)(*[e.value for e in self.handles])
 
@@ -201,7 +203,8 @@ class StageEvents:
     def __del__(self):
         try:
             for e in self.handles:
-                _hip_rt().hipEventDestroy(e)
+                if e.value:
+                    _hip_rt().hipEventDestroy(e)
         except Exception:
             pass
 
