@@ -79,6 +79,14 @@ hipError_t launch_w2_small(const moe_dims& d, const int2* items, const int32_t* 
                            int item_rows, const int32_t* offsets, const int32_t* sorted_pairs,
                            const uint8_t* h_q, const uint8_t* h_s, const uint8_t* w2, const uint8_t* w2_s,
                            float* o, hipStream_t s);
+bool large_path_supported(const moe_dims& d);
+hipError_t launch_w13_large(const moe_dims& d, const int2* items, const int32_t* n_items, int64_t max_items,
+                            const int32_t* offsets, const int32_t* sorted_pairs, const uint8_t* x_q,
+                            const uint8_t* x_s, const uint8_t* w13, const uint8_t* w13_s, uint8_t* h_q,
+                            uint8_t* h_s, hipStream_t s);
+hipError_t launch_w2_large(const moe_dims& d, const int2* items, const int32_t* n_items, int64_t max_items,
+                           const int32_t* offsets, const int32_t* sorted_pairs, const uint8_t* h_q,
+                           const uint8_t* h_s, const uint8_t* w2, const uint8_t* w2_s, float* o, hipStream_t s);
 hipError_t launch_combine(const float* o, const float* topk_weights, const int32_t* pair_rows, const float* so,
                           uint16_t* y, int T, int H, int K, hipStream_t s);
 
