@@ -50,9 +50,10 @@ def h_code_mismatch(hq, hs, hq_ref, hs_ref, amax_ref, block: int = 128) -> dict:
       equal  -- same decoded value (+0 and -0 are equal);
       close  -- the values are neighbours:
                 * same scale and grid positions one apart; or
-                * same scale, both values below 2^-5 * scale (where the E4M3 grid
-                  has the fixed step 2^-9 * scale, finer than the rounding inside
-                  a hardware MX dot product) and at most 2^-6 * scale apart; or
+                * same scale, both values at most 2^-5 * scale in magnitude (the
+                  E4M3 grid is uniform with step 2^-9 * scale from 0 up to and
+                  including 2^-5 * scale, finer there than the rounding inside a
+                  hardware MX dot product) and at most 2^-6 * scale apart; or
                 * a scale that differs in a block whose oracle amax is within
                   2^-16 (relative) of a scale boundary 1.75 * 2^p, and values at
                   most one grid step of the coarser scale apart;
@@ -77,7 +78,7 @@ def h_code_mismatch(hq, hs, hq_ref, hs_ref, amax_ref, block: int = 128) -> dict:
     equal = va == vb
     same = (hs == hs_ref)[..., None]
     dist = np.abs(_signed_index(a) - _signed_index(b))
-    fixed_step = (np.abs(E4M3_VALUES[a]) < 2.0 ** -5) & (np.abs(E4M3_VALUES[b]) < 2.0 ** -5) & \
+    fixed_step = (np.abs(E4M3_VALUES[a]) <= 2.0 ** -5) & (np.abs(E4M3_VALUES[b]) <= 2.0 ** -5) & \
         (np.abs(va - vb) <= 2.0 ** -6 * scale_b)
 
     _, ex = np.frexp(amax)               # amax = 2m * 2^(ex-1)

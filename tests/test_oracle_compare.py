@@ -36,6 +36,13 @@ def test_fixed_step_region():
     assert m["bad"] == 0 and m["differ"] == 1
     g[0, 0] = 0x12                              # 2^-5 * 1.25: outside the fixed-step region
     assert h_code_mismatch(g, s, q2, s, a)["bad"] == 1
+    # the region's top end, 2^-5 (code 0x10), is still on the uniform 2^-9 grid:
+    # 0x0E = 1.75 * 2^-6 lies two steps below it
+    g[0, 0], q2[0, 0] = 0x8E, 0x90
+    m = h_code_mismatch(g, s, q2, s, a)
+    assert m["bad"] == 0 and m["differ"] == 1
+    g[0, 0], q2[0, 0] = 0x90, 0x92              # 2^-5 vs 1.25 * 2^-5: step 2^-8 above the region
+    assert h_code_mismatch(g, s, q2, s, a)["bad"] == 1
 
 
 def test_sign_of_zero_is_equal_and_scale_flip_away_from_boundary_is_bad():
