@@ -127,6 +127,8 @@ def main():
     ap.add_argument("--prefill-steps", type=int, default=5)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--only", choices=["decode7", "prefill32k"], default=None,
+                    help="run one workload only (for profiling); prints its own JSON object")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU; multi-GPU runs are not part of it "
@@ -139,6 +141,13 @@ def main():
     W = make_expert_weights(WORKLOADS["decode7"], dev)     # one 384-expert set, shared by both workloads
     torch.cuda.synchronize()
     log(f"[bench] weights generated in {time.time() - t:.1f}s")
+
+    if args.only == "prefill32k":
+        pre = Runner("prefill32k", dev, W)
+        ps, p13_ms, pms = pre.run(args.prefill_steps, args.warmup)
+        log(f"[bench] prefill32k: {ps:.3f} ms/step, w13 {p13_ms:.3f} ms, stages {pms}")
+        print(json.dumps({"workload": "prefill32k", "ms_per_step": ps, "w13_ms": p13_ms, "stage_ms": pms}))
+        return
 
     # ---- decode verify, 7 tokens (headline)
     dec = Runner("decode7", dev, W)
@@ -175,7 +184,7 @@ def main():
     }
 
     # ---- prefill chunk, 32K tokens
-    if not args.no_prefill:
+    if not args.no_prefill and args.only is None:
         pre = Runner("prefill32k", dev, W)
         ps, p13_ms, pms = pre.run(args.prefill_steps, 1)
         pw = pre.w
@@ -198,7 +207,7 @@ def main():
         del pre
 
     # ---- oracle on the host cores (bounded sample)
-    if not args.no_cpu:
+    if not args.no_cpu and args.only is None:
         out["cpu_baseline"] = cpu_baseline("decode7", W, list(range(WORKLOADS["decode7"].T)))
         log(f"[bench] cpu_baseline {out['cpu_baseline']}")
     print(json.dumps(out), flush=True)

@@ -17,13 +17,17 @@
 //        blog, section 4.3).
 //   W2:  256 output columns; the epilogue writes fp32 rows to token-major slots.
 //
-// Data movement: the codes of each 128-K step are copied HBM -> LDS with
-// direct-to-LDS buffer loads (buffer_load_dwordx4 ... lds): a wave's load of one
-// 16-row fragment lands in LDS in exactly the MFMA lane order (lane l's 16 bytes at
-// l*16), so the LDS reads of the MFMA operands are conflict-free and no VGPRs
-// stage the copy. Two LDS stages: the copy of step k+2 is issued as soon as step k
-// has been consumed. The E8M0 scales of four K steps are fetched together through
-// VGPRs one chunk ahead and stored to LDS.
+// Data movement: HBM/L2 -> LDS with direct-to-LDS buffer loads (buffer_load_dwordx4
+// ... lds; lane l's 16 bytes land at M0 + 16*l), issued from inline asm with explicit
+// vmcnt waits and barriers. Every copy instruction moves whole 128-byte lines: 8
+// weight rows x 128 B (two 128-K steps of E2M1 codes) or 8 routed rows x 128 B (one
+// step of E4M3 codes). The vector L1 handles a limited number of line requests per
+// cycle, and copying 16 rows x 64 B per instruction ran at a third of the rate of 8
+// rows x 128 B. Rows sit in LDS row-major with the 16-byte chunk index XORed by
+// (row & 7), so the MFMA fragment reads (16 rows, one chunk) hit distinct banks.
+// A stage holds two K steps (32 KB of weights + 32 KB of activations); two stages.
+// The weight E8M0 scales of eight K steps (32 B per row) come by dword copies of 8
+// rows each; the activation scales of the whole tile are read once.
 #include "device_common.h"
 #include "host_internal.h"
 
@@ -32,12 +36,12 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kTokTile = kLargeRows;      // 128 routed rows per tile
-constexpr int kAFrags = 16;               // 256 weight rows
-constexpr int kBFrags = kTokTile / 16;    // 8 fragments of 16 routed rows
-constexpr int kStageA = kAFrags * 1024;   // bytes of A codes per K step
-constexpr int kStageB = kBFrags * 2048;   // bytes of B codes per K step
-constexpr int kStages = 3;                // K steps of codes in flight in LDS
-constexpr int kCodeDma = 4 + 4;           // direct-to-LDS code loads per wave per K step
+constexpr int kARows = 256;               // weight rows per tile
+constexpr int kStageK = 2;                // 128-K steps per LDS stage
+constexpr int kStageA = kARows * 128;     // bytes of E2M1 codes per stage (128 B per row)
+constexpr int kStageB = kTokTile * 128;   // bytes of E4M3 codes per K step
+constexpr int kCodeDma = 16;              // direct-to-LDS code copies per wave per stage
+constexpr int kScaleSteps = 8;            // K steps per weight-scale chunk (32 B per row)
 constexpr int kMaxKS = 64;                // K steps whose activation scales fit the tile's LDS
 
 typedef int v4i_s __attribute__((ext_vector_type(4)));
@@ -91,15 +95,16 @@ struct LargeArgs {
   uint8_t* h_q;            // W13 out
   uint8_t* h_s;
   float* o;                // W2 out
+  uint32_t act_bytes;      // size of act
   int H, I, K;
 };
 
 template <bool W13>
 __global__ __launch_bounds__(kThreads, 1) void k_gemm_large(LargeArgs a) {
-  __shared__ __attribute__((aligned(1024))) uint8_t sA[kStages][kStageA];
-  __shared__ __attribute__((aligned(1024))) uint8_t sB[kStages][kStageB];
-  __shared__ __attribute__((aligned(16))) uint32_t sSa[2][4][kAFrags * 16];   // [chunk buf][step][row]
-  __shared__ __attribute__((aligned(16))) uint8_t sSb[kTokTile][kMaxKS];     // [row][step]
+  __shared__ __attribute__((aligned(1024))) uint8_t sA[2][kStageA];                 // [stage][row][128 B]
+  __shared__ __attribute__((aligned(1024))) uint8_t sB[2][kStageK][kStageB];        // [stage][step][row][128 B]
+  __shared__ __attribute__((aligned(16))) uint32_t sSa[2][kARows][kScaleSteps];     // [chunk buf][row][step]
+  __shared__ __attribute__((aligned(16))) uint8_t sSb[kTokTile][kMaxKS];            // [row][step]
   __shared__ int sTok[kTokTile];
   __shared__ float sRed[2][kTokTile];
 
@@ -117,7 +122,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_large(LargeArgs a) {
 
   const int Kdim = W13 ? a.H : a.I;                     // reduction length
   const int N = W13 ? 2 * a.I : a.H;                    // weight rows per expert
-  const int KS = Kdim / 128;
+  const int KS = Kdim / 128;                            // 128-K steps
+  const int NS = (KS + kStageK - 1) / kStageK;          // stages
   const int wrow = Kdim / 2, srow = Kdim / 32, arow = Kdim;
 
   // routed rows of the tile -> activation row index (padding repeats the first row)
@@ -149,35 +155,48 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_large(LargeArgs a) {
 
   const v4i_s rw = rsrc4(a.w + (int64_t)e * N * wrow, (uint32_t)(N * wrow));
   const v4i_s rws = rsrc4(a.w_s + (int64_t)e * N * srow, (uint32_t)(N * srow));
-  const v4i_s ra = rsrc4(a.act, 0xFFFFFFFFu);
+  const v4i_s ra = rsrc4(a.act, a.act_bytes);   // copies past the tensor read zeros
 
-  // weight row of LDS A fragment f (0..15)
-  auto a_row = [&](int f) -> int {
-    if (W13) return (f < 8 ? 0 : a.I) + nb * 128 + (f & 7) * 16;
-    return nb * 256 + f * 16;
+  // expert weight row of LDS row r (0..255): fragments of 16 rows
+  auto w_row = [&](int r) -> int {
+    const int f = r >> 4;
+    if (W13) return (f < 8 ? 0 : a.I) + nb * 128 + (f & 7) * 16 + (r & 15);
+    return nb * 256 + r;
   };
-  // this wave copies A fragments wave + 4i (i < 4) and B fragments wave + 4i (i < 2)
-  int dA[4], dB[2];
+  // Copy plan (per wave, per stage): 8 weight instructions, LDS rows 64*wave + 8i ..
+  // +7, lane l -> row +l/8, physical chunk l%8 holding logical chunk (l%8)^(row&7);
+  // 8 activation instructions, step wave/2 of the stage, routed rows
+  // 64*(wave%2) + 8i .. +7, same chunk mapping. The 64 weight rows a wave copies
+  // are consecutive expert rows (16-row fragments of the gate or the up half, or
+  // of the W2 column block), so one lane offset plus a wave-uniform row step
+  // addresses them; routed rows are arbitrary and take one lane offset each.
+  const int r_lane = 64 * wave + (lane >> 3);           // LDS row of instruction 0
+  const int sw = ((lane & 7) ^ (lane >> 3)) << 4;       // swizzled chunk (row & 7 == lane / 8)
+  const int dA = w_row(r_lane) * wrow + sw;
+  const int dS = w_row(r_lane) * srow + (lane & 7) * 4;
+  int dB[8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) dA[i] = (a_row(wave + 4 * i) + c) * wrow + q * 16;
-#pragma unroll
-  for (int i = 0; i < 2; ++i) dB[i] = sTok[(wave + 4 * i) * 16 + c] * arow + q * 16;
-  // A scales: lane l of this wave fetches LDS row wave*64 + l = fragment (wave*4 + l/16), row l%16
-  const int dS = (a_row(wave * 4 + (lane >> 4)) + c) * srow;
+  for (int i = 0; i < 8; ++i) dB[i] = sTok[64 * (wave & 1) + 8 * i + (lane >> 3)] * arow + sw;
+  const int b_step = wave >> 1;                         // step of the stage this wave copies
 
-  auto issue_codes = [&](int stage, int ks) {
+  auto issue_stage = [&](int buf, int stg) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dma16(rw, lds_addr(&sA[stage][(wave + 4 * i) * 1024]), dA[i], ks * 64);
+    for (int i = 0; i < 8; ++i)
+      dma16(rw, lds_addr(&sA[buf][(64 * wave + 8 * i) * 128]), dA, stg * 128 + 8 * i * wrow);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      dma16(ra, lds_addr(&sB[stage][(wave + 4 * i) * 2048]), dB[i], ks * 128);
-      dma16(ra, lds_addr(&sB[stage][(wave + 4 * i) * 2048 + 1024]), dB[i], ks * 128 + 64);
-    }
+    for (int i = 0; i < 8; ++i)
+      dma16(ra, lds_addr(&sB[buf][b_step][(64 * (wave & 1) + 8 * i) * 128]), dB[i],
+            (stg * kStageK + b_step) * 128);
   };
-  auto issue_scales = [&](int chunk) {   // E8M0 dwords of steps 4*chunk .. 4*chunk+3
-#pragma unroll
-    for (int d = 0; d < 4; ++d)
-      dma4(rws, lds_addr(&sSa[chunk & 1][d][wave * 64]), dS, min(4 * chunk + d, KS - 1) * 4);
+  // Weight scales: chunk c (K steps 8c .. 8c+7, 32 B per row) goes to buffer c % 2.
+  // A wave copies its 64 rows with 8 instructions of 8 rows; stage k issues two
+  // of them (m = k % 4: instructions 2m, 2m+1) for chunk k/4 + 1 while that chunk
+  // holds K steps, so the chunk is complete when step 8(k/4 + 1) is read at the
+  // end of stage 4(k/4) + 3. Steps past the last one in a chunk read zeros or
+  // unused bytes that no MFMA uses.
+  auto issue_scales = [&](int chunk, int first, int count) {
+    for (int i = first; i < first + count; ++i)
+      dma4(rws, lds_addr(&sSa[chunk & 1][64 * wave + 8 * i][0]), dS, chunk * kScaleSteps * 4 + 8 * i * srow);
   };
 
   v4f acc[8][4];
@@ -186,61 +205,104 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_large(LargeArgs a) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  // LDS A fragments this wave multiplies
-  int fA[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) fA[i] = W13 ? (i < 4 ? 4 * wn + i : 8 + 4 * wn + (i - 4)) : 8 * wn + i;
+  // LDS byte offsets of the operand reads. Fragment rows are multiples of 16, so a
+  // row's swizzle (row & 7) is c & 7 and the two 16-byte chunks a lane reads for
+  // a K step (E2M1: chunk q of step 0 / 4+q of step 1 of the stage; E4M3: chunks
+  // q and 4+q of its step) sit at two fixed per-lane offsets; stage, step and
+  // fragment add compile-time constants.
+  const int off0 = c * 128 + ((q ^ (c & 7)) << 4);
+  const int off1 = c * 128 + (((4 + q) ^ (c & 7)) << 4);
+  // this wave's 8 weight fragments: W13 gate 4wn..4wn+3 and up 8+4wn..; W2 8wn..8wn+7
+  const int a_wave = W13 ? wn * 4 * 2048 : wn * 8 * 2048;
+  auto a_frag = [](int i) { return W13 ? (i < 4 ? i : 8 + (i - 4)) * 2048 : i * 2048; };
+  const uint8_t* pA0 = &sA[0][0] + a_wave + off0;
+  const uint8_t* pA1 = &sA[0][0] + a_wave + off1;
+  const uint8_t* pB0 = &sB[0][0][0] + wm * 4 * 2048 + off0;
+  const uint8_t* pB1 = &sB[0][0][0] + wm * 4 * 2048 + off1;
+  const uint8_t* pSa = reinterpret_cast<const uint8_t*>(&sSa[0][0][0]) + a_wave / 4 + c * 32;
+  const uint8_t* pSb = &sSb[0][0] + wm * 4 * 16 * kMaxKS + c * kMaxKS;
 
-  auto compute = [&](int stage, int ks) {
-    const int cb = (ks >> 2) & 1, d = ks & 3;
-    v8i bop[4];
-    int sbv[4];
+  // Operands of one K step in registers: this wave's 4 routed-row fragments (E4M3)
+  // and 8 weight fragments (E2M1) with their E8M0 scales.
+  struct Ops {
+    v8i b[4];
+    v4i w[8];
+    int sb[4];
+    int sa[8];
+  };
+  auto load_ops = [&](Ops& o, const int buf, const int h, int ks) {   // h: step within the stage
+    const uint8_t* sa = pSa + ((ks / kScaleSteps) & 1) * (kARows * kScaleSteps * 4) + (ks % kScaleSteps) * 4;
+    const uint8_t* sb = pSb + ks;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int fb = 4 * wm + j;
-      const v4i lo = *reinterpret_cast<const v4i*>(&sB[stage][fb * 2048 + lane * 16]);
-      const v4i hi = *reinterpret_cast<const v4i*>(&sB[stage][fb * 2048 + 1024 + lane * 16]);
-      bop[j][0] = lo[0]; bop[j][1] = lo[1]; bop[j][2] = lo[2]; bop[j][3] = lo[3];
-      bop[j][4] = hi[0]; bop[j][5] = hi[1]; bop[j][6] = hi[2]; bop[j][7] = hi[3];
-      sbv[j] = sSb[fb * 16 + c][ks];
+      const int ob = buf * kStageK * kStageB + h * kStageB + j * 2048;
+      const v4i lo = *reinterpret_cast<const v4i*>(pB0 + ob);
+      const v4i hi = *reinterpret_cast<const v4i*>(pB1 + ob);
+      o.b[j][0] = lo[0]; o.b[j][1] = lo[1]; o.b[j][2] = lo[2]; o.b[j][3] = lo[3];
+      o.b[j][4] = hi[0]; o.b[j][5] = hi[1]; o.b[j][6] = hi[2]; o.b[j][7] = hi[3];
+      o.sb[j] = sb[j * 16 * kMaxKS];
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const v4i w4 = *reinterpret_cast<const v4i*>(&sA[stage][fA[i] * 1024 + lane * 16]);
+      const int oa = buf * kStageA + a_frag(i);
+      o.w[i] = *reinterpret_cast<const v4i*>((h ? pA1 : pA0) + oa);
+      o.sa[i] = *reinterpret_cast<const int*>(sa + a_frag(i) / 4);   // lane group q uses byte q (shifted at use)
+    }
+  };
+  auto mma = [&](const Ops& o) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
       v8i aop;
-      aop[0] = w4[0]; aop[1] = w4[1]; aop[2] = w4[2]; aop[3] = w4[3];
+      aop[0] = o.w[i][0]; aop[1] = o.w[i][1]; aop[2] = o.w[i][2]; aop[3] = o.w[i][3];
       aop[4] = 0; aop[5] = 0; aop[6] = 0; aop[7] = 0;
-      const int sav = (int)(sSa[cb][d][fA[i] * 16 + c] >> (8 * q));
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        acc[i][j] = mfma_scale_16x16x128<kFmtE2M1, kFmtE4M3>(aop, bop[j], acc[i][j], sav, sbv[j]);
+        acc[i][j] = mfma_scale_16x16x128<kFmtE2M1, kFmtE4M3>(aop, o.b[j], acc[i][j], o.sa[i] >> (8 * q), o.sb[j]);
     }
   };
 
-  // prologue: scales of chunk 0, codes of steps 0 .. kStages-1
-  issue_scales(0);
-#pragma unroll
-  for (int s = 0; s < kStages; ++s)
-    if (s < KS) issue_codes(s, s);
-
-  // Step ks waits for its codes; the only later loads are the codes of the (up to
-  // two) following steps and possibly a scale chunk, which makes the wait stricter.
-  for (int ks0 = 0; ks0 < KS; ks0 += kStages) {
-#pragma unroll
-    for (int st = 0; st < kStages; ++st) {
-      const int ks = ks0 + st;
-      if (ks < KS) {
-        if (ks + 2 < KS) wait_vmcnt<2 * kCodeDma>();
-        else if (ks + 1 < KS) wait_vmcnt<kCodeDma>();
-        else wait_vmcnt<0>();
-        __syncthreads();
-        compute(st, ks);
-        __syncthreads();
-        if ((ks & 3) == 0) issue_scales((ks >> 2) + 1);
-        if (ks + kStages < KS) issue_codes(st, ks + kStages);
-      }
-    }
+  // Prologue: weight scales of chunk 0, codes of stages 0 and 1, operands of step 0.
+  issue_scales(0, 0, 8);
+  issue_stage(0, 0);
+  if (NS > 1) {
+    issue_stage(1, 1);
+    wait_vmcnt<kCodeDma>();
+  } else {
+    wait_vmcnt<0>();
   }
+  __syncthreads();
+  Ops opsA, opsB;
+  load_ops(opsA, 0, 0, 0);
+
+  // Stage k (both K steps valid, buffer k % 2). On entry opsA holds step 2k. Read
+  // step 2k+1 into opsB and multiply step 2k; barrier: every wave has read stage
+  // k, so its buffer takes the copy of stage k+2 (and two scale copies); wait for
+  // stage k+1's copies (the 16 newest loads are stage k+2's); barrier; read step
+  // 2k+2 into opsA (after the last full stage with an even K-step count this reads
+  // a stale buffer, never used); multiply step 2k+1. Only scalar code (copy issue,
+  // waits) branches, so the MFMA operands and accumulators keep one register
+  // assignment; scheduling barriers keep the MFMAs between the LDS barriers.
+  const int NF = KS / kStageK;   // stages with both K steps
+  for (int k = 0; k < NF; ++k) {
+    const int buf = k & 1;
+    load_ops(opsB, buf, 1, 2 * k + 1);
+    mma(opsA);
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+    if ((k / 4 + 1) * kScaleSteps < KS) issue_scales(k / 4 + 1, 2 * (k % 4), 2);
+    if (k + 2 < NS) {
+      issue_stage(buf, k + 2);
+      wait_vmcnt<kCodeDma>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+    load_ops(opsA, buf ^ 1, 0, min(2 * k + 2, KS - 1));
+    mma(opsB);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (KS & 1) mma(opsA);         // the last K step, alone in its stage
   wait_vmcnt<0>();
 
   if (W13) {
@@ -314,7 +376,9 @@ hipError_t launch_w13_large(const moe_dims& d, const int2* items, const int32_t*
                             const uint8_t* x_s, const uint8_t* w13, const uint8_t* w13_s, uint8_t* h_q,
                             uint8_t* h_s, hipStream_t s) {
   if (max_items <= 0) return hipSuccess;
-  LargeArgs a{items, n_items, offsets, sorted_pairs, x_q, x_s, w13, w13_s, h_q, h_s, nullptr, d.H, d.I, d.K};
+  LargeArgs a{items, n_items, offsets, sorted_pairs, x_q,     x_s,
+              w13,   w13_s,   h_q,     h_s,          nullptr, (uint32_t)((int64_t)d.T * d.H),
+              d.H,   d.I,     d.K};
   hipLaunchKernelGGL(k_gemm_large<true>, dim3(d.I / 128, (unsigned)max_items), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
@@ -323,7 +387,8 @@ hipError_t launch_w2_large(const moe_dims& d, const int2* items, const int32_t* 
                            const int32_t* offsets, const int32_t* sorted_pairs, const uint8_t* h_q,
                            const uint8_t* h_s, const uint8_t* w2, const uint8_t* w2_s, float* o, hipStream_t s) {
   if (max_items <= 0) return hipSuccess;
-  LargeArgs a{items, n_items, offsets, sorted_pairs, h_q, h_s, w2, w2_s, nullptr, nullptr, o, d.H, d.I, d.K};
+  LargeArgs a{items, n_items, offsets, sorted_pairs, h_q, h_s, w2, w2_s, nullptr, nullptr, o,
+              (uint32_t)((int64_t)d.T * d.K * d.I), d.H, d.I, d.K};
   hipLaunchKernelGGL(k_gemm_large<false>, dim3(d.H / 256, (unsigned)max_items), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }

@@ -106,17 +106,23 @@ def test_ffn_tiny(dev, small_max):
     check_ffn(inp, p, y, dbg, label=f"tiny small_max={small_max}")
 
 
-@pytest.mark.parametrize("T,H,I,E,K,seed", [
-    (1, 128, 128, 1, 1, 41),        # degenerate: one token, one expert
-    (33, 384, 384, 5, 3, 42),       # ragged: odd T, H and I not multiples of 256
-    (130, 640, 256, 3, 2, 43),      # experts with > 128 rows (several large tiles + a tail)
-    (17, 256, 1152, 40, 8, 44),     # many experts, I = 9 * 128
+@pytest.mark.parametrize("T,H,I,E,K,seed,small_max", [
+    (1, 128, 128, 1, 1, 41, 0),        # degenerate: one token, one expert
+    (33, 384, 384, 5, 3, 42, 0),       # ragged: odd T, H and I not multiples of 256
+    (130, 640, 256, 3, 2, 43, 0),      # experts with > 128 rows (several large tiles + a tail)
+    (17, 256, 1152, 40, 8, 44, 0),     # many experts, I = 9 * 128
+    # small_max 1 sends experts with 2+ rows to the large-M path: odd K-step
+    # counts (W2 K = 1152 and 384: 9 and 3 steps), a count that ends inside a
+    # weight-scale chunk (W13 K = 1280: 10 steps), 17 steps
+    (130, 256, 1152, 3, 2, 45, 1),
+    (200, 1280, 384, 4, 2, 46, 1),
+    (150, 256, 2176, 2, 1, 47, 1),
 ])
-def test_ffn_shapes(dev, T, H, I, E, K, seed):
+def test_ffn_shapes(dev, T, H, I, E, K, seed, small_max):
     wl = scaled("tiny", T=T, H=H, I=I, E=E, K=K, seed=seed, weight_seed=seed, name=f"s{seed}")
     inp = make_inputs(wl).to(dev)
-    p, (y, dbg) = run_path(inp)
-    check_ffn(inp, p, y, dbg, label=f"shape {T}x{H} I{I} E{E} K{K}")
+    p, (y, dbg) = run_path(inp, small_max=small_max)
+    check_ffn(inp, p, y, dbg, label=f"shape {T}x{H} I{I} E{E} K{K} small_max={small_max}")
 
 
 def test_ffn_invalid_ids(dev):
