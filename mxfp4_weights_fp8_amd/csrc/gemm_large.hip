@@ -153,9 +153,18 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_large(LargeArgs a) {
     for (int i = 0; i < kMaxKS / 8; ++i) *reinterpret_cast<uint32_t*>(&sSb[r][s0 + 4 * i]) = v[i];
   }
 
+  // Buffer resources of this expert's weights and scales and of the activations.
+  // The hardware range check applies to the lane offset, so every offset that can
+  // run past a row end (the last stage of an odd K-step count, scale chunks past
+  // the last step) is in the lane offset, and copies that would only fetch unused
+  // bytes take a resource of size 0: they write zeros to LDS and touch no memory.
   const v4i_s rw = rsrc4(a.w + (int64_t)e * N * wrow, (uint32_t)(N * wrow));
   const v4i_s rws = rsrc4(a.w_s + (int64_t)e * N * srow, (uint32_t)(N * srow));
-  const v4i_s ra = rsrc4(a.act, a.act_bytes);   // copies past the tensor read zeros
+  const v4i_s ra = rsrc4(a.act, a.act_bytes);
+  auto sized = [](v4i_s r, bool keep) {
+    r[2] = keep ? r[2] : 0;
+    return r;
+  };
 
   // expert weight row of LDS row r (0..255): fragments of 16 rows
   auto w_row = [&](int r) -> int {
@@ -168,8 +177,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_large(LargeArgs a) {
   // 8 activation instructions, step wave/2 of the stage, routed rows
   // 64*(wave%2) + 8i .. +7, same chunk mapping. The 64 weight rows a wave copies
   // are consecutive expert rows (16-row fragments of the gate or the up half, or
-  // of the W2 column block), so one lane offset plus a wave-uniform row step
-  // addresses them; routed rows are arbitrary and take one lane offset each.
+  // of the W2 column block), so instruction i adds 8i rows to one lane offset;
+  // routed rows are arbitrary and take one lane offset each.
   const int r_lane = 64 * wave + (lane >> 3);           // LDS row of instruction 0
   const int sw = ((lane & 7) ^ (lane >> 3)) << 4;       // swizzled chunk (row & 7 == lane / 8)
   const int dA = w_row(r_lane) * wrow + sw;
@@ -179,24 +188,30 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_large(LargeArgs a) {
   for (int i = 0; i < 8; ++i) dB[i] = sTok[64 * (wave & 1) + 8 * i + (lane >> 3)] * arow + sw;
   const int b_step = wave >> 1;                         // step of the stage this wave copies
 
-  auto issue_stage = [&](int buf, int stg) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      dma16(rw, lds_addr(&sA[buf][(64 * wave + 8 * i) * 128]), dA, stg * 128 + 8 * i * wrow);
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      dma16(ra, lds_addr(&sB[buf][b_step][(64 * (wave & 1) + 8 * i) * 128]), dB[i],
-            (stg * kStageK + b_step) * 128);
+  // Copy instructions i (weight rows 64*wave + 8i .., routed rows 64*(wave%2) + 8i ..)
+  // of stage stg (K steps 2stg, 2stg+1) into LDS buffer buf; valid == false (a
+  // stage past the last) writes zeros.
+  auto issue_part = [&](int buf, int stg, bool valid, int i) {
+    dma16(sized(rw, valid), lds_addr(&sA[buf][(64 * wave + 8 * i) * 128]), dA + 8 * i * wrow + stg * 128, 0);
+    dma16(sized(ra, valid), lds_addr(&sB[buf][b_step][(64 * (wave & 1) + 8 * i) * 128]),
+          dB[i] + (stg * kStageK + b_step) * 128, 0);
   };
-  // Weight scales: chunk c (K steps 8c .. 8c+7, 32 B per row) goes to buffer c % 2.
-  // A wave copies its 64 rows with 8 instructions of 8 rows; stage k issues two
-  // of them (m = k % 4: instructions 2m, 2m+1) for chunk k/4 + 1 while that chunk
-  // holds K steps, so the chunk is complete when step 8(k/4 + 1) is read at the
-  // end of stage 4(k/4) + 3. Steps past the last one in a chunk read zeros or
-  // unused bytes that no MFMA uses.
-  auto issue_scales = [&](int chunk, int first, int count) {
-    for (int i = first; i < first + count; ++i)
-      dma4(rws, lds_addr(&sSa[chunk & 1][64 * wave + 8 * i][0]), dS, chunk * kScaleSteps * 4 + 8 * i * srow);
+  auto issue_stage = [&](int buf, int stg, bool valid) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) issue_part(buf, stg, valid, i);
+  };
+  // Weight scales: chunk c (K steps 8c .. 8c+7, 32 B per row) goes to buffer c % 2,
+  // in four parts of two 8-row copy instructions per wave. Part m of chunk c is
+  // issued by stage 4c - 5 + m: the part that reuses chunk c-2's buffer follows the
+  // last read of chunk c-2 (stage 4c-5's first step), and the last part is waited
+  // for before step 8c is read (at stage 4c-1). Chunks past the last step write zeros.
+  auto issue_scales = [&](int chunk, int part) {
+    const v4i_s r_s = sized(rws, chunk * kScaleSteps < KS);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int i = 2 * part + h;
+      dma4(r_s, lds_addr(&sSa[chunk & 1][64 * wave + 8 * i][0]), dS + chunk * kScaleSteps * 4 + 8 * i * srow, 0);
+    }
   };
 
   v4f acc[8][4];
@@ -219,90 +234,97 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_large(LargeArgs a) {
   const uint8_t* pA1 = &sA[0][0] + a_wave + off1;
   const uint8_t* pB0 = &sB[0][0][0] + wm * 4 * 2048 + off0;
   const uint8_t* pB1 = &sB[0][0][0] + wm * 4 * 2048 + off1;
-  const uint8_t* pSa = reinterpret_cast<const uint8_t*>(&sSa[0][0][0]) + a_wave / 4 + c * 32;
+  // weight scales: lane group q reads its K block's byte of the (row, step) dword
+  const uint8_t* pSa = reinterpret_cast<const uint8_t*>(&sSa[0][0][0]) + a_wave / 4 + c * 32 + q;
   const uint8_t* pSb = &sSb[0][0] + wm * 4 * 16 * kMaxKS + c * kMaxKS;
 
   // Operands of one K step in registers: this wave's 4 routed-row fragments (E4M3)
-  // and 8 weight fragments (E2M1) with their E8M0 scales.
+  // and 8 weight fragments (E2M1) with their E8M0 scales. They are read in 8
+  // parts (p < 4: routed-row fragment p; p >= 4: weight fragments 2(p-4), 2(p-4)+1)
+  // so that LDS reads interleave with the MFMAs of the other register set.
   struct Ops {
     v8i b[4];
     v4i w[8];
     int sb[4];
     int sa[8];
   };
-  auto load_ops = [&](Ops& o, const int buf, const int h, int ks) {   // h: step within the stage
-    const uint8_t* sa = pSa + ((ks / kScaleSteps) & 1) * (kARows * kScaleSteps * 4) + (ks % kScaleSteps) * 4;
-    const uint8_t* sb = pSb + ks;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int ob = buf * kStageK * kStageB + h * kStageB + j * 2048;
+  auto load_part = [&](Ops& o, const int buf, const int h, int ks, const int p) {   // h: step within the stage
+    if (p < 4) {
+      const int ob = buf * kStageK * kStageB + h * kStageB + p * 2048;
       const v4i lo = *reinterpret_cast<const v4i*>(pB0 + ob);
       const v4i hi = *reinterpret_cast<const v4i*>(pB1 + ob);
-      o.b[j][0] = lo[0]; o.b[j][1] = lo[1]; o.b[j][2] = lo[2]; o.b[j][3] = lo[3];
-      o.b[j][4] = hi[0]; o.b[j][5] = hi[1]; o.b[j][6] = hi[2]; o.b[j][7] = hi[3];
-      o.sb[j] = sb[j * 16 * kMaxKS];
-    }
+      o.b[p][0] = lo[0]; o.b[p][1] = lo[1]; o.b[p][2] = lo[2]; o.b[p][3] = lo[3];
+      o.b[p][4] = hi[0]; o.b[p][5] = hi[1]; o.b[p][6] = hi[2]; o.b[p][7] = hi[3];
+      o.sb[p] = pSb[ks + p * 16 * kMaxKS];
+    } else {
+      const uint8_t* sa = pSa + ((ks / kScaleSteps) & 1) * (kARows * kScaleSteps * 4) + (ks % kScaleSteps) * 4;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int oa = buf * kStageA + a_frag(i);
-      o.w[i] = *reinterpret_cast<const v4i*>((h ? pA1 : pA0) + oa);
-      o.sa[i] = *reinterpret_cast<const int*>(sa + a_frag(i) / 4);   // lane group q uses byte q (shifted at use)
+      for (int i = 2 * (p - 4); i < 2 * (p - 4) + 2; ++i) {
+        o.w[i] = *reinterpret_cast<const v4i*>((h ? pA1 : pA0) + buf * kStageA + a_frag(i));
+        o.sa[i] = sa[a_frag(i) / 4];
+      }
     }
   };
-  auto mma = [&](const Ops& o) {
+  // the 4 MFMAs of weight fragment i
+  auto mma_row = [&](const Ops& o, const int i) {
+    v8i aop;
+    aop[0] = o.w[i][0]; aop[1] = o.w[i][1]; aop[2] = o.w[i][2]; aop[3] = o.w[i][3];
+    aop[4] = 0; aop[5] = 0; aop[6] = 0; aop[7] = 0;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      v8i aop;
-      aop[0] = o.w[i][0]; aop[1] = o.w[i][1]; aop[2] = o.w[i][2]; aop[3] = o.w[i][3];
-      aop[4] = 0; aop[5] = 0; aop[6] = 0; aop[7] = 0;
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[i][j] = mfma_scale_16x16x128<kFmtE2M1, kFmtE4M3>(aop, o.b[j], acc[i][j], o.sa[i] >> (8 * q), o.sb[j]);
-    }
+    for (int j = 0; j < 4; ++j)
+      acc[i][j] = mfma_scale_16x16x128<kFmtE2M1, kFmtE4M3>(aop, o.b[j], acc[i][j], o.sa[i], o.sb[j]);
   };
 
-  // Prologue: weight scales of chunk 0, codes of stages 0 and 1, operands of step 0.
-  issue_scales(0, 0, 8);
-  issue_stage(0, 0);
-  if (NS > 1) {
-    issue_stage(1, 1);
-    wait_vmcnt<kCodeDma>();
-  } else {
-    wait_vmcnt<0>();
-  }
+  // Prologue: weight scales of chunk 0 and part 0 of chunk 1, codes of stages 0
+  // and 1, operands of step 0.
+#pragma unroll
+  for (int m = 0; m < 4; ++m) issue_scales(0, m);
+  issue_scales(1, 0);
+  issue_stage(0, 0, true);
+  issue_stage(1, 1, NS > 1);
+  wait_vmcnt<kCodeDma>();
   __syncthreads();
   Ops opsA, opsB;
-  load_ops(opsA, 0, 0, 0);
+#pragma unroll
+  for (int p = 0; p < 8; ++p) load_part(opsA, 0, 0, 0, p);
 
-  // Stage k (both K steps valid, buffer k % 2). On entry opsA holds step 2k. Read
-  // step 2k+1 into opsB and multiply step 2k; barrier: every wave has read stage
-  // k, so its buffer takes the copy of stage k+2 (and two scale copies); wait for
-  // stage k+1's copies (the 16 newest loads are stage k+2's); barrier; read step
-  // 2k+2 into opsA (after the last full stage with an even K-step count this reads
-  // a stale buffer, never used); multiply step 2k+1. Only scalar code (copy issue,
-  // waits) branches, so the MFMA operands and accumulators keep one register
-  // assignment; scheduling barriers keep the MFMAs between the LDS barriers.
+  // Stage k (both K steps valid, buffer k % 2); on entry opsA holds step 2k.
+  //   Multiply step 2k while reading step 2k+1 into opsB.
+  //   Wait for this wave's copies of stage k+1 (issued one stage earlier) and
+  //   barrier: stage k+1 is in LDS, and every wave has read stage k.
+  //   Multiply step 2k+1 while reading step 2k+2 into opsA (after the last full
+  //   stage with an even K-step count this reads a stale buffer, never used) and
+  //   issuing the copies of stage k+2 into stage k's buffer and one scale part.
+  // The body has no branches. Each half is 8 groups of 4 MFMAs, one operand part
+  // and (second half) two copy instructions, separated by scheduling barriers, so
+  // LDS reads and copies issue between MFMAs instead of in bursts that would stall
+  // the wave with the MFMA pipe idle.
   const int NF = KS / kStageK;   // stages with both K steps
   for (int k = 0; k < NF; ++k) {
     const int buf = k & 1;
-    load_ops(opsB, buf, 1, 2 * k + 1);
-    mma(opsA);
-    __builtin_amdgcn_sched_barrier(0);
-    __syncthreads();
-    if ((k / 4 + 1) * kScaleSteps < KS) issue_scales(k / 4 + 1, 2 * (k % 4), 2);
-    if (k + 2 < NS) {
-      issue_stage(buf, k + 2);
-      wait_vmcnt<kCodeDma>();
-    } else {
-      wait_vmcnt<0>();
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      mma_row(opsA, p);
+      load_part(opsB, buf, 1, 2 * k + 1, p);
+      __builtin_amdgcn_sched_barrier(0);
     }
+    wait_vmcnt<0>();
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
-    load_ops(opsA, buf ^ 1, 0, min(2 * k + 2, KS - 1));
-    mma(opsB);
-    __builtin_amdgcn_sched_barrier(0);
+    const bool more = k + 2 < NS;
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      mma_row(opsB, p);
+      load_part(opsA, buf ^ 1, 0, min(2 * k + 2, KS - 1), p);
+      if (p == 0) issue_scales((k + 1) / 4 + 1, (k + 1) % 4);
+      issue_part(buf, k + 2, more, p);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
-  if (KS & 1) mma(opsA);         // the last K step, alone in its stage
+  if (KS & 1) {                  // the last K step, alone in its stage
+#pragma unroll
+    for (int p = 0; p < 8; ++p) mma_row(opsA, p);
+  }
   wait_vmcnt<0>();
 
   if (W13) {
