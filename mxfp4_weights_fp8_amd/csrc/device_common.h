@@ -71,7 +71,14 @@ __device__ __forceinline__ uint16_t bf16_rne(float f) {
 
 __device__ __forceinline__ float bf16_to_float(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
-__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
+// SiLU(g) * u = g * u / (1 + e^-g), with the hardware exp2 and reciprocal (about
+// 1 ulp each): the result is requantized to E4M3 (3 mantissa bits), so fp32
+// rounding of this order only moves values that sit on a rounding boundary. For
+// g << 0, e^-g is +inf and the reciprocal 0, giving a signed zero.
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  const float e = __builtin_amdgcn_exp2f(g * -1.44269504088896341f);
+  return g * __builtin_amdgcn_rcpf(1.0f + e) * u;
+}
 
 __device__ __forceinline__ v4i load16(const void* p) { return *reinterpret_cast<const v4i*>(p); }
 

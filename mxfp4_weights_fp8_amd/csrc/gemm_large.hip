@@ -24,7 +24,9 @@
 // step of E4M3 codes). The vector L1 handles a limited number of line requests per
 // cycle, and copying 16 rows x 64 B per instruction ran at a third of the rate of 8
 // rows x 128 B. Rows sit in LDS row-major with the 16-byte chunk index XORed by
-// (row & 7), so the MFMA fragment reads (16 rows, one chunk) hit distinct banks.
+// (row / 2) % 8: an MFMA fragment read (16 rows, one chunk per lane group) then
+// covers all 64 banks once per 16 lanes (even rows in one 128-byte half of a bank
+// row, odd rows in the other, each with 8 distinct chunks).
 // A stage holds two K steps (32 KB of weights + 32 KB of activations); two stages.
 // The weight E8M0 scales of eight K steps (32 B per row) come by dword copies of 8
 // rows each; the activation scales of the whole tile are read once.
@@ -173,26 +175,29 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_large(LargeArgs a) {
     return nb * 256 + r;
   };
   // Copy plan (per wave, per stage): 8 weight instructions, LDS rows 64*wave + 8i ..
-  // +7, lane l -> row +l/8, physical chunk l%8 holding logical chunk (l%8)^(row&7);
+  // +7, lane l -> row +l/8, physical chunk l%8 holding logical chunk (l%8) ^ s(row),
+  // s(row) = (row / 2) % 8 = 4 (i % 2) + l / 16;
   // 8 activation instructions, step wave/2 of the stage, routed rows
   // 64*(wave%2) + 8i .. +7, same chunk mapping. The 64 weight rows a wave copies
   // are consecutive expert rows (16-row fragments of the gate or the up half, or
   // of the W2 column block), so instruction i adds 8i rows to one lane offset;
   // routed rows are arbitrary and take one lane offset each.
   const int r_lane = 64 * wave + (lane >> 3);           // LDS row of instruction 0
-  const int sw = ((lane & 7) ^ (lane >> 3)) << 4;       // swizzled chunk (row & 7 == lane / 8)
-  const int dA = w_row(r_lane) * wrow + sw;
+  const int sw0 = ((lane & 7) ^ (lane >> 4)) << 4;      // swizzled chunk, even i
+  const int sw1 = ((lane & 7) ^ (4 | (lane >> 4))) << 4; // odd i
+  const int dA = w_row(r_lane) * wrow;
   const int dS = w_row(r_lane) * srow + (lane & 7) * 4;
   int dB[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) dB[i] = sTok[64 * (wave & 1) + 8 * i + (lane >> 3)] * arow + sw;
+  for (int i = 0; i < 8; ++i) dB[i] = sTok[64 * (wave & 1) + 8 * i + (lane >> 3)] * arow + ((i & 1) ? sw1 : sw0);
   const int b_step = wave >> 1;                         // step of the stage this wave copies
 
   // Copy instructions i (weight rows 64*wave + 8i .., routed rows 64*(wave%2) + 8i ..)
   // of stage stg (K steps 2stg, 2stg+1) into LDS buffer buf; valid == false (a
   // stage past the last) writes zeros.
   auto issue_part = [&](int buf, int stg, bool valid, int i) {
-    dma16(sized(rw, valid), lds_addr(&sA[buf][(64 * wave + 8 * i) * 128]), dA + 8 * i * wrow + stg * 128, 0);
+    dma16(sized(rw, valid), lds_addr(&sA[buf][(64 * wave + 8 * i) * 128]),
+          dA + ((i & 1) ? sw1 : sw0) + 8 * i * wrow + stg * 128, 0);
     dma16(sized(ra, valid), lds_addr(&sB[buf][b_step][(64 * (wave & 1) + 8 * i) * 128]),
           dB[i] + (stg * kStageK + b_step) * 128, 0);
   };
@@ -221,12 +226,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_large(LargeArgs a) {
     for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
   // LDS byte offsets of the operand reads. Fragment rows are multiples of 16, so a
-  // row's swizzle (row & 7) is c & 7 and the two 16-byte chunks a lane reads for
+  // row's swizzle (row / 2) % 8 is (c / 2) % 8 and the two 16-byte chunks a lane reads for
   // a K step (E2M1: chunk q of step 0 / 4+q of step 1 of the stage; E4M3: chunks
   // q and 4+q of its step) sit at two fixed per-lane offsets; stage, step and
   // fragment add compile-time constants.
-  const int off0 = c * 128 + ((q ^ (c & 7)) << 4);
-  const int off1 = c * 128 + (((4 + q) ^ (c & 7)) << 4);
+  const int off0 = c * 128 + ((q ^ (c >> 1)) << 4);
+  const int off1 = c * 128 + (((4 + q) ^ (c >> 1)) << 4);
   // this wave's 8 weight fragments: W13 gate 4wn..4wn+3 and up 8+4wn..; W2 8wn..8wn+7
   const int a_wave = W13 ? wn * 4 * 2048 : wn * 8 * 2048;
   auto a_frag = [](int i) { return W13 ? (i < 4 ? i : 8 + (i - 4)) * 2048 : i * 2048; };
