@@ -45,6 +45,12 @@ constexpr int kStageB = kTokTile * 128;   // bytes of E4M3 codes per K step
 constexpr int kCodeDma = 16;              // direct-to-LDS code copies per wave per stage
 constexpr int kScaleSteps = 8;            // K steps per weight-scale chunk (32 B per row)
 constexpr int kMaxKS = 64;                // K steps whose activation scales fit the tile's LDS
+// LDS strides of the scale tables, padded so that the 16 rows of an MFMA fragment
+// fall on 16 distinct banks: weight scales in groups of 8 rows x 32 B with 32 B of
+// padding per group (the fragment's second 8 rows shift by 8 banks), activation
+// scales 68 B per routed row (17 dwords).
+constexpr int kSaGroup = 8 * kScaleSteps * 4 + 32;   // bytes per 8-row group
+constexpr int kSbRow = kMaxKS + 4;
 
 typedef int v4i_s __attribute__((ext_vector_type(4)));
 
@@ -105,8 +111,8 @@ template <bool W13>
 __global__ __launch_bounds__(kThreads, 1) void k_gemm_large(LargeArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t sA[2][kStageA];                 // [stage][row][128 B]
   __shared__ __attribute__((aligned(1024))) uint8_t sB[2][kStageK][kStageB];        // [stage][step][row][128 B]
-  __shared__ __attribute__((aligned(16))) uint32_t sSa[2][kARows][kScaleSteps];     // [chunk buf][row][step]
-  __shared__ __attribute__((aligned(16))) uint8_t sSb[kTokTile][kMaxKS];            // [row][step]
+  __shared__ __attribute__((aligned(16))) uint8_t sSa[2][kARows / 8][kSaGroup];     // [chunk buf][8-row group][row][step][4]
+  __shared__ __attribute__((aligned(16))) uint8_t sSb[kTokTile][kSbRow];            // [row][step]
   __shared__ int sTok[kTokTile];
   __shared__ float sRed[2][kTokTile];
 
@@ -215,7 +221,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_large(LargeArgs a) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int i = 2 * part + h;
-      dma4(r_s, lds_addr(&sSa[chunk & 1][64 * wave + 8 * i][0]), dS + chunk * kScaleSteps * 4 + 8 * i * srow, 0);
+      dma4(r_s, lds_addr(&sSa[chunk & 1][8 * wave + i][0]), dS + chunk * kScaleSteps * 4 + 8 * i * srow, 0);
     }
   };
 
@@ -240,8 +246,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_large(LargeArgs a) {
   const uint8_t* pB0 = &sB[0][0][0] + wm * 4 * 2048 + off0;
   const uint8_t* pB1 = &sB[0][0][0] + wm * 4 * 2048 + off1;
   // weight scales: lane group q reads its K block's byte of the (row, step) dword
-  const uint8_t* pSa = reinterpret_cast<const uint8_t*>(&sSa[0][0][0]) + a_wave / 4 + c * 32 + q;
-  const uint8_t* pSb = &sSb[0][0] + wm * 4 * 16 * kMaxKS + c * kMaxKS;
+  // (fragment f, row c) -> group 2f + c/8, row c%8 of the group
+  const uint8_t* pSa = &sSa[0][0][0] + (a_wave / 2048) * 2 * kSaGroup + (c >> 3) * kSaGroup + (c & 7) * 32 + q;
+  const uint8_t* pSb = &sSb[0][0] + (wm * 4 * 16 + c) * kSbRow;
 
   // Operands of one K step in registers: this wave's 4 routed-row fragments (E4M3)
   // and 8 weight fragments (E2M1) with their E8M0 scales. They are read in 8
@@ -260,13 +267,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_large(LargeArgs a) {
       const v4i hi = *reinterpret_cast<const v4i*>(pB1 + ob);
       o.b[p][0] = lo[0]; o.b[p][1] = lo[1]; o.b[p][2] = lo[2]; o.b[p][3] = lo[3];
       o.b[p][4] = hi[0]; o.b[p][5] = hi[1]; o.b[p][6] = hi[2]; o.b[p][7] = hi[3];
-      o.sb[p] = pSb[ks + p * 16 * kMaxKS];
+      o.sb[p] = pSb[ks + p * 16 * kSbRow];
     } else {
-      const uint8_t* sa = pSa + ((ks / kScaleSteps) & 1) * (kARows * kScaleSteps * 4) + (ks % kScaleSteps) * 4;
+      const uint8_t* sa = pSa + ((ks / kScaleSteps) & 1) * (kARows / 8 * kSaGroup) + (ks % kScaleSteps) * 4;
 #pragma unroll
       for (int i = 2 * (p - 4); i < 2 * (p - 4) + 2; ++i) {
         o.w[i] = *reinterpret_cast<const v4i*>((h ? pA1 : pA0) + buf * kStageA + a_frag(i));
-        o.sa[i] = sa[a_frag(i) / 4];
+        o.sa[i] = sa[a_frag(i) / 2048 * 2 * kSaGroup];
       }
     }
   };
