@@ -17,7 +17,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .formats import E4M3_VALUES, bf16_to_f64, f64_to_bf16_rne
+from .formats import E4M3_VALUES, bf16_to_f64, e4m3_encode, f64_to_bf16_rne
 
 
 def y_metrics(y_bits: np.ndarray, y_ref: np.ndarray) -> dict:
@@ -42,7 +42,7 @@ def _signed_index(codes: np.ndarray) -> np.ndarray:
     return np.where(c & 0x80, -mag, mag)
 
 
-def h_code_mismatch(hq, hs, hq_ref, hs_ref, amax_ref, block: int = 128) -> dict:
+def h_code_mismatch(hq, hs, hq_ref, hs_ref, amax_ref, block: int = 128, h_ref=None, h_err=None) -> dict:
     """Compare SwiGLU-output codes element by element.
 
     hq, hq_ref uint8 [R, C]; hs, hs_ref uint8 [R, C/block]; amax_ref float64
@@ -57,6 +57,10 @@ def h_code_mismatch(hq, hs, hq_ref, hs_ref, amax_ref, block: int = 128) -> dict:
                 * a scale that differs in a block whose oracle amax is within
                   2^-16 (relative) of a scale boundary 1.75 * 2^p, and values at
                   most one grid step of the coarser scale apart;
+                * with an envelope (h_ref, the exact values, and h_err >= 0): same
+                  scale and a code between the codes of h_ref - h_err and
+                  h_ref + h_err (the value rounds from somewhere in the envelope);
+                  the scale-boundary window widens to the block's largest h_err;
       bad    -- anything else (a scale that differs away from a boundary makes
                 every element of its block bad).
     The bar: no bad element, and at most 0.1% of elements close-but-unequal.
@@ -81,16 +85,26 @@ def h_code_mismatch(hq, hs, hq_ref, hs_ref, amax_ref, block: int = 128) -> dict:
     fixed_step = (np.abs(E4M3_VALUES[a]) <= 2.0 ** -5) & (np.abs(E4M3_VALUES[b]) <= 2.0 ** -5) & \
         (np.abs(va - vb) <= 2.0 ** -6 * scale_b)
 
+    in_env = np.zeros_like(equal)
+    window = amax * 2.0 ** -16
+    if h_ref is not None:
+        hr = np.asarray(h_ref, dtype=np.float64).reshape(R, nb, block)
+        he = np.asarray(h_err, dtype=np.float64).reshape(R, nb, block)
+        lo = e4m3_encode(np.ldexp(hr - he, -(hs_ref - 127)[..., None]))
+        hi = e4m3_encode(np.ldexp(hr + he, -(hs_ref - 127)[..., None]))
+        ia, ilo, ihi = _signed_index(a), _signed_index(lo), _signed_index(hi)
+        in_env = (ia >= np.minimum(ilo, ihi)) & (ia <= np.maximum(ilo, ihi))
+        window = np.maximum(window, he.max(axis=-1))
     _, ex = np.frexp(amax)               # amax = 2m * 2^(ex-1)
     boundary = 1.75 * np.ldexp(1.0, ex - 1)
-    near = np.abs(amax - boundary) <= amax * 2.0 ** -16
+    near = np.abs(amax - boundary) <= window
     coarse = np.ldexp(1.0, np.maximum(hs, hs_ref) - 127)[..., None]
     mag = np.maximum(np.abs(va), np.abs(vb)) / coarse
     _, mex = np.frexp(np.maximum(mag, 2.0 ** -6))
     step = np.ldexp(1.0, mex - 1 - 3) * coarse
     close_diff = near[..., None] & (np.abs(va - vb) <= step)
 
-    close = ~equal & np.where(same, (dist <= 1) | fixed_step, close_diff)
+    close = ~equal & np.where(same, (dist <= 1) | fixed_step | in_env, close_diff)
     bad = ~equal & ~close
     n = int(a.size)
     idx = np.argwhere(bad)[:5]

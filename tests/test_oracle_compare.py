@@ -3,7 +3,7 @@
 import numpy as np
 
 from oracle.compare import h_code_mismatch, y_metrics
-from oracle.formats import f64_to_bf16_rne, quantize_blocks
+from oracle.formats import e4m3_encode, f64_to_bf16_rne, quantize_blocks
 
 
 def _blocks(seed=0, R=8, C=256):
@@ -64,3 +64,25 @@ def test_y_metrics():
     assert m["frac_equal_bf16"] == 1.0 and m["mean_rel"] < 4e-3 and m["max_rel"] < 4e-3
     m2 = y_metrics(f64_to_bf16_rne(2 * r), r)
     assert abs(m2["mean_rel"] - 1.0) < 1e-2
+
+
+def test_envelope_accepts_codes_reachable_from_the_envelope_only():
+    """A code two grid steps from the oracle's is accepted only when the
+    envelope [h - err, h + err] around the exact value reaches it (scale 2^-8,
+    binade [2^-5, 2^-4) of the scaled grid: step 2^-8 * 2^-8)."""
+    R, C = 1, 128
+    scale_code = np.array([[119]], dtype=np.uint8)            # 2^-8
+    amax = np.array([[1.19]])
+    h = np.zeros((R, C))
+    h[0, 0] = -1.75 * 2.0 ** -5 * 2.0 ** -8                    # exactly code 0x96 after scaling
+    ref = e4m3_encode(np.ldexp(h, 8))
+    assert ref[0, 0] == 0x96
+    gpu = ref.copy()
+    gpu[0, 0] = 0x98                                           # -2^-4 * 2^-8: two steps away
+    err_wide = np.full((R, C), 4e-5)
+    m = h_code_mismatch(gpu, scale_code, ref, scale_code, amax, h_ref=h, h_err=err_wide)
+    assert m["bad"] == 0 and m["differ"] == 1
+    m = h_code_mismatch(gpu, scale_code, ref, scale_code, amax, h_ref=h, h_err=np.full((R, C), 1e-6))
+    assert m["bad"] == 1
+    m = h_code_mismatch(gpu, scale_code, ref, scale_code, amax)  # no envelope: the default rules
+    assert m["bad"] == 1
