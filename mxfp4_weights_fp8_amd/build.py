@@ -16,7 +16,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmoe_mxfp4.so")
-SOURCES = ["moe_api.hip", "plan.hip", "quant.hip", "gemm_small.hip", "gemm_large.hip", "combine.hip"]
+SOURCES = ["moe_api.hip", "plan.hip", "quant.hip", "gemm_small.hip", "gemm_large.hip", "gemm_dense.hip",
+           "combine.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 
@@ -24,11 +25,12 @@ HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 # does not know the feature; that is harmless).
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno-unused-function",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
-# Per-source extras. The large-M GEMM keeps its 128 accumulator registers in the
+# Per-source extras. The LDS-staged GEMMs keep their 128 accumulator registers in the
 # unified VGPR file: with MFMA results in AGPRs, the register allocator rotates
 # accumulators through copies inside the K loop (v_accvgpr moves between dependent
 # MFMAs), which halves the MFMA issue rate.
-EXTRA = {"gemm_large.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+EXTRA = {"gemm_large.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+         "gemm_dense.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str) -> str:

@@ -32,6 +32,7 @@
 // rows each; the activation scales of the whole tile are read once.
 #include "device_common.h"
 #include "host_internal.h"
+#include "lds_copy.h"
 
 namespace moe {
 namespace {
@@ -51,45 +52,6 @@ constexpr int kMaxKS = 64;                // K steps whose activation scales fit
 // scales 68 B per routed row (17 dwords).
 constexpr int kSaGroup = 8 * kScaleSteps * 4 + 32;   // bytes per 8-row group
 constexpr int kSbRow = kMaxKS + 4;
-
-typedef int v4i_s __attribute__((ext_vector_type(4)));
-
-// Buffer resource as four SGPRs (base, stride 0, size, raw access) for inline asm.
-__device__ __forceinline__ v4i_s rsrc4(const void* base, uint32_t bytes) {
-  const uint64_t b = (uint64_t)base;
-  v4i_s r;
-  r[0] = (int)(uint32_t)b;
-  r[1] = (int)(uint32_t)(b >> 32);
-  r[2] = (int)bytes;
-  r[3] = kRsrcWord3;
-  return r;
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-
-// Direct-to-LDS buffer loads: lane l's data lands at M0 + l*size. Issued from
-// inline asm so the compiler does not serialize later LDS reads against these
-// writes; every use of the copied data is preceded by an explicit vmcnt wait and
-// a barrier.
-__device__ __forceinline__ void dma16(v4i_s r, uint32_t lds, int voff, int soff) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds" ::"s"(lds), "v"(voff), "s"(r),
-               "s"(soff)
-               : "memory", "m0");
-}
-__device__ __forceinline__ void dma4(v4i_s r, uint32_t lds, int voff, int soff) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds" ::"s"(lds), "v"(voff), "s"(r),
-               "s"(soff)
-               : "memory", "m0");
-}
-
-// s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] |
-// lgkmcnt[11:8] | vmcnt[5:4] << 14).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
 
 struct LargeArgs {
   const int2* items;
@@ -169,10 +131,6 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_large(LargeArgs a) {
   const v4i_s rw = rsrc4(a.w + (int64_t)e * N * wrow, (uint32_t)(N * wrow));
   const v4i_s rws = rsrc4(a.w_s + (int64_t)e * N * srow, (uint32_t)(N * srow));
   const v4i_s ra = rsrc4(a.act, a.act_bytes);
-  auto sized = [](v4i_s r, bool keep) {
-    r[2] = keep ? r[2] : 0;
-    return r;
-  };
 
   // expert weight row of LDS row r (0..255): fragments of 16 rows
   auto w_row = [&](int r) -> int {
@@ -202,9 +160,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_large(LargeArgs a) {
   // of stage stg (K steps 2stg, 2stg+1) into LDS buffer buf; valid == false (a
   // stage past the last) writes zeros.
   auto issue_part = [&](int buf, int stg, bool valid, int i) {
-    dma16(sized(rw, valid), lds_addr(&sA[buf][(64 * wave + 8 * i) * 128]),
+    dma16(rsrc_sized(rw, valid), lds_addr(&sA[buf][(64 * wave + 8 * i) * 128]),
           dA + ((i & 1) ? sw1 : sw0) + 8 * i * wrow + stg * 128, 0);
-    dma16(sized(ra, valid), lds_addr(&sB[buf][b_step][(64 * (wave & 1) + 8 * i) * 128]),
+    dma16(rsrc_sized(ra, valid), lds_addr(&sB[buf][b_step][(64 * (wave & 1) + 8 * i) * 128]),
           dB[i] + (stg * kStageK + b_step) * 128, 0);
   };
   auto issue_stage = [&](int buf, int stg, bool valid) {
@@ -217,7 +175,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_large(LargeArgs a) {
   // last read of chunk c-2 (stage 4c-5's first step), and the last part is waited
   // for before step 8c is read (at stage 4c-1). Chunks past the last step write zeros.
   auto issue_scales = [&](int chunk, int part) {
-    const v4i_s r_s = sized(rws, chunk * kScaleSteps < KS);
+    const v4i_s r_s = rsrc_sized(rws, chunk * kScaleSteps < KS);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int i = 2 * part + h;

@@ -87,6 +87,13 @@ hipError_t launch_w13_large(const moe_dims& d, const int2* items, const int32_t*
 hipError_t launch_w2_large(const moe_dims& d, const int2* items, const int32_t* n_items, int64_t max_items,
                            const int32_t* offsets, const int32_t* sorted_pairs, const uint8_t* h_q,
                            const uint8_t* h_s, const uint8_t* w2, const uint8_t* w2_s, float* o, hipStream_t s);
+// Dense FP8 shared expert: W13s + SwiGLU/requant into sh_q/sh_s, then W2s into
+// fp32 rows so [T, H]. Needs H/128 and Is/128 at most 64.
+bool dense_path_supported(const moe_dims& d);
+hipError_t launch_shared13(const moe_dims& d, const uint8_t* x_q, const uint8_t* x_s, const uint8_t* w13s,
+                           const uint8_t* w13s_s, uint8_t* sh_q, uint8_t* sh_s, hipStream_t s);
+hipError_t launch_shared2(const moe_dims& d, const uint8_t* sh_q, const uint8_t* sh_s, const uint8_t* w2s,
+                          const uint8_t* w2s_s, float* so, hipStream_t s);
 hipError_t launch_combine(const float* o, const float* topk_weights, const int32_t* pair_rows, const float* so,
                           uint16_t* y, int T, int H, int K, hipStream_t s);
 

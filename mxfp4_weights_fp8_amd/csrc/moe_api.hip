@@ -113,7 +113,7 @@ int moe_ffn(const moe_dims* dims, const uint16_t* x, const float* topk_weights, 
       !w2_s || !y || !ws)
     return MOE_EINVAL;
   if (use_shared && (!shared->w13s || !shared->w13s_s || !shared->w2s || !shared->w2s_s)) return MOE_EINVAL;
-  if (use_shared) return MOE_EUNSUPPORTED;
+  if (use_shared && !dense_path_supported(d)) return MOE_EUNSUPPORTED;
   FfnWs fw;
   if (ws_bytes < ffn_ws_layout(d, ws, &fw)) return MOE_EWORKSPACE;
   PlanWs pw;
@@ -152,9 +152,18 @@ int moe_ffn(const moe_dims* dims, const uint16_t* x, const float* topk_weights, 
                           h_q, h_s, w2, w2_s, fw.o, s);
   if (err != hipSuccess) return MOE_EHIP;
   record(dbg, MOE_EV_W2_DONE, s);
+
+  if (use_shared) {
+    uint8_t* sh_q = dbg && dbg->sh_q ? dbg->sh_q : fw.sh_q;
+    uint8_t* sh_s = dbg && dbg->sh_s ? dbg->sh_s : fw.sh_s;
+    err = launch_shared13(d, x_q, x_s, shared->w13s, shared->w13s_s, sh_q, sh_s, s);
+    if (err != hipSuccess) return MOE_EHIP;
+    err = launch_shared2(d, sh_q, sh_s, shared->w2s, shared->w2s_s, fw.so, s);
+    if (err != hipSuccess) return MOE_EHIP;
+  }
   record(dbg, MOE_EV_SHARED_DONE, s);
 
-  err = launch_combine(fw.o, topk_weights, pair_rows, nullptr, y, d.T, d.H, d.K, s);
+  err = launch_combine(fw.o, topk_weights, pair_rows, use_shared ? fw.so : nullptr, y, d.T, d.H, d.K, s);
   if (err != hipSuccess) return MOE_EHIP;
   record(dbg, MOE_EV_END, s);
   return MOE_OK;

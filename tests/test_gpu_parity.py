@@ -10,7 +10,7 @@ import mxfp4_weights_fp8_amd as moe
 from gpu_helpers import check_ffn, check_plan, run_path, say, u16
 from oracle.formats import bf16_to_f64
 from oracle.moe import quant_act_ref
-from synth import WORKLOADS, make_expert_weights, make_inputs, make_routing, scaled
+from synth import WORKLOADS, make_expert_weights, make_inputs, make_routing, make_shared_weights, scaled
 
 pytestmark = pytest.mark.gpu
 
@@ -125,6 +125,22 @@ def test_ffn_shapes(dev, T, H, I, E, K, seed, small_max):
     check_ffn(inp, p, y, dbg, label=f"shape {T}x{H} I{I} E{E} K{K} small_max={small_max}")
 
 
+@pytest.mark.parametrize("T,H,I,E,K,Is,seed,small_max", [
+    (1, 128, 128, 1, 1, 128, 51, 0),      # degenerate: one token, one expert, one shared tile
+    (33, 256, 256, 5, 3, 128, 52, 0),     # ragged token tile (33 of 128 rows)
+    (130, 384, 128, 4, 2, 256, 53, 1),    # H = 3 * 128: the shared W2 tile's second half is masked
+    (200, 1280, 384, 4, 2, 384, 54, 1),   # odd K-step count in the shared W2 (Is = 3 * 128)
+])
+def test_ffn_shared_shapes(dev, T, H, I, E, K, Is, seed, small_max):
+    """Routed experts plus the dense FP8 shared expert (128 x 128 block scales):
+    y, the shared SwiGLU codes and scales against the oracle."""
+    wl = scaled("tiny", T=T, H=H, I=I, E=E, K=K, Is=Is, seed=seed, weight_seed=seed, name=f"sh{seed}")
+    inp = make_inputs(wl).to(dev)
+    assert inp.shared is not None
+    p, (y, dbg) = run_path(inp, small_max=small_max)
+    check_ffn(inp, p, y, dbg, label=f"shared {T}x{H} I{I} Is{Is} E{E} K{K}")
+
+
 def test_ffn_invalid_ids(dev):
     inp = make_inputs("tiny").to(dev)
     ids = inp.topk_ids.clone()
@@ -195,4 +211,24 @@ def test_ffn_prefill32k_sampled(dev, full_weights):
     toks += list(np.random.default_rng(2).choice(inp.wl.T, 4, replace=False))
     toks += [inp.wl.T - 1]
     check_ffn(inp, p, y, dbg, tokens=toks, label="prefill32k sampled")
+    assert torch.isfinite(y.float()).all()
+
+
+def test_ffn_tp8rank32k_sampled(dev):
+    """One TP8 rank of the 32K prefill (routed I 384 slice + the FP8 shared expert),
+    sampled tokens: the hottest expert's first and last token, random ones, the last."""
+    import time
+    t = time.time()
+    inp = make_inputs("tp8rank32k", weights=False).to(dev)
+    inp.weights = make_expert_weights(inp.wl, dev)
+    inp.shared = make_shared_weights(inp.wl, dev)
+    torch.cuda.synchronize()
+    say(f"[tp8rank32k weights] generated in {time.time() - t:.1f}s")
+    p, (y, dbg) = run_path(inp)
+    ids = inp.topk_ids.cpu().numpy()
+    hot = int(np.argmax(np.bincount(ids.ravel(), minlength=inp.wl.E)))
+    toks = list(np.nonzero((ids == hot).any(1))[0][[0, -1]])
+    toks += list(np.random.default_rng(5).choice(inp.wl.T, 4, replace=False))
+    toks += [inp.wl.T - 1]
+    check_ffn(inp, p, y, dbg, tokens=toks, label="tp8rank32k sampled")
     assert torch.isfinite(y.float()).all()
