@@ -22,7 +22,8 @@ MEAN_REL_MIN_ELEMENTS = 1024
 #: SwiGLU-output codes: at most this fraction may differ (each by at most one grid step)
 H_DIFFER = 1e-3
 #: shared expert (FP8 x FP8 dot products, not exact in hardware): every differing
-#: code must lie inside the oracle's envelope; this caps how many may differ
+#: code must lie inside the oracle's envelope; on samples of 1024+ codes this also
+#: caps how many may differ
 SH_DIFFER = 1e-2
 
 
@@ -87,5 +88,7 @@ def check_ffn(inp, p, y, dbg, tokens=None, label=""):
     assert m["h_bad"] == 0, m
     assert m["h_frac_differ"] <= H_DIFFER, m
     if inp.shared is not None:
-        assert m["sh_bad"] == 0 and m["sh_frac_differ"] <= SH_DIFFER, m
+        assert m["sh_bad"] == 0, m
+        if m["sh_elements"] >= MEAN_REL_MIN_ELEMENTS:
+            assert m["sh_frac_differ"] <= SH_DIFFER, m
     return m
