@@ -18,6 +18,7 @@ bounded sample is reported as cpu_baseline.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -30,7 +31,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 import mxfp4_weights_fp8_amd as moe  # noqa: E402
-from synth import WORKLOADS, make_expert_weights, make_inputs  # noqa: E402
+from synth import WORKLOADS, make_expert_weights, make_inputs, make_shared_weights  # noqa: E402
 
 METRIC = "MoE FFN tokens/s + % MFMA peak (32K prefill) + HBM GB/s (decode M=7)"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
@@ -50,6 +51,24 @@ def expert_bytes(w) -> dict:
     return {"w13": w13, "w2": w2}
 
 
+def measured_traffic(workload: str, kernel: str):
+    """HBM bytes per launch of ``kernel`` from the committed rocprofv3 counter
+    summary of ``workload`` (FETCH_SIZE and WRITE_SIZE scaled by a plain copy of
+    known size), or None when there is no summary or the kernel's sources have
+    changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"{workload}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    for line in open(path):
+        f = line.strip().split(",")
+        if len(f) == 7 and f[0] == kernel and f[5] != "-":
+            h = hashlib.sha256()
+            for name in f[5].split("+"):
+                h.update(open(os.path.join(ROOT, "mxfp4_weights_fp8_amd", "csrc", name), "rb").read())
+            return float(f[4]) if h.hexdigest() == f[6] else None
+    return None
+
+
 class Runner:
     """Holds one workload resident on the GPU and runs steps of the hot path."""
 
@@ -58,6 +77,7 @@ class Runner:
         w = self.w
         inp = make_inputs(name, weights=False).to(dev)
         inp.weights = weights if weights is not None else make_expert_weights(w, dev)
+        inp.shared = make_shared_weights(w, dev) if w.Is else None
         self.inp = inp
         self.dev = dev
         self.plan = moe.plan(inp.topk_ids, w.E, w.H, w.I, Is=w.Is)
@@ -127,8 +147,9 @@ def main():
     ap.add_argument("--prefill-steps", type=int, default=5)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--only", choices=["decode7", "prefill32k"], default=None,
-                    help="run one workload only (for profiling); prints its own JSON object")
+    ap.add_argument("--only", choices=["decode7", "prefill32k", "tp8rank32k", "copy"], default=None,
+                    help="run one workload only (for profiling); prints its own JSON object. 'copy' runs "
+                         "a 1 GiB device-to-device copy, the known-size reference for HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU; multi-GPU runs are not part of it "
@@ -136,17 +157,25 @@ def main():
         sys.exit(2)
 
     dev = torch.device("cuda:0")
+    if args.only == "copy":
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)   # contents do not matter for a copy
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"workload": "copy", "bytes_read": src.numel(), "bytes_written": dst.numel(), "launches": 3}))
+        return
     moe.lib()
     t = time.time()
     W = make_expert_weights(WORKLOADS["decode7"], dev)     # one 384-expert set, shared by both workloads
     torch.cuda.synchronize()
     log(f"[bench] weights generated in {time.time() - t:.1f}s")
 
-    if args.only == "prefill32k":
-        pre = Runner("prefill32k", dev, W)
+    if args.only in ("prefill32k", "tp8rank32k"):
+        pre = Runner(args.only, dev, W if args.only == "prefill32k" else None)
         ps, p13_ms, pms = pre.run(args.prefill_steps, args.warmup)
-        log(f"[bench] prefill32k: {ps:.3f} ms/step, w13 {p13_ms:.3f} ms, stages {pms}")
-        print(json.dumps({"workload": "prefill32k", "ms_per_step": ps, "w13_ms": p13_ms, "stage_ms": pms}))
+        log(f"[bench] {args.only}: {ps:.3f} ms/step, w13 {p13_ms:.3f} ms, stages {pms}")
+        print(json.dumps({"workload": args.only, "ms_per_step": ps, "w13_ms": p13_ms, "stage_ms": pms}))
         return
 
     # ---- decode verify, 7 tokens (headline)
@@ -178,7 +207,8 @@ def main():
                    "top_k": w.K, "routing": f"zipf s={w.zipf_s}", "distinct_experts": dec.distinct},
         "roofline": {"bound": "hbm", "kernel": "W13 grouped GEMM + SwiGLU/requant (k_w13_small)",
                      "achieved": w13_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": w13_gbs / HBM_PEAK_GBS,
-                     "traffic": None, "algorithmic_bytes_per_launch": w13_bytes, "avg_launch_ms": w13_ms},
+                     "traffic": measured_traffic("decode7", "moe::k_w13_small"),
+                     "algorithmic_bytes_per_launch": w13_bytes, "avg_launch_ms": w13_ms},
         "step_hbm_gbs": step_bytes / (ms_step * 1e-3) / 1e9,
         "stage_ms_untimed_pass": ms,
     }
@@ -199,12 +229,33 @@ def main():
             "mfma_frac_fp8_peak": (f13 + f2) / (ps * 1e-3) / 1e12 / MFMA_PEAK_FP8_TFLOPS,
             "roofline": {"bound": "mfma", "kernel": "W13 grouped GEMM + SwiGLU/requant", "achieved": t13,
                          "peak": MFMA_PEAK_FP8_TFLOPS, "unit": "TFLOP/s", "frac": t13 / MFMA_PEAK_FP8_TFLOPS,
-                         "frac_of_fp4_peak": t13 / MFMA_PEAK_FP4_TFLOPS, "traffic": None,
+                         "frac_of_fp4_peak": t13 / MFMA_PEAK_FP4_TFLOPS,
+                         "traffic": measured_traffic("prefill32k", "moe::k_gemm_large<true>"),
                          "algorithmic_flops_per_launch": f13, "avg_launch_ms": p13_ms},
             "stage_ms_untimed_pass": pms,
         }
         log(f"[bench] prefill32k: {ps:.3f} ms/step, w13 {p13_ms:.3f} ms, stages {pms}")
         del pre
+
+    # ---- one MoE-TP8 rank of the 32K chunk: routed I 384 slice + FP8 shared expert
+    if not args.no_prefill and args.only is None:
+        tp = Runner("tp8rank32k", dev)
+        ts, t13_ms, tms = tp.run(args.prefill_steps, 1)
+        tw = tp.w
+        Pt = tw.T * tw.K
+        fr = 2.0 * Pt * (2 * tw.I) * tw.H + 2.0 * Pt * tw.H * tw.I
+        fs = 2.0 * tw.T * (2 * tw.Is) * tw.H + 2.0 * tw.T * tw.H * tw.Is
+        out["tp8rank32k"] = {
+            "value": tw.T / (ts * 1e-3), "unit": "tokens/s", "ms_per_step": ts, "steps": args.prefill_steps,
+            "config": {"workload": "tp8rank32k", "tokens": tw.T, "intermediate_per_rank": tw.I,
+                       "shared_intermediate": tw.Is, "routing": f"zipf s={tw.zipf_s}"},
+            "effective_tflops": (fr + fs) / (ts * 1e-3) / 1e12,
+            "mfma_frac_fp8_peak": (fr + fs) / (ts * 1e-3) / 1e12 / MFMA_PEAK_FP8_TFLOPS,
+            "shared_tflops": fs / (tms["shared"] * 1e-3) / 1e12,
+            "stage_ms_untimed_pass": tms,
+        }
+        log(f"[bench] tp8rank32k: {ts:.3f} ms/step, stages {tms}")
+        del tp
 
     # ---- oracle on the host cores (bounded sample)
     if not args.no_cpu and args.only is None:
