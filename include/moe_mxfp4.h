@@ -56,8 +56,9 @@ enum {
 
 /* Problem dimensions.
  *   T  tokens (>= 0; T == 0 is a valid no-op)
- *   H  hidden size, multiple of 128 (K of W13, N of W2)
- *   I  intermediate size per expert, multiple of 128 (per rank for an MoE-TP slice)
+ *   H  hidden size, multiple of 128, at most 16384 (K of W13, N of W2)
+ *   I  intermediate size per expert, multiple of 128, at most 16384 (per rank for
+ *      an MoE-TP slice)
  *   E  routed experts, 1..4096
  *   K  picks per token (top-k), 1..64
  *   Is shared-expert intermediate size, multiple of 128, 0 = no shared expert

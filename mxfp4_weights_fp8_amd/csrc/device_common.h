@@ -20,12 +20,13 @@ constexpr int kFmtE2M1 = 4;
 //   8-bit operand: register bytes 0..15 hold K = 16q + i, bytes 16..31 hold
 //     K = 64 + 16q + i (two 16-byte halves of the 128-long K step).
 //   4-bit operand: the low 16 bytes hold K = 32q .. 32q+31, low nibble first.
-//   scale operand (E8M0 in the low byte with op_sel 0): row/column l % 16,
-//     K block q (K = 32q .. 32q+31).
+//   scale operand (E8M0 in byte OPSEL of the VGPR): row/column l % 16, K block q
+//     (K = 32q .. 32q+31).
 //   D (16 x 16 fp32): column l % 16, rows 4q .. 4q+3.
-template <int FMT_A, int FMT_B>
+//   OPSEL_A / OPSEL_B (0..3) pick which byte of the 32-bit scale operand is used.
+template <int FMT_A, int FMT_B, int OPSEL_A = 0, int OPSEL_B = 0>
 __device__ __forceinline__ v4f mfma_scale_16x16x128(v8i a, v8i b, v4f c, int scale_a, int scale_b) {
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, FMT_A, FMT_B, 0, scale_a, 0, scale_b);
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, FMT_A, FMT_B, OPSEL_A, scale_a, OPSEL_B, scale_b);
 }
 
 // Smallest e with amax <= 448 * 2^e, from the fp32 bit pattern of amax >= 0:

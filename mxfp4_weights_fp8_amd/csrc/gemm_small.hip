@@ -20,6 +20,7 @@
 // pair's fp32 row to its token-major slot p = t*K + j for the top-k combine.
 #include "device_common.h"
 #include "host_internal.h"
+#include "lds_copy.h"
 
 namespace moe {
 namespace {
@@ -45,12 +46,15 @@ struct Step {
 };
 
 // Where a wave's operands live: buffer resources (wave-uniform) and per-lane
-// byte offsets; step s adds s*64 (codes), s*4 (scale dwords), s*128 (activation
-// codes), s (activation scales) as wave-uniform offsets.
+// byte offsets; step s adds s*64 (codes), s*128 (activation codes), s (activation
+// scales) as wave-uniform offsets. The weight scales are in LDS: sl[f] is the
+// lane's row of fragment f there (KS dwords, dword s = the four 32-block scales
+// of step s).
 template <int NF>
 struct Stream {
-  rsrc_t w, ws, x, xs;
-  int wo[NF], so[NF];
+  rsrc_t w, x, xs;
+  int wo[NF];
+  const uint8_t* sl[NF];
   int xo, xso;
 };
 
@@ -59,7 +63,7 @@ __device__ __forceinline__ void load_step(Step<NF>& r, const Stream<NF>& p, int 
 #pragma unroll
   for (int f = 0; f < NF; ++f) {
     r.w[f] = buf_load16(p.w, p.wo[f], s * 64);
-    r.ws[f] = buf_load4(p.ws, p.so[f], s * 4);
+    r.ws[f] = *reinterpret_cast<const int*>(p.sl[f] + s * 4);
   }
   const v4i lo = buf_load16(p.x, p.xo, s * 128), hi = buf_load16(p.x, p.xo, s * 128 + 64);
   r.x[0] = lo[0]; r.x[1] = lo[1]; r.x[2] = lo[2]; r.x[3] = lo[3];
@@ -72,6 +76,24 @@ __device__ __forceinline__ void mma_step(const Step<NF>& r, int qshift, v4f* acc
 #pragma unroll
   for (int f = 0; f < NF; ++f)
     acc[f] = mfma_scale_16x16x128<kFmtE2M1, kFmtE4M3>(fp4_operand(r.w[f]), r.x, acc[f], r.ws[f] >> qshift, r.xs);
+}
+
+// LDS bytes of one staged run of `bytes`: whole 1 KB copy instructions.
+__host__ __device__ constexpr int staged_bytes(int bytes) { return (bytes + 1023) / 1024 * 1024; }
+
+// Copy one or two contiguous byte runs (src0, then src1 when non-null, `bytes`
+// each; wave-uniform arguments) into LDS at dst, run h at dst + h*staged_bytes,
+// with direct-to-LDS 16-byte-per-lane copies (1 KB per instruction; lanes past
+// the run read zeros into the run's padding). The wave alone reads what it copied;
+// stream_k waits for the copies (vmcnt 0) before its first LDS read, so no
+// barrier is needed.
+__device__ __forceinline__ void stage_scales(const uint8_t* src0, const uint8_t* src1, int bytes, uint8_t* dst,
+                                             int lane) {
+  for (int h = 0; h < (src1 ? 2 : 1); ++h) {
+    const v4i_s r = rsrc4(h ? src1 : src0, (uint32_t)bytes);
+    for (int off = 0; off < bytes; off += 1024)
+      dma16(r, lds_addr(dst + h * staged_bytes(bytes) + off), lane * 16 + off, 0);
+  }
 }
 
 // Codes of one K step (the scales travel separately, four steps at a time).
@@ -92,20 +114,34 @@ __device__ __forceinline__ void load_codes(Codes<NF>& r, const Stream<NF>& p, in
 
 // acc[f] += sum over KS steps of 128 K.
 // Main path (KS a multiple of 4): the codes of kQuad = 4 steps stay in flight in a
-// register ring; the E8M0 scales of a 4-step chunk come in one 16-byte load per
-// fragment (the four dwords of those steps; lane group q uses byte q of each) and
-// one dword for the activation scales (byte d for step d), fetched a chunk ahead.
-// A scale load touches as many cache lines as a code load but carries a sixteenth
-// of the bytes, so fetching them four steps at a time cuts the cache requests of
-// the stream by about a third. Prefetch step indices are clamped on the
-// wave-uniform offset, so the loop is branch-free; the clamped reloads hit the
-// cache and go unused.
+// register ring. At the start of each 4-step chunk a lane reads the chunk's 16
+// bytes of E8M0 scales of its rows from LDS and packs its own K block's byte of
+// the four steps into one register; the MFMA's op_sel picks byte d for step d. The
+// activation scales come in one dword per chunk (byte d for step d). Prefetch step
+// indices are clamped on the wave-uniform offset, so the loop is branch-free; the
+// clamped reloads hit the cache and go unused.
 // Other K (short or not a multiple of 4 steps): a plain per-step loop.
 constexpr int kQuad = 4;
+
+// byte q of each of the four dwords of v, packed as bytes 0..3
+__device__ __forceinline__ int pack_lane_bytes(v4i v, int qshift) {
+  uint32_t r = 0;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) r |= (((uint32_t)v[d] >> qshift) & 0xFFu) << (8 * d);
+  return (int)r;
+}
+
+template <int NF, int D>
+__device__ __forceinline__ void mma_quad_step(const Codes<NF>& r, const int* sc, int xsc, v4f* acc) {
+#pragma unroll
+  for (int f = 0; f < NF; ++f)
+    acc[f] = mfma_scale_16x16x128<kFmtE2M1, kFmtE4M3, D, D>(fp4_operand(r.w[f]), r.x, acc[f], sc[f], xsc);
+}
 
 template <int NF>
 __device__ __forceinline__ void stream_k(v4f* acc, const Stream<NF>& p, int KS, int qshift) {
   if (KS % kQuad != 0) {
+    wait_vmcnt<0>();   // the weight-scale copies into LDS
     for (int s = 0; s < KS; ++s) {
       Step<NF> r;
       load_step(r, p, s);
@@ -114,29 +150,24 @@ __device__ __forceinline__ void stream_k(v4f* acc, const Stream<NF>& p, int KS, 
     return;
   }
   Codes<NF> buf[kQuad];
-  v4i sc[NF];
-  int xsc;
+  int sc[NF];
 #pragma unroll
   for (int d = 0; d < kQuad; ++d) load_codes(buf[d], p, d);
-#pragma unroll
-  for (int f = 0; f < NF; ++f) sc[f] = buf_load16(p.ws, p.so[f], 0);
-  xsc = buf_load4(p.xs, p.xso, 0);
+  int xsc = buf_load4(p.xs, p.xso, 0);
+  wait_vmcnt<0>();   // the weight-scale copies into LDS (and the first codes)
   for (int s0 = 0; s0 < KS; s0 += kQuad) {
+#pragma unroll
+    for (int f = 0; f < NF; ++f) sc[f] = pack_lane_bytes(*reinterpret_cast<const v4i*>(p.sl[f] + s0 * 4), qshift);
     const int nxt = min(s0 + kQuad, KS - kQuad);
-    v4i scn[NF];
-#pragma unroll
-    for (int f = 0; f < NF; ++f) scn[f] = buf_load16(p.ws, p.so[f], nxt * 4);
     const int xscn = buf_load4(p.xs, p.xso, nxt);
-#pragma unroll
-    for (int d = 0; d < kQuad; ++d) {
-#pragma unroll
-      for (int f = 0; f < NF; ++f)
-        acc[f] = mfma_scale_16x16x128<kFmtE2M1, kFmtE4M3>(fp4_operand(buf[d].w[f]), buf[d].x, acc[f],
-                                                          sc[f][d] >> qshift, xsc >> (8 * d));
-      load_codes(buf[d], p, min(s0 + kQuad + d, KS - 1));
-    }
-#pragma unroll
-    for (int f = 0; f < NF; ++f) sc[f] = scn[f];
+    mma_quad_step<NF, 0>(buf[0], sc, xsc, acc);
+    load_codes(buf[0], p, min(s0 + kQuad + 0, KS - 1));
+    mma_quad_step<NF, 1>(buf[1], sc, xsc, acc);
+    load_codes(buf[1], p, min(s0 + kQuad + 1, KS - 1));
+    mma_quad_step<NF, 2>(buf[2], sc, xsc, acc);
+    load_codes(buf[2], p, min(s0 + kQuad + 2, KS - 1));
+    mma_quad_step<NF, 3>(buf[3], sc, xsc, acc);
+    load_codes(buf[3], p, min(s0 + kQuad + 3, KS - 1));
     xsc = xscn;
   }
 }
@@ -148,27 +179,36 @@ __global__ __launch_bounds__(kThreads) void k_w13_small(
     const uint8_t* __restrict__ w13_s, uint8_t* __restrict__ h_q, uint8_t* __restrict__ h_s, int H, int I,
     int K) {
   __shared__ float red[kThreads / 64][16];
+  extern __shared__ __attribute__((aligned(16))) uint8_t sS[];   // [256 weight rows][H/32] E8M0
   const int item = blockIdx.y;
   if (item >= n_items[0]) return;
   const int2 it = items[item];
   const int e = it.x;
   const int e_begin = offsets[e], e_end = offsets[e + 1];
   const int nb = blockIdx.x;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, q = lane >> 4, c = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, q = lane >> 4, c = lane & 15;
   const int KS = H / 128;
   const int64_t wrow = H / 2, srow = H / 32;
 
   // 8-bit activation operand of a K step: bytes [16q, 16q+16) and [64+16q, 64+16q+16)
   Stream<4> p;
   p.w = make_rsrc(w13 + (int64_t)e * 2 * I * wrow, (uint32_t)(2 * I * wrow));
-  p.ws = make_rsrc(w13_s + (int64_t)e * 2 * I * srow, (uint32_t)(2 * I * srow));
   p.x = make_rsrc(x_q, 0xFFFFFFFFu);
   p.xs = make_rsrc(x_s, 0xFFFFFFFFu);
+  // Weight scales of the wave's 64 rows (gate rows nb*128 + wave*32 + [0, 32) and
+  // the matching up rows) into LDS rows wave*64 .. +63: two contiguous runs of
+  // 32 * srow bytes, copied in full 1 KB instructions (each cache line once; read
+  // per 4-step chunk straight from memory, a row's scale lines were refetched).
+  const int run = staged_bytes(32 * (int)srow);
+  stage_scales(w13_s + ((int64_t)e * 2 * I + nb * 128 + wave * 32) * srow,
+               w13_s + ((int64_t)e * 2 * I + I + nb * 128 + wave * 32) * srow, 32 * (int)srow,
+               sS + wave * 2 * run, lane);
 #pragma unroll
   for (int f = 0; f < 4; ++f) {
     const int n = (f >= 2 ? I : 0) + nb * 128 + wave * 32 + (f & 1) * 16 + c;
     p.wo[f] = n * (int)wrow + q * 16;
-    p.so[f] = n * (int)srow;
+    p.sl[f] = sS + wave * 2 * run + (f >> 1) * run + ((f & 1) * 16 + c) * srow;
   }
 
   for (int m0 = it.y; m0 < it.y + item_rows && e_begin + m0 < e_end; m0 += kSmallRows) {
@@ -223,9 +263,11 @@ __global__ __launch_bounds__(kThreads) void k_w2_small(
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_pairs,
     const uint8_t* __restrict__ h_q, const uint8_t* __restrict__ h_s, const uint8_t* __restrict__ w2,
     const uint8_t* __restrict__ w2_s, float* __restrict__ o, int H, int I) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t sS[];   // [256 weight rows][I/32] E8M0
   const int item = blockIdx.y;
   if (item >= n_items[0]) return;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, q = lane >> 4, c = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, q = lane >> 4, c = lane & 15;
   const int n_wave = blockIdx.x * 256 + wave * 64;
   if (n_wave >= H) return;
   const int2 it = items[item];
@@ -236,14 +278,16 @@ __global__ __launch_bounds__(kThreads) void k_w2_small(
 
   Stream<4> p;
   p.w = make_rsrc(w2 + (int64_t)e * H * wrow, (uint32_t)(H * wrow));
-  p.ws = make_rsrc(w2_s + (int64_t)e * H * srow, (uint32_t)(H * srow));
   p.x = make_rsrc(h_q, 0xFFFFFFFFu);
   p.xs = make_rsrc(h_s, 0xFFFFFFFFu);
+  // weight scales of the wave's 64 rows (one contiguous run) into LDS rows wave*64..
+  const int run = staged_bytes(64 * (int)srow);
+  stage_scales(w2_s + ((int64_t)e * H + n_wave) * srow, nullptr, 64 * (int)srow, sS + wave * run, lane);
 #pragma unroll
   for (int f = 0; f < 4; ++f) {
     const int n = n_wave + f * 16 + c;
     p.wo[f] = n * (int)wrow + q * 16;
-    p.so[f] = n * (int)srow;
+    p.sl[f] = sS + wave * run + (f * 16 + c) * srow;
   }
 
   for (int m0 = it.y; m0 < it.y + item_rows && e_begin + m0 < e_end; m0 += kSmallRows) {
@@ -276,7 +320,10 @@ hipError_t launch_w13_small(const moe_dims& d, const int2* items, const int32_t*
                             uint8_t* h_q, uint8_t* h_s, hipStream_t s) {
   if (max_items <= 0) return hipSuccess;
   dim3 grid(d.I / 128, (unsigned)max_items);
-  hipLaunchKernelGGL(k_w13_small, grid, dim3(kThreads), 0, s, items, n_items, item_rows, offsets, sorted_pairs,
+  // weight scales in LDS: per wave two runs of 32 rows x H/32 bytes
+  const size_t lds = (size_t)(kThreads / 64) * 2 * staged_bytes(32 * (d.H / 32));
+  hipLaunchKernelGGL(k_w13_small, grid, dim3(kThreads), lds, s, items, n_items, item_rows,
+                     offsets, sorted_pairs,
                      x_q, x_s, w13, w13_s, h_q, h_s, d.H, d.I, d.K);
   return hipGetLastError();
 }
@@ -287,7 +334,10 @@ hipError_t launch_w2_small(const moe_dims& d, const int2* items, const int32_t* 
                            float* o, hipStream_t s) {
   if (max_items <= 0) return hipSuccess;
   dim3 grid((unsigned)ceil_div(d.H, 256), (unsigned)max_items);
-  hipLaunchKernelGGL(k_w2_small, grid, dim3(kThreads), 0, s, items, n_items, item_rows, offsets, sorted_pairs,
+  // weight scales in LDS: per wave one run of 64 rows x I/32 bytes
+  const size_t lds = (size_t)(kThreads / 64) * staged_bytes(64 * (d.I / 32));
+  hipLaunchKernelGGL(k_w2_small, grid, dim3(kThreads), lds, s, items, n_items, item_rows,
+                     offsets, sorted_pairs,
                      h_q, h_s, w2, w2_s, o, d.H, d.I);
   return hipGetLastError();
 }

@@ -45,6 +45,8 @@ int validate(const moe_dims* d) {
   if (d->H % 128 || d->I % 128 || d->Is % 128) return MOE_EUNSUPPORTED;
   if ((int64_t)d->T * d->K > (int64_t)1 << 30) return MOE_EUNSUPPORTED;
   if (d->H > (1 << 20) || d->I > (1 << 20) || d->Is > (1 << 20)) return MOE_EUNSUPPORTED;
+  // the small-M kernels stage a workgroup's weight scales in LDS (8 H or 8 I bytes)
+  if (d->H > kMaxSmallDim || d->I > kMaxSmallDim) return MOE_EUNSUPPORTED;
   // kernels address activations, SwiGLU outputs and one expert's weights with
   // 32-bit byte offsets
   const int64_t lim = (int64_t)1 << 31;

@@ -43,6 +43,9 @@ def test_status_strings():
     ((4, 256, 512, 4097, 2), moe.MOE_EINVAL),
     ((4, 200, 512, 8, 2), moe.MOE_EUNSUPPORTED),
     ((4, 256, 500, 8, 2), moe.MOE_EUNSUPPORTED),
+    ((4, 16384, 16384, 8, 2), moe.MOE_OK),
+    ((4, 16512, 512, 8, 2), moe.MOE_EUNSUPPORTED),   # H above the small-M kernels' LDS scale staging
+    ((4, 256, 16512, 8, 2), moe.MOE_EUNSUPPORTED),
 ])
 def test_validate(dims, code):
     assert moe.validate(moe.make_dims(*dims)) == code
