@@ -29,7 +29,8 @@
 // row, odd rows in the other, each with 8 distinct chunks).
 // A stage holds two K steps (32 KB of weights + 32 KB of activations); two stages.
 // The weight E8M0 scales of eight K steps (32 B per row) come by dword copies of 8
-// rows each; the activation scales of the whole tile are read once.
+// rows each; the activation scales of the whole tile are copied once, before the
+// first stage.
 #include "device_common.h"
 #include "host_internal.h"
 #include "lds_copy.h"
@@ -52,6 +53,7 @@ constexpr int kMaxKS = 64;                // K steps whose activation scales fit
 // scales 68 B per routed row (17 dwords).
 constexpr int kSaGroup = 8 * kScaleSteps * 4 + 32;   // bytes per 8-row group
 constexpr int kSbRow = kMaxKS + 4;
+constexpr int kSbBytes = (kTokTile * kSbRow + 255) / 256 * 256;   // whole 256-byte copy blocks
 
 struct LargeArgs {
   const int2* items;
@@ -66,6 +68,8 @@ struct LargeArgs {
   uint8_t* h_s;
   float* o;                // W2 out
   uint32_t act_bytes;      // size of act
+  uint32_t act_s_bytes;    // size of act_s
+  int act_s_dma;           // act_s rows are 4-byte aligned: copy them with dword copies
   int H, I, K;
 };
 
@@ -74,8 +78,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_large(LargeArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t sA[2][kStageA];                 // [stage][row][128 B]
   __shared__ __attribute__((aligned(1024))) uint8_t sB[2][kStageK][kStageB];        // [stage][step][row][128 B]
   __shared__ __attribute__((aligned(16))) uint8_t sSa[2][kARows / 8][kSaGroup];     // [chunk buf][8-row group][row][step][4]
-  __shared__ __attribute__((aligned(16))) uint8_t sSb[kTokTile][kSbRow];            // [row][step]
+  __shared__ __attribute__((aligned(16))) uint8_t sSb[kSbBytes];                    // [row][step], kSbRow B per row
   __shared__ int sTok[kTokTile];
+  __shared__ int sSlot[W13 ? 1 : kTokTile];
   __shared__ float sRed[2][kTokTile];
 
   const int item = blockIdx.y;
@@ -96,15 +101,33 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_large(LargeArgs a) {
   const int NS = (KS + kStageK - 1) / kStageK;          // stages
   const int wrow = Kdim / 2, srow = Kdim / 32, arow = Kdim;
 
-  // routed rows of the tile -> activation row index (padding repeats the first row)
+  // routed rows of the tile -> activation row index (padding repeats the first row);
+  // W2 also keeps each row's output slot for the epilogue
   if (tid < kTokTile) {
     const int r = row0 + (tid < nrows ? tid : 0);
-    sTok[tid] = W13 ? a.sorted_pairs[r] / a.K : r;
+    const int pair = a.sorted_pairs[r];
+    sTok[tid] = W13 ? pair / a.K : r;
+    if (!W13) sSlot[W13 ? 0 : tid] = pair;
   }
   __syncthreads();
-  // activation scales of the whole tile (KS bytes per routed row): two threads per
-  // row, 32 steps each, every load issued before the first LDS store
-  {
+  // Activation scales of the whole tile (KS bytes per routed row) into rows of
+  // kSbRow bytes. Aligned rows: dword copies straight into LDS, issued with the
+  // prologue copies (instruction i of wave w covers LDS dwords 64(4i + w) .. +63, row
+  // = dword / 17; the 17th dword of a row and dwords past KS fetch bytes that are
+  // never read, and offsets past the tensor read zeros). Otherwise two threads per
+  // row load bytes, all loads issued before the first LDS store.
+  const v4i_s ras = rsrc4(a.act_s, a.act_s_bytes);
+  constexpr int kSbDw = kSbRow / 4;                       // 17 dwords per row
+  constexpr int kSbDma = (kTokTile * kSbDw + 255) / 256;  // dword copies per wave
+  auto issue_act_scales = [&]() {
+#pragma unroll
+    for (int i = 0; i < kSbDma; ++i) {
+      const int dw = 64 * (4 * i + wave) + lane;
+      const int row = min(dw / kSbDw, kTokTile - 1);
+      dma4(ras, lds_addr(sSb + 256 * (4 * i + wave)), sTok[row] * KS + 4 * (dw - (dw / kSbDw) * kSbDw), 0);
+    }
+  };
+  if (!a.act_s_dma) {
     const int r = tid >> 1, s0 = (tid & 1) * (kMaxKS / 2);
     const uint8_t* src = a.act_s + (int64_t)sTok[r] * KS;
     uint32_t v[kMaxKS / 8];
@@ -120,7 +143,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_large(LargeArgs a) {
       v[i] = w;
     }
 #pragma unroll
-    for (int i = 0; i < kMaxKS / 8; ++i) *reinterpret_cast<uint32_t*>(&sSb[r][s0 + 4 * i]) = v[i];
+    for (int i = 0; i < kMaxKS / 8; ++i) *reinterpret_cast<uint32_t*>(&sSb[r * kSbRow + s0 + 4 * i]) = v[i];
   }
 
   // Buffer resources of this expert's weights and scales and of the activations.
@@ -206,7 +229,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_large(LargeArgs a) {
   // weight scales: lane group q reads its K block's byte of the (row, step) dword
   // (fragment f, row c) -> group 2f + c/8, row c%8 of the group
   const uint8_t* pSa = &sSa[0][0][0] + (a_wave / 2048) * 2 * kSaGroup + (c >> 3) * kSaGroup + (c & 7) * 32 + q;
-  const uint8_t* pSb = &sSb[0][0] + (wm * 4 * 16 + c) * kSbRow;
+  const uint8_t* pSb = sSb + (wm * 4 * 16 + c) * kSbRow;
 
   // Operands of one K step in registers: this wave's 4 routed-row fragments (E4M3)
   // and 8 weight fragments (E2M1) with their E8M0 scales. They are read in 8
@@ -245,8 +268,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_large(LargeArgs a) {
       acc[i][j] = mfma_scale_16x16x128<kFmtE2M1, kFmtE4M3>(aop, o.b[j], acc[i][j], o.sa[i], o.sb[j]);
   };
 
-  // Prologue: weight scales of chunk 0 and part 0 of chunk 1, codes of stages 0
-  // and 1, operands of step 0.
+  // Prologue: activation scales (aligned rows), weight scales of chunk 0 and part 0
+  // of chunk 1, codes of stages 0 and 1, operands of step 0. A wave whose copies
+  // are all in LDS has no copies of its own left but those of stage 1, so after
+  // the barrier every copy but stage 1's has landed.
+  if (a.act_s_dma) issue_act_scales();
 #pragma unroll
   for (int m = 0; m < 4; ++m) issue_scales(0, m);
   issue_scales(1, 0);
@@ -345,7 +371,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_large(LargeArgs a) {
     for (int j = 0; j < 4; ++j) {
       const int row = 64 * wm + 16 * j + c;
       if (row < nrows) {
-        const int64_t slot = a.sorted_pairs[row0 + row];
+        const int64_t slot = sSlot[W13 ? 0 : row];
         float* dst = a.o + slot * a.H + nb * 256 + 128 * wn + q * 4;
 #pragma unroll
         for (int i = 0; i < 8; ++i)
@@ -368,9 +394,10 @@ hipError_t launch_w13_large(const moe_dims& d, const int2* items, const int32_t*
                             const uint8_t* x_s, const uint8_t* w13, const uint8_t* w13_s, uint8_t* h_q,
                             uint8_t* h_s, hipStream_t s) {
   if (max_items <= 0) return hipSuccess;
-  LargeArgs a{items, n_items, offsets, sorted_pairs, x_q,     x_s,
-              w13,   w13_s,   h_q,     h_s,          nullptr, (uint32_t)((int64_t)d.T * d.H),
-              d.H,   d.I,     d.K};
+  const int KS = d.H / 128;
+  LargeArgs a{items, n_items, offsets, sorted_pairs, x_q, x_s, w13, w13_s, h_q, h_s, nullptr,
+              (uint32_t)((int64_t)d.T * d.H), (uint32_t)((int64_t)d.T * KS),
+              KS % 4 == 0 && (uintptr_t)x_s % 4 == 0, d.H, d.I, d.K};
   hipLaunchKernelGGL(k_gemm_large<true>, dim3(d.I / 128, (unsigned)max_items), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
@@ -379,8 +406,11 @@ hipError_t launch_w2_large(const moe_dims& d, const int2* items, const int32_t* 
                            const int32_t* offsets, const int32_t* sorted_pairs, const uint8_t* h_q,
                            const uint8_t* h_s, const uint8_t* w2, const uint8_t* w2_s, float* o, hipStream_t s) {
   if (max_items <= 0) return hipSuccess;
+  const int KS = d.I / 128;
+  const int64_t P = (int64_t)d.T * d.K;
   LargeArgs a{items, n_items, offsets, sorted_pairs, h_q, h_s, w2, w2_s, nullptr, nullptr, o,
-              (uint32_t)((int64_t)d.T * d.K * d.I), d.H, d.I, d.K};
+              (uint32_t)(P * d.I), (uint32_t)(P * KS), KS % 4 == 0 && (uintptr_t)h_s % 4 == 0,
+              d.H, d.I, d.K};
   hipLaunchKernelGGL(k_gemm_large<false>, dim3(d.H / 256, (unsigned)max_items), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
