@@ -252,10 +252,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_dense(DenseArgs a) {
         uint8_t* dst = a.h_q + (int64_t)(t0 + row) * a.Is + nb * 128 + 64 * wn + q * 4;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          uint32_t packed = 0;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) packed |= e4m3_encode(acc[i][j][r] * inv) << (8 * r);
-          *reinterpret_cast<uint32_t*>(dst + 16 * i) = packed;
+          *reinterpret_cast<uint32_t*>(dst + 16 * i) =
+              e4m3_pack4(acc[i][j][0] * inv, acc[i][j][1] * inv, acc[i][j][2] * inv, acc[i][j][3] * inv);
         }
         if (wn == 0 && q == 0) a.h_s[(int64_t)(t0 + row) * (a.Is / 128) + nb] = (uint8_t)(ex + 127);
       }

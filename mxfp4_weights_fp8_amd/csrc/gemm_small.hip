@@ -248,10 +248,7 @@ __global__ __launch_bounds__(kThreads) void k_w13_small(
       uint8_t* dst = h_q + (int64_t)(row0 + c) * I + nb * 128 + wave * 32 + q * 4;
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
-        uint32_t packed = 0;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) packed |= e4m3_encode(h[g][j] * inv) << (8 * j);
-        *reinterpret_cast<uint32_t*>(dst + g * 16) = packed;
+        *reinterpret_cast<uint32_t*>(dst + g * 16) = e4m3_pack4(h[g][0] * inv, h[g][1] * inv, h[g][2] * inv, h[g][3] * inv);
       }
       if (wave == 0 && q == 0) h_s[(int64_t)(row0 + c) * (I / 128) + nb] = (uint8_t)(ex + 127);
     }

@@ -34,11 +34,8 @@ __global__ __launch_bounds__(kQuantThreads) void k_quant_act(const uint16_t* __r
     for (int m = 1; m < 16; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
     const int e = e8m0_exponent(amax);
     const float inv = exp2_neg(e);
-    uint32_t lo = 0, hi = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) lo |= e4m3_encode(v[i] * inv) << (8 * i);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) hi |= e4m3_encode(v[4 + i] * inv) << (8 * i);
+    const uint32_t lo = e4m3_pack4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
+    const uint32_t hi = e4m3_pack4(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv);
     *reinterpret_cast<uint2*>(x_q + base) = make_uint2(lo, hi);
     if (sub == 0) x_s[blk] = (uint8_t)(e + 127);
   }
