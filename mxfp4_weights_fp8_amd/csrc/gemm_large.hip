@@ -70,6 +70,7 @@ struct LargeArgs {
   uint32_t act_bytes;      // size of act
   uint32_t act_s_bytes;    // size of act_s
   int act_s_dma;           // act_s rows are 4-byte aligned: copy them with dword copies
+  int item_shift;          // 1: items hold 256 rows, workgroup y covers half y % 2 of item y / 2
   int H, I, K;
 };
 
@@ -83,13 +84,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_large(LargeArgs a) {
   __shared__ int sSlot[W13 ? 1 : kTokTile];
   __shared__ float sRed[2][kTokTile];
 
-  const int item = blockIdx.y;
+  const int item = blockIdx.y >> a.item_shift;
   if (item >= a.n_items[0]) return;
   const int2 it = a.items[item];
   const int e = it.x;
   const int e_begin = a.offsets[e], e_end = a.offsets[e + 1];
-  const int row0 = e_begin + it.y;                      // first sorted row of the tile
+  const int row0 = e_begin + it.y + (blockIdx.y & a.item_shift) * kTokTile;   // first sorted row of the tile
   const int nrows = min(kTokTile, e_end - row0);
+  if (nrows <= 0) return;                               // empty second half of a 256-row item
   const int nb = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4, c = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -388,28 +390,31 @@ bool large_path_supported(const moe_dims& d) {
 }
 
 hipError_t launch_w13_large(const moe_dims& d, const int2* items, const int32_t* n_items, int64_t max_items,
-                            const int32_t* offsets, const int32_t* sorted_pairs, const uint8_t* x_q,
-                            const uint8_t* x_s, const uint8_t* w13, const uint8_t* w13_s, uint8_t* h_q,
-                            uint8_t* h_s, hipStream_t s) {
+                            int item_rows, const int32_t* offsets, const int32_t* sorted_pairs,
+                            const uint8_t* x_q, const uint8_t* x_s, const uint8_t* w13, const uint8_t* w13_s,
+                            uint8_t* h_q, uint8_t* h_s, hipStream_t s) {
   if (max_items <= 0) return hipSuccess;
+  const int shift = item_rows == 2 * kTokTile ? 1 : 0;
   const int KS = d.H / 128;
   LargeArgs a{items, n_items, offsets, sorted_pairs, x_q, x_s, w13, w13_s, h_q, h_s, nullptr,
               (uint32_t)((int64_t)d.T * d.H), (uint32_t)((int64_t)d.T * KS),
-              KS % 4 == 0 && (uintptr_t)x_s % 4 == 0, d.H, d.I, d.K};
-  hipLaunchKernelGGL(k_gemm_large<true>, dim3(d.I / 128, (unsigned)max_items), dim3(kThreads), 0, s, a);
+              KS % 4 == 0 && (uintptr_t)x_s % 4 == 0, shift, d.H, d.I, d.K};
+  hipLaunchKernelGGL(k_gemm_large<true>, dim3(d.I / 128, (unsigned)(max_items << shift)), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_w2_large(const moe_dims& d, const int2* items, const int32_t* n_items, int64_t max_items,
-                           const int32_t* offsets, const int32_t* sorted_pairs, const uint8_t* h_q,
-                           const uint8_t* h_s, const uint8_t* w2, const uint8_t* w2_s, float* o, hipStream_t s) {
+                           int item_rows, const int32_t* offsets, const int32_t* sorted_pairs,
+                           const uint8_t* h_q, const uint8_t* h_s, const uint8_t* w2, const uint8_t* w2_s,
+                           float* o, hipStream_t s) {
   if (max_items <= 0) return hipSuccess;
+  const int shift = item_rows == 2 * kTokTile ? 1 : 0;
   const int KS = d.I / 128;
   const int64_t P = (int64_t)d.T * d.K;
   LargeArgs a{items, n_items, offsets, sorted_pairs, h_q, h_s, w2, w2_s, nullptr, nullptr, o,
               (uint32_t)(P * d.I), (uint32_t)(P * KS), KS % 4 == 0 && (uintptr_t)h_s % 4 == 0,
-              d.H, d.I, d.K};
-  hipLaunchKernelGGL(k_gemm_large<false>, dim3(d.H / 256, (unsigned)max_items), dim3(kThreads), 0, s, a);
+              shift, d.H, d.I, d.K};
+  hipLaunchKernelGGL(k_gemm_large<false>, dim3(d.H / 256, (unsigned)(max_items << shift)), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 

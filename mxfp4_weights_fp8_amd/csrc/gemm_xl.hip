@@ -1,0 +1,396 @@
+// Large-M grouped GEMMs on 256-row work items: 256 routed rows x 256 weight rows
+// per workgroup, on the gfx950 block-scaled MFMA v_mfma_scale_f32_16x16x128_f8f6f4.
+//
+// Prefill routing puts most routed rows in a few heavy experts ("Pushing the Limits
+// of Serving DeepSeek-V4-Pro", section 3.3), whose rows fill whole 256-row items;
+// the planner sends the remainder of each expert (1..128 rows) to the 128-row tile.
+// Per MFMA, a 256 x 256 tile moves 25% fewer bytes from L2 into LDS than a 256 x 128
+// tile (0.5 B per weight element and 1 B per routed-row element, each loaded once
+// per workgroup and K step) and reads 25% fewer operand bytes from LDS (each wave
+// owns 128 x 128 outputs).
+//
+// Waves: a 2 x 2 grid; wave (wm, wn) owns routed rows [128 wm, +128) (8 fragments
+// of 16, MFMA B side, E4M3) and 128 weight rows (8 fragments, MFMA A side, E2M1):
+//   W13: gate fragments 4wn..4wn+3 and up fragments 8+4wn.. of the tile's 128 gate
+//        rows [n0, n0+128) and 128 up rows [I+n0, I+n0+128), so one lane holds gate
+//        and up of the same h columns and the workgroup sees whole 128-column
+//        blocks for the fused FP8 requantization (same blog, section 4.3);
+//   W2:  output columns [128 wn, +128) of the tile's 256.
+// The 64 accumulator tiles of a wave (256 registers) live in the AGPR file; the
+// MFMAs are issued from inline asm with "+a" operands so that the compiler keeps
+// each tile in fixed AGPRs (its own register choice copied accumulators between
+// the register files inside the K loop).
+//
+// LDS (161792 bytes for W13, 162816 for W2):
+//   weights: two stages of two K steps (128 B of E2M1 per row and stage), 64 KB;
+//   routed rows: two buffers of one K step (128 B of E4M3 per row), 64 KB;
+//   weight E8M0 scales: three chunks of four K steps (16 B per row), 12 KB;
+//   activation scales of the whole tile: 68 B per routed row, 17 KB.
+// Rows are stored as 128-byte lines with the 16-byte chunk index XORed by
+// (row / 2) % 8, so that a fragment read hits every bank once per 16 lanes.
+//
+// Schedule of one K step s (per wave): 8 columns; column j issues the 8 MFMAs of
+// routed-row fragment j against the 8 weight fragments of step s, reads routed-row
+// fragment j+1 of step s (four rotating register buffers) and weight fragment j of
+// step s+1 (two register sets). After column 6 every wave has read all routed-row
+// fragments of step s, so a barrier there (M_s) frees that buffer; the copies
+// issued after M_{s-1} are exactly the ones needed after M_s, so each M_s waits
+// for all of this wave's copies:
+//   routed rows of step s+1 (into the buffer step s-1 used);
+//   for even s = 2k, weights of stage k+1 (into the buffer of stage k-1, last read
+//     while step 2k-2 ran);
+//   one quarter of weight-scale chunk (s+5)/4 (needed from the reads of step
+//     4*chunk, made while step 4*chunk-1 runs; its buffer held chunk-3).
+// Copies past the last step use a buffer resource of size 0 (they write zeros and
+// touch no memory), so the loop body has no branches.
+#include "device_common.h"
+#include "host_internal.h"
+#include "lds_copy.h"
+
+namespace moe {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kTok = kXlRows;            // routed rows per tile
+constexpr int kARows = 256;              // weight rows per tile
+constexpr int kStageA = kARows * 128;    // E2M1 codes of one weight stage (two K steps)
+constexpr int kStepB = kTok * 128;       // E4M3 codes of one K step
+constexpr int kChunkRow = 16;            // weight-scale bytes per row and chunk (four K steps)
+constexpr int kChunk = kARows * kChunkRow;
+constexpr int kMaxKS = 64;               // K steps whose activation scales fit in LDS
+constexpr int kSbRow = kMaxKS + 4;       // activation-scale bytes per routed row (17 dwords)
+constexpr int kSbBytes = kTok * kSbRow;  // a whole number of 256-byte copy blocks
+
+struct XlArgs {
+  const int2* items;
+  const int32_t* n_items;
+  const int32_t* offsets;
+  const int32_t* sorted_pairs;
+  const uint8_t* act;      // W13: x_q [T, H]; W2: h_q [P, I]
+  const uint8_t* act_s;    // scales of act
+  const uint8_t* w;        // W13 [E, 2I, H/2] or W2 [E, H, I/2]
+  const uint8_t* w_s;
+  uint8_t* h_q;            // W13 out
+  uint8_t* h_s;
+  float* o;                // W2 out
+  uint32_t act_bytes;      // size of act
+  uint32_t act_s_bytes;    // size of act_s
+  int act_s_dma;           // act_s rows are 4-byte aligned: copy them with dword copies
+  int H, I, K;
+};
+
+// acc += A (E2M1, 32 K values per lane) x B (E4M3) with E8M0 scales sa, sb (byte 0);
+// acc stays in AGPRs. The compiler does not know that the statement is an MFMA, so
+// it inserts no wait states after VALU writes of the operands: s_nop 4 provides
+// them (the MFMA pipe is busy with the previous MFMA meanwhile).
+__device__ __forceinline__ void mma_agpr(v4f& acc, const v4i& a, const v8i& b, int sa, int sb) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("s_nop 4\n\tv_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0] cbsz:4"
+               : "+a"(acc)
+               : "v"(a), "v"(b), "v"(sa), "v"(sb));
+#endif
+}
+
+struct AOps {     // one K step of this wave's 8 weight fragments
+  v4i w[8];
+  int sa[8];
+};
+
+template <bool W13>
+__global__ __launch_bounds__(kThreads, 1) void k_gemm_xl(XlArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint8_t sA[2][kStageA];   // [stage][row][128 B]
+  __shared__ __attribute__((aligned(1024))) uint8_t sB[2][kStepB];    // [step][row][128 B]
+  __shared__ __attribute__((aligned(16))) uint8_t sSa[3][kChunk];     // [chunk][row][16 B]
+  __shared__ __attribute__((aligned(16))) uint8_t sSb[kSbBytes];      // [row][kSbRow B]
+  __shared__ int sTok[kTok];
+  __shared__ int sSlot[W13 ? 1 : kTok];
+
+  const int item = blockIdx.y;
+  if (item >= a.n_items[0]) return;
+  const int2 it = a.items[item];
+  const int e = it.x;
+  const int e_begin = a.offsets[e], e_end = a.offsets[e + 1];
+  const int row0 = e_begin + it.y;                      // first sorted row of the tile
+  const int nrows = min(kTok, e_end - row0);
+  const int nb = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4, c = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave & 1, wn = wave >> 1;
+
+  const int Kdim = W13 ? a.H : a.I;                     // reduction length
+  const int N = W13 ? 2 * a.I : a.H;                    // weight rows per expert
+  const int KS = Kdim / 128;                            // K steps (even)
+  const int wrow = Kdim / 2, srow = Kdim / 32, arow = Kdim;
+
+  // routed rows of the tile -> activation row (padding repeats the first row); W2
+  // also keeps each row's output slot
+  {
+    const int r = row0 + (tid < nrows ? tid : 0);
+    const int pair = a.sorted_pairs[r];
+    sTok[tid] = W13 ? pair / a.K : r;
+    if (!W13) sSlot[W13 ? 0 : tid] = pair;
+  }
+  __syncthreads();
+
+  const v4i_s rw = rsrc4(a.w + (int64_t)e * N * wrow, (uint32_t)(N * wrow));
+  const v4i_s rws = rsrc4(a.w_s + (int64_t)e * N * srow, (uint32_t)(N * srow));
+  const v4i_s ra = rsrc4(a.act, a.act_bytes);
+  const v4i_s ras = rsrc4(a.act_s, a.act_s_bytes);
+
+  // Activation scales: aligned rows by dword copies (instruction i of wave w covers
+  // LDS dwords 64(4i + w) .. +63 of the table, row = dword / 17; the 17th dword of a
+  // row and dwords past KS fetch bytes that are never read, offsets past the tensor
+  // read zeros); otherwise one thread per row loads bytes.
+  constexpr int kSbDw = kSbRow / 4;
+  constexpr int kSbDma = kSbBytes / 1024;               // dword copies per wave
+  if (a.act_s_dma) {
+#pragma unroll
+    for (int i = 0; i < kSbDma; ++i) {
+      const int dw = 64 * (4 * i + wave) + lane;
+      const int row = dw / kSbDw;
+      dma4(ras, lds_addr(sSb + 256 * (4 * i + wave)), sTok[row] * KS + 4 * (dw - row * kSbDw), 0);
+    }
+  } else {
+    const uint8_t* src = a.act_s + (int64_t)sTok[tid] * KS;
+    uint32_t v[kMaxKS / 4];
+#pragma unroll
+    for (int i = 0; i < kMaxKS / 4; ++i) {
+      uint32_t w = 0;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int st = 4 * i + b;
+        const uint32_t byte = src[min(st, KS - 1)];    // unconditional load, masked below
+        w |= (st < KS ? byte : 0u) << (8 * b);
+      }
+      v[i] = w;
+    }
+#pragma unroll
+    for (int i = 0; i < kMaxKS / 4; ++i) *reinterpret_cast<uint32_t*>(&sSb[tid * kSbRow + 4 * i]) = v[i];
+  }
+
+  // expert weight row of LDS row r (0..255): fragments of 16 rows
+  auto w_row = [&](int r) -> int {
+    const int f = r >> 4;
+    if (W13) return (f < 8 ? 0 : a.I) + nb * 128 + (f & 7) * 16 + (r & 15);
+    return nb * 256 + r;
+  };
+  // Copy plans (per wave). Weights and routed rows: instruction i moves LDS rows
+  // 64*wave + 8i .. +7, lane l -> row +l/8, physical chunk l%8 holding logical chunk
+  // (l%8) ^ s(row), s(row) = (row / 2) % 8 = 4 (i % 2) + l / 16. The 64 weight rows a
+  // wave copies are consecutive expert rows, so instruction i adds 8i rows to one
+  // lane offset; routed rows take one lane offset each. Weight scales: instruction i
+  // moves rows 64*wave + 16i .. +15, lane l -> row +l/4, dword l%4 of the chunk.
+  const int r_lane = 64 * wave + (lane >> 3);
+  const int sw0 = ((lane & 7) ^ (lane >> 4)) << 4;
+  const int sw1 = ((lane & 7) ^ (4 | (lane >> 4))) << 4;
+  const int dA = w_row(r_lane) * wrow;
+  const int dS = w_row(64 * wave + (lane >> 2)) * srow + (lane & 3) * 4;
+  int dB[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) dB[i] = sTok[64 * wave + 8 * i + (lane >> 3)] * arow + ((i & 1) ? sw1 : sw0);
+
+  auto copy_w = [&](int stage, int i) {   // weight stage (K steps 2 stage, 2 stage + 1), instruction i
+    dma16(rsrc_sized(rw, 2 * stage < KS), lds_addr(&sA[stage & 1][(64 * wave + 8 * i) * 128]),
+          dA + ((i & 1) ? sw1 : sw0) + 8 * i * wrow + stage * 128, 0);
+  };
+  auto copy_t = [&](int step, int i) {    // routed rows of K step `step`, instruction i
+    dma16(rsrc_sized(ra, step < KS), lds_addr(&sB[step & 1][(64 * wave + 8 * i) * 128]), dB[i] + step * 128, 0);
+  };
+  auto copy_s = [&](int chunk, int i) {   // weight scales of K steps 4 chunk .. +3, instruction i
+    dma4(rsrc_sized(rws, 4 * chunk < KS), lds_addr(&sSa[chunk % 3][(64 * wave + 16 * i) * kChunkRow]),
+         dS + 16 * i * srow + chunk * kChunkRow, 0);
+  };
+
+  // Prologue: scale chunk 0 and quarter 0 of chunk 1, weight stage 0, routed rows
+  // of step 0; then (after M_{-1}) the first half of window 0.
+#pragma unroll
+  for (int i = 0; i < 4; ++i) copy_s(0, i);
+  copy_s(1, 0);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) copy_w(0, i);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) copy_t(0, i);
+  wait_vmcnt<0>();
+  __syncthreads();
+
+  // LDS byte offsets of the operand reads (fragment rows are multiples of 16, so
+  // row c of a fragment has swizzle (c / 2) % 8): chunk q and chunk 4 + q of a row.
+  const int off0 = c * 128 + ((q ^ (c >> 1)) << 4);
+  const int off1 = c * 128 + (((4 + q) ^ (c >> 1)) << 4);
+  auto a_row = [&](int i) {   // first LDS row of this wave's weight fragment i
+    return W13 ? (i < 4 ? 64 * wn + 16 * i : 128 + 64 * wn + 16 * (i - 4)) : 128 * wn + 16 * i;
+  };
+  const uint8_t* pB = &sB[0][0] + 128 * wm * 128;                 // + buffer, fragment
+  const uint8_t* pSb = sSb + (128 * wm + c) * kSbRow;             // + 16 j kSbRow + step
+  const uint8_t* pSa = &sSa[0][0] + c * kChunkRow + q;            // + chunk buffer, a_row(i) * 16, (step % 4) * 4
+
+  auto read_a = [&](AOps& o, int step, int i) {   // weight fragment i of K step `step`
+    const uint8_t* base = &sA[(step >> 1) & 1][0] + a_row(i) * 128;
+    o.w[i] = *reinterpret_cast<const v4i*>(base + ((step & 1) ? off1 : off0));
+    o.sa[i] = pSa[((step >> 2) % 3) * kChunk + a_row(i) * kChunkRow + (step & 3) * 4];
+  };
+  v8i bf[4];
+  int bs[4];
+  auto read_b = [&](int step, int j, int slot) {  // routed-row fragment j of K step `step`
+    const uint8_t* base = pB + (step & 1) * kStepB + j * 2048;
+    const v4i lo = *reinterpret_cast<const v4i*>(base + off0);
+    const v4i hi = *reinterpret_cast<const v4i*>(base + off1);
+    bf[slot][0] = lo[0]; bf[slot][1] = lo[1]; bf[slot][2] = lo[2]; bf[slot][3] = lo[3];
+    bf[slot][4] = hi[0]; bf[slot][5] = hi[1]; bf[slot][6] = hi[2]; bf[slot][7] = hi[3];
+    bs[slot] = pSb[16 * j * kSbRow + step];
+  };
+
+  v4f acc[8][8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  AOps ops[2];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) read_a(ops[0], 0, i);
+  read_b(0, 0, 0);
+  // first part of window 0 (normally issued in column 7 of the previous step)
+#pragma unroll
+  for (int i = 0; i < 8; ++i) copy_t(1, i);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) copy_w(1, i);
+
+  // One K step. P = s & 1 (register set of step s), s even issues the weight copies.
+  auto step = [&](const int s, AOps& cur, AOps& nxt, const bool even) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (j < 7) read_b(s, j + 1, (j + 1) & 3);
+      else read_b(s + 1, 0, 0);          // after M_s: routed rows of step s+1 are in LDS
+      read_a(nxt, min(s + 1, KS - 1), j);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) mma_agpr(acc[i][j], cur.w[i], bf[j & 3], cur.sa[i], bs[j & 3]);
+      // window s (deadline M_s): second part; window s+1: first part after M_s
+      if (j < 4 && even) copy_w(s / 2 + 1, 4 + j);
+      if (j == 0) copy_s((s + 5) >> 2, (s + 5) & 3);
+      if (j == 7) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) copy_t(s + 2, i);
+        if (!even) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) copy_w((s + 1) / 2 + 1, i);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if (j == 6) {                      // M_s
+        wait_vmcnt<0>();
+        __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+
+  for (int s = 0; s < KS; s += 2) {
+    step(s, ops[0], ops[1], true);
+    step(s + 1, ops[1], ops[0], false);
+  }
+  wait_vmcnt<0>();
+  // The compiler does not see the MFMAs in the asm statements, so it inserts no wait
+  // states before the accumulators are read: 64 of them here, with scheduling
+  // barriers so that no read moves above.
+  __builtin_amdgcn_sched_barrier(0);
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+#endif
+  __builtin_amdgcn_sched_barrier(0);
+
+  if (W13) {
+    // SwiGLU + FP8 requantization. Lane (c, q) of routed-row fragment j holds h
+    // columns 64wn + 16i + 4q .. +3 (i = 0..3: gate acc[i], up acc[4+i]) of tile row
+    // 128wm + 16j + c. The two waves sharing a row exchange their amax in LDS (the
+    // routed-row buffers are free once every copy has landed).
+    __syncthreads();
+    float* sRed = reinterpret_cast<float*>(&sB[0][0]);          // [2 halves][2 waves][kTok]
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {    // routed-row fragments 4 half .. +3
+      float hv[4][4][4];
+      float amax[4];
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int j = 4 * half + jj;
+        float m = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float h = silu_mul(acc[i][j][r], acc[4 + i][j][r]);
+            hv[jj][i][r] = h;
+            m = fmaxf(m, fabsf(h));
+          }
+        m = fmaxf(m, __shfl_xor(m, 16));
+        m = fmaxf(m, __shfl_xor(m, 32));
+        amax[jj] = m;
+      }
+      float* red = sRed + half * 2 * kTok;
+      if (q == 0) {
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) red[wn * kTok + 128 * wm + 16 * (4 * half + jj) + c] = amax[jj];
+      }
+      __syncthreads();
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int row = 128 * wm + 16 * (4 * half + jj) + c;
+        const float m = fmaxf(red[row], red[kTok + row]);
+        const int ex = e8m0_exponent(m);
+        const float inv = exp2_neg(ex);
+        if (row < nrows) {
+          uint8_t* dst = a.h_q + (int64_t)(row0 + row) * a.I + nb * 128 + 64 * wn + q * 4;
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            *reinterpret_cast<uint32_t*>(dst + 16 * i) =
+                e4m3_pack4(hv[jj][i][0] * inv, hv[jj][i][1] * inv, hv[jj][i][2] * inv, hv[jj][i][3] * inv);
+          if (wn == 0 && q == 0) a.h_s[(int64_t)(row0 + row) * (a.I / 128) + nb] = (uint8_t)(ex + 127);
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int row = 128 * wm + 16 * j + c;
+      if (row < nrows) {
+        const int64_t slot = sSlot[W13 ? 0 : row];
+        float* dst = a.o + slot * a.H + nb * 256 + 128 * wn + q * 4;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          *reinterpret_cast<float4*>(dst + 16 * i) = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+      }
+    }
+  }
+}
+
+}  // namespace
+
+bool xl13_supported(const moe_dims& d) { return large_path_supported(d) && (d.H / 128) % 2 == 0; }
+bool xl2_supported(const moe_dims& d) { return large_path_supported(d) && (d.I / 128) % 2 == 0; }
+
+hipError_t launch_w13_xl(const moe_dims& d, const int2* items, const int32_t* n_items, int64_t max_items,
+                         const int32_t* offsets, const int32_t* sorted_pairs, const uint8_t* x_q,
+                         const uint8_t* x_s, const uint8_t* w13, const uint8_t* w13_s, uint8_t* h_q,
+                         uint8_t* h_s, hipStream_t s) {
+  if (max_items <= 0) return hipSuccess;
+  const int KS = d.H / 128;
+  XlArgs a{items, n_items, offsets, sorted_pairs, x_q, x_s, w13, w13_s, h_q, h_s, nullptr,
+           (uint32_t)((int64_t)d.T * d.H), (uint32_t)((int64_t)d.T * KS),
+           KS % 4 == 0 && (uintptr_t)x_s % 4 == 0, d.H, d.I, d.K};
+  hipLaunchKernelGGL(k_gemm_xl<true>, dim3(d.I / 128, (unsigned)max_items), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_w2_xl(const moe_dims& d, const int2* items, const int32_t* n_items, int64_t max_items,
+                        const int32_t* offsets, const int32_t* sorted_pairs, const uint8_t* h_q,
+                        const uint8_t* h_s, const uint8_t* w2, const uint8_t* w2_s, float* o, hipStream_t s) {
+  if (max_items <= 0) return hipSuccess;
+  const int KS = d.I / 128;
+  const int64_t P = (int64_t)d.T * d.K;
+  XlArgs a{items, n_items, offsets, sorted_pairs, h_q, h_s, w2, w2_s, nullptr, nullptr, o,
+           (uint32_t)(P * d.I), (uint32_t)(P * KS), KS % 4 == 0 && (uintptr_t)h_s % 4 == 0, d.H, d.I, d.K};
+  hipLaunchKernelGGL(k_gemm_xl<false>, dim3(d.H / 256, (unsigned)max_items), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -14,6 +14,7 @@ namespace moe {
 constexpr int kSmallRows = 16;       // rows per small-M tile (MFMA N side)
 constexpr int kDefaultSmallMax = 16; // experts with <= this many pairs take the small-M path
 constexpr int kLargeRows = 128;      // rows per large-M tile
+constexpr int kXlRows = 256;         // rows per extra-large (256 x 256) large-M tile
 constexpr int kPlanChunk = 2048;     // pairs per route-planner block
 constexpr int kMaxExperts = 4096;
 constexpr int kMaxTopK = 64;
@@ -32,25 +33,31 @@ inline int64_t small_items_bound(const moe_dims& d) {
   // each small expert (1 <= M <= sm) yields ceil(M / kSmallRows) tiles
   return sm <= kSmallRows ? experts : experts + P / kSmallRows;
 }
-inline int64_t large_items_bound(const moe_dims& d) {
+// Experts with more than small_max pairs split into 256-row items (the last one
+// when more than 128 rows remain) and at most one 128-row item (a remainder of
+// 1..128 rows).
+inline int64_t big_experts_bound(const moe_dims& d) {
   int64_t P = (int64_t)d.T * d.K;
-  int64_t sm = small_max_of(d);
-  int64_t big = P / (sm + 1);            // experts with more than sm pairs
-  if (big > d.E) big = d.E;
-  return P / kLargeRows + big;
+  int64_t big = P / (small_max_of(d) + 1);   // experts with more than small_max pairs
+  return big > d.E ? d.E : big;
+}
+inline int64_t large_items_bound(const moe_dims& d) { return big_experts_bound(d); }
+inline int64_t xl_items_bound(const moe_dims& d) {
+  return (int64_t)d.T * d.K / kXlRows + big_experts_bound(d);
 }
 
 // ---------------------------------------------------------------- plan workspace
 // int32 header, then the two tile lists (int2 = {expert, first row}), then the
 // planner's per-block scratch.
 struct PlanWs {
-  int32_t* hdr;           // [0] small item count, [1] large item count
+  int32_t* hdr;           // [0] small, [1] 128-row large, [2] 256-row large item counts
   int2* small_items;
-  int2* large_items;
+  int2* large_items;      // 128-row items
+  int2* xl_items;         // 256-row items
   int32_t* local_rank;    // [P]
   int32_t* block_counts;  // [NB * E]
   int32_t* block_base;    // [NB * E]
-  int64_t small_cap, large_cap, nb;
+  int64_t small_cap, large_cap, xl_cap, nb;
 };
 size_t plan_ws_layout(const moe_dims& d, void* base, PlanWs* out);
 
@@ -80,14 +87,28 @@ hipError_t launch_w2_small(const moe_dims& d, const int2* items, const int32_t* 
                            int item_rows, const int32_t* offsets, const int32_t* sorted_pairs,
                            const uint8_t* h_q, const uint8_t* h_s, const uint8_t* w2, const uint8_t* w2_s,
                            float* o, hipStream_t s);
+// 128-row large-M tiles; item_rows 128 or 256 (a 256-row item runs as two
+// 128-row workgroups).
 bool large_path_supported(const moe_dims& d);
 hipError_t launch_w13_large(const moe_dims& d, const int2* items, const int32_t* n_items, int64_t max_items,
-                            const int32_t* offsets, const int32_t* sorted_pairs, const uint8_t* x_q,
-                            const uint8_t* x_s, const uint8_t* w13, const uint8_t* w13_s, uint8_t* h_q,
-                            uint8_t* h_s, hipStream_t s);
+                            int item_rows, const int32_t* offsets, const int32_t* sorted_pairs,
+                            const uint8_t* x_q, const uint8_t* x_s, const uint8_t* w13, const uint8_t* w13_s,
+                            uint8_t* h_q, uint8_t* h_s, hipStream_t s);
 hipError_t launch_w2_large(const moe_dims& d, const int2* items, const int32_t* n_items, int64_t max_items,
-                           const int32_t* offsets, const int32_t* sorted_pairs, const uint8_t* h_q,
-                           const uint8_t* h_s, const uint8_t* w2, const uint8_t* w2_s, float* o, hipStream_t s);
+                           int item_rows, const int32_t* offsets, const int32_t* sorted_pairs,
+                           const uint8_t* h_q, const uint8_t* h_s, const uint8_t* w2, const uint8_t* w2_s,
+                           float* o, hipStream_t s);
+// 256 x 256 large-M tiles on 256-row items (an even K-step count and the
+// large-M shape limits).
+bool xl13_supported(const moe_dims& d);
+bool xl2_supported(const moe_dims& d);
+hipError_t launch_w13_xl(const moe_dims& d, const int2* items, const int32_t* n_items, int64_t max_items,
+                         const int32_t* offsets, const int32_t* sorted_pairs, const uint8_t* x_q,
+                         const uint8_t* x_s, const uint8_t* w13, const uint8_t* w13_s, uint8_t* h_q,
+                         uint8_t* h_s, hipStream_t s);
+hipError_t launch_w2_xl(const moe_dims& d, const int2* items, const int32_t* n_items, int64_t max_items,
+                        const int32_t* offsets, const int32_t* sorted_pairs, const uint8_t* h_q,
+                        const uint8_t* h_s, const uint8_t* w2, const uint8_t* w2_s, float* o, hipStream_t s);
 // Dense FP8 shared expert: W13s + SwiGLU/requant into sh_q/sh_s, then W2s into
 // fp32 rows so [T, H]. Needs H/128 and Is/128 at most 64.
 bool dense_path_supported(const moe_dims& d);

@@ -133,11 +133,22 @@ int moe_ffn(const moe_dims* dims, const uint16_t* x, const float* topk_weights, 
   err = launch_w13_small(d, pw.small_items, pw.hdr + 0, pw.small_cap, kSmallRows, expert_offsets, sorted_pairs,
                          x_q, x_s, w13, w13_s, h_q, h_s, s);
   if (err != hipSuccess) return MOE_EHIP;
+  // large experts: 256-row items, then the 128-row remainders
   const bool large = large_path_supported(d);
+  if (large && xl13_supported(d))
+    err = launch_w13_xl(d, pw.xl_items, pw.hdr + 2, pw.xl_cap, expert_offsets, sorted_pairs, x_q, x_s, w13, w13_s,
+                        h_q, h_s, s);
+  else if (large)
+    err = launch_w13_large(d, pw.xl_items, pw.hdr + 2, pw.xl_cap, kXlRows, expert_offsets, sorted_pairs, x_q, x_s,
+                           w13, w13_s, h_q, h_s, s);
+  else   // shapes the large-M tiles do not cover: the small-M kernel walks the items
+    err = launch_w13_small(d, pw.xl_items, pw.hdr + 2, pw.xl_cap, kXlRows, expert_offsets, sorted_pairs, x_q, x_s,
+                           w13, w13_s, h_q, h_s, s);
+  if (err != hipSuccess) return MOE_EHIP;
   if (large)
-    err = launch_w13_large(d, pw.large_items, pw.hdr + 1, pw.large_cap, expert_offsets, sorted_pairs, x_q, x_s, w13,
-                           w13_s, h_q, h_s, s);
-  else   // shapes the large-M tiles do not cover: run the small-M kernel over 128-row items
+    err = launch_w13_large(d, pw.large_items, pw.hdr + 1, pw.large_cap, kLargeRows, expert_offsets, sorted_pairs,
+                           x_q, x_s, w13, w13_s, h_q, h_s, s);
+  else
     err = launch_w13_small(d, pw.large_items, pw.hdr + 1, pw.large_cap, kLargeRows, expert_offsets, sorted_pairs,
                            x_q, x_s, w13, w13_s, h_q, h_s, s);
   if (err != hipSuccess) return MOE_EHIP;
@@ -146,9 +157,19 @@ int moe_ffn(const moe_dims* dims, const uint16_t* x, const float* topk_weights, 
   err = launch_w2_small(d, pw.small_items, pw.hdr + 0, pw.small_cap, kSmallRows, expert_offsets, sorted_pairs, h_q,
                         h_s, w2, w2_s, fw.o, s);
   if (err != hipSuccess) return MOE_EHIP;
+  if (large && xl2_supported(d))
+    err = launch_w2_xl(d, pw.xl_items, pw.hdr + 2, pw.xl_cap, expert_offsets, sorted_pairs, h_q, h_s, w2, w2_s,
+                       fw.o, s);
+  else if (large)
+    err = launch_w2_large(d, pw.xl_items, pw.hdr + 2, pw.xl_cap, kXlRows, expert_offsets, sorted_pairs, h_q, h_s,
+                          w2, w2_s, fw.o, s);
+  else
+    err = launch_w2_small(d, pw.xl_items, pw.hdr + 2, pw.xl_cap, kXlRows, expert_offsets, sorted_pairs, h_q, h_s,
+                          w2, w2_s, fw.o, s);
+  if (err != hipSuccess) return MOE_EHIP;
   if (large)
-    err = launch_w2_large(d, pw.large_items, pw.hdr + 1, pw.large_cap, expert_offsets, sorted_pairs, h_q, h_s, w2,
-                          w2_s, fw.o, s);
+    err = launch_w2_large(d, pw.large_items, pw.hdr + 1, pw.large_cap, kLargeRows, expert_offsets, sorted_pairs,
+                          h_q, h_s, w2, w2_s, fw.o, s);
   else
     err = launch_w2_small(d, pw.large_items, pw.hdr + 1, pw.large_cap, kLargeRows, expert_offsets, sorted_pairs,
                           h_q, h_s, w2, w2_s, fw.o, s);

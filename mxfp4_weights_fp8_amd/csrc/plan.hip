@@ -93,11 +93,13 @@ __device__ void local_ranks(const int32_t* __restrict__ ids, int begin, int end,
 }
 
 // Work lists from per-expert counts cnt[E] (LDS): small-M tiles of kSmallRows rows
-// for experts with 1..small_max pairs (expert order), large-M tiles of kLargeRows
-// rows for the rest, heaviest expert first (ties: lower id first).
+// for experts with 1..small_max pairs (expert order); the rest, heaviest expert
+// first (ties: lower id first), in 256-row items (the last one when more than 128
+// rows remain) and a 128-row item for a remainder of 1..128 rows.
 __device__ void build_worklists(const int32_t* cnt, int E, int small_max, int2* __restrict__ small_items,
                                 int64_t small_cap, int2* __restrict__ large_items, int64_t large_cap,
-                                int32_t* __restrict__ hdr, int32_t* a1, int32_t* a2, int32_t* part) {
+                                int2* __restrict__ xl_items, int64_t xl_cap, int32_t* __restrict__ hdr,
+                                int32_t* a1, int32_t* a2, int32_t* part) {
   const int t = threadIdx.x, nt = blockDim.x;
   for (int e = t; e < E; e += nt) {
     const int m = cnt[e];
@@ -129,17 +131,31 @@ __device__ void build_worklists(const int32_t* cnt, int E, int small_max, int2* 
   for (int e = t; e < E; e += nt) a1[e] = cnt[e] > small_max ? 1 : 0;
   __syncthreads();
   const int n_big = block_exclusive_scan(a1, E, part);
-  for (int r = t; r < E; r += nt) a1[r] = r < n_big ? (cnt[a2[r]] + kLargeRows - 1) / kLargeRows : 0;
+  // 256-row items
+  for (int r = t; r < E; r += nt) a1[r] = r < n_big ? (cnt[a2[r]] + kXlRows / 2 - 1) / kXlRows : 0;
+  __syncthreads();
+  const int n_xl = block_exclusive_scan(a1, E, part);
+  for (int r = t; r < n_big; r += nt) {
+    const int e = a2[r], m = cnt[e], s = a1[r];
+    for (int i = 0; i < (m + kXlRows / 2 - 1) / kXlRows; ++i)
+      if (s + i < xl_cap) xl_items[s + i] = make_int2(e, i * kXlRows);
+  }
+  __syncthreads();
+  // 128-row remainders
+  for (int r = t; r < E; r += nt) {
+    const int m = r < n_big ? cnt[a2[r]] : 0, rem = m % kXlRows;
+    a1[r] = (rem >= 1 && rem <= kXlRows / 2) ? 1 : 0;
+  }
   __syncthreads();
   const int n_large = block_exclusive_scan(a1, E, part);
   for (int r = t; r < n_big; r += nt) {
-    const int e = a2[r], m = cnt[e], s = a1[r];
-    for (int i = 0; i * kLargeRows < m; ++i)
-      if (s + i < large_cap) large_items[s + i] = make_int2(e, i * kLargeRows);
+    const int e = a2[r], m = cnt[e], rem = m % kXlRows;
+    if (rem >= 1 && rem <= kXlRows / 2 && a1[r] < large_cap) large_items[a1[r]] = make_int2(e, m - rem);
   }
   if (t == 0) {
     hdr[0] = n_small < small_cap ? n_small : (int)small_cap;
     hdr[1] = n_large < large_cap ? n_large : (int)large_cap;
+    hdr[2] = n_xl < xl_cap ? n_xl : (int)xl_cap;
   }
 }
 
@@ -152,10 +168,11 @@ struct PlanArgs {
   int32_t* hdr;
   int2* small_items;
   int2* large_items;
+  int2* xl_items;
   int32_t* local_rank;
   int32_t* block_counts;
   int32_t* block_base;
-  int64_t small_cap, large_cap;
+  int64_t small_cap, large_cap, xl_cap;
   int P, E, nbits, small_max, nb;
 };
 
@@ -193,8 +210,8 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan_fused(PlanArgs a) {
     }
     if (p >= n_valid) a.sorted_pairs[p] = -1;
   }
-  build_worklists(cnt, E, a.small_max, a.small_items, a.small_cap, a.large_items, a.large_cap, a.hdr, a1, a2,
-                  part);
+  build_worklists(cnt, E, a.small_max, a.small_items, a.small_cap, a.large_items, a.large_cap, a.xl_items, a.xl_cap,
+                  a.hdr, a1, a2, part);
 }
 
 // Multi-block phase 1.
@@ -242,8 +259,8 @@ __global__ __launch_bounds__(kScanThreads) void k_plan_scan(PlanArgs a) {
   for (int e = t; e <= E; e += kScanThreads) a.offsets[e] = off[e];
   for (int e = t; e < E; e += kScanThreads)
     for (int b = 0; b < nb; ++b) a.block_base[(int64_t)b * E + e] += off[e];
-  build_worklists(cnt, E, a.small_max, a.small_items, a.small_cap, a.large_items, a.large_cap, a.hdr, a1, a2,
-                  part);
+  build_worklists(cnt, E, a.small_max, a.small_items, a.small_cap, a.large_items, a.large_cap, a.xl_items, a.xl_cap,
+                  a.hdr, a1, a2, part);
 }
 
 // Multi-block phase 3.
@@ -266,7 +283,7 @@ __global__ __launch_bounds__(256) void k_plan_scatter(PlanArgs a) {
 size_t plan_ws_layout(const moe_dims& d, void* base, PlanWs* out) {
   const int64_t P = (int64_t)d.T * d.K;
   const int64_t nb = ceil_div(P, kPlanChunk) < 1 ? 1 : ceil_div(P, kPlanChunk);
-  const int64_t sc = small_items_bound(d), lc = large_items_bound(d);
+  const int64_t sc = small_items_bound(d), lc = large_items_bound(d), xc = xl_items_bound(d);
   size_t off = 0;
   auto take = [&](size_t bytes) {
     size_t o = off;
@@ -276,6 +293,7 @@ size_t plan_ws_layout(const moe_dims& d, void* base, PlanWs* out) {
   const size_t o_hdr = take(64);
   const size_t o_small = take(sizeof(int2) * (size_t)(sc > 0 ? sc : 1));
   const size_t o_large = take(sizeof(int2) * (size_t)(lc > 0 ? lc : 1));
+  const size_t o_xl = take(sizeof(int2) * (size_t)(xc > 0 ? xc : 1));
   const size_t o_rank = take(sizeof(int32_t) * (size_t)(P > 0 ? P : 1));
   const size_t o_bc = take(sizeof(int32_t) * (size_t)(nb * d.E));
   const size_t o_bb = take(sizeof(int32_t) * (size_t)(nb * d.E));
@@ -284,11 +302,13 @@ size_t plan_ws_layout(const moe_dims& d, void* base, PlanWs* out) {
     out->hdr = reinterpret_cast<int32_t*>(b + o_hdr);
     out->small_items = reinterpret_cast<int2*>(b + o_small);
     out->large_items = reinterpret_cast<int2*>(b + o_large);
+    out->xl_items = reinterpret_cast<int2*>(b + o_xl);
     out->local_rank = reinterpret_cast<int32_t*>(b + o_rank);
     out->block_counts = reinterpret_cast<int32_t*>(b + o_bc);
     out->block_base = reinterpret_cast<int32_t*>(b + o_bb);
     out->small_cap = sc;
     out->large_cap = lc;
+    out->xl_cap = xc;
     out->nb = nb;
   }
   return off;
@@ -305,11 +325,13 @@ hipError_t launch_plan(const moe_dims& d, const int32_t* ids, int32_t* offsets, 
   a.hdr = ws.hdr;
   a.small_items = ws.small_items;
   a.large_items = ws.large_items;
+  a.xl_items = ws.xl_items;
   a.local_rank = ws.local_rank;
   a.block_counts = ws.block_counts;
   a.block_base = ws.block_base;
   a.small_cap = ws.small_cap;
   a.large_cap = ws.large_cap;
+  a.xl_cap = ws.xl_cap;
   a.P = d.T * d.K;
   a.E = d.E;
   int nbits = 0;
