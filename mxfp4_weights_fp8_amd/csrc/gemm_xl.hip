@@ -47,6 +47,8 @@
 #include "host_internal.h"
 #include "lds_copy.h"
 
+#include <type_traits>
+
 namespace moe {
 namespace {
 
@@ -79,15 +81,25 @@ struct XlArgs {
   int H, I, K;
 };
 
-// acc += A (E2M1, 32 K values per lane) x B (E4M3) with E8M0 scales sa, sb (byte 0);
-// acc stays in AGPRs. The compiler does not know that the statement is an MFMA, so
-// it inserts no wait states after VALU writes of the operands: s_nop 4 provides
-// them (the MFMA pipe is busy with the previous MFMA meanwhile).
+// acc += A (E2M1, 32 K values per lane) x B (E4M3) with E8M0 scales: byte 0 of sa,
+// byte OB of sb (op_sel); acc stays in AGPRs. The compiler does not know that the
+// statement is an MFMA, so it inserts no wait states after VALU writes of the
+// operands: s_nop 4 provides them (the MFMA pipe is busy with the previous MFMA).
+template <int OB>
 __device__ __forceinline__ void mma_agpr(v4f& acc, const v4i& a, const v8i& b, int sa, int sb) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  asm volatile("s_nop 4\n\tv_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0] cbsz:4"
-               : "+a"(acc)
-               : "v"(a), "v"(b), "v"(sa), "v"(sb));
+  if constexpr (OB == 0)
+    asm volatile("s_nop 4\n\tv_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0] cbsz:4"
+                 : "+a"(acc) : "v"(a), "v"(b), "v"(sa), "v"(sb));
+  else if constexpr (OB == 1)
+    asm volatile("s_nop 4\n\tv_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel:[0,1,0] op_sel_hi:[0,0,0] cbsz:4"
+                 : "+a"(acc) : "v"(a), "v"(b), "v"(sa), "v"(sb));
+  else if constexpr (OB == 2)
+    asm volatile("s_nop 4\n\tv_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,1,0] cbsz:4"
+                 : "+a"(acc) : "v"(a), "v"(b), "v"(sa), "v"(sb));
+  else
+    asm volatile("s_nop 4\n\tv_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel:[0,1,0] op_sel_hi:[0,1,0] cbsz:4"
+                 : "+a"(acc) : "v"(a), "v"(b), "v"(sa), "v"(sb));
 #endif
 }
 
@@ -119,7 +131,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_xl(XlArgs a) {
 
   const int Kdim = W13 ? a.H : a.I;                     // reduction length
   const int N = W13 ? 2 * a.I : a.H;                    // weight rows per expert
-  const int KS = Kdim / 128;                            // K steps (even)
+  const int KS = Kdim / 128;                            // K steps (a multiple of 4)
   const int wrow = Kdim / 2, srow = Kdim / 32, arow = Kdim;
 
   // routed rows of the tile -> activation row (padding repeats the first row); W2
@@ -176,29 +188,33 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_xl(XlArgs a) {
   };
   // Copy plans (per wave). Weights and routed rows: instruction i moves LDS rows
   // 64*wave + 8i .. +7, lane l -> row +l/8, physical chunk l%8 holding logical chunk
-  // (l%8) ^ s(row), s(row) = (row / 2) % 8 = 4 (i % 2) + l / 16. The 64 weight rows a
-  // wave copies are consecutive expert rows, so instruction i adds 8i rows to one
-  // lane offset; routed rows take one lane offset each. Weight scales: instruction i
-  // moves rows 64*wave + 16i .. +15, lane l -> row +l/4, dword l%4 of the chunk.
-  const int r_lane = 64 * wave + (lane >> 3);
+  // (l%8) ^ s(row), s(row) = (row / 2) % 8 = 4 (i % 2) + l / 16. Weight scales:
+  // instruction i moves rows 64*wave + 16i .. +15, lane l -> row +l/4, dword l%4 of
+  // the chunk. Lane offsets are loop-invariant registers; the K position goes in the
+  // scalar offset (the hardware range check covers the lane offset only, and a copy
+  // past the last step takes a size-0 resource, which masks every lane).
   const int sw0 = ((lane & 7) ^ (lane >> 4)) << 4;
   const int sw1 = ((lane & 7) ^ (4 | (lane >> 4))) << 4;
-  const int dA = w_row(r_lane) * wrow;
+  const int dA = w_row(64 * wave + (lane >> 3)) * wrow;   // 64 consecutive expert rows per wave
   const int dS = w_row(64 * wave + (lane >> 2)) * srow + (lane & 3) * 4;
-  int dB[8];
+  int dW[8], dB[8], dSc[4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) dB[i] = sTok[64 * wave + 8 * i + (lane >> 3)] * arow + ((i & 1) ? sw1 : sw0);
+  for (int i = 0; i < 8; ++i) {
+    dW[i] = dA + ((i & 1) ? sw1 : sw0) + 8 * i * wrow;
+    dB[i] = sTok[64 * wave + 8 * i + (lane >> 3)] * arow + ((i & 1) ? sw1 : sw0);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) dSc[i] = dS + 16 * i * srow;
 
   auto copy_w = [&](int stage, int i) {   // weight stage (K steps 2 stage, 2 stage + 1), instruction i
-    dma16(rsrc_sized(rw, 2 * stage < KS), lds_addr(&sA[stage & 1][(64 * wave + 8 * i) * 128]),
-          dA + ((i & 1) ? sw1 : sw0) + 8 * i * wrow + stage * 128, 0);
+    dma16(rsrc_sized(rw, 2 * stage < KS), lds_addr(&sA[stage & 1][(64 * wave + 8 * i) * 128]), dW[i], stage * 128);
   };
   auto copy_t = [&](int step, int i) {    // routed rows of K step `step`, instruction i
-    dma16(rsrc_sized(ra, step < KS), lds_addr(&sB[step & 1][(64 * wave + 8 * i) * 128]), dB[i] + step * 128, 0);
+    dma16(rsrc_sized(ra, step < KS), lds_addr(&sB[step & 1][(64 * wave + 8 * i) * 128]), dB[i], step * 128);
   };
   auto copy_s = [&](int chunk, int i) {   // weight scales of K steps 4 chunk .. +3, instruction i
-    dma4(rsrc_sized(rws, 4 * chunk < KS), lds_addr(&sSa[chunk % 3][(64 * wave + 16 * i) * kChunkRow]),
-         dS + 16 * i * srow + chunk * kChunkRow, 0);
+    dma4(rsrc_sized(rws, 4 * chunk < KS), lds_addr(&sSa[chunk % 3][(64 * wave + 16 * i) * kChunkRow]), dSc[i],
+         chunk * kChunkRow);
   };
 
   // Prologue: scale chunk 0 and quarter 0 of chunk 1, weight stage 0, routed rows
@@ -213,32 +229,38 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_xl(XlArgs a) {
   wait_vmcnt<0>();
   __syncthreads();
 
-  // LDS byte offsets of the operand reads (fragment rows are multiples of 16, so
-  // row c of a fragment has swizzle (c / 2) % 8): chunk q and chunk 4 + q of a row.
+  // Operand reads. A lane reads 16-byte chunk q (and 4 + q) of its fragment row;
+  // fragment rows are multiples of 16, so row c has swizzle (c / 2) % 8. Buffer,
+  // fragment and step-in-chunk offsets are compile-time constants added to a few
+  // per-lane base addresses (LDS reads take them as immediate offsets).
   const int off0 = c * 128 + ((q ^ (c >> 1)) << 4);
   const int off1 = c * 128 + (((4 + q) ^ (c >> 1)) << 4);
   auto a_row = [&](int i) {   // first LDS row of this wave's weight fragment i
     return W13 ? (i < 4 ? 64 * wn + 16 * i : 128 + 64 * wn + 16 * (i - 4)) : 128 * wn + 16 * i;
   };
-  const uint8_t* pB = &sB[0][0] + 128 * wm * 128;                 // + buffer, fragment
-  const uint8_t* pSb = sSb + (128 * wm + c) * kSbRow;             // + 16 j kSbRow + step
-  const uint8_t* pSa = &sSa[0][0] + c * kChunkRow + q;            // + chunk buffer, a_row(i) * 16, (step % 4) * 4
+  const uint8_t* pA0 = &sA[0][0] + off0;
+  const uint8_t* pA1 = &sA[0][0] + off1;
+  const uint8_t* pB0 = &sB[0][0] + 128 * wm * 128 + off0;
+  const uint8_t* pB1 = &sB[0][0] + 128 * wm * 128 + off1;
+  const uint8_t* pSa = &sSa[0][0] + c * kChunkRow + q;   // + chunk buffer, a_row(i) * 16, (step % 4) * 4
+  const uint8_t* pSb = sSb + (128 * wm + c) * kSbRow;     // + 16 j kSbRow + 4 (step / 4)
 
-  auto read_a = [&](AOps& o, int step, int i) {   // weight fragment i of K step `step`
-    const uint8_t* base = &sA[(step >> 1) & 1][0] + a_row(i) * 128;
-    o.w[i] = *reinterpret_cast<const v4i*>(base + ((step & 1) ? off1 : off0));
-    o.sa[i] = pSa[((step >> 2) % 3) * kChunk + a_row(i) * kChunkRow + (step & 3) * 4];
+  // weight fragment i of a K step: stage buffer sb, half h (step % 2), scale chunk
+  // base sa (buffer of the step's chunk), step % 4 = u
+  auto read_a = [&](AOps& o, int sbuf, int h, const uint8_t* sa, int u, int i) {
+    o.w[i] = *reinterpret_cast<const v4i*>((h ? pA1 : pA0) + sbuf * kStageA + a_row(i) * 128);
+    o.sa[i] = sa[a_row(i) * kChunkRow + u * 4];
   };
   v8i bf[4];
-  int bs[4];
-  auto read_b = [&](int step, int j, int slot) {  // routed-row fragment j of K step `step`
-    const uint8_t* base = pB + (step & 1) * kStepB + j * 2048;
-    const v4i lo = *reinterpret_cast<const v4i*>(base + off0);
-    const v4i hi = *reinterpret_cast<const v4i*>(base + off1);
+  auto read_b = [&](int buf, int j, int slot) {  // routed-row fragment j from buffer buf
+    const v4i lo = *reinterpret_cast<const v4i*>(pB0 + buf * kStepB + j * 2048);
+    const v4i hi = *reinterpret_cast<const v4i*>(pB1 + buf * kStepB + j * 2048);
     bf[slot][0] = lo[0]; bf[slot][1] = lo[1]; bf[slot][2] = lo[2]; bf[slot][3] = lo[3];
     bf[slot][4] = hi[0]; bf[slot][5] = hi[1]; bf[slot][6] = hi[2]; bf[slot][7] = hi[3];
-    bs[slot] = pSb[16 * j * kSbRow + step];
   };
+  // activation-scale bytes of four K steps of routed-row fragment j (one dword; the
+  // MFMA's op_sel picks the step's byte)
+  auto read_bs = [&](int t, int j) { return *reinterpret_cast<const int*>(pSb + 16 * j * kSbRow + 4 * t); };
 
   v4f acc[8][8];
 #pragma unroll
@@ -247,8 +269,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_xl(XlArgs a) {
     for (int j = 0; j < 8; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
   AOps ops[2];
+  int bsc[8], bsn[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) read_a(ops[0], 0, i);
+  for (int i = 0; i < 8; ++i) read_a(ops[0], 0, 0, pSa, 0, i);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) bsc[j] = read_bs(0, j);
   read_b(0, 0, 0);
   // first part of window 0 (normally issued in column 7 of the previous step)
 #pragma unroll
@@ -256,38 +281,50 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_xl(XlArgs a) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) copy_w(1, i);
 
-  // One K step. P = s & 1 (register set of step s), s even issues the weight copies.
-  auto step = [&](const int s, AOps& cur, AOps& nxt, const bool even) {
+  // K steps 4t .. 4t+3; step u uses register set u % 2 and reads step 4t+u+1 into
+  // the other one.
+  for (int t = 0; t < KS / 4; ++t) {
+    const uint8_t* saC = pSa + (t % 3) * kChunk;          // chunk t
+    const uint8_t* saN = pSa + ((t + 1) % 3) * kChunk;    // chunk t + 1
+    auto step = [&](auto U) {
+      constexpr int u = decltype(U)::value;
+      const int s = 4 * t + u;
+      AOps& cur = ops[u & 1];
+      AOps& nxt = ops[(u + 1) & 1];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if (j < 7) read_b(s, j + 1, (j + 1) & 3);
-      else read_b(s + 1, 0, 0);          // after M_s: routed rows of step s+1 are in LDS
-      read_a(nxt, min(s + 1, KS - 1), j);
+      for (int j = 0; j < 8; ++j) {
+        if (j < 7) read_b(u & 1, j + 1, (j + 1) & 3);
+        else read_b((u + 1) & 1, 0, 0);      // after M_s: routed rows of step s+1 are in LDS
+        // weight fragment j of step s+1 (stage (s+1)/2, half (s+1)%2, chunk (s+1)/4)
+        read_a(nxt, ((u + 1) >> 1) & 1, (u + 1) & 1, u < 3 ? saC : saN, (u + 1) & 3, j);
+        if (u == 3) bsn[j] = read_bs(t + 1, j);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) mma_agpr(acc[i][j], cur.w[i], bf[j & 3], cur.sa[i], bs[j & 3]);
-      // window s (deadline M_s): second part; window s+1: first part after M_s
-      if (j < 4 && even) copy_w(s / 2 + 1, 4 + j);
-      if (j == 0) copy_s((s + 5) >> 2, (s + 5) & 3);
-      if (j == 7) {
+        for (int i = 0; i < 8; ++i) mma_agpr<u>(acc[i][j], cur.w[i], bf[j & 3], cur.sa[i], bsc[j]);
+        // window s (deadline M_s): second part; window s+1: first part after M_s
+        if (j < 4 && (u & 1) == 0) copy_w(s / 2 + 1, 4 + j);
+        if (j == 0) copy_s((s + 5) >> 2, (s + 5) & 3);
+        if (j == 7) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) copy_t(s + 2, i);
-        if (!even) {
+          for (int i = 0; i < 8; ++i) copy_t(s + 2, i);
+          if (u & 1) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) copy_w((s + 1) / 2 + 1, i);
+            for (int i = 0; i < 4; ++i) copy_w((s + 1) / 2 + 1, i);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (j == 6) {                    // M_s
+          wait_vmcnt<0>();
+          __syncthreads();
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
-      __builtin_amdgcn_sched_barrier(0);
-      if (j == 6) {                      // M_s
-        wait_vmcnt<0>();
-        __syncthreads();
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-  };
-
-  for (int s = 0; s < KS; s += 2) {
-    step(s, ops[0], ops[1], true);
-    step(s + 1, ops[1], ops[0], false);
+    };
+    step(std::integral_constant<int, 0>{});
+    step(std::integral_constant<int, 1>{});
+    step(std::integral_constant<int, 2>{});
+    step(std::integral_constant<int, 3>{});
+#pragma unroll
+    for (int j = 0; j < 8; ++j) bsc[j] = bsn[j];
   }
   wait_vmcnt<0>();
   // The compiler does not see the MFMAs in the asm statements, so it inserts no wait
@@ -365,8 +402,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_xl(XlArgs a) {
 
 }  // namespace
 
-bool xl13_supported(const moe_dims& d) { return large_path_supported(d) && (d.H / 128) % 2 == 0; }
-bool xl2_supported(const moe_dims& d) { return large_path_supported(d) && (d.I / 128) % 2 == 0; }
+bool xl13_supported(const moe_dims& d) { return large_path_supported(d) && (d.H / 128) % 4 == 0; }
+bool xl2_supported(const moe_dims& d) { return large_path_supported(d) && (d.I / 128) % 4 == 0; }
 
 hipError_t launch_w13_xl(const moe_dims& d, const int2* items, const int32_t* n_items, int64_t max_items,
                          const int32_t* offsets, const int32_t* sorted_pairs, const uint8_t* x_q,

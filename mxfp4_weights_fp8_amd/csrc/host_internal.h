@@ -98,7 +98,7 @@ hipError_t launch_w2_large(const moe_dims& d, const int2* items, const int32_t* 
                            int item_rows, const int32_t* offsets, const int32_t* sorted_pairs,
                            const uint8_t* h_q, const uint8_t* h_s, const uint8_t* w2, const uint8_t* w2_s,
                            float* o, hipStream_t s);
-// 256 x 256 large-M tiles on 256-row items (an even K-step count and the
+// 256 x 256 large-M tiles on 256-row items (a K-step count that is a multiple of 4 and the
 // large-M shape limits).
 bool xl13_supported(const moe_dims& d);
 bool xl2_supported(const moe_dims& d);

@@ -117,17 +117,21 @@ def test_ffn_tiny(dev, small_max):
     (130, 256, 1152, 3, 2, 45, 1),
     (200, 1280, 384, 4, 2, 46, 1),
     (150, 256, 2176, 2, 1, 47, 1),
-    # 256-row items (256 x 256 tiles): one full item + a 44-row remainder item; two
-    # experts with full items and remainders; a second item with 144 of 256 rows;
-    # W2 with 3 K steps (odd: its 256-row items run as two 128-row halves); 16 W13
-    # K steps (the weight-scale chunk buffers rotate); 6 W13 K steps (activation
-    # scale rows not 4-byte aligned, a partial last scale chunk)
+    # 256-row items (256 x 256 tiles need a K-step count divisible by 4; other counts
+    # run those items as two 128-row halves): one full item + a 44-row remainder
+    # item; two experts with full items and remainders (W13 on halves, W2 with 6
+    # steps on halves); a second item with 144 of 256 rows (W2 on 256 x 256 tiles);
+    # W2 with 3 K steps; 16 W13 K steps (the weight-scale chunk buffers rotate); 6
+    # W13 K steps (activation scale rows not 4-byte aligned, a partial last scale
+    # chunk); 144-row second items and remainders with both GEMMs on 256 x 256 tiles
     (300, 512, 512, 1, 1, 48, 0),
     (700, 256, 768, 2, 1, 49, 0),
     (400, 256, 512, 1, 1, 51, 0),
     (400, 256, 384, 1, 1, 52, 0),
     (300, 2048, 1024, 1, 1, 53, 0),
     (300, 768, 256, 1, 1, 54, 0),
+    (400, 512, 512, 1, 1, 55, 0),
+    (700, 1024, 512, 2, 1, 56, 0),
 ])
 def test_ffn_shapes(dev, T, H, I, E, K, seed, small_max):
     wl = scaled("tiny", T=T, H=H, I=I, E=E, K=K, seed=seed, weight_seed=seed, name=f"s{seed}")
