@@ -21,15 +21,28 @@ __global__ __launch_bounds__(kThreads) void k_combine(const float* __restrict__ 
     const int64_t t = g / groups_per_row;
     const int64_t c4 = g - t * groups_per_row;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int j = 0; j < K; ++j) {
-      const int64_t p = t * K + j;
-      if (pair_rows[p] < 0) continue;
-      const float wt = w[p];
-      const float4 v = reinterpret_cast<const float4*>(o)[p * groups_per_row + c4];
-      acc.x = fmaf(wt, v.x, acc.x);
-      acc.y = fmaf(wt, v.y, acc.y);
-      acc.z = fmaf(wt, v.z, acc.z);
-      acc.w = fmaf(wt, v.w, acc.w);
+    // j in order; batches of 8 pairs issue all their loads before the first add (a
+    // dropped pair's row is loaded but not added: its slot was never written)
+    for (int j0 = 0; j0 < K; j0 += 8) {
+      float4 v[8];
+      float wt[8];
+      bool ok[8];
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        const int64_t p = t * K + min(j0 + jj, K - 1);
+        ok[jj] = j0 + jj < K && pair_rows[p] >= 0;
+        wt[jj] = w[p];
+        v[jj] = reinterpret_cast<const float4*>(o)[p * groups_per_row + c4];
+      }
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        if (ok[jj]) {
+          acc.x = fmaf(wt[jj], v[jj].x, acc.x);
+          acc.y = fmaf(wt[jj], v[jj].y, acc.y);
+          acc.z = fmaf(wt[jj], v[jj].z, acc.z);
+          acc.w = fmaf(wt[jj], v[jj].w, acc.w);
+        }
+      }
     }
     if (so) {
       const float4 v = reinterpret_cast<const float4*>(so)[g];

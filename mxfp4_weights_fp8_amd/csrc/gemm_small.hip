@@ -8,7 +8,7 @@
 // per-128 activation scale replicated over the four 32-blocks). The work is a
 // stream of the expert's weights: each lane loads one 16-byte run of 32 E2M1
 // codes per fragment and K step straight from HBM into registers (no reuse
-// across waves, so no LDS staging), four fragments per wave in flight.
+// across waves, so no LDS staging), four K steps of a wave's fragments in flight.
 //
 // W13 (gate/up, "Pushing the Limits of Serving DeepSeek-V4-Pro", section 3.3):
 // a workgroup owns 128 columns of h = silu(gate) * up, i.e. gate rows
@@ -16,8 +16,9 @@
 // FP8 requantization epilogue (same blog, section 4.3) sees a whole 128-column
 // scale block per routed row and writes W2's E4M3 operand and E8M0 scales
 // directly.
-// W2 (down): a workgroup owns 256 output columns; the epilogue writes each routed
-// pair's fp32 row to its token-major slot p = t*K + j for the top-k combine.
+// W2 (down): a workgroup owns 64 * kW2Frags output columns; the epilogue writes
+// each routed pair's fp32 row to its token-major slot p = t*K + j for the top-k
+// combine.
 #include "device_common.h"
 #include "host_internal.h"
 #include "lds_copy.h"
@@ -26,6 +27,13 @@ namespace moe {
 namespace {
 
 constexpr int kThreads = 256;
+// Work split (measured on decode7, 39 experts): W13 workgroups of 8 waves, each
+// streaming one gate and one up fragment (0.1875 -> 0.1745 ms against 4 waves of
+// two pairs); W2 waves of 2 fragments, 4 waves per workgroup (0.111 -> 0.097 ms
+// against 4 fragments): more, shorter streams keep more of HBM busy for the same
+// bytes.
+constexpr int kW13Waves = 8;
+constexpr int kW2Frags = 2;
 
 __device__ __forceinline__ v8i fp4_operand(const v4i w) {
   v8i a;
@@ -172,13 +180,16 @@ __device__ __forceinline__ void stream_k(v4f* acc, const Stream<NF>& p, int KS, 
   }
 }
 
-__global__ __launch_bounds__(kThreads) void k_w13_small(
+template <int WAVES>
+__global__ __launch_bounds__(WAVES * 64) void k_w13_small(
     const int2* __restrict__ items, const int32_t* __restrict__ n_items, int item_rows,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_pairs,
     const uint8_t* __restrict__ x_q, const uint8_t* __restrict__ x_s, const uint8_t* __restrict__ w13,
     const uint8_t* __restrict__ w13_s, uint8_t* __restrict__ h_q, uint8_t* __restrict__ h_s, int H, int I,
     int K) {
-  __shared__ float red[kThreads / 64][16];
+  constexpr int NF = 256 / (16 * WAVES);    // weight fragments per wave: NF/2 gate + NF/2 up
+  constexpr int HC = 128 / WAVES;            // h columns per wave
+  __shared__ float red[WAVES][16];
   extern __shared__ __attribute__((aligned(16))) uint8_t sS[];   // [256 weight rows][H/32] E8M0
   const int item = blockIdx.y;
   if (item >= n_items[0]) return;
@@ -192,7 +203,7 @@ __global__ __launch_bounds__(kThreads) void k_w13_small(
   const int64_t wrow = H / 2, srow = H / 32;
 
   // 8-bit activation operand of a K step: bytes [16q, 16q+16) and [64+16q, 64+16q+16)
-  Stream<4> p;
+  Stream<NF> p;
   p.w = make_rsrc(w13 + (int64_t)e * 2 * I * wrow, (uint32_t)(2 * I * wrow));
   p.x = make_rsrc(x_q, 0xFFFFFFFFu);
   p.xs = make_rsrc(x_s, 0xFFFFFFFFu);
@@ -200,15 +211,16 @@ __global__ __launch_bounds__(kThreads) void k_w13_small(
   // the matching up rows) into LDS rows wave*64 .. +63: two contiguous runs of
   // 32 * srow bytes, copied in full 1 KB instructions (each cache line once; read
   // per 4-step chunk straight from memory, a row's scale lines were refetched).
-  const int run = staged_bytes(32 * (int)srow);
-  stage_scales(w13_s + ((int64_t)e * 2 * I + nb * 128 + wave * 32) * srow,
-               w13_s + ((int64_t)e * 2 * I + I + nb * 128 + wave * 32) * srow, 32 * (int)srow,
+  const int run = staged_bytes(HC * (int)srow);
+  stage_scales(w13_s + ((int64_t)e * 2 * I + nb * 128 + wave * HC) * srow,
+               w13_s + ((int64_t)e * 2 * I + I + nb * 128 + wave * HC) * srow, HC * (int)srow,
                sS + wave * 2 * run, lane);
 #pragma unroll
-  for (int f = 0; f < 4; ++f) {
-    const int n = (f >= 2 ? I : 0) + nb * 128 + wave * 32 + (f & 1) * 16 + c;
+  for (int f = 0; f < NF; ++f) {
+    const int up = f >= NF / 2, fi = f % (NF / 2);
+    const int n = (up ? I : 0) + nb * 128 + wave * HC + fi * 16 + c;
     p.wo[f] = n * (int)wrow + q * 16;
-    p.sl[f] = sS + wave * 2 * run + (f >> 1) * run + ((f & 1) * 16 + c) * srow;
+    p.sl[f] = sS + wave * 2 * run + up * run + (fi * 16 + c) * srow;
   }
 
   for (int m0 = it.y; m0 < it.y + item_rows && e_begin + m0 < e_end; m0 += kSmallRows) {
@@ -220,34 +232,36 @@ __global__ __launch_bounds__(kThreads) void k_w13_small(
     p.xo = tok * H + q * 16;
     p.xso = tok * KS;
 
-    v4f acc[4];
+    v4f acc[NF];
 #pragma unroll
-    for (int f = 0; f < 4; ++f) acc[f] = v4f{0.f, 0.f, 0.f, 0.f};
-    stream_k<4>(acc, p, KS, 8 * q);
+    for (int f = 0; f < NF; ++f) acc[f] = v4f{0.f, 0.f, 0.f, 0.f};
+    stream_k<NF>(acc, p, KS, 8 * q);
 
     // SwiGLU + FP8 requantization: lane (c, q) holds h columns 4q..4q+3 of each
     // 16-column fragment pair, for routed row c.
-    float h[2][4];
+    float h[NF / 2][4];
     float amax = 0.f;
 #pragma unroll
-    for (int g = 0; g < 2; ++g)
+    for (int g = 0; g < NF / 2; ++g)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        h[g][j] = silu_mul(acc[g][j], acc[g + 2][j]);
+        h[g][j] = silu_mul(acc[g][j], acc[g + NF / 2][j]);
         amax = fmaxf(amax, fabsf(h[g][j]));
       }
     amax = fmaxf(amax, __shfl_xor(amax, 16));
     amax = fmaxf(amax, __shfl_xor(amax, 32));
     if (q == 0) red[wave][c] = amax;
     __syncthreads();
-    amax = fmaxf(fmaxf(red[0][c], red[1][c]), fmaxf(red[2][c], red[3][c]));
+    amax = red[0][c];
+#pragma unroll
+    for (int w = 1; w < WAVES; ++w) amax = fmaxf(amax, red[w][c]);
     __syncthreads();
     const int ex = e8m0_exponent(amax);
     const float inv = exp2_neg(ex);
     if (has) {
-      uint8_t* dst = h_q + (int64_t)(row0 + c) * I + nb * 128 + wave * 32 + q * 4;
+      uint8_t* dst = h_q + (int64_t)(row0 + c) * I + nb * 128 + wave * HC + q * 4;
 #pragma unroll
-      for (int g = 0; g < 2; ++g) {
+      for (int g = 0; g < NF / 2; ++g) {
         *reinterpret_cast<uint32_t*>(dst + g * 16) = e4m3_pack4(h[g][0] * inv, h[g][1] * inv, h[g][2] * inv, h[g][3] * inv);
       }
       if (wave == 0 && q == 0) h_s[(int64_t)(row0 + c) * (I / 128) + nb] = (uint8_t)(ex + 127);
@@ -255,6 +269,7 @@ __global__ __launch_bounds__(kThreads) void k_w13_small(
   }
 }
 
+template <int NF>
 __global__ __launch_bounds__(kThreads) void k_w2_small(
     const int2* __restrict__ items, const int32_t* __restrict__ n_items, int item_rows,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_pairs,
@@ -265,7 +280,7 @@ __global__ __launch_bounds__(kThreads) void k_w2_small(
   if (item >= n_items[0]) return;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63, q = lane >> 4, c = lane & 15;
-  const int n_wave = blockIdx.x * 256 + wave * 64;
+  const int n_wave = blockIdx.x * 64 * NF + wave * 16 * NF;
   if (n_wave >= H) return;
   const int2 it = items[item];
   const int e = it.x;
@@ -273,15 +288,15 @@ __global__ __launch_bounds__(kThreads) void k_w2_small(
   const int KS = I / 128;
   const int64_t wrow = I / 2, srow = I / 32;
 
-  Stream<4> p;
+  Stream<NF> p;
   p.w = make_rsrc(w2 + (int64_t)e * H * wrow, (uint32_t)(H * wrow));
   p.x = make_rsrc(h_q, 0xFFFFFFFFu);
   p.xs = make_rsrc(h_s, 0xFFFFFFFFu);
-  // weight scales of the wave's 64 rows (one contiguous run) into LDS rows wave*64..
-  const int run = staged_bytes(64 * (int)srow);
-  stage_scales(w2_s + ((int64_t)e * H + n_wave) * srow, nullptr, 64 * (int)srow, sS + wave * run, lane);
+  // weight scales of the wave's 16*NF rows (one contiguous run) into LDS
+  const int run = staged_bytes(16 * NF * (int)srow);
+  stage_scales(w2_s + ((int64_t)e * H + n_wave) * srow, nullptr, 16 * NF * (int)srow, sS + wave * run, lane);
 #pragma unroll
-  for (int f = 0; f < 4; ++f) {
+  for (int f = 0; f < NF; ++f) {
     const int n = n_wave + f * 16 + c;
     p.wo[f] = n * (int)wrow + q * 16;
     p.sl[f] = sS + wave * run + (f * 16 + c) * srow;
@@ -295,15 +310,15 @@ __global__ __launch_bounds__(kThreads) void k_w2_small(
     p.xo = hrow * I + q * 16;
     p.xso = hrow * KS;
 
-    v4f acc[4];
+    v4f acc[NF];
 #pragma unroll
-    for (int f = 0; f < 4; ++f) acc[f] = v4f{0.f, 0.f, 0.f, 0.f};
-    stream_k<4>(acc, p, KS, 8 * q);
+    for (int f = 0; f < NF; ++f) acc[f] = v4f{0.f, 0.f, 0.f, 0.f};
+    stream_k<NF>(acc, p, KS, 8 * q);
     if (has) {
       const int64_t slot = sorted_pairs[row0 + c];
       float* dst = o + slot * H + n_wave + q * 4;
 #pragma unroll
-      for (int f = 0; f < 4; ++f)
+      for (int f = 0; f < NF; ++f)
         *reinterpret_cast<float4*>(dst + f * 16) = make_float4(acc[f][0], acc[f][1], acc[f][2], acc[f][3]);
     }
   }
@@ -316,10 +331,11 @@ hipError_t launch_w13_small(const moe_dims& d, const int2* items, const int32_t*
                             const uint8_t* x_q, const uint8_t* x_s, const uint8_t* w13, const uint8_t* w13_s,
                             uint8_t* h_q, uint8_t* h_s, hipStream_t s) {
   if (max_items <= 0) return hipSuccess;
+  constexpr int WAVES = kW13Waves;
   dim3 grid(d.I / 128, (unsigned)max_items);
-  // weight scales in LDS: per wave two runs of 32 rows x H/32 bytes
-  const size_t lds = (size_t)(kThreads / 64) * 2 * staged_bytes(32 * (d.H / 32));
-  hipLaunchKernelGGL(k_w13_small, grid, dim3(kThreads), lds, s, items, n_items, item_rows,
+  // weight scales in LDS: per wave two runs of 128/WAVES rows x H/32 bytes
+  const size_t lds = (size_t)WAVES * 2 * staged_bytes(128 / WAVES * (d.H / 32));
+  hipLaunchKernelGGL(k_w13_small<WAVES>, grid, dim3(WAVES * 64), lds, s, items, n_items, item_rows,
                      offsets, sorted_pairs,
                      x_q, x_s, w13, w13_s, h_q, h_s, d.H, d.I, d.K);
   return hipGetLastError();
@@ -330,10 +346,11 @@ hipError_t launch_w2_small(const moe_dims& d, const int2* items, const int32_t* 
                            const uint8_t* h_q, const uint8_t* h_s, const uint8_t* w2, const uint8_t* w2_s,
                            float* o, hipStream_t s) {
   if (max_items <= 0) return hipSuccess;
-  dim3 grid((unsigned)ceil_div(d.H, 256), (unsigned)max_items);
-  // weight scales in LDS: per wave one run of 64 rows x I/32 bytes
-  const size_t lds = (size_t)(kThreads / 64) * staged_bytes(64 * (d.I / 32));
-  hipLaunchKernelGGL(k_w2_small, grid, dim3(kThreads), lds, s, items, n_items, item_rows,
+  constexpr int NF = kW2Frags;
+  dim3 grid((unsigned)ceil_div(d.H, 64 * NF), (unsigned)max_items);
+  // weight scales in LDS: per wave one run of 16*NF rows x I/32 bytes
+  const size_t lds = (size_t)(kThreads / 64) * staged_bytes(16 * NF * (d.I / 32));
+  hipLaunchKernelGGL(k_w2_small<NF>, grid, dim3(kThreads), lds, s, items, n_items, item_rows,
                      offsets, sorted_pairs,
                      h_q, h_s, w2, w2_s, o, d.H, d.I);
   return hipGetLastError();

@@ -18,7 +18,7 @@ constexpr int kXlRows = 256;         // rows per extra-large (256 x 256) large-M
 constexpr int kPlanChunk = 2048;     // pairs per route-planner block
 constexpr int kMaxExperts = 4096;
 constexpr int kMaxTopK = 64;
-constexpr int kMaxSmallDim = 16384;  // H and I: the small-M kernels keep 8*H (W13) or 8*I (W2) bytes of scales in LDS
+constexpr int kMaxSmallDim = 16384;  // H and I: the small-M kernels keep 8*H (W13) or 4*I (W2) bytes of scales in LDS
 
 inline int small_max_of(const moe_dims& d) { return d.small_max > 0 ? d.small_max : kDefaultSmallMax; }
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }

@@ -133,9 +133,16 @@ int moe_ffn(const moe_dims* dims, const uint16_t* x, const float* topk_weights, 
   err = launch_w13_small(d, pw.small_items, pw.hdr + 0, pw.small_cap, kSmallRows, expert_offsets, sorted_pairs,
                          x_q, x_s, w13, w13_s, h_q, h_s, s);
   if (err != hipSuccess) return MOE_EHIP;
-  // large experts: 256-row items, then the 128-row remainders
+  // large experts: 256-row items, then the 128-row remainders. A 256-row item needs
+  // an expert with more than 128 pairs and a 128-row item one with more than
+  // small_max, so with fewer pairs in total those launches (which would find empty
+  // lists) are skipped.
   const bool large = large_path_supported(d);
-  if (large && xl13_supported(d))
+  const int64_t P = (int64_t)d.T * d.K;
+  const bool any_xl = P > kXlRows / 2, any_l = P > small_max_of(d);
+  if (!any_xl)
+    err = hipSuccess;
+  else if (large && xl13_supported(d))
     err = launch_w13_xl(d, pw.xl_items, pw.hdr + 2, pw.xl_cap, expert_offsets, sorted_pairs, x_q, x_s, w13, w13_s,
                         h_q, h_s, s);
   else if (large)
@@ -145,7 +152,9 @@ int moe_ffn(const moe_dims* dims, const uint16_t* x, const float* topk_weights, 
     err = launch_w13_small(d, pw.xl_items, pw.hdr + 2, pw.xl_cap, kXlRows, expert_offsets, sorted_pairs, x_q, x_s,
                            w13, w13_s, h_q, h_s, s);
   if (err != hipSuccess) return MOE_EHIP;
-  if (large)
+  if (!any_l)
+    err = hipSuccess;
+  else if (large)
     err = launch_w13_large(d, pw.large_items, pw.hdr + 1, pw.large_cap, kLargeRows, expert_offsets, sorted_pairs,
                            x_q, x_s, w13, w13_s, h_q, h_s, s);
   else
@@ -157,7 +166,9 @@ int moe_ffn(const moe_dims* dims, const uint16_t* x, const float* topk_weights, 
   err = launch_w2_small(d, pw.small_items, pw.hdr + 0, pw.small_cap, kSmallRows, expert_offsets, sorted_pairs, h_q,
                         h_s, w2, w2_s, fw.o, s);
   if (err != hipSuccess) return MOE_EHIP;
-  if (large && xl2_supported(d))
+  if (!any_xl)
+    err = hipSuccess;
+  else if (large && xl2_supported(d))
     err = launch_w2_xl(d, pw.xl_items, pw.hdr + 2, pw.xl_cap, expert_offsets, sorted_pairs, h_q, h_s, w2, w2_s,
                        fw.o, s);
   else if (large)
@@ -167,7 +178,9 @@ int moe_ffn(const moe_dims* dims, const uint16_t* x, const float* topk_weights, 
     err = launch_w2_small(d, pw.xl_items, pw.hdr + 2, pw.xl_cap, kXlRows, expert_offsets, sorted_pairs, h_q, h_s,
                           w2, w2_s, fw.o, s);
   if (err != hipSuccess) return MOE_EHIP;
-  if (large)
+  if (!any_l)
+    err = hipSuccess;
+  else if (large)
     err = launch_w2_large(d, pw.large_items, pw.hdr + 1, pw.large_cap, kLargeRows, expert_offsets, sorted_pairs,
                           h_q, h_s, w2, w2_s, fw.o, s);
   else
