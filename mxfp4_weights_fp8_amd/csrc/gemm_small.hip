@@ -182,7 +182,7 @@ __device__ __forceinline__ void stream_k(v4f* acc, const Stream<NF>& p, int KS, 
 
 template <int WAVES>
 __global__ __launch_bounds__(WAVES * 64) void k_w13_small(
-    const int2* __restrict__ items, const int32_t* __restrict__ n_items, int item_rows,
+    const SmallLists lists,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_pairs,
     const uint8_t* __restrict__ x_q, const uint8_t* __restrict__ x_s, const uint8_t* __restrict__ w13,
     const uint8_t* __restrict__ w13_s, uint8_t* __restrict__ h_q, uint8_t* __restrict__ h_s, int H, int I,
@@ -191,9 +191,11 @@ __global__ __launch_bounds__(WAVES * 64) void k_w13_small(
   constexpr int HC = 128 / WAVES;            // h columns per wave
   __shared__ float red[WAVES][16];
   extern __shared__ __attribute__((aligned(16))) uint8_t sS[];   // [256 weight rows][H/32] E8M0
-  const int item = blockIdx.y;
-  if (item >= n_items[0]) return;
-  const int2 it = items[item];
+  const int l = blockIdx.y >= lists.cap0;
+  const int item = blockIdx.y - (l ? lists.cap0 : 0);
+  if (item >= lists.n_items[l][0]) return;
+  const int2 it = lists.items[l][item];
+  const int item_rows = lists.rows[l];
   const int e = it.x;
   const int e_begin = offsets[e], e_end = offsets[e + 1];
   const int nb = blockIdx.x;
@@ -271,18 +273,20 @@ __global__ __launch_bounds__(WAVES * 64) void k_w13_small(
 
 template <int NF>
 __global__ __launch_bounds__(kThreads) void k_w2_small(
-    const int2* __restrict__ items, const int32_t* __restrict__ n_items, int item_rows,
+    const SmallLists lists,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_pairs,
     const uint8_t* __restrict__ h_q, const uint8_t* __restrict__ h_s, const uint8_t* __restrict__ w2,
     const uint8_t* __restrict__ w2_s, float* __restrict__ o, int H, int I) {
   extern __shared__ __attribute__((aligned(16))) uint8_t sS[];   // [256 weight rows][I/32] E8M0
-  const int item = blockIdx.y;
-  if (item >= n_items[0]) return;
+  const int l = blockIdx.y >= lists.cap0;
+  const int item = blockIdx.y - (l ? lists.cap0 : 0);
+  if (item >= lists.n_items[l][0]) return;
+  const int item_rows = lists.rows[l];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63, q = lane >> 4, c = lane & 15;
   const int n_wave = blockIdx.x * 64 * NF + wave * 16 * NF;
   if (n_wave >= H) return;
-  const int2 it = items[item];
+  const int2 it = lists.items[l][item];
   const int e = it.x;
   const int e_begin = offsets[e], e_end = offsets[e + 1];
   const int KS = I / 128;
@@ -326,31 +330,33 @@ __global__ __launch_bounds__(kThreads) void k_w2_small(
 
 }  // namespace
 
-hipError_t launch_w13_small(const moe_dims& d, const int2* items, const int32_t* n_items, int64_t max_items,
-                            int item_rows, const int32_t* offsets, const int32_t* sorted_pairs,
+hipError_t launch_w13_small(const moe_dims& d, const SmallLists& lists, const int32_t* offsets,
+                            const int32_t* sorted_pairs,
                             const uint8_t* x_q, const uint8_t* x_s, const uint8_t* w13, const uint8_t* w13_s,
                             uint8_t* h_q, uint8_t* h_s, hipStream_t s) {
+  const int64_t max_items = (int64_t)lists.cap0 + lists.cap1;
   if (max_items <= 0) return hipSuccess;
   constexpr int WAVES = kW13Waves;
   dim3 grid(d.I / 128, (unsigned)max_items);
   // weight scales in LDS: per wave two runs of 128/WAVES rows x H/32 bytes
   const size_t lds = (size_t)WAVES * 2 * staged_bytes(128 / WAVES * (d.H / 32));
-  hipLaunchKernelGGL(k_w13_small<WAVES>, grid, dim3(WAVES * 64), lds, s, items, n_items, item_rows,
+  hipLaunchKernelGGL(k_w13_small<WAVES>, grid, dim3(WAVES * 64), lds, s, lists,
                      offsets, sorted_pairs,
                      x_q, x_s, w13, w13_s, h_q, h_s, d.H, d.I, d.K);
   return hipGetLastError();
 }
 
-hipError_t launch_w2_small(const moe_dims& d, const int2* items, const int32_t* n_items, int64_t max_items,
-                           int item_rows, const int32_t* offsets, const int32_t* sorted_pairs,
+hipError_t launch_w2_small(const moe_dims& d, const SmallLists& lists, const int32_t* offsets,
+                           const int32_t* sorted_pairs,
                            const uint8_t* h_q, const uint8_t* h_s, const uint8_t* w2, const uint8_t* w2_s,
                            float* o, hipStream_t s) {
+  const int64_t max_items = (int64_t)lists.cap0 + lists.cap1;
   if (max_items <= 0) return hipSuccess;
   constexpr int NF = kW2Frags;
   dim3 grid((unsigned)ceil_div(d.H, 64 * NF), (unsigned)max_items);
   // weight scales in LDS: per wave one run of 16*NF rows x I/32 bytes
   const size_t lds = (size_t)(kThreads / 64) * staged_bytes(16 * NF * (d.I / 32));
-  hipLaunchKernelGGL(k_w2_small<NF>, grid, dim3(kThreads), lds, s, items, n_items, item_rows,
+  hipLaunchKernelGGL(k_w2_small<NF>, grid, dim3(kThreads), lds, s, lists,
                      offsets, sorted_pairs,
                      h_q, h_s, w2, w2_s, o, d.H, d.I);
   return hipGetLastError();

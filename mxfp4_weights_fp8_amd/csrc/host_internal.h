@@ -18,6 +18,7 @@ constexpr int kXlRows = 256;         // rows per extra-large (256 x 256) large-M
 constexpr int kPlanChunk = 2048;     // pairs per route-planner block
 constexpr int kMaxExperts = 4096;
 constexpr int kMaxTopK = 64;
+constexpr int kFoldPairs = 512;      // up to this many pairs the small-M launch also takes the 128-row items
 constexpr int kMaxSmallDim = 16384;  // H and I: the small-M kernels keep 8*H (W13) or 4*I (W2) bytes of scales in LDS
 
 inline int small_max_of(const moe_dims& d) { return d.small_max > 0 ? d.small_max : kDefaultSmallMax; }
@@ -79,14 +80,24 @@ size_t ffn_ws_layout(const moe_dims& d, void* base, FfnWs* out);
 hipError_t launch_plan(const moe_dims& d, const int32_t* ids, int32_t* offsets, int32_t* sorted_pairs,
                        int32_t* pair_rows, int32_t* status, const PlanWs& ws, hipStream_t s);
 hipError_t launch_quant_act(const uint16_t* x, uint8_t* x_q, uint8_t* x_s, int T, int H, hipStream_t s);
-hipError_t launch_w13_small(const moe_dims& d, const int2* items, const int32_t* n_items, int64_t max_items,
-                            int item_rows, const int32_t* offsets, const int32_t* sorted_pairs,
-                            const uint8_t* x_q, const uint8_t* x_s, const uint8_t* w13, const uint8_t* w13_s,
-                            uint8_t* h_q, uint8_t* h_s, hipStream_t s);
-hipError_t launch_w2_small(const moe_dims& d, const int2* items, const int32_t* n_items, int64_t max_items,
-                           int item_rows, const int32_t* offsets, const int32_t* sorted_pairs,
-                           const uint8_t* h_q, const uint8_t* h_s, const uint8_t* w2, const uint8_t* w2_s,
-                           float* o, hipStream_t s);
+// Small-M kernels walk up to two work lists in one launch: workgroup row y <
+// cap0 takes item y of list 0, the rest item y - cap0 of list 1; an item covers
+// rows[l] routed rows in 16-row tiles (counts live on the device).
+struct SmallLists {
+  const int2* items[2];
+  const int32_t* n_items[2];
+  int cap0, cap1;
+  int rows[2];
+};
+inline SmallLists small_lists(const int2* items, const int32_t* n_items, int64_t cap, int rows) {
+  return SmallLists{{items, items}, {n_items, n_items}, (int)cap, 0, {rows, rows}};
+}
+hipError_t launch_w13_small(const moe_dims& d, const SmallLists& lists, const int32_t* offsets,
+                            const int32_t* sorted_pairs, const uint8_t* x_q, const uint8_t* x_s,
+                            const uint8_t* w13, const uint8_t* w13_s, uint8_t* h_q, uint8_t* h_s, hipStream_t s);
+hipError_t launch_w2_small(const moe_dims& d, const SmallLists& lists, const int32_t* offsets,
+                           const int32_t* sorted_pairs, const uint8_t* h_q, const uint8_t* h_s,
+                           const uint8_t* w2, const uint8_t* w2_s, float* o, hipStream_t s);
 // 128-row large-M tiles; item_rows 128 or 256 (a 256-row item runs as two
 // 128-row workgroups).
 bool large_path_supported(const moe_dims& d);

@@ -130,63 +130,63 @@ int moe_ffn(const moe_dims* dims, const uint16_t* x, const float* topk_weights, 
   if (err != hipSuccess) return MOE_EHIP;
   record(dbg, MOE_EV_QUANT_DONE, s);
 
-  err = launch_w13_small(d, pw.small_items, pw.hdr + 0, pw.small_cap, kSmallRows, expert_offsets, sorted_pairs,
-                         x_q, x_s, w13, w13_s, h_q, h_s, s);
-  if (err != hipSuccess) return MOE_EHIP;
-  // large experts: 256-row items, then the 128-row remainders. A 256-row item needs
-  // an expert with more than 128 pairs and a 128-row item one with more than
-  // small_max, so with fewer pairs in total those launches (which would find empty
-  // lists) are skipped.
+  // Work lists: 16-row items (small experts), 256-row items and 128-row remainders
+  // (large experts). A 256-row item needs an expert with more than 128 pairs and a
+  // 128-row item one with more than small_max, so launches that could only find
+  // empty lists are skipped. Up to kFoldPairs pairs the few 128-row items ride in
+  // the small-M launch (one launch less; a 128-row item is then walked as 16-row
+  // tiles).
   const bool large = large_path_supported(d);
   const int64_t P = (int64_t)d.T * d.K;
   const bool any_xl = P > kXlRows / 2, any_l = P > small_max_of(d);
-  if (!any_xl)
-    err = hipSuccess;
-  else if (large && xl13_supported(d))
-    err = launch_w13_xl(d, pw.xl_items, pw.hdr + 2, pw.xl_cap, expert_offsets, sorted_pairs, x_q, x_s, w13, w13_s,
-                        h_q, h_s, s);
-  else if (large)
-    err = launch_w13_large(d, pw.xl_items, pw.hdr + 2, pw.xl_cap, kXlRows, expert_offsets, sorted_pairs, x_q, x_s,
-                           w13, w13_s, h_q, h_s, s);
-  else   // shapes the large-M tiles do not cover: the small-M kernel walks the items
-    err = launch_w13_small(d, pw.xl_items, pw.hdr + 2, pw.xl_cap, kXlRows, expert_offsets, sorted_pairs, x_q, x_s,
-                           w13, w13_s, h_q, h_s, s);
+  const bool fold = any_l && (P <= kFoldPairs || !large);
+  SmallLists sl = small_lists(pw.small_items, pw.hdr + 0, pw.small_cap, kSmallRows);
+  if (fold) {
+    sl.items[1] = pw.large_items;
+    sl.n_items[1] = pw.hdr + 1;
+    sl.cap1 = (int)pw.large_cap;
+    sl.rows[1] = kLargeRows;
+  }
+  const SmallLists sxl = small_lists(pw.xl_items, pw.hdr + 2, pw.xl_cap, kXlRows);
+
+  err = launch_w13_small(d, sl, expert_offsets, sorted_pairs, x_q, x_s, w13, w13_s, h_q, h_s, s);
   if (err != hipSuccess) return MOE_EHIP;
-  if (!any_l)
-    err = hipSuccess;
-  else if (large)
+  if (any_xl) {
+    if (large && xl13_supported(d))
+      err = launch_w13_xl(d, pw.xl_items, pw.hdr + 2, pw.xl_cap, expert_offsets, sorted_pairs, x_q, x_s, w13,
+                          w13_s, h_q, h_s, s);
+    else if (large)
+      err = launch_w13_large(d, pw.xl_items, pw.hdr + 2, pw.xl_cap, kXlRows, expert_offsets, sorted_pairs, x_q,
+                             x_s, w13, w13_s, h_q, h_s, s);
+    else   // shapes the large-M tiles do not cover: the small-M kernel walks the items
+      err = launch_w13_small(d, sxl, expert_offsets, sorted_pairs, x_q, x_s, w13, w13_s, h_q, h_s, s);
+    if (err != hipSuccess) return MOE_EHIP;
+  }
+  if (any_l && !fold) {
     err = launch_w13_large(d, pw.large_items, pw.hdr + 1, pw.large_cap, kLargeRows, expert_offsets, sorted_pairs,
                            x_q, x_s, w13, w13_s, h_q, h_s, s);
-  else
-    err = launch_w13_small(d, pw.large_items, pw.hdr + 1, pw.large_cap, kLargeRows, expert_offsets, sorted_pairs,
-                           x_q, x_s, w13, w13_s, h_q, h_s, s);
-  if (err != hipSuccess) return MOE_EHIP;
+    if (err != hipSuccess) return MOE_EHIP;
+  }
   record(dbg, MOE_EV_W13_DONE, s);
 
-  err = launch_w2_small(d, pw.small_items, pw.hdr + 0, pw.small_cap, kSmallRows, expert_offsets, sorted_pairs, h_q,
-                        h_s, w2, w2_s, fw.o, s);
+  err = launch_w2_small(d, sl, expert_offsets, sorted_pairs, h_q, h_s, w2, w2_s, fw.o, s);
   if (err != hipSuccess) return MOE_EHIP;
-  if (!any_xl)
-    err = hipSuccess;
-  else if (large && xl2_supported(d))
-    err = launch_w2_xl(d, pw.xl_items, pw.hdr + 2, pw.xl_cap, expert_offsets, sorted_pairs, h_q, h_s, w2, w2_s,
-                       fw.o, s);
-  else if (large)
-    err = launch_w2_large(d, pw.xl_items, pw.hdr + 2, pw.xl_cap, kXlRows, expert_offsets, sorted_pairs, h_q, h_s,
-                          w2, w2_s, fw.o, s);
-  else
-    err = launch_w2_small(d, pw.xl_items, pw.hdr + 2, pw.xl_cap, kXlRows, expert_offsets, sorted_pairs, h_q, h_s,
-                          w2, w2_s, fw.o, s);
-  if (err != hipSuccess) return MOE_EHIP;
-  if (!any_l)
-    err = hipSuccess;
-  else if (large)
+  if (any_xl) {
+    if (large && xl2_supported(d))
+      err = launch_w2_xl(d, pw.xl_items, pw.hdr + 2, pw.xl_cap, expert_offsets, sorted_pairs, h_q, h_s, w2, w2_s,
+                         fw.o, s);
+    else if (large)
+      err = launch_w2_large(d, pw.xl_items, pw.hdr + 2, pw.xl_cap, kXlRows, expert_offsets, sorted_pairs, h_q, h_s,
+                            w2, w2_s, fw.o, s);
+    else
+      err = launch_w2_small(d, sxl, expert_offsets, sorted_pairs, h_q, h_s, w2, w2_s, fw.o, s);
+    if (err != hipSuccess) return MOE_EHIP;
+  }
+  if (any_l && !fold) {
     err = launch_w2_large(d, pw.large_items, pw.hdr + 1, pw.large_cap, kLargeRows, expert_offsets, sorted_pairs,
                           h_q, h_s, w2, w2_s, fw.o, s);
-  else
-    err = launch_w2_small(d, pw.large_items, pw.hdr + 1, pw.large_cap, kLargeRows, expert_offsets, sorted_pairs,
-                          h_q, h_s, w2, w2_s, fw.o, s);
-  if (err != hipSuccess) return MOE_EHIP;
+    if (err != hipSuccess) return MOE_EHIP;
+  }
   record(dbg, MOE_EV_W2_DONE, s);
 
   if (use_shared) {

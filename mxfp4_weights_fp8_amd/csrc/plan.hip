@@ -26,27 +26,35 @@ constexpr int kPlanWaves = kPlanThreads / 64;
 constexpr int kScanThreads = 1024;
 
 // Exclusive scan of a[0..n) in LDS with all threads of the block; returns the total.
+// Each thread sums a contiguous run, the runs are scanned within each wave with
+// lane shuffles and across waves through part[] (at least blockDim/64 entries),
+// then each thread writes its run's prefixes: two barriers per scan.
 __device__ int block_exclusive_scan(int32_t* a, int n, int32_t* part) {
-  const int t = threadIdx.x, nt = blockDim.x;
+  const int t = threadIdx.x, nt = blockDim.x, lane = t & 63, wave = t >> 6, nw = nt >> 6;
   const int per = (n + nt - 1) / nt;
   const int lo = min(n, t * per), hi = min(n, lo + per);
   int s = 0;
   for (int i = lo; i < hi; ++i) s += a[i];
-  part[t] = s;
+  int v = s;                                   // inclusive scan within the wave
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int u = __shfl_up(v, off);
+    if (lane >= off) v += u;
+  }
+  if (lane == 63) part[wave] = v;
   __syncthreads();
-  for (int off = 1; off < nt; off <<= 1) {
-    int v = t >= off ? part[t - off] : 0;
-    __syncthreads();
-    part[t] += v;
-    __syncthreads();
+  int base = 0, total = 0;
+  for (int w = 0; w < nw; ++w) {
+    const int pw = part[w];
+    base += w < wave ? pw : 0;
+    total += pw;
   }
-  int run = part[t] - s;
+  int run = base + v - s;
   for (int i = lo; i < hi; ++i) {
-    int v = a[i];
+    const int x = a[i];
     a[i] = run;
-    run += v;
+    run += x;
   }
-  const int total = part[nt - 1];
   __syncthreads();
   return total;
 }
