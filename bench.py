@@ -51,22 +51,27 @@ def expert_bytes(w) -> dict:
     return {"w13": w13, "w2": w2}
 
 
-def measured_traffic(workload: str, kernel: str):
-    """HBM bytes per launch of ``kernel`` from the committed rocprofv3 counter
-    summary of ``workload`` (FETCH_SIZE and WRITE_SIZE scaled by a plain copy of
-    known size), or None when there is no summary or the kernel's sources have
-    changed since the counters were taken."""
+def measured_traffic(workload: str, kernels):
+    """HBM bytes per launch of the given kernels together (one name or a list: a
+    stage made of several launches) from the committed rocprofv3 counter summary
+    of ``workload`` (FETCH_SIZE and WRITE_SIZE scaled by a plain copy of known
+    size), or None when there is no summary, a kernel is missing from it, or a
+    kernel's sources have changed since the counters were taken."""
     path = os.path.join(ROOT, "profiles", f"{workload}_traffic.txt")
     if not os.path.exists(path):
         return None
+    names = [kernels] if isinstance(kernels, str) else list(kernels)
+    found = {}
     for line in open(path):
         f = line.strip().split(",")
-        if len(f) == 7 and f[0] == kernel and f[5] != "-":
+        if len(f) == 7 and f[0] in names and f[5] != "-":
             h = hashlib.sha256()
             for name in f[5].split("+"):
                 h.update(open(os.path.join(ROOT, "mxfp4_weights_fp8_amd", "csrc", name), "rb").read())
-            return float(f[4]) if h.hexdigest() == f[6] else None
-    return None
+            if h.hexdigest() != f[6]:
+                return None
+            found[f[0]] = float(f[4])
+    return sum(found.values()) if len(found) == len(names) else None
 
 
 class Runner:
@@ -205,9 +210,9 @@ def main():
         "data": "synthetic (seeded: x N(0,1) bf16, Zipf routing, N(0,0.02) weights packed to MXFP4)",
         "config": {"workload": "decode7", "tokens": w.T, "hidden": w.H, "experts": w.E, "intermediate": w.I,
                    "top_k": w.K, "routing": f"zipf s={w.zipf_s}", "distinct_experts": dec.distinct},
-        "roofline": {"bound": "hbm", "kernel": "W13 grouped GEMM + SwiGLU/requant (k_w13_small)",
+        "roofline": {"bound": "hbm", "kernel": "W13 grouped GEMM + SwiGLU/requant (k_w13_small<8>)",
                      "achieved": w13_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": w13_gbs / HBM_PEAK_GBS,
-                     "traffic": measured_traffic("decode7", "moe::k_w13_small"),
+                     "traffic": measured_traffic("decode7", "moe::k_w13_small<8>"),
                      "algorithmic_bytes_per_launch": w13_bytes, "avg_launch_ms": w13_ms},
         "step_hbm_gbs": step_bytes / (ms_step * 1e-3) / 1e9,
         "stage_ms_untimed_pass": ms,
@@ -227,10 +232,14 @@ def main():
             "config": {"workload": "prefill32k", "tokens": pw.T, "routing": f"zipf s={pw.zipf_s}"},
             "effective_tflops": (f13 + f2) / (ps * 1e-3) / 1e12,
             "mfma_frac_fp8_peak": (f13 + f2) / (ps * 1e-3) / 1e12 / MFMA_PEAK_FP8_TFLOPS,
-            "roofline": {"bound": "mfma", "kernel": "W13 grouped GEMM + SwiGLU/requant", "achieved": t13,
+            "roofline": {"bound": "mfma",
+                         "kernel": "W13 stage: k_gemm_xl<true> (256-row items) + k_gemm_large<true> (128-row "
+                                   "remainders) + SwiGLU/requant",
+                         "achieved": t13,
                          "peak": MFMA_PEAK_FP8_TFLOPS, "unit": "TFLOP/s", "frac": t13 / MFMA_PEAK_FP8_TFLOPS,
                          "frac_of_fp4_peak": t13 / MFMA_PEAK_FP4_TFLOPS,
-                         "traffic": measured_traffic("prefill32k", "moe::k_gemm_large<true>"),
+                         "traffic": measured_traffic("prefill32k", ["moe::k_gemm_xl<true>",
+                                                                    "moe::k_gemm_large<true>"]),
                          "algorithmic_flops_per_launch": f13, "avg_launch_ms": p13_ms},
             "stage_ms_untimed_pass": pms,
         }
