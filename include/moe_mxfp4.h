@@ -23,9 +23,10 @@
  *   bf16 passed as uint16_t bit patterns.
  *
  * Conventions for every entry point below:
- *   - All tensor pointers are DEVICE pointers, row-major, 16-byte aligned; the
- *     caller allocates and owns every buffer. The library never allocates or
- *     frees memory and keeps no pointer past the call.
+ *   - All tensor pointers are DEVICE pointers, 16-byte aligned, row-major unless
+ *     stated otherwise (moe_ffn's expert weight codes are in the layout of
+ *     moe_pack_weights); the caller allocates and owns every buffer. The library
+ *     never allocates or frees memory and keeps no pointer past the call.
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *     Every call only enqueues work on it: no host synchronization, no host
  *     read of device data, so calls can be captured into a HIP graph.
@@ -141,6 +142,21 @@ int moe_plan(const moe_dims* dims, const int32_t* topk_ids, int32_t* expert_offs
 int moe_quant_act(const moe_dims* dims, const uint16_t* x, uint8_t* x_q, uint8_t* x_s,
                   void* stream);
 
+/* Kernel-native layout of the MXFP4 expert weights, converted once when the
+ * weights are loaded (the scales keep their row-major layout). A row-major code
+ * tensor w[R][K/2] (R rows of K weights) becomes blocks of 16 rows x 128 K: block
+ * (g, s), rows 16g .. 16g+15 and code bytes 64s .. 64s+63 of each row, is 1 KB at
+ * byte offset g*16*(K/2) + s*1024, and inside it byte 16*(16q + c) + b holds
+ * w[16g + c][64s + 16q + b] (q = 0..3, c = 0..15, b = 0..15): the order in which a
+ * 64-lane wave holds a 16-row fragment of one 128-K step of the MFMA, so each
+ * fragment streams as one contiguous kilobyte. Same size as the input.
+ *   w13 [E, 2I, H/2] -> w13_packed (R = E*2I, K = H)
+ *   w2  [E, H, I/2]  -> w2_packed  (R = E*H,  K = I)
+ * Either pair may be NULL (that tensor is skipped); outputs must not alias inputs.
+ * Errors: MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EHIP. */
+int moe_pack_weights(const moe_dims* dims, const uint8_t* w13, uint8_t* w13_packed, const uint8_t* w2,
+                     uint8_t* w2_packed, void* stream);
+
 /* Bytes of device workspace moe_ffn needs for these dims. */
 size_t moe_ffn_workspace_bytes(const moe_dims* dims);
 
@@ -150,8 +166,10 @@ size_t moe_ffn_workspace_bytes(const moe_dims* dims);
  *   x              [T, H] bf16
  *   topk_weights   [T, K] float32  routing weight of each pick, applied after W2
  *   expert_offsets, sorted_pairs, pair_rows, plan_ws   from moe_plan (same dims)
- *   w13   [E, 2I, H/2]  MXFP4 codes     w13_s [E, 2I, H/32]  E8M0 scales
- *   w2    [E, H, I/2]   MXFP4 codes     w2_s  [E, H, I/32]   E8M0 scales
+ *   w13   [E, 2I, H/2]  MXFP4 codes in the layout of moe_pack_weights
+ *   w13_s [E, 2I, H/32] E8M0 scales, row-major
+ *   w2    [E, H, I/2]   MXFP4 codes in the layout of moe_pack_weights
+ *   w2_s  [E, H, I/32]  E8M0 scales, row-major
  *   shared          optional dense FP8 shared expert (NULL or dims->Is == 0: none)
  *   y     [T, H] bf16 out
  *   dbg             optional inspection outputs / stage events (NULL: none)

@@ -58,6 +58,7 @@ _SIGNATURES = {
     "moe_plan_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(Dims)]),
     "moe_plan": (ctypes.c_int, [ctypes.POINTER(Dims)] + [ctypes.c_void_p] * 6 + [ctypes.c_size_t, ctypes.c_void_p]),
     "moe_quant_act": (ctypes.c_int, [ctypes.POINTER(Dims)] + [ctypes.c_void_p] * 4),
+    "moe_pack_weights": (ctypes.c_int, [ctypes.POINTER(Dims)] + [ctypes.c_void_p] * 5),
     "moe_ffn_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(Dims)]),
     "moe_ffn": (ctypes.c_int, [ctypes.POINTER(Dims)] + [ctypes.c_void_p] * 10 + [ctypes.POINTER(Shared),
                 ctypes.c_void_p, ctypes.POINTER(Debug), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
@@ -164,6 +165,27 @@ def quant_act(x: torch.Tensor):
     return x_q, x_s
 
 
+def pack_weights(weights: dict) -> dict:
+    """moe_pack_weights on the current stream: a new weights dict whose w13 and w2
+    codes are in the kernel-native layout that moe_ffn reads (the scale tensors are
+    shared with the input dict). weights: dict w13 [E, 2I, H/2], w13_s, w2
+    [E, H, I/2], w2_s (uint8 cuda, row-major codes as produced by MXFP4 packing)."""
+    w13, w2 = weights["w13"], weights["w2"]
+    E, I2, Hh = w13.shape
+    H, I = 2 * Hh, I2 // 2
+    _require(w13, torch.uint8, (E, 2 * I, H // 2), "w13")
+    _require(w2, torch.uint8, (E, H, I // 2), "w2")
+    d = make_dims(1, H, I, E, 1)
+    _check(validate(d), "moe_pack_weights dims")
+    p13 = torch.empty_like(w13)
+    p2 = torch.empty_like(w2)
+    _check(lib().moe_pack_weights(ctypes.byref(d), _ptr(w13), _ptr(p13), _ptr(w2), _ptr(p2), _stream(w13.device)),
+           "moe_pack_weights")
+    out = dict(weights)
+    out.update(w13=p13, w2=p2, layout="packed")
+    return out
+
+
 _hip = None
 
 
@@ -212,8 +234,9 @@ class StageEvents:
 def ffn(x: torch.Tensor, topk_weights: torch.Tensor, p: Plan, weights: dict, shared: Optional[dict] = None,
         debug: bool = False, ws: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None,
         events=None):
-    """moe_ffn on the current stream. weights: dict w13, w13_s, w2, w2_s (uint8
-    cuda, layouts as in the header); shared: optional dict w13s, w13s_s, w2s, w2s_s.
+    """moe_ffn on the current stream. weights: dict from pack_weights (w13 and w2 in
+    the kernel-native layout, w13_s and w2_s row-major; uint8 cuda); shared:
+    optional dict w13s, w13s_s, w2s, w2s_s.
     Returns y (bf16 [T, H]); with debug=True returns (y, dict of x_q, x_s, h_q, h_s,
     sh_q, sh_s). ``events``: optional StageEvents recorded at the stage boundaries."""
     d = p.dims
@@ -221,6 +244,8 @@ def ffn(x: torch.Tensor, topk_weights: torch.Tensor, p: Plan, weights: dict, sha
     dev = x.device
     _require(x, torch.bfloat16, (T, H), "x")
     _require(topk_weights, torch.float32, (T, K), "topk_weights")
+    if weights.get("layout") != "packed":
+        raise ValueError("moe_ffn reads expert weights in the kernel-native layout: convert them with pack_weights")
     _require(weights["w13"], torch.uint8, (E, 2 * I, H // 2), "w13")
     _require(weights["w13_s"], torch.uint8, (E, 2 * I, H // 32), "w13_s")
     _require(weights["w2"], torch.uint8, (E, H, I // 2), "w2")

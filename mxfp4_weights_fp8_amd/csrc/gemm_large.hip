@@ -19,14 +19,16 @@
 //
 // Data movement: HBM/L2 -> LDS with direct-to-LDS buffer loads (buffer_load_dwordx4
 // ... lds; lane l's 16 bytes land at M0 + 16*l), issued from inline asm with explicit
-// vmcnt waits and barriers. Every copy instruction moves whole 128-byte lines: 8
-// weight rows x 128 B (two 128-K steps of E2M1 codes) or 8 routed rows x 128 B (one
-// step of E4M3 codes). The vector L1 handles a limited number of line requests per
-// cycle, and copying 16 rows x 64 B per instruction ran at a third of the rate of 8
-// rows x 128 B. Rows sit in LDS row-major with the 16-byte chunk index XORed by
-// (row / 2) % 8: an MFMA fragment read (16 rows, one chunk per lane group) then
-// covers all 64 banks once per 16 lanes (even rows in one 128-byte half of a bank
-// row, odd rows in the other, each with 8 distinct chunks).
+// vmcnt waits and barriers. Every copy instruction moves whole 128-byte lines: one
+// weight fragment of one K step (the weights are in the kernel-native layout, 1 KB
+// of consecutive bytes in the MFMA's lane order, read back by each lane at 16*l:
+// no bank conflicts) or 8 routed rows x 128 B (one step of E4M3 codes). The vector
+// L1 handles a limited number of line requests per cycle, and copying 16 rows x
+// 64 B per instruction ran at a third of the rate of 8 rows x 128 B. Routed rows sit
+// in LDS row-major with the 16-byte chunk index XORed by (row / 2) % 8: an MFMA
+// fragment read (16 rows, one chunk per lane group) then covers all 64 banks once
+// per 16 lanes (even rows in one 128-byte half of a bank row, odd rows in the
+// other, each with 8 distinct chunks).
 // A stage holds two K steps (32 KB of weights + 32 KB of activations); two stages.
 // The weight E8M0 scales of eight K steps (32 B per row) come by dword copies of 8
 // rows each; the activation scales of the whole tile are copied once, before the
@@ -163,18 +165,20 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_large(LargeArgs a) {
     if (W13) return (f < 8 ? 0 : a.I) + nb * 128 + (f & 7) * 16 + (r & 15);
     return nb * 256 + r;
   };
-  // Copy plan (per wave, per stage): 8 weight instructions, LDS rows 64*wave + 8i ..
-  // +7, lane l -> row +l/8, physical chunk l%8 holding logical chunk (l%8) ^ s(row),
-  // s(row) = (row / 2) % 8 = 4 (i % 2) + l / 16;
+  // Copy plan (per wave, per stage): 8 weight instructions, instruction i copies the
+  // 1 KB block of LDS fragment 4*wave + i/2 and K step 2*stage + i%2 (the weights are
+  // in the kernel-native layout: a fragment's codes of one K step are 1 KB in lane
+  // order) to LDS [fragment][step][1 KB]; the 64 weight rows a wave copies are
+  // consecutive expert rows (fragments of the gate or the up half, or of the W2
+  // column block), so instruction i adds i/2 fragments to one lane offset.
   // 8 activation instructions, step wave/2 of the stage, routed rows
-  // 64*(wave%2) + 8i .. +7, same chunk mapping. The 64 weight rows a wave copies
-  // are consecutive expert rows (16-row fragments of the gate or the up half, or
-  // of the W2 column block), so instruction i adds 8i rows to one lane offset;
-  // routed rows are arbitrary and take one lane offset each.
-  const int r_lane = 64 * wave + (lane >> 3);           // LDS row of instruction 0
+  // 64*(wave%2) + 8i .. +7, lane l -> row +l/8, physical chunk l%8 holding logical
+  // chunk (l%8) ^ s(row), s(row) = (row / 2) % 8 = 4 (i % 2) + l / 16; routed rows
+  // are arbitrary and take one lane offset each.
+  const int r_lane = 64 * wave + (lane >> 3);           // LDS row of scale copy 0
   const int sw0 = ((lane & 7) ^ (lane >> 4)) << 4;      // swizzled chunk, even i
   const int sw1 = ((lane & 7) ^ (4 | (lane >> 4))) << 4; // odd i
-  const int dA = w_row(r_lane) * wrow;
+  const int dA = w_row(64 * wave) * wrow + lane * 16;
   const int dS = w_row(r_lane) * srow + (lane & 7) * 4;
   int dB[8];
 #pragma unroll
@@ -185,8 +189,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_large(LargeArgs a) {
   // of stage stg (K steps 2stg, 2stg+1) into LDS buffer buf; valid == false (a
   // stage past the last) writes zeros.
   auto issue_part = [&](int buf, int stg, bool valid, int i) {
-    dma16(rsrc_sized(rw, valid), lds_addr(&sA[buf][(64 * wave + 8 * i) * 128]),
-          dA + ((i & 1) ? sw1 : sw0) + 8 * i * wrow + stg * 128, 0);
+    dma16(rsrc_sized(rw, valid), lds_addr(&sA[buf][(4 * wave + (i >> 1)) * 2048 + (i & 1) * 1024]),
+          dA + 16 * (i >> 1) * wrow + (i & 1) * 1024 + stg * 2048, 0);
     dma16(rsrc_sized(ra, valid), lds_addr(&sB[buf][b_step][(64 * (wave & 1) + 8 * i) * 128]),
           dB[i] + (stg * kStageK + b_step) * 128, 0);
   };
@@ -224,8 +228,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_large(LargeArgs a) {
   // this wave's 8 weight fragments: W13 gate 4wn..4wn+3 and up 8+4wn..; W2 8wn..8wn+7
   const int a_wave = W13 ? wn * 4 * 2048 : wn * 8 * 2048;
   auto a_frag = [](int i) { return W13 ? (i < 4 ? i : 8 + (i - 4)) * 2048 : i * 2048; };
-  const uint8_t* pA0 = &sA[0][0] + a_wave + off0;
-  const uint8_t* pA1 = &sA[0][0] + a_wave + off1;
+  const uint8_t* pA = &sA[0][0] + a_wave + lane * 16;   // + stage, fragment, step * 1 KB
   const uint8_t* pB0 = &sB[0][0][0] + wm * 4 * 2048 + off0;
   const uint8_t* pB1 = &sB[0][0][0] + wm * 4 * 2048 + off1;
   // weight scales: lane group q reads its K block's byte of the (row, step) dword
@@ -255,7 +258,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_large(LargeArgs a) {
       const uint8_t* sa = pSa + ((ks / kScaleSteps) & 1) * (kARows / 8 * kSaGroup) + (ks % kScaleSteps) * 4;
 #pragma unroll
       for (int i = 2 * (p - 4); i < 2 * (p - 4) + 2; ++i) {
-        o.w[i] = *reinterpret_cast<const v4i*>((h ? pA1 : pA0) + buf * kStageA + a_frag(i));
+        o.w[i] = *reinterpret_cast<const v4i*>(pA + buf * kStageA + a_frag(i) + h * 1024);
         o.sa[i] = sa[a_frag(i) / 2048 * 2 * kSaGroup];
       }
     }

@@ -6,9 +6,12 @@
 // Optimization 06). Here the weights take the MFMA's 16-row A side (E2M1, one
 // E8M0 scale per 32 K) and the routed tokens its 16-column B side (E4M3, the
 // per-128 activation scale replicated over the four 32-blocks). The work is a
-// stream of the expert's weights: each lane loads one 16-byte run of 32 E2M1
-// codes per fragment and K step straight from HBM into registers (no reuse
-// across waves, so no LDS staging), four K steps of a wave's fragments in flight.
+// stream of the expert's weights, in the kernel-native layout (a fragment's codes of
+// one K step are 1 KB of consecutive bytes in lane order): each lane loads its 16
+// bytes per fragment and K step straight from HBM into registers (no reuse across
+// waves, so no LDS staging), four K steps of a wave's fragments in flight.
+// (Measured on decode7: W13 0.1725 -> 0.155 ms and W2 0.096 -> 0.082 ms against
+// loading the same bytes from row-major codes, 16 rows x 64 B per instruction.)
 //
 // W13 (gate/up, "Pushing the Limits of Serving DeepSeek-V4-Pro", section 3.3):
 // a workgroup owns 128 columns of h = silu(gate) * up, i.e. gate rows
@@ -54,7 +57,7 @@ struct Step {
 };
 
 // Where a wave's operands live: buffer resources (wave-uniform) and per-lane
-// byte offsets; step s adds s*64 (codes), s*128 (activation codes), s (activation
+// byte offsets; step s adds s*1024 (codes), s*128 (activation codes), s (activation
 // scales) as wave-uniform offsets. The weight scales are in LDS: sl[f] is the
 // lane's row of fragment f there (KS dwords, dword s = the four 32-block scales
 // of step s).
@@ -70,7 +73,7 @@ template <int NF>
 __device__ __forceinline__ void load_step(Step<NF>& r, const Stream<NF>& p, int s) {
 #pragma unroll
   for (int f = 0; f < NF; ++f) {
-    r.w[f] = buf_load16(p.w, p.wo[f], s * 64);
+    r.w[f] = buf_load16(p.w, p.wo[f], s * 1024);
     r.ws[f] = *reinterpret_cast<const int*>(p.sl[f] + s * 4);
   }
   const v4i lo = buf_load16(p.x, p.xo, s * 128), hi = buf_load16(p.x, p.xo, s * 128 + 64);
@@ -114,7 +117,7 @@ struct Codes {
 template <int NF>
 __device__ __forceinline__ void load_codes(Codes<NF>& r, const Stream<NF>& p, int s) {
 #pragma unroll
-  for (int f = 0; f < NF; ++f) r.w[f] = buf_load16(p.w, p.wo[f], s * 64);
+  for (int f = 0; f < NF; ++f) r.w[f] = buf_load16(p.w, p.wo[f], s * 1024);
   const v4i lo = buf_load16(p.x, p.xo, s * 128), hi = buf_load16(p.x, p.xo, s * 128 + 64);
   r.x[0] = lo[0]; r.x[1] = lo[1]; r.x[2] = lo[2]; r.x[3] = lo[3];
   r.x[4] = hi[0]; r.x[5] = hi[1]; r.x[6] = hi[2]; r.x[7] = hi[3];
@@ -220,8 +223,8 @@ __global__ __launch_bounds__(WAVES * 64) void k_w13_small(
 #pragma unroll
   for (int f = 0; f < NF; ++f) {
     const int up = f >= NF / 2, fi = f % (NF / 2);
-    const int n = (up ? I : 0) + nb * 128 + wave * HC + fi * 16 + c;
-    p.wo[f] = n * (int)wrow + q * 16;
+    const int n0 = (up ? I : 0) + nb * 128 + wave * HC + fi * 16;   // first row of the fragment
+    p.wo[f] = n0 * (int)wrow + lane * 16;
     p.sl[f] = sS + wave * 2 * run + up * run + (fi * 16 + c) * srow;
   }
 
@@ -301,8 +304,7 @@ __global__ __launch_bounds__(kThreads) void k_w2_small(
   stage_scales(w2_s + ((int64_t)e * H + n_wave) * srow, nullptr, 16 * NF * (int)srow, sS + wave * run, lane);
 #pragma unroll
   for (int f = 0; f < NF; ++f) {
-    const int n = n_wave + f * 16 + c;
-    p.wo[f] = n * (int)wrow + q * 16;
+    p.wo[f] = (n_wave + f * 16) * (int)wrow + lane * 16;
     p.sl[f] = sS + wave * run + (f * 16 + c) * srow;
   }
 

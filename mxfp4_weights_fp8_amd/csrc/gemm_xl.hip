@@ -22,12 +22,14 @@
 // the register files inside the K loop).
 //
 // LDS (161792 bytes for W13, 162816 for W2):
-//   weights: two stages of two K steps (128 B of E2M1 per row and stage), 64 KB;
+//   weights: two stages of two K steps, [fragment][step][1 KB in lane order] (the
+//     kernel-native weight layout, copied block by block), 64 KB;
 //   routed rows: two buffers of one K step (128 B of E4M3 per row), 64 KB;
 //   weight E8M0 scales: three chunks of four K steps (16 B per row), 12 KB;
 //   activation scales of the whole tile: 68 B per routed row, 17 KB.
-// Rows are stored as 128-byte lines with the 16-byte chunk index XORed by
-// (row / 2) % 8, so that a fragment read hits every bank once per 16 lanes.
+// Routed rows are stored as 128-byte lines with the 16-byte chunk index XORed by
+// (row / 2) % 8, so that a fragment read hits every bank once per 16 lanes; a
+// weight fragment is read by lane l at 16*l.
 //
 // Schedule of one K step s (per wave): 8 columns; column j issues the 8 MFMAs of
 // routed-row fragment j against the 8 weight fragments of step s, reads routed-row
@@ -186,28 +188,32 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_xl(XlArgs a) {
     if (W13) return (f < 8 ? 0 : a.I) + nb * 128 + (f & 7) * 16 + (r & 15);
     return nb * 256 + r;
   };
-  // Copy plans (per wave). Weights and routed rows: instruction i moves LDS rows
-  // 64*wave + 8i .. +7, lane l -> row +l/8, physical chunk l%8 holding logical chunk
-  // (l%8) ^ s(row), s(row) = (row / 2) % 8 = 4 (i % 2) + l / 16. Weight scales:
-  // instruction i moves rows 64*wave + 16i .. +15, lane l -> row +l/4, dword l%4 of
-  // the chunk. Lane offsets are loop-invariant registers; the K position goes in the
-  // scalar offset (the hardware range check covers the lane offset only, and a copy
-  // past the last step takes a size-0 resource, which masks every lane).
+  // Copy plans (per wave). Weights (kernel-native layout: a fragment's codes of one
+  // K step are 1 KB in lane order): instruction i of a stage copies the block of LDS
+  // fragment 4*wave + i/2 and K step 2*stage + i%2 to LDS [fragment][step][1 KB]; a
+  // wave's 64 weight rows are consecutive expert rows. Routed rows: instruction i
+  // moves LDS rows 64*wave + 8i .. +7, lane l -> row +l/8, physical chunk l%8 holding
+  // logical chunk (l%8) ^ s(row), s(row) = (row / 2) % 8 = 4 (i % 2) + l / 16. Weight
+  // scales: instruction i moves rows 64*wave + 16i .. +15, lane l -> row +l/4, dword
+  // l%4 of the chunk. Lane offsets are loop-invariant registers; the K position goes
+  // in the scalar offset (the hardware range check covers the lane offset only, and
+  // a copy past the last step takes a size-0 resource, which masks every lane).
   const int sw0 = ((lane & 7) ^ (lane >> 4)) << 4;
   const int sw1 = ((lane & 7) ^ (4 | (lane >> 4))) << 4;
-  const int dA = w_row(64 * wave + (lane >> 3)) * wrow;   // 64 consecutive expert rows per wave
+  const int dA = w_row(64 * wave) * wrow + lane * 16;   // 64 consecutive expert rows per wave
   const int dS = w_row(64 * wave + (lane >> 2)) * srow + (lane & 3) * 4;
   int dW[8], dB[8], dSc[4];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    dW[i] = dA + ((i & 1) ? sw1 : sw0) + 8 * i * wrow;
+    dW[i] = dA + 16 * (i >> 1) * wrow + (i & 1) * 1024;
     dB[i] = sTok[64 * wave + 8 * i + (lane >> 3)] * arow + ((i & 1) ? sw1 : sw0);
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) dSc[i] = dS + 16 * i * srow;
 
   auto copy_w = [&](int stage, int i) {   // weight stage (K steps 2 stage, 2 stage + 1), instruction i
-    dma16(rsrc_sized(rw, 2 * stage < KS), lds_addr(&sA[stage & 1][(64 * wave + 8 * i) * 128]), dW[i], stage * 128);
+    dma16(rsrc_sized(rw, 2 * stage < KS), lds_addr(&sA[stage & 1][(4 * wave + (i >> 1)) * 2048 + (i & 1) * 1024]),
+          dW[i], stage * 2048);
   };
   auto copy_t = [&](int step, int i) {    // routed rows of K step `step`, instruction i
     dma16(rsrc_sized(ra, step < KS), lds_addr(&sB[step & 1][(64 * wave + 8 * i) * 128]), dB[i], step * 128);
@@ -238,8 +244,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_xl(XlArgs a) {
   auto a_row = [&](int i) {   // first LDS row of this wave's weight fragment i
     return W13 ? (i < 4 ? 64 * wn + 16 * i : 128 + 64 * wn + 16 * (i - 4)) : 128 * wn + 16 * i;
   };
-  const uint8_t* pA0 = &sA[0][0] + off0;
-  const uint8_t* pA1 = &sA[0][0] + off1;
+  const uint8_t* pA = &sA[0][0] + lane * 16;   // + stage, fragment (a_row * 128), step * 1 KB
   const uint8_t* pB0 = &sB[0][0] + 128 * wm * 128 + off0;
   const uint8_t* pB1 = &sB[0][0] + 128 * wm * 128 + off1;
   const uint8_t* pSa = &sSa[0][0] + c * kChunkRow + q;   // + chunk buffer, a_row(i) * 16, (step % 4) * 4
@@ -248,7 +253,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_xl(XlArgs a) {
   // weight fragment i of a K step: stage buffer sb, half h (step % 2), scale chunk
   // base sa (buffer of the step's chunk), step % 4 = u
   auto read_a = [&](AOps& o, int sbuf, int h, const uint8_t* sa, int u, int i) {
-    o.w[i] = *reinterpret_cast<const v4i*>((h ? pA1 : pA0) + sbuf * kStageA + a_row(i) * 128);
+    o.w[i] = *reinterpret_cast<const v4i*>(pA + sbuf * kStageA + a_row(i) * 128 + h * 1024);
     o.sa[i] = sa[a_row(i) * kChunkRow + u * 4];
   };
   v8i bf[4];

@@ -79,6 +79,9 @@ size_t ffn_ws_layout(const moe_dims& d, void* base, FfnWs* out);
 // Each returns hipSuccess or the launch error.
 hipError_t launch_plan(const moe_dims& d, const int32_t* ids, int32_t* offsets, int32_t* sorted_pairs,
                        int32_t* pair_rows, int32_t* status, const PlanWs& ws, hipStream_t s);
+// Row-major E2M1 codes [rows, K/2] -> the kernel-native blocked layout (rows % 16
+// == 0, K % 128 == 0).
+hipError_t launch_pack_weights(const uint8_t* w, uint8_t* out, int64_t rows, int K, hipStream_t s);
 hipError_t launch_quant_act(const uint16_t* x, uint8_t* x_q, uint8_t* x_s, int T, int H, hipStream_t s);
 // Small-M kernels walk up to two work lists in one launch: workgroup row y <
 // cap0 takes item y of list 0, the rest item y - cap0 of list 1; an item covers

@@ -101,6 +101,19 @@ int moe_quant_act(const moe_dims* dims, const uint16_t* x, uint8_t* x_q, uint8_t
   return hip_status(launch_quant_act(x, x_q, x_s, dims->T, dims->H, (hipStream_t)stream));
 }
 
+int moe_pack_weights(const moe_dims* dims, const uint8_t* w13, uint8_t* w13_packed, const uint8_t* w2,
+                     uint8_t* w2_packed, void* stream) {
+  int rc = validate(dims);
+  if (rc != MOE_OK) return rc;
+  if (!w13 != !w13_packed || !w2 != !w2_packed) return MOE_EINVAL;
+  if ((w13 && w13 == w13_packed) || (w2 && w2 == w2_packed)) return MOE_EINVAL;   // not in place
+  const moe_dims& d = *dims;
+  hipStream_t s = (hipStream_t)stream;
+  if (w13 && launch_pack_weights(w13, w13_packed, (int64_t)d.E * 2 * d.I, d.H, s) != hipSuccess) return MOE_EHIP;
+  if (w2 && launch_pack_weights(w2, w2_packed, (int64_t)d.E * d.H, d.I, s) != hipSuccess) return MOE_EHIP;
+  return MOE_OK;
+}
+
 int moe_ffn(const moe_dims* dims, const uint16_t* x, const float* topk_weights, const int32_t* expert_offsets,
             const int32_t* sorted_pairs, const int32_t* pair_rows, const void* plan_ws, const uint8_t* w13,
             const uint8_t* w13_s, const uint8_t* w2, const uint8_t* w2_s, const moe_shared* shared, uint16_t* y,

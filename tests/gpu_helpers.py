@@ -40,7 +40,9 @@ def run_path(inp, small_max=0, debug=True):
     """plan + ffn on the GPU for MoEInputs already on the device."""
     w = inp.wl
     p = moe.plan(inp.topk_ids, w.E, w.H, w.I, small_max=small_max, Is=w.Is if inp.shared else 0)
-    out = moe.ffn(inp.x, inp.topk_weights, p, inp.weights, shared=inp.shared, debug=debug)
+    packed = moe.pack_weights(inp.weights)
+    out = moe.ffn(inp.x, inp.topk_weights, p, packed, shared=inp.shared, debug=debug)
+    del packed
     torch.cuda.synchronize()
     return p, out
 

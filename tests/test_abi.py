@@ -81,6 +81,14 @@ def test_host_checks_reject_before_enqueue():
     args[0] = None
     assert L.moe_ffn(ctypes.byref(d), *args, None, fake, None, fake, 1 << 30, None) == moe.MOE_EINVAL
     assert L.moe_quant_act(ctypes.byref(d), None, fake, fake, None) == moe.MOE_EINVAL
+    # weight packing: an input without its output, and in-place conversion, are refused
+    assert L.moe_pack_weights(ctypes.byref(d), fake, None, None, None, None) == moe.MOE_EINVAL
+    assert L.moe_pack_weights(ctypes.byref(d), fake, fake, None, None, None) == moe.MOE_EINVAL
+    assert L.moe_pack_weights(ctypes.byref(d), None, None, fake, fake, None) == moe.MOE_EINVAL
+    bad = moe.make_dims(4, 200, 512, 8, 2)
+    assert L.moe_pack_weights(ctypes.byref(bad), fake, ctypes.c_void_p(0x2000), None, None, None) == \
+        moe.MOE_EUNSUPPORTED
+    assert L.moe_pack_weights(ctypes.byref(d), None, None, None, None, None) == moe.MOE_OK   # nothing to do
     # T == 0 is a no-op for the FFN and the quantizer
     z = moe.make_dims(0, 256, 512, 8, 2)
     assert L.moe_ffn(ctypes.byref(z), *([None] * 10), None, None, None, None, 0, None) == moe.MOE_OK

@@ -21,6 +21,36 @@ def dev(gpu):
     return gpu
 
 
+# ----------------------------------------------------------------------------- weight layout
+
+def test_pack_weights_layout(dev):
+    """moe_pack_weights against the layout definition written out in numpy: block
+    (g, s) of 16 rows x 128 K at g*16*(K/2) + s*1024, byte 16*(16q + c) + b =
+    w[16g + c][64s + 16q + b]; bit-exact, both tensors, and the scales untouched."""
+    g = torch.Generator().manual_seed(7)
+    E, H, I = 3, 384, 256
+    W = {"w13": torch.randint(0, 256, (E, 2 * I, H // 2), generator=g, dtype=torch.uint8),
+         "w13_s": torch.randint(0, 256, (E, 2 * I, H // 32), generator=g, dtype=torch.uint8),
+         "w2": torch.randint(0, 256, (E, H, I // 2), generator=g, dtype=torch.uint8),
+         "w2_s": torch.randint(0, 256, (E, H, I // 32), generator=g, dtype=torch.uint8)}
+    packed = moe.pack_weights({k: v.to(dev) for k, v in W.items()})
+    torch.cuda.synchronize()
+
+    def expect(w):
+        R, kb = w.shape[0] * w.shape[1], w.shape[2]
+        a = w.numpy().reshape(R // 16, 16, kb // 64, 4, 16)      # [g, c, s, q, b]
+        return a.transpose(0, 2, 3, 1, 4).reshape(w.shape)      # [g, s, q, c, b]
+
+    for k in ("w13", "w2"):
+        assert np.array_equal(packed[k].cpu().numpy(), expect(W[k])), k
+    for k in ("w13_s", "w2_s"):
+        assert np.array_equal(packed[k].cpu().numpy(), W[k].numpy()), k
+    assert packed["layout"] == "packed"
+    with pytest.raises(ValueError):
+        moe.ffn(torch.zeros((1, H), dtype=torch.bfloat16, device=dev), torch.ones((1, 1), device=dev),
+                moe.plan(torch.zeros((1, 1), dtype=torch.int32, device=dev), E, H, I), {k: v.to(dev) for k, v in W.items()})
+
+
 # ----------------------------------------------------------------------------- quantizer
 
 def test_quant_act_every_bf16_value(dev):
