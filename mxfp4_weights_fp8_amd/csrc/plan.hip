@@ -123,7 +123,17 @@ __device__ void build_worklists(const int32_t* cnt, int E, int small_max, int2* 
         if (s + i < small_cap) small_items[s + i] = make_int2(e, i * kSmallRows);
     }
   }
-  __syncthreads();
+  // no expert above small_max (decode batches): empty large-M lists, done
+  int any_big = 0;
+  for (int e = t; e < E; e += nt) any_big |= cnt[e] > small_max;
+  if (!__syncthreads_or(any_big)) {
+    if (t == 0) {
+      hdr[0] = n_small < small_cap ? n_small : (int)small_cap;
+      hdr[1] = 0;
+      hdr[2] = 0;
+    }
+    return;
+  }
   // heavy-first order of the large experts: a2[rank] = expert
   for (int e = t; e < E; e += nt) {
     const int m = cnt[e];
