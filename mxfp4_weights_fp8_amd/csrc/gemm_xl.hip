@@ -81,6 +81,8 @@ struct XlArgs {
   uint32_t act_s_bytes;    // size of act_s
   int act_s_dma;           // act_s rows are 4-byte aligned: copy them with dword copies
   int H, I, K;
+  int gi, gn;              // XCD group: gi work items x gn column blocks
+  int ngn;                 // column groups (column blocks / gn)
 };
 
 // acc += A (E2M1, 32 K values per lane) x B (E4M3) with E8M0 scales: byte 0 of sa,
@@ -119,14 +121,22 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_xl(XlArgs a) {
   __shared__ int sTok[kTok];
   __shared__ int sSlot[W13 ? 1 : kTok];
 
-  const int item = blockIdx.y;
+  // Workgroup -> (work item, column block). The hardware hands out workgroups to
+  // the 8 XCDs round-robin by linear id, and each XCD has its own L2, so the
+  // workgroups an XCD runs together form one group of gi work items x gn column
+  // blocks: the group's routed-row tiles are fetched once per XCD and shared by gn
+  // workgroups, its weight slices shared by gi. Groups run heavy items first.
+  const int L = blockIdx.x, xcd = L & 7, idx = L >> 3, gsz = a.gi * a.gn;
+  const int sl = idx / gsz, pos = idx - sl * gsz;
+  const int grp = sl * 8 + xcd, ig = grp / a.ngn, ng = grp - ig * a.ngn;
+  const int item = ig * a.gi + pos / a.gn;
   if (item >= a.n_items[0]) return;
   const int2 it = a.items[item];
   const int e = it.x;
   const int e_begin = a.offsets[e], e_end = a.offsets[e + 1];
   const int row0 = e_begin + it.y;                      // first sorted row of the tile
   const int nrows = min(kTok, e_end - row0);
-  const int nb = blockIdx.x;
+  const int nb = ng * a.gn + pos % a.gn;
   const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4, c = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave & 1, wn = wave >> 1;
@@ -407,6 +417,30 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_xl(XlArgs a) {
 
 }  // namespace
 
+// XCD group shape: gn divides the column-block count, gi = 32 / gn (one workgroup
+// per CU, 32 CUs per XCD); the shape with the fewest fetched bytes per workgroup
+// (routed-row tile act_b over gn workgroups, weight slice w_b over gi) wins. The
+// grid is a whole number of groups per XCD.
+struct XcdGroups {
+  int gi, gn, ngn;
+  int64_t grid;
+};
+static XcdGroups xcd_groups(int n_blocks, int64_t max_items, double act_b, double w_b) {
+  constexpr int kCusPerXcd = 32;
+  XcdGroups g{1, 1, n_blocks, 0};
+  double best = 1e300;
+  for (int gn = 1; gn <= n_blocks && gn <= kCusPerXcd; ++gn) {
+    if (n_blocks % gn) continue;
+    const int gi = kCusPerXcd / gn;
+    const double cost = (gi * act_b + gn * w_b) / (gi * gn);
+    if (cost < best) { best = cost; g.gi = gi; g.gn = gn; }
+  }
+  g.ngn = n_blocks / g.gn;
+  const int64_t groups = (max_items + g.gi - 1) / g.gi * g.ngn;
+  g.grid = (groups + 7) / 8 * 8 * g.gi * g.gn;
+  return g;
+}
+
 bool xl13_supported(const moe_dims& d) { return large_path_supported(d) && (d.H / 128) % 4 == 0; }
 bool xl2_supported(const moe_dims& d) { return large_path_supported(d) && (d.I / 128) % 4 == 0; }
 
@@ -416,10 +450,11 @@ hipError_t launch_w13_xl(const moe_dims& d, const int2* items, const int32_t* n_
                          uint8_t* h_s, hipStream_t s) {
   if (max_items <= 0) return hipSuccess;
   const int KS = d.H / 128;
+  const XcdGroups g = xcd_groups(d.I / 128, max_items, (double)kTok * d.H, 256.0 * (d.H / 2 + d.H / 32));
   XlArgs a{items, n_items, offsets, sorted_pairs, x_q, x_s, w13, w13_s, h_q, h_s, nullptr,
            (uint32_t)((int64_t)d.T * d.H), (uint32_t)((int64_t)d.T * KS),
-           KS % 4 == 0 && (uintptr_t)x_s % 4 == 0, d.H, d.I, d.K};
-  hipLaunchKernelGGL(k_gemm_xl<true>, dim3(d.I / 128, (unsigned)max_items), dim3(kThreads), 0, s, a);
+           KS % 4 == 0 && (uintptr_t)x_s % 4 == 0, d.H, d.I, d.K, g.gi, g.gn, g.ngn};
+  hipLaunchKernelGGL(k_gemm_xl<true>, dim3((unsigned)g.grid), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
@@ -429,9 +464,11 @@ hipError_t launch_w2_xl(const moe_dims& d, const int2* items, const int32_t* n_i
   if (max_items <= 0) return hipSuccess;
   const int KS = d.I / 128;
   const int64_t P = (int64_t)d.T * d.K;
+  const XcdGroups g = xcd_groups(d.H / 256, max_items, (double)kTok * d.I, 256.0 * (d.I / 2 + d.I / 32));
   XlArgs a{items, n_items, offsets, sorted_pairs, h_q, h_s, w2, w2_s, nullptr, nullptr, o,
-           (uint32_t)(P * d.I), (uint32_t)(P * KS), KS % 4 == 0 && (uintptr_t)h_s % 4 == 0, d.H, d.I, d.K};
-  hipLaunchKernelGGL(k_gemm_xl<false>, dim3(d.H / 256, (unsigned)max_items), dim3(kThreads), 0, s, a);
+           (uint32_t)(P * d.I), (uint32_t)(P * KS), KS % 4 == 0 && (uintptr_t)h_s % 4 == 0, d.H, d.I, d.K,
+           g.gi, g.gn, g.ngn};
+  hipLaunchKernelGGL(k_gemm_xl<false>, dim3((unsigned)g.grid), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
