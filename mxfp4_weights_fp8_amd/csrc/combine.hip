@@ -1,10 +1,11 @@
 // Top-k weighted combine ("Pushing the Limits of Serving DeepSeek-V4-Pro",
 // section 3.2: the top-k reduction is fused with the shared-expert add):
 //   y[t, :] = bf16( sum_j w[t, j] * o[t*K + j, :]  (+ shared[t, :]) )
-// Atomic-free gather: each lane owns 4 columns of one token, reads the K per-pair
-// fp32 rows (contiguous, token-major slots), accumulates in fp32 in pick order,
-// adds the shared expert last and rounds once to bf16. Dropped picks
-// (pair_rows == -1) contribute nothing. HBM-bound.
+// Atomic-free gather: each lane owns 8 columns of one token, reads the K per-pair
+// rows (contiguous, token-major slots; fp16 codes with a power-of-two scale per 32
+// columns, decoded exactly to fp32), accumulates in fp32 in pick order, adds the
+// shared expert last and rounds once to bf16. Dropped picks (pair_rows == -1)
+// contribute nothing. HBM-bound.
 #include "device_common.h"
 #include "host_internal.h"
 
@@ -13,18 +14,24 @@ namespace {
 
 constexpr int kThreads = 256;
 
-__global__ __launch_bounds__(kThreads) void k_combine(const float* __restrict__ o, const float* __restrict__ w,
+__device__ __forceinline__ float f16_lo(uint32_t v) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(v & 0xFFFFu)); }
+__device__ __forceinline__ float f16_hi(uint32_t v) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(v >> 16)); }
+
+__global__ __launch_bounds__(kThreads) void k_combine(const uint16_t* __restrict__ o, const uint8_t* __restrict__ os,
+                                                       const float* __restrict__ w,
                                                        const int32_t* __restrict__ pair_rows,
                                                        const float* __restrict__ so, uint16_t* __restrict__ y,
                                                        int64_t n_groups, int groups_per_row, int K) {
+  const int scales_per_row = groups_per_row / 4;   // one scale per 32 columns = 4 groups of 8
   for (int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x; g < n_groups; g += (int64_t)gridDim.x * kThreads) {
     const int64_t t = g / groups_per_row;
-    const int64_t c4 = g - t * groups_per_row;
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    const int64_t c8 = g - t * groups_per_row;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     // j in order; batches of 8 pairs issue all their loads before the first add (a
     // dropped pair's row is loaded but not added: its slot was never written)
     for (int j0 = 0; j0 < K; j0 += 8) {
-      float4 v[8];
+      uint4 v[8];
+      int ex[8];
       float wt[8];
       bool ok[8];
 #pragma unroll
@@ -32,41 +39,46 @@ __global__ __launch_bounds__(kThreads) void k_combine(const float* __restrict__ 
         const int64_t p = t * K + min(j0 + jj, K - 1);
         ok[jj] = j0 + jj < K && pair_rows[p] >= 0;
         wt[jj] = w[p];
-        v[jj] = reinterpret_cast<const float4*>(o)[p * groups_per_row + c4];
+        v[jj] = reinterpret_cast<const uint4*>(o)[p * groups_per_row + c8];
+        ex[jj] = (int)os[p * scales_per_row + (c8 >> 2)] - 127;
       }
 #pragma unroll
       for (int jj = 0; jj < 8; ++jj) {
         if (ok[jj]) {
-          acc.x = fmaf(wt[jj], v[jj].x, acc.x);
-          acc.y = fmaf(wt[jj], v[jj].y, acc.y);
-          acc.z = fmaf(wt[jj], v[jj].z, acc.z);
-          acc.w = fmaf(wt[jj], v[jj].w, acc.w);
+          const uint32_t u[4] = {v[jj].x, v[jj].y, v[jj].z, v[jj].w};
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            acc[2 * k] = fmaf(wt[jj], __builtin_amdgcn_ldexpf(f16_lo(u[k]), ex[jj]), acc[2 * k]);
+            acc[2 * k + 1] = fmaf(wt[jj], __builtin_amdgcn_ldexpf(f16_hi(u[k]), ex[jj]), acc[2 * k + 1]);
+          }
         }
       }
     }
     if (so) {
-      const float4 v = reinterpret_cast<const float4*>(so)[g];
-      acc.x += v.x;
-      acc.y += v.y;
-      acc.z += v.z;
-      acc.w += v.w;
+      const float4 a = reinterpret_cast<const float4*>(so)[2 * g];
+      const float4 b = reinterpret_cast<const float4*>(so)[2 * g + 1];
+      acc[0] += a.x; acc[1] += a.y; acc[2] += a.z; acc[3] += a.w;
+      acc[4] += b.x; acc[5] += b.y; acc[6] += b.z; acc[7] += b.w;
     }
-    const uint32_t lo = (uint32_t)bf16_rne(acc.x) | ((uint32_t)bf16_rne(acc.y) << 16);
-    const uint32_t hi = (uint32_t)bf16_rne(acc.z) | ((uint32_t)bf16_rne(acc.w) << 16);
-    reinterpret_cast<uint2*>(y)[g] = make_uint2(lo, hi);
+    uint4 r;
+    r.x = (uint32_t)bf16_rne(acc[0]) | ((uint32_t)bf16_rne(acc[1]) << 16);
+    r.y = (uint32_t)bf16_rne(acc[2]) | ((uint32_t)bf16_rne(acc[3]) << 16);
+    r.z = (uint32_t)bf16_rne(acc[4]) | ((uint32_t)bf16_rne(acc[5]) << 16);
+    r.w = (uint32_t)bf16_rne(acc[6]) | ((uint32_t)bf16_rne(acc[7]) << 16);
+    reinterpret_cast<uint4*>(y)[g] = r;
   }
 }
 
 }  // namespace
 
-hipError_t launch_combine(const float* o, const float* topk_weights, const int32_t* pair_rows, const float* so,
-                          uint16_t* y, int T, int H, int K, hipStream_t s) {
-  const int64_t n_groups = (int64_t)T * (H / 4);
+hipError_t launch_combine(const uint16_t* o, const uint8_t* os, const float* topk_weights, const int32_t* pair_rows,
+                          const float* so, uint16_t* y, int T, int H, int K, hipStream_t s) {
+  const int64_t n_groups = (int64_t)T * (H / 8);
   if (n_groups == 0) return hipSuccess;
   int64_t ctas = ceil_div(n_groups, kThreads);
   if (ctas > 256 * 32) ctas = 256 * 32;
-  hipLaunchKernelGGL(k_combine, dim3((unsigned)ctas), dim3(kThreads), 0, s, o, topk_weights, pair_rows, so, y,
-                     n_groups, H / 4, K);
+  hipLaunchKernelGGL(k_combine, dim3((unsigned)ctas), dim3(kThreads), 0, s, o, os, topk_weights, pair_rows, so, y,
+                     n_groups, H / 8, K);
   return hipGetLastError();
 }
 

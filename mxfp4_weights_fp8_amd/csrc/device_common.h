@@ -72,6 +72,54 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
   return g * __builtin_amdgcn_rcpf(1.0f + e) * u;
 }
 
+// Per-pair W2 outputs are stored as fp16 codes of o * 2^-e with one power-of-two
+// scale 2^e per 32 columns (stored as the byte e + 127): e = floor(log2 amax) - 14,
+// at least -127, so every scaled value is below 2^15 (the fp16 maximum is 65504)
+// and values within 2^28 of the block's amax keep a relative error <= 2^-11.
+__device__ __forceinline__ int o_exponent(float amax) {
+  const int be = (int)((__float_as_uint(amax) & 0x7FFFFFFFu) >> 23);
+  return be - 141 < -127 ? -127 : be - 141;
+}
+
+// Four floats to fp16 (round to nearest even), packed low to high.
+__device__ __forceinline__ uint2 f16_pack4(float a, float b, float c, float d) {
+  const uint32_t lo = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)a) |
+                      ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)b) << 16);
+  const uint32_t hi = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)c) |
+                      ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)d) << 16);
+  return make_uint2(lo, hi);
+}
+
+// One routed row's 128 output columns held by a wave as 8 fragments of 16 columns
+// (lane (c, q) holds columns 16 i + 4 q .. +3 of its row in r[i]): fp16 codes to
+// dst (the row's column 4 q) and the four 32-column scale bytes to sdst (by the
+// q == 0 lanes). Every lane of the wave must call it (the amax goes through lane
+// shuffles); `store` masks the writes.
+__device__ __forceinline__ void store_o_row128(const v4f (&r)[8], bool store, uint16_t* dst, uint8_t* sdst, int q) {
+  int ex[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    float m = 0.f;
+#pragma unroll
+    for (int i = 2 * b; i < 2 * b + 2; ++i)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) m = fmaxf(m, fabsf(r[i][k]));
+    m = fmaxf(m, __shfl_xor(m, 16));
+    m = fmaxf(m, __shfl_xor(m, 32));
+    ex[b] = o_exponent(m);
+  }
+  if (store) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float inv = exp2_neg(ex[i >> 1]);
+      *reinterpret_cast<uint2*>(dst + 16 * i) = f16_pack4(r[i][0] * inv, r[i][1] * inv, r[i][2] * inv, r[i][3] * inv);
+    }
+    if (q == 0)
+      *reinterpret_cast<uint32_t*>(sdst) = (uint32_t)(ex[0] + 127) | ((uint32_t)(ex[1] + 127) << 8) |
+                                           ((uint32_t)(ex[2] + 127) << 16) | ((uint32_t)(ex[3] + 127) << 24);
+  }
+}
+
 __device__ __forceinline__ v4i load16(const void* p) { return *reinterpret_cast<const v4i*>(p); }
 
 // Buffer loads: a wave-uniform resource (base, size in bytes, kept in SGPRs), a

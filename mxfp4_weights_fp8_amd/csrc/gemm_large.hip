@@ -68,7 +68,8 @@ struct LargeArgs {
   const uint8_t* w_s;
   uint8_t* h_q;            // W13 out
   uint8_t* h_s;
-  float* o;                // W2 out
+  uint16_t* o;             // W2 out: fp16 codes per pair slot
+  uint8_t* os;             // and their 32-column scales
   uint32_t act_bytes;      // size of act
   uint32_t act_s_bytes;    // size of act_s
   int act_s_dma;           // act_s rows are 4-byte aligned: copy them with dword copies
@@ -373,13 +374,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_large(LargeArgs a) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int row = 64 * wm + 16 * j + c;
-      if (row < nrows) {
-        const int64_t slot = sSlot[W13 ? 0 : row];
-        float* dst = a.o + slot * a.H + nb * 256 + 128 * wn + q * 4;
+      const int64_t slot = sSlot[W13 ? 0 : (row < nrows ? row : 0)];
+      const int col0 = nb * 256 + 128 * wn;
+      v4f r[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-          *reinterpret_cast<float4*>(dst + 16 * i) = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
-      }
+      for (int i = 0; i < 8; ++i) r[i] = acc[i][j];
+      store_o_row128(r, row < nrows, a.o + slot * a.H + col0 + q * 4, a.os + slot * (a.H / 32) + col0 / 32, q);
     }
   }
 }
@@ -399,7 +399,7 @@ hipError_t launch_w13_large(const moe_dims& d, const int2* items, const int32_t*
   if (max_items <= 0) return hipSuccess;
   const int shift = item_rows == 2 * kTokTile ? 1 : 0;
   const int KS = d.H / 128;
-  LargeArgs a{items, n_items, offsets, sorted_pairs, x_q, x_s, w13, w13_s, h_q, h_s, nullptr,
+  LargeArgs a{items, n_items, offsets, sorted_pairs, x_q, x_s, w13, w13_s, h_q, h_s, nullptr, nullptr,
               (uint32_t)((int64_t)d.T * d.H), (uint32_t)((int64_t)d.T * KS),
               KS % 4 == 0 && (uintptr_t)x_s % 4 == 0, shift, d.H, d.I, d.K};
   hipLaunchKernelGGL(k_gemm_large<true>, dim3(d.I / 128, (unsigned)(max_items << shift)), dim3(kThreads), 0, s, a);
@@ -409,12 +409,12 @@ hipError_t launch_w13_large(const moe_dims& d, const int2* items, const int32_t*
 hipError_t launch_w2_large(const moe_dims& d, const int2* items, const int32_t* n_items, int64_t max_items,
                            int item_rows, const int32_t* offsets, const int32_t* sorted_pairs,
                            const uint8_t* h_q, const uint8_t* h_s, const uint8_t* w2, const uint8_t* w2_s,
-                           float* o, hipStream_t s) {
+                           uint16_t* o, uint8_t* os, hipStream_t s) {
   if (max_items <= 0) return hipSuccess;
   const int shift = item_rows == 2 * kTokTile ? 1 : 0;
   const int KS = d.I / 128;
   const int64_t P = (int64_t)d.T * d.K;
-  LargeArgs a{items, n_items, offsets, sorted_pairs, h_q, h_s, w2, w2_s, nullptr, nullptr, o,
+  LargeArgs a{items, n_items, offsets, sorted_pairs, h_q, h_s, w2, w2_s, nullptr, nullptr, o, os,
               (uint32_t)(P * d.I), (uint32_t)(P * KS), KS % 4 == 0 && (uintptr_t)h_s % 4 == 0,
               shift, d.H, d.I, d.K};
   hipLaunchKernelGGL(k_gemm_large<false>, dim3(d.H / 256, (unsigned)(max_items << shift)), dim3(kThreads), 0, s, a);

@@ -279,7 +279,8 @@ __global__ __launch_bounds__(kThreads) void k_w2_small(
     const SmallLists lists,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_pairs,
     const uint8_t* __restrict__ h_q, const uint8_t* __restrict__ h_s, const uint8_t* __restrict__ w2,
-    const uint8_t* __restrict__ w2_s, float* __restrict__ o, int H, int I) {
+    const uint8_t* __restrict__ w2_s, uint16_t* __restrict__ o, uint8_t* __restrict__ os, int H, int I) {
+  static_assert(NF == 2, "a wave's 16 * NF columns form one 32-column scale block of the per-pair output");
   extern __shared__ __attribute__((aligned(16))) uint8_t sS[];   // [256 weight rows][I/32] E8M0
   const int l = blockIdx.y >= lists.cap0;
   const int item = blockIdx.y - (l ? lists.cap0 : 0);
@@ -320,12 +321,23 @@ __global__ __launch_bounds__(kThreads) void k_w2_small(
 #pragma unroll
     for (int f = 0; f < NF; ++f) acc[f] = v4f{0.f, 0.f, 0.f, 0.f};
     stream_k<NF>(acc, p, KS, 8 * q);
+    // fp16 codes + one scale per 32 columns (the wave's two fragments)
+    float m = 0.f;
+#pragma unroll
+    for (int f = 0; f < NF; ++f)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) m = fmaxf(m, fabsf(acc[f][k]));
+    m = fmaxf(m, __shfl_xor(m, 16));
+    m = fmaxf(m, __shfl_xor(m, 32));
+    const int ex = o_exponent(m);
+    const float inv = exp2_neg(ex);
     if (has) {
       const int64_t slot = sorted_pairs[row0 + c];
-      float* dst = o + slot * H + n_wave + q * 4;
+      uint16_t* dst = o + slot * H + n_wave + q * 4;
 #pragma unroll
       for (int f = 0; f < NF; ++f)
-        *reinterpret_cast<float4*>(dst + f * 16) = make_float4(acc[f][0], acc[f][1], acc[f][2], acc[f][3]);
+        *reinterpret_cast<uint2*>(dst + f * 16) = f16_pack4(acc[f][0] * inv, acc[f][1] * inv, acc[f][2] * inv, acc[f][3] * inv);
+      if (q == 0) os[slot * (H / 32) + n_wave / 32] = (uint8_t)(ex + 127);
     }
   }
 }
@@ -351,7 +363,7 @@ hipError_t launch_w13_small(const moe_dims& d, const SmallLists& lists, const in
 hipError_t launch_w2_small(const moe_dims& d, const SmallLists& lists, const int32_t* offsets,
                            const int32_t* sorted_pairs,
                            const uint8_t* h_q, const uint8_t* h_s, const uint8_t* w2, const uint8_t* w2_s,
-                           float* o, hipStream_t s) {
+                           uint16_t* o, uint8_t* os, hipStream_t s) {
   const int64_t max_items = (int64_t)lists.cap0 + lists.cap1;
   if (max_items <= 0) return hipSuccess;
   constexpr int NF = kW2Frags;
@@ -360,7 +372,7 @@ hipError_t launch_w2_small(const moe_dims& d, const SmallLists& lists, const int
   const size_t lds = (size_t)(kThreads / 64) * staged_bytes(16 * NF * (d.I / 32));
   hipLaunchKernelGGL(k_w2_small<NF>, grid, dim3(kThreads), lds, s, lists,
                      offsets, sorted_pairs,
-                     h_q, h_s, w2, w2_s, o, d.H, d.I);
+                     h_q, h_s, w2, w2_s, o, os, d.H, d.I);
   return hipGetLastError();
 }
 

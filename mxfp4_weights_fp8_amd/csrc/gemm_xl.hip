@@ -76,7 +76,8 @@ struct XlArgs {
   const uint8_t* w_s;
   uint8_t* h_q;            // W13 out
   uint8_t* h_s;
-  float* o;                // W2 out
+  uint16_t* o;             // W2 out: fp16 codes per pair slot
+  uint8_t* os;             // and their 32-column scales
   uint32_t act_bytes;      // size of act
   uint32_t act_s_bytes;    // size of act_s
   int act_s_dma;           // act_s rows are 4-byte aligned: copy them with dword copies
@@ -404,13 +405,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_xl(XlArgs a) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int row = 128 * wm + 16 * j + c;
-      if (row < nrows) {
-        const int64_t slot = sSlot[W13 ? 0 : row];
-        float* dst = a.o + slot * a.H + nb * 256 + 128 * wn + q * 4;
+      const int64_t slot = sSlot[W13 ? 0 : (row < nrows ? row : 0)];
+      const int col0 = nb * 256 + 128 * wn;
+      v4f r[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-          *reinterpret_cast<float4*>(dst + 16 * i) = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
-      }
+      for (int i = 0; i < 8; ++i) r[i] = acc[i][j];
+      store_o_row128(r, row < nrows, a.o + slot * a.H + col0 + q * 4, a.os + slot * (a.H / 32) + col0 / 32, q);
     }
   }
 }
@@ -451,7 +451,7 @@ hipError_t launch_w13_xl(const moe_dims& d, const int2* items, const int32_t* n_
   if (max_items <= 0) return hipSuccess;
   const int KS = d.H / 128;
   const XcdGroups g = xcd_groups(d.I / 128, max_items, (double)kTok * d.H, 256.0 * (d.H / 2 + d.H / 32));
-  XlArgs a{items, n_items, offsets, sorted_pairs, x_q, x_s, w13, w13_s, h_q, h_s, nullptr,
+  XlArgs a{items, n_items, offsets, sorted_pairs, x_q, x_s, w13, w13_s, h_q, h_s, nullptr, nullptr,
            (uint32_t)((int64_t)d.T * d.H), (uint32_t)((int64_t)d.T * KS),
            KS % 4 == 0 && (uintptr_t)x_s % 4 == 0, d.H, d.I, d.K, g.gi, g.gn, g.ngn};
   hipLaunchKernelGGL(k_gemm_xl<true>, dim3((unsigned)g.grid), dim3(kThreads), 0, s, a);
@@ -460,12 +460,12 @@ hipError_t launch_w13_xl(const moe_dims& d, const int2* items, const int32_t* n_
 
 hipError_t launch_w2_xl(const moe_dims& d, const int2* items, const int32_t* n_items, int64_t max_items,
                         const int32_t* offsets, const int32_t* sorted_pairs, const uint8_t* h_q,
-                        const uint8_t* h_s, const uint8_t* w2, const uint8_t* w2_s, float* o, hipStream_t s) {
+                        const uint8_t* h_s, const uint8_t* w2, const uint8_t* w2_s, uint16_t* o, uint8_t* os, hipStream_t s) {
   if (max_items <= 0) return hipSuccess;
   const int KS = d.I / 128;
   const int64_t P = (int64_t)d.T * d.K;
   const XcdGroups g = xcd_groups(d.H / 256, max_items, (double)kTok * d.I, 256.0 * (d.I / 2 + d.I / 32));
-  XlArgs a{items, n_items, offsets, sorted_pairs, h_q, h_s, w2, w2_s, nullptr, nullptr, o,
+  XlArgs a{items, n_items, offsets, sorted_pairs, h_q, h_s, w2, w2_s, nullptr, nullptr, o, os,
            (uint32_t)(P * d.I), (uint32_t)(P * KS), KS % 4 == 0 && (uintptr_t)h_s % 4 == 0, d.H, d.I, d.K,
            g.gi, g.gn, g.ngn};
   hipLaunchKernelGGL(k_gemm_xl<false>, dim3((unsigned)g.grid), dim3(kThreads), 0, s, a);

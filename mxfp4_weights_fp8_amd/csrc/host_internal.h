@@ -68,7 +68,8 @@ struct FfnWs {
   uint8_t* x_s;   // [T, H/128]
   uint8_t* h_q;   // [P, I]
   uint8_t* h_s;   // [P, I/128]
-  float* o;       // [P, H] per-pair W2 outputs, slot p = t*K + j
+  uint16_t* o;    // [P, H] per-pair W2 outputs (fp16 codes of o * 2^-e), slot p = t*K + j
+  uint8_t* os;    // [P, H/32] their scales (byte e + 127 per 32 columns)
   uint8_t* sh_q;  // [T, Is]
   uint8_t* sh_s;  // [T, Is/128]
   float* so;      // [T, H] shared-expert output
@@ -100,7 +101,7 @@ hipError_t launch_w13_small(const moe_dims& d, const SmallLists& lists, const in
                             const uint8_t* w13, const uint8_t* w13_s, uint8_t* h_q, uint8_t* h_s, hipStream_t s);
 hipError_t launch_w2_small(const moe_dims& d, const SmallLists& lists, const int32_t* offsets,
                            const int32_t* sorted_pairs, const uint8_t* h_q, const uint8_t* h_s,
-                           const uint8_t* w2, const uint8_t* w2_s, float* o, hipStream_t s);
+                           const uint8_t* w2, const uint8_t* w2_s, uint16_t* o, uint8_t* os, hipStream_t s);
 // 128-row large-M tiles; item_rows 128 or 256 (a 256-row item runs as two
 // 128-row workgroups).
 bool large_path_supported(const moe_dims& d);
@@ -111,7 +112,7 @@ hipError_t launch_w13_large(const moe_dims& d, const int2* items, const int32_t*
 hipError_t launch_w2_large(const moe_dims& d, const int2* items, const int32_t* n_items, int64_t max_items,
                            int item_rows, const int32_t* offsets, const int32_t* sorted_pairs,
                            const uint8_t* h_q, const uint8_t* h_s, const uint8_t* w2, const uint8_t* w2_s,
-                           float* o, hipStream_t s);
+                           uint16_t* o, uint8_t* os, hipStream_t s);
 // 256 x 256 large-M tiles on 256-row items (a K-step count that is a multiple of 4 and the
 // large-M shape limits).
 bool xl13_supported(const moe_dims& d);
@@ -122,7 +123,7 @@ hipError_t launch_w13_xl(const moe_dims& d, const int2* items, const int32_t* n_
                          uint8_t* h_s, hipStream_t s);
 hipError_t launch_w2_xl(const moe_dims& d, const int2* items, const int32_t* n_items, int64_t max_items,
                         const int32_t* offsets, const int32_t* sorted_pairs, const uint8_t* h_q,
-                        const uint8_t* h_s, const uint8_t* w2, const uint8_t* w2_s, float* o, hipStream_t s);
+                        const uint8_t* h_s, const uint8_t* w2, const uint8_t* w2_s, uint16_t* o, uint8_t* os, hipStream_t s);
 // Dense FP8 shared expert: W13s + SwiGLU/requant into sh_q/sh_s, then W2s into
 // fp32 rows so [T, H]. Needs H/128 and Is/128 at most 64.
 bool dense_path_supported(const moe_dims& d);
@@ -130,7 +131,7 @@ hipError_t launch_shared13(const moe_dims& d, const uint8_t* x_q, const uint8_t*
                            const uint8_t* w13s_s, uint8_t* sh_q, uint8_t* sh_s, hipStream_t s);
 hipError_t launch_shared2(const moe_dims& d, const uint8_t* sh_q, const uint8_t* sh_s, const uint8_t* w2s,
                           const uint8_t* w2s_s, float* so, hipStream_t s);
-hipError_t launch_combine(const float* o, const float* topk_weights, const int32_t* pair_rows, const float* so,
+hipError_t launch_combine(const uint16_t* o, const uint8_t* os, const float* topk_weights, const int32_t* pair_rows, const float* so,
                           uint16_t* y, int T, int H, int K, hipStream_t s);
 
 }  // namespace moe

@@ -17,7 +17,8 @@ size_t ffn_ws_layout(const moe_dims& d, void* base, FfnWs* out) {
   const size_t o_xs = take((size_t)(T * H / 128));
   const size_t o_hq = take((size_t)(P * I));
   const size_t o_hs = take((size_t)(P * I / 128));
-  const size_t o_o = take(sizeof(float) * (size_t)(P * H));
+  const size_t o_o = take(sizeof(uint16_t) * (size_t)(P * H));
+  const size_t o_os = take((size_t)(P * H / 32));
   const size_t o_shq = take((size_t)(T * Is));
   const size_t o_shs = take((size_t)(T * Is / 128));
   const size_t o_so = take(Is ? sizeof(float) * (size_t)(T * H) : 0);
@@ -27,7 +28,8 @@ size_t ffn_ws_layout(const moe_dims& d, void* base, FfnWs* out) {
     out->x_s = reinterpret_cast<uint8_t*>(b + o_xs);
     out->h_q = reinterpret_cast<uint8_t*>(b + o_hq);
     out->h_s = reinterpret_cast<uint8_t*>(b + o_hs);
-    out->o = reinterpret_cast<float*>(b + o_o);
+    out->o = reinterpret_cast<uint16_t*>(b + o_o);
+    out->os = reinterpret_cast<uint8_t*>(b + o_os);
     out->sh_q = reinterpret_cast<uint8_t*>(b + o_shq);
     out->sh_s = reinterpret_cast<uint8_t*>(b + o_shs);
     out->so = reinterpret_cast<float*>(b + o_so);
@@ -182,22 +184,22 @@ int moe_ffn(const moe_dims* dims, const uint16_t* x, const float* topk_weights, 
   }
   record(dbg, MOE_EV_W13_DONE, s);
 
-  err = launch_w2_small(d, sl, expert_offsets, sorted_pairs, h_q, h_s, w2, w2_s, fw.o, s);
+  err = launch_w2_small(d, sl, expert_offsets, sorted_pairs, h_q, h_s, w2, w2_s, fw.o, fw.os, s);
   if (err != hipSuccess) return MOE_EHIP;
   if (any_xl) {
     if (large && xl2_supported(d))
       err = launch_w2_xl(d, pw.xl_items, pw.hdr + 2, pw.xl_cap, expert_offsets, sorted_pairs, h_q, h_s, w2, w2_s,
-                         fw.o, s);
+                         fw.o, fw.os, s);
     else if (large)
       err = launch_w2_large(d, pw.xl_items, pw.hdr + 2, pw.xl_cap, kXlRows, expert_offsets, sorted_pairs, h_q, h_s,
-                            w2, w2_s, fw.o, s);
+                            w2, w2_s, fw.o, fw.os, s);
     else
-      err = launch_w2_small(d, sxl, expert_offsets, sorted_pairs, h_q, h_s, w2, w2_s, fw.o, s);
+      err = launch_w2_small(d, sxl, expert_offsets, sorted_pairs, h_q, h_s, w2, w2_s, fw.o, fw.os, s);
     if (err != hipSuccess) return MOE_EHIP;
   }
   if (any_l && !fold) {
     err = launch_w2_large(d, pw.large_items, pw.hdr + 1, pw.large_cap, kLargeRows, expert_offsets, sorted_pairs,
-                          h_q, h_s, w2, w2_s, fw.o, s);
+                          h_q, h_s, w2, w2_s, fw.o, fw.os, s);
     if (err != hipSuccess) return MOE_EHIP;
   }
   record(dbg, MOE_EV_W2_DONE, s);
@@ -212,7 +214,7 @@ int moe_ffn(const moe_dims* dims, const uint16_t* x, const float* topk_weights, 
   }
   record(dbg, MOE_EV_SHARED_DONE, s);
 
-  err = launch_combine(fw.o, topk_weights, pair_rows, use_shared ? fw.so : nullptr, y, d.T, d.H, d.K, s);
+  err = launch_combine(fw.o, fw.os, topk_weights, pair_rows, use_shared ? fw.so : nullptr, y, d.T, d.H, d.K, s);
   if (err != hipSuccess) return MOE_EHIP;
   record(dbg, MOE_EV_END, s);
   return MOE_OK;

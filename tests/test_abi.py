@@ -61,7 +61,8 @@ def test_workspace_sizes():
     d = moe.make_dims(32768, 7168, 3072, 384, 8)
     ffn = moe.ffn_workspace_bytes(d)
     P = 32768 * 8
-    assert ffn >= 32768 * 7168 + P * 3072 + 4 * P * 7168       # x_q + h_q + fp32 per-pair rows
+    # x_q + h_q + per-pair rows (fp16 codes + one scale byte per 32 columns)
+    assert ffn >= 32768 * 7168 + P * 3072 + 2 * P * 7168 + P * 7168 // 32
     assert moe.plan_workspace_bytes(d) >= 4 * P
     assert moe.ffn_workspace_bytes(moe.make_dims(4, 200, 512, 8, 2)) == 0   # invalid dims -> 0
     small = moe.make_dims(7, 7168, 3072, 384, 8)
