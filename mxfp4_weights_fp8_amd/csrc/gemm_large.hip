@@ -15,7 +15,8 @@
 //        16 h columns, so SwiGLU pairs registers of one lane, and the workgroup
 //        sees whole 128-column scale blocks for the fused FP8 requantization (same
 //        blog, section 4.3).
-//   W2:  256 output columns; the epilogue writes fp32 rows to token-major slots.
+//   W2:  256 output columns; the epilogue writes each pair's row to its token-major
+//        slot (fp16 codes with one power-of-two scale per 32 columns).
 //
 // Data movement: HBM/L2 -> LDS with direct-to-LDS buffer loads (buffer_load_dwordx4
 // ... lds; lane l's 16 bytes land at M0 + 16*l), issued from inline asm with explicit

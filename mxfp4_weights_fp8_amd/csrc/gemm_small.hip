@@ -20,8 +20,8 @@
 // scale block per routed row and writes W2's E4M3 operand and E8M0 scales
 // directly.
 // W2 (down): a workgroup owns 64 * kW2Frags output columns; the epilogue writes
-// each routed pair's fp32 row to its token-major slot p = t*K + j for the top-k
-// combine.
+// each routed pair's row to its token-major slot p = t*K + j for the top-k combine
+// (fp16 codes with one power-of-two scale per 32 columns).
 #include "device_common.h"
 #include "host_internal.h"
 #include "lds_copy.h"
