@@ -17,7 +17,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmoe_mxfp4.so")
 SOURCES = ["moe_api.hip", "plan.hip", "quant.hip", "pack.hip", "gemm_small.hip", "gemm_large.hip", "gemm_xl.hip",
-           "gemm_dense.hip", "combine.hip"]
+           "gemm_fewk.hip", "gemm_dense.hip", "combine.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 
@@ -30,6 +30,7 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno-
 # accumulators through copies inside the K loop (v_accvgpr moves between dependent
 # MFMAs), which halves the MFMA issue rate.
 EXTRA = {"gemm_large.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+         "gemm_fewk.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
          "gemm_dense.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 

@@ -1,0 +1,217 @@
+// W2 grouped GEMM for a short reduction: I <= 384, at most three 128-K steps, as
+// in one MoE-TP8 rank's share of the expert intermediate ("Pushing the Limits of
+// Serving DeepSeek-V4-Pro", section 3.1: MoE-TP splits the 3072 intermediate
+// columns of every expert 8 ways, 384 per rank).
+//
+// With so few K steps, a 128-row x 256-column workgroup of the large-M kernel
+// spends most of its time on its own prologue (routed-row tile, scales, first
+// copies) and epilogue. Here a workgroup keeps its 128 routed rows for every K step
+// in LDS (E4M3, copied once) and walks a run of 256-column blocks of W2: the codes
+// and E8M0 scales of block b+1 are copied into the other half of a double buffer
+// while block b is multiplied and its per-pair rows are written.
+//
+// Waves: a 2 x 2 grid, wave (wm, wn) = routed rows [64 wm, +64) (4 fragments, MFMA B
+// side) x output columns [128 wn, +128) of the block (8 weight fragments, MFMA A
+// side), 32 accumulator tiles of v_mfma_scale_f32_16x16x128_f8f6f4 in VGPRs.
+// LDS (KS = 3: 155,136 bytes): routed rows [step][row][128 B] with the 16-byte chunk
+// index XORed by (row / 2) % 8; weights [buffer][step][fragment][1 KB in the
+// MFMA's lane order] (the kernel-native layout, copied block by block); weight
+// scales [buffer][row][4 KS B] in their global order; activation scales one dword
+// per routed row.
+#include "device_common.h"
+#include "host_internal.h"
+#include "lds_copy.h"
+
+namespace moe {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kRows = kLargeRows;   // routed rows per workgroup
+constexpr int kCols = 256;          // output columns per block
+constexpr int kMaxKS = 3;
+
+struct FewKArgs {
+  const int2* items;
+  const int32_t* n_items;
+  const int32_t* offsets;
+  const int32_t* sorted_pairs;
+  const uint8_t* h_q;      // [P, I] E4M3, rows in plan order
+  const uint8_t* h_s;      // [P, I/128] E8M0
+  const uint8_t* w2;       // [E, H, I/2], kernel-native layout
+  const uint8_t* w2_s;     // [E, H, I/32]
+  uint16_t* o;             // per-pair rows: fp16 codes
+  uint8_t* os;             // and their 32-column scales
+  uint32_t h_bytes;        // size of h_q
+  int item_shift;          // 1: items hold 256 rows, workgroup y covers half y % 2 of item y / 2
+  int H, I;
+  int blocks_per_wg;       // 256-column blocks per workgroup (the last run may be shorter)
+};
+
+template <int KS>
+__global__ __launch_bounds__(kThreads, 1) void k_w2_fewk(FewKArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint8_t sB[KS][kRows * 128];      // [step][row][128 B]
+  __shared__ __attribute__((aligned(1024))) uint8_t sA[2][KS][16 * 1024];     // [buf][step][fragment][1 KB]
+  __shared__ __attribute__((aligned(16))) uint8_t sSa[2][kCols * 4 * KS];      // [buf][row][4 KS B]
+  __shared__ uint32_t sSb[kRows];                                              // [row] byte s = step s
+  __shared__ int sTok[kRows];
+  __shared__ int sSlot[kRows];
+
+  const int item = blockIdx.y >> a.item_shift;
+  if (item >= a.n_items[0]) return;
+  const int2 it = a.items[item];
+  const int e = it.x;
+  const int e_begin = a.offsets[e], e_end = a.offsets[e + 1];
+  const int row0 = e_begin + it.y + (blockIdx.y & a.item_shift) * kRows;   // first sorted row of the tile
+  const int nrows = min(kRows, e_end - row0);
+  if (nrows <= 0) return;                               // empty second half of a 256-row item
+  const int n_blocks = a.H / kCols;
+  const int b_first = blockIdx.x * a.blocks_per_wg;
+  const int b_count = min(n_blocks, b_first + a.blocks_per_wg) - b_first;
+  if (b_count <= 0) return;
+  const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4, c = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave & 1, wn = wave >> 1;
+  const int I = a.I, srow = I / 32;                     // srow = 4 KS scale bytes per weight row
+
+  // routed rows of the tile (padding repeats the first row), their output slots and
+  // activation scales (KS bytes per row, one dword)
+  if (tid < kRows) {
+    const int r = row0 + (tid < nrows ? tid : 0);
+    sTok[tid] = r;
+    sSlot[tid] = a.sorted_pairs[r];
+    uint32_t v = 0;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) v |= (uint32_t)a.h_s[(int64_t)r * KS + s] << (8 * s);
+    sSb[tid] = v;
+  }
+  __syncthreads();
+
+  const int64_t w_bytes = (int64_t)a.H * (I / 2);
+  const v4i_s ra = rsrc4(a.h_q, a.h_bytes);
+  const v4i_s rw = rsrc4(a.w2 + (int64_t)e * w_bytes, (uint32_t)w_bytes);
+  const v4i_s rws = rsrc4(a.w2_s + (int64_t)e * a.H * srow, (uint32_t)(a.H * srow));
+
+  // Routed rows, once: instruction (s, i) of wave w copies rows 32w + 8i .. +7 of K
+  // step s, lane l -> row + l/8, physical chunk l%8 holding logical chunk
+  // (l%8) ^ (row / 2) % 8.
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = 32 * wave + 8 * i + (lane >> 3);
+    const int off = sTok[row] * I + (((lane & 7) ^ ((row >> 1) & 7)) << 4);
+#pragma unroll
+    for (int s = 0; s < KS; ++s) dma16(ra, lds_addr(&sB[s][(32 * wave + 8 * i) * 128]), off + s * 128, 0);
+  }
+  // Weight block b into buffer buf: wave w copies fragments 4w .. 4w+3 (expert rows
+  // 256b + 16f ..) for every K step, then KS blocks of 256 scale bytes of the
+  // block's 256 contiguous scale rows.
+  auto copy_block = [&](int b, int buf) {
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      const int frag = 4 * wave + f;
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+        dma16(rw, lds_addr(&sA[buf][s][frag * 1024]), (16 * b + frag) * 16 * (I / 2) + s * 1024 + lane * 16, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < KS; ++i) {
+      const int blk = KS * wave + i;
+      dma4(rws, lds_addr(&sSa[buf][blk * 256]), b * kCols * srow + blk * 256 + lane * 4, 0);
+    }
+  };
+  constexpr int kCopiesPerBlock = 5 * KS;               // per wave
+  copy_block(b_first, 0);
+
+  // operand read offsets: routed-row fragment j = rows 64 wm + 16 j + c, whose
+  // swizzle (row / 2) % 8 is (c / 2) % 8; lane (c, q) reads logical chunks q and 4+q
+  const int offB0 = (64 * wm + c) * 128 + ((q ^ (c >> 1)) << 4);
+  const int offB1 = (64 * wm + c) * 128 + (((4 + q) ^ (c >> 1)) << 4);
+
+  for (int bi = 0; bi < b_count; ++bi) {
+    const int buf = bi & 1;
+    if (bi + 1 < b_count) {
+      copy_block(b_first + bi + 1, buf ^ 1);
+      wait_vmcnt<kCopiesPerBlock>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    __syncthreads();
+
+    v4f acc[8][4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      v8i bf[4];
+      int sb[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const v4i lo = *reinterpret_cast<const v4i*>(&sB[s][offB0 + j * 16 * 128]);
+        const v4i hi = *reinterpret_cast<const v4i*>(&sB[s][offB1 + j * 16 * 128]);
+        bf[j][0] = lo[0]; bf[j][1] = lo[1]; bf[j][2] = lo[2]; bf[j][3] = lo[3];
+        bf[j][4] = hi[0]; bf[j][5] = hi[1]; bf[j][6] = hi[2]; bf[j][7] = hi[3];
+        sb[j] = (int)((sSb[64 * wm + 16 * j + c] >> (8 * s)) & 0xFFu);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int frag = 8 * wn + i;
+        const v4i w = *reinterpret_cast<const v4i*>(&sA[buf][s][frag * 1024 + lane * 16]);
+        const int sa = sSa[buf][(frag * 16 + c) * srow + 4 * s + q];
+        v8i aop;
+        aop[0] = w[0]; aop[1] = w[1]; aop[2] = w[2]; aop[3] = w[3];
+        aop[4] = 0; aop[5] = 0; aop[6] = 0; aop[7] = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = mfma_scale_16x16x128<kFmtE2M1, kFmtE4M3>(aop, bf[j], acc[i][j], sa, sb[j]);
+      }
+    }
+
+    // per-pair rows of this block: lane (c, q) of routed-row fragment j holds output
+    // columns 16 i + 4 q .. +3 of the wave's 128
+    const int col0 = (b_first + bi) * kCols + 128 * wn;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = 64 * wm + 16 * j + c;
+      const int64_t slot = sSlot[row < nrows ? row : 0];
+      v4f r[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) r[i] = acc[i][j];
+      store_o_row128(r, row < nrows, a.o + slot * a.H + col0 + q * 4, a.os + slot * (a.H / 32) + col0 / 32, q);
+    }
+    __syncthreads();   // every wave has read buffer buf before block bi+2 is copied into it
+  }
+}
+
+}  // namespace
+
+bool fewk2_supported(const moe_dims& d) {
+  const int64_t P = (int64_t)d.T * d.K;
+  return d.I / 128 <= kMaxKS && d.H % kCols == 0 && P * d.I < ((int64_t)1 << 31) &&
+         (int64_t)d.H * (d.I / 2) < ((int64_t)1 << 31);
+}
+
+hipError_t launch_w2_fewk(const moe_dims& d, const int2* items, const int32_t* n_items, int64_t max_items,
+                          int item_rows, const int32_t* offsets, const int32_t* sorted_pairs, const uint8_t* h_q,
+                          const uint8_t* h_s, const uint8_t* w2, const uint8_t* w2_s, uint16_t* o, uint8_t* os,
+                          hipStream_t s) {
+  if (max_items <= 0) return hipSuccess;
+  const int shift = item_rows == 2 * kRows ? 1 : 0;
+  const int n_blocks = d.H / kCols;
+  // two runs of column blocks per routed-row tile: twice the workgroups of one run
+  // (a shorter tail at the end of the grid) for one more copy of the routed rows
+  const int per_wg = n_blocks >= 2 ? (n_blocks + 1) / 2 : 1;
+  const int64_t P = (int64_t)d.T * d.K;
+  FewKArgs a{items, n_items, offsets, sorted_pairs, h_q, h_s, w2, w2_s, o, os, (uint32_t)(P * d.I), shift,
+             d.H, d.I, per_wg};
+  dim3 grid((unsigned)ceil_div(n_blocks, per_wg), (unsigned)(max_items << shift));
+  switch (d.I / 128) {
+    case 1: hipLaunchKernelGGL(k_w2_fewk<1>, grid, dim3(kThreads), 0, s, a); break;
+    case 2: hipLaunchKernelGGL(k_w2_fewk<2>, grid, dim3(kThreads), 0, s, a); break;
+    case 3: hipLaunchKernelGGL(k_w2_fewk<3>, grid, dim3(kThreads), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe

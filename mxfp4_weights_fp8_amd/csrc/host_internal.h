@@ -115,6 +115,13 @@ hipError_t launch_w2_large(const moe_dims& d, const int2* items, const int32_t* 
                            uint16_t* o, uint8_t* os, hipStream_t s);
 // 256 x 256 large-M tiles on 256-row items (a K-step count that is a multiple of 4 and the
 // large-M shape limits).
+// W2 with at most 3 K steps (I <= 384): a workgroup keeps its 128 routed rows in LDS
+// and walks a run of 256-column blocks.
+bool fewk2_supported(const moe_dims& d);
+hipError_t launch_w2_fewk(const moe_dims& d, const int2* items, const int32_t* n_items, int64_t max_items,
+                          int item_rows, const int32_t* offsets, const int32_t* sorted_pairs, const uint8_t* h_q,
+                          const uint8_t* h_s, const uint8_t* w2, const uint8_t* w2_s, uint16_t* o, uint8_t* os,
+                          hipStream_t s);
 bool xl13_supported(const moe_dims& d);
 bool xl2_supported(const moe_dims& d);
 hipError_t launch_w13_xl(const moe_dims& d, const int2* items, const int32_t* n_items, int64_t max_items,

@@ -186,8 +186,12 @@ int moe_ffn(const moe_dims* dims, const uint16_t* x, const float* topk_weights, 
 
   err = launch_w2_small(d, sl, expert_offsets, sorted_pairs, h_q, h_s, w2, w2_s, fw.o, fw.os, s);
   if (err != hipSuccess) return MOE_EHIP;
+  const bool fewk = large && fewk2_supported(d);
   if (any_xl) {
-    if (large && xl2_supported(d))
+    if (fewk)
+      err = launch_w2_fewk(d, pw.xl_items, pw.hdr + 2, pw.xl_cap, kXlRows, expert_offsets, sorted_pairs, h_q, h_s,
+                           w2, w2_s, fw.o, fw.os, s);
+    else if (large && xl2_supported(d))
       err = launch_w2_xl(d, pw.xl_items, pw.hdr + 2, pw.xl_cap, expert_offsets, sorted_pairs, h_q, h_s, w2, w2_s,
                          fw.o, fw.os, s);
     else if (large)
@@ -198,8 +202,12 @@ int moe_ffn(const moe_dims* dims, const uint16_t* x, const float* topk_weights, 
     if (err != hipSuccess) return MOE_EHIP;
   }
   if (any_l && !fold) {
-    err = launch_w2_large(d, pw.large_items, pw.hdr + 1, pw.large_cap, kLargeRows, expert_offsets, sorted_pairs,
-                          h_q, h_s, w2, w2_s, fw.o, fw.os, s);
+    if (fewk)
+      err = launch_w2_fewk(d, pw.large_items, pw.hdr + 1, pw.large_cap, kLargeRows, expert_offsets, sorted_pairs,
+                           h_q, h_s, w2, w2_s, fw.o, fw.os, s);
+    else
+      err = launch_w2_large(d, pw.large_items, pw.hdr + 1, pw.large_cap, kLargeRows, expert_offsets, sorted_pairs,
+                            h_q, h_s, w2, w2_s, fw.o, fw.os, s);
     if (err != hipSuccess) return MOE_EHIP;
   }
   record(dbg, MOE_EV_W2_DONE, s);

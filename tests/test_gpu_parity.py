@@ -162,6 +162,12 @@ def test_ffn_tiny(dev, small_max):
     (300, 768, 256, 1, 1, 54, 0),
     (400, 512, 512, 1, 1, 55, 0),
     (700, 1024, 512, 2, 1, 56, 0),
+    # W2 with 1..3 K steps on the few-K kernel (routed rows kept in LDS, runs of
+    # 256-column blocks; H 1280 = 5 blocks -> runs of 3 and 2): one expert with a
+    # 256-row item and a remainder, several experts with 128-row items only
+    (300, 512, 128, 1, 1, 57, 0),
+    (400, 1280, 256, 3, 2, 58, 0),
+    (600, 1280, 384, 2, 1, 59, 0),
 ])
 def test_ffn_shapes(dev, T, H, I, E, K, seed, small_max):
     wl = scaled("tiny", T=T, H=H, I=I, E=E, K=K, seed=seed, weight_seed=seed, name=f"s{seed}")
