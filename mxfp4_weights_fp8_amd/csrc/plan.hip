@@ -12,7 +12,8 @@
 //      rounds. No atomics decide an order, so the result is deterministic.
 //   2. scan: per expert, an exclusive scan over blocks, then over experts ->
 //      expert_offsets; the work lists are built from the per-expert counts.
-//   3. scatter: position = block base of the pair's expert + local rank.
+//   3. scatter: position = expert offset + block base of the pair's expert +
+//      local rank.
 // One block (P <= kPlanChunk, the decode shapes) runs all three phases in a
 // single fused launch; larger P uses three launches.
 #include "device_common.h"
@@ -59,12 +60,14 @@ __device__ int block_exclusive_scan(int32_t* a, int n, int32_t* part) {
   return total;
 }
 
-// Phase 1 for pairs [begin, end): local_rank[p] = number of earlier pairs of the
-// same expert inside [begin, end). cursor[E] must start at zero and ends holding
-// the per-expert counts of the range; wcnt[kPlanWaves * E] must start at zero and
-// ends at zero.
+// Phase 1 for pairs [begin, end): local_rank[p - rank_base] = number of earlier
+// pairs of the same expert inside [begin, end); key[p - rank_base] (when given) =
+// the pair's expert, or -1 for an id outside [0, E). cursor[E] must start at zero
+// and ends holding the per-expert counts of the range; wcnt[kPlanWaves * E] must
+// start at zero and ends at zero.
 __device__ void local_ranks(const int32_t* __restrict__ ids, int begin, int end, int E, int nbits,
-                            int32_t* __restrict__ local_rank, int32_t* cursor, int32_t* wcnt) {
+                            int32_t* __restrict__ local_rank, int rank_base, int32_t* key_out, int32_t* cursor,
+                            int32_t* wcnt) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const uint64_t lower = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   for (int base = begin; base < end; base += kPlanThreads) {
@@ -75,6 +78,7 @@ __device__ void local_ranks(const int32_t* __restrict__ ids, int begin, int end,
       key = (v >= 0 && v < E) ? v : -1;
     }
     const bool valid = key >= 0;
+    if (key_out && p < end) key_out[p - rank_base] = key;
     uint64_t peer = __ballot(valid);
     for (int bit = 0; bit < nbits; ++bit) {
       const bool b = valid && ((key >> bit) & 1);
@@ -89,7 +93,7 @@ __device__ void local_ranks(const int32_t* __restrict__ ids, int begin, int end,
     if (valid) {
       int r = cursor[key] + rank;
       for (int w = 0; w < wave; ++w) r += wcnt[w * E + key];
-      local_rank[p] = r;
+      local_rank[p - rank_base] = r;
     }
     __syncthreads();
     if (leader) {
@@ -204,10 +208,12 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan_fused(PlanArgs a) {
   int32_t* a1 = off + E + 1;                  // [E]
   int32_t* a2 = a1 + E;                       // [E]
   int32_t* part = a2 + E;                     // [kPlanThreads]
+  int32_t* rank = part + kPlanThreads;        // [P] local ranks
+  int32_t* key = rank + a.P;                  // [P] experts (-1: dropped)
   const int t = threadIdx.x;
   for (int i = t; i < (kPlanWaves + 1) * E; i += kPlanThreads) lds[i] = 0;
   __syncthreads();
-  local_ranks(a.ids, 0, a.P, E, a.nbits, a.local_rank, cnt, wcnt);
+  local_ranks(a.ids, 0, a.P, E, a.nbits, rank, 0, key, cnt, wcnt);
   for (int e = t; e < E; e += kPlanThreads) off[e] = cnt[e];
   __syncthreads();
   const int n_valid = block_exclusive_scan(off, E, part);
@@ -217,10 +223,10 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan_fused(PlanArgs a) {
   }
   __syncthreads();
   for (int e = t; e <= E; e += kPlanThreads) a.offsets[e] = off[e];
-  for (int p = t; p < a.P; p += kPlanThreads) {
-    const int v = a.ids[p];
-    if (v >= 0 && v < E) {
-      const int pos = off[v] + a.local_rank[p];
+  for (int p = t; p < a.P; p += kPlanThreads) {   // the thread that ranked pair p
+    const int v = key[p];
+    if (v >= 0) {
+      const int pos = off[v] + rank[p];
       a.sorted_pairs[pos] = p;
       a.pair_rows[p] = pos;
     } else {
@@ -243,7 +249,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan_local(PlanArgs a) {
   __syncthreads();
   const int begin = b * kPlanChunk;
   const int end = min(a.P, begin + kPlanChunk);
-  local_ranks(a.ids, begin, end, E, a.nbits, a.local_rank, cnt, wcnt);
+  local_ranks(a.ids, begin, end, E, a.nbits, a.local_rank, 0, nullptr, cnt, wcnt);
   for (int e = t; e < E; e += kPlanThreads) a.block_counts[(int64_t)b * E + e] = cnt[e];
 }
 
@@ -256,16 +262,46 @@ __global__ __launch_bounds__(kScanThreads) void k_plan_scan(PlanArgs a) {
   int32_t* a1 = off + E + 1;        // [E]
   int32_t* a2 = a1 + E;             // [E]
   int32_t* part = a2 + E;           // [kScanThreads]
-  const int t = threadIdx.x;
-  for (int e = t; e < E; e += kScanThreads) {
-    int run = 0;
-    for (int b = 0; b < nb; ++b) {
-      const int c = a.block_counts[(int64_t)b * E + e];
-      a.block_base[(int64_t)b * E + e] = run;
-      run += c;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  constexpr int kWaves = kScanThreads / 64;
+  constexpr int kBatch = 8;                 // experts whose counts one wave loads at once
+  // Per expert, the exclusive scan of its block counts over the blocks (the rank of
+  // a block's first pair of that expert among the expert's pairs): one wave per
+  // expert, 64 blocks per round, lane shuffles; a wave loads the counts of kBatch
+  // experts before it scans any, so their load latencies overlap.
+  for (int e0 = wave; e0 < E; e0 += kWaves * kBatch) {
+    int run[kBatch];
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) run[k] = 0;
+    for (int b0 = 0; b0 < nb; b0 += 64) {
+      const int b = b0 + lane;
+      int c[kBatch];
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k) {
+        const int e = e0 + k * kWaves;
+        c[k] = (b < nb && e < E) ? a.block_counts[(int64_t)b * E + e] : 0;
+      }
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k) {
+        const int e = e0 + k * kWaves;
+        int v = c[k];
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const int u = __shfl_up(v, o);
+          if (lane >= o) v += u;
+        }
+        if (b < nb && e < E) a.block_base[(int64_t)b * E + e] = run[k] + v - c[k];
+        run[k] += __shfl(v, 63);
+      }
     }
-    cnt[e] = run;
-    off[e] = run;
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const int e = e0 + k * kWaves;
+      if (lane == 0 && e < E) {
+        cnt[e] = run[k];
+        off[e] = run[k];
+      }
+    }
   }
   __syncthreads();
   const int n_valid = block_exclusive_scan(off, E, part);
@@ -275,8 +311,6 @@ __global__ __launch_bounds__(kScanThreads) void k_plan_scan(PlanArgs a) {
   }
   __syncthreads();
   for (int e = t; e <= E; e += kScanThreads) a.offsets[e] = off[e];
-  for (int e = t; e < E; e += kScanThreads)
-    for (int b = 0; b < nb; ++b) a.block_base[(int64_t)b * E + e] += off[e];
   build_worklists(cnt, E, a.small_max, a.small_items, a.small_cap, a.large_items, a.large_cap, a.xl_items, a.xl_cap,
                   a.hdr, a1, a2, part);
 }
@@ -287,7 +321,7 @@ __global__ __launch_bounds__(256) void k_plan_scatter(PlanArgs a) {
   if (p >= a.P) return;
   const int v = a.ids[p];
   if (v >= 0 && v < a.E) {
-    const int pos = a.block_base[(int64_t)(p / kPlanChunk) * a.E + v] + a.local_rank[p];
+    const int pos = a.offsets[v] + a.block_base[(int64_t)(p / kPlanChunk) * a.E + v] + a.local_rank[p];
     a.sorted_pairs[pos] = p;
     a.pair_rows[p] = pos;
   } else {
@@ -358,7 +392,7 @@ hipError_t launch_plan(const moe_dims& d, const int32_t* ids, int32_t* offsets, 
   a.small_max = small_max_of(d);
   a.nb = (int)ws.nb;
   if (a.P <= kPlanChunk) {
-    const size_t lds = sizeof(int32_t) * ((size_t)(kPlanWaves + 4) * d.E + 1 + kPlanThreads);
+    const size_t lds = sizeof(int32_t) * ((size_t)(kPlanWaves + 4) * d.E + 1 + kPlanThreads + 2 * (size_t)a.P);
     if (lds > 65536) {
       hipError_t e = hipFuncSetAttribute((const void*)k_plan_fused, hipFuncAttributeMaxDynamicSharedMemorySize,
                                          (int)lds);
