@@ -56,8 +56,8 @@ struct PlanWs {
   int2* large_items;      // 128-row items
   int2* xl_items;         // 256-row items
   int32_t* local_rank;    // [P]
-  int32_t* block_counts;  // [NB * E]
-  int32_t* block_base;    // [NB * E]
+  int32_t* block_counts;  // [E][NB]
+  int32_t* block_base;    // [E][NB]
   int64_t small_cap, large_cap, xl_cap, nb;
 };
 size_t plan_ws_layout(const moe_dims& d, void* base, PlanWs* out);

@@ -250,7 +250,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan_local(PlanArgs a) {
   const int begin = b * kPlanChunk;
   const int end = min(a.P, begin + kPlanChunk);
   local_ranks(a.ids, begin, end, E, a.nbits, a.local_rank, 0, nullptr, cnt, wcnt);
-  for (int e = t; e < E; e += kPlanThreads) a.block_counts[(int64_t)b * E + e] = cnt[e];
+  for (int e = t; e < E; e += kPlanThreads) a.block_counts[(int64_t)e * a.nb + b] = cnt[e];   // [E][nb]
 }
 
 // Multi-block phase 2 (one block of kScanThreads).
@@ -268,7 +268,8 @@ __global__ __launch_bounds__(kScanThreads) void k_plan_scan(PlanArgs a) {
   // Per expert, the exclusive scan of its block counts over the blocks (the rank of
   // a block's first pair of that expert among the expert's pairs): one wave per
   // expert, 64 blocks per round, lane shuffles; a wave loads the counts of kBatch
-  // experts before it scans any, so their load latencies overlap.
+  // experts before it scans any, so their load latencies overlap. Counts and bases
+  // are stored [expert][block], so a wave's load covers 64 consecutive words.
   for (int e0 = wave; e0 < E; e0 += kWaves * kBatch) {
     int run[kBatch];
 #pragma unroll
@@ -279,7 +280,7 @@ __global__ __launch_bounds__(kScanThreads) void k_plan_scan(PlanArgs a) {
 #pragma unroll
       for (int k = 0; k < kBatch; ++k) {
         const int e = e0 + k * kWaves;
-        c[k] = (b < nb && e < E) ? a.block_counts[(int64_t)b * E + e] : 0;
+        c[k] = (b < nb && e < E) ? a.block_counts[(int64_t)e * nb + b] : 0;
       }
 #pragma unroll
       for (int k = 0; k < kBatch; ++k) {
@@ -290,7 +291,7 @@ __global__ __launch_bounds__(kScanThreads) void k_plan_scan(PlanArgs a) {
           const int u = __shfl_up(v, o);
           if (lane >= o) v += u;
         }
-        if (b < nb && e < E) a.block_base[(int64_t)b * E + e] = run[k] + v - c[k];
+        if (b < nb && e < E) a.block_base[(int64_t)e * nb + b] = run[k] + v - c[k];
         run[k] += __shfl(v, 63);
       }
     }
@@ -321,7 +322,7 @@ __global__ __launch_bounds__(256) void k_plan_scatter(PlanArgs a) {
   if (p >= a.P) return;
   const int v = a.ids[p];
   if (v >= 0 && v < a.E) {
-    const int pos = a.offsets[v] + a.block_base[(int64_t)(p / kPlanChunk) * a.E + v] + a.local_rank[p];
+    const int pos = a.offsets[v] + a.block_base[(int64_t)v * a.nb + p / kPlanChunk] + a.local_rank[p];
     a.sorted_pairs[pos] = p;
     a.pair_rows[p] = pos;
   } else {
