@@ -192,6 +192,31 @@ def test_ffn_shared_shapes(dev, T, H, I, E, K, Is, seed, small_max):
     check_ffn(inp, p, y, dbg, label=f"shared {T}x{H} I{I} Is{Is} E{E} K{K}")
 
 
+@pytest.mark.parametrize("T,H,I,E,K,seed", [
+    (3, 16384, 256, 4, 2, 60),     # H at the small-M limit (W13 scale runs of 8 KB per wave in LDS)
+    (2, 256, 16384, 2, 1, 61),     # I at the small-M limit (W2 scale runs of 4*I bytes)
+    (300, 8192, 256, 1, 1, 62),    # H/128 = 64 K steps, the most the large-M tiles keep scales for
+    (300, 8320, 256, 1, 1, 63),    # 65 K steps: the large-M tiles do not apply, the small-M kernels walk the items
+])
+def test_ffn_size_limits(dev, T, H, I, E, K, seed):
+    wl = scaled("tiny", T=T, H=H, I=I, E=E, K=K, seed=seed, weight_seed=seed, name=f"lim{seed}")
+    inp = make_inputs(wl).to(dev)
+    p, (y, dbg) = run_path(inp)
+    check_ffn(inp, p, y, dbg, label=f"limit {T}x{H} I{I} E{E} K{K}")
+
+
+def test_ffn_empty_batch(dev):
+    """T = 0 is a valid no-op for both calls."""
+    wl = scaled("tiny", T=1, name="empty")
+    W = moe.pack_weights(make_inputs(wl).to(dev).weights)
+    ids = torch.zeros((0, wl.K), dtype=torch.int32, device=dev)
+    p = moe.plan(ids, wl.E, wl.H, wl.I)
+    y = moe.ffn(torch.zeros((0, wl.H), dtype=torch.bfloat16, device=dev),
+                torch.zeros((0, wl.K), dtype=torch.float32, device=dev), p, W)
+    torch.cuda.synchronize()
+    assert tuple(y.shape) == (0, wl.H)
+
+
 def test_ffn_invalid_ids(dev):
     inp = make_inputs("tiny").to(dev)
     ids = inp.topk_ids.clone()
