@@ -20,7 +20,8 @@ __device__ __forceinline__ float f16_hi(uint32_t v) { return (float)__builtin_bi
 __global__ __launch_bounds__(kThreads) void k_combine(const uint16_t* __restrict__ o, const uint8_t* __restrict__ os,
                                                        const float* __restrict__ w,
                                                        const int32_t* __restrict__ pair_rows,
-                                                       const float* __restrict__ so, uint16_t* __restrict__ y,
+                                                       const uint16_t* __restrict__ so,
+                                                       const uint8_t* __restrict__ sos, uint16_t* __restrict__ y,
                                                        int64_t n_groups, int groups_per_row, int K) {
   const int scales_per_row = groups_per_row / 4;   // one scale per 32 columns = 4 groups of 8
   for (int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x; g < n_groups; g += (int64_t)gridDim.x * kThreads) {
@@ -54,11 +55,15 @@ __global__ __launch_bounds__(kThreads) void k_combine(const uint16_t* __restrict
         }
       }
     }
-    if (so) {
-      const float4 a = reinterpret_cast<const float4*>(so)[2 * g];
-      const float4 b = reinterpret_cast<const float4*>(so)[2 * g + 1];
-      acc[0] += a.x; acc[1] += a.y; acc[2] += a.z; acc[3] += a.w;
-      acc[4] += b.x; acc[5] += b.y; acc[6] += b.z; acc[7] += b.w;
+    if (so) {   // the shared expert's row, same storage as the per-pair rows, added last
+      const uint4 v = reinterpret_cast<const uint4*>(so)[g];
+      const int ex = (int)sos[t * scales_per_row + (c8 >> 2)] - 127;
+      const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        acc[2 * k] += __builtin_amdgcn_ldexpf(f16_lo(u[k]), ex);
+        acc[2 * k + 1] += __builtin_amdgcn_ldexpf(f16_hi(u[k]), ex);
+      }
     }
     uint4 r;
     r.x = (uint32_t)bf16_rne(acc[0]) | ((uint32_t)bf16_rne(acc[1]) << 16);
@@ -72,12 +77,12 @@ __global__ __launch_bounds__(kThreads) void k_combine(const uint16_t* __restrict
 }  // namespace
 
 hipError_t launch_combine(const uint16_t* o, const uint8_t* os, const float* topk_weights, const int32_t* pair_rows,
-                          const float* so, uint16_t* y, int T, int H, int K, hipStream_t s) {
+                          const uint16_t* so, const uint8_t* sos, uint16_t* y, int T, int H, int K, hipStream_t s) {
   const int64_t n_groups = (int64_t)T * (H / 8);
   if (n_groups == 0) return hipSuccess;
   int64_t ctas = ceil_div(n_groups, kThreads);
   if (ctas > 256 * 32) ctas = 256 * 32;
-  hipLaunchKernelGGL(k_combine, dim3((unsigned)ctas), dim3(kThreads), 0, s, o, os, topk_weights, pair_rows, so, y,
+  hipLaunchKernelGGL(k_combine, dim3((unsigned)ctas), dim3(kThreads), 0, s, o, os, topk_weights, pair_rows, so, sos, y,
                      n_groups, H / 8, K);
   return hipGetLastError();
 }

@@ -13,7 +13,8 @@
 //   W13s: weight rows = gate rows [n0, n0+128) and up rows [Is+n0, Is+n0+128);
 //         the epilogue applies SwiGLU and requantizes each token's 128 h columns
 //         to E4M3 with one E8M0 scale (same blog, section 4.3).
-//   W2s:  256 output columns, fp32 rows [T, H] for the combine; when H is an odd
+//   W2s:  256 output columns, rows [T, H] for the combine (fp16 codes with one
+//         power-of-two scale per 32 columns, as the routed per-pair rows); when H is an odd
 //         multiple of 128 the last tile's second half reads zeros and is not stored.
 //
 // Data movement: three one-step LDS stages (32 KB of weight codes + 16 KB of
@@ -46,7 +47,8 @@ struct DenseArgs {
   const uint8_t* w_s;      // [N/128, Kd/128] E8M0
   uint8_t* h_q;            // W13s out [T, Is]
   uint8_t* h_s;            // [T, Is/128]
-  float* o;                // W2s out [T, N]
+  uint16_t* o;             // W2s out [T, N]: fp16 codes
+  uint8_t* os;             // and their 32-column scales [T, N/32]
   uint32_t act_bytes, w_bytes;
   int T, Kd, N, Is;
 };
@@ -260,17 +262,15 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_dense(DenseArgs a) {
     }
   } else {
     const int col0 = nb * 256 + 128 * wn;
-    if (col0 < a.N) {
+    if (col0 < a.N) {   // wave-uniform
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int row = 64 * wm + 16 * j + c;
-        if (row < nrows) {
-          float* dst = a.o + (int64_t)(t0 + row) * a.N + col0 + q * 4;
+        const int64_t t = t0 + (row < nrows ? row : 0);
+        v4f r[8];
 #pragma unroll
-          for (int i = 0; i < 8; ++i)
-            *reinterpret_cast<float4*>(dst + 16 * i) =
-                make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
-        }
+        for (int i = 0; i < 8; ++i) r[i] = acc[i][j];
+        store_o_row128(r, row < nrows, a.o + t * a.N + col0 + q * 4, a.os + t * (a.N / 32) + col0 / 32, q);
       }
     }
   }
@@ -282,7 +282,7 @@ bool dense_path_supported(const moe_dims& d) { return d.H / 128 <= kMaxSteps && 
 
 hipError_t launch_shared13(const moe_dims& d, const uint8_t* x_q, const uint8_t* x_s, const uint8_t* w13s,
                            const uint8_t* w13s_s, uint8_t* sh_q, uint8_t* sh_s, hipStream_t s) {
-  DenseArgs a{x_q, x_s, w13s, w13s_s, sh_q, sh_s, nullptr,
+  DenseArgs a{x_q, x_s, w13s, w13s_s, sh_q, sh_s, nullptr, nullptr,
               (uint32_t)((int64_t)d.T * d.H), (uint32_t)((int64_t)2 * d.Is * d.H), d.T, d.H, 2 * d.Is, d.Is};
   hipLaunchKernelGGL(k_gemm_dense<true>, dim3(d.Is / 128, (unsigned)ceil_div(d.T, kTokRows)), dim3(kThreads), 0, s,
                      a);
@@ -290,8 +290,8 @@ hipError_t launch_shared13(const moe_dims& d, const uint8_t* x_q, const uint8_t*
 }
 
 hipError_t launch_shared2(const moe_dims& d, const uint8_t* sh_q, const uint8_t* sh_s, const uint8_t* w2s,
-                          const uint8_t* w2s_s, float* so, hipStream_t s) {
-  DenseArgs a{sh_q, sh_s, w2s, w2s_s, nullptr, nullptr, so,
+                          const uint8_t* w2s_s, uint16_t* so, uint8_t* sos, hipStream_t s) {
+  DenseArgs a{sh_q, sh_s, w2s, w2s_s, nullptr, nullptr, so, sos,
               (uint32_t)((int64_t)d.T * d.Is), (uint32_t)((int64_t)d.H * d.Is), d.T, d.Is, d.H, d.Is};
   hipLaunchKernelGGL(k_gemm_dense<false>, dim3((unsigned)ceil_div(d.H, kWRows), (unsigned)ceil_div(d.T, kTokRows)),
                      dim3(kThreads), 0, s, a);

@@ -72,7 +72,8 @@ struct FfnWs {
   uint8_t* os;    // [P, H/32] their scales (byte e + 127 per 32 columns)
   uint8_t* sh_q;  // [T, Is]
   uint8_t* sh_s;  // [T, Is/128]
-  float* so;      // [T, H] shared-expert output
+  uint16_t* so;   // [T, H] shared-expert output (fp16 codes)
+  uint8_t* sos;   // [T, H/32] their scales
 };
 size_t ffn_ws_layout(const moe_dims& d, void* base, FfnWs* out);
 
@@ -137,8 +138,9 @@ bool dense_path_supported(const moe_dims& d);
 hipError_t launch_shared13(const moe_dims& d, const uint8_t* x_q, const uint8_t* x_s, const uint8_t* w13s,
                            const uint8_t* w13s_s, uint8_t* sh_q, uint8_t* sh_s, hipStream_t s);
 hipError_t launch_shared2(const moe_dims& d, const uint8_t* sh_q, const uint8_t* sh_s, const uint8_t* w2s,
-                          const uint8_t* w2s_s, float* so, hipStream_t s);
-hipError_t launch_combine(const uint16_t* o, const uint8_t* os, const float* topk_weights, const int32_t* pair_rows, const float* so,
+                          const uint8_t* w2s_s, uint16_t* so, uint8_t* sos, hipStream_t s);
+hipError_t launch_combine(const uint16_t* o, const uint8_t* os, const float* topk_weights, const int32_t* pair_rows,
+                          const uint16_t* so, const uint8_t* sos,
                           uint16_t* y, int T, int H, int K, hipStream_t s);
 
 }  // namespace moe

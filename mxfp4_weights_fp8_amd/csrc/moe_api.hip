@@ -21,7 +21,8 @@ size_t ffn_ws_layout(const moe_dims& d, void* base, FfnWs* out) {
   const size_t o_os = take((size_t)(P * H / 32));
   const size_t o_shq = take((size_t)(T * Is));
   const size_t o_shs = take((size_t)(T * Is / 128));
-  const size_t o_so = take(Is ? sizeof(float) * (size_t)(T * H) : 0);
+  const size_t o_so = take(Is ? sizeof(uint16_t) * (size_t)(T * H) : 0);
+  const size_t o_sos = take(Is ? (size_t)(T * H / 32) : 0);
   if (out) {
     char* b = static_cast<char*>(base);
     out->x_q = reinterpret_cast<uint8_t*>(b + o_xq);
@@ -32,7 +33,8 @@ size_t ffn_ws_layout(const moe_dims& d, void* base, FfnWs* out) {
     out->os = reinterpret_cast<uint8_t*>(b + o_os);
     out->sh_q = reinterpret_cast<uint8_t*>(b + o_shq);
     out->sh_s = reinterpret_cast<uint8_t*>(b + o_shs);
-    out->so = reinterpret_cast<float*>(b + o_so);
+    out->so = reinterpret_cast<uint16_t*>(b + o_so);
+    out->sos = reinterpret_cast<uint8_t*>(b + o_sos);
   }
   return off;
 }
@@ -217,12 +219,13 @@ int moe_ffn(const moe_dims* dims, const uint16_t* x, const float* topk_weights, 
     uint8_t* sh_s = dbg && dbg->sh_s ? dbg->sh_s : fw.sh_s;
     err = launch_shared13(d, x_q, x_s, shared->w13s, shared->w13s_s, sh_q, sh_s, s);
     if (err != hipSuccess) return MOE_EHIP;
-    err = launch_shared2(d, sh_q, sh_s, shared->w2s, shared->w2s_s, fw.so, s);
+    err = launch_shared2(d, sh_q, sh_s, shared->w2s, shared->w2s_s, fw.so, fw.sos, s);
     if (err != hipSuccess) return MOE_EHIP;
   }
   record(dbg, MOE_EV_SHARED_DONE, s);
 
-  err = launch_combine(fw.o, fw.os, topk_weights, pair_rows, use_shared ? fw.so : nullptr, y, d.T, d.H, d.K, s);
+  err = launch_combine(fw.o, fw.os, topk_weights, pair_rows, use_shared ? fw.so : nullptr, use_shared ? fw.sos : nullptr,
+                       y, d.T, d.H, d.K, s);
   if (err != hipSuccess) return MOE_EHIP;
   record(dbg, MOE_EV_END, s);
   return MOE_OK;
