@@ -90,15 +90,17 @@ __device__ __forceinline__ uint2 f16_pack4(float a, float b, float c, float d) {
   return make_uint2(lo, hi);
 }
 
-// One routed row's 128 output columns held by a wave as 8 fragments of 16 columns
+// One row's 16 NF output columns held by a wave as NF fragments of 16 columns
 // (lane (c, q) holds columns 16 i + 4 q .. +3 of its row in r[i]): fp16 codes to
-// dst (the row's column 4 q) and the four 32-column scale bytes to sdst (by the
-// q == 0 lanes). Every lane of the wave must call it (the amax goes through lane
-// shuffles); `store` masks the writes.
-__device__ __forceinline__ void store_o_row128(const v4f (&r)[8], bool store, uint16_t* dst, uint8_t* sdst, int q) {
-  int ex[4];
+// dst (the row's column 4 q) and the NF / 2 scale bytes of its 32-column blocks to
+// sdst (by the q == 0 lanes). Every lane of the wave must call it (the amax goes
+// through lane shuffles); `store` masks the writes.
+template <int NF>
+__device__ __forceinline__ void store_o_rows(const v4f (&r)[NF], bool store, uint16_t* dst, uint8_t* sdst, int q) {
+  static_assert(NF == 4 || NF == 8, "64 or 128 columns");
+  int ex[NF / 2];
 #pragma unroll
-  for (int b = 0; b < 4; ++b) {
+  for (int b = 0; b < NF / 2; ++b) {
     float m = 0.f;
 #pragma unroll
     for (int i = 2 * b; i < 2 * b + 2; ++i)
@@ -110,14 +112,21 @@ __device__ __forceinline__ void store_o_row128(const v4f (&r)[8], bool store, ui
   }
   if (store) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < NF; ++i) {
       const float inv = exp2_neg(ex[i >> 1]);
       *reinterpret_cast<uint2*>(dst + 16 * i) = f16_pack4(r[i][0] * inv, r[i][1] * inv, r[i][2] * inv, r[i][3] * inv);
     }
-    if (q == 0)
-      *reinterpret_cast<uint32_t*>(sdst) = (uint32_t)(ex[0] + 127) | ((uint32_t)(ex[1] + 127) << 8) |
-                                           ((uint32_t)(ex[2] + 127) << 16) | ((uint32_t)(ex[3] + 127) << 24);
+    if (q == 0) {
+      if constexpr (NF == 8)
+        *reinterpret_cast<uint32_t*>(sdst) = (uint32_t)(ex[0] + 127) | ((uint32_t)(ex[1] + 127) << 8) |
+                                             ((uint32_t)(ex[2] + 127) << 16) | ((uint32_t)(ex[3] + 127) << 24);
+      else
+        *reinterpret_cast<uint16_t*>(sdst) = (uint16_t)((ex[0] + 127) | ((ex[1] + 127) << 8));
+    }
   }
+}
+__device__ __forceinline__ void store_o_row128(const v4f (&r)[8], bool store, uint16_t* dst, uint8_t* sdst, int q) {
+  store_o_rows<8>(r, store, dst, sdst, q);
 }
 
 __device__ __forceinline__ v4i load16(const void* p) { return *reinterpret_cast<const v4i*>(p); }

@@ -183,6 +183,130 @@ __global__ __launch_bounds__(kThreads, 1) void k_w2_fewk(FewKArgs a) {
   }
 }
 
+// Dense shared expert, W2s with a short reduction (Is <= 384, as for one MoE-TP8
+// rank: the pages split the shared expert's intermediate like the routed experts'):
+// out[t, n] = sum_k sh[t, k] W2s[n, k], FP8 E4M3 x E4M3 with the token's E8M0 scale
+// per 128 columns of sh and one E8M0 scale per 128 x 128 block of W2s. A workgroup
+// owns 128 tokens; each wave keeps its 4 token fragments for every K step in
+// registers (read once from memory), and the workgroup walks a run of 128-column
+// blocks of W2s, double-buffering each block's codes in LDS (rows of 128 bytes per K
+// step, 16-byte chunk index XORed by (row / 2) % 8) behind the previous block's
+// MFMAs and stores. Waves: 2 x 2, wave (wm, wn) = tokens [64 wm, +64) x columns
+// [64 wn, +64) of the block; rows are written like the routed per-pair rows.
+constexpr int kSCols = 128;   // output columns per block
+
+struct SharedFewKArgs {
+  const uint8_t* sh_q;     // [T, Is] E4M3
+  const uint8_t* sh_s;     // [T, Is/128] E8M0
+  const uint8_t* w;        // W2s [H, Is] E4M3
+  const uint8_t* w_s;      // [H/128, Is/128] E8M0
+  uint16_t* o;             // [T, H] fp16 codes
+  uint8_t* os;             // [T, H/32] their scales
+  int T, H, Is;
+  int blocks_per_wg;
+};
+
+template <int KS>
+__global__ __launch_bounds__(kThreads, 1) void k_shared2_fewk(SharedFewKArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint8_t sW[2][KS][kSCols * 128];   // [buf][step][row][128 B]
+
+  const int t0 = blockIdx.y * kRows;
+  const int n_blocks = a.H / kSCols;
+  const int b_first = blockIdx.x * a.blocks_per_wg;
+  const int b_count = min(n_blocks, b_first + a.blocks_per_wg) - b_first;
+  if (b_count <= 0) return;
+  const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4, c = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave & 1, wn = wave >> 1;
+  const int Is = a.Is;
+
+  // token fragments j (rows 64 wm + 16 j + c) of every K step: lane (c, q) holds K
+  // 16q .. +15 and 64 + 16q .. +15 of the step; tokens past T read zeros
+  const rsrc_t rs = make_rsrc(a.sh_q, (uint32_t)((int64_t)a.T * Is));
+  v8i bq[4][KS];
+  int sb[4][KS];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int t = t0 + 64 * wm + 16 * j + c;
+    const int tc = min(t, a.T);
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const v4i lo = buf_load16(rs, tc * Is + s * 128 + 16 * q, 0);
+      const v4i hi = buf_load16(rs, tc * Is + s * 128 + 64 + 16 * q, 0);
+      bq[j][s][0] = lo[0]; bq[j][s][1] = lo[1]; bq[j][s][2] = lo[2]; bq[j][s][3] = lo[3];
+      bq[j][s][4] = hi[0]; bq[j][s][5] = hi[1]; bq[j][s][6] = hi[2]; bq[j][s][7] = hi[3];
+      sb[j][s] = t < a.T ? (int)a.sh_s[(int64_t)t * KS + s] : 127;
+    }
+  }
+  wait_vmcnt<0>();
+
+  // Block b into buffer buf: instruction (i, s) of wave w copies rows 32w + 8i .. +7
+  // of K step s, lane l -> row + l/8, physical chunk l%8 holding logical chunk
+  // (l%8) ^ (row / 2) % 8.
+  const v4i_s rw = rsrc4(a.w, (uint32_t)((int64_t)a.H * Is));
+  auto copy_block = [&](int b, int buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 32 * wave + 8 * i + (lane >> 3);
+      const int off = (b * kSCols + row) * Is + (((lane & 7) ^ ((row >> 1) & 7)) << 4);
+#pragma unroll
+      for (int s = 0; s < KS; ++s) dma16(rw, lds_addr(&sW[buf][s][(32 * wave + 8 * i) * 128]), off + s * 128, 0);
+    }
+  };
+  constexpr int kCopiesPerBlock = 4 * KS;               // per wave
+  copy_block(b_first, 0);
+
+  // weight fragment i = block rows 64 wn + 16 i + c, swizzle (c / 2) % 8
+  const int offA0 = (64 * wn + c) * 128 + ((q ^ (c >> 1)) << 4);
+  const int offA1 = (64 * wn + c) * 128 + (((4 + q) ^ (c >> 1)) << 4);
+
+  for (int bi = 0; bi < b_count; ++bi) {
+    const int buf = bi & 1;
+    const int b = b_first + bi;
+    if (bi + 1 < b_count) {
+      copy_block(b + 1, buf ^ 1);
+      wait_vmcnt<kCopiesPerBlock>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    __syncthreads();
+
+    v4f acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const int sw = a.w_s[b * KS + s];                  // the block's 128 x 128 scale of step s
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const v4i lo = *reinterpret_cast<const v4i*>(&sW[buf][s][offA0 + i * 16 * 128]);
+        const v4i hi = *reinterpret_cast<const v4i*>(&sW[buf][s][offA1 + i * 16 * 128]);
+        v8i aop;
+        aop[0] = lo[0]; aop[1] = lo[1]; aop[2] = lo[2]; aop[3] = lo[3];
+        aop[4] = hi[0]; aop[5] = hi[1]; aop[6] = hi[2]; aop[7] = hi[3];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = mfma_scale_16x16x128<kFmtE4M3, kFmtE4M3>(aop, bq[j][s], acc[i][j], sw, sb[j][s]);
+      }
+    }
+
+    // lane (c, q) of token fragment j holds columns 16 i + 4 q .. +3 of the wave's 64
+    const int col0 = b * kSCols + 64 * wn;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int t = t0 + 64 * wm + 16 * j + c;
+      const int64_t tt = t < a.T ? t : t0;
+      v4f r[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) r[i] = acc[i][j];
+      store_o_rows<4>(r, t < a.T, a.o + tt * a.H + col0 + q * 4, a.os + tt * (a.H / 32) + col0 / 32, q);
+    }
+    __syncthreads();   // every wave has read buffer buf before block bi+2 is copied into it
+  }
+}
+
 }  // namespace
 
 bool fewk2_supported(const moe_dims& d) {
@@ -209,6 +333,25 @@ hipError_t launch_w2_fewk(const moe_dims& d, const int2* items, const int32_t* n
     case 1: hipLaunchKernelGGL(k_w2_fewk<1>, grid, dim3(kThreads), 0, s, a); break;
     case 2: hipLaunchKernelGGL(k_w2_fewk<2>, grid, dim3(kThreads), 0, s, a); break;
     case 3: hipLaunchKernelGGL(k_w2_fewk<3>, grid, dim3(kThreads), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+bool shared2_fewk_supported(const moe_dims& d) {
+  return d.Is > 0 && d.Is / 128 <= kMaxKS && d.H % kSCols == 0 && (int64_t)d.H * d.Is < ((int64_t)1 << 31);
+}
+
+hipError_t launch_shared2_fewk(const moe_dims& d, const uint8_t* sh_q, const uint8_t* sh_s, const uint8_t* w2s,
+                               const uint8_t* w2s_s, uint16_t* so, uint8_t* sos, hipStream_t s) {
+  const int n_blocks = d.H / kSCols;
+  const int per_wg = n_blocks >= 2 ? (n_blocks + 1) / 2 : 1;
+  SharedFewKArgs a{sh_q, sh_s, w2s, w2s_s, so, sos, d.T, d.H, d.Is, per_wg};
+  dim3 grid((unsigned)ceil_div(n_blocks, per_wg), (unsigned)ceil_div(d.T, kRows));
+  switch (d.Is / 128) {
+    case 1: hipLaunchKernelGGL(k_shared2_fewk<1>, grid, dim3(kThreads), 0, s, a); break;
+    case 2: hipLaunchKernelGGL(k_shared2_fewk<2>, grid, dim3(kThreads), 0, s, a); break;
+    case 3: hipLaunchKernelGGL(k_shared2_fewk<3>, grid, dim3(kThreads), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -119,6 +119,11 @@ hipError_t launch_w2_large(const moe_dims& d, const int2* items, const int32_t* 
 // W2 with at most 3 K steps (I <= 384): a workgroup keeps its 128 routed rows in LDS
 // and walks a run of 256-column blocks.
 bool fewk2_supported(const moe_dims& d);
+// The shared expert's W2s with at most 3 K steps (Is <= 384): token fragments in
+// registers, runs of 128-column blocks.
+bool shared2_fewk_supported(const moe_dims& d);
+hipError_t launch_shared2_fewk(const moe_dims& d, const uint8_t* sh_q, const uint8_t* sh_s, const uint8_t* w2s,
+                               const uint8_t* w2s_s, uint16_t* so, uint8_t* sos, hipStream_t s);
 hipError_t launch_w2_fewk(const moe_dims& d, const int2* items, const int32_t* n_items, int64_t max_items,
                           int item_rows, const int32_t* offsets, const int32_t* sorted_pairs, const uint8_t* h_q,
                           const uint8_t* h_s, const uint8_t* w2, const uint8_t* w2_s, uint16_t* o, uint8_t* os,

@@ -219,7 +219,9 @@ int moe_ffn(const moe_dims* dims, const uint16_t* x, const float* topk_weights, 
     uint8_t* sh_s = dbg && dbg->sh_s ? dbg->sh_s : fw.sh_s;
     err = launch_shared13(d, x_q, x_s, shared->w13s, shared->w13s_s, sh_q, sh_s, s);
     if (err != hipSuccess) return MOE_EHIP;
-    err = launch_shared2(d, sh_q, sh_s, shared->w2s, shared->w2s_s, fw.so, fw.sos, s);
+    err = shared2_fewk_supported(d)
+              ? launch_shared2_fewk(d, sh_q, sh_s, shared->w2s, shared->w2s_s, fw.so, fw.sos, s)
+              : launch_shared2(d, sh_q, sh_s, shared->w2s, shared->w2s_s, fw.so, fw.sos, s);
     if (err != hipSuccess) return MOE_EHIP;
   }
   record(dbg, MOE_EV_SHARED_DONE, s);
