@@ -5,19 +5,21 @@
 //
 // With so few K steps, a 128-row x 256-column workgroup of the large-M kernel
 // spends most of its time on its own prologue (routed-row tile, scales, first
-// copies) and epilogue. Here a workgroup keeps its 128 routed rows for every K step
-// in LDS (E4M3, copied once) and walks a run of 256-column blocks of W2: the codes
-// and E8M0 scales of block b+1 are copied into the other half of a double buffer
-// while block b is multiplied and its per-pair rows are written.
+// copies) and epilogue, and with one such workgroup per CU the MFMAs and the
+// epilogue of all four waves run one after the other. Here a workgroup owns 128
+// routed rows and walks a run of 128-column blocks of W2: each wave keeps its 4
+// routed-row fragments of every K step in registers (read once from memory), the
+// E2M1 codes and E8M0 scales of block b+1 are copied into the other half of a
+// double buffer while block b is multiplied and written, and the LDS footprint
+// (about 52 KB) leaves room for two workgroups per CU, so one workgroup's
+// epilogue overlaps the other's MFMAs.
 //
-// Waves: a 2 x 2 grid, wave (wm, wn) = routed rows [64 wm, +64) (4 fragments, MFMA B
-// side) x output columns [128 wn, +128) of the block (8 weight fragments, MFMA A
-// side), 32 accumulator tiles of v_mfma_scale_f32_16x16x128_f8f6f4 in VGPRs.
-// LDS (KS = 3: 155,136 bytes): routed rows [step][row][128 B] with the 16-byte chunk
-// index XORed by (row / 2) % 8; weights [buffer][step][fragment][1 KB in the
-// MFMA's lane order] (the kernel-native layout, copied block by block); weight
-// scales [buffer][row][4 KS B] in their global order; activation scales one dword
-// per routed row.
+// Waves: a 2 x 2 grid, wave (wm, wn) = routed rows [64 wm, +64) (4 fragments, MFMA
+// B side, E4M3) x output columns [64 wn, +64) of the block (4 weight fragments,
+// MFMA A side), 16 accumulator tiles of v_mfma_scale_f32_16x16x128_f8f6f4.
+// LDS: weights [buffer][step][fragment][1 KB in the MFMA's lane order] (the
+// kernel-native layout, copied block by block); weight scales [buffer][row][4 KS B]
+// in their global order; the routed rows' output slots.
 #include "device_common.h"
 #include "host_internal.h"
 #include "lds_copy.h"
@@ -27,7 +29,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kRows = kLargeRows;   // routed rows per workgroup
-constexpr int kCols = 256;          // output columns per block
+constexpr int kCols = 128;          // output columns per block (8 weight fragments)
 constexpr int kMaxKS = 3;
 
 struct FewKArgs {
@@ -44,16 +46,17 @@ struct FewKArgs {
   uint32_t h_bytes;        // size of h_q
   int item_shift;          // 1: items hold 256 rows, workgroup y covers half y % 2 of item y / 2
   int H, I;
-  int blocks_per_wg;       // 256-column blocks per workgroup (the last run may be shorter)
+  int blocks_per_wg;       // 128-column blocks per workgroup (the last run may be shorter)
 };
 
 template <int KS>
-__global__ __launch_bounds__(kThreads, 1) void k_w2_fewk(FewKArgs a) {
-  __shared__ __attribute__((aligned(1024))) uint8_t sB[KS][kRows * 128];      // [step][row][128 B]
-  __shared__ __attribute__((aligned(1024))) uint8_t sA[2][KS][16 * 1024];     // [buf][step][fragment][1 KB]
-  __shared__ __attribute__((aligned(16))) uint8_t sSa[2][kCols * 4 * KS];      // [buf][row][4 KS B]
-  __shared__ uint32_t sSb[kRows];                                              // [row] byte s = step s
-  __shared__ int sTok[kRows];
+__global__ __launch_bounds__(kThreads, 2) void k_w2_fewk(FewKArgs a) {
+  // weight scales of a block: 128 rows x 4 KS bytes, copied as 256-byte dword
+  // copies, kScaleCopies per wave (the ones past the block's bytes fetch nothing
+  // and land in the padding)
+  constexpr int kScaleCopies = (2 * KS + 3) / 4;
+  __shared__ __attribute__((aligned(1024))) uint8_t sA[2][KS][8 * 1024];       // [buf][step][fragment][1 KB]
+  __shared__ __attribute__((aligned(16))) uint8_t sSa[2][4 * kScaleCopies * 256];  // [buf][row][4 KS B] + padding
   __shared__ int sSlot[kRows];
 
   const int item = blockIdx.y >> a.item_shift;
@@ -73,58 +76,52 @@ __global__ __launch_bounds__(kThreads, 1) void k_w2_fewk(FewKArgs a) {
   const int wm = wave & 1, wn = wave >> 1;
   const int I = a.I, srow = I / 32;                     // srow = 4 KS scale bytes per weight row
 
-  // routed rows of the tile (padding repeats the first row), their output slots and
-  // activation scales (KS bytes per row, one dword)
-  if (tid < kRows) {
-    const int r = row0 + (tid < nrows ? tid : 0);
-    sTok[tid] = r;
-    sSlot[tid] = a.sorted_pairs[r];
-    uint32_t v = 0;
+  if (tid < kRows) sSlot[tid] = a.sorted_pairs[row0 + (tid < nrows ? tid : 0)];
+
+  // routed-row fragments j (rows 64 wm + 16 j + c; padding repeats the first row):
+  // lane (c, q) holds K 16q .. +15 and 64 + 16q .. +15 of every K step
+  const rsrc_t rh = make_rsrc(a.h_q, a.h_bytes);
+  v8i bq[4][KS];
+  int sb[4][KS];
 #pragma unroll
-    for (int s = 0; s < KS; ++s) v |= (uint32_t)a.h_s[(int64_t)r * KS + s] << (8 * s);
-    sSb[tid] = v;
+  for (int j = 0; j < 4; ++j) {
+    const int r = 64 * wm + 16 * j + c;
+    const int hr = row0 + (r < nrows ? r : 0);
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const v4i lo = buf_load16(rh, hr * I + s * 128 + 16 * q, 0);
+      const v4i hi = buf_load16(rh, hr * I + s * 128 + 64 + 16 * q, 0);
+      bq[j][s][0] = lo[0]; bq[j][s][1] = lo[1]; bq[j][s][2] = lo[2]; bq[j][s][3] = lo[3];
+      bq[j][s][4] = hi[0]; bq[j][s][5] = hi[1]; bq[j][s][6] = hi[2]; bq[j][s][7] = hi[3];
+      sb[j][s] = a.h_s[(int64_t)hr * KS + s];
+    }
   }
-  __syncthreads();
+  wait_vmcnt<0>();
 
   const int64_t w_bytes = (int64_t)a.H * (I / 2);
-  const v4i_s ra = rsrc4(a.h_q, a.h_bytes);
   const v4i_s rw = rsrc4(a.w2 + (int64_t)e * w_bytes, (uint32_t)w_bytes);
   const v4i_s rws = rsrc4(a.w2_s + (int64_t)e * a.H * srow, (uint32_t)(a.H * srow));
-
-  // Routed rows, once: instruction (s, i) of wave w copies rows 32w + 8i .. +7 of K
-  // step s, lane l -> row + l/8, physical chunk l%8 holding logical chunk
-  // (l%8) ^ (row / 2) % 8.
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = 32 * wave + 8 * i + (lane >> 3);
-    const int off = sTok[row] * I + (((lane & 7) ^ ((row >> 1) & 7)) << 4);
-#pragma unroll
-    for (int s = 0; s < KS; ++s) dma16(ra, lds_addr(&sB[s][(32 * wave + 8 * i) * 128]), off + s * 128, 0);
-  }
-  // Weight block b into buffer buf: wave w copies fragments 4w .. 4w+3 (expert rows
-  // 256b + 16f ..) for every K step, then KS blocks of 256 scale bytes of the
-  // block's 256 contiguous scale rows.
+  // Weight block b into buffer buf: wave w copies fragments 2w, 2w+1 (expert rows
+  // 128 b + 16 f ..) of every K step, then its share of the block's 128 contiguous
+  // scale rows (256-byte chunk 4k + w for copy k).
   auto copy_block = [&](int b, int buf) {
 #pragma unroll
-    for (int f = 0; f < 4; ++f) {
-      const int frag = 4 * wave + f;
+    for (int f = 0; f < 2; ++f) {
+      const int frag = 2 * wave + f;
 #pragma unroll
       for (int s = 0; s < KS; ++s)
-        dma16(rw, lds_addr(&sA[buf][s][frag * 1024]), (16 * b + frag) * 16 * (I / 2) + s * 1024 + lane * 16, 0);
+        dma16(rw, lds_addr(&sA[buf][s][frag * 1024]), (8 * b + frag) * 16 * (I / 2) + s * 1024 + lane * 16, 0);
     }
 #pragma unroll
-    for (int i = 0; i < KS; ++i) {
-      const int blk = KS * wave + i;
-      dma4(rws, lds_addr(&sSa[buf][blk * 256]), b * kCols * srow + blk * 256 + lane * 4, 0);
+    for (int k = 0; k < kScaleCopies; ++k) {
+      const int chunk = 4 * k + wave;
+      dma4(rsrc_sized(rws, chunk < 2 * KS), lds_addr(&sSa[buf][chunk * 256]),
+           b * kCols * srow + chunk * 256 + lane * 4, 0);
     }
   };
-  constexpr int kCopiesPerBlock = 5 * KS;               // per wave
+  constexpr int kCopiesPerBlock = 2 * KS + kScaleCopies;   // per wave
   copy_block(b_first, 0);
-
-  // operand read offsets: routed-row fragment j = rows 64 wm + 16 j + c, whose
-  // swizzle (row / 2) % 8 is (c / 2) % 8; lane (c, q) reads logical chunks q and 4+q
-  const int offB0 = (64 * wm + c) * 128 + ((q ^ (c >> 1)) << 4);
-  const int offB1 = (64 * wm + c) * 128 + (((4 + q) ^ (c >> 1)) << 4);
+  __syncthreads();                                      // sSlot
 
   for (int bi = 0; bi < b_count; ++bi) {
     const int buf = bi & 1;
@@ -136,26 +133,16 @@ __global__ __launch_bounds__(kThreads, 1) void k_w2_fewk(FewKArgs a) {
     }
     __syncthreads();
 
-    v4f acc[8][4];
+    v4f acc[4][4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      v8i bf[4];
-      int sb[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const v4i lo = *reinterpret_cast<const v4i*>(&sB[s][offB0 + j * 16 * 128]);
-        const v4i hi = *reinterpret_cast<const v4i*>(&sB[s][offB1 + j * 16 * 128]);
-        bf[j][0] = lo[0]; bf[j][1] = lo[1]; bf[j][2] = lo[2]; bf[j][3] = lo[3];
-        bf[j][4] = hi[0]; bf[j][5] = hi[1]; bf[j][6] = hi[2]; bf[j][7] = hi[3];
-        sb[j] = (int)((sSb[64 * wm + 16 * j + c] >> (8 * s)) & 0xFFu);
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int frag = 8 * wn + i;
+      for (int i = 0; i < 4; ++i) {
+        const int frag = 4 * wn + i;
         const v4i w = *reinterpret_cast<const v4i*>(&sA[buf][s][frag * 1024 + lane * 16]);
         const int sa = sSa[buf][(frag * 16 + c) * srow + 4 * s + q];
         v8i aop;
@@ -163,21 +150,21 @@ __global__ __launch_bounds__(kThreads, 1) void k_w2_fewk(FewKArgs a) {
         aop[4] = 0; aop[5] = 0; aop[6] = 0; aop[7] = 0;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          acc[i][j] = mfma_scale_16x16x128<kFmtE2M1, kFmtE4M3>(aop, bf[j], acc[i][j], sa, sb[j]);
+          acc[i][j] = mfma_scale_16x16x128<kFmtE2M1, kFmtE4M3>(aop, bq[j][s], acc[i][j], sa, sb[j][s]);
       }
     }
 
     // per-pair rows of this block: lane (c, q) of routed-row fragment j holds output
-    // columns 16 i + 4 q .. +3 of the wave's 128
-    const int col0 = (b_first + bi) * kCols + 128 * wn;
+    // columns 16 i + 4 q .. +3 of the wave's 64
+    const int col0 = (b_first + bi) * kCols + 64 * wn;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int row = 64 * wm + 16 * j + c;
       const int64_t slot = sSlot[row < nrows ? row : 0];
-      v4f r[8];
+      v4f r[4];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) r[i] = acc[i][j];
-      store_o_row128(r, row < nrows, a.o + slot * a.H + col0 + q * 4, a.os + slot * (a.H / 32) + col0 / 32, q);
+      for (int i = 0; i < 4; ++i) r[i] = acc[i][j];
+      store_o_rows<4>(r, row < nrows, a.o + slot * a.H + col0 + q * 4, a.os + slot * (a.H / 32) + col0 / 32, q);
     }
     __syncthreads();   // every wave has read buffer buf before block bi+2 is copied into it
   }
@@ -322,9 +309,9 @@ hipError_t launch_w2_fewk(const moe_dims& d, const int2* items, const int32_t* n
   if (max_items <= 0) return hipSuccess;
   const int shift = item_rows == 2 * kRows ? 1 : 0;
   const int n_blocks = d.H / kCols;
-  // two runs of column blocks per routed-row tile: twice the workgroups of one run
-  // (a shorter tail at the end of the grid) for one more copy of the routed rows
-  const int per_wg = n_blocks >= 2 ? (n_blocks + 1) / 2 : 1;
+  // four runs of column blocks per routed-row tile: more, shorter workgroups (a
+  // shorter tail at the end of the grid) for three more reads of the routed rows
+  const int per_wg = (n_blocks + 3) / 4;
   const int64_t P = (int64_t)d.T * d.K;
   FewKArgs a{items, n_items, offsets, sorted_pairs, h_q, h_s, w2, w2_s, o, os, (uint32_t)(P * d.I), shift,
              d.H, d.I, per_wg};
