@@ -10,9 +10,8 @@
 // routed rows and walks a run of 128-column blocks of W2: each wave keeps its 4
 // routed-row fragments of every K step in registers (read once from memory), the
 // E2M1 codes and E8M0 scales of block b+1 are copied into the other half of a
-// double buffer while block b is multiplied and written, and the LDS footprint
-// (about 52 KB) leaves room for two workgroups per CU, so one workgroup's
-// epilogue overlaps the other's MFMAs.
+// double buffer while block b is multiplied and written, and the footprint (about
+// 52 KB of LDS, 212 VGPRs at three K steps) lets two workgroups share a CU.
 //
 // Waves: a 2 x 2 grid, wave (wm, wn) = routed rows [64 wm, +64) (4 fragments, MFMA
 // B side, E4M3) x output columns [64 wn, +64) of the block (4 weight fragments,
