@@ -221,6 +221,7 @@ def main():
                      "traffic": measured_traffic("decode7", "moe::k_w13_small<8>"),
                      "algorithmic_bytes_per_launch": w13_bytes, "avg_launch_ms": w13_ms},
         "step_hbm_gbs": step_bytes / (ms_step * 1e-3) / 1e9,
+        "step_hbm_frac": step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "stage_ms_untimed_pass": ms,
     }
 
