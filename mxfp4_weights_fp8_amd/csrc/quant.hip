@@ -46,8 +46,9 @@ __global__ __launch_bounds__(kQuantThreads) void k_quant_act(const uint16_t* __r
 hipError_t launch_quant_act(const uint16_t* x, uint8_t* x_q, uint8_t* x_s, int T, int H, hipStream_t s) {
   const int64_t n_blocks = (int64_t)T * (H / 128);
   if (n_blocks == 0) return hipSuccess;
-  int64_t ctas = ceil_div(n_blocks, kQuantThreads / 16);
-  if (ctas > 256 * 16) ctas = 256 * 16;
+  // one 128-column block per 16 lanes (at 32K tokens 0.120 ms against 0.127 ms with the
+  // grid capped at 4096 workgroups and a grid-stride loop)
+  const int64_t ctas = ceil_div(n_blocks, kQuantThreads / 16);
   hipLaunchKernelGGL(k_quant_act, dim3((unsigned)ctas), dim3(kQuantThreads), 0, s, x, x_q, x_s, n_blocks);
   return hipGetLastError();
 }
