@@ -331,7 +331,7 @@ bool shared2_fewk_supported(const moe_dims& d) {
 hipError_t launch_shared2_fewk(const moe_dims& d, const uint8_t* sh_q, const uint8_t* sh_s, const uint8_t* w2s,
                                const uint8_t* w2s_s, uint16_t* so, uint8_t* sos, hipStream_t s) {
   const int n_blocks = d.H / kSCols;
-  const int per_wg = n_blocks >= 2 ? (n_blocks + 1) / 2 : 1;
+  const int per_wg = (n_blocks + 3) / 4;
   SharedFewKArgs a{sh_q, sh_s, w2s, w2s_s, so, sos, d.T, d.H, d.Is, per_wg};
   dim3 grid((unsigned)ceil_div(n_blocks, per_wg), (unsigned)ceil_div(d.T, kRows));
   switch (d.Is / 128) {
