@@ -3,7 +3,9 @@ captured once and replayed). moe_plan + moe_ffn only enqueue kernels (no host
 synchronization, no allocation, no memset), so both can be captured into one HIP
 graph. Each replay reads new routing and activations that were written into the
 captured input buffers, with eager work and synchronizations between replays, and
-must give bit for bit the plan and the output of an eager run on the same inputs."""
+must give bit for bit the plan and the output of an eager run on the same inputs.
+Two independent steps enqueued on two streams at once must match their sequential
+runs (the calls keep no state of their own)."""
 
 import pytest
 import torch
@@ -71,3 +73,30 @@ def test_graph_replay_matches_eager(dev, T, H, I, E, K, Is):
         assert torch.equal(y_graph.view(torch.int16), y2.view(torch.int16)), f"replay {rep}: y differs"
         assert bool(torch.isfinite(y2.float()).all())
         say(f"[graph {T}x{H} I{I} E{E} K{K} Is{Is}] replay {rep} equal to eager")
+
+
+def test_two_streams_match_sequential(dev):
+    """Two independent steps (different shapes, weights and routing) enqueued on two
+    streams before either is synchronized give bit for bit the outputs of running
+    them one after the other: the library keeps no state between calls."""
+    cases = []
+    for T, H, I, E, K, seed in [(300, 512, 512, 3, 2, 90), (7, 256, 384, 16, 8, 91)]:
+        wl = scaled("tiny", T=T, H=H, I=I, E=E, K=K, seed=seed, weight_seed=seed, name=f"st{seed}")
+        inp = make_inputs(wl).to(dev)
+        W = moe.pack_weights(inp.weights)
+        p = moe.plan(inp.topk_ids, E, H, I)
+        y = moe.ffn(inp.x, inp.topk_weights, p, W)
+        torch.cuda.synchronize()
+        cases.append((inp, W, y.clone()))
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for s in streams:
+        s.wait_stream(torch.cuda.current_stream())
+    outs = []
+    for (inp, W, _), s in zip(cases, streams):
+        with torch.cuda.stream(s):
+            w = inp.wl
+            p = moe.plan(inp.topk_ids, w.E, w.H, w.I)
+            outs.append(moe.ffn(inp.x, inp.topk_weights, p, W))
+    torch.cuda.synchronize()
+    for (inp, _, y_seq), y in zip(cases, outs):
+        assert torch.equal(y.view(torch.int16), y_seq.view(torch.int16)), f"{inp.wl.name}: concurrent != sequential"
