@@ -73,7 +73,7 @@ template <int NF>
 __device__ __forceinline__ void load_step(Step<NF>& r, const Stream<NF>& p, int s) {
 #pragma unroll
   for (int f = 0; f < NF; ++f) {
-    r.w[f] = buf_load16(p.w, p.wo[f], s * 1024);
+    r.w[f] = buf_load16_nt(p.w, p.wo[f], s * 1024);
     r.ws[f] = *reinterpret_cast<const int*>(p.sl[f] + s * 4);
   }
   const v4i lo = buf_load16(p.x, p.xo, s * 128), hi = buf_load16(p.x, p.xo, s * 128 + 64);
@@ -117,7 +117,7 @@ struct Codes {
 template <int NF>
 __device__ __forceinline__ void load_codes(Codes<NF>& r, const Stream<NF>& p, int s) {
 #pragma unroll
-  for (int f = 0; f < NF; ++f) r.w[f] = buf_load16(p.w, p.wo[f], s * 1024);
+  for (int f = 0; f < NF; ++f) r.w[f] = buf_load16_nt(p.w, p.wo[f], s * 1024);   // read once per step
   const v4i lo = buf_load16(p.x, p.xo, s * 128), hi = buf_load16(p.x, p.xo, s * 128 + 64);
   r.x[0] = lo[0]; r.x[1] = lo[1]; r.x[2] = lo[2]; r.x[3] = lo[3];
   r.x[4] = hi[0]; r.x[5] = hi[1]; r.x[6] = hi[2]; r.x[7] = hi[3];
