@@ -40,7 +40,8 @@ __global__ __launch_bounds__(kThreads) void k_combine(const uint16_t* __restrict
         const int64_t p = t * K + min(j0 + jj, K - 1);
         ok[jj] = j0 + jj < K && pair_rows[p] >= 0;
         wt[jj] = w[p];
-        v[jj] = reinterpret_cast<const uint4*>(o)[p * groups_per_row + c8];
+        const v4i r = load16_nt(reinterpret_cast<const uint4*>(o) + p * groups_per_row + c8);
+        v[jj] = make_uint4((uint32_t)r.x, (uint32_t)r.y, (uint32_t)r.z, (uint32_t)r.w);
         ex[jj] = (int)os[p * scales_per_row + (c8 >> 2)] - 127;
       }
 #pragma unroll
@@ -56,7 +57,8 @@ __global__ __launch_bounds__(kThreads) void k_combine(const uint16_t* __restrict
       }
     }
     if (so) {   // the shared expert's row, same storage as the per-pair rows, added last
-      const uint4 v = reinterpret_cast<const uint4*>(so)[g];
+      const v4i r = load16_nt(reinterpret_cast<const uint4*>(so) + g);
+      const uint4 v = make_uint4((uint32_t)r.x, (uint32_t)r.y, (uint32_t)r.z, (uint32_t)r.w);
       const int ex = (int)sos[t * scales_per_row + (c8 >> 2)] - 127;
       const uint32_t u[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll

@@ -130,6 +130,11 @@ __device__ __forceinline__ void store_o_row128(const v4f (&r)[8], bool store, ui
 }
 
 __device__ __forceinline__ v4i load16(const void* p) { return *reinterpret_cast<const v4i*>(p); }
+// 16 bytes read once per step (activations into the quantizer, per-pair rows into the
+// combine), loaded with the nontemporal hint so that they do not displace reused lines.
+__device__ __forceinline__ v4i load16_nt(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const v4i*>(p));
+}
 
 // Buffer loads: a wave-uniform resource (base, size in bytes, kept in SGPRs), a
 // 32-bit per-lane offset and a wave-uniform offset. Reads past `bytes` return 0.

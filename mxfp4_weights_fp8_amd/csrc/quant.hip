@@ -20,7 +20,7 @@ __global__ __launch_bounds__(kQuantThreads) void k_quant_act(const uint16_t* __r
   for (int64_t blk = (int64_t)blockIdx.x * groups_per_cta + (threadIdx.x >> 4); blk < n_blocks;
        blk += (int64_t)gridDim.x * groups_per_cta) {
     const int64_t base = blk * 128 + sub * 8;   // element index of this lane's 8 values
-    const v4i raw = load16(x + base);
+    const v4i raw = load16_nt(x + base);
     float v[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
