@@ -22,8 +22,8 @@
 // the register files inside the K loop).
 //
 // LDS (161792 bytes for W13, 162816 for W2):
-//   weights: two stages of two K steps, [fragment][step][1 KB in lane order] (the
-//     kernel-native weight layout, copied block by block), 64 KB;
+//   weights: four one-step buffers (buffer s % 4 holds K step s), [fragment][1 KB
+//     in lane order] (the kernel-native weight layout, copied block by block), 64 KB;
 //   routed rows: two buffers of one K step (128 B of E4M3 per row), 64 KB;
 //   weight E8M0 scales: three chunks of four K steps (16 B per row), 12 KB;
 //   activation scales of the whole tile: 68 B per routed row, 17 KB.
@@ -35,22 +35,23 @@
 // routed-row fragment j against the 8 weight fragments of step s, reads routed-row
 // fragment j+1 of step s (four rotating register buffers) and weight fragment j of
 // step s+1 (two register sets). After column 6 every wave has read all routed-row
-// fragments of step s, so a barrier there (M_s) frees that buffer; the copies
-// issued after M_{s-1} are exactly the ones needed after M_s, so each M_s waits
-// for all of this wave's copies:
-//   routed rows of step s+1 (into the buffer step s-1 used);
-//   for even s = 2k, weights of stage k+1 (into the buffer of stage k-1, last read
-//     while step 2k-2 ran);
-//   one quarter of weight-scale chunk (s+5)/4 (needed from the reads of step
-//     4*chunk, made while step 4*chunk-1 runs; its buffer held chunk-3).
-// The copies of one window (after M_s, before the wait of M_{s+1}) are spread over
-// columns 7, 0, 1, 2, 3 rather than issued together after M_s: half of the routed
-// rows and two weight blocks in column 7, two routed-row copies in each of columns 0
-// and 1, and the other six weight blocks of an odd window in columns 0-3 (measured
-// on the 32K prefill: 2.5% less W13 time than issuing them all in column 7; a copy
-// instruction holds up its wave's MFMA issue, and bunched copies queue behind each
-// other). Nothing is issued later than column 3, so each copy has at least three
-// columns of MFMAs to land in.
+// fragments of step s, so a barrier there (M_s) frees that buffer. The window of
+// copies between M_{s-1} and M_s (column 7 of step s-1, columns 0-3 of step s) holds,
+// in this order:
+//   routed rows of step s+1 (into the buffer step s-1 used): four copies in column
+//     7, two in each of columns 0 and 1;
+//   one quarter of weight-scale chunk (s+5)/4 in column 0 (needed from the reads of
+//     step 4*chunk, made while step 4*chunk-1 runs; its buffer held chunk-3);
+//   the weights of step s+3, two blocks in each of columns 2 and 3, into the buffer
+//     of step s-1 (last read while step s-2 ran).
+// Copies complete in issue order, so M_s waits until at most this wave's 4 weight
+// copies are in flight: everything needed after M_s has landed, and the weights,
+// which come from HBM more often than the routed rows, have until M_{s+1} (eleven
+// columns of MFMAs) instead of a few columns. Measured on the 32K prefill: spreading
+// the copies over five columns instead of issuing them together after the barrier
+// took 2.5% off the W13 launch; the one-step buffers with the longer weight lead
+// (against two-step stages copied in one window and waited at the next barrier)
+// another 2.5–4% off W13 and 3.5% off W2.
 // Copies past the last step use a buffer resource of size 0 (they write zeros and
 // touch no memory), so the loop body has no branches.
 #include "device_common.h"
@@ -65,7 +66,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kTok = kXlRows;            // routed rows per tile
 constexpr int kARows = 256;              // weight rows per tile
-constexpr int kStageA = kARows * 128;    // E2M1 codes of one weight stage (two K steps)
+constexpr int kStepA = kARows * 64;     // E2M1 codes of one K step
 constexpr int kStepB = kTok * 128;       // E4M3 codes of one K step
 constexpr int kChunkRow = 16;            // weight-scale bytes per row and chunk (four K steps)
 constexpr int kChunk = kARows * kChunkRow;
@@ -123,7 +124,7 @@ struct AOps {     // one K step of this wave's 8 weight fragments
 
 template <bool W13>
 __global__ __launch_bounds__(kThreads, 1) void k_gemm_xl(XlArgs a) {
-  __shared__ __attribute__((aligned(1024))) uint8_t sA[2][kStageA];   // [stage][row][128 B]
+  __shared__ __attribute__((aligned(1024))) uint8_t sA[4][kStepA];    // [step % 4][fragment][1 KB]
   __shared__ __attribute__((aligned(1024))) uint8_t sB[2][kStepB];    // [step][row][128 B]
   __shared__ __attribute__((aligned(16))) uint8_t sSa[3][kChunk];     // [chunk][row][16 B]
   __shared__ __attribute__((aligned(16))) uint8_t sSb[kSbBytes];      // [row][kSbRow B]
@@ -208,9 +209,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_xl(XlArgs a) {
     return nb * 256 + r;
   };
   // Copy plans (per wave). Weights (kernel-native layout: a fragment's codes of one
-  // K step are 1 KB in lane order): instruction i of a stage copies the block of LDS
-  // fragment 4*wave + i/2 and K step 2*stage + i%2 to LDS [fragment][step][1 KB]; a
-  // wave's 64 weight rows are consecutive expert rows. Routed rows: instruction i
+  // K step are 1 KB in lane order): instruction i of a K step copies the block of LDS
+  // fragment 4*wave + i to LDS [fragment][1 KB] of the step's buffer; a wave's 64
+  // weight rows are consecutive expert rows. Routed rows: instruction i
   // moves LDS rows 64*wave + 8i .. +7, lane l -> row +l/8, physical chunk l%8 holding
   // logical chunk (l%8) ^ s(row), s(row) = (row / 2) % 8 = 4 (i % 2) + l / 16. Weight
   // scales: instruction i moves rows 64*wave + 16i .. +15, lane l -> row +l/4, dword
@@ -221,18 +222,18 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_xl(XlArgs a) {
   const int sw1 = ((lane & 7) ^ (4 | (lane >> 4))) << 4;
   const int dA = w_row(64 * wave) * wrow + lane * 16;   // 64 consecutive expert rows per wave
   const int dS = w_row(64 * wave + (lane >> 2)) * srow + (lane & 3) * 4;
-  int dW[8], dB[8], dSc[4];
+  int dW[4], dB[8], dSc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) dW[i] = dA + 16 * i * wrow;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    dW[i] = dA + 16 * (i >> 1) * wrow + (i & 1) * 1024;
     dB[i] = sTok[64 * wave + 8 * i + (lane >> 3)] * arow + ((i & 1) ? sw1 : sw0);
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) dSc[i] = dS + 16 * i * srow;
 
-  auto copy_w = [&](int stage, int i) {   // weight stage (K steps 2 stage, 2 stage + 1), instruction i
-    dma16(rsrc_sized(rw, 2 * stage < KS), lds_addr(&sA[stage & 1][(4 * wave + (i >> 1)) * 2048 + (i & 1) * 1024]),
-          dW[i], stage * 2048);
+  auto copy_w = [&](int step, int i) {    // weight fragment 4 wave + i of K step `step`
+    dma16(rsrc_sized(rw, step < KS), lds_addr(&sA[step & 3][(4 * wave + i) * 1024]), dW[i], step * 1024);
   };
   auto copy_t = [&](int step, int i) {    // routed rows of K step `step`, instruction i
     dma16(rsrc_sized(ra, step < KS), lds_addr(&sB[step & 1][(64 * wave + 8 * i) * 128]), dB[i], step * 128);
@@ -242,13 +243,15 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_xl(XlArgs a) {
          chunk * kChunkRow);
   };
 
-  // Prologue: scale chunk 0 and quarter 0 of chunk 1, weight stage 0, routed rows
-  // of step 0; then (after M_{-1}) the first half of window 0.
+  // Prologue: scale chunk 0 and quarter 0 of chunk 1, weights of steps 0-2, routed
+  // rows of step 0; then (after M_{-1}) the column-7 part of window 0.
 #pragma unroll
   for (int i = 0; i < 4; ++i) copy_s(0, i);
   copy_s(1, 0);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) copy_w(0, i);
+  for (int st = 0; st < 3; ++st)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) copy_w(st, i);
 #pragma unroll
   for (int i = 0; i < 8; ++i) copy_t(0, i);
   wait_vmcnt<0>();
@@ -263,16 +266,16 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_xl(XlArgs a) {
   auto a_row = [&](int i) {   // first LDS row of this wave's weight fragment i
     return W13 ? (i < 4 ? 64 * wn + 16 * i : 128 + 64 * wn + 16 * (i - 4)) : 128 * wn + 16 * i;
   };
-  const uint8_t* pA = &sA[0][0] + lane * 16;   // + stage, fragment (a_row * 128), step * 1 KB
+  const uint8_t* pA = &sA[0][0] + lane * 16;   // + step buffer, fragment (a_row * 64)
   const uint8_t* pB0 = &sB[0][0] + 128 * wm * 128 + off0;
   const uint8_t* pB1 = &sB[0][0] + 128 * wm * 128 + off1;
   const uint8_t* pSa = &sSa[0][0] + c * kChunkRow + q;   // + chunk buffer, a_row(i) * 16, (step % 4) * 4
   const uint8_t* pSb = sSb + (128 * wm + c) * kSbRow;     // + 16 j kSbRow + 4 (step / 4)
 
-  // weight fragment i of a K step: stage buffer sb, half h (step % 2), scale chunk
-  // base sa (buffer of the step's chunk), step % 4 = u
-  auto read_a = [&](AOps& o, int sbuf, int h, const uint8_t* sa, int u, int i) {
-    o.w[i] = *reinterpret_cast<const v4i*>(pA + sbuf * kStageA + a_row(i) * 128 + h * 1024);
+  // weight fragment i of a K step: step buffer sbuf (step % 4), scale chunk base sa
+  // (buffer of the step's chunk), step % 4 = u
+  auto read_a = [&](AOps& o, int sbuf, const uint8_t* sa, int u, int i) {
+    o.w[i] = *reinterpret_cast<const v4i*>(pA + sbuf * kStepA + a_row(i) * 64);
     o.sa[i] = sa[a_row(i) * kChunkRow + u * 4];
   };
   v8i bf[4];
@@ -295,15 +298,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_xl(XlArgs a) {
   AOps ops[2];
   int bsc[8], bsn[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) read_a(ops[0], 0, 0, pSa, 0, i);
+  for (int i = 0; i < 8; ++i) read_a(ops[0], 0, pSa, 0, i);
 #pragma unroll
   for (int j = 0; j < 8; ++j) bsc[j] = read_bs(0, j);
   read_b(0, 0, 0);
   // column-7 part of window 0 (normally issued in column 7 of the previous step)
 #pragma unroll
   for (int i = 0; i < 4; ++i) copy_t(1, i);
-#pragma unroll
-  for (int i = 0; i < 2; ++i) copy_w(1, i);
 
   // K steps 4t .. 4t+3; step u uses register set u % 2 and reads step 4t+u+1 into
   // the other one.
@@ -319,33 +320,30 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_xl(XlArgs a) {
       for (int j = 0; j < 8; ++j) {
         if (j < 7) read_b(u & 1, j + 1, (j + 1) & 3);
         else read_b((u + 1) & 1, 0, 0);      // after M_s: routed rows of step s+1 are in LDS
-        // weight fragment j of step s+1 (stage (s+1)/2, half (s+1)%2, chunk (s+1)/4)
-        read_a(nxt, ((u + 1) >> 1) & 1, (u + 1) & 1, u < 3 ? saC : saN, (u + 1) & 3, j);
+        // weight fragment j of step s+1 (buffer (s+1)%4, chunk (s+1)/4)
+        read_a(nxt, (u + 1) & 3, u < 3 ? saC : saN, (u + 1) & 3, j);
         if (u == 3) bsn[j] = read_bs(t + 1, j);
 #pragma unroll
         for (int i = 0; i < 8; ++i) mma_agpr<u>(acc[i][j], cur.w[i], bf[j & 3], cur.sa[i], bsc[j]);
-        // window s (deadline M_s), columns 0-3: the rest of the routed rows of step
-        // s+1, weights of stage s/2+1 for even s, one weight-scale quarter
+        // window s (before M_s), columns 0-3: the rest of the routed rows of step s+1,
+        // one weight-scale quarter, then the weights of step s+3
         if (j < 2) {
           copy_t(s + 1, 4 + 2 * j);
           copy_t(s + 1, 5 + 2 * j);
         }
-        if (j < 4 && (u & 1) == 0) copy_w(s / 2 + 1, 4 + j);
-        if ((j == 2 || j == 3) && (u & 1) == 0) copy_w(s / 2 + 1, j);
+        if (j == 2 || j == 3) {          // weights of step s+3, last in the window
+          copy_w(s + 3, 2 * (j - 2));
+          copy_w(s + 3, 2 * (j - 2) + 1);
+        }
         if (j == 0) copy_s((s + 5) >> 2, (s + 5) & 3);
-        // window s+1, column 7 (after M_s): half of the routed rows of step s+2, and
-        // for odd s two weight blocks of stage (s+1)/2+1
+        // window s+1, column 7 (after M_s): half of the routed rows of step s+2
         if (j == 7) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) copy_t(s + 2, i);
-          if (u & 1) {
-            copy_w((s + 1) / 2 + 1, 0);
-            copy_w((s + 1) / 2 + 1, 1);
-          }
         }
         __builtin_amdgcn_sched_barrier(0);
-        if (j == 6) {                    // M_s
-          wait_vmcnt<0>();
+        if (j == 6) {                    // M_s: all but the 4 weight copies of step s+3
+          wait_vmcnt<4>();
           __syncthreads();
           __builtin_amdgcn_sched_barrier(0);
         }
