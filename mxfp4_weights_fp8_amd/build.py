@@ -43,6 +43,24 @@ def _compile(src: str) -> str:
     return obj
 
 
+def build_test_support(verbose: bool = False) -> str:
+    """Compile the test-support library tests/native/libmfma_probe.so (single-MFMA
+    probes the GPU tests use to check the hardware dot product; not part of the
+    product library)."""
+    root = os.path.dirname(HERE)
+    src = os.path.join(root, "tests", "native", "mfma_probe.hip")
+    out = os.path.join(root, "tests", "native", "libmfma_probe.so")
+    tmp = out + ".tmp"
+    cmd = [HIPCC, *FLAGS, "-shared", src, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, out)
+    if verbose:
+        print(f"built {out}")
+    return out
+
+
 def build(verbose: bool = False) -> str:
     """Compile every source and link the shared library; returns its path."""
     os.makedirs(BUILD, exist_ok=True)
@@ -62,4 +80,5 @@ def build(verbose: bool = False) -> str:
 
 if __name__ == "__main__":
     build(verbose=True)
+    build_test_support(verbose=True)
     sys.exit(0)

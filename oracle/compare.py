@@ -3,14 +3,25 @@
 TEST INFRASTRUCTURE ONLY (see the package docstring).
 
 * Final output y (bf16): relative error of the whole tensor against the float64
-  oracle, max_rel = max|y - r| / max|r| and mean_rel = sum|y - r| / sum|r|.
-  Elementwise ratios are not used: they blow up where r is near zero. Rounding
-  y to bf16 alone already gives mean_rel near 1.4e-3 on these workloads.
-* SwiGLU-output FP8 codes: the GPU evaluates the W13 GEMM in fp32 and silu with
-  its own exp, so a code may land one grid step away from the oracle's, and a
-  block whose amax sits right at a scale boundary (1.75 * 2^p) may take the
-  neighbouring scale. ``h_code_mismatch`` counts the elements that differ by
-  more than that.
+  oracle, max_rel = max|y - r| / max|r| and mean_rel = sum|y - r| / sum|r|, and
+  the largest per-row max_rel. Elementwise ratios are not used: they blow up
+  where r is near zero. Rounding y to bf16 alone already gives mean_rel near
+  1.4e-3 on these workloads.
+* SwiGLU-output FP8 codes. The bar: at most 1 grid step of difference on at
+  most 0.1% of the elements. ``h_code_mismatch`` sorts every element into
+    equal       -- same decoded value (+0 and -0 are equal);
+    one_step    -- same block scale, grid positions one apart;
+    scale_flip  -- a block scale that differs where the oracle's block amax sits
+                   within 2^-16 (relative) of a scale boundary 1.75 * 2^p, and
+                   values at most one grid step of the coarser scale apart;
+    beyond      -- any other difference. With an ``envelope`` (the exact SwiGLU
+                   value and a rigorous bound on the GPU's deviation from it,
+                   oracle/envelope.py) a beyond element is ``in_envelope`` when
+                   its code rounds from a value inside that bound under the GPU's
+                   block scale (and, where that scale differs, the block's exact
+                   amax lies within the block's largest bound of a boundary);
+                   otherwise, and always without an envelope, it is ``bad``.
+  Tests require bad == 0, frac_differ <= 0.1% and beyond at most a small cap.
 """
 
 from __future__ import annotations
@@ -26,9 +37,11 @@ def y_metrics(y_bits: np.ndarray, y_ref: np.ndarray) -> dict:
     r = np.asarray(y_ref, dtype=np.float64)
     d = np.abs(y - r)
     eq = (np.asarray(y_bits, dtype=np.uint16) == f64_to_bf16_rne(r))
+    row_rel = d.max(axis=-1) / np.maximum(np.abs(r).max(axis=-1), 1e-300) if d.size else np.zeros(1)
     return {
         "max_rel": float(d.max() / max(np.abs(r).max(), 1e-300)) if d.size else 0.0,
         "mean_rel": float(d.sum() / max(np.abs(r).sum(), 1e-300)) if d.size else 0.0,
+        "row_max_rel": float(row_rel.max()) if d.size else 0.0,
         "frac_equal_bf16": float(eq.mean()) if eq.size else 1.0,
         "finite": bool(np.isfinite(y).all()),
     }
@@ -42,28 +55,19 @@ def _signed_index(codes: np.ndarray) -> np.ndarray:
     return np.where(c & 0x80, -mag, mag)
 
 
-def h_code_mismatch(hq, hs, hq_ref, hs_ref, amax_ref, block: int = 128, h_ref=None, h_err=None) -> dict:
-    """Compare SwiGLU-output codes element by element.
+def _boundary_distance(amax: np.ndarray) -> np.ndarray:
+    """|amax - 1.75 * 2^p| for the boundary in amax's binade (amax = m * 2^p)."""
+    _, ex = np.frexp(amax)               # amax = 2m * 2^(ex-1)
+    return np.abs(amax - 1.75 * np.ldexp(1.0, ex - 1))
+
+
+def h_code_mismatch(hq, hs, hq_ref, hs_ref, amax_ref, block: int = 128, envelope=None) -> dict:
+    """Compare SwiGLU-output codes element by element (categories in the module
+    docstring).
 
     hq, hq_ref uint8 [R, C]; hs, hs_ref uint8 [R, C/block]; amax_ref float64
-    [R, C/block] (the oracle's block amax). Each element is
-      equal  -- same decoded value (+0 and -0 are equal);
-      close  -- the values are neighbours:
-                * same scale and grid positions one apart; or
-                * same scale, both values at most 2^-5 * scale in magnitude (the
-                  E4M3 grid is uniform with step 2^-9 * scale from 0 up to and
-                  including 2^-5 * scale, finer there than the rounding inside a
-                  hardware MX dot product) and at most 2^-6 * scale apart; or
-                * a scale that differs in a block whose oracle amax is within
-                  2^-16 (relative) of a scale boundary 1.75 * 2^p, and values at
-                  most one grid step of the coarser scale apart;
-                * with an envelope (h_ref, the exact values, and h_err >= 0): same
-                  scale and a code between the codes of h_ref - h_err and
-                  h_ref + h_err (the value rounds from somewhere in the envelope);
-                  the scale-boundary window widens to the block's largest h_err;
-      bad    -- anything else (a scale that differs away from a boundary makes
-                every element of its block bad).
-    The bar: no bad element, and at most 0.1% of elements close-but-unequal.
+    [R, C/block] (the oracle's block amax). ``envelope``: optional callable
+    (rows, cols) -> (h_exact, h_err), float64 arrays for the listed elements.
     """
     hq = np.asarray(hq).reshape(-1, np.asarray(hq).shape[-1])
     hq_ref = np.asarray(hq_ref).reshape(hq.shape)
@@ -75,42 +79,49 @@ def h_code_mismatch(hq, hs, hq_ref, hs_ref, amax_ref, block: int = 128, h_ref=No
 
     a = hq.reshape(R, nb, block)
     b = hq_ref.reshape(R, nb, block)
-    scale_a = np.ldexp(1.0, hs - 127)[..., None]
-    scale_b = np.ldexp(1.0, hs_ref - 127)[..., None]
-    va = E4M3_VALUES[a] * scale_a
-    vb = E4M3_VALUES[b] * scale_b
+    va = E4M3_VALUES[a] * np.ldexp(1.0, hs - 127)[..., None]
+    vb = E4M3_VALUES[b] * np.ldexp(1.0, hs_ref - 127)[..., None]
     equal = va == vb
     same = (hs == hs_ref)[..., None]
     dist = np.abs(_signed_index(a) - _signed_index(b))
-    fixed_step = (np.abs(E4M3_VALUES[a]) <= 2.0 ** -5) & (np.abs(E4M3_VALUES[b]) <= 2.0 ** -5) & \
-        (np.abs(va - vb) <= 2.0 ** -6 * scale_b)
+    one_step = ~equal & same & (dist == 1)
 
-    in_env = np.zeros_like(equal)
-    window = amax * 2.0 ** -16
-    if h_ref is not None:
-        hr = np.asarray(h_ref, dtype=np.float64).reshape(R, nb, block)
-        he = np.asarray(h_err, dtype=np.float64).reshape(R, nb, block)
-        lo = e4m3_encode(np.ldexp(hr - he, -(hs_ref - 127)[..., None]))
-        hi = e4m3_encode(np.ldexp(hr + he, -(hs_ref - 127)[..., None]))
-        ia, ilo, ihi = _signed_index(a), _signed_index(lo), _signed_index(hi)
-        in_env = (ia >= np.minimum(ilo, ihi)) & (ia <= np.maximum(ilo, ihi))
-        window = np.maximum(window, he.max(axis=-1))
-    _, ex = np.frexp(amax)               # amax = 2m * 2^(ex-1)
-    boundary = 1.75 * np.ldexp(1.0, ex - 1)
-    near = np.abs(amax - boundary) <= window
+    near = _boundary_distance(amax) <= amax * 2.0 ** -16
     coarse = np.ldexp(1.0, np.maximum(hs, hs_ref) - 127)[..., None]
     mag = np.maximum(np.abs(va), np.abs(vb)) / coarse
     _, mex = np.frexp(np.maximum(mag, 2.0 ** -6))
     step = np.ldexp(1.0, mex - 1 - 3) * coarse
-    close_diff = near[..., None] & (np.abs(va - vb) <= step)
+    scale_flip = ~equal & ~same & near[..., None] & (np.abs(va - vb) <= step)
 
-    close = ~equal & np.where(same, (dist <= 1) | fixed_step | in_env, close_diff)
-    bad = ~equal & ~close
+    beyond = ~equal & ~one_step & ~scale_flip
+    in_env = np.zeros_like(beyond)
+    if envelope is not None and beyond.any():
+        # every element of a block whose scale differs is needed for its amax bound
+        blk_rows, blk_ids = np.nonzero(beyond.any(axis=-1))
+        cols = (blk_ids[:, None] * block + np.arange(block)[None, :]).ravel()
+        rows = np.repeat(blk_rows, block)
+        h, err = envelope(rows, cols)
+        h = np.asarray(h, np.float64).reshape(-1, block)
+        err = np.asarray(err, np.float64).reshape(-1, block)
+        sg = hs[blk_rows, blk_ids]
+        lo = e4m3_encode(np.ldexp(h - err, -(sg - 127)[:, None]))
+        hi = e4m3_encode(np.ldexp(h + err, -(sg - 127)[:, None]))
+        ia = _signed_index(a[blk_rows, blk_ids])
+        ok = (ia >= _signed_index(lo)) & (ia <= _signed_index(hi))
+        exact_amax = np.abs(h).max(axis=-1)
+        scale_ok = (sg == hs_ref[blk_rows, blk_ids]) | (_boundary_distance(exact_amax) <= err.max(axis=-1))
+        in_env[blk_rows, blk_ids] = ok & scale_ok[:, None]
+    in_env &= beyond
+    bad = beyond & ~in_env
+
     n = int(a.size)
     idx = np.argwhere(bad)[:5]
     examples = [(int(a[i, j, k]), int(b[i, j, k]), float(va[i, j, k]), float(vb[i, j, k]), float(amax[i, j]))
                 for i, j, k in idx]
-    return {"elements": n, "bad_examples": examples, "differ": int((~equal).sum()), "bad": int(bad.sum()),
-            "frac_differ": float((~equal).sum()) / max(n, 1),
+    differ = int((~equal).sum())
+    return {"elements": n, "differ": differ, "frac_differ": differ / max(n, 1),
+            "one_step": int(one_step.sum()), "scale_flip": int(scale_flip.sum()),
+            "beyond": int(beyond.sum()), "in_envelope": int(in_env.sum()), "bad": int(bad.sum()),
             "scale_diff_blocks": int((~same[..., 0]).sum()),
-            "max_code_dist_same_scale": int(np.where(same, dist, 0).max()) if n else 0}
+            "max_code_dist_same_scale": int(np.where(same, dist, 0).max()) if n else 0,
+            "bad_examples": examples}

@@ -94,13 +94,14 @@ _BYTE_PAIR = torch.stack([_E2M1_T[torch.arange(256) & 15], _E2M1_T[torch.arange(
 
 
 def dequant_mxfp4(codes, scales) -> torch.Tensor:
-    """MXFP4 [N, K/2] codes + [N, K/32] E8M0 scales -> exact float64 [N, K]."""
+    """MXFP4 [N, K/2] codes + [N, K/32] E8M0 scales -> exact float64 [N, K]: each
+    byte looked up as its (low nibble, high nibble) value pair, each 32-element
+    block multiplied by its scale."""
     codes = torch.as_tensor(codes).cpu()
     scales = torch.as_tensor(scales).cpu()
     N, half = codes.shape
-    Kd = 2 * half
-    w = _BYTE_PAIR[codes.long()].reshape(N, Kd // 32, 32)
-    return (w * _E8M0_T[scales.long()].unsqueeze(-1)).reshape(N, Kd)
+    w = _BYTE_PAIR.index_select(0, codes.reshape(-1).to(torch.int32)).view(N, half // 16, 32)
+    return w.mul_(_E8M0_T[scales.to(torch.int64)].unsqueeze(-1)).view(N, 2 * half)
 
 
 def dequant_fp8_block(codes, scales) -> torch.Tensor:
@@ -117,40 +118,20 @@ def _silu_mul(g: np.ndarray, u: np.ndarray) -> np.ndarray:
         return g / (1.0 + np.exp(-g)) * u
 
 
-def _expert_ffn(xh: torch.Tensor, W13: torch.Tensor, W2: torch.Tensor, I: int, dot_rel_err: float = 0.0):
+def _expert_ffn(xh: torch.Tensor, W13: torch.Tensor, W2: torch.Tensor, I: int):
     """One expert on the dequantized rows xh [m, H] (float64): W13 GEMM, SwiGLU,
     requantization of the SwiGLU output, W2 GEMM. Returns (out [m, H] float64,
-    h codes, h scale codes, h block amax, h [m, I] float64, h_err [m, I]).
-
-    h_err is a comparison envelope, not part of the result: an upper bound on how
-    far an implementation's SwiGLU value may sit from h when each gate/up dot
-    product may err by dot_rel_err * sum_k |x_k w_k| (first-order propagation
-    through silu(g) * u, |d silu/dg| <= 1.1, plus 2^-20 relative for an fp32
-    evaluation). Zero when dot_rel_err is 0."""
+    h codes, h scale codes, h block amax)."""
     acc = (xh @ W13.T).numpy()
     g, u = acc[:, :I], acc[:, I:]
     h = _silu_mul(g, u)
+    del acc, g, u
     hq, hs, amax = quantize_blocks(h, 128)
     hh = torch.from_numpy(dequantize_blocks(hq, hs, 128))
-    h_err = np.zeros_like(h)
-    if dot_rel_err:
-        dacc = dot_rel_err * (xh.abs() @ W13.abs().T).numpy()
-        with np.errstate(over="ignore"):
-            silu = g / (1.0 + np.exp(-g))
-        h_err = 1.1 * np.abs(u) * dacc[:, :I] + np.abs(silu) * dacc[:, I:] + 2.0 ** -20 * np.abs(h)
-    return (hh @ W2.T).numpy(), hq, hs, amax, h, h_err
+    return (hh @ W2.T).numpy(), hq, hs, amax
 
 
 # ----------------------------------------------------------------------------- FFN
-
-
-#: Comparison envelope for the shared expert's FP8 x FP8 dot products. A hardware
-#: MX dot product (E4M3 x E4M3, one scale per 32 K) may sum the products of a
-#: 32-block in fixed point aligned to the block's largest product, so it is not
-#: exact; the envelope allows |error| <= 2^-12 * sum_k |x_k w_k| per gate/up dot.
-#: (E2M1 x E4M3 products have at most 5 significant bits and sum exactly, so the
-#: routed experts get no envelope.)
-FP8_DOT_REL_ERR = 2.0 ** -12
 
 
 def ffn_ref(x, topk_ids, topk_weights, w13, w13_s, w2, w2_s, shared=None, tokens=None) -> dict:
@@ -168,9 +149,12 @@ def ffn_ref(x, topk_ids, topk_weights, w13, w13_s, w2, w2_s, shared=None, tokens
       h_s    uint8 [n, K, I/128]
       h_amax float64 [n, K, I/128]
       valid  bool [n, K]       pick has an id in [0, E)
-      shared_h_q / shared_h_s / shared_h_amax (when a shared expert is given), and
-      shared_h / shared_h_err: the exact SwiGLU values and their comparison envelope
-      (see FP8_DOT_REL_ERR)
+      shared_h_q / shared_h_s / shared_h_amax (when a shared expert is given).
+
+    Memory stays near one expert's working set: each expert's W2 outputs are
+    added into y as soon as they are computed (the top-k reduction is a sum, so
+    the order of its terms only moves float64 rounding), and no per-pair output
+    rows are kept.
     """
     xb = _u16(x)
     ids = np.asarray(torch.as_tensor(topk_ids).cpu()).astype(np.int64)
@@ -191,28 +175,27 @@ def ffn_ref(x, topk_ids, topk_weights, w13, w13_s, w2, w2_s, shared=None, tokens
     h_amax = np.zeros((n, K, I // 128), dtype=np.float64)
     sid = ids[sel]
     valid = (sid >= 0) & (sid < E)
-    outs = np.zeros((n, K, H), dtype=np.float64)
     for e in np.unique(sid[valid]):
         rows, picks = np.nonzero(sid == e)
         W13 = dequant_mxfp4(w13[int(e)], w13_s[int(e)])
         W2 = dequant_mxfp4(w2[int(e)], w2_s[int(e)])
-        o, hq, hs, am, _, _ = _expert_ffn(xh[torch.from_numpy(rows)], W13, W2, I)
-        outs[rows, picks] = o
+        o, hq, hs, am = _expert_ffn(xh[torch.from_numpy(rows)], W13, W2, I)
+        del W13, W2
+        # top-k weighted reduction: a token may pick the same expert twice
+        np.add.at(y, rows, wts[sel[rows], picks][:, None] * o)
+        del o
         h_q[rows, picks] = hq
         h_s[rows, picks] = hs
         h_amax[rows, picks] = am
-    # top-k weighted reduction, picks in order, dropped picks contribute nothing
-    for j in range(K):
-        y += np.where(valid[:, j:j + 1], wts[sel, j:j + 1] * outs[:, j], 0.0)
     res = {"y": y, "x_q": x_q, "x_s": x_s, "h_q": h_q, "h_s": h_s, "h_amax": h_amax,
            "valid": valid}
     if shared is not None:
         Is = shared["w2s"].shape[1]
         W13s = dequant_fp8_block(shared["w13s"], shared["w13s_s"])
         W2s = dequant_fp8_block(shared["w2s"], shared["w2s_s"])
-        o, hq, hs, am, h, h_err = _expert_ffn(xh, W13s, W2s, Is, dot_rel_err=FP8_DOT_REL_ERR)
+        o, hq, hs, am = _expert_ffn(xh, W13s, W2s, Is)
         y += o
-        res.update(shared_h_q=hq, shared_h_s=hs, shared_h_amax=am, shared_h=h, shared_h_err=h_err)
+        res.update(shared_h_q=hq, shared_h_s=hs, shared_h_amax=am)
     return res
 
 

@@ -27,24 +27,6 @@ def test_one_step_is_close_two_steps_is_bad():
     assert m["differ"] == 2 and m["bad"] == 1
 
 
-def test_fixed_step_region():
-    q, s, a = _blocks()
-    g = q.copy()
-    g[0, 0], q2 = 0x0A, q.copy()
-    q2[0, 0] = 0x08                             # 1.25 * 2^-6 vs 2^-6: two 2^-9 steps apart
-    m = h_code_mismatch(g, s, q2, s, a)
-    assert m["bad"] == 0 and m["differ"] == 1
-    g[0, 0] = 0x12                              # 2^-5 * 1.25: outside the fixed-step region
-    assert h_code_mismatch(g, s, q2, s, a)["bad"] == 1
-    # the region's top end, 2^-5 (code 0x10), is still on the uniform 2^-9 grid:
-    # 0x0E = 1.75 * 2^-6 lies two steps below it
-    g[0, 0], q2[0, 0] = 0x8E, 0x90
-    m = h_code_mismatch(g, s, q2, s, a)
-    assert m["bad"] == 0 and m["differ"] == 1
-    g[0, 0], q2[0, 0] = 0x90, 0x92              # 2^-5 vs 1.25 * 2^-5: step 2^-8 above the region
-    assert h_code_mismatch(g, s, q2, s, a)["bad"] == 1
-
-
 def test_sign_of_zero_is_equal_and_scale_flip_away_from_boundary_is_bad():
     q, s, a = _blocks()
     g = q.copy()
@@ -66,23 +48,80 @@ def test_y_metrics():
     assert abs(m2["mean_rel"] - 1.0) < 1e-2
 
 
-def test_envelope_accepts_codes_reachable_from_the_envelope_only():
-    """A code two grid steps from the oracle's is accepted only when the
-    envelope [h - err, h + err] around the exact value reaches it (scale 2^-8,
-    binade [2^-5, 2^-4) of the scaled grid: step 2^-8 * 2^-8)."""
+def test_two_steps_near_zero_are_beyond_without_an_envelope():
+    """The former fixed-step region is gone: near zero, two grid steps are two
+    steps (counted beyond, bad without an envelope)."""
+    q, s, a = _blocks()
+    g, q2 = q.copy(), q.copy()
+    g[0, 0], q2[0, 0] = 0x0A, 0x08             # 1.25 * 2^-6 vs 2^-6: two 2^-9 steps
+    m = h_code_mismatch(g, s, q2, s, a)
+    assert m["beyond"] == 1 and m["bad"] == 1 and m["one_step"] == 0
+
+
+def test_categories_are_counted():
+    q, s, a = _blocks(R=4, C=256)
+    g = q.copy()
+    big = np.argwhere((q & 0x7F) > 0x40)
+    g[tuple(big[0])] += 1
+    g[tuple(big[1])] += 1
+    g[tuple(big[2])] += 3
+    m = h_code_mismatch(g, s, q, s, a)
+    assert (m["differ"], m["one_step"], m["beyond"], m["bad"]) == (3, 2, 1, 1)
+    assert m["max_code_dist_same_scale"] == 3 and abs(m["frac_differ"] - 3 / q.size) < 1e-15
+
+
+def _envelope_case():
+    """One block, scale 2^-8 (code 119); the exact value sits exactly on code
+    0x96 = -1.75 * 2^-5 of the scaled grid (step 2^-8 there)."""
     R, C = 1, 128
-    scale_code = np.array([[119]], dtype=np.uint8)            # 2^-8
+    scale_code = np.array([[119]], dtype=np.uint8)
     amax = np.array([[1.19]])
     h = np.zeros((R, C))
-    h[0, 0] = -1.75 * 2.0 ** -5 * 2.0 ** -8                    # exactly code 0x96 after scaling
+    h[0, 0] = -1.75 * 2.0 ** -5 * 2.0 ** -8
+    h[0, 1] = 1.19                              # the block's amax element (code unchanged)
     ref = e4m3_encode(np.ldexp(h, 8))
     assert ref[0, 0] == 0x96
     gpu = ref.copy()
-    gpu[0, 0] = 0x98                                           # -2^-4 * 2^-8: two steps away
-    err_wide = np.full((R, C), 4e-5)
-    m = h_code_mismatch(gpu, scale_code, ref, scale_code, amax, h_ref=h, h_err=err_wide)
-    assert m["bad"] == 0 and m["differ"] == 1
-    m = h_code_mismatch(gpu, scale_code, ref, scale_code, amax, h_ref=h, h_err=np.full((R, C), 1e-6))
-    assert m["bad"] == 1
-    m = h_code_mismatch(gpu, scale_code, ref, scale_code, amax)  # no envelope: the default rules
-    assert m["bad"] == 1
+    gpu[0, 0] = 0x98                            # -2^-4 * 2^-8: two steps away
+    return gpu, scale_code, ref, amax, h
+
+
+def test_envelope_accepts_codes_reachable_from_the_envelope_only():
+    gpu, sc, ref, amax, h = _envelope_case()
+    calls = []
+
+    def env_of(err):
+        def f(rows, cols):
+            calls.append((rows.copy(), cols.copy()))
+            return h[rows, cols], np.full(rows.size, err)
+        return f
+
+    m = h_code_mismatch(gpu, sc, ref, sc, amax, envelope=env_of(4e-5))
+    assert (m["beyond"], m["in_envelope"], m["bad"]) == (1, 1, 0)
+    # the envelope is asked for the whole block of the beyond element only
+    assert np.array_equal(calls[0][0], np.zeros(128)) and np.array_equal(calls[0][1], np.arange(128))
+    m = h_code_mismatch(gpu, sc, ref, sc, amax, envelope=env_of(1e-6))
+    assert (m["in_envelope"], m["bad"]) == (0, 1)
+    assert h_code_mismatch(gpu, sc, ref, sc, amax)["bad"] == 1
+
+
+def test_envelope_scale_change_needs_amax_near_a_boundary():
+    """A GPU block scale one above the oracle's: accepted through the envelope only
+    when the block's exact amax lies within the block's largest bound of a scale
+    boundary and every code rounds from inside the envelope under the GPU scale."""
+    R, C = 1, 128
+    h = np.random.default_rng(4).uniform(-1, 1, (R, C))
+    h[0, 7] = 1.75 * (1 - 2.0 ** -12)           # amax just below the boundary 1.75
+    qr, sr, ar = quantize_blocks(h)
+    qg, sg, _ = quantize_blocks(h * (1 + 2.0 ** -11))   # the GPU's values crossed it
+    assert sg[0, 0] == sr[0, 0] + 1
+
+    def env_of(err):
+        return lambda rows, cols: (h[rows, cols], np.full(rows.size, err))
+
+    # 2^-16-relative window of the plain rule does not cover this amax distance
+    assert h_code_mismatch(qg, sg, qr, sr, ar)["bad"] > 0
+    m = h_code_mismatch(qg, sg, qr, sr, ar, envelope=env_of(2.0 ** -10))
+    assert m["bad"] == 0 and m["in_envelope"] == m["beyond"] > 0
+    m = h_code_mismatch(qg, sg, qr, sr, ar, envelope=env_of(2.0 ** -16))
+    assert m["bad"] > 0
