@@ -54,6 +54,11 @@ __device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c, float 
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
 }
 
+// Four E4M3 codes (byte i of `word`) times 2^e, as two packed bf16 pairs (code 0
+// in the low half of the first). Exact when the values lie in bf16's range: an
+// E4M3 value has at most 4 significant bits.
+__device__ __forceinline__ uint2 e4m3x4_to_bf16(uint32_t word, int e);
+
 // fp32 -> bf16 bit pattern, round to nearest even (finite inputs).
 __device__ __forceinline__ uint16_t bf16_rne(float f) {
   uint32_t b = __float_as_uint(f);
@@ -62,6 +67,16 @@ __device__ __forceinline__ uint16_t bf16_rne(float f) {
 }
 
 __device__ __forceinline__ float bf16_to_float(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+__device__ __forceinline__ uint2 e4m3x4_to_bf16(uint32_t word, int e) {
+  const int w = (int)word;
+  const float v0 = __builtin_amdgcn_ldexpf(__builtin_amdgcn_cvt_f32_fp8(w, 0), e);
+  const float v1 = __builtin_amdgcn_ldexpf(__builtin_amdgcn_cvt_f32_fp8(w, 1), e);
+  const float v2 = __builtin_amdgcn_ldexpf(__builtin_amdgcn_cvt_f32_fp8(w, 2), e);
+  const float v3 = __builtin_amdgcn_ldexpf(__builtin_amdgcn_cvt_f32_fp8(w, 3), e);
+  return make_uint2((uint32_t)bf16_rne(v0) | ((uint32_t)bf16_rne(v1) << 16),
+                    (uint32_t)bf16_rne(v2) | ((uint32_t)bf16_rne(v3) << 16));
+}
 
 // SiLU(g) * u = g * u / (1 + e^-g), with the hardware exp2 and reciprocal (about
 // 1 ulp each): the result is requantized to E4M3 (3 mantissa bits), so fp32

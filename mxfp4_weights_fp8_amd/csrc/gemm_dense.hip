@@ -23,6 +23,20 @@
 // step k+3 is issued while step k is multiplied, so two steps of copies are in
 // flight. The K-step count is padded to even with a step of zeros (exact: the
 // MFMA adds zero products).
+//
+// W13s in bf16 (the form moe_ffn runs). The block-scaled MFMA sums the products of
+// a 32-element block after truncating each to 13 fraction bits below the block's
+// largest exponent sum; with FP8 x FP8 operands (up to 8 significant bits per
+// product, wide dynamic range inside a block) that moves gate/up values by about
+// 1e-5 of their size and changed 0.1-0.2% of the SwiGLU codes. Every dequantized
+// E4M3 value (code x power-of-two scale) is exact in bf16, and the bf16 MFMA keeps
+// 24 fraction bits (about 1e-7 relative on the same dots), so the gate/up GEMM
+// runs on v_mfma_f32_16x16x32_bf16 over operands expanded to bf16 once per call:
+// the weights with their block scale folded in, the activations written by the
+// quantizer. A 128-byte LDS row of a stage then holds 64 K; lane (c, q) reads the
+// chunks q and 4 + q of its row, which are exactly the bf16 instruction's K
+// 8q .. 8q+7 of the stage's first and second 32 K. Costs twice the MFMA time of
+// the FP8 form (0.36 TFLOP at 32K tokens, Is 384).
 #include "device_common.h"
 #include "host_internal.h"
 #include "lds_copy.h"
@@ -41,10 +55,10 @@ constexpr int kMaxSteps = 64;             // K steps whose scales fit the tile's
 constexpr int kSbRow = kMaxSteps + 4;     // activation-scale row stride (17 dwords: distinct banks)
 
 struct DenseArgs {
-  const uint8_t* act;      // W13s: x_q [T, H]; W2s: sh_q [T, Is]
-  const uint8_t* act_s;    // [T, Kd/128]
-  const uint8_t* w;        // [N, Kd] E4M3
-  const uint8_t* w_s;      // [N/128, Kd/128] E8M0
+  const uint8_t* act;      // W13s: x_q [T, H] (bf16 form: x_hat [T, H] bf16); W2s: sh_q [T, Is]
+  const uint8_t* act_s;    // [T, Kd/128] (unused in the bf16 form)
+  const uint8_t* w;        // [N, Kd] E4M3 (bf16 form: [N, Kd] bf16, scales folded in)
+  const uint8_t* w_s;      // [N/128, Kd/128] E8M0 (unused in the bf16 form)
   uint8_t* h_q;            // W13s out [T, Is]
   uint8_t* h_s;            // [T, Is/128]
   uint16_t* o;             // W2s out [T, N]: fp16 codes
@@ -53,8 +67,15 @@ struct DenseArgs {
   int T, Kd, N, Is;
 };
 
-template <bool W13>
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ v4f mfma_bf16_16x16x32(const v4i a, const v4i b, v4f c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a), __builtin_bit_cast(v8bf, b), c, 0, 0, 0);
+}
+
+template <bool W13, bool BF16 = false>
 __global__ __launch_bounds__(kThreads, 1) void k_gemm_dense(DenseArgs a) {
+  static_assert(W13 || !BF16, "the bf16 form is the gate/up GEMM");
   __shared__ __attribute__((aligned(1024))) uint8_t sA[kBufs][kStageA];   // [buf][row][128 B]
   __shared__ __attribute__((aligned(1024))) uint8_t sB[kBufs][kStageB];
   __shared__ __attribute__((aligned(16))) uint8_t sSb[kTokRows][kSbRow];  // [row][step]
@@ -67,8 +88,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_dense(DenseArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4, c = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave & 1, wn = wave >> 1;
-  const int KS = a.Kd / 128;
-  const int KSp = (KS + 1) & ~1;                        // padded to even with a zero step
+  const int row_bytes = BF16 ? 2 * a.Kd : a.Kd;      // one operand row in global memory
+  const int KS = row_bytes / 128;                     // 128-byte LDS steps (bf16: 64 K each)
+  const int KSp = (KS + 1) & ~1;                      // padded to even with a zero step
 
   // first weight row of each 128-row half of the tile
   const int wbase0 = W13 ? nb * 128 : nb * 256;
@@ -77,7 +99,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_dense(DenseArgs a) {
   // scale tables: activation scales of the tile's tokens (padding rows repeat the
   // last valid token; steps past the last read as 2^-127), weight block scales of
   // the two 128-row halves (a half past N reads 2^-127)
-  {
+  if constexpr (!BF16) {
     const int r = tid >> 1, s0 = (tid & 1) * (kMaxSteps / 2);
     const uint8_t* src = a.act_s + (int64_t)(t0 + min(r, nrows - 1)) * KS;
     uint32_t v[kMaxSteps / 8];
@@ -112,11 +134,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_dense(DenseArgs a) {
   const int sw0 = ((lane & 7) ^ (lane >> 4)) << 4;
   const int sw1 = ((lane & 7) ^ (4 | (lane >> 4))) << 4;
   const int wrow_lane = (wave < 2 ? wbase0 : wbase1) + 64 * (wave & 1) + (lane >> 3);
-  const int dA = wrow_lane * a.Kd;
+  const int dA = wrow_lane * row_bytes;
   int dB[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
-    dB[i] = (t0 + min(32 * wave + 8 * i + (lane >> 3), nrows - 1)) * a.Kd + ((i & 1) ? sw1 : sw0);
+    dB[i] = (t0 + min(32 * wave + 8 * i + (lane >> 3), nrows - 1)) * row_bytes + ((i & 1) ? sw1 : sw0);
 
   // copy instructions of step st into buffer buf, 3 per part (parts 0..3: weight
   // 2p, 2p+1 and activation p), so they spread over the MFMA groups
@@ -125,7 +147,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_dense(DenseArgs a) {
 #pragma unroll
     for (int i = 2 * p; i < 2 * p + 2; ++i)
       dma16(rsrc_sized(rw, valid), lds_addr(&sA[buf][(64 * wave + 8 * i) * 128]),
-            dA + 8 * i * a.Kd + ((i & 1) ? sw1 : sw0) + st * 128, 0);
+            dA + 8 * i * row_bytes + ((i & 1) ? sw1 : sw0) + st * 128, 0);
     dma16(rsrc_sized(ra, valid), lds_addr(&sB[buf][(32 * wave + 8 * p) * 128]), dB[p] + st * 128, 0);
   };
 
@@ -162,10 +184,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_dense(DenseArgs a) {
       const v4i hi = *reinterpret_cast<const v4i*>(pB1 + ob);
       o.b[p][0] = lo[0]; o.b[p][1] = lo[1]; o.b[p][2] = lo[2]; o.b[p][3] = lo[3];
       o.b[p][4] = hi[0]; o.b[p][5] = hi[1]; o.b[p][6] = hi[2]; o.b[p][7] = hi[3];
-      o.sb[p] = pSb[st + p * 16 * kSbRow];
-      if (p == 0) {
-        o.sw[0] = sSw[W13 ? 0 : wn][st];
-        o.sw[1] = sSw[W13 ? 1 : wn][st];
+      if constexpr (!BF16) {
+        o.sb[p] = pSb[st + p * 16 * kSbRow];
+        if (p == 0) {
+          o.sw[0] = sSw[W13 ? 0 : wn][st];
+          o.sw[1] = sSw[W13 ? 1 : wn][st];
+        }
       }
     } else {
 #pragma unroll
@@ -180,8 +204,17 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_dense(DenseArgs a) {
   };
   auto mma_row = [&](const Ops& o, int i) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      acc[i][j] = mfma_scale_16x16x128<kFmtE4M3, kFmtE4M3>(o.w[i], o.b[j], acc[i][j], o.sw[i < 4 ? 0 : 1], o.sb[j]);
+    for (int j = 0; j < 4; ++j) {
+      if constexpr (BF16) {
+        // K 0..31 of the stage (ints 0..3 of each operand), then K 32..63
+        acc[i][j] = mfma_bf16_16x16x32(v4i{o.w[i][0], o.w[i][1], o.w[i][2], o.w[i][3]},
+                                       v4i{o.b[j][0], o.b[j][1], o.b[j][2], o.b[j][3]}, acc[i][j]);
+        acc[i][j] = mfma_bf16_16x16x32(v4i{o.w[i][4], o.w[i][5], o.w[i][6], o.w[i][7]},
+                                       v4i{o.b[j][4], o.b[j][5], o.b[j][6], o.b[j][7]}, acc[i][j]);
+      } else {
+        acc[i][j] = mfma_scale_16x16x128<kFmtE4M3, kFmtE4M3>(o.w[i], o.b[j], acc[i][j], o.sw[i < 4 ? 0 : 1], o.sb[j]);
+      }
+    }
   };
 
   // Prologue: copies of steps 0..2, operands of step 0.
@@ -276,16 +309,39 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_dense(DenseArgs a) {
   }
 }
 
+// FP8 E4M3 codes with one E8M0 scale per 128 x 128 block -> bf16 values with the
+// scale folded in: w[n][k] = E4M3(code) * 2^(scale - 127). Exact while the value
+// stays inside bf16's range (block scales 2^-124 .. 2^119). One thread per 8
+// consecutive codes.
+__global__ __launch_bounds__(256) void k_fp8_block_to_bf16(const uint8_t* __restrict__ w,
+                                                            const uint8_t* __restrict__ w_s,
+                                                            uint16_t* __restrict__ out, int64_t n8, int Kd) {
+  const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (g >= n8) return;
+  const int64_t e0 = g * 8;
+  const int64_t n = e0 / Kd;
+  const int k = (int)(e0 - n * Kd);
+  const int ex = (int)w_s[(n / 128) * (Kd / 128) + k / 128] - 127;
+  const uint2 c = *reinterpret_cast<const uint2*>(w + e0);
+  const uint2 lo = e4m3x4_to_bf16(c.x, ex), hi = e4m3x4_to_bf16(c.y, ex);
+  const uint32_t r[4] = {lo.x, lo.y, hi.x, hi.y};
+  *reinterpret_cast<uint4*>(out + e0) = make_uint4(r[0], r[1], r[2], r[3]);
+}
+
 }  // namespace
 
 bool dense_path_supported(const moe_dims& d) { return d.H / 128 <= kMaxSteps && d.Is / 128 <= kMaxSteps; }
 
-hipError_t launch_shared13(const moe_dims& d, const uint8_t* x_q, const uint8_t* x_s, const uint8_t* w13s,
-                           const uint8_t* w13s_s, uint8_t* sh_q, uint8_t* sh_s, hipStream_t s) {
-  DenseArgs a{x_q, x_s, w13s, w13s_s, sh_q, sh_s, nullptr, nullptr,
-              (uint32_t)((int64_t)d.T * d.H), (uint32_t)((int64_t)2 * d.Is * d.H), d.T, d.H, 2 * d.Is, d.Is};
-  hipLaunchKernelGGL(k_gemm_dense<true>, dim3(d.Is / 128, (unsigned)ceil_div(d.T, kTokRows)), dim3(kThreads), 0, s,
-                     a);
+hipError_t launch_shared13_bf16(const moe_dims& d, const uint16_t* x_hat, const uint8_t* w13s, const uint8_t* w13s_s,
+                                uint16_t* w13s_bf16, uint8_t* sh_q, uint8_t* sh_s, hipStream_t s) {
+  const int64_t n8 = (int64_t)2 * d.Is * d.H / 8;
+  hipLaunchKernelGGL(k_fp8_block_to_bf16, dim3((unsigned)ceil_div(n8, 256)), dim3(256), 0, s, w13s, w13s_s, w13s_bf16,
+                     n8, d.H);
+  DenseArgs a{reinterpret_cast<const uint8_t*>(x_hat), nullptr, reinterpret_cast<const uint8_t*>(w13s_bf16), nullptr,
+              sh_q, sh_s, nullptr, nullptr,
+              (uint32_t)((int64_t)d.T * d.H * 2), (uint32_t)((int64_t)2 * d.Is * d.H * 2), d.T, d.H, 2 * d.Is, d.Is};
+  hipLaunchKernelGGL((k_gemm_dense<true, true>), dim3(d.Is / 128, (unsigned)ceil_div(d.T, kTokRows)), dim3(kThreads),
+                     0, s, a);
   return hipGetLastError();
 }
 

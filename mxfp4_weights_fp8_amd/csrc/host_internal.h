@@ -74,6 +74,8 @@ struct FfnWs {
   uint8_t* sh_s;  // [T, Is/128]
   uint16_t* so;   // [T, H] shared-expert output (fp16 codes)
   uint8_t* sos;   // [T, H/32] their scales
+  uint16_t* x_hat;      // [T, H] bf16 quantized activations (shared expert only)
+  uint16_t* w13s_bf16;  // [2Is, H] bf16 shared gate/up weights, block scales folded in
 };
 size_t ffn_ws_layout(const moe_dims& d, void* base, FfnWs* out);
 
@@ -84,7 +86,9 @@ hipError_t launch_plan(const moe_dims& d, const int32_t* ids, int32_t* offsets, 
 // Row-major E2M1 codes [rows, K/2] -> the kernel-native blocked layout (rows % 16
 // == 0, K % 128 == 0).
 hipError_t launch_pack_weights(const uint8_t* w, uint8_t* out, int64_t rows, int K, hipStream_t s);
-hipError_t launch_quant_act(const uint16_t* x, uint8_t* x_q, uint8_t* x_s, int T, int H, hipStream_t s);
+// x_hat (optional): the quantized values E4M3(code) * scale as bf16 [T, H].
+hipError_t launch_quant_act(const uint16_t* x, uint8_t* x_q, uint8_t* x_s, int T, int H, hipStream_t s,
+                            uint16_t* x_hat = nullptr);
 // Small-M kernels walk up to two work lists in one launch: workgroup row y <
 // cap0 takes item y of list 0, the rest item y - cap0 of list 1; an item covers
 // rows[l] routed rows in 16-row tiles (counts live on the device).
@@ -140,8 +144,11 @@ hipError_t launch_w2_xl(const moe_dims& d, const int2* items, const int32_t* n_i
 // Dense FP8 shared expert: W13s + SwiGLU/requant into sh_q/sh_s, then W2s into
 // fp32 rows so [T, H]. Needs H/128 and Is/128 at most 64.
 bool dense_path_supported(const moe_dims& d);
-hipError_t launch_shared13(const moe_dims& d, const uint8_t* x_q, const uint8_t* x_s, const uint8_t* w13s,
-                           const uint8_t* w13s_s, uint8_t* sh_q, uint8_t* sh_s, hipStream_t s);
+// The gate/up GEMM in bf16: expands w13s (FP8, 128 x 128 block scales) into
+// w13s_bf16 (workspace, [2Is, H]) and multiplies by x_hat (bf16 quantized
+// activations). Needs T * H < 2^30.
+hipError_t launch_shared13_bf16(const moe_dims& d, const uint16_t* x_hat, const uint8_t* w13s, const uint8_t* w13s_s,
+                                uint16_t* w13s_bf16, uint8_t* sh_q, uint8_t* sh_s, hipStream_t s);
 hipError_t launch_shared2(const moe_dims& d, const uint8_t* sh_q, const uint8_t* sh_s, const uint8_t* w2s,
                           const uint8_t* w2s_s, uint16_t* so, uint8_t* sos, hipStream_t s);
 hipError_t launch_combine(const uint16_t* o, const uint8_t* os, const float* topk_weights, const int32_t* pair_rows,

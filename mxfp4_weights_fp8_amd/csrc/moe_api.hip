@@ -23,6 +23,8 @@ size_t ffn_ws_layout(const moe_dims& d, void* base, FfnWs* out) {
   const size_t o_shs = take((size_t)(T * Is / 128));
   const size_t o_so = take(Is ? sizeof(uint16_t) * (size_t)(T * H) : 0);
   const size_t o_sos = take(Is ? (size_t)(T * H / 32) : 0);
+  const size_t o_xhat = take(Is ? sizeof(uint16_t) * (size_t)(T * H) : 0);
+  const size_t o_w13s = take(Is ? sizeof(uint16_t) * (size_t)(2 * Is * H) : 0);
   if (out) {
     char* b = static_cast<char*>(base);
     out->x_q = reinterpret_cast<uint8_t*>(b + o_xq);
@@ -35,6 +37,8 @@ size_t ffn_ws_layout(const moe_dims& d, void* base, FfnWs* out) {
     out->sh_s = reinterpret_cast<uint8_t*>(b + o_shs);
     out->so = reinterpret_cast<uint16_t*>(b + o_so);
     out->sos = reinterpret_cast<uint8_t*>(b + o_sos);
+    out->x_hat = reinterpret_cast<uint16_t*>(b + o_xhat);
+    out->w13s_bf16 = reinterpret_cast<uint16_t*>(b + o_w13s);
   }
   return off;
 }
@@ -132,7 +136,8 @@ int moe_ffn(const moe_dims* dims, const uint16_t* x, const float* topk_weights, 
       !w2_s || !y || !ws)
     return MOE_EINVAL;
   if (use_shared && (!shared->w13s || !shared->w13s_s || !shared->w2s || !shared->w2s_s)) return MOE_EINVAL;
-  if (use_shared && !dense_path_supported(d)) return MOE_EUNSUPPORTED;
+  if (use_shared && (!dense_path_supported(d) || (int64_t)d.T * d.H >= ((int64_t)1 << 30)))
+    return MOE_EUNSUPPORTED;
   FfnWs fw;
   if (ws_bytes < ffn_ws_layout(d, ws, &fw)) return MOE_EWORKSPACE;
   PlanWs pw;
@@ -143,7 +148,7 @@ int moe_ffn(const moe_dims* dims, const uint16_t* x, const float* topk_weights, 
   uint8_t* h_s = dbg && dbg->h_s ? dbg->h_s : fw.h_s;
 
   record(dbg, MOE_EV_START, s);
-  hipError_t err = launch_quant_act(x, x_q, x_s, d.T, d.H, s);
+  hipError_t err = launch_quant_act(x, x_q, x_s, d.T, d.H, s, use_shared ? fw.x_hat : nullptr);
   if (err != hipSuccess) return MOE_EHIP;
   record(dbg, MOE_EV_QUANT_DONE, s);
 
@@ -217,7 +222,7 @@ int moe_ffn(const moe_dims* dims, const uint16_t* x, const float* topk_weights, 
   if (use_shared) {
     uint8_t* sh_q = dbg && dbg->sh_q ? dbg->sh_q : fw.sh_q;
     uint8_t* sh_s = dbg && dbg->sh_s ? dbg->sh_s : fw.sh_s;
-    err = launch_shared13(d, x_q, x_s, shared->w13s, shared->w13s_s, sh_q, sh_s, s);
+    err = launch_shared13_bf16(d, fw.x_hat, shared->w13s, shared->w13s_s, fw.w13s_bf16, sh_q, sh_s, s);
     if (err != hipSuccess) return MOE_EHIP;
     err = shared2_fewk_supported(d)
               ? launch_shared2_fewk(d, sh_q, sh_s, shared->w2s, shared->w2s_s, fw.so, fw.sos, s)

@@ -4,6 +4,10 @@
 // each loads 8 bf16 (16 B) and stores 8 codes (8 B); the block amax is a 16-lane
 // butterfly. The scale is the smallest power of two with amax <= 448 * scale, so
 // x / scale is exact and no code saturates; codes round to nearest-even.
+// Optionally the quantized values themselves, E4M3(code) * scale, are written as
+// bf16 too (exact: at most 4 significant bits, inside bf16's range for every
+// scale a finite bf16 block below 2^127 can take): the operand of the shared
+// expert's bf16 gate/up GEMM.
 #include "device_common.h"
 #include "host_internal.h"
 
@@ -14,7 +18,8 @@ constexpr int kQuantThreads = 256;
 
 __global__ __launch_bounds__(kQuantThreads) void k_quant_act(const uint16_t* __restrict__ x,
                                                               uint8_t* __restrict__ x_q,
-                                                              uint8_t* __restrict__ x_s, int64_t n_blocks) {
+                                                              uint8_t* __restrict__ x_s,
+                                                              uint16_t* __restrict__ x_hat, int64_t n_blocks) {
   const int sub = threadIdx.x & 15;
   const int64_t groups_per_cta = kQuantThreads / 16;
   for (int64_t blk = (int64_t)blockIdx.x * groups_per_cta + (threadIdx.x >> 4); blk < n_blocks;
@@ -38,18 +43,24 @@ __global__ __launch_bounds__(kQuantThreads) void k_quant_act(const uint16_t* __r
     const uint32_t hi = e4m3_pack4(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv);
     *reinterpret_cast<uint2*>(x_q + base) = make_uint2(lo, hi);
     if (sub == 0) x_s[blk] = (uint8_t)(e + 127);
+    if (x_hat) {
+      const uint2 a = e4m3x4_to_bf16(lo, e), b = e4m3x4_to_bf16(hi, e);
+      *reinterpret_cast<uint4*>(x_hat + base) = make_uint4(a.x, a.y, b.x, b.y);
+    }
   }
 }
 
 }  // namespace
 
-hipError_t launch_quant_act(const uint16_t* x, uint8_t* x_q, uint8_t* x_s, int T, int H, hipStream_t s) {
+hipError_t launch_quant_act(const uint16_t* x, uint8_t* x_q, uint8_t* x_s, int T, int H, hipStream_t s,
+                            uint16_t* x_hat) {
   const int64_t n_blocks = (int64_t)T * (H / 128);
   if (n_blocks == 0) return hipSuccess;
   // one 128-column block per 16 lanes (at 32K tokens 0.120 ms against 0.127 ms with the
   // grid capped at 4096 workgroups and a grid-stride loop)
   const int64_t ctas = ceil_div(n_blocks, kQuantThreads / 16);
-  hipLaunchKernelGGL(k_quant_act, dim3((unsigned)ctas), dim3(kQuantThreads), 0, s, x, x_q, x_s, n_blocks);
+  hipLaunchKernelGGL(k_quant_act, dim3((unsigned)ctas), dim3(kQuantThreads), 0, s, x, x_q, x_s, x_hat,
+                     n_blocks);
   return hipGetLastError();
 }
 

@@ -1,6 +1,8 @@
 """GPU parity: the HIP path (through the C-ABI) against the CPU oracle on the same
-seeded inputs. Plans and activation codes bit-exact; SwiGLU codes within one grid
-step on at most 0.1% of elements; y within max-rel 2e-2 / mean-rel 2e-3."""
+seeded inputs. Plans and activation codes bit-exact; SwiGLU codes: at most 0.1%
+differ, by one grid step, except a capped count that must round from inside the
+hardware-dot envelope (tests/gpu_helpers.py); y within max-rel 2e-2 / mean-rel
+2e-3. The full-size workloads are compared on every token and every pair."""
 
 import numpy as np
 import pytest
@@ -136,6 +138,29 @@ def test_ffn_tiny(dev, small_max):
     check_ffn(inp, p, y, dbg, label=f"tiny small_max={small_max}")
 
 
+@pytest.mark.parametrize("wl", [
+    dict(base="tiny"),
+    dict(base="tiny", T=700, H=1024, I=512, E=2, K=1, seed=56, weight_seed=56),    # 256-row items + remainders
+    dict(base="tiny", T=400, H=256, I=384, E=1, K=1, seed=52, weight_seed=52),     # few-K W2
+])
+def test_tilings_agree_bit_for_bit(dev, wl):
+    """The small-M tiles (weights on the MFMA's A side, 16 tokens per tile), the
+    128-row and the 256 x 256 large-M tiles all sum each dot product over
+    ascending 128-K steps with the same instruction, so y and the SwiGLU codes
+    are identical bit for bit whichever tiling the split sends an expert to."""
+    base = wl.pop("base")
+    inp = make_inputs(scaled(base, name="tilings", **wl) if wl else base).to(dev)
+    outs = []
+    for small_max in (0, 1, 10 ** 6):
+        p, (y, dbg) = run_path(inp, small_max=small_max)
+        rows = p.pair_rows.cpu().numpy()
+        order = rows[rows >= 0]
+        outs.append((u16(y), dbg["h_q"].cpu().numpy()[order], dbg["h_s"].cpu().numpy()[order]))
+    for o in outs[1:]:
+        for a, b in zip(outs[0], o):
+            assert np.array_equal(a, b)
+
+
 @pytest.mark.parametrize("T,H,I,E,K,seed,small_max", [
     (1, 128, 128, 1, 1, 41, 0),        # degenerate: one token, one expert
     (33, 384, 384, 5, 3, 42, 0),       # ragged: odd T, H and I not multiples of 256
@@ -181,6 +206,7 @@ def test_ffn_shapes(dev, T, H, I, E, K, seed, small_max):
     (33, 256, 256, 5, 3, 128, 52, 0),     # ragged token tile (33 of 128 rows)
     (130, 384, 128, 4, 2, 256, 53, 1),    # H = 3 * 128: the shared W2 tile's second half is masked
     (200, 1280, 384, 4, 2, 384, 54, 1),   # odd K-step count in the shared W2 (Is = 3 * 128)
+    (130, 384, 128, 4, 2, 512, 55, 1),    # Is = 512: the generic shared W2 tiles, H/128 odd (masked half)
 ])
 def test_ffn_shared_shapes(dev, T, H, I, E, K, Is, seed, small_max):
     """Routed experts plus the dense FP8 shared expert (128 x 128 block scales):
@@ -268,31 +294,30 @@ def test_ffn_decode7_full(dev, full_weights):
     check_ffn(inp, p, y, dbg, label="decode7 full")
 
 
-def test_ffn_decode256_sampled(dev, full_weights):
+@pytest.mark.timeout(600)
+def test_ffn_decode256_full(dev, full_weights):
+    """32 requests x 8 speculative positions at full size: every token and pair."""
     inp = _full_inputs("decode256", dev, full_weights)
     p, (y, dbg) = run_path(inp)
-    toks = np.random.default_rng(1).choice(inp.wl.T, 12, replace=False)
-    check_ffn(inp, p, y, dbg, tokens=toks, label="decode256 sampled")
-    assert torch.isfinite(y.float()).all()
+    check_plan(p, inp.topk_ids.cpu().numpy(), inp.wl.E)
+    check_ffn(inp, p, y, dbg, label="decode256 full")
 
 
-def test_ffn_prefill32k_sampled(dev, full_weights):
+@pytest.mark.timeout(900)
+def test_ffn_prefill32k_full(dev, full_weights):
+    """The 32K prefill chunk at full size: all 32,768 tokens and 262,144 pairs
+    (every 256-row and 128-row work item, every column block)."""
     inp = _full_inputs("prefill32k", dev, full_weights)
     p, (y, dbg) = run_path(inp)
-    # tokens routed to the hottest expert, to a median one, and random ones
-    counts = np.bincount(inp.topk_ids.cpu().numpy().ravel(), minlength=384)
-    hot = int(np.argmax(counts))
-    ids = inp.topk_ids.cpu().numpy()
-    toks = list(np.nonzero((ids == hot).any(1))[0][[0, -1]])
-    toks += list(np.random.default_rng(2).choice(inp.wl.T, 4, replace=False))
-    toks += [inp.wl.T - 1]
-    check_ffn(inp, p, y, dbg, tokens=toks, label="prefill32k sampled")
-    assert torch.isfinite(y.float()).all()
+    check_plan(p, inp.topk_ids.cpu().numpy(), inp.wl.E)
+    say("[prefill32k full] GPU done, running the oracle on every token")
+    check_ffn(inp, p, y, dbg, label="prefill32k full")
 
 
-def test_ffn_tp8rank32k_sampled(dev):
-    """One TP8 rank of the 32K prefill (routed I 384 slice + the FP8 shared expert),
-    sampled tokens: the hottest expert's first and last token, random ones, the last."""
+@pytest.mark.timeout(600)
+def test_ffn_tp8rank32k_full(dev):
+    """One TP8 rank of the 32K prefill (routed I 384 slice + the FP8 shared
+    expert): all tokens and pairs."""
     import time
     t = time.time()
     inp = make_inputs("tp8rank32k", weights=False).to(dev)
@@ -301,10 +326,5 @@ def test_ffn_tp8rank32k_sampled(dev):
     torch.cuda.synchronize()
     say(f"[tp8rank32k weights] generated in {time.time() - t:.1f}s")
     p, (y, dbg) = run_path(inp)
-    ids = inp.topk_ids.cpu().numpy()
-    hot = int(np.argmax(np.bincount(ids.ravel(), minlength=inp.wl.E)))
-    toks = list(np.nonzero((ids == hot).any(1))[0][[0, -1]])
-    toks += list(np.random.default_rng(5).choice(inp.wl.T, 4, replace=False))
-    toks += [inp.wl.T - 1]
-    check_ffn(inp, p, y, dbg, tokens=toks, label="tp8rank32k sampled")
-    assert torch.isfinite(y.float()).all()
+    check_plan(p, inp.topk_ids.cpu().numpy(), inp.wl.E)
+    check_ffn(inp, p, y, dbg, label="tp8rank32k full")
