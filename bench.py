@@ -6,11 +6,20 @@ requantization, W2 GEMM and the top-k combine (moe_ffn).
 
 The headline line is the 7-token decode verify (H 7168, 384 experts, I 3072,
 top-8, Zipf 1.0 routing): tokens/s, with the roofline of its dominant kernel
-(the W13 weight stream, HBM-bound). The same JSON line carries the 32K-token
-prefill chunk (Zipf 1.2) as "prefill32k", with the MFMA roofline of its W13
-GEMM, because the metric names both. Kernel durations come from HIP events the
-library records on the stream it launches on; the oracle's CPU time on a
-bounded sample is reported as cpu_baseline.
+(the W13 weight stream, HBM-bound). The same JSON line carries the 256-token
+decode step (32 requests x 8 positions) as "decode256" (HBM roofline), the
+32K-token prefill chunk (Zipf 1.2) as "prefill32k" (MFMA roofline of its W13
+GEMM) and one MoE-TP8 rank of it as "tp8rank32k" (MFMA and HBM bounds), because
+the metric names them. Kernel durations come from HIP events the library records
+on the stream it launches on; the oracle's CPU time on bounded samples is
+reported as cpu_baseline.
+
+Every workload is timed twice: back-to-back steps (the contract's timed region,
+``ms_per_step``), and steps each preceded by a 1 GiB read that evicts the
+256 MB last-level cache, timed one by one with events (``mall_flushed``), so the
+HBM figures cannot include last-level-cache hits from the previous step. The
+flush reads rather than writes: a written flush leaves up to 256 MB of dirty
+lines whose write-back would be charged to the next step.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-prefill] [--no-cpu]
 """
@@ -126,6 +135,22 @@ class Runner:
         ms = {k: float(np.mean([e.elapsed_ms(a, b) for e in diag])) for k, (a, b) in stages.items()}
         return (t1 - t0) * 1e3 / steps, focus_ms, ms
 
+    def run_flushed(self, steps: int, flush: torch.Tensor, focus=(moe.EV_QUANT_DONE, moe.EV_W13_DONE)):
+        """`steps` steps, each after a read of `flush` (1 GiB of clean lines that
+        evict the 256 MB last-level cache), outside the events that time the step
+        (plan + FFN) and the focus stage. Returns (mean ms per step, mean
+        focus-stage ms)."""
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+                moe.StageEvents(only=focus)) for _ in range(steps)]
+        for i, (a, b, st) in enumerate(evs):
+            flush.max()
+            a.record()
+            self.step(st)
+            b.record()
+        torch.cuda.synchronize()
+        return (float(np.mean([a.elapsed_time(b) for a, b, _ in evs])),
+                float(np.mean([st.elapsed_ms(*focus) for _, _, st in evs])))
+
 
 def cpu_baseline(name: str, weights_dev, tokens) -> dict:
     """The oracle, as it stands, on a bounded sample of the workload's tokens.
@@ -147,6 +172,84 @@ def cpu_baseline(name: str, weights_dev, tokens) -> dict:
                       f"{dt:.1f} s"}
 
 
+def decode_object(r: Runner, steps: int, warmup: int, flush: torch.Tensor) -> dict:
+    """A decode workload: tokens/s, the HBM roofline of its W13 stage (the weight
+    stream of every touched expert), the whole step's HBM rate, and the same with
+    the last-level cache flushed before each step."""
+    w = r.w
+    ms_step, w13_ms, stages = r.run(steps, warmup)
+    fl_step, fl_w13 = r.run_flushed(steps, flush)
+    eb = expert_bytes(w)
+    P = w.T * w.K
+    # W13 stage: every touched expert's W13 codes + scales once, the routed activation
+    # rows (codes + scales) and the SwiGLU outputs (codes + scales) of every pair
+    w13_bytes = r.distinct * eb["w13"] + w.T * (w.H + w.H // 128) + P * (w.I + w.I // 128)
+    # whole step: both weight sets of every touched expert, x in and y out (bf16)
+    step_bytes = r.distinct * (eb["w13"] + eb["w2"]) + w.T * w.H * 2 * 2
+    gbs = lambda b, ms: b / (ms * 1e-3) / 1e9
+    log(f"[bench] {w.name}: {ms_step:.4f} ms/step ({fl_step:.4f} flushed), w13 {w13_ms:.4f} ms "
+        f"({fl_w13:.4f} flushed), distinct experts {r.distinct}, stages {stages}")
+    return {
+        "value": w.T / (ms_step * 1e-3), "unit": "tokens/s", "ms_per_step": ms_step, "steps": steps,
+        "config": {"workload": w.name, "tokens": w.T, "hidden": w.H, "experts": w.E, "intermediate": w.I,
+                   "top_k": w.K, "routing": w.routing + f" s={w.zipf_s}", "distinct_experts": r.distinct},
+        "roofline": {"bound": "hbm", "kernel": "W13 stage: grouped GEMM + SwiGLU/requant (k_w13_small<8>"
+                                                + (" + large-M tiles" if P > 512 else "") + ")",
+                     "achieved": gbs(w13_bytes, w13_ms), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs(w13_bytes, w13_ms) / HBM_PEAK_GBS,
+                     "traffic": measured_traffic(w.name, "moe::k_w13_small<8>") if P <= 512 else None,
+                     "algorithmic_bytes_per_launch": w13_bytes, "avg_launch_ms": w13_ms},
+        "step_hbm_gbs": gbs(step_bytes, ms_step), "step_hbm_frac": gbs(step_bytes, ms_step) / HBM_PEAK_GBS,
+        "step_algorithmic_bytes": step_bytes,
+        "mall_flushed": {"ms_per_step": fl_step, "value": w.T / (fl_step * 1e-3), "w13_ms": fl_w13,
+                         "w13_hbm_frac": gbs(w13_bytes, fl_w13) / HBM_PEAK_GBS,
+                         "step_hbm_frac": gbs(step_bytes, fl_step) / HBM_PEAK_GBS},
+        "stage_ms_untimed_pass": stages,
+    }
+
+
+def prefill_object(r: Runner, steps: int, flush: torch.Tensor) -> dict:
+    """A prefill workload: tokens/s, the MFMA roofline of its W13 stage, the whole
+    step against both the MFMA and the HBM bound, and the cache-flushed times."""
+    w = r.w
+    ps, p13_ms, stages = r.run(steps, 1)
+    fl_step, fl_w13 = r.run_flushed(steps, flush)
+    P = w.T * w.K
+    f13 = 2.0 * P * (2 * w.I) * w.H
+    f2 = 2.0 * P * w.H * w.I
+    fs = (2.0 * w.T * (2 * w.Is) * w.H + 2.0 * w.T * w.H * w.Is) if w.Is else 0.0
+    flops = f13 + f2 + fs
+    eb = expert_bytes(w)
+    # algorithmic bytes of the step: every expert's weights once, the shared expert's
+    # FP8 weights + scales, x in and y out (bf16)
+    shared_bytes = (3 * w.Is * w.H + 3 * w.Is * w.H // (128 * 128)) if w.Is else 0
+    step_bytes = r.distinct * (eb["w13"] + eb["w2"]) + shared_bytes + w.T * w.H * 2 * 2
+    t13 = f13 / (p13_ms * 1e-3) / 1e12
+    tstep = flops / (ps * 1e-3) / 1e12
+    log(f"[bench] {w.name}: {ps:.3f} ms/step ({fl_step:.3f} flushed), w13 {p13_ms:.3f} ms, stages {stages}")
+    return {
+        "value": w.T / (ps * 1e-3), "unit": "tokens/s", "ms_per_step": ps, "steps": steps,
+        "config": {"workload": w.name, "tokens": w.T, "intermediate": w.I, "shared_intermediate": w.Is,
+                   "routing": f"zipf s={w.zipf_s}"},
+        "effective_tflops": tstep,
+        "mfma_frac_fp8_peak": tstep / MFMA_PEAK_FP8_TFLOPS,
+        "roofline": {"bound": "mfma",
+                     "kernel": "W13 stage: k_gemm_xl<true> (256-row items) + k_gemm_large<true> (128-row "
+                               "remainders) + SwiGLU/requant",
+                     "achieved": t13, "peak": MFMA_PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                     "frac": t13 / MFMA_PEAK_FP8_TFLOPS, "frac_of_fp4_peak": t13 / MFMA_PEAK_FP4_TFLOPS,
+                     "traffic": measured_traffic(w.name, ["moe::k_gemm_xl<true>", "moe::k_gemm_large<true>"]),
+                     "algorithmic_flops_per_launch": f13, "avg_launch_ms": p13_ms},
+        "step_bounds": {"algorithmic_flops": flops, "algorithmic_bytes": step_bytes,
+                        "mfma_frac": tstep / MFMA_PEAK_FP8_TFLOPS,
+                        "hbm_frac": step_bytes / (ps * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                        "ideal_ms": max(flops / (MFMA_PEAK_FP8_TFLOPS * 1e9), step_bytes / (HBM_PEAK_GBS * 1e6))},
+        "mall_flushed": {"ms_per_step": fl_step, "value": w.T / (fl_step * 1e-3), "w13_ms": fl_w13},
+        **({"shared_tflops": fs / (stages["shared"] * 1e-3) / 1e12} if w.Is else {}),
+        "stage_ms_untimed_pass": stages,
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -155,7 +258,7 @@ def main():
     ap.add_argument("--prefill-steps", type=int, default=5)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--only", choices=["decode7", "prefill32k", "tp8rank32k", "copy"], default=None,
+    ap.add_argument("--only", choices=["decode7", "decode256", "prefill32k", "tp8rank32k", "copy"], default=None,
                     help="run one workload only (for profiling); prints its own JSON object. 'copy' runs "
                          "a 1 GiB device-to-device copy, the known-size reference for HBM byte counters")
     args = ap.parse_args()
@@ -175,108 +278,61 @@ def main():
         return
     moe.lib()
     t = time.time()
-    # one 384-expert set, shared by both workloads, converted once to the kernel-native
-    # layout (a weight-load step, outside every timed region)
+    # one 384-expert set, shared by the full-size workloads, converted once to the
+    # kernel-native layout (a weight-load step, outside every timed region)
     W_rows = make_expert_weights(WORKLOADS["decode7"], dev)   # row-major codes (the oracle's input)
     W = moe.pack_weights(W_rows)
+    flush = torch.zeros(1 << 27, dtype=torch.int64, device=dev)    # 1 GiB, read to evict the cache
     torch.cuda.synchronize()
     log(f"[bench] weights generated and packed in {time.time() - t:.1f}s")
 
-    if args.only in ("prefill32k", "tp8rank32k"):
-        pre = Runner(args.only, dev, W if args.only == "prefill32k" else None)
-        ps, p13_ms, pms = pre.run(args.prefill_steps, args.warmup)
-        log(f"[bench] {args.only}: {ps:.3f} ms/step, w13 {p13_ms:.3f} ms, stages {pms}")
-        print(json.dumps({"workload": args.only, "ms_per_step": ps, "w13_ms": p13_ms, "stage_ms": pms}))
+    if args.only is not None:
+        r = Runner(args.only, dev, W if args.only != "tp8rank32k" else None)
+        if args.only.startswith("decode"):
+            obj = decode_object(r, args.steps, args.warmup, flush)
+        else:
+            obj = prefill_object(r, args.prefill_steps, flush)
+        print(json.dumps(obj))
         return
 
     # ---- decode verify, 7 tokens (headline)
-    dec = Runner("decode7", dev, W)
-    ms_step, w13_ms, ms = dec.run(args.steps, args.warmup)
-    w = dec.w
-    eb = expert_bytes(w)
-    # W13 stage: every touched expert's W13 codes + scales once, the routed activation
-    # rows (codes + scales) and the SwiGLU output (codes + scales) of every pair
-    P = w.T * w.K
-    w13_bytes = dec.distinct * eb["w13"] + w.T * (w.H + w.H // 128) + P * (w.I + w.I // 128)
-    w13_gbs = w13_bytes / (w13_ms * 1e-3) / 1e9
-    step_bytes = dec.distinct * (eb["w13"] + eb["w2"]) + w.T * w.H * 2 * 2
-    log(f"[bench] decode7: {ms_step:.3f} ms/step, w13 {w13_ms:.4f} ms, stages {ms}, distinct experts {dec.distinct}")
+    d7 = decode_object(Runner("decode7", dev, W), args.steps, args.warmup, flush)
+    w = WORKLOADS["decode7"]
     out = {
         "metric": METRIC,
-        "value": w.T / (ms_step * 1e-3),
+        "value": d7["value"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_step,
+        "ms_per_step": d7["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "fp8e4m3 x fp4e2m1 (E8M0 block scales), fp32 accumulate",
         "data": "synthetic (seeded: x N(0,1) bf16, Zipf routing, N(0,0.02) weights packed to MXFP4)",
-        "config": {"workload": "decode7", "tokens": w.T, "hidden": w.H, "experts": w.E, "intermediate": w.I,
-                   "top_k": w.K, "routing": f"zipf s={w.zipf_s}", "distinct_experts": dec.distinct},
-        "roofline": {"bound": "hbm", "kernel": "W13 grouped GEMM + SwiGLU/requant (k_w13_small<8>)",
-                     "achieved": w13_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": w13_gbs / HBM_PEAK_GBS,
-                     "traffic": measured_traffic("decode7", "moe::k_w13_small<8>"),
-                     "algorithmic_bytes_per_launch": w13_bytes, "avg_launch_ms": w13_ms},
-        "step_hbm_gbs": step_bytes / (ms_step * 1e-3) / 1e9,
-        "step_hbm_frac": step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
-        "stage_ms_untimed_pass": ms,
+        "config": d7["config"],
+        "roofline": d7["roofline"],
+        "step_hbm_gbs": d7["step_hbm_gbs"],
+        "step_hbm_frac": d7["step_hbm_frac"],
+        "mall_flushed": d7["mall_flushed"],
+        "stage_ms_untimed_pass": d7["stage_ms_untimed_pass"],
     }
+    # ---- high-concurrency decode step, 256 tokens
+    out["decode256"] = decode_object(Runner("decode256", dev, W), max(args.steps // 2, 5), args.warmup, flush)
 
-    # ---- prefill chunk, 32K tokens
-    if not args.no_prefill and args.only is None:
-        pre = Runner("prefill32k", dev, W)
-        ps, p13_ms, pms = pre.run(args.prefill_steps, 1)
-        pw = pre.w
-        Pp = pw.T * pw.K
-        f13 = 2.0 * Pp * (2 * pw.I) * pw.H
-        f2 = 2.0 * Pp * pw.H * pw.I
-        t13 = f13 / (p13_ms * 1e-3) / 1e12
-        out["prefill32k"] = {
-            "value": pw.T / (ps * 1e-3), "unit": "tokens/s", "ms_per_step": ps, "steps": args.prefill_steps,
-            "config": {"workload": "prefill32k", "tokens": pw.T, "routing": f"zipf s={pw.zipf_s}"},
-            "effective_tflops": (f13 + f2) / (ps * 1e-3) / 1e12,
-            "mfma_frac_fp8_peak": (f13 + f2) / (ps * 1e-3) / 1e12 / MFMA_PEAK_FP8_TFLOPS,
-            "roofline": {"bound": "mfma",
-                         "kernel": "W13 stage: k_gemm_xl<true> (256-row items) + k_gemm_large<true> (128-row "
-                                   "remainders) + SwiGLU/requant",
-                         "achieved": t13,
-                         "peak": MFMA_PEAK_FP8_TFLOPS, "unit": "TFLOP/s", "frac": t13 / MFMA_PEAK_FP8_TFLOPS,
-                         "frac_of_fp4_peak": t13 / MFMA_PEAK_FP4_TFLOPS,
-                         "traffic": measured_traffic("prefill32k", ["moe::k_gemm_xl<true>",
-                                                                    "moe::k_gemm_large<true>"]),
-                         "algorithmic_flops_per_launch": f13, "avg_launch_ms": p13_ms},
-            "stage_ms_untimed_pass": pms,
-        }
-        log(f"[bench] prefill32k: {ps:.3f} ms/step, w13 {p13_ms:.3f} ms, stages {pms}")
-        del pre
+    # ---- prefill chunk, 32K tokens, and one MoE-TP8 rank of it
+    if not args.no_prefill:
+        out["prefill32k"] = prefill_object(Runner("prefill32k", dev, W), args.prefill_steps, flush)
+        out["tp8rank32k"] = prefill_object(Runner("tp8rank32k", dev), args.prefill_steps, flush)
 
-    # ---- one MoE-TP8 rank of the 32K chunk: routed I 384 slice + FP8 shared expert
-    if not args.no_prefill and args.only is None:
-        tp = Runner("tp8rank32k", dev)
-        ts, t13_ms, tms = tp.run(args.prefill_steps, 1)
-        tw = tp.w
-        Pt = tw.T * tw.K
-        fr = 2.0 * Pt * (2 * tw.I) * tw.H + 2.0 * Pt * tw.H * tw.I
-        fs = 2.0 * tw.T * (2 * tw.Is) * tw.H + 2.0 * tw.T * tw.H * tw.Is
-        out["tp8rank32k"] = {
-            "value": tw.T / (ts * 1e-3), "unit": "tokens/s", "ms_per_step": ts, "steps": args.prefill_steps,
-            "config": {"workload": "tp8rank32k", "tokens": tw.T, "intermediate_per_rank": tw.I,
-                       "shared_intermediate": tw.Is, "routing": f"zipf s={tw.zipf_s}"},
-            "effective_tflops": (fr + fs) / (ts * 1e-3) / 1e12,
-            "mfma_frac_fp8_peak": (fr + fs) / (ts * 1e-3) / 1e12 / MFMA_PEAK_FP8_TFLOPS,
-            "shared_tflops": fs / (tms["shared"] * 1e-3) / 1e12,
-            "stage_ms_untimed_pass": tms,
-        }
-        log(f"[bench] tp8rank32k: {ts:.3f} ms/step, stages {tms}")
-        del tp
-
-    # ---- oracle on the host cores (bounded sample)
-    if not args.no_cpu and args.only is None:
+    # ---- oracle on the host cores (bounded samples)
+    if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline("decode7", W_rows, list(range(WORKLOADS["decode7"].T)))
         log(f"[bench] cpu_baseline {out['cpu_baseline']}")
+        if not args.no_prefill:
+            out["prefill32k"]["cpu_baseline"] = cpu_baseline("prefill32k", W_rows, list(range(32)))
+            log(f"[bench] prefill32k cpu_baseline {out['prefill32k']['cpu_baseline']}")
     print(json.dumps(out), flush=True)
 
 
