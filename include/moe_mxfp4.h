@@ -26,7 +26,9 @@
  *   - All tensor pointers are DEVICE pointers, 16-byte aligned, row-major unless
  *     stated otherwise (moe_ffn's expert weight codes are in the layout of
  *     moe_pack_weights); the caller allocates and owns every buffer. The library
- *     never allocates or frees memory and keeps no pointer past the call.
+ *     never allocates or frees memory and keeps no pointer past the call
+ *     (moe_ffn_static alone uses a static device array of the library's own in
+ *     place of a workspace; see there).
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *     Every call only enqueues work on it: no host synchronization, no host
  *     read of device data, so calls can be captured into a HIP graph.
@@ -52,7 +54,8 @@ enum {
   MOE_EINVAL = -1,        /* null pointer or dimension out of range */
   MOE_EUNSUPPORTED = -2,  /* shape outside what the kernels support (e.g. H % 128) */
   MOE_EWORKSPACE = -3,    /* workspace too small */
-  MOE_EHIP = -4           /* a HIP launch failed (hipGetLastError after enqueue) */
+  MOE_EHIP = -4,          /* a HIP launch failed (hipGetLastError after enqueue) */
+  MOE_ESCRATCH = -5       /* moe_ffn_static: the call needs more than MOE_FFN_STATIC_MAX_BYTES */
 };
 
 /* Problem dimensions.
@@ -163,6 +166,12 @@ size_t moe_ffn_workspace_bytes(const moe_dims* dims);
 /* The routed MoE FFN, y = sum_j w[t,j] * W2[e] . Q(silu(W1[e] . Q(x_t)) * (W3[e] . Q(x_t)))
  * (+ shared expert), e = topk_ids[t, j]; Q = FP8 E4M3 quantization with one
  * power-of-two scale per 128 elements; W1/W3 = W13 rows [0, I) / [I, 2I).
+ * "Pushing the Limits of Serving DeepSeek-V4-Pro": MXFP4 expert weights with FP8
+ * activations quantized online (section 2.2), separate W13 and W2 grouped GEMMs
+ * (section 3.3), SwiGLU fused with the quantization that writes W2's FP8 operand
+ * and scales (section 4.3), top-k reduction plus the shared-expert add (section
+ * 3.2); the route comes from moe_plan ("Optimization progress report",
+ * Optimization 14).
  *   x              [T, H] bf16
  *   topk_weights   [T, K] float32  routing weight of each pick, applied after W2
  *   expert_offsets, sorted_pairs, pair_rows, plan_ws   from moe_plan (same dims)
@@ -170,16 +179,40 @@ size_t moe_ffn_workspace_bytes(const moe_dims* dims);
  *   w13_s [E, 2I, H/32] E8M0 scales, row-major
  *   w2    [E, H, I/2]   MXFP4 codes in the layout of moe_pack_weights
  *   w2_s  [E, H, I/32]  E8M0 scales, row-major
- *   shared          optional dense FP8 shared expert (NULL or dims->Is == 0: none)
+ *   shared          optional dense FP8 shared expert (NULL or dims->Is == 0: none);
+ *                   with one, T * H must be below 2^30
  *   y     [T, H] bf16 out
  *   dbg             optional inspection outputs / stage events (NULL: none)
- *   ws, ws_bytes    workspace (>= moe_ffn_workspace_bytes)
+ *   ws, ws_bytes    workspace (>= moe_ffn_workspace_bytes), owned by the caller;
+ *                   nothing in it needs to be initialized
  * Errors: MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP. */
 int moe_ffn(const moe_dims* dims, const uint16_t* x, const float* topk_weights,
             const int32_t* expert_offsets, const int32_t* sorted_pairs, const int32_t* pair_rows,
             const void* plan_ws, const uint8_t* w13, const uint8_t* w13_s, const uint8_t* w2,
             const uint8_t* w2_s, const moe_shared* shared, uint16_t* y, const moe_debug* dbg,
             void* ws, size_t ws_bytes, void* stream);
+
+/* For callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc. moe_ffn with the same
+ * arguments and results, minus the workspace: the library uses a static device
+ * array of MOE_FFN_STATIC_MAX_BYTES instead, one per GPU, set up on the first
+ * call on each device and held until the process ends. The call itself allocates
+ * nothing (no hipMalloc, hipFree or allocating library routine).
+ *   Limit: moe_ffn_workspace_bytes(dims) must be at most MOE_FFN_STATIC_MAX_BYTES
+ *   (64 MiB: decode steps of up to about 256 tokens x top-8 at hidden 7168);
+ *   larger calls return MOE_ESCRATCH and enqueue nothing.
+ *   Every call on one GPU shares that GPU's array: calls that overlap on one GPU
+ *   (two streams, or two host threads) race and must be serialized by the caller.
+ *   The array keeps the last call's contents; nothing in it needs to start at
+ *   zero (every byte a call reads was written earlier in the same call).
+ * Errors: as moe_ffn, plus MOE_ESCRATCH; MOE_EHIP also if the array's device
+ * address cannot be looked up. */
+#define MOE_FFN_STATIC_MAX_BYTES ((size_t)64 << 20)
+int moe_ffn_static(const moe_dims* dims, const uint16_t* x, const float* topk_weights,
+                   const int32_t* expert_offsets, const int32_t* sorted_pairs, const int32_t* pair_rows,
+                   const void* plan_ws, const uint8_t* w13, const uint8_t* w13_s, const uint8_t* w2,
+                   const uint8_t* w2_s, const moe_shared* shared, uint16_t* y, const moe_debug* dbg,
+                   void* stream);
 
 /* Static, human-readable name of a status code. */
 const char* moe_status_string(int code);

@@ -9,6 +9,7 @@ call fails, an exception is raised.
     plan(topk_ids, E)                     -> Plan          (moe_plan)
     quant_act(x)                          -> (x_q, x_s)    (moe_quant_act)
     ffn(x, topk_weights, plan, weights)   -> y             (moe_ffn)
+    ffn(..., static=True)                 -> y             (moe_ffn_static: no workspace)
 """
 
 from __future__ import annotations
@@ -23,7 +24,9 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe_mxfp4.so")
 
-MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP = 0, -1, -2, -3, -4
+MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP, MOE_ESCRATCH = 0, -1, -2, -3, -4, -5
+#: workspace bytes moe_ffn_static can serve (MOE_FFN_STATIC_MAX_BYTES)
+FFN_STATIC_MAX_BYTES = 64 << 20
 EV_START, EV_QUANT_DONE, EV_W13_DONE, EV_W2_DONE, EV_SHARED_DONE, EV_END = range(6)
 NUM_EVENTS = 6
 
@@ -62,6 +65,8 @@ _SIGNATURES = {
     "moe_ffn_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(Dims)]),
     "moe_ffn": (ctypes.c_int, [ctypes.POINTER(Dims)] + [ctypes.c_void_p] * 10 + [ctypes.POINTER(Shared),
                 ctypes.c_void_p, ctypes.POINTER(Debug), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "moe_ffn_static": (ctypes.c_int, [ctypes.POINTER(Dims)] + [ctypes.c_void_p] * 10 + [ctypes.POINTER(Shared),
+                       ctypes.c_void_p, ctypes.POINTER(Debug), ctypes.c_void_p]),
     "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
 }
 
@@ -233,12 +238,14 @@ class StageEvents:
 
 def ffn(x: torch.Tensor, topk_weights: torch.Tensor, p: Plan, weights: dict, shared: Optional[dict] = None,
         debug: bool = False, ws: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None,
-        events=None):
+        events=None, static: bool = False):
     """moe_ffn on the current stream. weights: dict from pack_weights (w13 and w2 in
     the kernel-native layout, w13_s and w2_s row-major; uint8 cuda); shared:
     optional dict w13s, w13s_s, w2s, w2s_s.
     Returns y (bf16 [T, H]); with debug=True returns (y, dict of x_q, x_s, h_q, h_s,
-    sh_q, sh_s). ``events``: optional StageEvents recorded at the stage boundaries."""
+    sh_q, sh_s). ``events``: optional StageEvents recorded at the stage boundaries.
+    ``static``: call moe_ffn_static (the library's static scratch instead of a
+    workspace; ``ws`` must then be None)."""
     d = p.dims
     T, H, I, E, K, Is = d.T, d.H, d.I, d.E, d.K, d.Is
     dev = x.device
@@ -260,7 +267,9 @@ def ffn(x: torch.Tensor, topk_weights: torch.Tensor, p: Plan, weights: dict, sha
                     shared["w2s_s"].data_ptr())
     if y is None:
         y = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
-    if ws is None:
+    if static and ws is not None:
+        raise ValueError("moe_ffn_static takes no workspace")
+    if ws is None and not static:
         ws = torch.empty(ffn_workspace_bytes(d), dtype=torch.uint8, device=dev)
     dbg_t = None
     dbg = None
@@ -280,11 +289,14 @@ def ffn(x: torch.Tensor, topk_weights: torch.Tensor, p: Plan, weights: dict, sha
         if events is not None:
             ev_arr = events.array
             dbg.events = ctypes.cast(ev_arr, ctypes.POINTER(ctypes.c_void_p))
-    rc = lib().moe_ffn(ctypes.byref(d), _ptr(x), _ptr(topk_weights), _ptr(p.expert_offsets), _ptr(p.sorted_pairs),
-                       _ptr(p.pair_rows), _ptr(p.ws), _ptr(weights["w13"]), _ptr(weights["w13_s"]),
-                       _ptr(weights["w2"]), _ptr(weights["w2_s"]), ctypes.byref(sh) if sh is not None else None,
-                       _ptr(y), ctypes.byref(dbg) if dbg is not None else None, _ptr(ws), ws.numel(), _stream(dev))
-    _check(rc, "moe_ffn")
+    args = [ctypes.byref(d), _ptr(x), _ptr(topk_weights), _ptr(p.expert_offsets), _ptr(p.sorted_pairs),
+            _ptr(p.pair_rows), _ptr(p.ws), _ptr(weights["w13"]), _ptr(weights["w13_s"]), _ptr(weights["w2"]),
+            _ptr(weights["w2_s"]), ctypes.byref(sh) if sh is not None else None, _ptr(y),
+            ctypes.byref(dbg) if dbg is not None else None]
+    if static:
+        _check(lib().moe_ffn_static(*args, _stream(dev)), "moe_ffn_static")
+    else:
+        _check(lib().moe_ffn(*args, _ptr(ws), ws.numel(), _stream(dev)), "moe_ffn")
     if debug:
         return y, dbg_t
     return y

@@ -1,6 +1,8 @@
 // C ABI of the routed MoE FFN (declared in include/moe_mxfp4.h): argument checks,
 // workspace carving and the launch sequence. Nothing here allocates, synchronizes
 // or reads device memory, so every call is an enqueue on the caller's stream.
+#include <mutex>
+
 #include "host_internal.h"
 
 namespace moe {
@@ -122,24 +124,39 @@ int moe_pack_weights(const moe_dims* dims, const uint8_t* w13, uint8_t* w13_pack
   return MOE_OK;
 }
 
-int moe_ffn(const moe_dims* dims, const uint16_t* x, const float* topk_weights, const int32_t* expert_offsets,
-            const int32_t* sorted_pairs, const int32_t* pair_rows, const void* plan_ws, const uint8_t* w13,
-            const uint8_t* w13_s, const uint8_t* w2, const uint8_t* w2_s, const moe_shared* shared, uint16_t* y,
-            const moe_debug* dbg, void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace moe {
+namespace {
+
+// Argument checks of moe_ffn / moe_ffn_static that need no workspace.
+int ffn_args(const moe_dims* dims, const uint16_t* x, const float* topk_weights, const int32_t* expert_offsets,
+             const int32_t* sorted_pairs, const int32_t* pair_rows, const void* plan_ws, const uint8_t* w13,
+             const uint8_t* w13_s, const uint8_t* w2, const uint8_t* w2_s, const moe_shared* shared,
+             const uint16_t* y) {
   int rc = validate(dims);
   if (rc != MOE_OK) return rc;
   const moe_dims& d = *dims;
-  hipStream_t s = (hipStream_t)stream;
-  const bool use_shared = shared != nullptr && d.Is > 0;
   if (d.T == 0) return MOE_OK;
   if (!x || !topk_weights || !expert_offsets || !sorted_pairs || !pair_rows || !plan_ws || !w13 || !w13_s || !w2 ||
-      !w2_s || !y || !ws)
+      !w2_s || !y)
     return MOE_EINVAL;
+  const bool use_shared = shared != nullptr && d.Is > 0;
   if (use_shared && (!shared->w13s || !shared->w13s_s || !shared->w2s || !shared->w2s_s)) return MOE_EINVAL;
   if (use_shared && (!dense_path_supported(d) || (int64_t)d.T * d.H >= ((int64_t)1 << 30)))
     return MOE_EUNSUPPORTED;
+  return MOE_OK;
+}
+
+// The launch sequence of the FFN on a checked argument set and a workspace of at
+// least ffn_ws_layout(d) bytes.
+int ffn_enqueue(const moe_dims& d, const uint16_t* x, const float* topk_weights, const int32_t* expert_offsets,
+                const int32_t* sorted_pairs, const int32_t* pair_rows, const void* plan_ws, const uint8_t* w13,
+                const uint8_t* w13_s, const uint8_t* w2, const uint8_t* w2_s, const moe_shared* shared, uint16_t* y,
+                const moe_debug* dbg, void* ws, hipStream_t s) {
+  const bool use_shared = shared != nullptr && d.Is > 0;
   FfnWs fw;
-  if (ws_bytes < ffn_ws_layout(d, ws, &fw)) return MOE_EWORKSPACE;
+  ffn_ws_layout(d, ws, &fw);
   PlanWs pw;
   plan_ws_layout(d, const_cast<void*>(plan_ws), &pw);
   uint8_t* x_q = dbg && dbg->x_q ? dbg->x_q : fw.x_q;
@@ -238,6 +255,73 @@ int moe_ffn(const moe_dims* dims, const uint16_t* x, const float* topk_weights, 
   return MOE_OK;
 }
 
+// ---------------------------------------------------------------- static scratch
+// The workspace of moe_ffn_static: one array per GPU, loaded with the library's
+// code object and held until the process ends. Host code never passes the array's
+// name to a kernel (on the host it is only a stand-in for the device symbol); it
+// uses the address hipGetSymbolAddress returns for the current device, looked up
+// once per device on that device's first call.
+constexpr size_t kStaticScratchBytes = MOE_FFN_STATIC_MAX_BYTES;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// This device's address of `scratch` (nullptr and the HIP error on failure).
+void* scratch_ptr(hipError_t* err) {
+  int dev = -1;
+  *err = hipGetDevice(&dev);
+  if (*err != hipSuccess) return nullptr;
+  if (dev < 0 || dev >= kMaxDevices) {
+    *err = hipErrorInvalidDevice;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    *err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (*err != hipSuccess) return nullptr;
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+}  // namespace moe
+
+extern "C" {
+
+int moe_ffn(const moe_dims* dims, const uint16_t* x, const float* topk_weights, const int32_t* expert_offsets,
+            const int32_t* sorted_pairs, const int32_t* pair_rows, const void* plan_ws, const uint8_t* w13,
+            const uint8_t* w13_s, const uint8_t* w2, const uint8_t* w2_s, const moe_shared* shared, uint16_t* y,
+            const moe_debug* dbg, void* ws, size_t ws_bytes, void* stream) {
+  int rc = ffn_args(dims, x, topk_weights, expert_offsets, sorted_pairs, pair_rows, plan_ws, w13, w13_s, w2, w2_s,
+                    shared, y);
+  if (rc != MOE_OK || dims->T == 0) return rc;
+  if (!ws) return MOE_EINVAL;
+  if (ws_bytes < ffn_ws_layout(*dims, nullptr, nullptr)) return MOE_EWORKSPACE;
+  return ffn_enqueue(*dims, x, topk_weights, expert_offsets, sorted_pairs, pair_rows, plan_ws, w13, w13_s, w2, w2_s,
+                     shared, y, dbg, ws, (hipStream_t)stream);
+}
+
+int moe_ffn_static(const moe_dims* dims, const uint16_t* x, const float* topk_weights,
+                   const int32_t* expert_offsets, const int32_t* sorted_pairs, const int32_t* pair_rows,
+                   const void* plan_ws, const uint8_t* w13, const uint8_t* w13_s, const uint8_t* w2,
+                   const uint8_t* w2_s, const moe_shared* shared, uint16_t* y, const moe_debug* dbg, void* stream) {
+  int rc = ffn_args(dims, x, topk_weights, expert_offsets, sorted_pairs, pair_rows, plan_ws, w13, w13_s, w2, w2_s,
+                    shared, y);
+  if (rc != MOE_OK || dims->T == 0) return rc;
+  if (ffn_ws_layout(*dims, nullptr, nullptr) > kStaticScratchBytes) return MOE_ESCRATCH;
+  hipError_t err;
+  void* ws = scratch_ptr(&err);
+  if (!ws) return MOE_EHIP;
+  // every workspace byte the kernels read is written earlier in the same call, so
+  // nothing is cleared
+  return ffn_enqueue(*dims, x, topk_weights, expert_offsets, sorted_pairs, pair_rows, plan_ws, w13, w13_s, w2, w2_s,
+                     shared, y, dbg, ws, (hipStream_t)stream);
+}
+
 const char* moe_status_string(int code) {
   switch (code) {
     case MOE_OK: return "MOE_OK";
@@ -245,6 +329,7 @@ const char* moe_status_string(int code) {
     case MOE_EUNSUPPORTED: return "MOE_EUNSUPPORTED: shape outside what the kernels support";
     case MOE_EWORKSPACE: return "MOE_EWORKSPACE: workspace too small";
     case MOE_EHIP: return "MOE_EHIP: a HIP launch failed";
+    case MOE_ESCRATCH: return "MOE_ESCRATCH: the call needs more workspace than moe_ffn_static's static scratch holds";
     default: return "unknown moe status code";
   }
 }

@@ -90,9 +90,17 @@ def test_host_checks_reject_before_enqueue():
     assert L.moe_pack_weights(ctypes.byref(bad), fake, ctypes.c_void_p(0x2000), None, None, None) == \
         moe.MOE_EUNSUPPORTED
     assert L.moe_pack_weights(ctypes.byref(d), None, None, None, None, None) == moe.MOE_OK   # nothing to do
+    # moe_ffn_static: a call whose workspace exceeds the static scratch is refused on
+    # the host, before the scratch is looked up; null arguments as for moe_ffn
+    big = moe.make_dims(4096, 1024, 512, 6, 8)
+    assert moe.ffn_workspace_bytes(big) > moe.FFN_STATIC_MAX_BYTES
+    assert L.moe_ffn_static(ctypes.byref(big), *([fake] * 10), None, fake, None, None) == moe.MOE_ESCRATCH
+    assert L.moe_ffn_static(ctypes.byref(big), *([None] * 10), None, fake, None, None) == moe.MOE_EINVAL
+    assert "static scratch" in moe.status_string(moe.MOE_ESCRATCH)
     # T == 0 is a no-op for the FFN and the quantizer
     z = moe.make_dims(0, 256, 512, 8, 2)
     assert L.moe_ffn(ctypes.byref(z), *([None] * 10), None, None, None, None, 0, None) == moe.MOE_OK
+    assert L.moe_ffn_static(ctypes.byref(z), *([None] * 10), None, None, None, None) == moe.MOE_OK
     assert L.moe_quant_act(ctypes.byref(z), None, None, None, None) == moe.MOE_OK
 
 
