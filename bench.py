@@ -86,9 +86,9 @@ def measured_traffic(workload: str, kernels):
 class Runner:
     """Holds one workload resident on the GPU and runs steps of the hot path."""
 
-    def __init__(self, name: str, dev, weights=None):
+    def __init__(self, name: str, dev, weights=None, flags: int = 0):
         """weights: expert weights already converted with moe.pack_weights (None:
-        generate and convert this workload's own)."""
+        generate and convert this workload's own); flags: moe_dims flags."""
         self.w = WORKLOADS[name]
         w = self.w
         inp = make_inputs(name, weights=False).to(dev)
@@ -96,7 +96,8 @@ class Runner:
         inp.shared = make_shared_weights(w, dev) if w.Is else None
         self.inp = inp
         self.dev = dev
-        self.plan = moe.plan(inp.topk_ids, w.E, w.H, w.I, Is=w.Is)
+        self.flags = flags
+        self.plan = moe.plan(inp.topk_ids, w.E, w.H, w.I, Is=w.Is, flags=flags)
         d = self.plan.dims
         self.ws = torch.empty(moe.ffn_workspace_bytes(d), dtype=torch.uint8, device=dev)
         self.y = torch.empty((w.T, w.H), dtype=torch.bfloat16, device=dev)
@@ -105,7 +106,7 @@ class Runner:
 
     def step(self, events=None):
         w = self.w
-        moe.plan(self.inp.topk_ids, w.E, w.H, w.I, Is=w.Is, out=self.plan)
+        moe.plan(self.inp.topk_ids, w.E, w.H, w.I, Is=w.Is, out=self.plan, flags=self.flags)
         moe.ffn(self.inp.x, self.inp.topk_weights, self.plan, self.inp.weights, shared=self.inp.shared,
                 ws=self.ws, y=self.y, events=events)
 
@@ -172,37 +173,52 @@ def cpu_baseline(name: str, weights_dev, tokens) -> dict:
                       f"{dt:.1f} s"}
 
 
+CHAIN_MAX_PAIRS = 512   # up to this many pairs MOE_FLAG_DECODE_CHAIN runs W13, W2 and the combine as one launch
+
+
 def decode_object(r: Runner, steps: int, warmup: int, flush: torch.Tensor) -> dict:
-    """A decode workload: tokens/s, the HBM roofline of its W13 stage (the weight
-    stream of every touched expert), the whole step's HBM rate, and the same with
-    the last-level cache flushed before each step."""
+    """A decode workload: tokens/s, the HBM roofline of its dominant launch (the
+    weight stream of every touched expert), the whole step's HBM rate, and the same
+    with the last-level cache flushed before each step.
+
+    With MOE_FLAG_DECODE_CHAIN (up to CHAIN_MAX_PAIRS pairs) the dominant launch is
+    the persistent decode chain (W13 + SwiGLU/requant, W2 and the combine): its
+    algorithmic bytes are both weight sets of every touched expert, the activation
+    codes read and y written, and its time the span between the stage events around
+    it. Otherwise it is the W13 stage (W13 weights, activation codes, SwiGLU codes
+    written)."""
     w = r.w
-    ms_step, w13_ms, stages = r.run(steps, warmup)
-    fl_step, fl_w13 = r.run_flushed(steps, flush)
-    eb = expert_bytes(w)
     P = w.T * w.K
-    # W13 stage: every touched expert's W13 codes + scales once, the routed activation
-    # rows (codes + scales) and the SwiGLU outputs (codes + scales) of every pair
-    w13_bytes = r.distinct * eb["w13"] + w.T * (w.H + w.H // 128) + P * (w.I + w.I // 128)
+    chain = bool(r.flags & moe.FLAG_DECODE_CHAIN) and P <= CHAIN_MAX_PAIRS
+    ms_step, dom_ms, stages = r.run(steps, warmup)
+    fl_step, fl_dom = r.run_flushed(steps, flush)
+    eb = expert_bytes(w)
+    if chain:
+        dom_bytes = r.distinct * (eb["w13"] + eb["w2"]) + w.T * (w.H + w.H // 128) + w.T * w.H * 2
+        dom_name = "decode chain: W13 + SwiGLU/requant, W2, combine in one launch (k_decode_chain)"
+        traffic = measured_traffic(w.name, "moe::k_decode_chain")
+    else:
+        dom_bytes = r.distinct * eb["w13"] + w.T * (w.H + w.H // 128) + P * (w.I + w.I // 128)
+        dom_name = "W13 stage: grouped GEMM + SwiGLU/requant (k_w13_small<8>" + \
+            (" + large-M tiles)" if P > CHAIN_MAX_PAIRS else ")")
+        traffic = measured_traffic(w.name, "moe::k_w13_small<8>") if P <= CHAIN_MAX_PAIRS else None
     # whole step: both weight sets of every touched expert, x in and y out (bf16)
     step_bytes = r.distinct * (eb["w13"] + eb["w2"]) + w.T * w.H * 2 * 2
     gbs = lambda b, ms: b / (ms * 1e-3) / 1e9
-    log(f"[bench] {w.name}: {ms_step:.4f} ms/step ({fl_step:.4f} flushed), w13 {w13_ms:.4f} ms "
-        f"({fl_w13:.4f} flushed), distinct experts {r.distinct}, stages {stages}")
+    log(f"[bench] {w.name}: {ms_step:.4f} ms/step ({fl_step:.4f} flushed), dominant launch {dom_ms:.4f} ms "
+        f"({fl_dom:.4f} flushed), distinct experts {r.distinct}, stages {stages}")
     return {
         "value": w.T / (ms_step * 1e-3), "unit": "tokens/s", "ms_per_step": ms_step, "steps": steps,
         "config": {"workload": w.name, "tokens": w.T, "hidden": w.H, "experts": w.E, "intermediate": w.I,
                    "top_k": w.K, "routing": w.routing + f" s={w.zipf_s}", "distinct_experts": r.distinct},
-        "roofline": {"bound": "hbm", "kernel": "W13 stage: grouped GEMM + SwiGLU/requant (k_w13_small<8>"
-                                                + (" + large-M tiles" if P > 512 else "") + ")",
-                     "achieved": gbs(w13_bytes, w13_ms), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": gbs(w13_bytes, w13_ms) / HBM_PEAK_GBS,
-                     "traffic": measured_traffic(w.name, "moe::k_w13_small<8>") if P <= 512 else None,
-                     "algorithmic_bytes_per_launch": w13_bytes, "avg_launch_ms": w13_ms},
+        "roofline": {"bound": "hbm", "kernel": dom_name,
+                     "achieved": gbs(dom_bytes, dom_ms), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs(dom_bytes, dom_ms) / HBM_PEAK_GBS, "traffic": traffic,
+                     "algorithmic_bytes_per_launch": dom_bytes, "avg_launch_ms": dom_ms},
         "step_hbm_gbs": gbs(step_bytes, ms_step), "step_hbm_frac": gbs(step_bytes, ms_step) / HBM_PEAK_GBS,
         "step_algorithmic_bytes": step_bytes,
-        "mall_flushed": {"ms_per_step": fl_step, "value": w.T / (fl_step * 1e-3), "w13_ms": fl_w13,
-                         "w13_hbm_frac": gbs(w13_bytes, fl_w13) / HBM_PEAK_GBS,
+        "mall_flushed": {"ms_per_step": fl_step, "value": w.T / (fl_step * 1e-3), "dominant_ms": fl_dom,
+                         "dominant_hbm_frac": gbs(dom_bytes, fl_dom) / HBM_PEAK_GBS,
                          "step_hbm_frac": gbs(step_bytes, fl_step) / HBM_PEAK_GBS},
         "stage_ms_untimed_pass": stages,
     }
@@ -258,7 +274,8 @@ def main():
     ap.add_argument("--prefill-steps", type=int, default=5)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--only", choices=["decode7", "decode256", "prefill32k", "tp8rank32k", "copy"], default=None,
+    ap.add_argument("--only", choices=["decode7", "decode7_chain", "decode256", "prefill32k", "tp8rank32k", "copy"],
+                    default=None,
                     help="run one workload only (for profiling); prints its own JSON object. 'copy' runs "
                          "a 1 GiB device-to-device copy, the known-size reference for HBM byte counters")
     args = ap.parse_args()
@@ -287,7 +304,9 @@ def main():
     log(f"[bench] weights generated and packed in {time.time() - t:.1f}s")
 
     if args.only is not None:
-        r = Runner(args.only, dev, W if args.only != "tp8rank32k" else None)
+        chain = args.only == "decode7_chain"
+        r = Runner("decode7" if chain else args.only, dev, W if args.only != "tp8rank32k" else None,
+                   flags=moe.FLAG_DECODE_CHAIN if chain else 0)
         if args.only.startswith("decode"):
             obj = decode_object(r, args.steps, args.warmup, flush)
         else:
@@ -318,6 +337,9 @@ def main():
         "mall_flushed": d7["mall_flushed"],
         "stage_ms_untimed_pass": d7["stage_ms_untimed_pass"],
     }
+    # ---- the same verify as one persistent launch (MOE_FLAG_DECODE_CHAIN)
+    out["decode7_chain"] = decode_object(Runner("decode7", dev, W, flags=moe.FLAG_DECODE_CHAIN), args.steps,
+                                         args.warmup, flush)
     # ---- high-concurrency decode step, 256 tokens
     out["decode256"] = decode_object(Runner("decode256", dev, W), max(args.steps // 2, 5), args.warmup, flush)
 

@@ -39,7 +39,12 @@ class MoEError(RuntimeError):
 
 class Dims(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int32), ("H", ctypes.c_int32), ("I", ctypes.c_int32), ("E", ctypes.c_int32),
-                ("K", ctypes.c_int32), ("Is", ctypes.c_int32), ("small_max", ctypes.c_int32)]
+                ("K", ctypes.c_int32), ("Is", ctypes.c_int32), ("small_max", ctypes.c_int32),
+                ("flags", ctypes.c_int32)]
+
+
+#: moe_dims.flags bit: run decode shapes as one persistent W13 -> W2 -> combine launch
+FLAG_DECODE_CHAIN = 1
 
 
 class Shared(ctypes.Structure):
@@ -90,8 +95,8 @@ def status_string(code: int) -> str:
     return lib().moe_status_string(code).decode()
 
 
-def make_dims(T, H, I, E, K, Is=0, small_max=0) -> Dims:
-    return Dims(int(T), int(H), int(I), int(E), int(K), int(Is), int(small_max))
+def make_dims(T, H, I, E, K, Is=0, small_max=0, flags=0) -> Dims:
+    return Dims(int(T), int(H), int(I), int(E), int(K), int(Is), int(small_max), int(flags))
 
 
 def validate(d: Dims) -> int:
@@ -136,11 +141,11 @@ class Plan:
 
 
 def plan(topk_ids: torch.Tensor, E: int, H: int, I: int, small_max: int = 0, Is: int = 0,
-         out: Optional[Plan] = None) -> Plan:
-    """moe_plan on the current stream. topk_ids: cuda int32 [T, K]. H, I (and Is)
-    complete the dims that moe_ffn will use with this plan."""
+         out: Optional[Plan] = None, flags: int = 0) -> Plan:
+    """moe_plan on the current stream. topk_ids: cuda int32 [T, K]. H, I (and Is,
+    flags) complete the dims that moe_ffn will use with this plan."""
     T, K = topk_ids.shape
-    d = make_dims(T, H, I, E, K, Is, small_max)
+    d = make_dims(T, H, I, E, K, Is, small_max, flags)
     _check(validate(d), "moe_plan dims")
     _require(topk_ids, torch.int32, (T, K), "topk_ids")
     dev = topk_ids.device

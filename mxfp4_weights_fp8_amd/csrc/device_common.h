@@ -159,8 +159,11 @@ constexpr int kRsrcWord3 = 0x00020000;   // raw (untyped) buffer access on gfx9-
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcWord3);
 }
+// POLICY: the instruction's cache-policy bits (0 = default; 16 = sc1, device-scope
+// coherent, for data another workgroup of the same launch wrote with sc1 stores).
+template <int POLICY = 0>
 __device__ __forceinline__ v4i buf_load16(rsrc_t r, int voff, int soff) {
-  return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+  return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, POLICY));
 }
 // The same load with the nontemporal cache policy (the `nt` bit, cache-policy value
 // 2 on gfx950): for data read once per step, such as the decode weight streams
@@ -168,11 +171,13 @@ __device__ __forceinline__ v4i buf_load16(rsrc_t r, int voff, int soff) {
 __device__ __forceinline__ v4i buf_load16_nt(rsrc_t r, int voff, int soff) {
   return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 2));
 }
+template <int POLICY = 0>
 __device__ __forceinline__ int buf_load4(rsrc_t r, int voff, int soff) {
-  return (int)__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+  return (int)__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, POLICY);
 }
+template <int POLICY = 0>
 __device__ __forceinline__ int buf_load1(rsrc_t r, int voff, int soff) {
-  return (int)__builtin_amdgcn_raw_buffer_load_b8(r, voff, soff, 0);
+  return (int)__builtin_amdgcn_raw_buffer_load_b8(r, voff, soff, POLICY);
 }
 
 }  // namespace moe

@@ -22,12 +22,12 @@
 // W2 (down): a workgroup owns 64 * kW2Frags output columns; the epilogue writes
 // each routed pair's row to its token-major slot p = t*K + j for the top-k combine
 // (fp16 codes with one power-of-two scale per 32 columns).
-#include "device_common.h"
-#include "host_internal.h"
-#include "lds_copy.h"
+#include "small_unit.h"
 
 namespace moe {
 namespace {
+
+using namespace small;
 
 constexpr int kThreads = 256;
 // Work split (measured on decode7, 39 experts): W13 workgroups of 8 waves, each
@@ -38,151 +38,6 @@ constexpr int kThreads = 256;
 constexpr int kW13Waves = 8;
 constexpr int kW2Frags = 2;
 
-__device__ __forceinline__ v8i fp4_operand(const v4i w) {
-  v8i a;
-  a[0] = w[0]; a[1] = w[1]; a[2] = w[2]; a[3] = w[3];
-  a[4] = 0; a[5] = 0; a[6] = 0; a[7] = 0;
-  return a;
-}
-
-// Operands of one K step for NF weight fragments: per fragment 16 bytes of E2M1
-// codes and the dword holding the four E8M0 scales of this step's 32-blocks
-// (lane group q uses byte q); the token rows' E4M3 codes and their scale.
-template <int NF>
-struct Step {
-  v4i w[NF];
-  int ws[NF];
-  v8i x;
-  int xs;
-};
-
-// Where a wave's operands live: buffer resources (wave-uniform) and per-lane
-// byte offsets; step s adds s*1024 (codes), s*128 (activation codes), s (activation
-// scales) as wave-uniform offsets. The weight scales are in LDS: sl[f] is the
-// lane's row of fragment f there (KS dwords, dword s = the four 32-block scales
-// of step s).
-template <int NF>
-struct Stream {
-  rsrc_t w, x, xs;
-  int wo[NF];
-  const uint8_t* sl[NF];
-  int xo, xso;
-};
-
-template <int NF>
-__device__ __forceinline__ void load_step(Step<NF>& r, const Stream<NF>& p, int s) {
-#pragma unroll
-  for (int f = 0; f < NF; ++f) {
-    r.w[f] = buf_load16_nt(p.w, p.wo[f], s * 1024);
-    r.ws[f] = *reinterpret_cast<const int*>(p.sl[f] + s * 4);
-  }
-  const v4i lo = buf_load16(p.x, p.xo, s * 128), hi = buf_load16(p.x, p.xo, s * 128 + 64);
-  r.x[0] = lo[0]; r.x[1] = lo[1]; r.x[2] = lo[2]; r.x[3] = lo[3];
-  r.x[4] = hi[0]; r.x[5] = hi[1]; r.x[6] = hi[2]; r.x[7] = hi[3];
-  r.xs = buf_load1(p.xs, p.xso, s);
-}
-
-template <int NF>
-__device__ __forceinline__ void mma_step(const Step<NF>& r, int qshift, v4f* acc) {
-#pragma unroll
-  for (int f = 0; f < NF; ++f)
-    acc[f] = mfma_scale_16x16x128<kFmtE2M1, kFmtE4M3>(fp4_operand(r.w[f]), r.x, acc[f], r.ws[f] >> qshift, r.xs);
-}
-
-// LDS bytes of one staged run of `bytes`: whole 1 KB copy instructions.
-__host__ __device__ constexpr int staged_bytes(int bytes) { return (bytes + 1023) / 1024 * 1024; }
-
-// Copy one or two contiguous byte runs (src0, then src1 when non-null, `bytes`
-// each; wave-uniform arguments) into LDS at dst, run h at dst + h*staged_bytes,
-// with direct-to-LDS 16-byte-per-lane copies (1 KB per instruction; lanes past
-// the run read zeros into the run's padding). The wave alone reads what it copied;
-// stream_k waits for the copies (vmcnt 0) before its first LDS read, so no
-// barrier is needed.
-__device__ __forceinline__ void stage_scales(const uint8_t* src0, const uint8_t* src1, int bytes, uint8_t* dst,
-                                             int lane) {
-  for (int h = 0; h < (src1 ? 2 : 1); ++h) {
-    const v4i_s r = rsrc4(h ? src1 : src0, (uint32_t)bytes);
-    for (int off = 0; off < bytes; off += 1024)
-      dma16(r, lds_addr(dst + h * staged_bytes(bytes) + off), lane * 16 + off, 0);
-  }
-}
-
-// Codes of one K step (the scales travel separately, four steps at a time).
-template <int NF>
-struct Codes {
-  v4i w[NF];
-  v8i x;
-};
-
-template <int NF>
-__device__ __forceinline__ void load_codes(Codes<NF>& r, const Stream<NF>& p, int s) {
-#pragma unroll
-  for (int f = 0; f < NF; ++f) r.w[f] = buf_load16_nt(p.w, p.wo[f], s * 1024);   // read once per step
-  const v4i lo = buf_load16(p.x, p.xo, s * 128), hi = buf_load16(p.x, p.xo, s * 128 + 64);
-  r.x[0] = lo[0]; r.x[1] = lo[1]; r.x[2] = lo[2]; r.x[3] = lo[3];
-  r.x[4] = hi[0]; r.x[5] = hi[1]; r.x[6] = hi[2]; r.x[7] = hi[3];
-}
-
-// acc[f] += sum over KS steps of 128 K.
-// Main path (KS a multiple of 4): the codes of kQuad = 4 steps stay in flight in a
-// register ring. At the start of each 4-step chunk a lane reads the chunk's 16
-// bytes of E8M0 scales of its rows from LDS and packs its own K block's byte of
-// the four steps into one register; the MFMA's op_sel picks byte d for step d. The
-// activation scales come in one dword per chunk (byte d for step d). Prefetch step
-// indices are clamped on the wave-uniform offset, so the loop is branch-free; the
-// clamped reloads hit the cache and go unused.
-// Other K (short or not a multiple of 4 steps): a plain per-step loop.
-constexpr int kQuad = 4;
-
-// byte q of each of the four dwords of v, packed as bytes 0..3
-__device__ __forceinline__ int pack_lane_bytes(v4i v, int qshift) {
-  uint32_t r = 0;
-#pragma unroll
-  for (int d = 0; d < 4; ++d) r |= (((uint32_t)v[d] >> qshift) & 0xFFu) << (8 * d);
-  return (int)r;
-}
-
-template <int NF, int D>
-__device__ __forceinline__ void mma_quad_step(const Codes<NF>& r, const int* sc, int xsc, v4f* acc) {
-#pragma unroll
-  for (int f = 0; f < NF; ++f)
-    acc[f] = mfma_scale_16x16x128<kFmtE2M1, kFmtE4M3, D, D>(fp4_operand(r.w[f]), r.x, acc[f], sc[f], xsc);
-}
-
-template <int NF>
-__device__ __forceinline__ void stream_k(v4f* acc, const Stream<NF>& p, int KS, int qshift) {
-  if (KS % kQuad != 0) {
-    wait_vmcnt<0>();   // the weight-scale copies into LDS
-    for (int s = 0; s < KS; ++s) {
-      Step<NF> r;
-      load_step(r, p, s);
-      mma_step(r, qshift, acc);
-    }
-    return;
-  }
-  Codes<NF> buf[kQuad];
-  int sc[NF];
-#pragma unroll
-  for (int d = 0; d < kQuad; ++d) load_codes(buf[d], p, d);
-  int xsc = buf_load4(p.xs, p.xso, 0);
-  wait_vmcnt<0>();   // the weight-scale copies into LDS (and the first codes)
-  for (int s0 = 0; s0 < KS; s0 += kQuad) {
-#pragma unroll
-    for (int f = 0; f < NF; ++f) sc[f] = pack_lane_bytes(*reinterpret_cast<const v4i*>(p.sl[f] + s0 * 4), qshift);
-    const int nxt = min(s0 + kQuad, KS - kQuad);
-    const int xscn = buf_load4(p.xs, p.xso, nxt);
-    mma_quad_step<NF, 0>(buf[0], sc, xsc, acc);
-    load_codes(buf[0], p, min(s0 + kQuad + 0, KS - 1));
-    mma_quad_step<NF, 1>(buf[1], sc, xsc, acc);
-    load_codes(buf[1], p, min(s0 + kQuad + 1, KS - 1));
-    mma_quad_step<NF, 2>(buf[2], sc, xsc, acc);
-    load_codes(buf[2], p, min(s0 + kQuad + 2, KS - 1));
-    mma_quad_step<NF, 3>(buf[3], sc, xsc, acc);
-    load_codes(buf[3], p, min(s0 + kQuad + 3, KS - 1));
-    xsc = xscn;
-  }
-}
-
 template <int WAVES>
 __global__ __launch_bounds__(WAVES * 64) void k_w13_small(
     const SmallLists lists,
@@ -190,88 +45,13 @@ __global__ __launch_bounds__(WAVES * 64) void k_w13_small(
     const uint8_t* __restrict__ x_q, const uint8_t* __restrict__ x_s, const uint8_t* __restrict__ w13,
     const uint8_t* __restrict__ w13_s, uint8_t* __restrict__ h_q, uint8_t* __restrict__ h_s, int H, int I,
     int K) {
-  constexpr int NF = 256 / (16 * WAVES);    // weight fragments per wave: NF/2 gate + NF/2 up
-  constexpr int HC = 128 / WAVES;            // h columns per wave
-  __shared__ float red[WAVES][16];
+  __shared__ float red[WAVES * 16];
   extern __shared__ __attribute__((aligned(16))) uint8_t sS[];   // [256 weight rows][H/32] E8M0
   const int l = blockIdx.y >= lists.cap0;
   const int item = blockIdx.y - (l ? lists.cap0 : 0);
   if (item >= lists.n_items[l][0]) return;
-  const int2 it = lists.items[l][item];
-  const int item_rows = lists.rows[l];
-  const int e = it.x;
-  const int e_begin = offsets[e], e_end = offsets[e + 1];
-  const int nb = blockIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63, q = lane >> 4, c = lane & 15;
-  const int KS = H / 128;
-  const int64_t wrow = H / 2, srow = H / 32;
-
-  // 8-bit activation operand of a K step: bytes [16q, 16q+16) and [64+16q, 64+16q+16)
-  Stream<NF> p;
-  p.w = make_rsrc(w13 + (int64_t)e * 2 * I * wrow, (uint32_t)(2 * I * wrow));
-  p.x = make_rsrc(x_q, 0xFFFFFFFFu);
-  p.xs = make_rsrc(x_s, 0xFFFFFFFFu);
-  // Weight scales of the wave's 64 rows (gate rows nb*128 + wave*32 + [0, 32) and
-  // the matching up rows) into LDS rows wave*64 .. +63: two contiguous runs of
-  // 32 * srow bytes, copied in full 1 KB instructions (each cache line once; read
-  // per 4-step chunk straight from memory, a row's scale lines were refetched).
-  const int run = staged_bytes(HC * (int)srow);
-  stage_scales(w13_s + ((int64_t)e * 2 * I + nb * 128 + wave * HC) * srow,
-               w13_s + ((int64_t)e * 2 * I + I + nb * 128 + wave * HC) * srow, HC * (int)srow,
-               sS + wave * 2 * run, lane);
-#pragma unroll
-  for (int f = 0; f < NF; ++f) {
-    const int up = f >= NF / 2, fi = f % (NF / 2);
-    const int n0 = (up ? I : 0) + nb * 128 + wave * HC + fi * 16;   // first row of the fragment
-    p.wo[f] = n0 * (int)wrow + lane * 16;
-    p.sl[f] = sS + wave * 2 * run + up * run + (fi * 16 + c) * srow;
-  }
-
-  for (int m0 = it.y; m0 < it.y + item_rows && e_begin + m0 < e_end; m0 += kSmallRows) {
-    const int row0 = e_begin + m0;
-    const int mcount = min(kSmallRows, e_end - row0);
-    const bool has = c < mcount;
-    // an absent token column repeats the first row (valid data, result unused)
-    const int tok = sorted_pairs[row0 + (has ? c : 0)] / K;
-    p.xo = tok * H + q * 16;
-    p.xso = tok * KS;
-
-    v4f acc[NF];
-#pragma unroll
-    for (int f = 0; f < NF; ++f) acc[f] = v4f{0.f, 0.f, 0.f, 0.f};
-    stream_k<NF>(acc, p, KS, 8 * q);
-
-    // SwiGLU + FP8 requantization: lane (c, q) holds h columns 4q..4q+3 of each
-    // 16-column fragment pair, for routed row c.
-    float h[NF / 2][4];
-    float amax = 0.f;
-#pragma unroll
-    for (int g = 0; g < NF / 2; ++g)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        h[g][j] = silu_mul(acc[g][j], acc[g + NF / 2][j]);
-        amax = fmaxf(amax, fabsf(h[g][j]));
-      }
-    amax = fmaxf(amax, __shfl_xor(amax, 16));
-    amax = fmaxf(amax, __shfl_xor(amax, 32));
-    if (q == 0) red[wave][c] = amax;
-    __syncthreads();
-    amax = red[0][c];
-#pragma unroll
-    for (int w = 1; w < WAVES; ++w) amax = fmaxf(amax, red[w][c]);
-    __syncthreads();
-    const int ex = e8m0_exponent(amax);
-    const float inv = exp2_neg(ex);
-    if (has) {
-      uint8_t* dst = h_q + (int64_t)(row0 + c) * I + nb * 128 + wave * HC + q * 4;
-#pragma unroll
-      for (int g = 0; g < NF / 2; ++g) {
-        *reinterpret_cast<uint32_t*>(dst + g * 16) = e4m3_pack4(h[g][0] * inv, h[g][1] * inv, h[g][2] * inv, h[g][3] * inv);
-      }
-      if (wave == 0 && q == 0) h_s[(int64_t)(row0 + c) * (I / 128) + nb] = (uint8_t)(ex + 127);
-    }
-  }
+  w13_small_unit<WAVES>(lists.items[l][item], lists.rows[l], blockIdx.x, offsets, sorted_pairs, x_q, x_s, w13,
+                        w13_s, h_q, h_s, H, I, K, sS, red);
 }
 
 template <int NF>
@@ -280,66 +60,14 @@ __global__ __launch_bounds__(kThreads) void k_w2_small(
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_pairs,
     const uint8_t* __restrict__ h_q, const uint8_t* __restrict__ h_s, const uint8_t* __restrict__ w2,
     const uint8_t* __restrict__ w2_s, uint16_t* __restrict__ o, uint8_t* __restrict__ os, int H, int I) {
-  static_assert(NF == 2, "a wave's 16 * NF columns form one 32-column scale block of the per-pair output");
   extern __shared__ __attribute__((aligned(16))) uint8_t sS[];   // [256 weight rows][I/32] E8M0
   const int l = blockIdx.y >= lists.cap0;
   const int item = blockIdx.y - (l ? lists.cap0 : 0);
   if (item >= lists.n_items[l][0]) return;
-  const int item_rows = lists.rows[l];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63, q = lane >> 4, c = lane & 15;
   const int n_wave = blockIdx.x * 64 * NF + wave * 16 * NF;
-  if (n_wave >= H) return;
-  const int2 it = lists.items[l][item];
-  const int e = it.x;
-  const int e_begin = offsets[e], e_end = offsets[e + 1];
-  const int KS = I / 128;
-  const int64_t wrow = I / 2, srow = I / 32;
-
-  Stream<NF> p;
-  p.w = make_rsrc(w2 + (int64_t)e * H * wrow, (uint32_t)(H * wrow));
-  p.x = make_rsrc(h_q, 0xFFFFFFFFu);
-  p.xs = make_rsrc(h_s, 0xFFFFFFFFu);
-  // weight scales of the wave's 16*NF rows (one contiguous run) into LDS
-  const int run = staged_bytes(16 * NF * (int)srow);
-  stage_scales(w2_s + ((int64_t)e * H + n_wave) * srow, nullptr, 16 * NF * (int)srow, sS + wave * run, lane);
-#pragma unroll
-  for (int f = 0; f < NF; ++f) {
-    p.wo[f] = (n_wave + f * 16) * (int)wrow + lane * 16;
-    p.sl[f] = sS + wave * run + (f * 16 + c) * srow;
-  }
-
-  for (int m0 = it.y; m0 < it.y + item_rows && e_begin + m0 < e_end; m0 += kSmallRows) {
-    const int row0 = e_begin + m0;
-    const int mcount = min(kSmallRows, e_end - row0);
-    const bool has = c < mcount;
-    const int hrow = row0 + (has ? c : 0);
-    p.xo = hrow * I + q * 16;
-    p.xso = hrow * KS;
-
-    v4f acc[NF];
-#pragma unroll
-    for (int f = 0; f < NF; ++f) acc[f] = v4f{0.f, 0.f, 0.f, 0.f};
-    stream_k<NF>(acc, p, KS, 8 * q);
-    // fp16 codes + one scale per 32 columns (the wave's two fragments)
-    float m = 0.f;
-#pragma unroll
-    for (int f = 0; f < NF; ++f)
-#pragma unroll
-      for (int k = 0; k < 4; ++k) m = fmaxf(m, fabsf(acc[f][k]));
-    m = fmaxf(m, __shfl_xor(m, 16));
-    m = fmaxf(m, __shfl_xor(m, 32));
-    const int ex = o_exponent(m);
-    const float inv = exp2_neg(ex);
-    if (has) {
-      const int64_t slot = sorted_pairs[row0 + c];
-      uint16_t* dst = o + slot * H + n_wave + q * 4;
-#pragma unroll
-      for (int f = 0; f < NF; ++f)
-        *reinterpret_cast<uint2*>(dst + f * 16) = f16_pack4(acc[f][0] * inv, acc[f][1] * inv, acc[f][2] * inv, acc[f][3] * inv);
-      if (q == 0) os[slot * (H / 32) + n_wave / 32] = (uint8_t)(ex + 127);
-    }
-  }
+  w2_small_wave<NF>(lists.items[l][item], lists.rows[l], n_wave, offsets, sorted_pairs, h_q, h_s, w2, w2_s, o, os,
+                    H, I, sS + wave * staged_bytes(16 * NF * (I / 32)));
 }
 
 }  // namespace

@@ -76,6 +76,7 @@ struct FfnWs {
   uint8_t* sos;   // [T, H/32] their scales
   uint16_t* x_hat;      // [T, H] bf16 quantized activations (shared expert only)
   uint16_t* w13s_bf16;  // [2Is, H] bf16 shared gate/up weights, block scales folded in
+  int32_t* sync;        // [chain_sync_words] counters of the decode chain, zeroed by the quantizer
 };
 size_t ffn_ws_layout(const moe_dims& d, void* base, FfnWs* out);
 
@@ -87,8 +88,10 @@ hipError_t launch_plan(const moe_dims& d, const int32_t* ids, int32_t* offsets, 
 // == 0, K % 128 == 0).
 hipError_t launch_pack_weights(const uint8_t* w, uint8_t* out, int64_t rows, int K, hipStream_t s);
 // x_hat (optional): the quantized values E4M3(code) * scale as bf16 [T, H].
+// zero / n_zero (optional): int32 words set to zero by the launch (counters that a
+// later kernel of the same call needs at zero).
 hipError_t launch_quant_act(const uint16_t* x, uint8_t* x_q, uint8_t* x_s, int T, int H, hipStream_t s,
-                            uint16_t* x_hat = nullptr);
+                            uint16_t* x_hat = nullptr, int32_t* zero = nullptr, int n_zero = 0);
 // Small-M kernels walk up to two work lists in one launch: workgroup row y <
 // cap0 takes item y of list 0, the rest item y - cap0 of list 1; an item covers
 // rows[l] routed rows in 16-row tiles (counts live on the device).
@@ -151,6 +154,16 @@ hipError_t launch_shared13_bf16(const moe_dims& d, const uint16_t* x_hat, const 
                                 uint16_t* w13s_bf16, uint8_t* sh_q, uint8_t* sh_s, hipStream_t s);
 hipError_t launch_shared2(const moe_dims& d, const uint8_t* sh_q, const uint8_t* sh_s, const uint8_t* w2s,
                           const uint8_t* w2s_s, uint16_t* so, uint8_t* sos, hipStream_t s);
+// The persistent decode chain (W13 + SwiGLU/requant, W2 and the combine in one
+// launch, per-expert and per-column-block counters in `sync`, which must be zero):
+// used when every item can be walked in 16-row tiles, T*K <= kFoldPairs.
+size_t chain_sync_words(const moe_dims& d);
+hipError_t launch_decode_chain(const moe_dims& d, const PlanWs& pw, const int32_t* offsets,
+                               const int32_t* sorted_pairs, const int32_t* pair_rows, const uint8_t* x_q,
+                               const uint8_t* x_s, const uint8_t* w13, const uint8_t* w13_s, uint8_t* h_q,
+                               uint8_t* h_s, const uint8_t* w2, const uint8_t* w2_s, uint16_t* o, uint8_t* os,
+                               const float* topk_weights, const uint16_t* so, const uint8_t* sos, uint16_t* y,
+                               int32_t* sync, hipStream_t s);
 hipError_t launch_combine(const uint16_t* o, const uint8_t* os, const float* topk_weights, const int32_t* pair_rows,
                           const uint16_t* so, const uint8_t* sos,
                           uint16_t* y, int T, int H, int K, hipStream_t s);

@@ -27,6 +27,7 @@ size_t ffn_ws_layout(const moe_dims& d, void* base, FfnWs* out) {
   const size_t o_sos = take(Is ? (size_t)(T * H / 32) : 0);
   const size_t o_xhat = take(Is ? sizeof(uint16_t) * (size_t)(T * H) : 0);
   const size_t o_w13s = take(Is ? sizeof(uint16_t) * (size_t)(2 * Is * H) : 0);
+  const size_t o_sync = take(sizeof(int32_t) * chain_sync_words(d));
   if (out) {
     char* b = static_cast<char*>(base);
     out->x_q = reinterpret_cast<uint8_t*>(b + o_xq);
@@ -41,6 +42,7 @@ size_t ffn_ws_layout(const moe_dims& d, void* base, FfnWs* out) {
     out->sos = reinterpret_cast<uint8_t*>(b + o_sos);
     out->x_hat = reinterpret_cast<uint16_t*>(b + o_xhat);
     out->w13s_bf16 = reinterpret_cast<uint16_t*>(b + o_w13s);
+    out->sync = reinterpret_cast<int32_t*>(b + o_sync);
   }
   return off;
 }
@@ -50,7 +52,7 @@ namespace {
 int validate(const moe_dims* d) {
   if (!d) return MOE_EINVAL;
   if (d->T < 0 || d->H <= 0 || d->I <= 0 || d->E < 1 || d->E > kMaxExperts || d->K < 1 || d->K > kMaxTopK ||
-      d->Is < 0 || d->small_max < 0)
+      d->Is < 0 || d->small_max < 0 || (d->flags & ~MOE_FLAG_DECODE_CHAIN) != 0)
     return MOE_EINVAL;
   if (d->H % 128 || d->I % 128 || d->Is % 128) return MOE_EUNSUPPORTED;
   if ((int64_t)d->T * d->K > (int64_t)1 << 30) return MOE_EUNSUPPORTED;
@@ -164,10 +166,36 @@ int ffn_enqueue(const moe_dims& d, const uint16_t* x, const float* topk_weights,
   uint8_t* h_q = dbg && dbg->h_q ? dbg->h_q : fw.h_q;
   uint8_t* h_s = dbg && dbg->h_s ? dbg->h_s : fw.h_s;
 
+  const int64_t P = (int64_t)d.T * d.K;
+  // Decode shapes on request (every item walkable in 16-row tiles): one persistent
+  // launch runs W13, W2 and the combine, with the shared expert ahead of it
+  const bool chain = (d.flags & MOE_FLAG_DECODE_CHAIN) && P <= kFoldPairs;
   record(dbg, MOE_EV_START, s);
-  hipError_t err = launch_quant_act(x, x_q, x_s, d.T, d.H, s, use_shared ? fw.x_hat : nullptr);
+  hipError_t err = launch_quant_act(x, x_q, x_s, d.T, d.H, s, use_shared ? fw.x_hat : nullptr,
+                                    chain ? fw.sync : nullptr, chain ? (int)chain_sync_words(d) : 0);
   if (err != hipSuccess) return MOE_EHIP;
   record(dbg, MOE_EV_QUANT_DONE, s);
+  if (chain) {
+    if (use_shared) {
+      uint8_t* sh_q = dbg && dbg->sh_q ? dbg->sh_q : fw.sh_q;
+      uint8_t* sh_s = dbg && dbg->sh_s ? dbg->sh_s : fw.sh_s;
+      err = launch_shared13_bf16(d, fw.x_hat, shared->w13s, shared->w13s_s, fw.w13s_bf16, sh_q, sh_s, s);
+      if (err != hipSuccess) return MOE_EHIP;
+      err = shared2_fewk_supported(d)
+                ? launch_shared2_fewk(d, sh_q, sh_s, shared->w2s, shared->w2s_s, fw.so, fw.sos, s)
+                : launch_shared2(d, sh_q, sh_s, shared->w2s, shared->w2s_s, fw.so, fw.sos, s);
+      if (err != hipSuccess) return MOE_EHIP;
+    }
+    record(dbg, MOE_EV_SHARED_DONE, s);
+    err = launch_decode_chain(d, pw, expert_offsets, sorted_pairs, pair_rows, x_q, x_s, w13, w13_s, h_q, h_s, w2,
+                              w2_s, fw.o, fw.os, topk_weights, use_shared ? fw.so : nullptr,
+                              use_shared ? fw.sos : nullptr, y, fw.sync, s);
+    if (err != hipSuccess) return MOE_EHIP;
+    record(dbg, MOE_EV_W13_DONE, s);
+    record(dbg, MOE_EV_W2_DONE, s);
+    record(dbg, MOE_EV_END, s);
+    return MOE_OK;
+  }
 
   // Work lists: 16-row items (small experts), 256-row items and 128-row remainders
   // (large experts). A 256-row item needs an expert with more than 128 pairs and a
@@ -176,7 +204,6 @@ int ffn_enqueue(const moe_dims& d, const uint16_t* x, const float* topk_weights,
   // the small-M launch (one launch less; a 128-row item is then walked as 16-row
   // tiles).
   const bool large = large_path_supported(d);
-  const int64_t P = (int64_t)d.T * d.K;
   const bool any_xl = P > kXlRows / 2, any_l = P > small_max_of(d);
   const bool fold = any_l && (P <= kFoldPairs || !large);
   SmallLists sl = small_lists(pw.small_items, pw.hdr + 0, pw.small_cap, kSmallRows);

@@ -11,6 +11,7 @@ import torch
 
 import mxfp4_weights_fp8_amd as moe
 from oracle.compare import h_code_mismatch, y_metrics
+from oracle.formats import bf16_to_f64
 from oracle.envelope import routed_swiglu_envelope, shared_swiglu_envelope
 from oracle.moe import ffn_ref, plan_ref
 
@@ -38,10 +39,10 @@ def u16(t: torch.Tensor) -> np.ndarray:
     return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
 
 
-def run_path(inp, small_max=0, debug=True):
+def run_path(inp, small_max=0, debug=True, flags=0):
     """plan + ffn on the GPU for MoEInputs already on the device."""
     w = inp.wl
-    p = moe.plan(inp.topk_ids, w.E, w.H, w.I, small_max=small_max, Is=w.Is if inp.shared else 0)
+    p = moe.plan(inp.topk_ids, w.E, w.H, w.I, small_max=small_max, Is=w.Is if inp.shared else 0, flags=flags)
     packed = moe.pack_weights(inp.weights)
     out = moe.ffn(inp.x, inp.topk_weights, p, packed, shared=inp.shared, debug=debug)
     del packed
@@ -163,6 +164,16 @@ def check_ffn(inp, p, y, dbg, tokens=None, label="", ref=None):
         m.update({"sh_" + k: v for k, v in shm.items()})
     say(f"[parity {label}] {m}")
     assert m["finite"], m
+    if m["max_rel"] > MAX_REL:
+        yv = bf16_to_f64(yb)
+        err = np.abs(yv - ref["y"]).max(axis=-1) / np.abs(ref["y"]).max()
+        worst = np.argsort(-err)[:8]
+        rows = []
+        for i in worst:
+            bad_cols = np.nonzero(np.abs(yv[i] - ref["y"][i]) > MAX_REL * np.abs(ref["y"]).max())[0]
+            rows.append((int(sel[i]), float(err[i]), int(bad_cols.size), bad_cols[:8].tolist(),
+                         inp.topk_ids[int(sel[i])].tolist()))
+        say(f"[parity {label}] worst rows (token, rel err, bad columns, first columns, experts): {rows}")
     assert m["max_rel"] <= MAX_REL, m
     assert m["mean_rel"] <= MEAN_REL, m
     check_codes(m, "h_")

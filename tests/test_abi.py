@@ -51,6 +51,11 @@ def test_validate(dims, code):
     assert moe.validate(moe.make_dims(*dims)) == code
 
 
+def test_validate_flags():
+    assert moe.validate(moe.make_dims(4, 256, 512, 8, 2, flags=moe.FLAG_DECODE_CHAIN)) == moe.MOE_OK
+    assert moe.validate(moe.make_dims(4, 256, 512, 8, 2, flags=2)) == moe.MOE_EINVAL
+
+
 def test_validate_null_and_shared():
     assert moe.lib().moe_validate(None) == moe.MOE_EINVAL
     assert moe.validate(moe.make_dims(4, 256, 512, 8, 2, Is=100)) == moe.MOE_EUNSUPPORTED

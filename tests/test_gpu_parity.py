@@ -254,6 +254,74 @@ def test_ffn_invalid_ids(dev):
     check_ffn(inp, p, y, dbg, label="tiny with dropped ids")
 
 
+@pytest.mark.parametrize("name,shared,flags", [("decode256", False, 0), ("decode7", False, 0),
+                                                ("decode7", False, moe.FLAG_DECODE_CHAIN),
+                                                ("tp8small", True, moe.FLAG_DECODE_CHAIN)])
+def test_ffn_bitwise_repeatable_whatever_the_workspace_holds(dev, full_weights, name, shared, flags):
+    """Identical inputs give bitwise identical outputs, and nothing in the workspace
+    needs initializing: the FFN runs four times with its workspace pre-filled with
+    different byte patterns and y is compared bit for bit. decode256 and decode7 on
+    the separate kernels, decode7 on the persistent chain, and the chain with the
+    shared expert."""
+    if shared:
+        wl = scaled("tiny", T=40, H=1024, I=512, E=6, K=4, Is=256, seed=81, weight_seed=81, name="rep_shared")
+        inp = make_inputs(wl).to(dev)
+        W = moe.pack_weights(inp.weights)
+    else:
+        inp = _full_inputs(name, dev, full_weights)
+        W = moe.pack_weights(full_weights)
+    w = inp.wl
+    p = moe.plan(inp.topk_ids, w.E, w.H, w.I, Is=w.Is if shared else 0, flags=flags)
+    ws = torch.empty(moe.ffn_workspace_bytes(p.dims), dtype=torch.uint8, device=dev)
+    ys = []
+    for fill in (0x00, 0xFF, 0x55, 0x7B):
+        ws.fill_(fill)
+        ys.append(u16(moe.ffn(inp.x, inp.topk_weights, p, W, shared=inp.shared if shared else None, ws=ws)))
+    for y in ys[1:]:
+        assert np.array_equal(y, ys[0])
+    del W
+
+
+@pytest.mark.parametrize("wl", [
+    dict(base="tiny"),
+    dict(base="tiny", T=40, H=1024, I=512, E=6, K=4, Is=256, seed=82, weight_seed=82),   # + shared expert
+    dict(base="tiny", T=300, H=512, I=512, E=1, K=1, seed=83, weight_seed=83),           # 256-row + 128-row items
+    dict(base="tiny", T=130, H=384, I=1152, E=3, K=2, seed=84, weight_seed=84),          # H/256 odd, I 9 x 128
+    dict(base="tiny", T=3, H=16384, I=256, E=4, K=2, seed=85, weight_seed=85),           # H at the small-M limit
+])
+def test_decode_chain_matches_separate_launches(dev, wl):
+    """MOE_FLAG_DECODE_CHAIN (one persistent launch of W13, W2 and the combine,
+    synchronized by per-expert and per-column-block counters) gives bitwise the
+    separate launches' y and SwiGLU codes, also with dropped picks and with every
+    pick dropped."""
+    base = wl.pop("base")
+    wl = scaled(base, name="chain", **wl) if wl else WORKLOADS[base]
+    inp = make_inputs(wl).to(dev)
+    for drop in (None, "some", "all"):
+        if drop == "some":
+            inp.topk_ids = inp.topk_ids.clone()
+            inp.topk_ids[::3, 0] = -1
+        elif drop == "all":
+            inp.topk_ids = torch.full_like(inp.topk_ids, wl.E + 5)
+        outs = []
+        for flags in (0, moe.FLAG_DECODE_CHAIN):
+            p, (y, dbg) = run_path(inp, flags=flags)
+            rows = p.pair_rows.cpu().numpy()
+            order = np.sort(rows[rows >= 0])
+            keys = ("h_q", "h_s") + (("sh_q", "sh_s") if inp.shared is not None else ())
+            outs.append([u16(y)] + [dbg[k].cpu().numpy()[order] if k[0] == "h" else dbg[k].cpu().numpy()
+                                    for k in keys])
+        for a, b in zip(*outs):
+            assert np.array_equal(a, b), drop
+
+
+def test_decode_chain_decode7_parity(dev, full_weights):
+    """The 7-token verify through the persistent chain, every token against the oracle."""
+    inp = _full_inputs("decode7", dev, full_weights)
+    p, (y, dbg) = run_path(inp, flags=moe.FLAG_DECODE_CHAIN)
+    check_ffn(inp, p, y, dbg, label="decode7 chain")
+
+
 def test_ffn_deterministic_and_token_permutation(dev):
     inp = make_inputs(scaled("tiny", T=200, E=16, K=4, name="perm")).to(dev)
     _, (y1, _) = run_path(inp)
