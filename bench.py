@@ -10,7 +10,8 @@ top-8, Zipf 1.0 routing): tokens/s, with the roofline of its dominant kernel
 decode step (32 requests x 8 positions) as "decode256" (HBM roofline), the
 32K-token prefill chunk (Zipf 1.2) as "prefill32k" (MFMA roofline of its W13
 GEMM) and one MoE-TP8 rank of it as "tp8rank32k" (MFMA and HBM bounds), because
-the metric names them. Kernel durations come from HIP events the library records
+the metric names them; "decode7_a16" and "decode256_a16" time the two decode
+steps with bf16 activations (the MXFP4A16 variant, MOE_FLAG_A16). Kernel durations come from HIP events the library records
 on the stream it launches on; the oracle's CPU time on bounded samples is
 reported as cpu_baseline.
 
@@ -186,10 +187,12 @@ def decode_object(r: Runner, steps: int, warmup: int, flush: torch.Tensor) -> di
     algorithmic bytes are both weight sets of every touched expert, the activation
     codes read and y written, and its time the span between the stage events around
     it. Otherwise it is the W13 stage (W13 weights, activation codes, SwiGLU codes
-    written)."""
+    written); with MOE_FLAG_A16 (bf16 activations) the activations read and the
+    SwiGLU rows written are bf16, 2 bytes per element and no scales."""
     w = r.w
     P = w.T * w.K
-    chain = bool(r.flags & moe.FLAG_DECODE_CHAIN) and P <= CHAIN_MAX_PAIRS
+    a16 = bool(r.flags & moe.FLAG_A16)
+    chain = bool(r.flags & moe.FLAG_DECODE_CHAIN) and P <= CHAIN_MAX_PAIRS and not a16
     ms_step, dom_ms, stages = r.run(steps, warmup)
     fl_step, fl_dom = r.run_flushed(steps, flush)
     eb = expert_bytes(w)
@@ -197,6 +200,10 @@ def decode_object(r: Runner, steps: int, warmup: int, flush: torch.Tensor) -> di
         dom_bytes = r.distinct * (eb["w13"] + eb["w2"]) + w.T * (w.H + w.H // 128) + w.T * w.H * 2
         dom_name = "decode chain: W13 + SwiGLU/requant, W2, combine in one launch (k_decode_chain)"
         traffic = measured_traffic(w.name, "moe::k_decode_chain")
+    elif a16:
+        dom_bytes = r.distinct * eb["w13"] + w.T * w.H * 2 + P * w.I * 2
+        dom_name = "W13 stage, bf16 activations: grouped GEMM + SwiGLU (k_w13_a16)"
+        traffic = measured_traffic(w.name + "_a16", "moe::k_w13_a16")
     else:
         dom_bytes = r.distinct * eb["w13"] + w.T * (w.H + w.H // 128) + P * (w.I + w.I // 128)
         dom_name = "W13 stage: grouped GEMM + SwiGLU/requant (k_w13_small<8>" + \
@@ -210,7 +217,8 @@ def decode_object(r: Runner, steps: int, warmup: int, flush: torch.Tensor) -> di
     return {
         "value": w.T / (ms_step * 1e-3), "unit": "tokens/s", "ms_per_step": ms_step, "steps": steps,
         "config": {"workload": w.name, "tokens": w.T, "hidden": w.H, "experts": w.E, "intermediate": w.I,
-                   "top_k": w.K, "routing": w.routing + f" s={w.zipf_s}", "distinct_experts": r.distinct},
+                   "top_k": w.K, "routing": w.routing + f" s={w.zipf_s}", "distinct_experts": r.distinct,
+                   **({"activations": "bf16 (MXFP4A16)"} if a16 else {})},
         "roofline": {"bound": "hbm", "kernel": dom_name,
                      "achieved": gbs(dom_bytes, dom_ms), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs(dom_bytes, dom_ms) / HBM_PEAK_GBS, "traffic": traffic,
@@ -274,7 +282,8 @@ def main():
     ap.add_argument("--prefill-steps", type=int, default=5)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--only", choices=["decode7", "decode7_chain", "decode256", "prefill32k", "tp8rank32k", "copy"],
+    ap.add_argument("--only", choices=["decode7", "decode7_chain", "decode7_a16", "decode256", "decode256_a16",
+                                       "prefill32k", "tp8rank32k", "copy"],
                     default=None,
                     help="run one workload only (for profiling); prints its own JSON object. 'copy' runs "
                          "a 1 GiB device-to-device copy, the known-size reference for HBM byte counters")
@@ -305,8 +314,10 @@ def main():
 
     if args.only is not None:
         chain = args.only == "decode7_chain"
-        r = Runner("decode7" if chain else args.only, dev, W if args.only != "tp8rank32k" else None,
-                   flags=moe.FLAG_DECODE_CHAIN if chain else 0)
+        a16 = args.only.endswith("_a16")
+        name = args.only.split("_")[0] if (chain or a16) else args.only
+        r = Runner(name, dev, W if args.only != "tp8rank32k" else None,
+                   flags=moe.FLAG_DECODE_CHAIN if chain else (moe.FLAG_A16 if a16 else 0))
         if args.only.startswith("decode"):
             obj = decode_object(r, args.steps, args.warmup, flush)
         else:
@@ -342,6 +353,10 @@ def main():
                                          args.warmup, flush)
     # ---- high-concurrency decode step, 256 tokens
     out["decode256"] = decode_object(Runner("decode256", dev, W), max(args.steps // 2, 5), args.warmup, flush)
+    # ---- the same decode steps with bf16 activations (MXFP4A16, MOE_FLAG_A16)
+    out["decode7_a16"] = decode_object(Runner("decode7", dev, W, flags=moe.FLAG_A16), args.steps, args.warmup, flush)
+    out["decode256_a16"] = decode_object(Runner("decode256", dev, W, flags=moe.FLAG_A16), max(args.steps // 2, 5),
+                                         args.warmup, flush)
 
     # ---- prefill chunk, 32K tokens, and one MoE-TP8 rank of it
     if not args.no_prefill:

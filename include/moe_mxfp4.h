@@ -69,7 +69,7 @@ enum {
  *   small_max  experts with at most this many routed pairs use the small-M
  *      (decode) tiling, larger ones the large-M (prefill) tiling; 0 selects the
  *      library default (16). moe_plan and moe_ffn must see the same value.
- *   flags  0 or MOE_FLAG_DECODE_CHAIN. */
+ *   flags  0, or MOE_FLAG_DECODE_CHAIN and / or MOE_FLAG_A16 (below). */
 typedef struct moe_dims {
   int32_t T, H, I, E, K, Is;
   int32_t small_max;
@@ -85,6 +85,18 @@ typedef struct moe_dims {
  * 0.232 ms with separate launches, so it is off by default. Ignored above 512
  * pairs. */
 #define MOE_FLAG_DECODE_CHAIN 1
+
+/* MXFP4 weights x bf16 activations ("MXFP4A16", the variant beside MXFP4AFP8 in
+ * "Pushing the Limits of Serving DeepSeek-V4-Pro", Appendix D.2): moe_ffn does not
+ * quantize x; gate/up = W13 . x with the MXFP4 weights dequantized exactly to bf16,
+ * h = bf16(silu(gate) * up) (round to nearest even) is W2's operand, y as usual.
+ * The same plan, weight layout and combine; no shared expert (MOE_EUNSUPPORTED);
+ * T*H and T*K*I below 2^30. Every item is walked in 16-row tiles (the decode
+ * tiling): HBM-bound and efficient at decode shapes, correct but slow for prefill.
+ * The workspace holds bf16 SwiGLU rows; moe_debug.h_q then receives them as bf16
+ * [P, I] (2 bytes per element) and x_q, x_s, h_s are not written.
+ * MOE_FLAG_DECODE_CHAIN is ignored with it. */
+#define MOE_FLAG_A16 2
 
 /* Dense shared expert ("Pushing the Limits of Serving DeepSeek-V4-Pro", section
  * 3.2: its output is added to the top-k reduction with weight 1). FP8 E4M3 weights

@@ -45,6 +45,8 @@ class Dims(ctypes.Structure):
 
 #: moe_dims.flags bit: run decode shapes as one persistent W13 -> W2 -> combine launch
 FLAG_DECODE_CHAIN = 1
+#: moe_dims.flags bit: bf16 activations (MXFP4A16): x not quantized, bf16 SwiGLU rows
+FLAG_A16 = 2
 
 
 class Shared(ctypes.Structure):
@@ -248,7 +250,8 @@ def ffn(x: torch.Tensor, topk_weights: torch.Tensor, p: Plan, weights: dict, sha
     the kernel-native layout, w13_s and w2_s row-major; uint8 cuda); shared:
     optional dict w13s, w13s_s, w2s, w2s_s.
     Returns y (bf16 [T, H]); with debug=True returns (y, dict of x_q, x_s, h_q, h_s,
-    sh_q, sh_s). ``events``: optional StageEvents recorded at the stage boundaries.
+    sh_q, sh_s); with FLAG_A16 in the plan's flags, h_q holds the bf16 SwiGLU rows
+    (int16 [P, I]) and x_q, x_s, h_s are left as allocated. ``events``: optional StageEvents recorded at the stage boundaries.
     ``static``: call moe_ffn_static (the library's static scratch instead of a
     workspace; ``ws`` must then be None)."""
     d = p.dims
@@ -285,7 +288,8 @@ def ffn(x: torch.Tensor, topk_weights: torch.Tensor, p: Plan, weights: dict, sha
             P = T * K
             dbg_t = {"x_q": torch.empty((T, H), dtype=torch.uint8, device=dev),
                      "x_s": torch.empty((T, H // 128), dtype=torch.uint8, device=dev),
-                     "h_q": torch.zeros((max(P, 1), I), dtype=torch.uint8, device=dev),
+                     "h_q": torch.zeros((max(P, 1), I), dtype=torch.int16 if d.flags & FLAG_A16 else torch.uint8,
+                                        device=dev),
                      "h_s": torch.zeros((max(P, 1), I // 128), dtype=torch.uint8, device=dev),
                      "sh_q": torch.zeros((T, max(Is, 128)), dtype=torch.uint8, device=dev),
                      "sh_s": torch.zeros((T, max(Is, 128) // 128), dtype=torch.uint8, device=dev)}

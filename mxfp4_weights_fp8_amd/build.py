@@ -17,7 +17,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmoe_mxfp4.so")
 SOURCES = ["moe_api.hip", "plan.hip", "quant.hip", "pack.hip", "gemm_small.hip", "gemm_large.hip", "gemm_xl.hip",
-           "gemm_fewk.hip", "gemm_dense.hip", "gemm_chain.hip", "combine.hip"]
+           "gemm_fewk.hip", "gemm_dense.hip", "gemm_chain.hip", "gemm_a16.hip", "combine.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 

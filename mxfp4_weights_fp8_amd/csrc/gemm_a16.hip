@@ -1,0 +1,261 @@
+// MXFP4 weights x bf16 activations ("MXFP4A16", the variant beside MXFP4AFP8 in
+// "Pushing the Limits of Serving DeepSeek-V4-Pro", Appendix D.2, accuracy table):
+// the activations are not quantized, the SwiGLU output stays bf16 as W2's operand,
+// and the expert weights keep their MXFP4 codes and E8M0 scales.
+//
+// The block-scaled MFMA takes 8-, 6- and 4-bit operands only, so each E2M1 code is
+// expanded with its 32-element block's scale into bf16 in registers (exact: an
+// E2M1 value has at most 2 significant bits and the scale is a power of two, inside
+// bf16's range for scales 2^-127 .. 2^125) by gfx950's scaled FP4-to-bf16 conversion,
+// and multiplied on v_mfma_f32_16x16x32_bf16 with fp32 accumulation.
+//
+// Same work split as the FP8 small-M kernels (gemm_small.hip): the weights take the
+// MFMA's 16-row A side, the routed tokens its 16-column B side, 16 routed rows per
+// tile, weight codes streamed from the kernel-native layout (lane (c, q) of a
+// fragment holds row c, K 32q .. 32q+31 of the 128-K step), their scales staged in
+// LDS per wave. One 128-K step is four bf16 MFMAs; in MFMA u, lane (c, q) supplies K
+// 32q + 8u .. +7 for both operands (the instruction sums over K, so any assignment
+// of K to its slots that the two operands share gives the same dot product), so the
+// lane's weights come from its own 16 code bytes and its activations are 64
+// consecutive bytes of the token row. Every item list of the plan is walked in
+// 16-row tiles: efficient for decode (HBM-bound weight streams), correct for any
+// shape.
+#include "small_unit.h"
+
+namespace moe {
+namespace {
+
+using namespace small;
+
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+constexpr int kW13Waves = 8;     // W13: 8 waves, one gate + one up fragment each (128 h columns)
+constexpr int kW2Waves = 4;      // W2: 4 waves of two fragments (128 output columns)
+constexpr int kQ = 4;            // K steps of codes in flight per wave
+
+// E8M0 scale byte -> 2^(scale - 127) as a float (byte 0 is the fp32 subnormal 2^-127).
+__device__ __forceinline__ float e8m0_float(uint32_t scale) {
+  return scale ? __uint_as_float(scale << 23) : __uint_as_float(0x00400000u);
+}
+
+// 8 codes (one 32-bit word, low nibble = lower K) times the block scale -> 8 bf16 (4
+// words, element 2i in the low half of word i), with gfx950's conversion of two
+// FP4 codes with an fp32 scale (v_cvt_scalef32_pk_bf16_fp4, byte i of the word).
+__device__ __forceinline__ v4i e2m1x8_bf16(uint32_t w, float scale) {
+  v4i r;
+  r[0] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0));
+  r[1] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1));
+  r[2] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2));
+  r[3] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3));
+  return r;
+}
+
+__device__ __forceinline__ v4f mfma_bf16(v4i a, v4i b, v4f c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a), __builtin_bit_cast(v8bf, b), c, 0, 0, 0);
+}
+
+// Operands of one K step: NF fragments' codes, the token column's 32 bf16.
+template <int NF>
+struct Step16 {
+  v4i w[NF];
+  v4i x[4];
+};
+
+// Where a wave's operands live: weight codes (resource + per-fragment lane offsets,
+// step s at +1024 s), the token rows (resource + lane offset, step s at +256 s), the
+// weight scales in LDS (sl[f]: the lane's row of fragment f, K/32 bytes).
+template <int NF>
+struct Stream16 {
+  rsrc_t w, x;
+  int wo[NF];
+  int xo;
+  const uint8_t* sl[NF];
+};
+
+template <int NF>
+__device__ __forceinline__ void load16(Step16<NF>& r, const Stream16<NF>& p, int s) {
+#pragma unroll
+  for (int f = 0; f < NF; ++f) r.w[f] = buf_load16_nt(p.w, p.wo[f], s * 1024);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) r.x[u] = buf_load16(p.x, p.xo, s * 256 + 16 * u);
+}
+
+// One K step: sc[f] is the scale (as a float) of fragment f's lane's block.
+template <int NF>
+__device__ __forceinline__ void mma16(const Step16<NF>& r, const float* sc, v4f* acc) {
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int f = 0; f < NF; ++f) acc[f] = mfma_bf16(e2m1x8_bf16((uint32_t)r.w[f][u], sc[f]), r.x[u], acc[f]);
+}
+
+// acc[f] += sum over KS steps of 128 K. Four steps of codes in flight in a register
+// ring (prefetch indices clamped, so the loop is branch-free; KS a multiple of 4),
+// else one step at a time. The weight-scale copies into LDS are waited for first.
+template <int NF>
+__device__ __forceinline__ void stream16(v4f* acc, const Stream16<NF>& p, int KS, int q) {
+  float sc[NF];
+  if (KS % kQ != 0) {
+    wait_vmcnt<0>();
+    for (int s = 0; s < KS; ++s) {
+      Step16<NF> r;
+      load16(r, p, s);
+#pragma unroll
+      for (int f = 0; f < NF; ++f) sc[f] = e8m0_float(p.sl[f][4 * s + q]);
+      mma16(r, sc, acc);
+    }
+    return;
+  }
+  Step16<NF> buf[kQ];
+#pragma unroll
+  for (int d = 0; d < kQ; ++d) load16(buf[d], p, d);
+  wait_vmcnt<0>();
+  for (int s0 = 0; s0 < KS; s0 += kQ) {
+#pragma unroll
+    for (int d = 0; d < kQ; ++d) {
+#pragma unroll
+      for (int f = 0; f < NF; ++f) sc[f] = e8m0_float(p.sl[f][4 * (s0 + d) + q]);
+      mma16(buf[d], sc, acc);
+      load16(buf[d], p, min(s0 + kQ + d, KS - 1));
+    }
+  }
+}
+
+// W13 unit: 128 h columns (nb) of one item, 8 waves x (one gate + one up fragment).
+__global__ __launch_bounds__(kW13Waves * 64) void k_w13_a16(
+    const SmallLists lists, const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_pairs,
+    const uint16_t* __restrict__ x, const uint8_t* __restrict__ w13, const uint8_t* __restrict__ w13_s,
+    uint16_t* __restrict__ h, int H, int I, int K) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t sS[];   // per wave: 2 runs of 16 rows x H/32
+  const int l = blockIdx.y >= lists.cap0;
+  const int item = blockIdx.y - (l ? lists.cap0 : 0);
+  if (item >= lists.n_items[l][0]) return;
+  const int2 it = lists.items[l][item];
+  const int item_rows = lists.rows[l];
+  const int e = it.x;
+  const int e_begin = offsets[e], e_end = offsets[e + 1];
+  const int nb = blockIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, q = lane >> 4, c = lane & 15;
+  const int KS = H / 128;
+  const int64_t wrow = H / 2, srow = H / 32;
+
+  Stream16<2> p;
+  p.w = make_rsrc(w13 + (int64_t)e * 2 * I * wrow, (uint32_t)(2 * I * wrow));
+  p.x = make_rsrc(x, 0xFFFFFFFFu);
+  const int n_gate = nb * 128 + wave * 16;   // first gate row of the wave; up row I + n_gate
+  const int run = staged_bytes(16 * (int)srow);
+  stage_scales(w13_s + ((int64_t)e * 2 * I + n_gate) * srow, w13_s + ((int64_t)e * 2 * I + I + n_gate) * srow,
+               16 * (int)srow, sS + wave * 2 * run, lane);
+  p.wo[0] = n_gate * (int)wrow + lane * 16;
+  p.wo[1] = (I + n_gate) * (int)wrow + lane * 16;
+  p.sl[0] = sS + wave * 2 * run + c * srow;
+  p.sl[1] = sS + wave * 2 * run + run + c * srow;
+
+  for (int m0 = it.y; m0 < it.y + item_rows && e_begin + m0 < e_end; m0 += kSmallRows) {
+    const int row0 = e_begin + m0;
+    const int mcount = min(kSmallRows, e_end - row0);
+    const bool has = c < mcount;
+    const int tok = sorted_pairs[row0 + (has ? c : 0)] / K;   // an absent column repeats the first row
+    p.xo = (tok * H + 32 * q) * 2;
+    v4f acc[2] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};
+    stream16<2>(acc, p, KS, q);
+    // lane (c, q): h columns n_gate + 4q .. +3 of routed row c, as bf16
+    if (has) {
+      uint16_t* dst = h + (int64_t)(row0 + c) * I + n_gate + 4 * q;
+      const uint32_t lo = (uint32_t)bf16_rne(silu_mul(acc[0][0], acc[1][0])) |
+                          ((uint32_t)bf16_rne(silu_mul(acc[0][1], acc[1][1])) << 16);
+      const uint32_t hi = (uint32_t)bf16_rne(silu_mul(acc[0][2], acc[1][2])) |
+                          ((uint32_t)bf16_rne(silu_mul(acc[0][3], acc[1][3])) << 16);
+      *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
+    }
+  }
+}
+
+// W2 unit: 128 output columns of one item, 4 waves x two fragments; per-pair rows as
+// fp16 codes with one power-of-two scale per 32 columns (the wave's two fragments).
+__global__ __launch_bounds__(kW2Waves * 64) void k_w2_a16(
+    const SmallLists lists, const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_pairs,
+    const uint16_t* __restrict__ h, const uint8_t* __restrict__ w2, const uint8_t* __restrict__ w2_s,
+    uint16_t* __restrict__ o, uint8_t* __restrict__ os, int H, int I) {
+  constexpr int NF = 2;
+  extern __shared__ __attribute__((aligned(16))) uint8_t sS[];   // per wave: 32 rows x I/32
+  const int l = blockIdx.y >= lists.cap0;
+  const int item = blockIdx.y - (l ? lists.cap0 : 0);
+  if (item >= lists.n_items[l][0]) return;
+  const int2 it = lists.items[l][item];
+  const int item_rows = lists.rows[l];
+  const int e = it.x;
+  const int e_begin = offsets[e], e_end = offsets[e + 1];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, q = lane >> 4, c = lane & 15;
+  const int n_wave = blockIdx.x * 64 * NF + wave * 16 * NF;
+  if (n_wave >= H) return;
+  const int KS = I / 128;
+  const int64_t wrow = I / 2, srow = I / 32;
+
+  Stream16<NF> p;
+  p.w = make_rsrc(w2 + (int64_t)e * H * wrow, (uint32_t)(H * wrow));
+  p.x = make_rsrc(h, 0xFFFFFFFFu);
+  const int run = staged_bytes(16 * NF * (int)srow);
+  stage_scales(w2_s + ((int64_t)e * H + n_wave) * srow, nullptr, 16 * NF * (int)srow, sS + wave * run, lane);
+#pragma unroll
+  for (int f = 0; f < NF; ++f) {
+    p.wo[f] = (n_wave + f * 16) * (int)wrow + lane * 16;
+    p.sl[f] = sS + wave * run + (f * 16 + c) * srow;
+  }
+
+  for (int m0 = it.y; m0 < it.y + item_rows && e_begin + m0 < e_end; m0 += kSmallRows) {
+    const int row0 = e_begin + m0;
+    const int mcount = min(kSmallRows, e_end - row0);
+    const bool has = c < mcount;
+    const int hrow = row0 + (has ? c : 0);
+    p.xo = (hrow * I + 32 * q) * 2;
+    v4f acc[NF] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};
+    stream16<NF>(acc, p, KS, q);
+    float m = 0.f;
+#pragma unroll
+    for (int f = 0; f < NF; ++f)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) m = fmaxf(m, fabsf(acc[f][k]));
+    m = fmaxf(m, __shfl_xor(m, 16));
+    m = fmaxf(m, __shfl_xor(m, 32));
+    const int ex = o_exponent(m);
+    const float inv = exp2_neg(ex);
+    if (has) {
+      const int64_t slot = sorted_pairs[row0 + c];
+      uint16_t* dst = o + slot * H + n_wave + q * 4;
+#pragma unroll
+      for (int f = 0; f < NF; ++f)
+        *reinterpret_cast<uint2*>(dst + f * 16) =
+            f16_pack4(acc[f][0] * inv, acc[f][1] * inv, acc[f][2] * inv, acc[f][3] * inv);
+      if (q == 0) os[slot * (H / 32) + n_wave / 32] = (uint8_t)(ex + 127);
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_w13_a16(const moe_dims& d, const SmallLists& lists, const int32_t* offsets,
+                          const int32_t* sorted_pairs, const uint16_t* x, const uint8_t* w13, const uint8_t* w13_s,
+                          uint16_t* h, hipStream_t s) {
+  const int64_t max_items = (int64_t)lists.cap0 + lists.cap1;
+  if (max_items <= 0) return hipSuccess;
+  const size_t lds = (size_t)kW13Waves * 2 * staged_bytes(16 * (d.H / 32));
+  hipLaunchKernelGGL(k_w13_a16, dim3(d.I / 128, (unsigned)max_items), dim3(kW13Waves * 64), lds, s, lists, offsets,
+                     sorted_pairs, x, w13, w13_s, h, d.H, d.I, d.K);
+  return hipGetLastError();
+}
+
+hipError_t launch_w2_a16(const moe_dims& d, const SmallLists& lists, const int32_t* offsets,
+                         const int32_t* sorted_pairs, const uint16_t* h, const uint8_t* w2, const uint8_t* w2_s,
+                         uint16_t* o, uint8_t* os, hipStream_t s) {
+  const int64_t max_items = (int64_t)lists.cap0 + lists.cap1;
+  if (max_items <= 0) return hipSuccess;
+  const size_t lds = (size_t)kW2Waves * staged_bytes(16 * 2 * (d.I / 32));
+  hipLaunchKernelGGL(k_w2_a16, dim3((unsigned)ceil_div(d.H, 128), (unsigned)max_items), dim3(kW2Waves * 64), lds, s,
+                     lists, offsets, sorted_pairs, h, w2, w2_s, o, os, d.H, d.I);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -17,7 +17,7 @@ size_t ffn_ws_layout(const moe_dims& d, void* base, FfnWs* out) {
   };
   const size_t o_xq = take((size_t)(T * H));
   const size_t o_xs = take((size_t)(T * H / 128));
-  const size_t o_hq = take((size_t)(P * I));
+  const size_t o_hq = take((size_t)(P * I) * ((d.flags & MOE_FLAG_A16) ? 2 : 1));   // A16: bf16 rows
   const size_t o_hs = take((size_t)(P * I / 128));
   const size_t o_o = take(sizeof(uint16_t) * (size_t)(P * H));
   const size_t o_os = take((size_t)(P * H / 32));
@@ -52,7 +52,7 @@ namespace {
 int validate(const moe_dims* d) {
   if (!d) return MOE_EINVAL;
   if (d->T < 0 || d->H <= 0 || d->I <= 0 || d->E < 1 || d->E > kMaxExperts || d->K < 1 || d->K > kMaxTopK ||
-      d->Is < 0 || d->small_max < 0 || (d->flags & ~MOE_FLAG_DECODE_CHAIN) != 0)
+      d->Is < 0 || d->small_max < 0 || (d->flags & ~(MOE_FLAG_DECODE_CHAIN | MOE_FLAG_A16)) != 0)
     return MOE_EINVAL;
   if (d->H % 128 || d->I % 128 || d->Is % 128) return MOE_EUNSUPPORTED;
   if ((int64_t)d->T * d->K > (int64_t)1 << 30) return MOE_EUNSUPPORTED;
@@ -64,6 +64,9 @@ int validate(const moe_dims* d) {
   const int64_t lim = (int64_t)1 << 31;
   if ((int64_t)d->T * d->H >= lim || (int64_t)d->T * d->K * d->I >= lim || (int64_t)d->I * d->H >= lim ||
       (int64_t)d->T * d->Is >= lim)
+    return MOE_EUNSUPPORTED;
+  // bf16 activations: no shared expert; 2-byte activation and SwiGLU rows
+  if ((d->flags & MOE_FLAG_A16) && (d->Is > 0 || 2 * (int64_t)d->T * d->H >= lim || 2 * (int64_t)d->T * d->K * d->I >= lim))
     return MOE_EUNSUPPORTED;
   return MOE_OK;
 }
@@ -167,6 +170,33 @@ int ffn_enqueue(const moe_dims& d, const uint16_t* x, const float* topk_weights,
   uint8_t* h_s = dbg && dbg->h_s ? dbg->h_s : fw.h_s;
 
   const int64_t P = (int64_t)d.T * d.K;
+  if (d.flags & MOE_FLAG_A16) {
+    // bf16 activations: no quantization; every item list walked in 16-row tiles
+    uint16_t* h = dbg && dbg->h_q ? reinterpret_cast<uint16_t*>(dbg->h_q) : reinterpret_cast<uint16_t*>(fw.h_q);
+    SmallLists sl = small_lists(pw.small_items, pw.hdr + 0, pw.small_cap, kSmallRows);
+    sl.items[1] = pw.large_items;
+    sl.n_items[1] = pw.hdr + 1;
+    sl.cap1 = (int)pw.large_cap;
+    sl.rows[1] = kLargeRows;
+    const SmallLists sxl = small_lists(pw.xl_items, pw.hdr + 2, pw.xl_cap, kXlRows);
+    record(dbg, MOE_EV_START, s);
+    record(dbg, MOE_EV_QUANT_DONE, s);
+    hipError_t err = launch_w13_a16(d, sl, expert_offsets, sorted_pairs, x, w13, w13_s, h, s);
+    if (err == hipSuccess && P > kXlRows / 2)
+      err = launch_w13_a16(d, sxl, expert_offsets, sorted_pairs, x, w13, w13_s, h, s);
+    if (err != hipSuccess) return MOE_EHIP;
+    record(dbg, MOE_EV_W13_DONE, s);
+    err = launch_w2_a16(d, sl, expert_offsets, sorted_pairs, h, w2, w2_s, fw.o, fw.os, s);
+    if (err == hipSuccess && P > kXlRows / 2)
+      err = launch_w2_a16(d, sxl, expert_offsets, sorted_pairs, h, w2, w2_s, fw.o, fw.os, s);
+    if (err != hipSuccess) return MOE_EHIP;
+    record(dbg, MOE_EV_W2_DONE, s);
+    record(dbg, MOE_EV_SHARED_DONE, s);
+    err = launch_combine(fw.o, fw.os, topk_weights, pair_rows, nullptr, nullptr, y, d.T, d.H, d.K, s);
+    if (err != hipSuccess) return MOE_EHIP;
+    record(dbg, MOE_EV_END, s);
+    return MOE_OK;
+  }
   // Decode shapes on request (every item walkable in 16-row tiles): one persistent
   // launch runs W13, W2 and the combine, with the shared expert ahead of it
   const bool chain = (d.flags & MOE_FLAG_DECODE_CHAIN) && P <= kFoldPairs;

@@ -6,8 +6,10 @@ Written independently of ``formats`` / ``moe`` so that the two can pin each
 other: element values come from exact fractions built from the bit fields,
 E4M3 rounding is a nearest-point search over every finite code (ties to the
 code with an even mantissa), the block scale is found by searching exponents
-upward until the block fits under 448, dot products are ``math.fsum`` over
-exact products, and everything loops token by token and pick by pick.
+upward until the block fits under 448, bf16 rounding is a binary search over the
+ordered positive bit patterns with exact comparisons, dot products are
+``math.fsum`` over exact products, and everything loops token by token and pick
+by pick.
 """
 
 from __future__ import annotations
@@ -58,6 +60,31 @@ def e4m3_nearest(v: Fraction, negative: bool = None) -> int:
             if bestd is None or d < bestd or (d == bestd and (c & 1) == 0 and (best & 1) == 1):
                 best, bestd = c, d
     return best | (0x80 if negative else 0)
+
+
+_BF16_MAX_FINITE = 0x7F7F
+
+
+def bf16_nearest(v: float) -> int:
+    """Nearest bf16 bit pattern to the float v (finite, within range); ties go
+    to the even pattern; the sign bit follows v's (also for -0.0 and values that
+    round to zero). Positive bf16 patterns 0 .. 0x7F7F increase with their value,
+    so the largest pattern at or below |v| is found by bisection."""
+    a = abs(Fraction(v))
+    lo, hi = 0, _BF16_MAX_FINITE
+    while lo < hi:                      # largest pattern with value <= a
+        mid = (lo + hi + 1) // 2
+        if bf16_value(mid) <= a:
+            lo = mid
+        else:
+            hi = mid - 1
+    best = lo
+    if lo < _BF16_MAX_FINITE:
+        d0 = a - bf16_value(lo)
+        d1 = bf16_value(lo + 1) - a
+        if d1 < d0 or (d1 == d0 and (lo & 1) == 1):
+            best = lo + 1
+    return best | (0x8000 if math.copysign(1.0, v) < 0 else 0)
 
 
 def block_scale(amax: Fraction) -> int:
@@ -116,31 +143,39 @@ def _quantize_dequant(vec, block=128):
     return out, codes, scales
 
 
-def _expert(xh, rows13, rows2, I):
+def _expert(xh, rows13, rows2, I, act="fp8"):
     acc = [_dot(r, xh) for r in rows13]
     h = []
     for n in range(I):
         g, u = acc[n], acc[I + n]
         # exp(-g) overflows below about -709: silu(g) is then -0.0 (g / inf)
         h.append((g / (1.0 + math.exp(-g)) if g > -700 else g * 0.0) * u)
+    if act == "bf16":
+        hq = [bf16_nearest(v) for v in h]
+        hh = [float(bf16_value(b & 0x7FFF)) * (-1.0 if b & 0x8000 else 1.0) for b in hq]
+        return [_dot(r, hh) for r in rows2], hq, None
     hh, hq, hs = _quantize_dequant(h)
     return [_dot(r, hh) for r in rows2], hq, hs
 
 
-def brute_ref(x_bits, topk_ids, topk_weights, w13, w13_s, w2, w2_s, shared=None):
+def brute_ref(x_bits, topk_ids, topk_weights, w13, w13_s, w2, w2_s, shared=None, act="fp8"):
     """Same contract as ``moe.ffn_ref`` (all tokens) for tiny numpy inputs.
-    Returns y (float64 [T, H]) and h codes/scales per (token, pick)."""
+    Returns y (float64 [T, H]) and h codes/scales per (token, pick). act="bf16":
+    x used as its bf16 values, h rounded to bf16 (h_q uint16 bit patterns)."""
     x_bits = np.asarray(x_bits, dtype=np.uint16)
     T, H = x_bits.shape
     K = topk_ids.shape[1]
     E = w13.shape[0]
     I = w2.shape[2] * 2
     y = np.zeros((T, H))
-    hq_all = np.zeros((T, K, I), dtype=np.uint8)
+    hq_all = np.zeros((T, K, I), dtype=np.uint16 if act == "bf16" else np.uint8)
     hs_all = np.zeros((T, K, I // 128), dtype=np.uint8)
     cache = {}
     for t in range(T):
-        xh, xq, xs = _quantize_dequant([bf16_value(int(b)) for b in x_bits[t]])
+        if act == "bf16":
+            xh = [float(bf16_value(int(b) & 0x7FFF)) * (-1.0 if int(b) & 0x8000 else 1.0) for b in x_bits[t]]
+        else:
+            xh, xq, xs = _quantize_dequant([bf16_value(int(b)) for b in x_bits[t]])
         terms = [[] for _ in range(H)]
         for j in range(K):
             e = int(topk_ids[t, j])
@@ -149,9 +184,10 @@ def brute_ref(x_bits, topk_ids, topk_weights, w13, w13_s, w2, w2_s, shared=None)
             if e not in cache:
                 cache[e] = (_floats(mxfp4_row(w13[e, n], w13_s[e, n]) for n in range(2 * I)),
                             _floats(mxfp4_row(w2[e, n], w2_s[e, n]) for n in range(H)))
-            o, hq, hs = _expert(xh, cache[e][0], cache[e][1], I)
+            o, hq, hs = _expert(xh, cache[e][0], cache[e][1], I, act)
             hq_all[t, j] = hq
-            hs_all[t, j] = hs
+            if hs is not None:
+                hs_all[t, j] = hs
             wt = float(topk_weights[t, j])
             for n in range(H):
                 terms[n].append(wt * o[n])

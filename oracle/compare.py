@@ -22,6 +22,12 @@ TEST INFRASTRUCTURE ONLY (see the package docstring).
                    amax lies within the block's largest bound of a boundary);
                    otherwise, and always without an envelope, it is ``bad``.
   Tests require bad == 0, frac_differ <= 0.1% and beyond at most a small cap.
+* SwiGLU outputs of the bf16-activation variant (bf16 bit patterns):
+  ``h_bf16_mismatch`` sorts them into equal / one_ulp (adjacent bf16 values,
+  across zero too) / beyond; with an envelope every differing element (one ulp
+  or more) is checked to be the bf16 rounding (nearest, ties to even, which is
+  monotone) of some value inside the bound, so that each difference is explained
+  by the GPU's arithmetic and none by a wrong result.
 """
 
 from __future__ import annotations
@@ -125,3 +131,46 @@ def h_code_mismatch(hq, hs, hq_ref, hs_ref, amax_ref, block: int = 128, envelope
             "scale_diff_blocks": int((~same[..., 0]).sum()),
             "max_code_dist_same_scale": int(np.where(same, dist, 0).max()) if n else 0,
             "bad_examples": examples}
+
+
+def _bf16_index(bits: np.ndarray) -> np.ndarray:
+    """bf16 pattern -> signed position on the ordered bf16 line (+-0 -> 0)."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.int64)
+    mag = b & 0x7FFF
+    return np.where(b & 0x8000, -mag, mag)
+
+
+def h_bf16_mismatch(hb, hb_ref, envelope=None) -> dict:
+    """hb, hb_ref: bf16 bit patterns of the same shape [R, C] (GPU, oracle).
+    envelope(rows, cols) -> (h_exact, h_err) float64 arrays: the exact SwiGLU
+    value of each listed element and a bound on the GPU's deviation from it
+    before its rounding to bf16."""
+    a = np.asarray(hb, dtype=np.uint16)
+    r = np.asarray(hb_ref, dtype=np.uint16)
+    ia, ir = _bf16_index(a), _bf16_index(r)
+    dist = np.abs(ia - ir)
+    differ = dist != 0
+    rows, cols = np.nonzero(differ)
+    out = {"elements": int(a.size), "differ": int(differ.sum()),
+           "frac_differ": float(differ.mean()) if a.size else 0.0,
+           "one_ulp": int((dist == 1).sum()), "beyond": int((dist > 1).sum()),
+           "max_ulp": int(dist.max()) if a.size else 0, "in_envelope": 0, "bad": 0, "bad_examples": []}
+    if rows.size == 0:
+        return out
+    if envelope is None:
+        out["bad"] = out["beyond"]
+        bi = np.nonzero(dist[rows, cols] > 1)[0][:5]
+        out["bad_examples"] = [(int(rows[i]), int(cols[i]), int(a[rows[i], cols[i]]), int(r[rows[i], cols[i]]))
+                               for i in bi]
+        return out
+    h, e = envelope(rows, cols)
+    lo = _bf16_index(f64_to_bf16_rne(h - e))
+    hi = _bf16_index(f64_to_bf16_rne(h + e))
+    g = ia[rows, cols]
+    ok = (g >= lo) & (g <= hi)
+    out["in_envelope"] = int(ok.sum())
+    out["bad"] = int((~ok).sum())
+    bi = np.nonzero(~ok)[0][:5]
+    out["bad_examples"] = [(int(rows[i]), int(cols[i]), int(a[rows[i], cols[i]]), int(r[rows[i], cols[i]]),
+                            float(h[i]), float(e[i])) for i in bi]
+    return out

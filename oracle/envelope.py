@@ -155,28 +155,32 @@ BF16_STEP = 32
 BF16_FRAC_BITS = 24
 
 
-def bf16_dot_bound(p: np.ndarray) -> np.ndarray:
+def bf16_dot_bound(p: np.ndarray, span: int = BF16_STEP) -> np.ndarray:
     """Upper bound on |hardware - exact| of bf16 MFMA dot products over K (a
-    multiple of 32) of exact products p [..., K]. Per instruction: each of the 32
-    products may lose one step of the grid 2^(E - 24), E one more than the binade
-    of the largest |product| (at least its exponent sum), plus one fp32 ulp of
-    |C + S| <= |partial sum so far| + the bound so far + the step's sum of
-    |products|."""
+    multiple of ``span``) of exact products p [..., K]. K is walked in spans of
+    ``span`` consecutive products (a multiple of 32), in order; each span is
+    summed by span/32 instructions that may split it among themselves in any
+    way. Per instruction: each of its 32 products may lose one step of the grid
+    2^(E - 24), E one more than the binade of the span's largest |product| (at
+    least any exponent sum in it), plus one fp32 ulp of |C + S| <= |partial sum
+    before the span| + the bound so far + the span's sum of |products|."""
     p = np.asarray(p, dtype=np.float64)
     K = p.shape[-1]
-    assert K % BF16_STEP == 0
+    assert span % BF16_STEP == 0 and K % span == 0
+    per = span // BF16_STEP
     lead = p.shape[:-1]
-    steps = p.reshape(lead + (K // BF16_STEP, BF16_STEP))
+    steps = p.reshape(lead + (K // span, span))
     step_sum = steps.sum(-1)
     step_abs = np.abs(steps).sum(-1)
     step_max = np.abs(steps).max(-1)
     partial = np.concatenate([np.zeros(lead + (1,)), np.cumsum(step_sum, axis=-1)[..., :-1]], axis=-1)
     err = np.zeros(lead)
-    for i in range(K // BF16_STEP):
+    for i in range(K // span):
         big = step_max[..., i]
         grid = np.ldexp(1.0, np.maximum(_binade(np.where(big > 0, big, 1.0)) + 1 - BF16_FRAC_BITS, -1074))
         grid = np.where(big > 0, grid, 0.0)
-        err = err + BF16_STEP * grid + FP32_ULP * (np.abs(partial[..., i]) + err + step_abs[..., i])
+        m = np.abs(partial[..., i]) + err + step_abs[..., i]
+        err = err + span * grid + per * FP32_ULP * m
     return err
 
 
@@ -296,6 +300,33 @@ def shared_swiglu_envelope(x_q, x_s, w13s, w13s_s, Is, tok, col, chunk: int = 51
             p = xv * _fp8_block_rows(w13s, w13s_s, rows)
             dots.append(p.sum(-1))
             bounds.append(bf16_dot_bound(p))
+        h[sl] = silu_mul(dots[0], dots[1])
+        err[sl] = swiglu_bound(dots[0], dots[1], bounds[0], bounds[1])
+    return h, err
+
+
+def routed_swiglu_envelope_a16(x_bits, w13, w13_s, I, tok, col, chunk: int = 512):
+    """MXFP4A16: exact SwiGLU values h = silu(g) u of one MXFP4 expert on bf16
+    activations at (token tok[i], column col[i]) and a rigorous bound on how far
+    a GPU that computes g and u with the bf16 MFMA (weights expanded exactly to
+    bf16, fp32 accumulation over ascending 128-K steps of four instructions each,
+    in any split of the step) and SwiGLU in fp32 can be from them. x_bits [T, H]:
+    bf16 bit patterns; w13 [2I, H/2] / w13_s [2I, H/32]: the expert's row-major
+    MXFP4 weights."""
+    tok = np.asarray(tok, np.int64)
+    col = np.asarray(col, np.int64)
+    xall = np.asarray(x_bits, dtype=np.uint16)
+    h = np.zeros(tok.size)
+    err = np.zeros(tok.size)
+    for s in range(0, tok.size, chunk):
+        sl = slice(s, s + chunk)
+        xv = (xall[tok[sl]].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        dots, bounds = [], []
+        for rows in (col[sl], col[sl] + I):
+            wv, _ = _mxfp4_rows(w13, w13_s, rows)
+            p = xv * wv
+            dots.append(p.sum(-1))                       # exact (see oracle.moe)
+            bounds.append(bf16_dot_bound(p, span=128))
         h[sl] = silu_mul(dots[0], dots[1])
         err[sl] = swiglu_bound(dots[0], dots[1], bounds[0], bounds[1])
     return h, err

@@ -18,11 +18,21 @@ Definition followed (per token t, with e = topk_ids[t, j]):
   projection; all MXFP4, dequantized exactly (E2M1 value * 2^(scale-127)).
 * silu(g) = g / (1 + exp(-g)), evaluated in float64, no clamp.
 
+MXFP4A16 variant (``act="bf16"``; MXFP4 weights with 16-bit activations, the
+variant the "Pushing the Limits of Serving DeepSeek-V4-Pro" blog compares against
+in Appendix D.2): x is used as its exact bf16 values, not quantized, and W2 takes
+B(silu(g) * u), the SwiGLU output rounded once to bf16 (nearest, ties to even).
+Reading: the page names the variant only; 16-bit activations mean the operands of
+both GEMMs are bf16, and the SwiGLU output is rounded once where it becomes W2's
+operand, as in the FP8 form where that is the FP8 quantization.
+
 Exactness: a product of an E4M3 value (4 significant bits) and an E2M1 value
 (2 significant bits) times power-of-two scales has at most 6 significant bits,
 and a dot product over 7168 such terms spans far fewer than float64's 53 bits
 for realistic scales, so the float64 GEMMs below are exact whatever order the
 BLAS library sums in (tests/test_oracle_ffn.py checks this against math.fsum).
+The same holds for bf16 activations (8 significant bits; products of 10) at
+realistic value spreads, checked the same way.
 The oracle therefore fixes the GEMM results exactly; only exp and the final
 combine carry float64 rounding.
 """
@@ -33,7 +43,7 @@ import numpy as np
 import torch
 
 from .formats import (E2M1_VALUES, E4M3_VALUES, E8M0_VALUES, bf16_to_f64,
-                      dequantize_blocks, quantize_blocks)
+                      dequantize_blocks, f64_to_bf16_rne, quantize_blocks)
 
 # ----------------------------------------------------------------------------- plan
 
@@ -131,10 +141,20 @@ def _expert_ffn(xh: torch.Tensor, W13: torch.Tensor, W2: torch.Tensor, I: int):
     return (hh @ W2.T).numpy(), hq, hs, amax
 
 
+def _expert_ffn_a16(xh: torch.Tensor, W13: torch.Tensor, W2: torch.Tensor, I: int):
+    """One expert with bf16 activations (MXFP4A16): W13 GEMM on the bf16 rows xh,
+    SwiGLU, the SwiGLU output rounded to bf16, W2 GEMM on it. Returns (out [m, H]
+    float64, h bf16 bit patterns [m, I])."""
+    acc = (xh @ W13.T).numpy()
+    hb = f64_to_bf16_rne(_silu_mul(acc[:, :I], acc[:, I:]))
+    del acc
+    return (torch.from_numpy(bf16_to_f64(hb)) @ W2.T).numpy(), hb
+
+
 # ----------------------------------------------------------------------------- FFN
 
 
-def ffn_ref(x, topk_ids, topk_weights, w13, w13_s, w2, w2_s, shared=None, tokens=None) -> dict:
+def ffn_ref(x, topk_ids, topk_weights, w13, w13_s, w2, w2_s, shared=None, tokens=None, act: str = "fp8") -> dict:
     """The routed MoE FFN in float64 for all tokens or for a subset ``tokens``.
 
     x bf16 [T, H]; topk_ids int [T, K]; topk_weights float32 [T, K]; w13 [E, 2I, H/2],
@@ -151,6 +171,10 @@ def ffn_ref(x, topk_ids, topk_weights, w13, w13_s, w2, w2_s, shared=None, tokens
       valid  bool [n, K]       pick has an id in [0, E)
       shared_h_q / shared_h_s / shared_h_amax (when a shared expert is given).
 
+    act="bf16" (MXFP4A16): x is not quantized; x_q / x_s are None, h_q holds the
+    bf16 SwiGLU outputs (uint16 bit patterns [n, K, I]) and h_s / h_amax are None;
+    no shared expert.
+
     Memory stays near one expert's working set: each expert's W2 outputs are
     added into y as soon as they are computed (the top-k reduction is a sum, so
     the order of its terms only moves float64 rounding), and no per-pair output
@@ -165,6 +189,12 @@ def ffn_ref(x, topk_ids, topk_weights, w13, w13_s, w2, w2_s, shared=None, tokens
     I = w2.shape[2] * 2
     sel = np.arange(T) if tokens is None else np.asarray(tokens, dtype=np.int64)
     n = sel.size
+    if act not in ("fp8", "bf16"):
+        raise ValueError(f"act must be 'fp8' or 'bf16', not {act!r}")
+    if act == "bf16":
+        if shared is not None:
+            raise ValueError("the bf16-activation variant has no shared expert")
+        return _ffn_ref_a16(xb[sel], ids[sel], wts[sel], w13, w13_s, w2, w2_s)
 
     x_q, x_s = quant_act_ref(xb[sel])
     xh = torch.from_numpy(dequantize_blocks(x_q, x_s, 128))
@@ -197,6 +227,26 @@ def ffn_ref(x, topk_ids, topk_weights, w13, w13_s, w2, w2_s, shared=None, tokens
         y += o
         res.update(shared_h_q=hq, shared_h_s=hs, shared_h_amax=am)
     return res
+
+
+def _ffn_ref_a16(xb, sid, wts, w13, w13_s, w2, w2_s) -> dict:
+    n, H = xb.shape
+    K = sid.shape[1]
+    E = w13.shape[0]
+    I = w2.shape[2] * 2
+    xh = torch.from_numpy(bf16_to_f64(xb))
+    y = np.zeros((n, H), dtype=np.float64)
+    h_q = np.zeros((n, K, I), dtype=np.uint16)
+    valid = (sid >= 0) & (sid < E)
+    for e in np.unique(sid[valid]):
+        rows, picks = np.nonzero(sid == e)
+        W13 = dequant_mxfp4(w13[int(e)], w13_s[int(e)])
+        W2 = dequant_mxfp4(w2[int(e)], w2_s[int(e)])
+        o, hb = _expert_ffn_a16(xh[torch.from_numpy(rows)], W13, W2, I)
+        del W13, W2
+        np.add.at(y, rows, wts[rows, picks][:, None] * o)
+        h_q[rows, picks] = hb
+    return {"y": y, "x_q": None, "x_s": None, "h_q": h_q, "h_s": None, "h_amax": None, "valid": valid}
 
 
 def ffn_ref_dense_single(x, w13, w13_s, w2, w2_s) -> np.ndarray:

@@ -10,9 +10,9 @@ import numpy as np
 import torch
 
 import mxfp4_weights_fp8_amd as moe
-from oracle.compare import h_code_mismatch, y_metrics
+from oracle.compare import h_bf16_mismatch, h_code_mismatch, y_metrics
 from oracle.formats import bf16_to_f64
-from oracle.envelope import routed_swiglu_envelope, shared_swiglu_envelope
+from oracle.envelope import routed_swiglu_envelope, routed_swiglu_envelope_a16, shared_swiglu_envelope
 from oracle.moe import ffn_ref, plan_ref
 
 #: the parity bar for the final output (vs the float64 oracle)
@@ -24,6 +24,12 @@ H_DIFFER = 1e-3
 #: codes more than one step away must round from inside the hardware-dot envelope
 #: (oracle/envelope.py), and at most this many may exist: max(2, 2e-5 of the codes)
 BEYOND_FRAC = 2e-5
+#: bf16 SwiGLU outputs (bf16-activation variant): every difference from the oracle
+#: must round from inside the hardware-dot envelope; as a coarse guard on top, at
+#: most this fraction may differ at all (a one-step bf16 difference needs the fp32
+#: SwiGLU value within the envelope of a rounding boundary: about 2 * err / ulp of
+#: the elements, err / ulp near 1e-3 .. 1e-2 on these workloads)
+H16_DIFFER = 2e-2
 
 
 def beyond_cap(n: int) -> int:
@@ -179,4 +185,45 @@ def check_ffn(inp, p, y, dbg, tokens=None, label="", ref=None):
     check_codes(m, "h_")
     if inp.shared is not None:
         check_codes(m, "sh_")
+    return m
+
+
+def check_ffn_a16(inp, p, y, dbg, tokens=None, label="", ref=None):
+    """The bf16-activation variant: oracle (act="bf16") on the selected tokens;
+    compare y and every valid pick's bf16 SwiGLU outputs. Returns metrics."""
+    t0 = time.time()
+    if ref is None:
+        ref = ffn_ref(inp.x, inp.topk_ids, inp.topk_weights, **inp.weights, tokens=tokens, act="bf16")
+    t_oracle = time.time() - t0
+    sel = np.arange(inp.wl.T) if tokens is None else np.asarray(tokens)
+    yb = u16(y)[sel]
+    m = y_metrics(yb, ref["y"])
+    K, I = inp.wl.K, inp.wl.I
+    valid = ref["valid"]
+    rows = p.pair_rows.cpu().numpy()
+    vi, vj = np.nonzero(valid)
+    prow = torch.from_numpy(rows[sel[vi] * K + vj].astype(np.int64))
+    hg = u16(dbg["h_q"][prow.to(dbg["h_q"].device)]) if prow.numel() else np.zeros((0, I), np.uint16)
+    ids = _host(inp.topk_ids)
+    xb = u16(inp.x)[sel]
+    W = inp.weights
+
+    def envelope(r, c):
+        h = np.zeros(r.size)
+        err = np.zeros(r.size)
+        exp = ids[sel[vi[r]], vj[r]]
+        for e in np.unique(exp):
+            mk = exp == e
+            h[mk], err[mk] = routed_swiglu_envelope_a16(xb, _host(W["w13"][int(e)]), _host(W["w13_s"][int(e)]), I,
+                                                        vi[r][mk], c[mk])
+        return h, err
+
+    hm = h_bf16_mismatch(hg, ref["h_q"][valid], envelope=envelope)
+    m.update({"h_" + k: v for k, v in hm.items()}, oracle_s=round(t_oracle, 2), label=label)
+    say(f"[parity a16 {label}] {m}")
+    assert m["finite"], m
+    assert m["max_rel"] <= MAX_REL, m
+    assert m["mean_rel"] <= MEAN_REL, m
+    assert m["h_bad"] == 0, m
+    assert m["h_frac_differ"] <= H16_DIFFER, m
     return m

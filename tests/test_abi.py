@@ -53,7 +53,26 @@ def test_validate(dims, code):
 
 def test_validate_flags():
     assert moe.validate(moe.make_dims(4, 256, 512, 8, 2, flags=moe.FLAG_DECODE_CHAIN)) == moe.MOE_OK
-    assert moe.validate(moe.make_dims(4, 256, 512, 8, 2, flags=2)) == moe.MOE_EINVAL
+    assert moe.validate(moe.make_dims(4, 256, 512, 8, 2, flags=moe.FLAG_A16)) == moe.MOE_OK
+    assert moe.validate(moe.make_dims(4, 256, 512, 8, 2, flags=moe.FLAG_A16 | moe.FLAG_DECODE_CHAIN)) == moe.MOE_OK
+    assert moe.validate(moe.make_dims(4, 256, 512, 8, 2, flags=4)) == moe.MOE_EINVAL
+    assert moe.validate(moe.make_dims(4, 256, 512, 8, 2, flags=-1)) == moe.MOE_EINVAL
+
+
+def test_validate_a16_limits():
+    # no shared expert with bf16 activations
+    assert moe.validate(moe.make_dims(4, 256, 512, 8, 2, Is=128, flags=moe.FLAG_A16)) == moe.MOE_EUNSUPPORTED
+    # bf16 rows addressed with 32-bit byte offsets: T*H and T*K*I below 2^30
+    assert moe.validate(moe.make_dims(131072, 8192, 512, 8, 2, flags=moe.FLAG_A16)) == moe.MOE_EUNSUPPORTED
+    assert moe.validate(moe.make_dims(131072, 8192, 512, 8, 2)) == moe.MOE_OK
+    assert moe.validate(moe.make_dims(65536, 256, 2048, 8, 8, flags=moe.FLAG_A16)) == moe.MOE_EUNSUPPORTED
+    assert moe.validate(moe.make_dims(65536, 256, 2048, 8, 4, flags=moe.FLAG_A16)) == moe.MOE_OK
+
+
+def test_a16_workspace_holds_bf16_rows():
+    d8 = moe.make_dims(4096, 1024, 512, 64, 8)
+    d16 = moe.make_dims(4096, 1024, 512, 64, 8, flags=moe.FLAG_A16)
+    assert moe.ffn_workspace_bytes(d16) - moe.ffn_workspace_bytes(d8) >= 4096 * 8 * 512
 
 
 def test_validate_null_and_shared():

@@ -125,3 +125,45 @@ def test_envelope_scale_change_needs_amax_near_a_boundary():
     assert m["bad"] == 0 and m["in_envelope"] == m["beyond"] > 0
     m = h_code_mismatch(qg, sg, qr, sr, ar, envelope=env_of(2.0 ** -16))
     assert m["bad"] > 0
+
+
+# ----------------------------------------------------------------------------- bf16 SwiGLU outputs
+
+from oracle.compare import h_bf16_mismatch  # noqa: E402
+from oracle.formats import bf16_to_f64 as _b2f, f64_to_bf16_rne as _f2b  # noqa: E402
+
+
+def _bf(vals):
+    return _f2b(np.asarray(vals, np.float64)).reshape(1, -1)
+
+
+def test_bf16_categories_without_envelope():
+    ref = _bf([1.0, -2.0, 0.0, 3.0, 1e-3])
+    gpu = ref.copy()
+    gpu[0, 0] += 1                         # one ulp up
+    gpu[0, 2] = 0x8001                     # -0 -> smallest negative subnormal: one ulp across zero
+    gpu[0, 3] += 2                         # two ulps: beyond, bad without an envelope
+    m = h_bf16_mismatch(gpu, ref)
+    assert (m["differ"], m["one_ulp"], m["beyond"], m["bad"], m["max_ulp"]) == (3, 2, 1, 1, 2)
+    assert m["bad_examples"][0][:2] == (0, 3)
+    assert h_bf16_mismatch(ref, ref)["differ"] == 0
+    assert h_bf16_mismatch(_bf([0.0]), np.array([[0x8000]], np.uint16))["differ"] == 0
+
+
+def test_bf16_envelope_explains_or_rejects_each_difference():
+    h = np.array([1.0 + 2.0 ** -8 - 2.0 ** -20, 5.0, 5.0])    # just below a rounding boundary; mid-step
+    ref = _f2b(h).reshape(1, -1)
+    gpu = ref.copy()
+    gpu[0, 0] += 1                         # reachable: h + 2^-19 rounds up
+    gpu[0, 1] += 1                         # one ulp from a value far from any boundary: wrong
+    gpu[0, 2] += 3                         # three ulps, reachable only with a wide bound
+
+    def env_fn(err):
+        return lambda rows, cols: (h[cols], np.asarray(err)[cols])
+
+    m = h_bf16_mismatch(gpu, ref, envelope=env_fn([2.0 ** -19, 2.0 ** -19, 2.0 ** -19]))
+    assert (m["in_envelope"], m["bad"]) == (1, 2)
+    m = h_bf16_mismatch(gpu, ref, envelope=env_fn([2.0 ** -19, 2.0 ** -19, 0.1]))
+    assert (m["in_envelope"], m["bad"]) == (2, 1)
+    assert m["bad_examples"][0][1] == 1
+    assert _b2f(gpu)[0, 2] <= 5.1

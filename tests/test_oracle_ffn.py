@@ -155,3 +155,96 @@ def test_token_subset_matches_full(small):
     part = ffn_ref(small.x, small.topk_ids, small.topk_weights, **small.weights, tokens=sub)
     assert np.array_equal(part["y"], full["y"][sub])
     assert np.array_equal(part["h_q"], full["h_q"][sub])
+
+
+# ----------------------------------------------------------------------------- bf16 activations (MXFP4A16)
+
+
+@pytest.mark.parametrize("T,H,I,E,K,seed", [
+    (3, 256, 256, 3, 2, 41),
+    (4, 128, 128, 1, 1, 42),
+])
+def test_a16_ffn_ref_equals_bruteforce(T, H, I, E, K, seed):
+    wl = scaled("tiny", T=T, H=H, I=I, E=E, K=K, seed=seed, weight_seed=seed, name="b16")
+    inp = make_inputs(wl)
+    ids = inp.topk_ids.numpy().copy()
+    if E > 1:
+        ids[1, 0] = -1
+    r = ffn_ref(inp.x, ids, inp.topk_weights, **inp.weights, act="bf16")
+    b = brute_ref(_bits(inp.x), ids, inp.topk_weights.numpy(), **_np(inp.weights), act="bf16")
+    assert r["h_q"].dtype == np.uint16 and r["x_q"] is None
+    assert np.array_equal(r["h_q"][r["valid"]], b["h_q"][r["valid"]])
+    np.testing.assert_allclose(r["y"], b["y"], rtol=1e-13, atol=1e-15 * np.abs(b["y"]).max())
+
+
+def test_a16_bf16_nearest_matches_brute_on_edges():
+    """Brute bf16 rounding (bisection over patterns, exact comparisons) against
+    values placed on and around rounding boundaries, including ties both ways."""
+    from oracle.brute import bf16_nearest
+    from oracle.formats import f64_to_bf16_rne
+    one = 1.0
+    vals = [0.0, -0.0, one, one + 2 ** -8, one + 3 * 2 ** -8, one + 2 ** -8 + 2 ** -30, -(one + 2 ** -8),
+            2 ** -126, 2 ** -133, 1.5 * 2 ** -133, 2.5 * 2 ** -133, 3.0e38, 1234.5678, -1e-20]
+    assert [bf16_nearest(v) for v in vals] == [int(b) for b in f64_to_bf16_rne(np.array(vals))]
+    assert bf16_nearest(one + 2 ** -8) == 0x3F80          # tie to even (down)
+    assert bf16_nearest(one + 3 * 2 ** -8) == 0x3F82      # tie to even (up)
+    assert bf16_nearest(-0.0) == 0x8000
+
+
+def test_a16_float64_gemm_is_exact_at_full_hidden_size():
+    """bf16 activations (8 significant bits) times MXFP4 values: the float64
+    BLAS dots still equal math.fsum of the exact products at H = 7168."""
+    from oracle.formats import bf16_to_f64
+    wl = scaled("decode7", E=1, T=8, I=128, full_I=0, weight_seed=78, seed=78, name="ex16")
+    W = make_expert_weights(wl, "cpu")
+    xh = bf16_to_f64(_bits(make_inputs(wl, weights=False).x))
+    Wd = dequant_mxfp4(W["w13"][0], W["w13_s"][0]).numpy()
+    blas = xh @ Wd.T
+    for t in range(xh.shape[0]):
+        for n in range(0, Wd.shape[0], 37):
+            assert blas[t, n] == math.fsum(xh[t] * Wd[n])
+
+
+def test_a16_invariants(small):
+    """K = 1 with weight 1 is the dense bf16 SwiGLU expert; uniform gating is the
+    mean; dropped picks add nothing."""
+    from oracle.formats import bf16_to_f64, f64_to_bf16_rne
+    T, I = small.wl.T, small.wl.I
+    W = small.weights
+    y = ffn_ref(small.x, np.full((T, 1), 2), np.ones((T, 1), np.float32), **W, act="bf16")
+    xh = bf16_to_f64(_bits(small.x))
+    acc = xh @ dequant_mxfp4(W["w13"][2], W["w13_s"][2]).numpy().T
+    g, u = acc[:, :I], acc[:, I:]
+    h = bf16_to_f64(f64_to_bf16_rne(g / (1 + np.exp(-g)) * u))
+    dense = h @ dequant_mxfp4(W["w2"][2], W["w2_s"][2]).numpy().T
+    np.testing.assert_allclose(y["y"], dense, rtol=1e-13, atol=1e-15 * np.abs(dense).max())
+    ids = small.topk_ids.numpy()
+    half = np.full(ids.shape, 0.5, dtype=np.float32)
+    one = np.ones((T, 1), dtype=np.float32)
+    y2 = ffn_ref(small.x, ids, half, **W, act="bf16")["y"]
+    y0 = ffn_ref(small.x, ids[:, :1], one, **W, act="bf16")["y"]
+    y1 = ffn_ref(small.x, ids[:, 1:], one, **W, act="bf16")["y"]
+    assert np.array_equal(y2, 0.5 * y0 + 0.5 * y1)
+    d = ids.copy()
+    d[:, 1] = E_OUT = small.wl.E + 5
+    assert E_OUT > small.wl.E
+    yd = ffn_ref(small.x, d, small.topk_weights, **W, act="bf16")
+    y0w = ffn_ref(small.x, ids[:, :1], small.topk_weights.numpy()[:, :1], **W, act="bf16")
+    assert np.array_equal(yd["y"], y0w["y"]) and not yd["valid"][:, 1].any()
+
+
+def test_a16_differs_from_fp8_path(small):
+    """The two activation modes are different computations: quantizing x to FP8
+    moves y by far more than float64 rounding."""
+    a = ffn_ref(small.x, small.topk_ids, small.topk_weights, **small.weights)["y"]
+    b = ffn_ref(small.x, small.topk_ids, small.topk_weights, **small.weights, act="bf16")["y"]
+    rel = np.abs(a - b).max() / np.abs(b).max()
+    assert 1e-4 < rel < 0.2
+
+
+def test_a16_refuses_shared_and_unknown_modes(small):
+    with pytest.raises(ValueError):
+        ffn_ref(small.x, small.topk_ids, small.topk_weights, **small.weights, act="fp16")
+    sh = make_inputs(scaled("tiny", T=4, H=256, I=256, E=2, K=1, Is=128, seed=3, weight_seed=3, name="s16")).shared
+    with pytest.raises(ValueError):
+        ffn_ref(small.x, small.topk_ids, small.topk_weights, **small.weights, shared=sh, act="bf16")
