@@ -105,6 +105,10 @@ def probe_lib():
                                                                                               ctypes.c_void_p]
         L.probe_mfma_bf16.restype = ctypes.c_int
         L.probe_mfma_bf16.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_int, ctypes.c_void_p]
+        L.probe_cvt_fp4_bf16.restype = ctypes.c_int
+        L.probe_cvt_fp4_bf16.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int, ctypes.c_void_p]
+        L.probe_cvt_fp4_f32.restype = ctypes.c_int
+        L.probe_cvt_fp4_f32.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int, ctypes.c_void_p]
         _lib = L
     return _lib
 

@@ -8,7 +8,9 @@
 //   c      [waves][64][4]       float   accumulator input
 //   d      [waves][64][4]       float   result
 // The caller lays values out in the instruction's lane order; nothing here
-// interprets them. Every pointer is a device pointer; `waves` >= 1; the launch
+// interprets them. probe_cvt_fp4_bf16 runs gfx950's scaled FP4 -> bf16 conversion
+// on n words (one thread per word, guarded by n); probe_cvt_fp4_f32 its
+// fp32-output form. Every pointer is a device pointer; `waves` >= 1; the launch
 // is one 64-lane workgroup per wave, so every access stays inside the arrays.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -58,6 +60,39 @@ __global__ __launch_bounds__(64) void k_bf16(const int* __restrict__ a, const in
   for (int i = 0; i < 4; ++i) d[r * 4 + i] = D[i];
 }
 
+__global__ __launch_bounds__(64) void k_cvt_fp4_bf16(const uint32_t* __restrict__ w, const float* __restrict__ sc,
+                                                     uint32_t* __restrict__ out, int n) {
+  const int i = blockIdx.x * 64 + threadIdx.x;
+  if (i >= n) return;
+  const uint32_t v = w[i];
+  const float s = sc[i];
+  out[4 * i + 0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, s, 0));
+  out[4 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, s, 1));
+  out[4 * i + 2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, s, 2));
+  out[4 * i + 3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, s, 3));
+}
+
+__global__ __launch_bounds__(64) void k_cvt_fp4_f32(const uint32_t* __restrict__ w, const float* __restrict__ sc,
+                                                    float* __restrict__ out, int n) {
+  const int i = blockIdx.x * 64 + threadIdx.x;
+  if (i >= n) return;
+  const uint32_t v = w[i];
+  const float s = sc[i];
+  typedef float v2f __attribute__((ext_vector_type(2)));
+  const v2f r0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(v, s, 0);
+  const v2f r1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(v, s, 1);
+  const v2f r2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(v, s, 2);
+  const v2f r3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(v, s, 3);
+  out[8 * i + 0] = r0[0];
+  out[8 * i + 1] = r0[1];
+  out[8 * i + 2] = r1[0];
+  out[8 * i + 3] = r1[1];
+  out[8 * i + 4] = r2[0];
+  out[8 * i + 5] = r2[1];
+  out[8 * i + 6] = r3[0];
+  out[8 * i + 7] = r3[1];
+}
+
 }  // namespace
 
 extern "C" {
@@ -84,6 +119,24 @@ int probe_mfma_scaled(int fmt_a, int fmt_b, const int* a, const int* b, const in
 int probe_mfma_bf16(const int* a, const int* b, const float* c, float* d, int waves, void* stream) {
   if (waves < 1) return -1;
   hipLaunchKernelGGL(k_bf16, dim3(waves), dim3(64), 0, (hipStream_t)stream, a, b, c, d);
+  return (int)hipGetLastError();
+}
+
+// v_cvt_scalef32_pk_bf16_fp4 on words[i] with scales[i], byte selects 0..3:
+// out[4i + k] = the two bf16 of byte k (n >= 0 words; device pointers).
+int probe_cvt_fp4_bf16(const uint32_t* words, const float* scales, uint32_t* out, int n, void* stream) {
+  if (n < 0) return -1;
+  if (n == 0) return 0;
+  hipLaunchKernelGGL(k_cvt_fp4_bf16, dim3((n + 63) / 64), dim3(64), 0, (hipStream_t)stream, words, scales, out, n);
+  return (int)hipGetLastError();
+}
+
+// v_cvt_scalef32_pk_f32_fp4 on words[i] with scales[i]: out[8i + 2k + h] = value
+// h (0 = low nibble) of byte k.
+int probe_cvt_fp4_f32(const uint32_t* words, const float* scales, float* out, int n, void* stream) {
+  if (n < 0) return -1;
+  if (n == 0) return 0;
+  hipLaunchKernelGGL(k_cvt_fp4_f32, dim3((n + 63) / 64), dim3(64), 0, (hipStream_t)stream, words, scales, out, n);
   return (int)hipGetLastError();
 }
 

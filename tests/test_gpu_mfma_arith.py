@@ -239,3 +239,86 @@ def test_bf16_mfma_chains_within_bound(dev, ops):
     print(f"[mfma chain bf16] max err/bound {(err / bound).max():.3f}, median rel err "
           f"{np.median(err / np.abs(exact)):.2e}, equal to the model {np.mean(got == emu):.4f}", flush=True)
     assert (err <= bound).all()
+
+
+# ----------------------------------------------------------------------------- FP4 -> bf16 conversion
+
+
+def _cvt_fp4(words: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """v_cvt_scalef32_pk_bf16_fp4 on the GPU: [n] words x [n] scales -> [n, 4, 2]
+    bf16 bit patterns (byte select k, low then high half)."""
+    import ctypes
+    w = torch.from_numpy(words.astype(np.uint32).view(np.int32)).to("cuda:0")
+    s = torch.from_numpy(scales.astype(np.float32)).to("cuda:0")
+    out = torch.zeros(4 * words.size, dtype=torch.int32, device="cuda:0")
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    assert ml.probe_lib().probe_cvt_fp4_bf16(w.data_ptr(), s.data_ptr(), out.data_ptr(), words.size, st) == 0
+    torch.cuda.synchronize()
+    o = out.cpu().numpy().view(np.uint32).reshape(-1, 4)
+    return np.stack([o & 0xFFFF, o >> 16], axis=-1).astype(np.uint16)
+
+
+def _fp4_words_all_bytes():
+    """Every byte value at every byte position: word i holds byte i % 256 at
+    position i // 256 and 0x00 elsewhere."""
+    i = np.arange(1024)
+    return ((i % 256).astype(np.uint64) << (8 * (i // 256)).astype(np.uint64)).astype(np.uint32)
+
+
+def _expected_fp4(words, scales):
+    from oracle.formats import f64_to_bf16_rne
+    b = (words[:, None] >> (8 * np.arange(4))[None, :]) & 0xFF            # [n, 4] bytes
+    nib = np.stack([b & 0xF, b >> 4], axis=-1)                              # low nibble first
+    return f64_to_bf16_rne(E2M1_VALUES[nib] * scales[:, None, None].astype(np.float64))
+
+
+@pytest.mark.parametrize("scale", [1.0, 2.0 ** -9, 2.0 ** 7, 2.0 ** -126])
+def test_cvt_fp4_bf16_power_of_two_scales(dev, scale):
+    """The MXFP4 x bf16 kernels expand codes with this conversion and an E8M0
+    scale: byte k of the word -> pair k, the low nibble -> the low bf16, value
+    E2M1 x scale exactly (every E2M1 value times a power of two is a bf16)."""
+    words = _fp4_words_all_bytes()
+    scales = np.full(words.size, scale, dtype=np.float32)
+    got = _cvt_fp4(words, scales)
+    exp = _expected_fp4(words, scales)
+    assert np.array_equal(got, exp), np.argwhere(got != exp)[:5]
+
+
+def test_cvt_fp4_bf16_takes_only_the_scale_exponent(dev):
+    """With a scale that is not a power of two (every positive E4M3 value is
+    tried) the conversion multiplies by 2^floor(log2 scale) only: the scale's
+    mantissa is dropped. A kernel that expands codes with NVFP4's E4M3 block
+    scales must therefore apply the scale's mantissa itself."""
+    words = _fp4_words_all_bytes()
+    pos = np.arange(1, 0x7F)                                                # every positive finite E4M3
+    for i in range(0, pos.size, 16):
+        sc = np.resize(E4M3_VALUES[pos[i:i + 16]], words.size).astype(np.float32)
+        pow2 = np.ldexp(1.0, np.frexp(sc.astype(np.float64))[1] - 1).astype(np.float32)
+        got = _cvt_fp4(words, sc)
+        assert np.array_equal(got, _expected_fp4(words, pow2))
+        if i == 0:
+            assert not np.array_equal(got, _expected_fp4(words, sc))       # the mantissa matters here
+
+
+def _cvt_fp4_f32(words: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    import ctypes
+    w = torch.from_numpy(words.astype(np.uint32).view(np.int32)).to("cuda:0")
+    s = torch.from_numpy(scales.astype(np.float32)).to("cuda:0")
+    out = torch.zeros(8 * words.size, dtype=torch.float32, device="cuda:0")
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    assert ml.probe_lib().probe_cvt_fp4_f32(w.data_ptr(), s.data_ptr(), out.data_ptr(), words.size, st) == 0
+    torch.cuda.synchronize()
+    return out.cpu().numpy().reshape(-1, 4, 2).astype(np.float64)
+
+
+@pytest.mark.parametrize("scale", [1.0, 2.0 ** -12, 2.0 ** 5])
+def test_cvt_fp4_f32_power_of_two_scales(dev, scale):
+    """The fp32-output form (v_cvt_scalef32_pk_f32_fp4), which the NVFP4 kernels
+    use before multiplying by the block scale's mantissa: byte k -> pair k, low
+    nibble first, E2M1 x scale exactly."""
+    words = _fp4_words_all_bytes()
+    sc = np.full(words.size, scale, dtype=np.float32)
+    b = (words[:, None] >> (8 * np.arange(4))[None, :]) & 0xFF
+    exp = E2M1_VALUES[np.stack([b & 0xF, b >> 4], axis=-1)] * scale
+    got = _cvt_fp4_f32(words, sc)
+    assert np.array_equal(got, exp) and np.array_equal(np.signbit(got), np.signbit(exp))
