@@ -11,7 +11,8 @@ decode step (32 requests x 8 positions) as "decode256" (HBM roofline), the
 32K-token prefill chunk (Zipf 1.2) as "prefill32k" (MFMA roofline of its W13
 GEMM) and one MoE-TP8 rank of it as "tp8rank32k" (MFMA and HBM bounds), because
 the metric names them; "decode7_a16" and "decode256_a16" time the two decode
-steps with bf16 activations (the MXFP4A16 variant, MOE_FLAG_A16). Kernel durations come from HIP events the library records
+steps with bf16 activations (the MXFP4A16 variant, MOE_FLAG_A16), and
+"decode7_nvfp4" / "decode256_nvfp4" with NVFP4 expert weights (moe_ffn_nvfp4). Kernel durations come from HIP events the library records
 on the stream it launches on; the oracle's CPU time on bounded samples is
 reported as cpu_baseline.
 
@@ -53,11 +54,13 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def expert_bytes(w) -> dict:
-    """Algorithmic bytes of one expert's MXFP4 weights (codes + E8M0 scales)."""
+def expert_bytes(w, nvfp4: bool = False) -> dict:
+    """Algorithmic bytes of one expert's 4-bit weights: MXFP4 codes + E8M0 scales
+    per 32, or NVFP4 codes + E4M3 scales per 16 + one fp32 tensor scale."""
     H, I = w.H, w.I
-    w13 = 2 * I * H // 2 + 2 * I * H // 32
-    w2 = H * I // 2 + H * I // 32
+    blk, extra = (16, 4) if nvfp4 else (32, 0)
+    w13 = 2 * I * H // 2 + 2 * I * H // blk + extra
+    w2 = H * I // 2 + H * I // blk + extra
     return {"w13": w13, "w2": w2}
 
 
@@ -191,19 +194,21 @@ def decode_object(r: Runner, steps: int, warmup: int, flush: torch.Tensor) -> di
     SwiGLU rows written are bf16, 2 bytes per element and no scales."""
     w = r.w
     P = w.T * w.K
-    a16 = bool(r.flags & moe.FLAG_A16)
+    nv = bool(r.flags & moe.FLAG_NVFP4)
+    a16 = bool(r.flags & (moe.FLAG_A16 | moe.FLAG_NVFP4))
     chain = bool(r.flags & moe.FLAG_DECODE_CHAIN) and P <= CHAIN_MAX_PAIRS and not a16
     ms_step, dom_ms, stages = r.run(steps, warmup)
     fl_step, fl_dom = r.run_flushed(steps, flush)
-    eb = expert_bytes(w)
+    eb = expert_bytes(w, nvfp4=nv)
     if chain:
         dom_bytes = r.distinct * (eb["w13"] + eb["w2"]) + w.T * (w.H + w.H // 128) + w.T * w.H * 2
         dom_name = "decode chain: W13 + SwiGLU/requant, W2, combine in one launch (k_decode_chain)"
         traffic = measured_traffic(w.name, "moe::k_decode_chain")
     elif a16:
         dom_bytes = r.distinct * eb["w13"] + w.T * w.H * 2 + P * w.I * 2
-        dom_name = "W13 stage, bf16 activations: grouped GEMM + SwiGLU (k_w13_a16)"
-        traffic = measured_traffic(w.name + "_a16", "moe::k_w13_a16")
+        dom_name = ("W13 stage, NVFP4 weights, bf16 activations: grouped GEMM + SwiGLU (k_w13_a16<true>)" if nv else
+                    "W13 stage, bf16 activations: grouped GEMM + SwiGLU (k_w13_a16<false>)")
+        traffic = measured_traffic(w.name + ("_nvfp4" if nv else "_a16"), "moe::k_w13_a16<%s>" % str(nv).lower())
     else:
         dom_bytes = r.distinct * eb["w13"] + w.T * (w.H + w.H // 128) + P * (w.I + w.I // 128)
         dom_name = "W13 stage: grouped GEMM + SwiGLU/requant (k_w13_small<8>" + \
@@ -218,7 +223,8 @@ def decode_object(r: Runner, steps: int, warmup: int, flush: torch.Tensor) -> di
         "value": w.T / (ms_step * 1e-3), "unit": "tokens/s", "ms_per_step": ms_step, "steps": steps,
         "config": {"workload": w.name, "tokens": w.T, "hidden": w.H, "experts": w.E, "intermediate": w.I,
                    "top_k": w.K, "routing": w.routing + f" s={w.zipf_s}", "distinct_experts": r.distinct,
-                   **({"activations": "bf16 (MXFP4A16)"} if a16 else {})},
+                   **({"weights": "NVFP4 (E4M3 per 16 + fp32 tensor scale)", "activations": "bf16"} if nv else
+                      {"activations": "bf16 (MXFP4A16)"} if a16 else {})},
         "roofline": {"bound": "hbm", "kernel": dom_name,
                      "achieved": gbs(dom_bytes, dom_ms), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs(dom_bytes, dom_ms) / HBM_PEAK_GBS, "traffic": traffic,
@@ -282,8 +288,8 @@ def main():
     ap.add_argument("--prefill-steps", type=int, default=5)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--only", choices=["decode7", "decode7_chain", "decode7_a16", "decode256", "decode256_a16",
-                                       "prefill32k", "tp8rank32k", "copy"],
+    ap.add_argument("--only", choices=["decode7", "decode7_chain", "decode7_a16", "decode7_nvfp4", "decode256",
+                                       "decode256_a16", "decode256_nvfp4", "prefill32k", "tp8rank32k", "copy"],
                     default=None,
                     help="run one workload only (for profiling); prints its own JSON object. 'copy' runs "
                          "a 1 GiB device-to-device copy, the known-size reference for HBM byte counters")
@@ -315,9 +321,14 @@ def main():
     if args.only is not None:
         chain = args.only == "decode7_chain"
         a16 = args.only.endswith("_a16")
-        name = args.only.split("_")[0] if (chain or a16) else args.only
-        r = Runner(name, dev, W if args.only != "tp8rank32k" else None,
-                   flags=moe.FLAG_DECODE_CHAIN if chain else (moe.FLAG_A16 if a16 else 0))
+        nv = args.only.endswith("_nvfp4")
+        name = args.only.split("_")[0] if (chain or a16 or nv) else args.only
+        if nv:
+            r = Runner(name, dev, moe.pack_weights(make_expert_weights(WORKLOADS["decode7"], dev, fmt="nvfp4")),
+                       flags=moe.FLAG_NVFP4)
+        else:
+            r = Runner(name, dev, W if args.only != "tp8rank32k" else None,
+                       flags=moe.FLAG_DECODE_CHAIN if chain else (moe.FLAG_A16 if a16 else 0))
         if args.only.startswith("decode"):
             obj = decode_object(r, args.steps, args.warmup, flush)
         else:
@@ -357,6 +368,13 @@ def main():
     out["decode7_a16"] = decode_object(Runner("decode7", dev, W, flags=moe.FLAG_A16), args.steps, args.warmup, flush)
     out["decode256_a16"] = decode_object(Runner("decode256", dev, W, flags=moe.FLAG_A16), max(args.steps // 2, 5),
                                          args.warmup, flush)
+    # ---- and with NVFP4 expert weights (the same float weights packed as NVFP4)
+    W_nv = moe.pack_weights(make_expert_weights(WORKLOADS["decode7"], dev, fmt="nvfp4"))
+    out["decode7_nvfp4"] = decode_object(Runner("decode7", dev, W_nv, flags=moe.FLAG_NVFP4), args.steps,
+                                         args.warmup, flush)
+    out["decode256_nvfp4"] = decode_object(Runner("decode256", dev, W_nv, flags=moe.FLAG_NVFP4),
+                                           max(args.steps // 2, 5), args.warmup, flush)
+    del W_nv
 
     # ---- prefill chunk, 32K tokens, and one MoE-TP8 rank of it
     if not args.no_prefill:

@@ -69,7 +69,7 @@ enum {
  *   small_max  experts with at most this many routed pairs use the small-M
  *      (decode) tiling, larger ones the large-M (prefill) tiling; 0 selects the
  *      library default (16). moe_plan and moe_ffn must see the same value.
- *   flags  0, or MOE_FLAG_DECODE_CHAIN and / or MOE_FLAG_A16 (below). */
+ *   flags  0, or MOE_FLAG_DECODE_CHAIN, MOE_FLAG_A16, MOE_FLAG_NVFP4 (below). */
 typedef struct moe_dims {
   int32_t T, H, I, E, K, Is;
   int32_t small_max;
@@ -97,6 +97,11 @@ typedef struct moe_dims {
  * [P, I] (2 bytes per element) and x_q, x_s, h_s are not written.
  * MOE_FLAG_DECODE_CHAIN is ignored with it. */
 #define MOE_FLAG_A16 2
+
+/* NVFP4 expert weights with bf16 activations, run through moe_ffn_nvfp4 (moe_ffn
+ * and moe_ffn_static return MOE_EINVAL for it). Same activation path, limits and
+ * workspace as MOE_FLAG_A16 (bf16 SwiGLU rows, no shared expert). */
+#define MOE_FLAG_NVFP4 4
 
 /* Dense shared expert ("Pushing the Limits of Serving DeepSeek-V4-Pro", section
  * 3.2: its output is added to the top-k reduction with weight 1). FP8 E4M3 weights
@@ -237,6 +242,29 @@ int moe_ffn_static(const moe_dims* dims, const uint16_t* x, const float* topk_we
                    const void* plan_ws, const uint8_t* w13, const uint8_t* w13_s, const uint8_t* w2,
                    const uint8_t* w2_s, const moe_shared* shared, uint16_t* y, const moe_debug* dbg,
                    void* stream);
+
+/* The routed MoE FFN with NVFP4 expert weights consumed as stored ("Optimization
+ * progress report", Optimization 05: native NVFP4 MoE, no re-quantization of the
+ * weights). The page names the format only; the layout is NVIDIA's published
+ * NVFP4: E2M1 codes, one E4M3 scale per 16 consecutive K elements and one fp32
+ * scale per tensor, w = E2M1 * E4M3 * tensor scale. Activations are bf16 and the
+ * SwiGLU output is rounded once to bf16 (as MOE_FLAG_A16); no shared expert.
+ *   dims->flags   must include MOE_FLAG_NVFP4 (plan, workspace size and this call)
+ *   w13    [E, 2I, H/2] E2M1 codes, low nibble = even K, in the layout of
+ *                       moe_pack_weights (the same packing as MXFP4 codes)
+ *   w13_s  [E, 2I, H/16] E4M3 block scales (non-negative, finite), row-major
+ *   w13_gs [E] float32   tensor scale of each expert's W13
+ *   w2     [E, H, I/2]   codes, packed as w13
+ *   w2_s   [E, H, I/16]  E4M3 block scales, row-major
+ *   w2_gs  [E] float32   tensor scale of each expert's W2
+ *   everything else as moe_ffn; dbg->h_q receives bf16 [P, I] SwiGLU rows.
+ * Errors: MOE_EINVAL (also without MOE_FLAG_NVFP4 or a tensor-scale pointer),
+ * MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP. */
+int moe_ffn_nvfp4(const moe_dims* dims, const uint16_t* x, const float* topk_weights,
+                  const int32_t* expert_offsets, const int32_t* sorted_pairs, const int32_t* pair_rows,
+                  const void* plan_ws, const uint8_t* w13, const uint8_t* w13_s, const float* w13_gs,
+                  const uint8_t* w2, const uint8_t* w2_s, const float* w2_gs, uint16_t* y,
+                  const moe_debug* dbg, void* ws, size_t ws_bytes, void* stream);
 
 /* Static, human-readable name of a status code. */
 const char* moe_status_string(int code);

@@ -47,6 +47,8 @@ class Dims(ctypes.Structure):
 FLAG_DECODE_CHAIN = 1
 #: moe_dims.flags bit: bf16 activations (MXFP4A16): x not quantized, bf16 SwiGLU rows
 FLAG_A16 = 2
+#: moe_dims.flags bit: NVFP4 expert weights with bf16 activations (ffn with NVFP4 weights)
+FLAG_NVFP4 = 4
 
 
 class Shared(ctypes.Structure):
@@ -74,6 +76,8 @@ _SIGNATURES = {
                 ctypes.c_void_p, ctypes.POINTER(Debug), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "moe_ffn_static": (ctypes.c_int, [ctypes.POINTER(Dims)] + [ctypes.c_void_p] * 10 + [ctypes.POINTER(Shared),
                        ctypes.c_void_p, ctypes.POINTER(Debug), ctypes.c_void_p]),
+    "moe_ffn_nvfp4": (ctypes.c_int, [ctypes.POINTER(Dims)] + [ctypes.c_void_p] * 13 + [ctypes.POINTER(Debug),
+                      ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
 }
 
@@ -250,8 +254,11 @@ def ffn(x: torch.Tensor, topk_weights: torch.Tensor, p: Plan, weights: dict, sha
     the kernel-native layout, w13_s and w2_s row-major; uint8 cuda); shared:
     optional dict w13s, w13s_s, w2s, w2s_s.
     Returns y (bf16 [T, H]); with debug=True returns (y, dict of x_q, x_s, h_q, h_s,
-    sh_q, sh_s); with FLAG_A16 in the plan's flags, h_q holds the bf16 SwiGLU rows
-    (int16 [P, I]) and x_q, x_s, h_s are left as allocated. ``events``: optional StageEvents recorded at the stage boundaries.
+    sh_q, sh_s); with FLAG_A16 or FLAG_NVFP4 in the plan's flags, h_q holds the bf16
+    SwiGLU rows (int16 [P, I]) and x_q, x_s, h_s are left as allocated.
+    With FLAG_NVFP4 (moe_ffn_nvfp4) the weights dict holds NVFP4 tensors: w13 / w2
+    codes (packed), w13_s [E, 2I, H/16] / w2_s [E, H, I/16] E4M3 block scales and
+    w13_gs / w2_gs [E] float32 tensor scales. ``events``: optional StageEvents recorded at the stage boundaries.
     ``static``: call moe_ffn_static (the library's static scratch instead of a
     workspace; ``ws`` must then be None)."""
     d = p.dims
@@ -261,10 +268,17 @@ def ffn(x: torch.Tensor, topk_weights: torch.Tensor, p: Plan, weights: dict, sha
     _require(topk_weights, torch.float32, (T, K), "topk_weights")
     if weights.get("layout") != "packed":
         raise ValueError("moe_ffn reads expert weights in the kernel-native layout: convert them with pack_weights")
+    nv = bool(d.flags & FLAG_NVFP4)
+    blk = 16 if nv else 32
     _require(weights["w13"], torch.uint8, (E, 2 * I, H // 2), "w13")
-    _require(weights["w13_s"], torch.uint8, (E, 2 * I, H // 32), "w13_s")
+    _require(weights["w13_s"], torch.uint8, (E, 2 * I, H // blk), "w13_s")
     _require(weights["w2"], torch.uint8, (E, H, I // 2), "w2")
-    _require(weights["w2_s"], torch.uint8, (E, H, I // 32), "w2_s")
+    _require(weights["w2_s"], torch.uint8, (E, H, I // blk), "w2_s")
+    if nv:
+        _require(weights["w13_gs"], torch.float32, (E,), "w13_gs")
+        _require(weights["w2_gs"], torch.float32, (E,), "w2_gs")
+        if static or (shared is not None and Is > 0):
+            raise ValueError("NVFP4 weights run through moe_ffn_nvfp4: no static scratch, no shared expert")
     sh = None
     if shared is not None and Is > 0:
         _require(shared["w13s"], torch.uint8, (2 * Is, H), "w13s")
@@ -288,7 +302,8 @@ def ffn(x: torch.Tensor, topk_weights: torch.Tensor, p: Plan, weights: dict, sha
             P = T * K
             dbg_t = {"x_q": torch.empty((T, H), dtype=torch.uint8, device=dev),
                      "x_s": torch.empty((T, H // 128), dtype=torch.uint8, device=dev),
-                     "h_q": torch.zeros((max(P, 1), I), dtype=torch.int16 if d.flags & FLAG_A16 else torch.uint8,
+                     "h_q": torch.zeros((max(P, 1), I),
+                                        dtype=torch.int16 if d.flags & (FLAG_A16 | FLAG_NVFP4) else torch.uint8,
                                         device=dev),
                      "h_s": torch.zeros((max(P, 1), I // 128), dtype=torch.uint8, device=dev),
                      "sh_q": torch.zeros((T, max(Is, 128)), dtype=torch.uint8, device=dev),
@@ -302,7 +317,14 @@ def ffn(x: torch.Tensor, topk_weights: torch.Tensor, p: Plan, weights: dict, sha
             _ptr(p.pair_rows), _ptr(p.ws), _ptr(weights["w13"]), _ptr(weights["w13_s"]), _ptr(weights["w2"]),
             _ptr(weights["w2_s"]), ctypes.byref(sh) if sh is not None else None, _ptr(y),
             ctypes.byref(dbg) if dbg is not None else None]
-    if static:
+    if nv:
+        _check(lib().moe_ffn_nvfp4(ctypes.byref(d), _ptr(x), _ptr(topk_weights), _ptr(p.expert_offsets),
+                                   _ptr(p.sorted_pairs), _ptr(p.pair_rows), _ptr(p.ws), _ptr(weights["w13"]),
+                                   _ptr(weights["w13_s"]), _ptr(weights["w13_gs"]), _ptr(weights["w2"]),
+                                   _ptr(weights["w2_s"]), _ptr(weights["w2_gs"]), _ptr(y),
+                                   ctypes.byref(dbg) if dbg is not None else None, _ptr(ws), ws.numel(),
+                                   _stream(dev)), "moe_ffn_nvfp4")
+    elif static:
         _check(lib().moe_ffn_static(*args, _stream(dev)), "moe_ffn_static")
     else:
         _check(lib().moe_ffn(*args, _ptr(ws), ws.numel(), _stream(dev)), "moe_ffn")

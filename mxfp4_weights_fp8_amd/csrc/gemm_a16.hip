@@ -20,6 +20,19 @@
 // consecutive bytes of the token row. Every item list of the plan is walked in
 // 16-row tiles: efficient for decode (HBM-bound weight streams), correct for any
 // shape.
+//
+// NVFP4 weights (template flag NV; "Optimization progress report", Optimization
+// 05, runs NVFP4 expert weights as stored): the same E2M1 codes, but one E4M3
+// scale per 16 K elements ([rows, K/16] bytes, row-major) and one fp32 scale per
+// expert tensor (NVIDIA's published NVFP4 layout; the page names the format
+// only). The conversion above takes only the power of two of its scale operand,
+// so a block scale v = f * 2^k (f an integer 8 .. 15, 0 for a zero scale) expands
+// its codes to fp32 with 2^k, multiplies them by f (exact: at most 6 significant
+// bits) and keeps the upper halves as bf16 (exact for the same reason). A lane's
+// 32 K of a step span two 16-blocks (MFMAs u = 0, 1 and u = 2, 3); their two scale
+// bytes come in one 4-byte load per fragment and step, in the same register ring
+// as the codes. The per-tensor scale multiplies the fp32 accumulators before the
+// epilogue (it is constant over the contraction).
 #include "small_unit.h"
 
 namespace moe {
@@ -50,83 +63,145 @@ __device__ __forceinline__ v4i e2m1x8_bf16(uint32_t w, float scale) {
   return r;
 }
 
+typedef float v2f __attribute__((ext_vector_type(2)));
+
+// NVFP4: 8 codes times the block scale f * 2^k (see above) -> 8 bf16, in the layout
+// of e2m1x8_bf16.
+__device__ __forceinline__ v4i e2m1x8_bf16_nv(uint32_t w, float pow2, float f) {
+  v4i r;
+#define NV_PAIR(k)                                                                           \
+  {                                                                                          \
+    const v2f p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, pow2, k);                      \
+    r[k] = (int)__builtin_amdgcn_perm(__float_as_uint(p[1] * f), __float_as_uint(p[0] * f),  \
+                                      0x07060302u);                                          \
+  }
+  NV_PAIR(0) NV_PAIR(1) NV_PAIR(2) NV_PAIR(3)
+#undef NV_PAIR
+  return r;
+}
+
+// An E4M3 block scale (finite, non-negative) as f * 2^k: pow2 = 2^k with
+// k = floor(log2 v) - 3 and f = v / 2^k, an integer 8 .. 15 (v >= 2^-9, the smallest
+// E4M3 subnormal, so k >= -12). A zero scale gives pow2 = 1 and f = 0, so its
+// block expands to zeros (an exponent taken from v = 0 would overflow the codes
+// to infinity first).
+__device__ __forceinline__ void nv_scale(float v, float& pow2, float& f) {
+  const uint32_t b = __float_as_uint(v);
+  const bool zero = v == 0.f;
+  pow2 = zero ? 1.f : __uint_as_float((b & 0x7F800000u) - (3u << 23));
+  f = zero ? 0.f : (float)(8u + ((b >> 20) & 7u));
+}
+
 __device__ __forceinline__ v4f mfma_bf16(v4i a, v4i b, v4f c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a), __builtin_bit_cast(v8bf, b), c, 0, 0, 0);
 }
 
-// Operands of one K step: NF fragments' codes, the token column's 32 bf16.
-template <int NF>
+// Operands of one K step: NF fragments' codes (and, for NVFP4, scale words), the
+// token column's 32 bf16.
+template <int NF, bool NV>
 struct Step16 {
   v4i w[NF];
   v4i x[4];
+  uint32_t sw[NF];
 };
 
 // Where a wave's operands live: weight codes (resource + per-fragment lane offsets,
 // step s at +1024 s), the token rows (resource + lane offset, step s at +256 s), the
-// weight scales in LDS (sl[f]: the lane's row of fragment f, K/32 bytes).
-template <int NF>
+// weight scales: MXFP4 in LDS (sl[f]: the lane's row of fragment f, K/32 bytes),
+// NVFP4 in memory (resource + per-fragment lane offsets of the 4-byte word holding
+// the lane's two block scales, step s at +8 s).
+template <int NF, bool NV>
 struct Stream16 {
-  rsrc_t w, x;
+  rsrc_t w, x, s;
   int wo[NF];
+  int so[NF];
   int xo;
   const uint8_t* sl[NF];
 };
 
-template <int NF>
-__device__ __forceinline__ void load16(Step16<NF>& r, const Stream16<NF>& p, int s) {
+template <int NF, bool NV>
+__device__ __forceinline__ void load16(Step16<NF, NV>& r, const Stream16<NF, NV>& p, int s) {
 #pragma unroll
   for (int f = 0; f < NF; ++f) r.w[f] = buf_load16_nt(p.w, p.wo[f], s * 1024);
+  if constexpr (NV) {
+#pragma unroll
+    for (int f = 0; f < NF; ++f) r.sw[f] = (uint32_t)buf_load4(p.s, p.so[f], s * 8);
+  }
 #pragma unroll
   for (int u = 0; u < 4; ++u) r.x[u] = buf_load16(p.x, p.xo, s * 256 + 16 * u);
 }
 
-// One K step: sc[f] is the scale (as a float) of fragment f's lane's block.
-template <int NF>
-__device__ __forceinline__ void mma16(const Step16<NF>& r, const float* sc, v4f* acc) {
+// One K step. MXFP4: sc[f] is the scale (as a float) of fragment f's lane's block.
+// NVFP4: the lane's two block scales come from r.sw (bytes 2 (q & 1) and +1).
+template <int NF, bool NV>
+__device__ __forceinline__ void mma16(const Step16<NF, NV>& r, const float* sc, int q, v4f* acc) {
+  if constexpr (NV) {
+    float p2[NF][2], fm[NF][2];
 #pragma unroll
-  for (int u = 0; u < 4; ++u)
+    for (int f = 0; f < NF; ++f) {
+      const uint32_t w = r.sw[f] >> (16 * (q & 1));
+      nv_scale(__builtin_amdgcn_cvt_f32_fp8((int)w, 0), p2[f][0], fm[f][0]);
+      nv_scale(__builtin_amdgcn_cvt_f32_fp8((int)w, 1), p2[f][1], fm[f][1]);
+    }
 #pragma unroll
-    for (int f = 0; f < NF; ++f) acc[f] = mfma_bf16(e2m1x8_bf16((uint32_t)r.w[f][u], sc[f]), r.x[u], acc[f]);
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int f = 0; f < NF; ++f)
+        acc[f] = mfma_bf16(e2m1x8_bf16_nv((uint32_t)r.w[f][u], p2[f][u >> 1], fm[f][u >> 1]), r.x[u], acc[f]);
+  } else {
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int f = 0; f < NF; ++f) acc[f] = mfma_bf16(e2m1x8_bf16((uint32_t)r.w[f][u], sc[f]), r.x[u], acc[f]);
+  }
+}
+
+template <int NF, bool NV>
+__device__ __forceinline__ void step_scales(const Stream16<NF, NV>& p, int s, int q, float* sc) {
+  if constexpr (!NV) {
+#pragma unroll
+    for (int f = 0; f < NF; ++f) sc[f] = e8m0_float(p.sl[f][4 * s + q]);
+  }
 }
 
 // acc[f] += sum over KS steps of 128 K. Four steps of codes in flight in a register
 // ring (prefetch indices clamped, so the loop is branch-free; KS a multiple of 4),
 // else one step at a time. The weight-scale copies into LDS are waited for first.
-template <int NF>
-__device__ __forceinline__ void stream16(v4f* acc, const Stream16<NF>& p, int KS, int q) {
+template <int NF, bool NV>
+__device__ __forceinline__ void stream16(v4f* acc, const Stream16<NF, NV>& p, int KS, int q) {
   float sc[NF];
   if (KS % kQ != 0) {
     wait_vmcnt<0>();
     for (int s = 0; s < KS; ++s) {
-      Step16<NF> r;
+      Step16<NF, NV> r;
       load16(r, p, s);
-#pragma unroll
-      for (int f = 0; f < NF; ++f) sc[f] = e8m0_float(p.sl[f][4 * s + q]);
-      mma16(r, sc, acc);
+      step_scales(p, s, q, sc);
+      mma16(r, sc, q, acc);
     }
     return;
   }
-  Step16<NF> buf[kQ];
+  Step16<NF, NV> buf[kQ];
 #pragma unroll
   for (int d = 0; d < kQ; ++d) load16(buf[d], p, d);
   wait_vmcnt<0>();
   for (int s0 = 0; s0 < KS; s0 += kQ) {
 #pragma unroll
     for (int d = 0; d < kQ; ++d) {
-#pragma unroll
-      for (int f = 0; f < NF; ++f) sc[f] = e8m0_float(p.sl[f][4 * (s0 + d) + q]);
-      mma16(buf[d], sc, acc);
+      step_scales(p, s0 + d, q, sc);
+      mma16(buf[d], sc, q, acc);
       load16(buf[d], p, min(s0 + kQ + d, KS - 1));
     }
   }
 }
 
 // W13 unit: 128 h columns (nb) of one item, 8 waves x (one gate + one up fragment).
+// gs: NVFP4's per-expert tensor scales (unused for MXFP4).
+template <bool NV>
 __global__ __launch_bounds__(kW13Waves * 64) void k_w13_a16(
     const SmallLists lists, const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_pairs,
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ w13, const uint8_t* __restrict__ w13_s,
-    uint16_t* __restrict__ h, int H, int I, int K) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t sS[];   // per wave: 2 runs of 16 rows x H/32
+    const float* __restrict__ gs, uint16_t* __restrict__ h, int H, int I, int K) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t sS[];   // MXFP4: per wave 2 runs of 16 rows x H/32
   const int l = blockIdx.y >= lists.cap0;
   const int item = blockIdx.y - (l ? lists.cap0 : 0);
   if (item >= lists.n_items[l][0]) return;
@@ -138,19 +213,29 @@ __global__ __launch_bounds__(kW13Waves * 64) void k_w13_a16(
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63, q = lane >> 4, c = lane & 15;
   const int KS = H / 128;
-  const int64_t wrow = H / 2, srow = H / 32;
+  const int64_t wrow = H / 2;
 
-  Stream16<2> p;
+  Stream16<2, NV> p;
   p.w = make_rsrc(w13 + (int64_t)e * 2 * I * wrow, (uint32_t)(2 * I * wrow));
   p.x = make_rsrc(x, 0xFFFFFFFFu);
   const int n_gate = nb * 128 + wave * 16;   // first gate row of the wave; up row I + n_gate
-  const int run = staged_bytes(16 * (int)srow);
-  stage_scales(w13_s + ((int64_t)e * 2 * I + n_gate) * srow, w13_s + ((int64_t)e * 2 * I + I + n_gate) * srow,
-               16 * (int)srow, sS + wave * 2 * run, lane);
   p.wo[0] = n_gate * (int)wrow + lane * 16;
   p.wo[1] = (I + n_gate) * (int)wrow + lane * 16;
-  p.sl[0] = sS + wave * 2 * run + c * srow;
-  p.sl[1] = sS + wave * 2 * run + run + c * srow;
+  float g_scale = 1.f;
+  if constexpr (NV) {
+    const int64_t srow = H / 16;
+    p.s = make_rsrc(w13_s + (int64_t)e * 2 * I * srow, (uint32_t)(2 * I * srow));
+    p.so[0] = (n_gate + c) * (int)srow + 4 * (q >> 1);
+    p.so[1] = (I + n_gate + c) * (int)srow + 4 * (q >> 1);
+    g_scale = gs[e];
+  } else {
+    const int64_t srow = H / 32;
+    const int run = staged_bytes(16 * (int)srow);
+    stage_scales(w13_s + ((int64_t)e * 2 * I + n_gate) * srow, w13_s + ((int64_t)e * 2 * I + I + n_gate) * srow,
+                 16 * (int)srow, sS + wave * 2 * run, lane);
+    p.sl[0] = sS + wave * 2 * run + c * srow;
+    p.sl[1] = sS + wave * 2 * run + run + c * srow;
+  }
 
   for (int m0 = it.y; m0 < it.y + item_rows && e_begin + m0 < e_end; m0 += kSmallRows) {
     const int row0 = e_begin + m0;
@@ -159,7 +244,14 @@ __global__ __launch_bounds__(kW13Waves * 64) void k_w13_a16(
     const int tok = sorted_pairs[row0 + (has ? c : 0)] / K;   // an absent column repeats the first row
     p.xo = (tok * H + 32 * q) * 2;
     v4f acc[2] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};
-    stream16<2>(acc, p, KS, q);
+    stream16<2, NV>(acc, p, KS, q);
+    if constexpr (NV) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[0][i] *= g_scale;
+        acc[1][i] *= g_scale;
+      }
+    }
     // lane (c, q): h columns n_gate + 4q .. +3 of routed row c, as bf16
     if (has) {
       uint16_t* dst = h + (int64_t)(row0 + c) * I + n_gate + 4 * q;
@@ -174,12 +266,13 @@ __global__ __launch_bounds__(kW13Waves * 64) void k_w13_a16(
 
 // W2 unit: 128 output columns of one item, 4 waves x two fragments; per-pair rows as
 // fp16 codes with one power-of-two scale per 32 columns (the wave's two fragments).
+template <bool NV>
 __global__ __launch_bounds__(kW2Waves * 64) void k_w2_a16(
     const SmallLists lists, const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_pairs,
     const uint16_t* __restrict__ h, const uint8_t* __restrict__ w2, const uint8_t* __restrict__ w2_s,
-    uint16_t* __restrict__ o, uint8_t* __restrict__ os, int H, int I) {
+    const float* __restrict__ gs, uint16_t* __restrict__ o, uint8_t* __restrict__ os, int H, int I) {
   constexpr int NF = 2;
-  extern __shared__ __attribute__((aligned(16))) uint8_t sS[];   // per wave: 32 rows x I/32
+  extern __shared__ __attribute__((aligned(16))) uint8_t sS[];   // MXFP4: per wave 32 rows x I/32
   const int l = blockIdx.y >= lists.cap0;
   const int item = blockIdx.y - (l ? lists.cap0 : 0);
   if (item >= lists.n_items[l][0]) return;
@@ -192,17 +285,26 @@ __global__ __launch_bounds__(kW2Waves * 64) void k_w2_a16(
   const int n_wave = blockIdx.x * 64 * NF + wave * 16 * NF;
   if (n_wave >= H) return;
   const int KS = I / 128;
-  const int64_t wrow = I / 2, srow = I / 32;
+  const int64_t wrow = I / 2;
 
-  Stream16<NF> p;
+  Stream16<NF, NV> p;
   p.w = make_rsrc(w2 + (int64_t)e * H * wrow, (uint32_t)(H * wrow));
   p.x = make_rsrc(h, 0xFFFFFFFFu);
-  const int run = staged_bytes(16 * NF * (int)srow);
-  stage_scales(w2_s + ((int64_t)e * H + n_wave) * srow, nullptr, 16 * NF * (int)srow, sS + wave * run, lane);
 #pragma unroll
-  for (int f = 0; f < NF; ++f) {
-    p.wo[f] = (n_wave + f * 16) * (int)wrow + lane * 16;
-    p.sl[f] = sS + wave * run + (f * 16 + c) * srow;
+  for (int f = 0; f < NF; ++f) p.wo[f] = (n_wave + f * 16) * (int)wrow + lane * 16;
+  float g_scale = 1.f;
+  if constexpr (NV) {
+    const int64_t srow = I / 16;
+    p.s = make_rsrc(w2_s + (int64_t)e * H * srow, (uint32_t)(H * srow));
+#pragma unroll
+    for (int f = 0; f < NF; ++f) p.so[f] = (n_wave + f * 16 + c) * (int)srow + 4 * (q >> 1);
+    g_scale = gs[e];
+  } else {
+    const int64_t srow = I / 32;
+    const int run = staged_bytes(16 * NF * (int)srow);
+    stage_scales(w2_s + ((int64_t)e * H + n_wave) * srow, nullptr, 16 * NF * (int)srow, sS + wave * run, lane);
+#pragma unroll
+    for (int f = 0; f < NF; ++f) p.sl[f] = sS + wave * run + (f * 16 + c) * srow;
   }
 
   for (int m0 = it.y; m0 < it.y + item_rows && e_begin + m0 < e_end; m0 += kSmallRows) {
@@ -212,12 +314,15 @@ __global__ __launch_bounds__(kW2Waves * 64) void k_w2_a16(
     const int hrow = row0 + (has ? c : 0);
     p.xo = (hrow * I + 32 * q) * 2;
     v4f acc[NF] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};
-    stream16<NF>(acc, p, KS, q);
+    stream16<NF, NV>(acc, p, KS, q);
     float m = 0.f;
 #pragma unroll
     for (int f = 0; f < NF; ++f)
 #pragma unroll
-      for (int k = 0; k < 4; ++k) m = fmaxf(m, fabsf(acc[f][k]));
+      for (int k = 0; k < 4; ++k) {
+        if constexpr (NV) acc[f][k] *= g_scale;
+        m = fmaxf(m, fabsf(acc[f][k]));
+      }
     m = fmaxf(m, __shfl_xor(m, 16));
     m = fmaxf(m, __shfl_xor(m, 32));
     const int ex = o_exponent(m);
@@ -238,23 +343,35 @@ __global__ __launch_bounds__(kW2Waves * 64) void k_w2_a16(
 
 hipError_t launch_w13_a16(const moe_dims& d, const SmallLists& lists, const int32_t* offsets,
                           const int32_t* sorted_pairs, const uint16_t* x, const uint8_t* w13, const uint8_t* w13_s,
-                          uint16_t* h, hipStream_t s) {
+                          const float* w13_gs, uint16_t* h, hipStream_t s) {
   const int64_t max_items = (int64_t)lists.cap0 + lists.cap1;
   if (max_items <= 0) return hipSuccess;
-  const size_t lds = (size_t)kW13Waves * 2 * staged_bytes(16 * (d.H / 32));
-  hipLaunchKernelGGL(k_w13_a16, dim3(d.I / 128, (unsigned)max_items), dim3(kW13Waves * 64), lds, s, lists, offsets,
-                     sorted_pairs, x, w13, w13_s, h, d.H, d.I, d.K);
+  const dim3 grid(d.I / 128, (unsigned)max_items), block(kW13Waves * 64);
+  if (w13_gs) {
+    hipLaunchKernelGGL(k_w13_a16<true>, grid, block, 0, s, lists, offsets, sorted_pairs, x, w13, w13_s, w13_gs, h,
+                       d.H, d.I, d.K);
+  } else {
+    const size_t lds = (size_t)kW13Waves * 2 * staged_bytes(16 * (d.H / 32));
+    hipLaunchKernelGGL(k_w13_a16<false>, grid, block, lds, s, lists, offsets, sorted_pairs, x, w13, w13_s, nullptr,
+                       h, d.H, d.I, d.K);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_w2_a16(const moe_dims& d, const SmallLists& lists, const int32_t* offsets,
                          const int32_t* sorted_pairs, const uint16_t* h, const uint8_t* w2, const uint8_t* w2_s,
-                         uint16_t* o, uint8_t* os, hipStream_t s) {
+                         const float* w2_gs, uint16_t* o, uint8_t* os, hipStream_t s) {
   const int64_t max_items = (int64_t)lists.cap0 + lists.cap1;
   if (max_items <= 0) return hipSuccess;
-  const size_t lds = (size_t)kW2Waves * staged_bytes(16 * 2 * (d.I / 32));
-  hipLaunchKernelGGL(k_w2_a16, dim3((unsigned)ceil_div(d.H, 128), (unsigned)max_items), dim3(kW2Waves * 64), lds, s,
-                     lists, offsets, sorted_pairs, h, w2, w2_s, o, os, d.H, d.I);
+  const dim3 grid((unsigned)ceil_div(d.H, 128), (unsigned)max_items), block(kW2Waves * 64);
+  if (w2_gs) {
+    hipLaunchKernelGGL(k_w2_a16<true>, grid, block, 0, s, lists, offsets, sorted_pairs, h, w2, w2_s, w2_gs, o, os,
+                       d.H, d.I);
+  } else {
+    const size_t lds = (size_t)kW2Waves * staged_bytes(16 * 2 * (d.I / 32));
+    hipLaunchKernelGGL(k_w2_a16<false>, grid, block, lds, s, lists, offsets, sorted_pairs, h, w2, w2_s, nullptr, o,
+                       os, d.H, d.I);
+  }
   return hipGetLastError();
 }
 

@@ -63,6 +63,10 @@ struct PlanWs {
 size_t plan_ws_layout(const moe_dims& d, void* base, PlanWs* out);
 
 // ---------------------------------------------------------------- ffn workspace
+// Activations and SwiGLU rows stay bf16 (no FP8 quantization): MOE_FLAG_A16 and
+// MOE_FLAG_NVFP4.
+inline bool bf16_rows(const moe_dims& d) { return (d.flags & (MOE_FLAG_A16 | MOE_FLAG_NVFP4)) != 0; }
+
 struct FfnWs {
   uint8_t* x_q;   // [T, H]
   uint8_t* x_s;   // [T, H/128]
@@ -154,14 +158,16 @@ hipError_t launch_shared13_bf16(const moe_dims& d, const uint16_t* x_hat, const 
                                 uint16_t* w13s_bf16, uint8_t* sh_q, uint8_t* sh_s, hipStream_t s);
 hipError_t launch_shared2(const moe_dims& d, const uint8_t* sh_q, const uint8_t* sh_s, const uint8_t* w2s,
                           const uint8_t* w2s_s, uint16_t* so, uint8_t* sos, hipStream_t s);
-// MXFP4 x bf16 activations (MOE_FLAG_A16): x [T, H] bf16 -> h [P, I] bf16 (SwiGLU
-// output, rows in plan order) -> per-pair rows; every item walked in 16-row tiles.
+// 4-bit weights x bf16 activations (MOE_FLAG_A16, MOE_FLAG_NVFP4): x [T, H] bf16 ->
+// h [P, I] bf16 (SwiGLU output, rows in plan order) -> per-pair rows; every item
+// walked in 16-row tiles. *_gs null: MXFP4 (E8M0 per 32); else NVFP4 (E4M3 per 16
+// and these per-expert fp32 tensor scales).
 hipError_t launch_w13_a16(const moe_dims& d, const SmallLists& lists, const int32_t* offsets,
                           const int32_t* sorted_pairs, const uint16_t* x, const uint8_t* w13, const uint8_t* w13_s,
-                          uint16_t* h, hipStream_t s);
+                          const float* w13_gs, uint16_t* h, hipStream_t s);
 hipError_t launch_w2_a16(const moe_dims& d, const SmallLists& lists, const int32_t* offsets,
                          const int32_t* sorted_pairs, const uint16_t* h, const uint8_t* w2, const uint8_t* w2_s,
-                         uint16_t* o, uint8_t* os, hipStream_t s);
+                         const float* w2_gs, uint16_t* o, uint8_t* os, hipStream_t s);
 // The persistent decode chain (W13 + SwiGLU/requant, W2 and the combine in one
 // launch, per-expert and per-column-block counters in `sync`, which must be zero):
 // used when every item can be walked in 16-row tiles, T*K <= kFoldPairs.

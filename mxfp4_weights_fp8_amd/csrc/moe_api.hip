@@ -17,7 +17,7 @@ size_t ffn_ws_layout(const moe_dims& d, void* base, FfnWs* out) {
   };
   const size_t o_xq = take((size_t)(T * H));
   const size_t o_xs = take((size_t)(T * H / 128));
-  const size_t o_hq = take((size_t)(P * I) * ((d.flags & MOE_FLAG_A16) ? 2 : 1));   // A16: bf16 rows
+  const size_t o_hq = take((size_t)(P * I) * (bf16_rows(d) ? 2 : 1));   // bf16 activations: bf16 rows
   const size_t o_hs = take((size_t)(P * I / 128));
   const size_t o_o = take(sizeof(uint16_t) * (size_t)(P * H));
   const size_t o_os = take((size_t)(P * H / 32));
@@ -52,7 +52,7 @@ namespace {
 int validate(const moe_dims* d) {
   if (!d) return MOE_EINVAL;
   if (d->T < 0 || d->H <= 0 || d->I <= 0 || d->E < 1 || d->E > kMaxExperts || d->K < 1 || d->K > kMaxTopK ||
-      d->Is < 0 || d->small_max < 0 || (d->flags & ~(MOE_FLAG_DECODE_CHAIN | MOE_FLAG_A16)) != 0)
+      d->Is < 0 || d->small_max < 0 || (d->flags & ~(MOE_FLAG_DECODE_CHAIN | MOE_FLAG_A16 | MOE_FLAG_NVFP4)) != 0)
     return MOE_EINVAL;
   if (d->H % 128 || d->I % 128 || d->Is % 128) return MOE_EUNSUPPORTED;
   if ((int64_t)d->T * d->K > (int64_t)1 << 30) return MOE_EUNSUPPORTED;
@@ -66,7 +66,7 @@ int validate(const moe_dims* d) {
       (int64_t)d->T * d->Is >= lim)
     return MOE_EUNSUPPORTED;
   // bf16 activations: no shared expert; 2-byte activation and SwiGLU rows
-  if ((d->flags & MOE_FLAG_A16) && (d->Is > 0 || 2 * (int64_t)d->T * d->H >= lim || 2 * (int64_t)d->T * d->K * d->I >= lim))
+  if (bf16_rows(*d) && (d->Is > 0 || 2 * (int64_t)d->T * d->H >= lim || 2 * (int64_t)d->T * d->K * d->I >= lim))
     return MOE_EUNSUPPORTED;
   return MOE_OK;
 }
@@ -134,7 +134,7 @@ int moe_pack_weights(const moe_dims* dims, const uint8_t* w13, uint8_t* w13_pack
 namespace moe {
 namespace {
 
-// Argument checks of moe_ffn / moe_ffn_static that need no workspace.
+// Argument checks of moe_ffn / moe_ffn_static / moe_ffn_nvfp4 that need no workspace.
 int ffn_args(const moe_dims* dims, const uint16_t* x, const float* topk_weights, const int32_t* expert_offsets,
              const int32_t* sorted_pairs, const int32_t* pair_rows, const void* plan_ws, const uint8_t* w13,
              const uint8_t* w13_s, const uint8_t* w2, const uint8_t* w2_s, const moe_shared* shared,
@@ -155,10 +155,12 @@ int ffn_args(const moe_dims* dims, const uint16_t* x, const float* topk_weights,
 
 // The launch sequence of the FFN on a checked argument set and a workspace of at
 // least ffn_ws_layout(d) bytes.
+// w13_gs / w2_gs: NVFP4's per-expert tensor scales (null for MXFP4 weights).
 int ffn_enqueue(const moe_dims& d, const uint16_t* x, const float* topk_weights, const int32_t* expert_offsets,
                 const int32_t* sorted_pairs, const int32_t* pair_rows, const void* plan_ws, const uint8_t* w13,
                 const uint8_t* w13_s, const uint8_t* w2, const uint8_t* w2_s, const moe_shared* shared, uint16_t* y,
-                const moe_debug* dbg, void* ws, hipStream_t s) {
+                const moe_debug* dbg, void* ws, hipStream_t s, const float* w13_gs = nullptr,
+                const float* w2_gs = nullptr) {
   const bool use_shared = shared != nullptr && d.Is > 0;
   FfnWs fw;
   ffn_ws_layout(d, ws, &fw);
@@ -170,7 +172,7 @@ int ffn_enqueue(const moe_dims& d, const uint16_t* x, const float* topk_weights,
   uint8_t* h_s = dbg && dbg->h_s ? dbg->h_s : fw.h_s;
 
   const int64_t P = (int64_t)d.T * d.K;
-  if (d.flags & MOE_FLAG_A16) {
+  if (bf16_rows(d)) {
     // bf16 activations: no quantization; every item list walked in 16-row tiles
     uint16_t* h = dbg && dbg->h_q ? reinterpret_cast<uint16_t*>(dbg->h_q) : reinterpret_cast<uint16_t*>(fw.h_q);
     SmallLists sl = small_lists(pw.small_items, pw.hdr + 0, pw.small_cap, kSmallRows);
@@ -181,14 +183,14 @@ int ffn_enqueue(const moe_dims& d, const uint16_t* x, const float* topk_weights,
     const SmallLists sxl = small_lists(pw.xl_items, pw.hdr + 2, pw.xl_cap, kXlRows);
     record(dbg, MOE_EV_START, s);
     record(dbg, MOE_EV_QUANT_DONE, s);
-    hipError_t err = launch_w13_a16(d, sl, expert_offsets, sorted_pairs, x, w13, w13_s, h, s);
+    hipError_t err = launch_w13_a16(d, sl, expert_offsets, sorted_pairs, x, w13, w13_s, w13_gs, h, s);
     if (err == hipSuccess && P > kXlRows / 2)
-      err = launch_w13_a16(d, sxl, expert_offsets, sorted_pairs, x, w13, w13_s, h, s);
+      err = launch_w13_a16(d, sxl, expert_offsets, sorted_pairs, x, w13, w13_s, w13_gs, h, s);
     if (err != hipSuccess) return MOE_EHIP;
     record(dbg, MOE_EV_W13_DONE, s);
-    err = launch_w2_a16(d, sl, expert_offsets, sorted_pairs, h, w2, w2_s, fw.o, fw.os, s);
+    err = launch_w2_a16(d, sl, expert_offsets, sorted_pairs, h, w2, w2_s, w2_gs, fw.o, fw.os, s);
     if (err == hipSuccess && P > kXlRows / 2)
-      err = launch_w2_a16(d, sxl, expert_offsets, sorted_pairs, h, w2, w2_s, fw.o, fw.os, s);
+      err = launch_w2_a16(d, sxl, expert_offsets, sorted_pairs, h, w2, w2_s, w2_gs, fw.o, fw.os, s);
     if (err != hipSuccess) return MOE_EHIP;
     record(dbg, MOE_EV_W2_DONE, s);
     record(dbg, MOE_EV_SHARED_DONE, s);
@@ -355,6 +357,7 @@ int moe_ffn(const moe_dims* dims, const uint16_t* x, const float* topk_weights, 
             const moe_debug* dbg, void* ws, size_t ws_bytes, void* stream) {
   int rc = ffn_args(dims, x, topk_weights, expert_offsets, sorted_pairs, pair_rows, plan_ws, w13, w13_s, w2, w2_s,
                     shared, y);
+  if (rc == MOE_OK && (dims->flags & MOE_FLAG_NVFP4)) return MOE_EINVAL;   // needs moe_ffn_nvfp4's tensor scales
   if (rc != MOE_OK || dims->T == 0) return rc;
   if (!ws) return MOE_EINVAL;
   if (ws_bytes < ffn_ws_layout(*dims, nullptr, nullptr)) return MOE_EWORKSPACE;
@@ -368,6 +371,7 @@ int moe_ffn_static(const moe_dims* dims, const uint16_t* x, const float* topk_we
                    const uint8_t* w2_s, const moe_shared* shared, uint16_t* y, const moe_debug* dbg, void* stream) {
   int rc = ffn_args(dims, x, topk_weights, expert_offsets, sorted_pairs, pair_rows, plan_ws, w13, w13_s, w2, w2_s,
                     shared, y);
+  if (rc == MOE_OK && (dims->flags & MOE_FLAG_NVFP4)) return MOE_EINVAL;
   if (rc != MOE_OK || dims->T == 0) return rc;
   if (ffn_ws_layout(*dims, nullptr, nullptr) > kStaticScratchBytes) return MOE_ESCRATCH;
   hipError_t err;
@@ -377,6 +381,20 @@ int moe_ffn_static(const moe_dims* dims, const uint16_t* x, const float* topk_we
   // nothing is cleared
   return ffn_enqueue(*dims, x, topk_weights, expert_offsets, sorted_pairs, pair_rows, plan_ws, w13, w13_s, w2, w2_s,
                      shared, y, dbg, ws, (hipStream_t)stream);
+}
+
+int moe_ffn_nvfp4(const moe_dims* dims, const uint16_t* x, const float* topk_weights, const int32_t* expert_offsets,
+                  const int32_t* sorted_pairs, const int32_t* pair_rows, const void* plan_ws, const uint8_t* w13,
+                  const uint8_t* w13_s, const float* w13_gs, const uint8_t* w2, const uint8_t* w2_s,
+                  const float* w2_gs, uint16_t* y, const moe_debug* dbg, void* ws, size_t ws_bytes, void* stream) {
+  int rc = ffn_args(dims, x, topk_weights, expert_offsets, sorted_pairs, pair_rows, plan_ws, w13, w13_s, w2, w2_s,
+                    nullptr, y);
+  if (rc == MOE_OK && !(dims->flags & MOE_FLAG_NVFP4)) return MOE_EINVAL;
+  if (rc != MOE_OK || dims->T == 0) return rc;
+  if (!w13_gs || !w2_gs || !ws) return MOE_EINVAL;
+  if (ws_bytes < ffn_ws_layout(*dims, nullptr, nullptr)) return MOE_EWORKSPACE;
+  return ffn_enqueue(*dims, x, topk_weights, expert_offsets, sorted_pairs, pair_rows, plan_ws, w13, w13_s, w2, w2_s,
+                     nullptr, y, dbg, ws, (hipStream_t)stream, w13_gs, w2_gs);
 }
 
 const char* moe_status_string(int code) {

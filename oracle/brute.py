@@ -117,6 +117,17 @@ def mxfp4_row(codes_row, scales_row):
     return out
 
 
+def nvfp4_row(codes_row, scales_row, tensor_scale):
+    """Packed NVFP4 row (E4M3 scale per 16) times the tensor scale -> Fractions."""
+    out = []
+    gs = Fraction(float(tensor_scale))
+    for byte in codes_row:
+        for nib in (int(byte) & 15, int(byte) >> 4):
+            k = len(out)
+            out.append(e2m1(nib) * e4m3(int(scales_row[k // 16])) * gs)
+    return out
+
+
 def fp8_block_row(codes_row, scales_grid, n: int):
     """FP8 weight row n with 128x128 block scales -> list of Fractions."""
     return [e4m3(int(c)) * Fraction(2) ** (int(scales_grid[n // 128][k // 128]) - 127)
@@ -203,3 +214,36 @@ def brute_ref(x_bits, topk_ids, topk_weights, w13, w13_s, w2, w2_s, shared=None,
         for n in range(H):
             y[t, n] = math.fsum(terms[n])
     return {"y": y, "h_q": hq_all, "h_s": hs_all}
+
+
+def brute_ref_nvfp4(x_bits, topk_ids, topk_weights, w13, w13_s, w13_gs, w2, w2_s, w2_gs):
+    """Same contract as ``moe.ffn_ref_nvfp4`` (all tokens), written from the
+    element definitions: every weight is E2M1 x E4M3 x tensor scale as an exact
+    fraction (its float has at most 30 significant bits, so every product with a
+    bf16 activation is exact in float64), dots by fsum, bf16 rounding by bisection."""
+    x_bits = np.asarray(x_bits, dtype=np.uint16)
+    T, H = x_bits.shape
+    K = topk_ids.shape[1]
+    E = w13.shape[0]
+    I = w2.shape[2] * 2
+    y = np.zeros((T, H))
+    hq_all = np.zeros((T, K, I), dtype=np.uint16)
+    cache = {}
+    for t in range(T):
+        xh = [float(bf16_value(int(b) & 0x7FFF)) * (-1.0 if int(b) & 0x8000 else 1.0) for b in x_bits[t]]
+        terms = [[] for _ in range(H)]
+        for j in range(K):
+            e = int(topk_ids[t, j])
+            if not (0 <= e < E):
+                continue
+            if e not in cache:
+                cache[e] = (_floats(nvfp4_row(w13[e, n], w13_s[e, n], w13_gs[e]) for n in range(2 * I)),
+                            _floats(nvfp4_row(w2[e, n], w2_s[e, n], w2_gs[e]) for n in range(H)))
+            o, hq, _ = _expert(xh, cache[e][0], cache[e][1], I, "bf16")
+            hq_all[t, j] = hq
+            wt = float(topk_weights[t, j])
+            for n in range(H):
+                terms[n].append(wt * o[n])
+        for n in range(H):
+            y[t, n] = math.fsum(terms[n])
+    return {"y": y, "h_q": hq_all}

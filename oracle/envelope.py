@@ -330,3 +330,40 @@ def routed_swiglu_envelope_a16(x_bits, w13, w13_s, I, tok, col, chunk: int = 512
         h[sl] = silu_mul(dots[0], dots[1])
         err[sl] = swiglu_bound(dots[0], dots[1], bounds[0], bounds[1])
     return h, err
+
+
+def _nvfp4_rows(w, w_s, rows):
+    """Exact values of NVFP4 weight rows without the tensor scale (codes [N, K/2],
+    low nibble = even K; one E4M3 scale per 16 along K)."""
+    c = np.asarray(w)[rows]
+    codes = np.empty(c.shape[:-1] + (2 * c.shape[-1],), dtype=np.int64)
+    codes[..., 0::2] = c & 0xF
+    codes[..., 1::2] = c >> 4
+    s = np.repeat(E4M3_VALUES[np.asarray(w_s)[rows].astype(np.int64)], 16, axis=-1)
+    return E2M1_VALUES[codes] * s
+
+
+def routed_swiglu_envelope_nvfp4(x_bits, w13, w13_s, gs, I, tok, col, chunk: int = 512):
+    """NVFP4 weights, bf16 activations: exact h = silu(g) u with g, u = gs * (x . W')
+    and a rigorous bound on a GPU that sums x . W' with the bf16 MFMA (the block
+    scaled codes are exact bf16 values; 128-K steps of four instructions in any
+    split), multiplies by the tensor scale gs in fp32 and evaluates SwiGLU in fp32."""
+    tok = np.asarray(tok, np.int64)
+    col = np.asarray(col, np.int64)
+    xall = np.asarray(x_bits, dtype=np.uint16)
+    gs = float(gs)
+    h = np.zeros(tok.size)
+    err = np.zeros(tok.size)
+    for s in range(0, tok.size, chunk):
+        sl = slice(s, s + chunk)
+        xv = (xall[tok[sl]].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        dots, bounds = [], []
+        for rows in (col[sl], col[sl] + I):
+            p = xv * _nvfp4_rows(w13, w13_s, rows)
+            d = p.sum(-1)                                # exact
+            b = bf16_dot_bound(p, span=128)
+            dots.append(gs * d)
+            bounds.append(abs(gs) * b + FP32_ULP * abs(gs) * (np.abs(d) + b))
+        h[sl] = silu_mul(dots[0], dots[1])
+        err[sl] = swiglu_bound(dots[0], dots[1], bounds[0], bounds[1])
+    return h, err

@@ -26,6 +26,15 @@ Reading: the page names the variant only; 16-bit activations mean the operands o
 both GEMMs are bf16, and the SwiGLU output is rounded once where it becomes W2's
 operand, as in the FP8 form where that is the FP8 quantization.
 
+NVFP4 weights (``ffn_ref_nvfp4``; "Optimization progress report", Optimization
+05: NVFP4 expert weights consumed as stored). The page names the format only; it
+is NVIDIA's published NVFP4: E2M1 codes, one E4M3 scale per 16 consecutive
+elements and one fp32 scale per tensor (here per expert and projection),
+w = E2M1 * E4M3 * tensor scale. Reading: activations bf16 as in the variant
+above (the page names no activation format). The tensor scale is constant over
+each contraction, so it multiplies the exact dot product once; that keeps the
+GEMMs exact (E2M1 * E4M3 has at most 6 significant bits).
+
 Exactness: a product of an E4M3 value (4 significant bits) and an E2M1 value
 (2 significant bits) times power-of-two scales has at most 6 significant bits,
 and a dot product over 7168 such terms spans far fewer than float64's 53 bits
@@ -112,6 +121,16 @@ def dequant_mxfp4(codes, scales) -> torch.Tensor:
     N, half = codes.shape
     w = _BYTE_PAIR.index_select(0, codes.reshape(-1).to(torch.int32)).view(N, half // 16, 32)
     return w.mul_(_E8M0_T[scales.to(torch.int64)].unsqueeze(-1)).view(N, 2 * half)
+
+
+def dequant_nvfp4(codes, scales) -> torch.Tensor:
+    """NVFP4 [N, K/2] codes + [N, K/16] E4M3 block scales -> exact float64 [N, K]
+    without the tensor scale: each 16-element block times its E4M3 scale."""
+    codes = torch.as_tensor(codes).cpu()
+    scales = torch.as_tensor(scales).cpu()
+    N, half = codes.shape
+    w = _BYTE_PAIR.index_select(0, codes.reshape(-1).to(torch.int32)).view(N, half // 8, 16)
+    return w.mul_(_E4M3_T[scales.to(torch.int64)].unsqueeze(-1)).view(N, 2 * half)
 
 
 def dequant_fp8_block(codes, scales) -> torch.Tensor:
@@ -247,6 +266,42 @@ def _ffn_ref_a16(xb, sid, wts, w13, w13_s, w2, w2_s) -> dict:
         np.add.at(y, rows, wts[rows, picks][:, None] * o)
         h_q[rows, picks] = hb
     return {"y": y, "x_q": None, "x_s": None, "h_q": h_q, "h_s": None, "h_amax": None, "valid": valid}
+
+
+def ffn_ref_nvfp4(x, topk_ids, topk_weights, w13, w13_s, w13_gs, w2, w2_s, w2_gs, tokens=None) -> dict:
+    """The routed MoE FFN with NVFP4 expert weights and bf16 activations, float64,
+    for all tokens or the subset ``tokens``. w13 [E, 2I, H/2] / w2 [E, H, I/2]
+    codes, w13_s [E, 2I, H/16] / w2_s [E, H, I/16] E4M3 block scales, w13_gs /
+    w2_gs [E] tensor scales. Per expert e:
+        g, u = gs13[e] * (x . W13'[e]^T) split at I   (W' = codes x block scales)
+        h    = bf16(silu(g) * u)
+        o    = gs2[e] * (h . W2'[e]^T)
+    and y = sum_j w[t, j] o. Returns y, h_q (bf16 bits [n, K, I]), valid."""
+    xb = _u16(x)
+    ids = np.asarray(torch.as_tensor(topk_ids).cpu()).astype(np.int64)
+    wts = np.asarray(torch.as_tensor(topk_weights).cpu()).astype(np.float64)
+    gs13 = np.asarray(torch.as_tensor(w13_gs).cpu()).astype(np.float64)
+    gs2 = np.asarray(torch.as_tensor(w2_gs).cpu()).astype(np.float64)
+    T, H = xb.shape
+    K = ids.shape[1]
+    E = w13.shape[0]
+    I = w2.shape[2] * 2
+    sel = np.arange(T) if tokens is None else np.asarray(tokens, dtype=np.int64)
+    n = sel.size
+    sid = ids[sel]
+    xh = torch.from_numpy(bf16_to_f64(xb[sel]))
+    y = np.zeros((n, H), dtype=np.float64)
+    h_q = np.zeros((n, K, I), dtype=np.uint16)
+    valid = (sid >= 0) & (sid < E)
+    for e in np.unique(sid[valid]):
+        rows, picks = np.nonzero(sid == e)
+        acc = (xh[torch.from_numpy(rows)] @ dequant_nvfp4(w13[int(e)], w13_s[int(e)]).T).numpy() * gs13[e]
+        hb = f64_to_bf16_rne(_silu_mul(acc[:, :I], acc[:, I:]))
+        del acc
+        o = (torch.from_numpy(bf16_to_f64(hb)) @ dequant_nvfp4(w2[int(e)], w2_s[int(e)]).T).numpy() * gs2[e]
+        np.add.at(y, rows, wts[sel[rows], picks][:, None] * o)
+        h_q[rows, picks] = hb
+    return {"y": y, "h_q": h_q, "valid": valid}
 
 
 def ffn_ref_dense_single(x, w13, w13_s, w2, w2_s) -> np.ndarray:

@@ -159,6 +159,18 @@ def make_x(w: Workload) -> torch.Tensor:
 
 # ----------------------------------------------------------------------------- weights
 
+def _e2m1_pack(v: torch.Tensor, N: int, Kd: int) -> torch.Tensor:
+    """Elements already divided by their scales -> E2M1 codes rounded to
+    nearest-even on the grid and saturated at +-6, two per byte (low nibble = even k)."""
+    a = v.abs()
+    q = torch.where(a < 2, 0.5, torch.where(a < 4, 1.0, 2.0))
+    r = torch.clamp(torch.round(a / q) * q, max=6.0)
+    idx = torch.where(r < 2, r * 2, torch.where(r < 4, r + 2, r / 2 + 4)).to(torch.uint8)
+    code = idx | (torch.signbit(v).to(torch.uint8) << 3)
+    code = code.reshape(N, Kd)
+    return (code[:, 0::2] | (code[:, 1::2] << 4)).contiguous()
+
+
 def _pack_mxfp4(wf: torch.Tensor):
     """Pack float weights [N, K] into MXFP4: codes [N, K/2] u8 (low nibble = even k)
     and E8M0 scales [N, K/32] u8, with the OCP MX weight rule (shared exponent
@@ -170,14 +182,22 @@ def _pack_mxfp4(wf: torch.Tensor):
     _, ex = torch.frexp(amax)                       # amax = m * 2^ex, m in [0.5, 1)
     X = torch.where(amax > 0, ex - 3, torch.full_like(ex, -127)).clamp(-127, 127)
     v = blk * torch.exp2(-X.to(torch.float32)).unsqueeze(-1)
-    a = v.abs()
-    q = torch.where(a < 2, 0.5, torch.where(a < 4, 1.0, 2.0))
-    r = torch.clamp(torch.round(a / q) * q, max=6.0)
-    idx = torch.where(r < 2, r * 2, torch.where(r < 4, r + 2, r / 2 + 4)).to(torch.uint8)
-    code = idx | (torch.signbit(v).to(torch.uint8) << 3)
-    code = code.reshape(N, Kd)
-    packed = code[:, 0::2] | (code[:, 1::2] << 4)
-    return packed.contiguous(), (X + 127).to(torch.uint8).contiguous()
+    return _e2m1_pack(v, N, Kd), (X + 127).to(torch.uint8).contiguous()
+
+
+def _pack_nvfp4(wf: torch.Tensor):
+    """Pack one float weight tensor [N, K] into NVFP4 (NVIDIA's published recipe):
+    a tensor scale gs = amax / (6 * 448) (float32), one E4M3 scale per 16 elements
+    s = E4M3(block amax / (6 gs)) (nearest), elements rounded to nearest-even on the
+    E2M1 grid of w / (s gs) and saturated at +-6. Returns codes [N, K/2] u8, block
+    scales [N, K/16] u8 (E4M3 bits) and gs."""
+    N, Kd = wf.shape
+    gs = (wf.abs().amax() / (6.0 * 448.0)).clamp(min=2.0 ** -100).to(torch.float32)
+    blk = wf.reshape(N, Kd // 16, 16)
+    s8 = (blk.abs().amax(-1) / (6.0 * gs)).clamp(max=448.0).to(torch.float8_e4m3fn)
+    sv = s8.to(torch.float32) * gs
+    v = torch.where(sv.unsqueeze(-1) > 0, blk / sv.unsqueeze(-1), torch.zeros_like(blk))
+    return _e2m1_pack(v, N, Kd), s8.view(torch.uint8).contiguous(), float(gs)
 
 
 def _pack_fp8_block(wf: torch.Tensor):
@@ -200,30 +220,42 @@ def _gen_device(w: Workload, device) -> torch.device:
     return torch.device("cpu") if n <= (1 << 27) else dev
 
 
-def make_expert_weights(w: Workload, device="cpu", experts: Optional[Sequence[int]] = None):
-    """MXFP4 expert weights on ``device``.
+def make_expert_weights(w: Workload, device="cpu", experts: Optional[Sequence[int]] = None, fmt: str = "mxfp4"):
+    """4-bit expert weights on ``device``.
 
     Returns dict with w13 [E, 2I, H/2], w13_s [E, 2I, H/32], w2 [E, H, I/2],
     w2_s [E, H, I/32] (all uint8). W13 rows [0, I) are the gate projection and
     rows [I, 2I) the up projection. ``experts`` restricts generation to a subset
     (the returned tensors then have len(experts) rows in that order).
+    fmt="nvfp4": the same float weights packed as NVFP4: w13_s [E, 2I, H/16] and
+    w2_s [E, H, I/16] E4M3 block scales, plus w13_gs / w2_gs [E] float32 tensor
+    scales (one per expert and projection).
     """
+    if fmt not in ("mxfp4", "nvfp4"):
+        raise ValueError(fmt)
+    nv = fmt == "nvfp4"
+    blk = 16 if nv else 32
     dev = torch.device(device)
     gdev = _gen_device(w, dev)
     ex = list(range(w.E)) if experts is None else list(experts)
     fI = w.full_I or w.I
     H, I = w.H, w.I
     w13 = torch.empty((len(ex), 2 * I, H // 2), dtype=torch.uint8, device=dev)
-    w13_s = torch.empty((len(ex), 2 * I, H // 32), dtype=torch.uint8, device=dev)
+    w13_s = torch.empty((len(ex), 2 * I, H // blk), dtype=torch.uint8, device=dev)
     w2 = torch.empty((len(ex), H, I // 2), dtype=torch.uint8, device=dev)
-    w2_s = torch.empty((len(ex), H, I // 32), dtype=torch.uint8, device=dev)
+    w2_s = torch.empty((len(ex), H, I // blk), dtype=torch.uint8, device=dev)
+    gs13 = torch.empty(len(ex), dtype=torch.float32)
+    gs2 = torch.empty(len(ex), dtype=torch.float32)
     g = torch.Generator(device=gdev)
     for i, e in enumerate(ex):
         g.manual_seed(w.weight_seed * 4096 + e)
         f13 = torch.randn((2 * fI, H), generator=g, device=gdev, dtype=torch.float32) * 0.02
         if fI != I:   # rank-0 column slice of the full gate and up projections
             f13 = torch.cat([f13[:I], f13[fI:fI + I]], 0)
-        c, s = _pack_mxfp4(f13)
+        if nv:
+            c, s, gs13[i] = _pack_nvfp4(f13)
+        else:
+            c, s = _pack_mxfp4(f13)
         w13[i].copy_(c)
         w13_s[i].copy_(s)
         del f13
@@ -231,11 +263,17 @@ def make_expert_weights(w: Workload, device="cpu", experts: Optional[Sequence[in
         f2 = torch.randn((H, fI), generator=g, device=gdev, dtype=torch.float32) * 0.02
         if fI != I:
             f2 = f2[:, :I].contiguous()
-        c, s = _pack_mxfp4(f2)
+        if nv:
+            c, s, gs2[i] = _pack_nvfp4(f2)
+        else:
+            c, s = _pack_mxfp4(f2)
         w2[i].copy_(c)
         w2_s[i].copy_(s)
         del f2
-    return {"w13": w13, "w13_s": w13_s, "w2": w2, "w2_s": w2_s}
+    out = {"w13": w13, "w13_s": w13_s, "w2": w2, "w2_s": w2_s}
+    if nv:
+        out.update(w13_gs=gs13.to(dev), w2_gs=gs2.to(dev))
+    return out
 
 
 def make_shared_weights(w: Workload, device="cpu"):

@@ -12,8 +12,9 @@ import torch
 import mxfp4_weights_fp8_amd as moe
 from oracle.compare import h_bf16_mismatch, h_code_mismatch, y_metrics
 from oracle.formats import bf16_to_f64
-from oracle.envelope import routed_swiglu_envelope, routed_swiglu_envelope_a16, shared_swiglu_envelope
-from oracle.moe import ffn_ref, plan_ref
+from oracle.envelope import (routed_swiglu_envelope, routed_swiglu_envelope_a16, routed_swiglu_envelope_nvfp4,
+                             shared_swiglu_envelope)
+from oracle.moe import ffn_ref, ffn_ref_nvfp4, plan_ref
 
 #: the parity bar for the final output (vs the float64 oracle)
 MAX_REL = 2e-2
@@ -188,12 +189,17 @@ def check_ffn(inp, p, y, dbg, tokens=None, label="", ref=None):
     return m
 
 
-def check_ffn_a16(inp, p, y, dbg, tokens=None, label="", ref=None):
-    """The bf16-activation variant: oracle (act="bf16") on the selected tokens;
-    compare y and every valid pick's bf16 SwiGLU outputs. Returns metrics."""
+def check_ffn_a16(inp, p, y, dbg, tokens=None, label="", ref=None, nvfp4=False):
+    """The bf16-activation variants (MXFP4 weights: oracle act="bf16"; nvfp4=True:
+    NVFP4 weights, ffn_ref_nvfp4, with inp.weights the row-major NVFP4 tensors) on
+    the selected tokens; compare y and every valid pick's bf16 SwiGLU outputs.
+    Returns metrics."""
     t0 = time.time()
     if ref is None:
-        ref = ffn_ref(inp.x, inp.topk_ids, inp.topk_weights, **inp.weights, tokens=tokens, act="bf16")
+        if nvfp4:
+            ref = ffn_ref_nvfp4(inp.x, inp.topk_ids, inp.topk_weights, **inp.weights, tokens=tokens)
+        else:
+            ref = ffn_ref(inp.x, inp.topk_ids, inp.topk_weights, **inp.weights, tokens=tokens, act="bf16")
     t_oracle = time.time() - t0
     sel = np.arange(inp.wl.T) if tokens is None else np.asarray(tokens)
     yb = u16(y)[sel]
@@ -214,13 +220,17 @@ def check_ffn_a16(inp, p, y, dbg, tokens=None, label="", ref=None):
         exp = ids[sel[vi[r]], vj[r]]
         for e in np.unique(exp):
             mk = exp == e
-            h[mk], err[mk] = routed_swiglu_envelope_a16(xb, _host(W["w13"][int(e)]), _host(W["w13_s"][int(e)]), I,
-                                                        vi[r][mk], c[mk])
+            if nvfp4:
+                h[mk], err[mk] = routed_swiglu_envelope_nvfp4(xb, _host(W["w13"][int(e)]), _host(W["w13_s"][int(e)]),
+                                                              float(W["w13_gs"][int(e)]), I, vi[r][mk], c[mk])
+            else:
+                h[mk], err[mk] = routed_swiglu_envelope_a16(xb, _host(W["w13"][int(e)]), _host(W["w13_s"][int(e)]),
+                                                            I, vi[r][mk], c[mk])
         return h, err
 
     hm = h_bf16_mismatch(hg, ref["h_q"][valid], envelope=envelope)
     m.update({"h_" + k: v for k, v in hm.items()}, oracle_s=round(t_oracle, 2), label=label)
-    say(f"[parity a16 {label}] {m}")
+    say(f"[parity {'nvfp4' if nvfp4 else 'a16'} {label}] {m}")
     assert m["finite"], m
     assert m["max_rel"] <= MAX_REL, m
     assert m["mean_rel"] <= MEAN_REL, m

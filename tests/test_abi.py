@@ -55,7 +55,8 @@ def test_validate_flags():
     assert moe.validate(moe.make_dims(4, 256, 512, 8, 2, flags=moe.FLAG_DECODE_CHAIN)) == moe.MOE_OK
     assert moe.validate(moe.make_dims(4, 256, 512, 8, 2, flags=moe.FLAG_A16)) == moe.MOE_OK
     assert moe.validate(moe.make_dims(4, 256, 512, 8, 2, flags=moe.FLAG_A16 | moe.FLAG_DECODE_CHAIN)) == moe.MOE_OK
-    assert moe.validate(moe.make_dims(4, 256, 512, 8, 2, flags=4)) == moe.MOE_EINVAL
+    assert moe.validate(moe.make_dims(4, 256, 512, 8, 2, flags=moe.FLAG_NVFP4)) == moe.MOE_OK
+    assert moe.validate(moe.make_dims(4, 256, 512, 8, 2, flags=8)) == moe.MOE_EINVAL
     assert moe.validate(moe.make_dims(4, 256, 512, 8, 2, flags=-1)) == moe.MOE_EINVAL
 
 
@@ -67,6 +68,14 @@ def test_validate_a16_limits():
     assert moe.validate(moe.make_dims(131072, 8192, 512, 8, 2)) == moe.MOE_OK
     assert moe.validate(moe.make_dims(65536, 256, 2048, 8, 8, flags=moe.FLAG_A16)) == moe.MOE_EUNSUPPORTED
     assert moe.validate(moe.make_dims(65536, 256, 2048, 8, 4, flags=moe.FLAG_A16)) == moe.MOE_OK
+
+
+def test_nvfp4_limits_follow_the_bf16_activation_path():
+    assert moe.validate(moe.make_dims(4, 256, 512, 8, 2, Is=128, flags=moe.FLAG_NVFP4)) == moe.MOE_EUNSUPPORTED
+    assert moe.validate(moe.make_dims(65536, 256, 2048, 8, 8, flags=moe.FLAG_NVFP4)) == moe.MOE_EUNSUPPORTED
+    d16 = moe.make_dims(4096, 1024, 512, 64, 8, flags=moe.FLAG_A16)
+    dnv = moe.make_dims(4096, 1024, 512, 64, 8, flags=moe.FLAG_NVFP4)
+    assert moe.ffn_workspace_bytes(dnv) == moe.ffn_workspace_bytes(d16)
 
 
 def test_a16_workspace_holds_bf16_rows():
@@ -126,6 +135,27 @@ def test_host_checks_reject_before_enqueue():
     assert L.moe_ffn(ctypes.byref(z), *([None] * 10), None, None, None, None, 0, None) == moe.MOE_OK
     assert L.moe_ffn_static(ctypes.byref(z), *([None] * 10), None, None, None, None) == moe.MOE_OK
     assert L.moe_quant_act(ctypes.byref(z), None, None, None, None) == moe.MOE_OK
+
+
+def test_nvfp4_host_checks():
+    """moe_ffn_nvfp4 needs MOE_FLAG_NVFP4 and both tensor-scale arrays; moe_ffn and
+    moe_ffn_static refuse NVFP4 dims; all before anything is enqueued."""
+    L = moe.lib()
+    fake = ctypes.c_void_p(0x1000)   # never dereferenced
+    nv = moe.make_dims(4, 256, 512, 8, 2, flags=moe.FLAG_NVFP4)
+    mx = moe.make_dims(4, 256, 512, 8, 2, flags=moe.FLAG_A16)
+    ok = [fake] * 13
+    assert L.moe_ffn_nvfp4(ctypes.byref(mx), *ok, None, fake, 1 << 30, None) == moe.MOE_EINVAL
+    for i in (9, 12):                 # w13_gs, w2_gs
+        a = list(ok)
+        a[i] = None
+        assert L.moe_ffn_nvfp4(ctypes.byref(nv), *a, None, fake, 1 << 30, None) == moe.MOE_EINVAL
+    assert L.moe_ffn_nvfp4(ctypes.byref(nv), *ok, None, fake, 1, None) == moe.MOE_EWORKSPACE
+    assert L.moe_ffn_nvfp4(ctypes.byref(nv), *ok, None, None, 1 << 30, None) == moe.MOE_EINVAL
+    assert L.moe_ffn(ctypes.byref(nv), *([fake] * 10), None, fake, None, fake, 1 << 30, None) == moe.MOE_EINVAL
+    assert L.moe_ffn_static(ctypes.byref(nv), *([fake] * 10), None, fake, None, None) == moe.MOE_EINVAL
+    z = moe.make_dims(0, 256, 512, 8, 2, flags=moe.FLAG_NVFP4)
+    assert L.moe_ffn_nvfp4(ctypes.byref(z), *([None] * 13), None, None, 0, None) == moe.MOE_OK
 
 
 def test_product_path_has_no_cpu_fallback():
