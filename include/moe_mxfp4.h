@@ -69,11 +69,22 @@ enum {
  *   small_max  experts with at most this many routed pairs use the small-M
  *      (decode) tiling, larger ones the large-M (prefill) tiling; 0 selects the
  *      library default (16). moe_plan and moe_ffn must see the same value.
- *   flags  0, or MOE_FLAG_DECODE_CHAIN, MOE_FLAG_A16, MOE_FLAG_NVFP4 (below). */
+ *   flags  0, or MOE_FLAG_DECODE_CHAIN, MOE_FLAG_A16, MOE_FLAG_NVFP4 (below).
+ *   tile_w13, tile_w2  exact-shape tiling per GEMM ("Pushing the Limits of Serving
+ *      DeepSeek-V4-Pro", section 3.3: separate W13 and W2 configurations tuned on the
+ *      expert sizes the routing produces). An expert above small_max pairs is split
+ *      into 256-row items and at most one item of 1..128 rows (its remainder, or the
+ *      whole expert when it has at most 128 pairs). Such an item of at most tile_w13
+ *      (tile_w2) rows runs W13 (W2) as 16-row small-M tiles, a larger one as one
+ *      128-row large-M tile. 0 selects the library's table, tuned on MI355X per
+ *      (H, I); -1 sends none to the small-M tiles; 1..128 is the row limit itself.
+ *      Results are bitwise identical for every choice (each dot product is summed in
+ *      the same order by every tiling). moe_plan and moe_ffn must see the same values. */
 typedef struct moe_dims {
   int32_t T, H, I, E, K, Is;
   int32_t small_max;
   int32_t flags;
+  int32_t tile_w13, tile_w2;
 } moe_dims;
 
 /* moe_ffn at decode shapes (T*K <= 512): run W13 + SwiGLU/requant, W2 and the

@@ -40,7 +40,8 @@ class MoEError(RuntimeError):
 class Dims(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int32), ("H", ctypes.c_int32), ("I", ctypes.c_int32), ("E", ctypes.c_int32),
                 ("K", ctypes.c_int32), ("Is", ctypes.c_int32), ("small_max", ctypes.c_int32),
-                ("flags", ctypes.c_int32)]
+                ("flags", ctypes.c_int32),
+                ("tile_w13", ctypes.c_int32), ("tile_w2", ctypes.c_int32)]
 
 
 #: moe_dims.flags bit: run decode shapes as one persistent W13 -> W2 -> combine launch
@@ -101,8 +102,11 @@ def status_string(code: int) -> str:
     return lib().moe_status_string(code).decode()
 
 
-def make_dims(T, H, I, E, K, Is=0, small_max=0, flags=0) -> Dims:
-    return Dims(int(T), int(H), int(I), int(E), int(K), int(Is), int(small_max), int(flags))
+def make_dims(T, H, I, E, K, Is=0, small_max=0, flags=0, tile_w13=0, tile_w2=0) -> Dims:
+    """moe_dims. tile_w13 / tile_w2: exact-shape tiling per GEMM (0 = the library's
+    tuned table, -1 = no 128-row item on the small-M tiles, 1..128 = row limit)."""
+    return Dims(int(T), int(H), int(I), int(E), int(K), int(Is), int(small_max), int(flags), int(tile_w13),
+                int(tile_w2))
 
 
 def validate(d: Dims) -> int:
@@ -147,11 +151,11 @@ class Plan:
 
 
 def plan(topk_ids: torch.Tensor, E: int, H: int, I: int, small_max: int = 0, Is: int = 0,
-         out: Optional[Plan] = None, flags: int = 0) -> Plan:
+         out: Optional[Plan] = None, flags: int = 0, tile_w13: int = 0, tile_w2: int = 0) -> Plan:
     """moe_plan on the current stream. topk_ids: cuda int32 [T, K]. H, I (and Is,
-    flags) complete the dims that moe_ffn will use with this plan."""
+    flags, tile_w13, tile_w2) complete the dims that moe_ffn will use with this plan."""
     T, K = topk_ids.shape
-    d = make_dims(T, H, I, E, K, Is, small_max, flags)
+    d = make_dims(T, H, I, E, K, Is, small_max, flags, tile_w13, tile_w2)
     _check(validate(d), "moe_plan dims")
     _require(topk_ids, torch.int32, (T, K), "topk_ids")
     dev = topk_ids.device

@@ -33,7 +33,7 @@ constexpr int kMaxKS = 3;
 
 struct FewKArgs {
   const int2* items;
-  const int32_t* n_items;
+  const int32_t* n_items;  // items [first[0], n_items[0]) of the list are this launch's
   const int32_t* offsets;
   const int32_t* sorted_pairs;
   const uint8_t* h_q;      // [P, I] E4M3, rows in plan order
@@ -46,6 +46,7 @@ struct FewKArgs {
   int item_shift;          // 1: items hold 256 rows, workgroup y covers half y % 2 of item y / 2
   int H, I;
   int blocks_per_wg;       // 128-column blocks per workgroup (the last run may be shorter)
+  const int32_t* first = nullptr;   // null: from item 0
 };
 
 template <int KS>
@@ -58,7 +59,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_w2_fewk(FewKArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t sSa[2][4 * kScaleCopies * 256];  // [buf][row][4 KS B] + padding
   __shared__ int sSlot[kRows];
 
-  const int item = blockIdx.y >> a.item_shift;
+  const int item = (a.first ? a.first[0] : 0) + (int)(blockIdx.y >> a.item_shift);
   if (item >= a.n_items[0]) return;
   const int2 it = a.items[item];
   const int e = it.x;
@@ -304,7 +305,7 @@ bool fewk2_supported(const moe_dims& d) {
 hipError_t launch_w2_fewk(const moe_dims& d, const int2* items, const int32_t* n_items, int64_t max_items,
                           int item_rows, const int32_t* offsets, const int32_t* sorted_pairs, const uint8_t* h_q,
                           const uint8_t* h_s, const uint8_t* w2, const uint8_t* w2_s, uint16_t* o, uint8_t* os,
-                          hipStream_t s) {
+                          hipStream_t s, const int32_t* first) {
   if (max_items <= 0) return hipSuccess;
   const int shift = item_rows == 2 * kRows ? 1 : 0;
   const int n_blocks = d.H / kCols;
@@ -314,6 +315,7 @@ hipError_t launch_w2_fewk(const moe_dims& d, const int2* items, const int32_t* n
   const int64_t P = (int64_t)d.T * d.K;
   FewKArgs a{items, n_items, offsets, sorted_pairs, h_q, h_s, w2, w2_s, o, os, (uint32_t)(P * d.I), shift,
              d.H, d.I, per_wg};
+  a.first = first;
   dim3 grid((unsigned)ceil_div(n_blocks, per_wg), (unsigned)(max_items << shift));
   switch (d.I / 128) {
     case 1: hipLaunchKernelGGL(k_w2_fewk<1>, grid, dim3(kThreads), 0, s, a); break;

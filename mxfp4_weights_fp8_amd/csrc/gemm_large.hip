@@ -60,7 +60,7 @@ constexpr int kSbBytes = (kTokTile * kSbRow + 255) / 256 * 256;   // whole 256-b
 
 struct LargeArgs {
   const int2* items;
-  const int32_t* n_items;
+  const int32_t* n_items;  // items [first[0], n_items[0]) of the list are this launch's
   const int32_t* offsets;
   const int32_t* sorted_pairs;
   const uint8_t* act;      // W13: x_q [T, H]; W2: h_q [P, I]
@@ -76,6 +76,7 @@ struct LargeArgs {
   int act_s_dma;           // act_s rows are 4-byte aligned: copy them with dword copies
   int item_shift;          // 1: items hold 256 rows, workgroup y covers half y % 2 of item y / 2
   int H, I, K;
+  const int32_t* first = nullptr;   // null: from item 0
 };
 
 template <bool W13>
@@ -88,7 +89,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_large(LargeArgs a) {
   __shared__ int sSlot[W13 ? 1 : kTokTile];
   __shared__ float sRed[2][kTokTile];
 
-  const int item = blockIdx.y >> a.item_shift;
+  const int item = (a.first ? a.first[0] : 0) + (int)(blockIdx.y >> a.item_shift);
   if (item >= a.n_items[0]) return;
   const int2 it = a.items[item];
   const int e = it.x;
@@ -396,13 +397,14 @@ bool large_path_supported(const moe_dims& d) {
 hipError_t launch_w13_large(const moe_dims& d, const int2* items, const int32_t* n_items, int64_t max_items,
                             int item_rows, const int32_t* offsets, const int32_t* sorted_pairs,
                             const uint8_t* x_q, const uint8_t* x_s, const uint8_t* w13, const uint8_t* w13_s,
-                            uint8_t* h_q, uint8_t* h_s, hipStream_t s) {
+                            uint8_t* h_q, uint8_t* h_s, hipStream_t s, const int32_t* first) {
   if (max_items <= 0) return hipSuccess;
   const int shift = item_rows == 2 * kTokTile ? 1 : 0;
   const int KS = d.H / 128;
   LargeArgs a{items, n_items, offsets, sorted_pairs, x_q, x_s, w13, w13_s, h_q, h_s, nullptr, nullptr,
               (uint32_t)((int64_t)d.T * d.H), (uint32_t)((int64_t)d.T * KS),
               KS % 4 == 0 && (uintptr_t)x_s % 4 == 0, shift, d.H, d.I, d.K};
+  a.first = first;
   hipLaunchKernelGGL(k_gemm_large<true>, dim3(d.I / 128, (unsigned)(max_items << shift)), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
@@ -410,7 +412,7 @@ hipError_t launch_w13_large(const moe_dims& d, const int2* items, const int32_t*
 hipError_t launch_w2_large(const moe_dims& d, const int2* items, const int32_t* n_items, int64_t max_items,
                            int item_rows, const int32_t* offsets, const int32_t* sorted_pairs,
                            const uint8_t* h_q, const uint8_t* h_s, const uint8_t* w2, const uint8_t* w2_s,
-                           uint16_t* o, uint8_t* os, hipStream_t s) {
+                           uint16_t* o, uint8_t* os, hipStream_t s, const int32_t* first) {
   if (max_items <= 0) return hipSuccess;
   const int shift = item_rows == 2 * kTokTile ? 1 : 0;
   const int KS = d.I / 128;
@@ -418,6 +420,7 @@ hipError_t launch_w2_large(const moe_dims& d, const int2* items, const int32_t* 
   LargeArgs a{items, n_items, offsets, sorted_pairs, h_q, h_s, w2, w2_s, nullptr, nullptr, o, os,
               (uint32_t)(P * d.I), (uint32_t)(P * KS), KS % 4 == 0 && (uintptr_t)h_s % 4 == 0,
               shift, d.H, d.I, d.K};
+  a.first = first;
   hipLaunchKernelGGL(k_gemm_large<false>, dim3(d.H / 256, (unsigned)(max_items << shift)), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }

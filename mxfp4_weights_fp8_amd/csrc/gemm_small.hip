@@ -37,6 +37,9 @@ constexpr int kThreads = 256;
 // bytes.
 constexpr int kW13Waves = 8;
 constexpr int kW2Frags = 2;
+// Rows of list slots a small-M launch covers at once; more slots are walked by a
+// grid-stride loop (decode lists stay below it: one slot per workgroup row).
+constexpr int64_t kMaxSlotRows = 1024;
 
 template <int WAVES>
 __global__ __launch_bounds__(WAVES * 64) void k_w13_small(
@@ -47,11 +50,15 @@ __global__ __launch_bounds__(WAVES * 64) void k_w13_small(
     int K) {
   __shared__ float red[WAVES * 16];
   extern __shared__ __attribute__((aligned(16))) uint8_t sS[];   // [256 weight rows][H/32] E8M0
-  const int l = blockIdx.y >= lists.cap0;
-  const int item = blockIdx.y - (l ? lists.cap0 : 0);
-  if (item >= lists.n_items[l][0]) return;
-  w13_small_unit<WAVES>(lists.items[l][item], lists.rows[l], blockIdx.x, offsets, sorted_pairs, x_q, x_s, w13,
-                        w13_s, h_q, h_s, H, I, K, sS, red);
+  // grid-stride over the list slots (the grid is capped; slots past a list's
+  // device-side count are empty); every thread walks the same slots
+  for (int y = blockIdx.y; y < lists.cap0 + lists.cap1; y += gridDim.y) {
+    const int l = y >= lists.cap0;
+    const int item = y - (l ? lists.cap0 : 0);
+    if (item >= lists.n_items[l][0]) continue;
+    w13_small_unit<WAVES>(lists.items[l][item], lists.rows[l], blockIdx.x, offsets, sorted_pairs, x_q, x_s, w13,
+                          w13_s, h_q, h_s, H, I, K, sS, red);
+  }
 }
 
 template <int NF>
@@ -61,13 +68,15 @@ __global__ __launch_bounds__(kThreads) void k_w2_small(
     const uint8_t* __restrict__ h_q, const uint8_t* __restrict__ h_s, const uint8_t* __restrict__ w2,
     const uint8_t* __restrict__ w2_s, uint16_t* __restrict__ o, uint8_t* __restrict__ os, int H, int I) {
   extern __shared__ __attribute__((aligned(16))) uint8_t sS[];   // [256 weight rows][I/32] E8M0
-  const int l = blockIdx.y >= lists.cap0;
-  const int item = blockIdx.y - (l ? lists.cap0 : 0);
-  if (item >= lists.n_items[l][0]) return;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n_wave = blockIdx.x * 64 * NF + wave * 16 * NF;
-  w2_small_wave<NF>(lists.items[l][item], lists.rows[l], n_wave, offsets, sorted_pairs, h_q, h_s, w2, w2_s, o, os,
-                    H, I, sS + wave * staged_bytes(16 * NF * (I / 32)));
+  for (int y = blockIdx.y; y < lists.cap0 + lists.cap1; y += gridDim.y) {   // as in k_w13_small
+    const int l = y >= lists.cap0;
+    const int item = y - (l ? lists.cap0 : 0);
+    if (item >= lists.n_items[l][0]) continue;
+    w2_small_wave<NF>(lists.items[l][item], lists.rows[l], n_wave, offsets, sorted_pairs, h_q, h_s, w2, w2_s, o, os,
+                      H, I, sS + wave * staged_bytes(16 * NF * (I / 32)));
+  }
 }
 
 }  // namespace
@@ -79,7 +88,7 @@ hipError_t launch_w13_small(const moe_dims& d, const SmallLists& lists, const in
   const int64_t max_items = (int64_t)lists.cap0 + lists.cap1;
   if (max_items <= 0) return hipSuccess;
   constexpr int WAVES = kW13Waves;
-  dim3 grid(d.I / 128, (unsigned)max_items);
+  dim3 grid(d.I / 128, (unsigned)(max_items < kMaxSlotRows ? max_items : kMaxSlotRows));
   // weight scales in LDS: per wave two runs of 128/WAVES rows x H/32 bytes
   const size_t lds = (size_t)WAVES * 2 * staged_bytes(128 / WAVES * (d.H / 32));
   hipLaunchKernelGGL(k_w13_small<WAVES>, grid, dim3(WAVES * 64), lds, s, lists,
@@ -95,7 +104,7 @@ hipError_t launch_w2_small(const moe_dims& d, const SmallLists& lists, const int
   const int64_t max_items = (int64_t)lists.cap0 + lists.cap1;
   if (max_items <= 0) return hipSuccess;
   constexpr int NF = kW2Frags;
-  dim3 grid((unsigned)ceil_div(d.H, 64 * NF), (unsigned)max_items);
+  dim3 grid((unsigned)ceil_div(d.H, 64 * NF), (unsigned)(max_items < kMaxSlotRows ? max_items : kMaxSlotRows));
   // weight scales in LDS: per wave one run of 16*NF rows x I/32 bytes
   const size_t lds = (size_t)(kThreads / 64) * staged_bytes(16 * NF * (d.I / 32));
   hipLaunchKernelGGL(k_w2_small<NF>, grid, dim3(kThreads), lds, s, lists,

@@ -51,7 +51,8 @@ inline int64_t xl_items_bound(const moe_dims& d) {
 // int32 header, then the two tile lists (int2 = {expert, first row}), then the
 // planner's per-block scratch.
 struct PlanWs {
-  int32_t* hdr;           // [0] small, [1] 128-row large, [2] 256-row large item counts
+  int32_t* hdr;           // [0] small, [1] 128-row, [2] 256-row item counts; [3] / [4] the 128-row
+                          // items (rows ascending) that W13 / W2 walk as 16-row tiles
   int2* small_items;
   int2* large_items;      // 128-row items
   int2* xl_items;         // 256-row items
@@ -61,6 +62,13 @@ struct PlanWs {
   int64_t small_cap, large_cap, xl_cap, nb;
 };
 size_t plan_ws_layout(const moe_dims& d, void* base, PlanWs* out);
+
+// Exact-shape tiling per GEMM: the 128-row items (1..128 rows each) of at most this
+// many rows run W13 (w13) or W2 as 16-row small-M tiles; the planner orders those
+// items by rows and counts them into hdr[3] / hdr[4]. 128 = all of them (batches of
+// at most kFoldPairs pairs, or shapes without large-M tiles); else moe_dims.tile_w13
+// / tile_w2, or the tuned table for (H, I).
+int tile_small_rows(const moe_dims& d, bool w13);
 
 // ---------------------------------------------------------------- ffn workspace
 // Activations and SwiGLU rows stay bf16 (no FP8 quantization): MOE_FLAG_A16 and
@@ -115,16 +123,19 @@ hipError_t launch_w2_small(const moe_dims& d, const SmallLists& lists, const int
                            const int32_t* sorted_pairs, const uint8_t* h_q, const uint8_t* h_s,
                            const uint8_t* w2, const uint8_t* w2_s, uint16_t* o, uint8_t* os, hipStream_t s);
 // 128-row large-M tiles; item_rows 128 or 256 (a 256-row item runs as two
-// 128-row workgroups).
+// 128-row workgroups). first: the launch takes items [first[0], n_items[0]) of the
+// list (null: from 0).
 bool large_path_supported(const moe_dims& d);
 hipError_t launch_w13_large(const moe_dims& d, const int2* items, const int32_t* n_items, int64_t max_items,
                             int item_rows, const int32_t* offsets, const int32_t* sorted_pairs,
                             const uint8_t* x_q, const uint8_t* x_s, const uint8_t* w13, const uint8_t* w13_s,
-                            uint8_t* h_q, uint8_t* h_s, hipStream_t s);
+                            uint8_t* h_q, uint8_t* h_s, hipStream_t s,
+                            const int32_t* first = nullptr);
 hipError_t launch_w2_large(const moe_dims& d, const int2* items, const int32_t* n_items, int64_t max_items,
                            int item_rows, const int32_t* offsets, const int32_t* sorted_pairs,
                            const uint8_t* h_q, const uint8_t* h_s, const uint8_t* w2, const uint8_t* w2_s,
-                           uint16_t* o, uint8_t* os, hipStream_t s);
+                           uint16_t* o, uint8_t* os, hipStream_t s,
+                            const int32_t* first = nullptr);
 // 256 x 256 large-M tiles on 256-row items (a K-step count that is a multiple of 4 and the
 // large-M shape limits).
 // W2 with at most 3 K steps (I <= 384): a workgroup keeps its 128 routed rows in LDS
@@ -138,7 +149,8 @@ hipError_t launch_shared2_fewk(const moe_dims& d, const uint8_t* sh_q, const uin
 hipError_t launch_w2_fewk(const moe_dims& d, const int2* items, const int32_t* n_items, int64_t max_items,
                           int item_rows, const int32_t* offsets, const int32_t* sorted_pairs, const uint8_t* h_q,
                           const uint8_t* h_s, const uint8_t* w2, const uint8_t* w2_s, uint16_t* o, uint8_t* os,
-                          hipStream_t s);
+                          hipStream_t s,
+                            const int32_t* first = nullptr);
 bool xl13_supported(const moe_dims& d);
 bool xl2_supported(const moe_dims& d);
 hipError_t launch_w13_xl(const moe_dims& d, const int2* items, const int32_t* n_items, int64_t max_items,

@@ -52,7 +52,8 @@ namespace {
 int validate(const moe_dims* d) {
   if (!d) return MOE_EINVAL;
   if (d->T < 0 || d->H <= 0 || d->I <= 0 || d->E < 1 || d->E > kMaxExperts || d->K < 1 || d->K > kMaxTopK ||
-      d->Is < 0 || d->small_max < 0 || (d->flags & ~(MOE_FLAG_DECODE_CHAIN | MOE_FLAG_A16 | MOE_FLAG_NVFP4)) != 0)
+      d->Is < 0 || d->small_max < 0 || (d->flags & ~(MOE_FLAG_DECODE_CHAIN | MOE_FLAG_A16 | MOE_FLAG_NVFP4)) != 0 ||
+      d->tile_w13 < -1 || d->tile_w13 > kLargeRows || d->tile_w2 < -1 || d->tile_w2 > kLargeRows)
     return MOE_EINVAL;
   if (d->H % 128 || d->I % 128 || d->Is % 128) return MOE_EUNSUPPORTED;
   if ((int64_t)d->T * d->K > (int64_t)1 << 30) return MOE_EUNSUPPORTED;
@@ -229,25 +230,31 @@ int ffn_enqueue(const moe_dims& d, const uint16_t* x, const float* topk_weights,
     return MOE_OK;
   }
 
-  // Work lists: 16-row items (small experts), 256-row items and 128-row remainders
-  // (large experts). A 256-row item needs an expert with more than 128 pairs and a
-  // 128-row item one with more than small_max, so launches that could only find
-  // empty lists are skipped. Up to kFoldPairs pairs the few 128-row items ride in
-  // the small-M launch (one launch less; a 128-row item is then walked as 16-row
-  // tiles).
+  // Work lists: 16-row items (small experts), 256-row items and 128-row items
+  // (remainders of 1..128 rows, by rows). A 256-row item needs an expert with more
+  // than 128 pairs and a 128-row item one with more than small_max, so launches that
+  // could only find empty lists are skipped. Exact-shape tiling per GEMM: the
+  // 128-row items of at most tile_small_rows(d, GEMM) rows (a prefix, hdr[3] for
+  // W13 and hdr[4] for W2) ride in that GEMM's small-M launch as 16-row tiles, the
+  // rest run as 128-row tiles from the cut on; up to kFoldPairs pairs (or without
+  // large-M tiles) all of them are small.
   const bool large = large_path_supported(d);
   const bool any_xl = P > kXlRows / 2, any_l = P > small_max_of(d);
-  const bool fold = any_l && (P <= kFoldPairs || !large);
-  SmallLists sl = small_lists(pw.small_items, pw.hdr + 0, pw.small_cap, kSmallRows);
-  if (fold) {
-    sl.items[1] = pw.large_items;
-    sl.n_items[1] = pw.hdr + 1;
-    sl.cap1 = (int)pw.large_cap;
-    sl.rows[1] = kLargeRows;
-  }
+  const int t13 = tile_small_rows(d, true), t2 = tile_small_rows(d, false);
+  auto lists_for = [&](int t, const int32_t* cut) {
+    SmallLists sl = small_lists(pw.small_items, pw.hdr + 0, pw.small_cap, kSmallRows);
+    if (any_l && t > 0) {
+      sl.items[1] = pw.large_items;
+      sl.n_items[1] = cut;
+      sl.cap1 = (int)pw.large_cap;
+      sl.rows[1] = kLargeRows;
+    }
+    return sl;
+  };
+  const SmallLists sl13 = lists_for(t13, pw.hdr + 3), sl2 = lists_for(t2, pw.hdr + 4);
   const SmallLists sxl = small_lists(pw.xl_items, pw.hdr + 2, pw.xl_cap, kXlRows);
 
-  err = launch_w13_small(d, sl, expert_offsets, sorted_pairs, x_q, x_s, w13, w13_s, h_q, h_s, s);
+  err = launch_w13_small(d, sl13, expert_offsets, sorted_pairs, x_q, x_s, w13, w13_s, h_q, h_s, s);
   if (err != hipSuccess) return MOE_EHIP;
   if (any_xl) {
     if (large && xl13_supported(d))
@@ -260,14 +267,14 @@ int ffn_enqueue(const moe_dims& d, const uint16_t* x, const float* topk_weights,
       err = launch_w13_small(d, sxl, expert_offsets, sorted_pairs, x_q, x_s, w13, w13_s, h_q, h_s, s);
     if (err != hipSuccess) return MOE_EHIP;
   }
-  if (any_l && !fold) {
+  if (any_l && t13 < kLargeRows) {
     err = launch_w13_large(d, pw.large_items, pw.hdr + 1, pw.large_cap, kLargeRows, expert_offsets, sorted_pairs,
-                           x_q, x_s, w13, w13_s, h_q, h_s, s);
+                           x_q, x_s, w13, w13_s, h_q, h_s, s, pw.hdr + 3);
     if (err != hipSuccess) return MOE_EHIP;
   }
   record(dbg, MOE_EV_W13_DONE, s);
 
-  err = launch_w2_small(d, sl, expert_offsets, sorted_pairs, h_q, h_s, w2, w2_s, fw.o, fw.os, s);
+  err = launch_w2_small(d, sl2, expert_offsets, sorted_pairs, h_q, h_s, w2, w2_s, fw.o, fw.os, s);
   if (err != hipSuccess) return MOE_EHIP;
   const bool fewk = large && fewk2_supported(d);
   if (any_xl) {
@@ -284,13 +291,13 @@ int ffn_enqueue(const moe_dims& d, const uint16_t* x, const float* topk_weights,
       err = launch_w2_small(d, sxl, expert_offsets, sorted_pairs, h_q, h_s, w2, w2_s, fw.o, fw.os, s);
     if (err != hipSuccess) return MOE_EHIP;
   }
-  if (any_l && !fold) {
+  if (any_l && t2 < kLargeRows) {
     if (fewk)
       err = launch_w2_fewk(d, pw.large_items, pw.hdr + 1, pw.large_cap, kLargeRows, expert_offsets, sorted_pairs,
-                           h_q, h_s, w2, w2_s, fw.o, fw.os, s);
+                           h_q, h_s, w2, w2_s, fw.o, fw.os, s, pw.hdr + 4);
     else
       err = launch_w2_large(d, pw.large_items, pw.hdr + 1, pw.large_cap, kLargeRows, expert_offsets, sorted_pairs,
-                            h_q, h_s, w2, w2_s, fw.o, fw.os, s);
+                            h_q, h_s, w2, w2_s, fw.o, fw.os, s, pw.hdr + 4);
     if (err != hipSuccess) return MOE_EHIP;
   }
   record(dbg, MOE_EV_W2_DONE, s);

@@ -60,6 +60,19 @@ __device__ int block_exclusive_scan(int32_t* a, int n, int32_t* part) {
   return total;
 }
 
+// Sum of v over the block (every thread gets it); part[] as for the scan.
+__device__ int block_sum(int v, int32_t* part) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+  if (lane == 0) part[wave] = v;
+  __syncthreads();
+  int total = 0;
+  for (int w = 0; w < nw; ++w) total += part[w];
+  __syncthreads();
+  return total;
+}
+
 // Phase 1 for pairs [begin, end): local_rank[p - rank_base] = number of earlier
 // pairs of the same expert inside [begin, end); key[p - rank_base] (when given) =
 // the pair's expert, or -1 for an id outside [0, E). cursor[E] must start at zero
@@ -105,13 +118,16 @@ __device__ void local_ranks(const int32_t* __restrict__ ids, int begin, int end,
 }
 
 // Work lists from per-expert counts cnt[E] (LDS): small-M tiles of kSmallRows rows
-// for experts with 1..small_max pairs (expert order); the rest, heaviest expert
-// first (ties: lower id first), in 256-row items (the last one when more than 128
-// rows remain) and a 128-row item for a remainder of 1..128 rows.
-__device__ void build_worklists(const int32_t* cnt, int E, int small_max, int2* __restrict__ small_items,
-                                int64_t small_cap, int2* __restrict__ large_items, int64_t large_cap,
-                                int2* __restrict__ xl_items, int64_t xl_cap, int32_t* __restrict__ hdr,
-                                int32_t* a1, int32_t* a2, int32_t* part) {
+// for experts with 1..small_max pairs (expert order); the rest in 256-row items (the
+// last one when more than 128 rows remain), heaviest expert first (ties: lower id
+// first), and at most one 128-row item per expert for a remainder of 1..128 rows,
+// ordered by rows (ties: heavier expert, then lower id), so that the items of at
+// most t13 (t2) rows, which W13 (W2) walks as 16-row tiles, are a prefix whose
+// length goes to hdr[3] (hdr[4]).
+__device__ void build_worklists(const int32_t* cnt, int E, int small_max, int t13, int t2,
+                                int2* __restrict__ small_items, int64_t small_cap, int2* __restrict__ large_items,
+                                int64_t large_cap, int2* __restrict__ xl_items, int64_t xl_cap,
+                                int32_t* __restrict__ hdr, int32_t* a1, int32_t* a2, int32_t* part) {
   const int t = threadIdx.x, nt = blockDim.x;
   for (int e = t; e < E; e += nt) {
     const int m = cnt[e];
@@ -135,6 +151,8 @@ __device__ void build_worklists(const int32_t* cnt, int E, int small_max, int2* 
       hdr[0] = n_small < small_cap ? n_small : (int)small_cap;
       hdr[1] = 0;
       hdr[2] = 0;
+      hdr[3] = 0;
+      hdr[4] = 0;
     }
     return;
   }
@@ -162,22 +180,34 @@ __device__ void build_worklists(const int32_t* cnt, int E, int small_max, int2* 
     for (int i = 0; i < (m + kXlRows / 2 - 1) / kXlRows; ++i)
       if (s + i < xl_cap) xl_items[s + i] = make_int2(e, i * kXlRows);
   }
-  __syncthreads();
-  // 128-row remainders
-  for (int r = t; r < E; r += nt) {
-    const int m = r < n_big ? cnt[a2[r]] : 0, rem = m % kXlRows;
-    a1[r] = (rem >= 1 && rem <= kXlRows / 2) ? 1 : 0;
+  // 128-row remainders, by rows: the position of an expert's item is the number of
+  // remainders that order before it (the counts stay in cnt, read by every thread)
+  int c13 = 0, c2 = 0, n_large = 0;
+  for (int e = t; e < E; e += nt) {
+    const int m = cnt[e], rem = m % kXlRows;
+    if (m > small_max && rem >= 1 && rem <= kXlRows / 2) {
+      int pos = 0;
+      for (int f = 0; f < E; ++f) {
+        const int mf = cnt[f], rf = mf % kXlRows;
+        pos += (mf > small_max) && rf >= 1 && rf <= kXlRows / 2 &&
+               (rf < rem || (rf == rem && (mf > m || (mf == m && f < e))));
+      }
+      if (pos < large_cap) large_items[pos] = make_int2(e, m - rem);
+      n_large += 1;
+      c13 += rem <= t13;
+      c2 += rem <= t2;
+    }
   }
-  __syncthreads();
-  const int n_large = block_exclusive_scan(a1, E, part);
-  for (int r = t; r < n_big; r += nt) {
-    const int e = a2[r], m = cnt[e], rem = m % kXlRows;
-    if (rem >= 1 && rem <= kXlRows / 2 && a1[r] < large_cap) large_items[a1[r]] = make_int2(e, m - rem);
-  }
+  n_large = block_sum(n_large, part);
+  c13 = block_sum(c13, part);
+  c2 = block_sum(c2, part);
   if (t == 0) {
+    const int nl = n_large < large_cap ? n_large : (int)large_cap;
     hdr[0] = n_small < small_cap ? n_small : (int)small_cap;
-    hdr[1] = n_large < large_cap ? n_large : (int)large_cap;
+    hdr[1] = nl;
     hdr[2] = n_xl < xl_cap ? n_xl : (int)xl_cap;
+    hdr[3] = c13 < nl ? c13 : nl;
+    hdr[4] = c2 < nl ? c2 : nl;
   }
 }
 
@@ -196,6 +226,7 @@ struct PlanArgs {
   int32_t* block_base;
   int64_t small_cap, large_cap, xl_cap;
   int P, E, nbits, small_max, nb;
+  int t13, t2;   // tile_small_rows of W13 and W2
 };
 
 // Single-block plan: all three phases in one launch (P <= kPlanChunk).
@@ -234,7 +265,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan_fused(PlanArgs a) {
     }
     if (p >= n_valid) a.sorted_pairs[p] = -1;
   }
-  build_worklists(cnt, E, a.small_max, a.small_items, a.small_cap, a.large_items, a.large_cap, a.xl_items, a.xl_cap,
+  build_worklists(cnt, E, a.small_max, a.t13, a.t2, a.small_items, a.small_cap, a.large_items, a.large_cap, a.xl_items, a.xl_cap,
                   a.hdr, a1, a2, part);
 }
 
@@ -312,7 +343,7 @@ __global__ __launch_bounds__(kScanThreads) void k_plan_scan(PlanArgs a) {
   }
   __syncthreads();
   for (int e = t; e <= E; e += kScanThreads) a.offsets[e] = off[e];
-  build_worklists(cnt, E, a.small_max, a.small_items, a.small_cap, a.large_items, a.large_cap, a.xl_items, a.xl_cap,
+  build_worklists(cnt, E, a.small_max, a.t13, a.t2, a.small_items, a.small_cap, a.large_items, a.large_cap, a.xl_items, a.xl_cap,
                   a.hdr, a1, a2, part);
 }
 
@@ -332,6 +363,34 @@ __global__ __launch_bounds__(256) void k_plan_scatter(PlanArgs a) {
 }
 
 }  // namespace
+
+namespace {
+// The tuned exact-shape table: for a shape (H, I), the largest 128-row item (rows)
+// that W13 and W2 walk as 16-row small-M tiles rather than one 128-row tile; 0 =
+// none. Measured on MI355X with tune_tiles.py on the routing histograms of the
+// 32K-token prefill chunk (236 such items, 10 of them at most 16 rows), one MoE-TP8
+// rank of it and the 256-token decode step. A 16-row pass re-streams the expert's
+// weight slice, so only items of at most 16 rows gain, and only in W13 at the full
+// intermediate size (9.44 vs 9.53 ms); every larger limit is slower in both GEMMs.
+struct TileRule {
+  int H, I, w13, w2;
+};
+constexpr TileRule kTileTable[] = {
+    {7168, 3072, 16, 0},
+    {7168, 384, 0, 0},
+};
+}  // namespace
+
+int tile_small_rows(const moe_dims& d, bool w13) {
+  const int64_t P = (int64_t)d.T * d.K;
+  if (P <= kFoldPairs || !large_path_supported(d)) return kLargeRows;
+  const int v = w13 ? d.tile_w13 : d.tile_w2;
+  if (v < 0) return 0;
+  if (v > 0) return v < kLargeRows ? v : kLargeRows;
+  for (const TileRule& r : kTileTable)
+    if (r.H == d.H && r.I == d.I) return w13 ? r.w13 : r.w2;
+  return 0;
+}
 
 size_t plan_ws_layout(const moe_dims& d, void* base, PlanWs* out) {
   const int64_t P = (int64_t)d.T * d.K;
@@ -391,6 +450,8 @@ hipError_t launch_plan(const moe_dims& d, const int32_t* ids, int32_t* offsets, 
   while ((1 << nbits) < d.E) ++nbits;
   a.nbits = nbits;
   a.small_max = small_max_of(d);
+  a.t13 = tile_small_rows(d, true);
+  a.t2 = tile_small_rows(d, false);
   a.nb = (int)ws.nb;
   if (a.P <= kPlanChunk) {
     const size_t lds = sizeof(int32_t) * ((size_t)(kPlanWaves + 4) * d.E + 1 + kPlanThreads + 2 * (size_t)a.P);

@@ -60,6 +60,14 @@ def test_validate_flags():
     assert moe.validate(moe.make_dims(4, 256, 512, 8, 2, flags=-1)) == moe.MOE_EINVAL
 
 
+def test_validate_tile_fields():
+    for v in (-1, 0, 1, 64, 128):
+        assert moe.validate(moe.make_dims(4, 256, 512, 8, 2, tile_w13=v, tile_w2=v)) == moe.MOE_OK
+    for v in (-2, 129):
+        assert moe.validate(moe.make_dims(4, 256, 512, 8, 2, tile_w13=v)) == moe.MOE_EINVAL
+        assert moe.validate(moe.make_dims(4, 256, 512, 8, 2, tile_w2=v)) == moe.MOE_EINVAL
+
+
 def test_validate_a16_limits():
     # no shared expert with bf16 activations
     assert moe.validate(moe.make_dims(4, 256, 512, 8, 2, Is=128, flags=moe.FLAG_A16)) == moe.MOE_EUNSUPPORTED

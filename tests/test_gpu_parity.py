@@ -396,3 +396,48 @@ def test_ffn_tp8rank32k_full(dev):
     p, (y, dbg) = run_path(inp)
     check_plan(p, inp.topk_ids.cpu().numpy(), inp.wl.E)
     check_ffn(inp, p, y, dbg, label="tp8rank32k full")
+
+
+# ----------------------------------------------------------------------------- exact-shape tiling per GEMM
+
+def _sized_routing(sizes, K, seed):
+    """topk_ids [T, K] with exactly sizes[e] pairs routed to expert e (distinct
+    experts per token are not required: duplicates are independent pairs)."""
+    rng = np.random.default_rng(seed)
+    ids = np.concatenate([np.full(m, e, dtype=np.int32) for e, m in enumerate(sizes)])
+    rng.shuffle(ids)
+    return torch.from_numpy(ids.reshape(-1, K).copy())
+
+
+def test_tile_choice_per_gemm_is_bitwise_neutral(dev):
+    """Expert sizes covering every item kind above the decode fold (P > 512): a
+    remainder of 44 and 88 rows after 256-row items, whole experts of 17, 20 and 100
+    rows (one 128-row item each), a 129-row expert and a 256 + 144-row one (partial
+    256-row items), and a 256-row expert with no remainder. Whatever prefix of the 128-row items (sorted by rows) each GEMM
+    walks as 16-row tiles, y and the SwiGLU codes are identical bit for bit; the
+    planner's per-GEMM counts follow the thresholds; the result matches the oracle."""
+    sizes = [300, 400, 20, 100, 129, 256, 17, 600]
+    K = 2
+    T = sum(sizes) // K
+    wl = scaled("tiny", T=T, H=1024, I=512, E=len(sizes), K=K, seed=121, weight_seed=121, name="tiles")
+    inp = make_inputs(wl).to(dev)
+    inp.topk_ids = _sized_routing(sizes, K, 121).to(dev)
+    packed = moe.pack_weights(inp.weights)
+    rems = sorted(m % 256 for m in sizes if m > 16 and 1 <= m % 256 <= 128)
+    assert rems == [17, 20, 44, 88, 100]
+    outs = []
+    for t13, t2 in ((-1, -1), (128, 128), (44, 20), (20, 100), (1, 99)):
+        p = moe.plan(inp.topk_ids, wl.E, wl.H, wl.I, tile_w13=t13, tile_w2=t2)
+        y, dbg = moe.ffn(inp.x, inp.topk_weights, p, packed, debug=True)
+        torch.cuda.synchronize()
+        hdr = p.ws[:20].view(torch.int32).cpu().numpy()
+        cnt = lambda t: sum(r <= t for r in rems) if t > 0 else 0
+        assert hdr[1] == len(rems) and hdr[3] == cnt(t13) and hdr[4] == cnt(t2), (t13, t2, hdr)
+        rows = p.pair_rows.cpu().numpy()
+        order = rows[rows >= 0]
+        outs.append((u16(y), dbg["h_q"].cpu().numpy()[order], dbg["h_s"].cpu().numpy()[order]))
+        if t13 == 44:
+            check_ffn(inp, p, y, dbg, label=f"tiles w13<={t13} w2<={t2}")
+    for o in outs[1:]:
+        for a, b in zip(outs[0], o):
+            assert np.array_equal(a, b)
