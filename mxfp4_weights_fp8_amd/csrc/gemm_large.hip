@@ -56,7 +56,9 @@ constexpr int kMaxKS = 64;                // K steps whose activation scales fit
 // scales 68 B per routed row (17 dwords).
 constexpr int kSaGroup = 8 * kScaleSteps * 4 + 32;   // bytes per 8-row group
 constexpr int kSbRow = kMaxKS + 4;
-constexpr int kSbBytes = (kTokTile * kSbRow + 255) / 256 * 256;   // whole 256-byte copy blocks
+// whole rounds of the 4 waves' 256-byte dword copies (the last round runs past the
+// tile's 128 * 68 bytes: without this padding it wrote into the next LDS array)
+constexpr int kSbBytes = (kTokTile * kSbRow + 1023) / 1024 * 1024;
 
 struct LargeArgs {
   const int2* items;
@@ -125,7 +127,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_large(LargeArgs a) {
   // row load bytes, all loads issued before the first LDS store.
   const v4i_s ras = rsrc4(a.act_s, a.act_s_bytes);
   constexpr int kSbDw = kSbRow / 4;                       // 17 dwords per row
-  constexpr int kSbDma = (kTokTile * kSbDw + 255) / 256;  // dword copies per wave
+  constexpr int kSbDma = (kTokTile * kSbDw + 255) / 256;  // rounds of copies (one per wave and round)
+  static_assert(kSbDma * 4 * 256 <= kSbBytes, "the activation-scale copies stay inside sSb");
   auto issue_act_scales = [&]() {
 #pragma unroll
     for (int i = 0; i < kSbDma; ++i) {

@@ -47,11 +47,15 @@ def u16(t: torch.Tensor) -> np.ndarray:
 
 
 def run_path(inp, small_max=0, debug=True, flags=0):
-    """plan + ffn on the GPU for MoEInputs already on the device."""
+    """plan + ffn on the GPU for MoEInputs already on the device. The workspace and
+    y start as 0xFF bytes (NaN as fp16 and bf16), so a row that no kernel writes
+    shows up in the comparison with the oracle instead of passing on stale data."""
     w = inp.wl
     p = moe.plan(inp.topk_ids, w.E, w.H, w.I, small_max=small_max, Is=w.Is if inp.shared else 0, flags=flags)
     packed = moe.pack_weights(inp.weights)
-    out = moe.ffn(inp.x, inp.topk_weights, p, packed, shared=inp.shared, debug=debug)
+    ws = torch.full((moe.ffn_workspace_bytes(p.dims),), 0xFF, dtype=torch.uint8, device=inp.x.device)
+    y = torch.full((w.T, w.H), -1, dtype=torch.int16, device=inp.x.device).view(torch.bfloat16)
+    out = moe.ffn(inp.x, inp.topk_weights, p, packed, shared=inp.shared, debug=debug, ws=ws, y=y)
     del packed
     torch.cuda.synchronize()
     return p, out

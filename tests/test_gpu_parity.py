@@ -9,9 +9,9 @@ import pytest
 import torch
 
 import mxfp4_weights_fp8_amd as moe
-from gpu_helpers import check_ffn, check_plan, run_path, say, u16
+from gpu_helpers import MAX_REL, check_ffn, check_plan, run_path, say, u16
 from oracle.formats import bf16_to_f64
-from oracle.moe import quant_act_ref
+from oracle.moe import ffn_ref, plan_ref, quant_act_ref
 from synth import WORKLOADS, make_expert_weights, make_inputs, make_routing, make_shared_weights, scaled
 
 pytestmark = pytest.mark.gpu
@@ -413,31 +413,61 @@ def test_tile_choice_per_gemm_is_bitwise_neutral(dev):
     """Expert sizes covering every item kind above the decode fold (P > 512): a
     remainder of 44 and 88 rows after 256-row items, whole experts of 17, 20 and 100
     rows (one 128-row item each), a 129-row expert and a 256 + 144-row one (partial
-    256-row items), and a 256-row expert with no remainder. Whatever prefix of the 128-row items (sorted by rows) each GEMM
-    walks as 16-row tiles, y and the SwiGLU codes are identical bit for bit; the
-    planner's per-GEMM counts follow the thresholds; the result matches the oracle."""
+    256-row items), and a 256-row expert with no remainder. Whatever prefix of the
+    128-row items (sorted by rows) each GEMM walks as 16-row tiles, y is identical
+    bit for bit, also with the workspace (which then holds the SwiGLU rows and the
+    per-pair rows) and y filled with other bytes beforehand (0xFF is NaN as fp16: a
+    row that no kernel wrote would show), and so are the SwiGLU codes; the planner's
+    per-GEMM counts follow the thresholds; the result matches the oracle."""
     sizes = [300, 400, 20, 100, 129, 256, 17, 600]
     K = 2
     T = sum(sizes) // K
+    P = T * K
     wl = scaled("tiny", T=T, H=1024, I=512, E=len(sizes), K=K, seed=121, weight_seed=121, name="tiles")
     inp = make_inputs(wl).to(dev)
     inp.topk_ids = _sized_routing(sizes, K, 121).to(dev)
     packed = moe.pack_weights(inp.weights)
     rems = sorted(m % 256 for m in sizes if m > 16 and 1 <= m % 256 <= 128)
     assert rems == [17, 20, 44, 88, 100]
-    outs = []
-    for t13, t2 in ((-1, -1), (128, 128), (44, 20), (20, 100), (1, 99)):
-        p = moe.plan(inp.topk_ids, wl.E, wl.H, wl.I, tile_w13=t13, tile_w2=t2)
-        y, dbg = moe.ffn(inp.x, inp.topk_weights, p, packed, debug=True)
-        torch.cuda.synchronize()
-        hdr = p.ws[:20].view(torch.int32).cpu().numpy()
-        cnt = lambda t: sum(r <= t for r in rems) if t > 0 else 0
-        assert hdr[1] == len(rems) and hdr[3] == cnt(t13) and hdr[4] == cnt(t2), (t13, t2, hdr)
-        rows = p.pair_rows.cpu().numpy()
-        order = rows[rows >= 0]
-        outs.append((u16(y), dbg["h_q"].cpu().numpy()[order], dbg["h_s"].cpu().numpy()[order]))
-        if t13 == 44:
-            check_ffn(inp, p, y, dbg, label=f"tiles w13<={t13} w2<={t2}")
-    for o in outs[1:]:
-        for a, b in zip(outs[0], o):
-            assert np.array_equal(a, b)
+    ids = inp.topk_ids.cpu().numpy()
+    configs = ((-1, -1), (128, 128), (44, 20), (20, 100), (1, 99))
+    cnt = lambda t: sum(r <= t for r in rems) if t > 0 else 0
+    ref_plan = plan_ref(ids, wl.E)
+    ys, codes, labels, plan_ok = [], [], [], []
+    for fill in (0xFF, 0x00, 0x5A):
+        for t13, t2 in configs:
+            p = moe.plan(inp.topk_ids, wl.E, wl.H, wl.I, tile_w13=t13, tile_w2=t2)
+            ws = torch.full((moe.ffn_workspace_bytes(p.dims),), fill, dtype=torch.uint8, device=dev)
+            y = torch.full((T, wl.H), fill * 0x101 - (0x10000 if fill >= 0x80 else 0), dtype=torch.int16,
+                           device=dev).view(torch.bfloat16)
+            moe.ffn(inp.x, inp.topk_weights, p, packed, ws=ws, y=y)
+            torch.cuda.synchronize()
+            hdr = p.ws[:20].view(torch.int32).cpu().numpy()
+            assert hdr[1] == len(rems) and hdr[3] == cnt(t13) and hdr[4] == cnt(t2), (t13, t2, hdr)
+            plan_ok.append(np.array_equal(p.sorted_pairs.cpu().numpy()[:P], ref_plan["sorted_pairs"]) and
+                           np.array_equal(p.pair_rows.cpu().numpy()[:P], ref_plan["pair_rows"]) and
+                           np.array_equal(p.expert_offsets.cpu().numpy(), ref_plan["expert_offsets"]))
+            ys.append(u16(y))
+            labels.append(f"fill {fill:#x} tiles w13<={t13} w2<={t2}")
+            if fill == 0x00:
+                y2, dbg = moe.ffn(inp.x, inp.topk_weights, p, packed, debug=True)
+                torch.cuda.synchronize()
+                rows = p.pair_rows.cpu().numpy()
+                order = rows[rows >= 0]
+                codes.append((dbg["h_q"].cpu().numpy()[order], dbg["h_s"].cpu().numpy()[order]))
+                if t13 == 44:
+                    check_ffn(inp, p, y2, dbg, label=labels[-1])
+    mismatch = [i for i in range(1, len(ys)) if not np.array_equal(ys[0], ys[i])]
+    if mismatch:
+        ref = ffn_ref(inp.x, inp.topk_ids, inp.topk_weights, **inp.weights)["y"]
+        sc = np.abs(ref).max()
+        for i, (lab, a) in enumerate(zip(labels, ys)):
+            err = np.abs(bf16_to_f64(a) - ref) / sc
+            bad = np.nonzero(~(err.max(axis=1) <= MAX_REL))[0]
+            cols = np.nonzero(~(err[bad] <= MAX_REL).all(axis=0))[0] if bad.size else np.zeros(0, int)
+            say(f"[tiles] '{lab}': plan arrays {'ok' if plan_ok[i] else 'DIFFER from plan_ref'}; tokens off the "
+                f"oracle {bad.size} {bad[:8].tolist()} (experts {ids[bad[:8]].tolist()}), columns {cols.size} "
+                f"[{cols.min() if cols.size else '-'}..{cols.max() if cols.size else '-'}]")
+    assert not mismatch, [labels[i] for i in mismatch]
+    for c in codes[1:]:
+        assert np.array_equal(codes[0][0], c[0]) and np.array_equal(codes[0][1], c[1])
