@@ -203,7 +203,7 @@ def decode_object(r: Runner, steps: int, warmup: int, flush: torch.Tensor) -> di
     if chain:
         dom_bytes = r.distinct * (eb["w13"] + eb["w2"]) + w.T * (w.H + w.H // 128) + w.T * w.H * 2
         dom_name = "decode chain: W13 + SwiGLU/requant, W2, combine in one launch (k_decode_chain)"
-        traffic = measured_traffic(w.name, "moe::k_decode_chain")
+        traffic = measured_traffic(w.name + "_chain", "moe::k_decode_chain")
     elif a16:
         dom_bytes = r.distinct * eb["w13"] + w.T * w.H * 2 + P * w.I * 2
         dom_name = ("W13 stage, NVFP4 weights, bf16 activations: grouped GEMM + SwiGLU (k_w13_a16<true>)" if nv else

@@ -156,16 +156,30 @@ __device__ void build_worklists(const int32_t* cnt, int E, int small_max, int t1
     }
     return;
   }
-  // heavy-first order of the large experts: a2[rank] = expert
-  for (int e = t; e < E; e += nt) {
+  // Ranks of the large experts, one expert per wave (its lanes compare it with E/64
+  // experts each, two wave sums): the heavy-first rank r (a2[r] = expert), and for an
+  // expert with a 128-row item (a remainder of 1..128 rows) that item's position in
+  // the by-rows order, where it is written.
+  const int lane = t & 63, wave = t >> 6, nwaves = nt >> 6;
+  for (int e = wave; e < E; e += nwaves) {
     const int m = cnt[e];
-    if (m > small_max) {
-      int r = 0;
-      for (int f = 0; f < E; ++f) {
-        const int mf = cnt[f];
-        r += (mf > small_max) && (mf > m || (mf == m && f < e));
-      }
+    if (m <= small_max) continue;                        // wave-uniform
+    const int rem = m % kXlRows;
+    int r = 0, pos = 0;
+    for (int f = lane; f < E; f += 64) {
+      const int mf = cnt[f], rf = mf % kXlRows;
+      const bool before = mf > m || (mf == m && f < e);   // heavier, or as heavy with a lower id
+      r += (mf > small_max) && before;
+      pos += (mf > small_max) && rf >= 1 && rf <= kXlRows / 2 && (rf < rem || (rf == rem && before));
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      r += __shfl_xor(r, off);
+      pos += __shfl_xor(pos, off);
+    }
+    if (lane == 0) {
       a2[r] = e;
+      if (rem >= 1 && rem <= kXlRows / 2 && pos < large_cap) large_items[pos] = make_int2(e, m - rem);
     }
   }
   for (int e = t; e < E; e += nt) a1[e] = cnt[e] > small_max ? 1 : 0;
@@ -180,19 +194,11 @@ __device__ void build_worklists(const int32_t* cnt, int E, int small_max, int t1
     for (int i = 0; i < (m + kXlRows / 2 - 1) / kXlRows; ++i)
       if (s + i < xl_cap) xl_items[s + i] = make_int2(e, i * kXlRows);
   }
-  // 128-row remainders, by rows: the position of an expert's item is the number of
-  // remainders that order before it (the counts stay in cnt, read by every thread)
+  // 128-row items (written above): their number, and how many have at most t13 / t2 rows
   int c13 = 0, c2 = 0, n_large = 0;
   for (int e = t; e < E; e += nt) {
     const int m = cnt[e], rem = m % kXlRows;
     if (m > small_max && rem >= 1 && rem <= kXlRows / 2) {
-      int pos = 0;
-      for (int f = 0; f < E; ++f) {
-        const int mf = cnt[f], rf = mf % kXlRows;
-        pos += (mf > small_max) && rf >= 1 && rf <= kXlRows / 2 &&
-               (rf < rem || (rf == rem && (mf > m || (mf == m && f < e))));
-      }
-      if (pos < large_cap) large_items[pos] = make_int2(e, m - rem);
       n_large += 1;
       c13 += rem <= t13;
       c2 += rem <= t2;
