@@ -2,8 +2,10 @@
 cannot call hipMalloc) against moe_ffn on the same inputs, through the C-ABI:
 bit-identical y and SwiGLU codes on two calls in a row on one GPU (the second
 smaller, so it runs over the first call's leftovers in the static scratch), with
-and without the shared expert; a call whose workspace exceeds the static
-scratch is refused on the host with MOE_ESCRATCH and leaves y untouched."""
+and without the shared expert, and with bf16 activations (MOE_FLAG_A16), also with
+every intermediate row (activation codes, SwiGLU rows, per-pair rows) held in the
+static scratch; a call whose workspace exceeds the static scratch is refused on
+the host with MOE_ESCRATCH and leaves y untouched."""
 
 import numpy as np
 import pytest
@@ -41,6 +43,23 @@ def test_static_scratch_matches_workspace_on_consecutive_calls(gpu, shared):
         assert torch.equal(y0, y1)
         for k in ("x_q", "x_s", "h_q", "h_s") + (("sh_q", "sh_s") if shared else ()):
             assert torch.equal(g0[k], g1[k]), k
+
+
+@pytest.mark.parametrize("flags", [0, moe.FLAG_A16])
+def test_static_scratch_holds_every_intermediate(gpu, flags):
+    """No debug outputs: the activation codes, SwiGLU rows and per-pair rows all
+    live in the scratch; y bit-identical to moe_ffn's on two calls in a row."""
+    for T, seed in ((300, 74), (5, 75)):
+        wl = scaled("tiny", T=T, H=1024, I=512, E=6, K=4, seed=seed, weight_seed=seed, name="static_nodbg")
+        inp = make_inputs(wl).to(gpu)
+        p = moe.plan(inp.topk_ids, wl.E, wl.H, wl.I, flags=flags)
+        assert moe.ffn_workspace_bytes(p.dims) <= moe.FFN_STATIC_MAX_BYTES
+        W = moe.pack_weights(inp.weights)
+        y_ws = moe.ffn(inp.x, inp.topk_weights, p, W)
+        y_st = moe.ffn(inp.x, inp.topk_weights, p, W, static=True)
+        torch.cuda.synchronize()
+        say(f"[static scratch, no debug] T={T} flags={flags}")
+        assert torch.equal(y_ws, y_st)
 
 
 def test_static_scratch_refuses_oversized_calls(gpu):
