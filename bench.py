@@ -12,9 +12,13 @@ decode step (32 requests x 8 positions) as "decode256" (HBM roofline), the
 GEMM) and one MoE-TP8 rank of it as "tp8rank32k" (MFMA and HBM bounds), because
 the metric names them; "decode7_a16" and "decode256_a16" time the two decode
 steps with bf16 activations (the MXFP4A16 variant, MOE_FLAG_A16), and
-"decode7_nvfp4" / "decode256_nvfp4" with NVFP4 expert weights (moe_ffn_nvfp4). Kernel durations come from HIP events the library records
-on the stream it launches on; the oracle's CPU time on bounded samples is
-reported as cpu_baseline.
+"decode7_nvfp4" / "decode256_nvfp4" with NVFP4 expert weights (moe_ffn_nvfp4).
+Kernel durations come from HIP events the library records on the stream it
+launches on (in the decode objects on every 4th timed step: an event record costs
+about 3 us of stream time); the oracle's CPU time on bounded samples is reported
+as cpu_baseline. The prefill objects also time the vendor library's dense FP8
+GEMM on each GEMM's total shape (``dense_fp8_gemm_reference``), as a practical
+reference for the MFMA fraction.
 
 Every workload is timed twice: back-to-back steps (the contract's timed region,
 ``ms_per_step``), and steps each preceded by a 1 GiB read that evicts the
@@ -114,22 +118,26 @@ class Runner:
         moe.ffn(self.inp.x, self.inp.topk_weights, self.plan, self.inp.weights, shared=self.inp.shared,
                 ws=self.ws, y=self.y, events=events)
 
-    def run(self, steps: int, warmup: int, focus=(moe.EV_QUANT_DONE, moe.EV_W13_DONE)):
-        """Warmup, then `steps` timed steps. In the timed steps the library records
-        only the two events around the focus stage (each event record costs a few
-        microseconds of stream time). Returns (ms per step, focus stage ms, per-stage
-        ms from a separate untimed pass with every stage event)."""
+    def run(self, steps: int, warmup: int, focus=(moe.EV_QUANT_DONE, moe.EV_W13_DONE), every: int = 1):
+        """Warmup, then `steps` timed steps. In every `every`-th timed step (from the
+        first) the library records the two events around the focus stage, and only
+        those: each event record costs about 3 us of stream time (decode7: 0.2274
+        ms per step with the events on every step, 0.2222 on every 4th, 0.2210 with
+        none, one box). Returns (ms per step, focus stage ms averaged over the timed
+        steps that recorded it, per-stage ms from a separate untimed pass with every
+        stage event)."""
         for _ in range(warmup):
             self.step()
         torch.cuda.synchronize()
-        evs = [moe.StageEvents(only=focus) for _ in range(steps)]
+        evs = [moe.StageEvents(only=focus) if i % every == 0 else None for i in range(steps)]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(steps):
             self.step(evs[i])
         torch.cuda.synchronize()
         t1 = time.perf_counter()
-        focus_ms = float(np.mean([e.elapsed_ms(*focus) for e in evs]))
+        self.focus_launches = sum(e is not None for e in evs)
+        focus_ms = float(np.mean([e.elapsed_ms(*focus) for e in evs if e is not None]))
         diag = [moe.StageEvents() for _ in range(max(3, min(steps, 10)))]
         for e in diag:
             self.step(e)
@@ -143,8 +151,10 @@ class Runner:
     def run_flushed(self, steps: int, flush: torch.Tensor, focus=(moe.EV_QUANT_DONE, moe.EV_W13_DONE)):
         """`steps` steps, each after a read of `flush` (1 GiB of clean lines that
         evict the 256 MB last-level cache), outside the events that time the step
-        (plan + FFN) and the focus stage. Returns (mean ms per step, mean
-        focus-stage ms)."""
+        (plan + FFN) and the focus stage. Returns (median ms per step, median
+        focus-stage ms, largest step ms): steps are timed one by one, and the median
+        keeps a rare stalled step (one of 50 took tens of ms once) from moving the
+        figure."""
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
                 moe.StageEvents(only=focus)) for _ in range(steps)]
         for i, (a, b, st) in enumerate(evs):
@@ -153,8 +163,9 @@ class Runner:
             self.step(st)
             b.record()
         torch.cuda.synchronize()
-        return (float(np.mean([a.elapsed_time(b) for a, b, _ in evs])),
-                float(np.mean([st.elapsed_ms(*focus) for _, _, st in evs])))
+        step_ms = [a.elapsed_time(b) for a, b, _ in evs]
+        return (float(np.median(step_ms)), float(np.median([st.elapsed_ms(*focus) for _, _, st in evs])),
+                float(np.max(step_ms)))
 
 
 def cpu_baseline(name: str, weights_dev, tokens) -> dict:
@@ -177,6 +188,9 @@ def cpu_baseline(name: str, weights_dev, tokens) -> dict:
                       f"{dt:.1f} s"}
 
 
+# The decode objects time their dominant launch with events on every 4th timed step:
+# the other steps run as a caller would run them, with no event records.
+DECODE_EVENT_EVERY = 4
 CHAIN_MAX_PAIRS = 512   # up to this many pairs MOE_FLAG_DECODE_CHAIN runs W13, W2 and the combine as one launch
 
 
@@ -197,8 +211,8 @@ def decode_object(r: Runner, steps: int, warmup: int, flush: torch.Tensor) -> di
     nv = bool(r.flags & moe.FLAG_NVFP4)
     a16 = bool(r.flags & (moe.FLAG_A16 | moe.FLAG_NVFP4))
     chain = bool(r.flags & moe.FLAG_DECODE_CHAIN) and P <= CHAIN_MAX_PAIRS and not a16
-    ms_step, dom_ms, stages = r.run(steps, warmup)
-    fl_step, fl_dom = r.run_flushed(steps, flush)
+    ms_step, dom_ms, stages = r.run(steps, warmup, every=DECODE_EVENT_EVERY)
+    fl_step, fl_dom, fl_max = r.run_flushed(steps, flush)
     eb = expert_bytes(w, nvfp4=nv)
     if chain:
         dom_bytes = r.distinct * (eb["w13"] + eb["w2"]) + w.T * (w.H + w.H // 128) + w.T * w.H * 2
@@ -234,14 +248,42 @@ def decode_object(r: Runner, steps: int, warmup: int, flush: torch.Tensor) -> di
         "roofline": {"bound": "hbm", "kernel": dom_name,
                      "achieved": gbs(dom_bytes, dom_ms), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs(dom_bytes, dom_ms) / HBM_PEAK_GBS, "traffic": traffic,
-                     "algorithmic_bytes_per_launch": dom_bytes, "avg_launch_ms": dom_ms},
+                     "algorithmic_bytes_per_launch": dom_bytes, "avg_launch_ms": dom_ms,
+                     "launches_timed": f"{r.focus_launches} of the {steps} timed steps (HIP events on the "
+                                       f"library's stream, every {DECODE_EVENT_EVERY}th step)"},
         "step_hbm_gbs": gbs(step_bytes, ms_step), "step_hbm_frac": gbs(step_bytes, ms_step) / HBM_PEAK_GBS,
         "step_algorithmic_bytes": step_bytes,
-        "mall_flushed": {"ms_per_step": fl_step, "value": w.T / (fl_step * 1e-3), "dominant_ms": fl_dom,
+        "mall_flushed": {"ms_per_step": fl_step, "max_ms_per_step": fl_max, "value": w.T / (fl_step * 1e-3),
+                         "dominant_ms": fl_dom,
                          "dominant_hbm_frac": gbs(dom_bytes, fl_dom) / HBM_PEAK_GBS,
                          "step_hbm_frac": gbs(step_bytes, fl_step) / HBM_PEAK_GBS},
         "stage_ms_untimed_pass": stages,
     }
+
+
+def dense_fp8_reference(M: int, N: int, K: int, dev, reps: int = 10) -> dict:
+    """The vendor library's dense FP8 GEMM (hipBLASLt through torch._scaled_mm: E4M3
+    operands, one scale per tensor, bf16 out) on the dense problem of the same total
+    shape, M rows x N outputs x K: no gather, no block scales, no fused epilogue, no
+    expert boundaries. Context for the MFMA fraction (what a tuned dense GEMM
+    reaches on this part at this shape), never part of a step."""
+    a = torch.randn((M, K), dtype=torch.bfloat16, device=dev).to(torch.float8_e4m3fn)
+    b = torch.randn((N, K), dtype=torch.bfloat16, device=dev).to(torch.float8_e4m3fn)
+    one = torch.ones((), dtype=torch.float32, device=dev)
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    for _ in range(3):
+        torch._scaled_mm(a, b.t(), one, one, out_dtype=torch.bfloat16, out=out)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        torch._scaled_mm(a, b.t(), one, one, out_dtype=torch.bfloat16, out=out)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    tf = 2.0 * M * N * K / (ms * 1e-3) / 1e12
+    del a, b, out
+    torch.cuda.empty_cache()
+    return {"shape_MNK": [M, N, K], "ms": ms, "tflops": tf, "frac_fp8_peak": tf / MFMA_PEAK_FP8_TFLOPS}
 
 
 def prefill_object(r: Runner, steps: int, flush: torch.Tensor) -> dict:
@@ -249,7 +291,7 @@ def prefill_object(r: Runner, steps: int, flush: torch.Tensor) -> dict:
     step against both the MFMA and the HBM bound, and the cache-flushed times."""
     w = r.w
     ps, p13_ms, stages = r.run(steps, 1)
-    fl_step, fl_w13 = r.run_flushed(steps, flush)
+    fl_step, fl_w13, fl_max = r.run_flushed(steps, flush)
     P = w.T * w.K
     f13 = 2.0 * P * (2 * w.I) * w.H
     f2 = 2.0 * P * w.H * w.I
@@ -262,7 +304,11 @@ def prefill_object(r: Runner, steps: int, flush: torch.Tensor) -> dict:
     step_bytes = r.distinct * (eb["w13"] + eb["w2"]) + shared_bytes + w.T * w.H * 2 * 2
     t13 = f13 / (p13_ms * 1e-3) / 1e12
     tstep = flops / (ps * 1e-3) / 1e12
-    log(f"[bench] {w.name}: {ps:.3f} ms/step ({fl_step:.3f} flushed), w13 {p13_ms:.3f} ms, stages {stages}")
+    ref13 = dense_fp8_reference(P, 2 * w.I, w.H, r.dev)
+    ref2 = dense_fp8_reference(P, w.H, w.I, r.dev)
+    t2 = f2 / (stages["w2"] * 1e-3) / 1e12
+    log(f"[bench] {w.name}: {ps:.3f} ms/step ({fl_step:.3f} flushed), w13 {p13_ms:.3f} ms, stages {stages}; "
+        f"dense FP8 GEMM of the same shapes: W13 {ref13['tflops']:.0f} TFLOP/s, W2 {ref2['tflops']:.0f} TFLOP/s")
     return {
         "value": w.T / (ps * 1e-3), "unit": "tokens/s", "ms_per_step": ps, "steps": steps,
         "config": {"workload": w.name, "tokens": w.T, "intermediate": w.I, "shared_intermediate": w.Is,
@@ -282,7 +328,14 @@ def prefill_object(r: Runner, steps: int, flush: torch.Tensor) -> dict:
                         "mfma_frac": tstep / MFMA_PEAK_FP8_TFLOPS,
                         "hbm_frac": step_bytes / (ps * 1e-3) / 1e9 / HBM_PEAK_GBS,
                         "ideal_ms": max(flops / (MFMA_PEAK_FP8_TFLOPS * 1e9), step_bytes / (HBM_PEAK_GBS * 1e6))},
-        "mall_flushed": {"ms_per_step": fl_step, "value": w.T / (fl_step * 1e-3), "w13_ms": fl_w13},
+        "mall_flushed": {"ms_per_step": fl_step, "max_ms_per_step": fl_max, "value": w.T / (fl_step * 1e-3),
+                         "w13_ms": fl_w13},
+        "dense_fp8_gemm_reference": {
+            "what": "hipBLASLt dense FP8 GEMM (torch._scaled_mm, per-tensor scales, bf16 out) on the dense "
+                    "problem of each GEMM's total shape (all pairs as rows): context, not part of the step",
+            "w13": ref13, "w2": ref2,
+            "w13_stage_vs_reference": t13 / ref13["tflops"],
+            "w2_stage_vs_reference": t2 / ref2["tflops"]},
         **({"shared_tflops": fs / (stages["shared"] * 1e-3) / 1e12} if w.Is else {}),
         "stage_ms_untimed_pass": stages,
     }
