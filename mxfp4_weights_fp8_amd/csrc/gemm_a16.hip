@@ -82,14 +82,13 @@ __device__ __forceinline__ v4i e2m1x8_bf16_nv(uint32_t w, float pow2, float f) {
 
 // An E4M3 block scale (finite, non-negative) as f * 2^k: pow2 = 2^k with
 // k = floor(log2 v) - 3 and f = v / 2^k, an integer 8 .. 15 (v >= 2^-9, the smallest
-// E4M3 subnormal, so k >= -12). A zero scale gives pow2 = 1 and f = 0, so its
-// block expands to zeros (an exponent taken from v = 0 would overflow the codes
-// to infinity first).
+// E4M3 subnormal, so k >= -12). With frexp's exponent x (v = g * 2^x, g in [0.5, 1))
+// k = x - 4; for v = 0 frexp gives x = 0, so pow2 = 2^-4 (finite codes) and f = 0,
+// and the block expands to zeros, with no test for zero.
 __device__ __forceinline__ void nv_scale(float v, float& pow2, float& f) {
-  const uint32_t b = __float_as_uint(v);
-  const bool zero = v == 0.f;
-  pow2 = zero ? 1.f : __uint_as_float((b & 0x7F800000u) - (3u << 23));
-  f = zero ? 0.f : (float)(8u + ((b >> 20) & 7u));
+  const int x = __builtin_amdgcn_frexp_expf(v);
+  pow2 = __builtin_amdgcn_ldexpf(0.0625f, x);   // 2^(x - 4)
+  f = __builtin_amdgcn_ldexpf(v, 4 - x);
 }
 
 __device__ __forceinline__ v4f mfma_bf16(v4i a, v4i b, v4f c) {
