@@ -11,14 +11,15 @@
 // routed-row fragments of every K step in registers (read once from memory), the
 // E2M1 codes and E8M0 scales of block b+1 are copied into the other half of a
 // double buffer while block b is multiplied and written, and the footprint (about
-// 52 KB of LDS, 212 VGPRs at three K steps) lets two workgroups share a CU.
+// 69 KB of LDS, 212 VGPRs at three K steps) lets two workgroups share a CU.
 //
 // Waves: a 2 x 2 grid, wave (wm, wn) = routed rows [64 wm, +64) (4 fragments, MFMA
 // B side, E4M3) x output columns [64 wn, +64) of the block (4 weight fragments,
 // MFMA A side), 16 accumulator tiles of v_mfma_scale_f32_16x16x128_f8f6f4.
 // LDS: weights [buffer][step][fragment][1 KB in the MFMA's lane order] (the
 // kernel-native layout, copied block by block); weight scales [buffer][row][4 KS B]
-// in their global order; the routed rows' output slots.
+// in their global order; the routed rows' output slots; 4 KB per wave for staging
+// output rows.
 #include "device_common.h"
 #include "host_internal.h"
 #include "lds_copy.h"
@@ -30,6 +31,70 @@ constexpr int kThreads = 256;
 constexpr int kRows = kLargeRows;   // routed rows per workgroup
 constexpr int kCols = 128;          // output columns per block (8 weight fragments)
 constexpr int kMaxKS = 3;
+
+// Output rows of a wave's 64 x 64 tile, stored through LDS. A row of the tile: its
+// first fp16 column (o), its first scale byte (os), and whether it is stored (ok;
+// padding rows are not).
+struct ORow {
+  uint16_t* o;
+  uint8_t* os;
+  bool ok;
+};
+constexpr int kStageBytes = 32 * 128;   // per wave: 32 rows x 64 fp16 columns
+
+// A wave's 64 x 64 output tile in acc[i][j] (lane (c, q): columns 16 i + 4 q .. +3 of
+// tile row 16 j + c), written as fp16 codes with one power-of-two scale per 32
+// columns (the codes and scale bytes of store_o_rows<4>). Written straight from the
+// MFMA layout, one store instruction covers 32-byte pieces of 16 rows; these rows
+// go through the wave's own LDS area instead, 32 rows at a time (16-byte chunk c of
+// row r at chunk c ^ (r % 8)), and are read back 8 lanes per row, so that each store
+// instruction writes whole 128-byte lines of 8 rows. (The few-K W2 at a MoE-TP8
+// rank's shape writes 4 GB of rows per call and is bound by these stores.) A
+// wave's LDS operations complete in order, so the area needs no barrier.
+// row_at(r), r = 0 .. 63: the tile row's ORow.
+template <typename RowFn>
+__device__ __forceinline__ void store_o_tile64(const v4f (&acc)[4][4], uint8_t* stage, const RowFn& row_at,
+                                               int lane) {
+  const int q = lane >> 4, c = lane & 15;
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+      const int j = 2 * half + jj;
+      int ex[2];
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        float m = 0.f;
+#pragma unroll
+        for (int i = 2 * b; i < 2 * b + 2; ++i)
+#pragma unroll
+          for (int k = 0; k < 4; ++k) m = fmaxf(m, fabsf(acc[i][j][k]));
+        m = fmaxf(m, __shfl_xor(m, 16));
+        m = fmaxf(m, __shfl_xor(m, 32));
+        ex[b] = o_exponent(m);
+      }
+      if (q == 0) {
+        const ORow w = row_at(16 * j + c);
+        if (w.ok) *reinterpret_cast<uint16_t*>(w.os) = (uint16_t)((ex[0] + 127) | ((ex[1] + 127) << 8));
+      }
+      const int r = 16 * jj + c;   // row of the staged half
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float inv = exp2_neg(ex[i >> 1]);
+        const int chunk = (2 * i + (q >> 1)) ^ (r & 7);
+        *reinterpret_cast<uint2*>(stage + r * 128 + chunk * 16 + 8 * (q & 1)) =
+            f16_pack4(acc[i][j][0] * inv, acc[i][j][1] * inv, acc[i][j][2] * inv, acc[i][j][3] * inv);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int r = 8 * k + (lane >> 3), chunk = lane & 7;
+      const v4i v = *reinterpret_cast<const v4i*>(stage + r * 128 + ((chunk ^ (r & 7)) << 4));
+      const ORow w = row_at(32 * half + r);
+      if (w.ok) *reinterpret_cast<v4i*>(w.o + 8 * chunk) = v;
+    }
+  }
+}
 
 struct FewKArgs {
   const int2* items;
@@ -58,6 +123,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_w2_fewk(FewKArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t sA[2][KS][8 * 1024];       // [buf][step][fragment][1 KB]
   __shared__ __attribute__((aligned(16))) uint8_t sSa[2][4 * kScaleCopies * 256];  // [buf][row][4 KS B] + padding
   __shared__ int sSlot[kRows];
+  __shared__ __attribute__((aligned(16))) uint8_t sStage[kThreads / 64][kStageBytes];
 
   const int item = (a.first ? a.first[0] : 0) + (int)(blockIdx.y >> a.item_shift);
   if (item >= a.n_items[0]) return;
@@ -154,18 +220,13 @@ __global__ __launch_bounds__(kThreads, 2) void k_w2_fewk(FewKArgs a) {
       }
     }
 
-    // per-pair rows of this block: lane (c, q) of routed-row fragment j holds output
-    // columns 16 i + 4 q .. +3 of the wave's 64
+    // per-pair rows of this block: tile row r is routed row 64 wm + r, at its slot
     const int col0 = (b_first + bi) * kCols + 64 * wn;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int row = 64 * wm + 16 * j + c;
+    store_o_tile64(acc, sStage[wave], [&](int r) {
+      const int row = 64 * wm + r;
       const int64_t slot = sSlot[row < nrows ? row : 0];
-      v4f r[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) r[i] = acc[i][j];
-      store_o_rows<4>(r, row < nrows, a.o + slot * a.H + col0 + q * 4, a.os + slot * (a.H / 32) + col0 / 32, q);
-    }
+      return ORow{a.o + slot * a.H + col0, a.os + slot * (a.H / 32) + col0 / 32, row < nrows};
+    }, lane);
     __syncthreads();   // every wave has read buffer buf before block bi+2 is copied into it
   }
 }
@@ -196,6 +257,7 @@ struct SharedFewKArgs {
 template <int KS>
 __global__ __launch_bounds__(kThreads, 1) void k_shared2_fewk(SharedFewKArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t sW[2][KS][kSCols * 128];   // [buf][step][row][128 B]
+  __shared__ __attribute__((aligned(16))) uint8_t sStage[kThreads / 64][kStageBytes];
 
   const int t0 = blockIdx.y * kRows;
   const int n_blocks = a.H / kSCols;
@@ -279,17 +341,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_shared2_fewk(SharedFewKArgs a) 
       }
     }
 
-    // lane (c, q) of token fragment j holds columns 16 i + 4 q .. +3 of the wave's 64
+    // tile row r is token t0 + 64 wm + r
     const int col0 = b * kSCols + 64 * wn;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int t = t0 + 64 * wm + 16 * j + c;
+    store_o_tile64(acc, sStage[wave], [&](int r) {
+      const int t = t0 + 64 * wm + r;
       const int64_t tt = t < a.T ? t : t0;
-      v4f r[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) r[i] = acc[i][j];
-      store_o_rows<4>(r, t < a.T, a.o + tt * a.H + col0 + q * 4, a.os + tt * (a.H / 32) + col0 / 32, q);
-    }
+      return ORow{a.o + tt * a.H + col0, a.os + tt * (a.H / 32) + col0 / 32, t < a.T};
+    }, lane);
     __syncthreads();   // every wave has read buffer buf before block bi+2 is copied into it
   }
 }
