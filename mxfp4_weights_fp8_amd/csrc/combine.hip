@@ -13,7 +13,15 @@ namespace moe {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kUniformMaxTokens = 4096;
 
+// UNIFORM: groups_per_row is a multiple of 64, so the 64 lanes of a wave serve one
+// token; its index is then made wave-uniform, and the token's pick weights and pair
+// rows come through scalar loads instead of one vector load per lane and pick. Used
+// for batches of at most kUniformMaxTokens, where the combine is a few waves bound
+// by load latency (decode7 0.2206 vs 0.2221 ms per step, 256 tokens 1.930 vs 1.932
+// ms); at 32K tokens, bound by streaming 4 GB of rows, it measured 0.6% slower.
+template <bool UNIFORM>
 __global__ __launch_bounds__(kThreads) void k_combine(const uint16_t* __restrict__ o, const uint8_t* __restrict__ os,
                                                        const float* __restrict__ w,
                                                        const int32_t* __restrict__ pair_rows,
@@ -21,7 +29,8 @@ __global__ __launch_bounds__(kThreads) void k_combine(const uint16_t* __restrict
                                                        const uint8_t* __restrict__ sos, uint16_t* __restrict__ y,
                                                        int64_t n_groups, int groups_per_row, int K) {
   for (int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x; g < n_groups; g += (int64_t)gridDim.x * kThreads) {
-    const int64_t t = g / groups_per_row;
+    int64_t t = g / groups_per_row;
+    if constexpr (UNIFORM) t = __builtin_amdgcn_readfirstlane((int)t);
     combine_group(o, os, w, pair_rows, so, sos, y, t, (int)(g - t * groups_per_row), groups_per_row, K);
   }
 }
@@ -35,8 +44,12 @@ hipError_t launch_combine(const uint16_t* o, const uint8_t* os, const float* top
   // one 8-column group per thread (measured at 32K tokens: 0.78 ms against 0.84 ms
   // with the grid capped at 8192 workgroups and a grid-stride loop)
   const int64_t ctas = ceil_div(n_groups, kThreads);
-  hipLaunchKernelGGL(k_combine, dim3((unsigned)ctas), dim3(kThreads), 0, s, o, os, topk_weights, pair_rows, so, sos, y,
-                     n_groups, H / 8, K);
+  if ((H / 8) % 64 == 0 && T <= kUniformMaxTokens)   // kThreads and the grid stride are multiples of 64 too
+    hipLaunchKernelGGL(k_combine<true>, dim3((unsigned)ctas), dim3(kThreads), 0, s, o, os, topk_weights, pair_rows,
+                       so, sos, y, n_groups, H / 8, K);
+  else
+    hipLaunchKernelGGL(k_combine<false>, dim3((unsigned)ctas), dim3(kThreads), 0, s, o, os, topk_weights, pair_rows,
+                       so, sos, y, n_groups, H / 8, K);
   return hipGetLastError();
 }
 
