@@ -290,7 +290,7 @@ def prefill_object(r: Runner, steps: int, flush: torch.Tensor) -> dict:
     """A prefill workload: tokens/s, the MFMA roofline of its W13 stage, the whole
     step against both the MFMA and the HBM bound, and the cache-flushed times."""
     w = r.w
-    ps, p13_ms, stages = r.run(steps, 1)
+    ps, p13_ms, stages = r.run(steps, 2)
     fl_step, fl_w13, fl_max = r.run_flushed(steps, flush)
     P = w.T * w.K
     f13 = 2.0 * P * (2 * w.I) * w.H
@@ -346,7 +346,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--prefill-steps", type=int, default=5)
+    ap.add_argument("--prefill-steps", type=int, default=8)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--only", choices=["decode7", "decode7_chain", "decode7_a16", "decode7_nvfp4", "decode256",
