@@ -42,8 +42,21 @@ using namespace small;
 
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
-constexpr int kW13Waves = 8;     // W13: 8 waves, one gate + one up fragment each (128 h columns)
-constexpr int kW2Waves = 4;      // W2: 4 waves of two fragments (128 output columns)
+// Work split per variant. Each 128-K step is four bf16 MFMAs per fragment, each
+// accumulating into the previous one, so a wave with more fragments has more
+// independent MFMA chains to interleave with the codes' expansion. Measured (one box,
+// bitwise-equal results, per step): MXFP4 x bf16 with W13 in 4 waves x (2 gate + 2 up
+// fragments) and W2 in 2 waves x 4 fragments: decode7 0.226 vs 0.246 ms and the
+// 256-token step 2.32 vs 2.80 ms against 8 x (1 + 1) and 4 x 2. NVFP4, whose codes take
+// four times the VALU work to expand, keeps 8 x (1 + 1) and 4 x 2: its 4 x (2 + 2) W13 ran
+// decode7 4% slower (0.366 vs 0.351 ms) and the 256-token step 3% faster, its 2 x 4 W2
+// decode7 1% slower.
+constexpr int kW13Waves = 4;      // MXFP4 W13: 4 waves, NG = 2 gate + 2 up fragments each (128 h columns)
+constexpr int kW13WavesNV = 8;    // NVFP4 W13: 8 waves, one gate + one up fragment each
+constexpr int kW2Waves = 2;       // MXFP4 W2: 2 waves of 4 fragments (128 output columns)
+constexpr int kW2Frags = 4;
+constexpr int kW2WavesNV = 4;     // NVFP4 W2: 4 waves of 2 fragments (128 output columns)
+constexpr int kW2FragsNV = 2;
 // K steps of codes in flight per wave: two (the ring then holds 52 registers, so
 // the kernels fit 4-5 waves per SIMD instead of 3; the codes' expansion is VALU
 // work that more waves hide better). Measured against four on one box, results
@@ -198,14 +211,16 @@ __device__ __forceinline__ void stream16(v4f* acc, const Stream16<NF, NV>& p, in
   }
 }
 
-// W13 unit: 128 h columns (nb) of one item, 8 waves x (one gate + one up fragment).
-// gs: NVFP4's per-expert tensor scales (unused for MXFP4).
-template <bool NV>
-__global__ __launch_bounds__(kW13Waves * 64) void k_w13_a16(
+// W13 unit: 128 h columns (nb) of one item, WAVES waves x (NG gate + NG up fragments),
+// NG = 8 / WAVES. gs: NVFP4's per-expert tensor scales (unused for MXFP4).
+template <bool NV, int WAVES>
+__global__ __launch_bounds__(WAVES * 64) void k_w13_a16(
     const SmallLists lists, const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_pairs,
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ w13, const uint8_t* __restrict__ w13_s,
     const float* __restrict__ gs, uint16_t* __restrict__ h, int H, int I, int K) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t sS[];   // MXFP4: per wave 2 runs of 16 rows x H/32
+  constexpr int NG = 8 / WAVES;
+  constexpr int NF = 2 * NG;
+  extern __shared__ __attribute__((aligned(16))) uint8_t sS[];   // MXFP4: per wave 2 runs of 16 NG rows x H/32
   const int l = blockIdx.y >= lists.cap0;
   const int item = blockIdx.y - (l ? lists.cap0 : 0);
   if (item >= lists.n_items[l][0]) return;
@@ -219,26 +234,27 @@ __global__ __launch_bounds__(kW13Waves * 64) void k_w13_a16(
   const int KS = H / 128;
   const int64_t wrow = H / 2;
 
-  Stream16<2, NV> p;
+  Stream16<NF, NV> p;
   p.w = make_rsrc(w13 + (int64_t)e * 2 * I * wrow, (uint32_t)(2 * I * wrow));
   p.x = make_rsrc(x, 0xFFFFFFFFu);
-  const int n_gate = nb * 128 + wave * 16;   // first gate row of the wave; up row I + n_gate
-  p.wo[0] = n_gate * (int)wrow + lane * 16;
-  p.wo[1] = (I + n_gate) * (int)wrow + lane * 16;
+  const int n_gate = nb * 128 + wave * 16 * NG;   // first gate row of the wave; up row I + n_gate
+#pragma unroll
+  for (int f = 0; f < NF; ++f) p.wo[f] = ((f < NG ? 0 : I) + n_gate + 16 * (f % NG)) * (int)wrow + lane * 16;
   float g_scale = 1.f;
   if constexpr (NV) {
     const int64_t srow = H / 16;
     p.s = make_rsrc(w13_s + (int64_t)e * 2 * I * srow, (uint32_t)(2 * I * srow));
-    p.so[0] = (n_gate + c) * (int)srow + 4 * (q >> 1);
-    p.so[1] = (I + n_gate + c) * (int)srow + 4 * (q >> 1);
+#pragma unroll
+    for (int f = 0; f < NF; ++f)
+      p.so[f] = ((f < NG ? 0 : I) + n_gate + 16 * (f % NG) + c) * (int)srow + 4 * (q >> 1);
     g_scale = gs[e];
   } else {
     const int64_t srow = H / 32;
-    const int run = staged_bytes(16 * (int)srow);
+    const int run = staged_bytes(16 * NG * (int)srow);
     stage_scales(w13_s + ((int64_t)e * 2 * I + n_gate) * srow, w13_s + ((int64_t)e * 2 * I + I + n_gate) * srow,
-                 16 * (int)srow, sS + wave * 2 * run, lane);
-    p.sl[0] = sS + wave * 2 * run + c * srow;
-    p.sl[1] = sS + wave * 2 * run + run + c * srow;
+                 16 * NG * (int)srow, sS + wave * 2 * run, lane);
+#pragma unroll
+    for (int f = 0; f < NF; ++f) p.sl[f] = sS + wave * 2 * run + (f < NG ? 0 : run) + (16 * (f % NG) + c) * srow;
   }
 
   for (int m0 = it.y; m0 < it.y + item_rows && e_begin + m0 < e_end; m0 += kSmallRows) {
@@ -247,36 +263,41 @@ __global__ __launch_bounds__(kW13Waves * 64) void k_w13_a16(
     const bool has = c < mcount;
     const int tok = sorted_pairs[row0 + (has ? c : 0)] / K;   // an absent column repeats the first row
     p.xo = (tok * H + 32 * q) * 2;
-    v4f acc[2] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};
-    stream16<2, NV>(acc, p, KS, q);
+    v4f acc[NF];
+#pragma unroll
+    for (int f = 0; f < NF; ++f) acc[f] = v4f{0.f, 0.f, 0.f, 0.f};
+    stream16<NF, NV>(acc, p, KS, q);
     if constexpr (NV) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        acc[0][i] *= g_scale;
-        acc[1][i] *= g_scale;
-      }
+      for (int f = 0; f < NF; ++f)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[f][i] *= g_scale;
     }
-    // lane (c, q): h columns n_gate + 4q .. +3 of routed row c, as bf16
+    // lane (c, q): h columns n_gate + 16 g + 4q .. +3 of routed row c, as bf16
     if (has) {
-      uint16_t* dst = h + (int64_t)(row0 + c) * I + n_gate + 4 * q;
-      const uint32_t lo = (uint32_t)bf16_rne(silu_mul(acc[0][0], acc[1][0])) |
-                          ((uint32_t)bf16_rne(silu_mul(acc[0][1], acc[1][1])) << 16);
-      const uint32_t hi = (uint32_t)bf16_rne(silu_mul(acc[0][2], acc[1][2])) |
-                          ((uint32_t)bf16_rne(silu_mul(acc[0][3], acc[1][3])) << 16);
-      *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        uint16_t* dst = h + (int64_t)(row0 + c) * I + n_gate + 16 * g + 4 * q;
+        const uint32_t lo = (uint32_t)bf16_rne(silu_mul(acc[g][0], acc[NG + g][0])) |
+                            ((uint32_t)bf16_rne(silu_mul(acc[g][1], acc[NG + g][1])) << 16);
+        const uint32_t hi = (uint32_t)bf16_rne(silu_mul(acc[g][2], acc[NG + g][2])) |
+                            ((uint32_t)bf16_rne(silu_mul(acc[g][3], acc[NG + g][3])) << 16);
+        *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
+      }
     }
   }
 }
 
-// W2 unit: 128 output columns of one item, 4 waves x two fragments; per-pair rows as
-// fp16 codes with one power-of-two scale per 32 columns (the wave's two fragments).
-template <bool NV>
-__global__ __launch_bounds__(kW2Waves * 64) void k_w2_a16(
+// W2 unit: WAVES * 16 * NF output columns of one item, WAVES waves x NF fragments;
+// per-pair rows as fp16 codes with one power-of-two scale per 32 columns (a pair of
+// the wave's fragments).
+template <bool NV, int WAVES, int NF>
+__global__ __launch_bounds__(WAVES * 64) void k_w2_a16(
     const SmallLists lists, const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_pairs,
     const uint16_t* __restrict__ h, const uint8_t* __restrict__ w2, const uint8_t* __restrict__ w2_s,
     const float* __restrict__ gs, uint16_t* __restrict__ o, uint8_t* __restrict__ os, int H, int I) {
-  constexpr int NF = 2;
-  extern __shared__ __attribute__((aligned(16))) uint8_t sS[];   // MXFP4: per wave 32 rows x I/32
+  static_assert(NF % 2 == 0, "whole 32-column scale blocks per wave");
+  extern __shared__ __attribute__((aligned(16))) uint8_t sS[];   // MXFP4: per wave 16 NF rows x I/32
   const int l = blockIdx.y >= lists.cap0;
   const int item = blockIdx.y - (l ? lists.cap0 : 0);
   if (item >= lists.n_items[l][0]) return;
@@ -286,7 +307,7 @@ __global__ __launch_bounds__(kW2Waves * 64) void k_w2_a16(
   const int e_begin = offsets[e], e_end = offsets[e + 1];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63, q = lane >> 4, c = lane & 15;
-  const int n_wave = blockIdx.x * 64 * NF + wave * 16 * NF;
+  const int n_wave = (blockIdx.x * WAVES + wave) * 16 * NF;
   if (n_wave >= H) return;
   const int KS = I / 128;
   const int64_t wrow = I / 2;
@@ -317,28 +338,38 @@ __global__ __launch_bounds__(kW2Waves * 64) void k_w2_a16(
     const bool has = c < mcount;
     const int hrow = row0 + (has ? c : 0);
     p.xo = (hrow * I + 32 * q) * 2;
-    v4f acc[NF] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};
+    v4f acc[NF];
+#pragma unroll
+    for (int f = 0; f < NF; ++f) acc[f] = v4f{0.f, 0.f, 0.f, 0.f};
     stream16<NF, NV>(acc, p, KS, q);
-    float m = 0.f;
+    int ex[NF / 2];
 #pragma unroll
-    for (int f = 0; f < NF; ++f)
+    for (int b = 0; b < NF / 2; ++b) {
+      float m = 0.f;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        if constexpr (NV) acc[f][k] *= g_scale;
-        m = fmaxf(m, fabsf(acc[f][k]));
-      }
-    m = fmaxf(m, __shfl_xor(m, 16));
-    m = fmaxf(m, __shfl_xor(m, 32));
-    const int ex = o_exponent(m);
-    const float inv = exp2_neg(ex);
+      for (int f = 2 * b; f < 2 * b + 2; ++f)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          if constexpr (NV) acc[f][k] *= g_scale;
+          m = fmaxf(m, fabsf(acc[f][k]));
+        }
+      m = fmaxf(m, __shfl_xor(m, 16));
+      m = fmaxf(m, __shfl_xor(m, 32));
+      ex[b] = o_exponent(m);
+    }
     if (has) {
       const int64_t slot = sorted_pairs[row0 + c];
       uint16_t* dst = o + slot * H + n_wave + q * 4;
 #pragma unroll
-      for (int f = 0; f < NF; ++f)
+      for (int f = 0; f < NF; ++f) {
+        const float inv = exp2_neg(ex[f / 2]);
         *reinterpret_cast<uint2*>(dst + f * 16) =
             f16_pack4(acc[f][0] * inv, acc[f][1] * inv, acc[f][2] * inv, acc[f][3] * inv);
-      if (q == 0) os[slot * (H / 32) + n_wave / 32] = (uint8_t)(ex + 127);
+      }
+      if (q == 0) {
+#pragma unroll
+        for (int b = 0; b < NF / 2; ++b) os[slot * (H / 32) + n_wave / 32 + b] = (uint8_t)(ex[b] + 127);
+      }
     }
   }
 }
@@ -350,14 +381,14 @@ hipError_t launch_w13_a16(const moe_dims& d, const SmallLists& lists, const int3
                           const float* w13_gs, uint16_t* h, hipStream_t s) {
   const int64_t max_items = (int64_t)lists.cap0 + lists.cap1;
   if (max_items <= 0) return hipSuccess;
-  const dim3 grid(d.I / 128, (unsigned)max_items), block(kW13Waves * 64);
+  const dim3 grid(d.I / 128, (unsigned)max_items);
   if (w13_gs) {
-    hipLaunchKernelGGL(k_w13_a16<true>, grid, block, 0, s, lists, offsets, sorted_pairs, x, w13, w13_s, w13_gs, h,
-                       d.H, d.I, d.K);
+    hipLaunchKernelGGL((k_w13_a16<true, kW13WavesNV>), grid, dim3(kW13WavesNV * 64), 0, s, lists, offsets,
+                       sorted_pairs, x, w13, w13_s, w13_gs, h, d.H, d.I, d.K);
   } else {
-    const size_t lds = (size_t)kW13Waves * 2 * staged_bytes(16 * (d.H / 32));
-    hipLaunchKernelGGL(k_w13_a16<false>, grid, block, lds, s, lists, offsets, sorted_pairs, x, w13, w13_s, nullptr,
-                       h, d.H, d.I, d.K);
+    const size_t lds = (size_t)kW13Waves * 2 * staged_bytes(16 * (8 / kW13Waves) * (d.H / 32));
+    hipLaunchKernelGGL((k_w13_a16<false, kW13Waves>), grid, dim3(kW13Waves * 64), lds, s, lists, offsets,
+                       sorted_pairs, x, w13, w13_s, nullptr, h, d.H, d.I, d.K);
   }
   return hipGetLastError();
 }
@@ -367,14 +398,15 @@ hipError_t launch_w2_a16(const moe_dims& d, const SmallLists& lists, const int32
                          const float* w2_gs, uint16_t* o, uint8_t* os, hipStream_t s) {
   const int64_t max_items = (int64_t)lists.cap0 + lists.cap1;
   if (max_items <= 0) return hipSuccess;
-  const dim3 grid((unsigned)ceil_div(d.H, 128), (unsigned)max_items), block(kW2Waves * 64);
   if (w2_gs) {
-    hipLaunchKernelGGL(k_w2_a16<true>, grid, block, 0, s, lists, offsets, sorted_pairs, h, w2, w2_s, w2_gs, o, os,
-                       d.H, d.I);
+    const dim3 grid((unsigned)ceil_div(d.H, kW2WavesNV * 16 * kW2FragsNV), (unsigned)max_items);
+    hipLaunchKernelGGL((k_w2_a16<true, kW2WavesNV, kW2FragsNV>), grid, dim3(kW2WavesNV * 64), 0, s, lists, offsets,
+                       sorted_pairs, h, w2, w2_s, w2_gs, o, os, d.H, d.I);
   } else {
-    const size_t lds = (size_t)kW2Waves * staged_bytes(16 * 2 * (d.I / 32));
-    hipLaunchKernelGGL(k_w2_a16<false>, grid, block, lds, s, lists, offsets, sorted_pairs, h, w2, w2_s, nullptr, o,
-                       os, d.H, d.I);
+    const dim3 grid((unsigned)ceil_div(d.H, kW2Waves * 16 * kW2Frags), (unsigned)max_items);
+    const size_t lds = (size_t)kW2Waves * staged_bytes(16 * kW2Frags * (d.I / 32));
+    hipLaunchKernelGGL((k_w2_a16<false, kW2Waves, kW2Frags>), grid, dim3(kW2Waves * 64), lds, s, lists, offsets,
+                       sorted_pairs, h, w2, w2_s, nullptr, o, os, d.H, d.I);
   }
   return hipGetLastError();
 }
