@@ -228,12 +228,12 @@ def decode_object(r: Runner, steps: int, warmup: int, flush: torch.Tensor) -> di
                    if P <= 128 else None)
     else:
         dom_bytes = r.distinct * eb["w13"] + w.T * (w.H + w.H // 128) + P * (w.I + w.I // 128)
-        dom_name = "W13 stage: grouped GEMM + SwiGLU/requant (k_w13_small<8>" + \
+        dom_name = "W13 stage: grouped GEMM + SwiGLU/requant (k_w13_small<4>" + \
             (" + large-M tiles)" if P > CHAIN_MAX_PAIRS else ")")
         # at most 512 pairs the stage is one launch; above, the small-M launch plus the
         # 256-row and 128-row launches (one dispatch each per step)
-        traffic = measured_traffic(w.name, "moe::k_w13_small<8>" if P <= CHAIN_MAX_PAIRS else
-                                   ["moe::k_w13_small<8>", "moe::k_gemm_xl<true>", "moe::k_gemm_large<true>"])
+        traffic = measured_traffic(w.name, "moe::k_w13_small<4>" if P <= CHAIN_MAX_PAIRS else
+                                   ["moe::k_w13_small<4>", "moe::k_gemm_xl<true>", "moe::k_gemm_large<true>"])
     # whole step: both weight sets of every touched expert, x in and y out (bf16)
     step_bytes = r.distinct * (eb["w13"] + eb["w2"]) + w.T * w.H * 2 * 2
     gbs = lambda b, ms: b / (ms * 1e-3) / 1e9
@@ -317,11 +317,11 @@ def prefill_object(r: Runner, steps: int, flush: torch.Tensor) -> dict:
         "mfma_frac_fp8_peak": tstep / MFMA_PEAK_FP8_TFLOPS,
         "roofline": {"bound": "mfma",
                      "kernel": "W13 stage: k_gemm_xl<true> (256-row items) + k_gemm_large<true> (128-row "
-                               "items) + k_w13_small<8> (items the exact-shape table sends to 16-row tiles) + "
+                               "items) + k_w13_small<4> (items the exact-shape table sends to 16-row tiles) + "
                                "SwiGLU/requant",
                      "achieved": t13, "peak": MFMA_PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
                      "frac": t13 / MFMA_PEAK_FP8_TFLOPS, "frac_of_fp4_peak": t13 / MFMA_PEAK_FP4_TFLOPS,
-                     "traffic": measured_traffic(w.name, ["moe::k_w13_small<8>", "moe::k_gemm_xl<true>",
+                     "traffic": measured_traffic(w.name, ["moe::k_w13_small<4>", "moe::k_gemm_xl<true>",
                                                           "moe::k_gemm_large<true>"]),
                      "algorithmic_flops_per_launch": f13, "avg_launch_ms": p13_ms},
         "step_bounds": {"algorithmic_flops": flops, "algorithmic_bytes": step_bytes,

@@ -30,12 +30,15 @@ namespace {
 using namespace small;
 
 constexpr int kThreads = 256;
-// Work split (measured on decode7, 39 experts): W13 workgroups of 8 waves, each
-// streaming one gate and one up fragment (0.1875 -> 0.1745 ms against 4 waves of
-// two pairs); W2 waves of 2 fragments, 4 waves per workgroup (0.111 -> 0.097 ms
-// against 4 fragments): more, shorter streams keep more of HBM busy for the same
-// bytes.
-constexpr int kW13Waves = 8;
+// Work split: W13 workgroups of 4 waves, each streaming two gate and two up
+// fragments; W2 waves of 2 fragments, 4 waves per workgroup (decode7, 39 experts:
+// 0.111 -> 0.097 ms against 4 fragments, more and shorter streams keep more of HBM
+// busy). W13 was 8 waves of one gate and one up fragment (0.1875 -> 0.1745 ms
+// against 4 waves of two pairs, measured on an earlier loop); with the current loop
+// (packed layout, four-step ring of scales) 4 waves of two pairs measured the same
+// on decode7 (0.2188 vs 0.2185 ms per step) and 1.1% faster on the 256-token step
+// (1.905 vs 1.926 ms), bitwise equal.
+constexpr int kW13Waves = 4;
 constexpr int kW2Frags = 2;
 // Rows of list slots a small-M launch covers at once; more slots are walked by a
 // grid-stride loop (decode lists stay below it: one slot per workgroup row).
