@@ -48,15 +48,17 @@ typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 // bitwise-equal results, per step): MXFP4 x bf16 with W13 in 4 waves x (2 gate + 2 up
 // fragments) and W2 in 2 waves x 4 fragments: decode7 0.226 vs 0.246 ms and the
 // 256-token step 2.32 vs 2.80 ms against 8 x (1 + 1) and 4 x 2. NVFP4, whose codes take
-// four times the VALU work to expand, keeps 8 x (1 + 1) and 4 x 2: its 4 x (2 + 2) W13 ran
-// decode7 4% slower (0.366 vs 0.351 ms) and the 256-token step 3% faster, its 2 x 4 W2
-// decode7 1% slower.
+// four times the VALU work to expand, keeps 8 x (1 + 1) and 4 x 2 up to kNvWidePairs
+// pairs: there its 4 x (2 + 2) W13 ran decode7 4% slower (0.366 vs 0.351 ms) and its
+// 2 x 4 W2 1% slower; above, as on the 256-token step, they ran 3% and 2% faster, and
+// are used.
 constexpr int kW13Waves = 4;      // MXFP4 W13: 4 waves, NG = 2 gate + 2 up fragments each (128 h columns)
 constexpr int kW13WavesNV = 8;    // NVFP4 W13: 8 waves, one gate + one up fragment each
 constexpr int kW2Waves = 2;       // MXFP4 W2: 2 waves of 4 fragments (128 output columns)
 constexpr int kW2Frags = 4;
 constexpr int kW2WavesNV = 4;     // NVFP4 W2: 4 waves of 2 fragments (128 output columns)
 constexpr int kW2FragsNV = 2;
+constexpr int64_t kNvWidePairs = 512;
 // K steps of codes in flight per wave: two (the ring then holds 52 registers, so
 // the kernels fit 4-5 waves per SIMD instead of 3; the codes' expansion is VALU
 // work that more waves hide better). Measured against four on one box, results
@@ -382,7 +384,10 @@ hipError_t launch_w13_a16(const moe_dims& d, const SmallLists& lists, const int3
   const int64_t max_items = (int64_t)lists.cap0 + lists.cap1;
   if (max_items <= 0) return hipSuccess;
   const dim3 grid(d.I / 128, (unsigned)max_items);
-  if (w13_gs) {
+  if (w13_gs && (int64_t)d.T * d.K > kNvWidePairs) {
+    hipLaunchKernelGGL((k_w13_a16<true, 4>), grid, dim3(4 * 64), 0, s, lists, offsets, sorted_pairs, x, w13, w13_s,
+                       w13_gs, h, d.H, d.I, d.K);
+  } else if (w13_gs) {
     hipLaunchKernelGGL((k_w13_a16<true, kW13WavesNV>), grid, dim3(kW13WavesNV * 64), 0, s, lists, offsets,
                        sorted_pairs, x, w13, w13_s, w13_gs, h, d.H, d.I, d.K);
   } else {
@@ -398,7 +403,11 @@ hipError_t launch_w2_a16(const moe_dims& d, const SmallLists& lists, const int32
                          const float* w2_gs, uint16_t* o, uint8_t* os, hipStream_t s) {
   const int64_t max_items = (int64_t)lists.cap0 + lists.cap1;
   if (max_items <= 0) return hipSuccess;
-  if (w2_gs) {
+  if (w2_gs && (int64_t)d.T * d.K > kNvWidePairs) {
+    const dim3 grid((unsigned)ceil_div(d.H, 2 * 16 * 4), (unsigned)max_items);
+    hipLaunchKernelGGL((k_w2_a16<true, 2, 4>), grid, dim3(2 * 64), 0, s, lists, offsets, sorted_pairs, h, w2, w2_s,
+                       w2_gs, o, os, d.H, d.I);
+  } else if (w2_gs) {
     const dim3 grid((unsigned)ceil_div(d.H, kW2WavesNV * 16 * kW2FragsNV), (unsigned)max_items);
     hipLaunchKernelGGL((k_w2_a16<true, kW2WavesNV, kW2FragsNV>), grid, dim3(kW2WavesNV * 64), 0, s, lists, offsets,
                        sorted_pairs, h, w2, w2_s, w2_gs, o, os, d.H, d.I);

@@ -45,6 +45,7 @@ def _inputs(wl, dev):
     (17, 1280, 1152, 40, 8, 104),  # 10 and 9 K steps, many experts
     (300, 512, 512, 1, 1, 105),    # a 256-row item and a remainder
     (400, 1024, 256, 3, 2, 106),   # 128-row items
+    (700, 384, 384, 3, 1, 107),    # above 512 pairs (the wider work split), H of three 128-column blocks
 ])
 def test_nvfp4_shapes(dev, T, H, I, E, K, seed):
     inp = _inputs(scaled("tiny", T=T, H=H, I=I, E=E, K=K, seed=seed, weight_seed=seed, name=f"nv_{seed}"), dev)
