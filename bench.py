@@ -220,11 +220,14 @@ def decode_object(r: Runner, steps: int, warmup: int, flush: torch.Tensor) -> di
         traffic = measured_traffic(w.name + "_chain", "moe::k_decode_chain")
     elif a16:
         dom_bytes = r.distinct * eb["w13"] + w.T * w.H * 2 + P * w.I * 2
-        dom_name = ("W13 stage, NVFP4 weights, bf16 activations: grouped GEMM + SwiGLU (k_w13_a16<true>)" if nv else
-                    "W13 stage, bf16 activations: grouped GEMM + SwiGLU (k_w13_a16<false>)")
+        # the kernel's second template argument is its wave count: MXFP4 4; NVFP4 8 up to
+        # 512 pairs, 4 above
+        kname = "k_w13_a16<true, %d>" % (8 if P <= 512 else 4) if nv else "k_w13_a16<false, 4>"
+        dom_name = ("W13 stage, NVFP4 weights, bf16 activations: grouped GEMM + SwiGLU (%s)" if nv else
+                    "W13 stage, bf16 activations: grouped GEMM + SwiGLU (%s)") % kname
         # one dispatch per step up to 128 pairs (above, a second one walks the 256-row
         # items, and the per-dispatch counter average no longer is the stage's traffic)
-        traffic = (measured_traffic(w.name + ("_nvfp4" if nv else "_a16"), "moe::k_w13_a16<%s>" % str(nv).lower())
+        traffic = (measured_traffic(w.name + ("_nvfp4" if nv else "_a16"), "moe::" + kname)
                    if P <= 128 else None)
     else:
         dom_bytes = r.distinct * eb["w13"] + w.T * (w.H + w.H // 128) + P * (w.I + w.I // 128)
