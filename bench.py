@@ -80,7 +80,9 @@ def measured_traffic(workload: str, kernels):
     names = [kernels] if isinstance(kernels, str) else list(kernels)
     found = {}
     for line in open(path):
-        f = line.strip().split(",")
+        if line.startswith("#"):
+            continue
+        f = line.strip().rsplit(",", 6)   # kernel names may hold commas (template arguments)
         if len(f) == 7 and f[0] in names and f[5] != "-":
             h = hashlib.sha256()
             for name in f[5].split("+"):
