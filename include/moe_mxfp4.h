@@ -92,8 +92,8 @@ typedef struct moe_dims {
  * when its W13 work has signalled and each 256-column block of y is combined by
  * the W2 unit that finishes it ("Pushing the Limits of Serving DeepSeek-V4-Pro",
  * section 4.3), instead of separate launches. Results are bitwise identical
- * either way. Measured on MI355X at the 7-token verify: 0.253 ms per step against
- * 0.232 ms with separate launches, so it is off by default. Ignored above 512
+ * either way. Measured on MI355X at the 7-token verify: 0.246 ms per step against
+ * 0.224 ms with separate launches, so it is off by default. Ignored above 512
  * pairs. */
 #define MOE_FLAG_DECODE_CHAIN 1
 
