@@ -156,26 +156,25 @@ __device__ void build_worklists(const int32_t* cnt, int E, int small_max, int t1
     }
     return;
   }
-  // Ranks of the large experts, one expert per wave (its lanes compare it with E/64
-  // experts each, two wave sums): the heavy-first rank r (a2[r] = expert), and for an
-  // expert with a 128-row item (a remainder of 1..128 rows) that item's position in
-  // the by-rows order, where it is written.
+  // Ranks of the large experts, one expert per wave: its lanes compare it with 64
+  // experts at a time and a ballot counts each comparison (no chain of cross-lane
+  // additions): the heavy-first rank r (a2[r] = expert), and for an expert with a
+  // 128-row item (a remainder of 1..128 rows) that item's position in the by-rows
+  // order, where it is written. At 32K tokens (every expert large) this O(E^2) pass
+  // is about 30 us of the plan: the single workgroup's four SIMDs issue it.
   const int lane = t & 63, wave = t >> 6, nwaves = nt >> 6;
   for (int e = wave; e < E; e += nwaves) {
     const int m = cnt[e];
     if (m <= small_max) continue;                        // wave-uniform
     const int rem = m % kXlRows;
     int r = 0, pos = 0;
-    for (int f = lane; f < E; f += 64) {
-      const int mf = cnt[f], rf = mf % kXlRows;
-      const bool before = mf > m || (mf == m && f < e);   // heavier, or as heavy with a lower id
-      r += (mf > small_max) && before;
-      pos += (mf > small_max) && rf >= 1 && rf <= kXlRows / 2 && (rf < rem || (rf == rem && before));
-    }
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-      r += __shfl_xor(r, off);
-      pos += __shfl_xor(pos, off);
+    for (int f0 = 0; f0 < E; f0 += 64) {
+      const int f = f0 + lane;
+      const int mf = f < E ? cnt[f] : 0, rf = mf % kXlRows;   // 0 pairs: never a large expert
+      const bool big = mf > small_max;
+      const bool before = mf > m || (mf == m && f < e);     // heavier, or as heavy with a lower id
+      r += __popcll(__ballot(big && before));
+      pos += __popcll(__ballot(big && rf >= 1 && rf <= kXlRows / 2 && (rf < rem || (rf == rem && before))));
     }
     if (lane == 0) {
       a2[r] = e;
@@ -185,14 +184,19 @@ __device__ void build_worklists(const int32_t* cnt, int E, int small_max, int t1
   for (int e = t; e < E; e += nt) a1[e] = cnt[e] > small_max ? 1 : 0;
   __syncthreads();
   const int n_big = block_exclusive_scan(a1, E, part);
-  // 256-row items
+  // 256-row items: a1[r] = the first item of rank r; item i belongs to the last rank r
+  // with a1[r] <= i (ranks without 256-row items share the next rank's start), found by
+  // binary search, one thread per item
   for (int r = t; r < E; r += nt) a1[r] = r < n_big ? (cnt[a2[r]] + kXlRows / 2 - 1) / kXlRows : 0;
   __syncthreads();
   const int n_xl = block_exclusive_scan(a1, E, part);
-  for (int r = t; r < n_big; r += nt) {
-    const int e = a2[r], m = cnt[e], s = a1[r];
-    for (int i = 0; i < (m + kXlRows / 2 - 1) / kXlRows; ++i)
-      if (s + i < xl_cap) xl_items[s + i] = make_int2(e, i * kXlRows);
+  for (int i = t; i < n_xl && i < xl_cap; i += nt) {
+    int lo = 0, hi = n_big - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (a1[mid] <= i) lo = mid; else hi = mid - 1;
+    }
+    xl_items[i] = make_int2(a2[lo], (i - a1[lo]) * kXlRows);
   }
   // 128-row items (written above): their number, and how many have at most t13 / t2 rows
   int c13 = 0, c2 = 0, n_large = 0;

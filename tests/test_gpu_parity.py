@@ -409,6 +409,85 @@ def _sized_routing(sizes, K, seed):
     return torch.from_numpy(ids.reshape(-1, K).copy())
 
 
+def _work_lists_ref(ids, E, small_max, t13, t2):
+    """The planner's tile work lists written out from their definition, from the
+    per-expert pair counts m: 16-row tiles (expert, 16 i) of the experts with
+    1..small_max pairs, in expert order; for the larger experts, heaviest first (ties:
+    lower id), 256-row items (expert, 256 i) for i < (m + 127) // 256, and one
+    128-row item (expert, m - r) when the remainder r = m % 256 is 1..128, these
+    ordered by r (ties: heavier, then lower id); the header: the three list lengths
+    and how many 128-row items have at most t13 / t2 rows."""
+    v = ids[(ids >= 0) & (ids < E)]
+    cnt = np.bincount(v, minlength=E)
+    small = [(e, 16 * i) for e in range(E) if 1 <= cnt[e] <= small_max for i in range(-(-cnt[e] // 16))]
+    big = sorted((e for e in range(E) if cnt[e] > small_max), key=lambda e: (-cnt[e], e))
+    xl = [(e, 256 * i) for e in big for i in range((cnt[e] + 127) // 256)]
+    rem = {e: cnt[e] % 256 for e in big}
+    with_rem = sorted((e for e in big if 1 <= rem[e] <= 128), key=lambda e: (rem[e], -cnt[e], e))
+    large = [(e, cnt[e] - rem[e]) for e in with_rem]
+    if not big:
+        hdr = [len(small), 0, 0, 0, 0]
+    else:
+        hdr = [len(small), len(large), len(xl), sum(rem[e] <= t13 for e in with_rem),
+               sum(rem[e] <= t2 for e in with_rem)]
+    return small, large, xl, hdr
+
+
+def _work_lists(p, T, K, E, small_max):
+    """The lists as the plan workspace holds them: a 64-byte int32 header, then the
+    small, 128-row and 256-row lists of {expert, first row} pairs, each region rounded
+    up to 256 bytes and sized by the library's host-side bounds (written out here:
+    min(P, E) small tiles, plus P / 16 when small_max > 16; min(P / (small_max + 1), E)
+    large experts; P / 256 + that 256-row items)."""
+    P = T * K
+    sc = min(P, E) + (P // 16 if small_max > 16 else 0)
+    big = min(P // (small_max + 1), E)
+    lc, xc = big, P // 256 + big
+    al = lambda n: (n + 255) // 256 * 256
+    o_small = 256
+    o_large = o_small + al(8 * max(sc, 1))
+    o_xl = o_large + al(8 * max(lc, 1))
+    ws = p.ws.cpu().numpy()
+    hdr = ws[:20].view(np.int32).tolist()
+    lst = lambda o, n: [tuple(r) for r in ws[o:o + 8 * n].view(np.int32).reshape(-1, 2).tolist()]
+    return lst(o_small, hdr[0]), lst(o_large, hdr[1]), lst(o_xl, hdr[2]), hdr
+
+
+@pytest.mark.parametrize("case", ["ties", "prefill32k", "small_max1", "decode7"])
+def test_plan_work_lists_match_definition(dev, case):
+    """Every tile work list and header count of the plan equals the definition above,
+    exactly: expert sizes with ties in pair count and in remainder, a 32K-token routing
+    (384 experts, every one above small_max), many large experts at small_max 1, and
+    a decode step (no large expert: empty large-M lists)."""
+    t13, t2 = 48, -1
+    if case == "ties":
+        sizes = [300, 300, 17, 17, 0, 600, 129, 256, 40, 40, 513, 5, 16, 3, 812, 44, 300]
+        ids = _sized_routing(sizes, 1, 131).numpy()
+        E, K, sm = len(sizes), 1, 16
+    elif case == "prefill32k":
+        ids = make_inputs("prefill32k", weights=False).topk_ids.numpy()
+        E, K, sm = 384, 8, 16
+        t13, t2 = 16, -1
+    elif case == "small_max1":
+        rng = np.random.default_rng(132)
+        E, K, sm = 64, 4, 1
+        ids = rng.integers(-2, E + 2, (700, K)).astype(np.int32)
+    else:
+        ids = make_inputs("decode7", weights=False).topk_ids.numpy()
+        E, K, sm = 384, 8, 16
+    T = ids.shape[0]
+    P = T * K
+    p = moe.plan(torch.from_numpy(ids).to(dev), E, 1024, 512, small_max=sm, tile_w13=t13, tile_w2=t2)
+    torch.cuda.synchronize()
+    eff = (128, 128) if P <= 512 else (t13 if t13 > 0 else 0, t2 if t2 > 0 else 0)
+    ref = _work_lists_ref(ids, E, sm, *eff)
+    got = _work_lists(p, T, K, E, sm)
+    for name, a, b in zip(("small", "large", "xl"), got[:3], ref[:3]):
+        assert a == b, (case, name, len(a), len(b), [i for i in range(min(len(a), len(b))) if a[i] != b[i]][:5])
+    assert got[3][:5] == ref[3], (case, got[3][:5], ref[3])
+    check_plan(p, ids, E)
+
+
 def test_tile_choice_per_gemm_is_bitwise_neutral(dev):
     """Expert sizes covering every item kind above the decode fold (P > 512): a
     remainder of 44 and 88 rows after 256-row items, whole experts of 17, 20 and 100
