@@ -73,6 +73,32 @@ __device__ int block_sum(int v, int32_t* part) {
   return total;
 }
 
+// Sorts v[0..n2) (n2 a power of two) into the order `before` defines, with all
+// threads of the block (bitonic network in LDS, one barrier per stage). before(x, y):
+// x goes ahead of y; it must be a strict weak order.
+template <typename Before>
+__device__ void block_bitonic_sort(int32_t* v, int n2, Before before) {
+  for (int k = 2; k <= n2; k <<= 1)
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = threadIdx.x; i < n2 / 2; i += blockDim.x) {
+        const int a = 2 * i - (i & (j - 1)), b = a + j;   // b = a + j, bit log2(j) of a clear
+        const int x = v[a], y = v[b];
+        // ascending runs put the element that goes first at a, descending ones at b
+        if ((a & k) == 0 ? before(y, x) : before(x, y)) {
+          v[a] = y;
+          v[b] = x;
+        }
+      }
+      __syncthreads();
+    }
+}
+
+__device__ __forceinline__ int pow2_at_least(int n) {
+  int p = 1;
+  while (p < n) p <<= 1;
+  return p;
+}
+
 // Phase 1 for pairs [begin, end): local_rank[p - rank_base] = number of earlier
 // pairs of the same expert inside [begin, end); key[p - rank_base] (when given) =
 // the pair's expert, or -1 for an id outside [0, E). cursor[E] must start at zero
@@ -123,11 +149,15 @@ __device__ void local_ranks(const int32_t* __restrict__ ids, int begin, int end,
 // first), and at most one 128-row item per expert for a remainder of 1..128 rows,
 // ordered by rows (ties: heavier expert, then lower id), so that the items of at
 // most t13 (t2) rows, which W13 (W2) walks as 16-row tiles, are a prefix whose
-// length goes to hdr[3] (hdr[4]).
+// length goes to hdr[3] (hdr[4]). Both orders come from bitonic sorts of the
+// compacted experts, O(E log^2 E) work (a count of the experts ahead of each one,
+// O(E^2), took 3.7 ms at 4096 experts). a1, a2: E words, part: blockDim words,
+// sortbuf: 2 E words of LDS.
 __device__ void build_worklists(const int32_t* cnt, int E, int small_max, int t13, int t2,
                                 int2* __restrict__ small_items, int64_t small_cap, int2* __restrict__ large_items,
                                 int64_t large_cap, int2* __restrict__ xl_items, int64_t xl_cap,
-                                int32_t* __restrict__ hdr, int32_t* a1, int32_t* a2, int32_t* part) {
+                                int32_t* __restrict__ hdr, int32_t* a1, int32_t* a2, int32_t* part,
+                                int32_t* sortbuf) {
   const int t = threadIdx.x, nt = blockDim.x;
   for (int e = t; e < E; e += nt) {
     const int m = cnt[e];
@@ -156,34 +186,45 @@ __device__ void build_worklists(const int32_t* cnt, int E, int small_max, int t1
     }
     return;
   }
-  // Ranks of the large experts, one expert per wave: its lanes compare it with 64
-  // experts at a time and a ballot counts each comparison (no chain of cross-lane
-  // additions): the heavy-first rank r (a2[r] = expert), and for an expert with a
-  // 128-row item (a remainder of 1..128 rows) that item's position in the by-rows
-  // order, where it is written. At 32K tokens (every expert large) this O(E^2) pass
-  // is about 30 us of the plan: the single workgroup's four SIMDs issue it.
-  const int lane = t & 63, wave = t >> 6, nwaves = nt >> 6;
-  for (int e = wave; e < E; e += nwaves) {
-    const int m = cnt[e];
-    if (m <= small_max) continue;                        // wave-uniform
-    const int rem = m % kXlRows;
-    int r = 0, pos = 0;
-    for (int f0 = 0; f0 < E; f0 += 64) {
-      const int f = f0 + lane;
-      const int mf = f < E ? cnt[f] : 0, rf = mf % kXlRows;   // 0 pairs: never a large expert
-      const bool big = mf > small_max;
-      const bool before = mf > m || (mf == m && f < e);     // heavier, or as heavy with a lower id
-      r += __popcll(__ballot(big && before));
-      pos += __popcll(__ballot(big && rf >= 1 && rf <= kXlRows / 2 && (rf < rem || (rf == rem && before))));
-    }
-    if (lane == 0) {
-      a2[r] = e;
-      if (rem >= 1 && rem <= kXlRows / 2 && pos < large_cap) large_items[pos] = make_int2(e, m - rem);
-    }
-  }
+  // The large experts (more than small_max pairs) in heavy-first order (ties: lower
+  // id): compacted in id order, then sorted (a2[r] = the expert of rank r).
   for (int e = t; e < E; e += nt) a1[e] = cnt[e] > small_max ? 1 : 0;
   __syncthreads();
   const int n_big = block_exclusive_scan(a1, E, part);
+  const int n2 = pow2_at_least(n_big);
+  for (int e = t; e < E; e += nt)
+    if (cnt[e] > small_max) sortbuf[a1[e]] = e;
+  for (int i = n_big + t; i < n2; i += nt) sortbuf[i] = E;   // padding, sorted last
+  __syncthreads();
+  block_bitonic_sort(sortbuf, n2, [&](int x, int y) {
+    if (x >= E || y >= E) return x < y;
+    return cnt[x] > cnt[y] || (cnt[x] == cnt[y] && x < y);
+  });
+  for (int r = t; r < n_big; r += nt) a2[r] = sortbuf[r];
+  // 128-row items: the large experts with a remainder of 1..128 rows, by rows (ties:
+  // heavier, then lower id), compacted and sorted the same way
+  for (int e = t; e < E; e += nt) {
+    const int m = cnt[e], rem = m % kXlRows;
+    a1[e] = m > small_max && rem >= 1 && rem <= kXlRows / 2;
+  }
+  __syncthreads();
+  const int n_rem = block_exclusive_scan(a1, E, part);
+  const int n2r = pow2_at_least(n_rem);
+  for (int e = t; e < E; e += nt) {
+    const int m = cnt[e], rem = m % kXlRows;
+    if (m > small_max && rem >= 1 && rem <= kXlRows / 2) sortbuf[a1[e]] = e;
+  }
+  for (int i = n_rem + t; i < n2r; i += nt) sortbuf[i] = E;
+  __syncthreads();
+  block_bitonic_sort(sortbuf, n2r, [&](int x, int y) {
+    if (x >= E || y >= E) return x < y;
+    const int mx = cnt[x], my = cnt[y], rx = mx % kXlRows, ry = my % kXlRows;
+    return rx < ry || (rx == ry && (mx > my || (mx == my && x < y)));
+  });
+  for (int i = t; i < n_rem && i < large_cap; i += nt) {
+    const int e = sortbuf[i], m = cnt[e];
+    large_items[i] = make_int2(e, m - m % kXlRows);
+  }
   // 256-row items: a1[r] = the first item of rank r; item i belongs to the last rank r
   // with a1[r] <= i (ranks without 256-row items share the next rank's start), found by
   // binary search, one thread per item
@@ -275,8 +316,9 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan_fused(PlanArgs a) {
     }
     if (p >= n_valid) a.sorted_pairs[p] = -1;
   }
+  // wcnt (4 E words, zero again after local_ranks) is free: the sort buffer
   build_worklists(cnt, E, a.small_max, a.t13, a.t2, a.small_items, a.small_cap, a.large_items, a.large_cap, a.xl_items, a.xl_cap,
-                  a.hdr, a1, a2, part);
+                  a.hdr, a1, a2, part, wcnt);
 }
 
 // Multi-block phase 1.
@@ -303,6 +345,7 @@ __global__ __launch_bounds__(kScanThreads) void k_plan_scan(PlanArgs a) {
   int32_t* a1 = off + E + 1;        // [E]
   int32_t* a2 = a1 + E;             // [E]
   int32_t* part = a2 + E;           // [kScanThreads]
+  int32_t* sortbuf = part + kScanThreads;   // [2 E]
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   constexpr int kWaves = kScanThreads / 64;
   constexpr int kBatch = 8;                 // experts whose counts one wave loads at once
@@ -354,7 +397,7 @@ __global__ __launch_bounds__(kScanThreads) void k_plan_scan(PlanArgs a) {
   __syncthreads();
   for (int e = t; e <= E; e += kScanThreads) a.offsets[e] = off[e];
   build_worklists(cnt, E, a.small_max, a.t13, a.t2, a.small_items, a.small_cap, a.large_items, a.large_cap, a.xl_items, a.xl_cap,
-                  a.hdr, a1, a2, part);
+                  a.hdr, a1, a2, part, sortbuf);
 }
 
 // Multi-block phase 3.
@@ -482,7 +525,7 @@ hipError_t launch_plan(const moe_dims& d, const int32_t* ids, int32_t* offsets, 
   hipLaunchKernelGGL(k_plan_local, dim3(a.nb), dim3(kPlanThreads), lds_local, s, a);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const size_t lds_scan = sizeof(int32_t) * ((size_t)4 * d.E + 1 + kScanThreads);
+  const size_t lds_scan = sizeof(int32_t) * ((size_t)6 * d.E + 1 + kScanThreads);
   if (lds_scan > 65536) {
     err = hipFuncSetAttribute((const void*)k_plan_scan, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_scan);
     if (err != hipSuccess) return err;

@@ -453,12 +453,13 @@ def _work_lists(p, T, K, E, small_max):
     return lst(o_small, hdr[0]), lst(o_large, hdr[1]), lst(o_xl, hdr[2]), hdr
 
 
-@pytest.mark.parametrize("case", ["ties", "prefill32k", "small_max1", "decode7"])
+@pytest.mark.parametrize("case", ["ties", "prefill32k", "small_max1", "decode7", "e4096"])
 def test_plan_work_lists_match_definition(dev, case):
     """Every tile work list and header count of the plan equals the definition above,
     exactly: expert sizes with ties in pair count and in remainder, a 32K-token routing
-    (384 experts, every one above small_max), many large experts at small_max 1, and
-    a decode step (no large expert: empty large-M lists)."""
+    (384 experts, every one above small_max), many large experts at small_max 1, a
+    decode step (no large expert: empty large-M lists), and 4096 experts of about 20
+    pairs each (thousands of ties on both sides of small_max)."""
     t13, t2 = 48, -1
     if case == "ties":
         sizes = [300, 300, 17, 17, 0, 600, 129, 256, 40, 40, 513, 5, 16, 3, 812, 44, 300]
@@ -472,9 +473,13 @@ def test_plan_work_lists_match_definition(dev, case):
         rng = np.random.default_rng(132)
         E, K, sm = 64, 4, 1
         ids = rng.integers(-2, E + 2, (700, K)).astype(np.int32)
-    else:
+    elif case == "decode7":
         ids = make_inputs("decode7", weights=False).topk_ids.numpy()
         E, K, sm = 384, 8, 16
+    else:
+        rng = np.random.default_rng(133)
+        E, K, sm = 4096, 4, 16
+        ids = rng.integers(0, E, (20000, K)).astype(np.int32)
     T = ids.shape[0]
     P = T * K
     p = moe.plan(torch.from_numpy(ids).to(dev), E, 1024, 512, small_max=sm, tile_w13=t13, tile_w2=t2)
