@@ -9,11 +9,11 @@
 // bf16's range for scales 2^-127 .. 2^125) by gfx950's scaled FP4-to-bf16 conversion,
 // and multiplied on v_mfma_f32_16x16x32_bf16 with fp32 accumulation.
 //
-// Same work split as the FP8 small-M kernels (gemm_small.hip): the weights take the
+// The structure of the FP8 small-M kernels (gemm_small.hip): the weights take the
 // MFMA's 16-row A side, the routed tokens its 16-column B side, 16 routed rows per
 // tile, weight codes streamed from the kernel-native layout (lane (c, q) of a
-// fragment holds row c, K 32q .. 32q+31 of the 128-K step), their scales staged in
-// LDS per wave. One 128-K step is four bf16 MFMAs; in MFMA u, lane (c, q) supplies K
+// fragment holds row c, K 32q .. 32q+31 of the 128-K step), MXFP4 scales staged in
+// LDS per wave; the number of fragments per wave is chosen per variant (below). One 128-K step is four bf16 MFMAs; in MFMA u, lane (c, q) supplies K
 // 32q + 8u .. +7 for both operands (the instruction sums over K, so any assignment
 // of K to its slots that the two operands share gives the same dot product), so the
 // lane's weights come from its own 16 code bytes and its activations are 64

@@ -11,7 +11,7 @@
 // routed-row fragments of every K step in registers (read once from memory), the
 // E2M1 codes and E8M0 scales of block b+1 are copied into the other half of a
 // double buffer while block b is multiplied and written, and the footprint (about
-// 69 KB of LDS, 212 VGPRs at three K steps) lets two workgroups share a CU.
+// 69 KB of LDS, 226 VGPRs at three K steps) lets two workgroups share a CU.
 //
 // Waves: a 2 x 2 grid, wave (wm, wn) = routed rows [64 wm, +64) (4 fragments, MFMA
 // B side, E4M3) x output columns [64 wn, +64) of the block (4 weight fragments,
