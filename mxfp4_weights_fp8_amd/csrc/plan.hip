@@ -10,12 +10,13 @@
 //      is the popcount of the lower peers; waves of the same round are ordered
 //      through a small LDS table; a per-expert LDS cursor carries the count across
 //      rounds. No atomics decide an order, so the result is deterministic.
-//   2. scan: per expert, an exclusive scan over blocks, then over experts ->
-//      expert_offsets; the work lists are built from the per-expert counts.
+//   2. scan: per expert, an exclusive scan over blocks (one wave per expert),
+//      then over experts -> expert_offsets; the work lists are built from the
+//      per-expert counts.
 //   3. scatter: position = expert offset + block base of the pair's expert +
 //      local rank.
 // One block (P <= kPlanChunk, the decode shapes) runs all three phases in a
-// single fused launch; larger P uses three launches.
+// single fused launch; larger P uses four launches (the scan takes two).
 #include "device_common.h"
 #include "host_internal.h"
 
@@ -336,57 +337,50 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan_local(PlanArgs a) {
   for (int e = t; e < E; e += kPlanThreads) a.block_counts[(int64_t)e * a.nb + b] = cnt[e];   // [E][nb]
 }
 
-// Multi-block phase 2 (one block of kScanThreads).
+// Multi-block phase 2: per expert, the exclusive scan of its block counts over the
+// blocks (the rank of a block's first pair of that expert among the expert's pairs),
+// one wave per expert, 64 blocks per round with lane shuffles; counts and bases are
+// stored [expert][block], so a wave's load covers 64 consecutive words. The expert's
+// total goes to offsets[e] for the next phase, which turns it into the offset.
+// (Done by the next phase's single workgroup, this took 10 us of a 32K-token plan at
+// 384 experts and most of its 0.39 ms at 4096.)
+__global__ __launch_bounds__(kPlanThreads) void k_plan_expert_scan(PlanArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int e = blockIdx.x * kPlanWaves + (threadIdx.x >> 6);
+  if (e >= a.E) return;                                   // wave-uniform
+  const int nb = a.nb;
+  int run = 0;
+  for (int b0 = 0; b0 < nb; b0 += 64) {
+    const int b = b0 + lane;
+    const int c = b < nb ? a.block_counts[(int64_t)e * nb + b] : 0;
+    int v = c;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int u = __shfl_up(v, o);
+      if (lane >= o) v += u;
+    }
+    if (b < nb) a.block_base[(int64_t)e * nb + b] = run + v - c;
+    run += __shfl(v, 63);
+  }
+  if (lane == 0) a.offsets[e] = run;
+}
+
+// Multi-block phase 3 (one block of kScanThreads): expert offsets and work lists
+// from the per-expert totals.
 __global__ __launch_bounds__(kScanThreads) void k_plan_scan(PlanArgs a) {
   extern __shared__ int32_t lds[];
-  const int E = a.E, nb = a.nb;
+  const int E = a.E;
   int32_t* cnt = lds;               // [E]
   int32_t* off = cnt + E;           // [E + 1]
   int32_t* a1 = off + E + 1;        // [E]
   int32_t* a2 = a1 + E;             // [E]
   int32_t* part = a2 + E;           // [kScanThreads]
   int32_t* sortbuf = part + kScanThreads;   // [2 E]
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  constexpr int kWaves = kScanThreads / 64;
-  constexpr int kBatch = 8;                 // experts whose counts one wave loads at once
-  // Per expert, the exclusive scan of its block counts over the blocks (the rank of
-  // a block's first pair of that expert among the expert's pairs): one wave per
-  // expert, 64 blocks per round, lane shuffles; a wave loads the counts of kBatch
-  // experts before it scans any, so their load latencies overlap. Counts and bases
-  // are stored [expert][block], so a wave's load covers 64 consecutive words.
-  for (int e0 = wave; e0 < E; e0 += kWaves * kBatch) {
-    int run[kBatch];
-#pragma unroll
-    for (int k = 0; k < kBatch; ++k) run[k] = 0;
-    for (int b0 = 0; b0 < nb; b0 += 64) {
-      const int b = b0 + lane;
-      int c[kBatch];
-#pragma unroll
-      for (int k = 0; k < kBatch; ++k) {
-        const int e = e0 + k * kWaves;
-        c[k] = (b < nb && e < E) ? a.block_counts[(int64_t)e * nb + b] : 0;
-      }
-#pragma unroll
-      for (int k = 0; k < kBatch; ++k) {
-        const int e = e0 + k * kWaves;
-        int v = c[k];
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-          const int u = __shfl_up(v, o);
-          if (lane >= o) v += u;
-        }
-        if (b < nb && e < E) a.block_base[(int64_t)e * nb + b] = run[k] + v - c[k];
-        run[k] += __shfl(v, 63);
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < kBatch; ++k) {
-      const int e = e0 + k * kWaves;
-      if (lane == 0 && e < E) {
-        cnt[e] = run[k];
-        off[e] = run[k];
-      }
-    }
+  const int t = threadIdx.x;
+  for (int e = t; e < E; e += kScanThreads) {
+    const int m = a.offsets[e];       // the expert's total, from the previous phase
+    cnt[e] = m;
+    off[e] = m;
   }
   __syncthreads();
   const int n_valid = block_exclusive_scan(off, E, part);
@@ -400,7 +394,7 @@ __global__ __launch_bounds__(kScanThreads) void k_plan_scan(PlanArgs a) {
                   a.hdr, a1, a2, part, sortbuf);
 }
 
-// Multi-block phase 3.
+// Multi-block phase 4.
 __global__ __launch_bounds__(256) void k_plan_scatter(PlanArgs a) {
   const int p = blockIdx.x * 256 + threadIdx.x;
   if (p >= a.P) return;
@@ -530,6 +524,9 @@ hipError_t launch_plan(const moe_dims& d, const int32_t* ids, int32_t* offsets, 
     err = hipFuncSetAttribute((const void*)k_plan_scan, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_scan);
     if (err != hipSuccess) return err;
   }
+  hipLaunchKernelGGL(k_plan_expert_scan, dim3((unsigned)ceil_div(d.E, kPlanWaves)), dim3(kPlanThreads), 0, s, a);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
   hipLaunchKernelGGL(k_plan_scan, dim3(1), dim3(kScanThreads), lds_scan, s, a);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
