@@ -74,24 +74,51 @@ __device__ int block_sum(int v, int32_t* part) {
   return total;
 }
 
-// Sorts v[0..n2) (n2 a power of two) into the order `before` defines, with all
-// threads of the block (bitonic network in LDS, one barrier per stage). before(x, y):
-// x goes ahead of y; it must be a strict weak order.
-template <typename Before>
-__device__ void block_bitonic_sort(int32_t* v, int n2, Before before) {
-  for (int k = 2; k <= n2; k <<= 1)
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = threadIdx.x; i < n2 / 2; i += blockDim.x) {
-        const int a = 2 * i - (i & (j - 1)), b = a + j;   // b = a + j, bit log2(j) of a clear
-        const int x = v[a], y = v[b];
-        // ascending runs put the element that goes first at a, descending ones at b
-        if ((a & k) == 0 ? before(y, x) : before(x, y)) {
+// Sorts the distinct keys v[0..n2) ascending (n2 a power of two), with all threads
+// of the block: a bitonic network. Element i of a register pass lives in lane i % 64
+// of its wave, so the stages whose partner distance j is below 64 exchange through
+// lane shuffles with no barrier (all of them for the merges of up to 64 elements,
+// the last six of every larger merge); the other stages go through LDS with one
+// barrier each (6 of the 45 stages at 512 keys).
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t x, int j) {
+  const int lo = __shfl_xor((int)(uint32_t)x, j), hi = __shfl_xor((int)(uint32_t)(x >> 32), j);
+  return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+__device__ void block_sort_keys(uint64_t* v, int n2) {
+  const int t = threadIdx.x, nt = blockDim.x;
+  // merges k_lo..k_hi, stages j = min(k/2, 32) .. 1, in registers (n2 and nt are
+  // powers of two: one round when n2 <= nt, otherwise whole rounds; elements past n2
+  // hold the largest key and are not written back)
+  auto reg_pass = [&](int k_lo, int k_hi) {
+    for (int base = 0; base < n2; base += nt) {
+      const int i = base + t;
+      uint64_t x = i < n2 ? v[i] : ~0ull;
+      for (int k = k_lo; k <= k_hi; k <<= 1)
+        for (int j = min(k >> 1, 32); j > 0; j >>= 1) {
+          const uint64_t y = shfl_xor_u64(x, j);
+          // the lower index of the pair keeps the smaller key in an ascending run
+          const bool keep_min = ((i & j) == 0) == ((i & k) == 0);
+          x = keep_min ? (y < x ? y : x) : (y > x ? y : x);
+        }
+      if (i < n2) v[i] = x;
+    }
+    __syncthreads();
+  };
+  reg_pass(2, n2 < 64 ? n2 : 64);
+  for (int k = 128; k <= n2; k <<= 1) {
+    for (int j = k >> 1; j >= 64; j >>= 1) {
+      for (int i = t; i < n2 / 2; i += nt) {
+        const int a = 2 * i - (i & (j - 1)), b = a + j;   // bit log2(j) of a clear
+        const uint64_t x = v[a], y = v[b];
+        if ((a & k) == 0 ? y < x : x < y) {
           v[a] = y;
           v[b] = x;
         }
       }
       __syncthreads();
     }
+    reg_pass(k, k);
+  }
 }
 
 __device__ __forceinline__ int pow2_at_least(int n) {
@@ -153,12 +180,12 @@ __device__ void local_ranks(const int32_t* __restrict__ ids, int begin, int end,
 // length goes to hdr[3] (hdr[4]). Both orders come from bitonic sorts of the
 // compacted experts, O(E log^2 E) work (a count of the experts ahead of each one,
 // O(E^2), took 3.7 ms at 4096 experts). a1, a2: E words, part: blockDim words,
-// sortbuf: 2 E words of LDS.
+// keys: LDS for 2 E sort keys (8-byte aligned).
 __device__ void build_worklists(const int32_t* cnt, int E, int small_max, int t13, int t2,
                                 int2* __restrict__ small_items, int64_t small_cap, int2* __restrict__ large_items,
                                 int64_t large_cap, int2* __restrict__ xl_items, int64_t xl_cap,
                                 int32_t* __restrict__ hdr, int32_t* a1, int32_t* a2, int32_t* part,
-                                int32_t* sortbuf) {
+                                uint64_t* keys) {
   const int t = threadIdx.x, nt = blockDim.x;
   for (int e = t; e < E; e += nt) {
     const int m = cnt[e];
@@ -188,22 +215,22 @@ __device__ void build_worklists(const int32_t* cnt, int E, int small_max, int t1
     return;
   }
   // The large experts (more than small_max pairs) in heavy-first order (ties: lower
-  // id): compacted in id order, then sorted (a2[r] = the expert of rank r).
+  // id): compacted in id order as keys (INT_MAX - pairs, id), then sorted (a2[r] =
+  // the expert of rank r). An id takes the low 24 bits of either key (E <= 4096).
   for (int e = t; e < E; e += nt) a1[e] = cnt[e] > small_max ? 1 : 0;
   __syncthreads();
   const int n_big = block_exclusive_scan(a1, E, part);
   const int n2 = pow2_at_least(n_big);
   for (int e = t; e < E; e += nt)
-    if (cnt[e] > small_max) sortbuf[a1[e]] = e;
-  for (int i = n_big + t; i < n2; i += nt) sortbuf[i] = E;   // padding, sorted last
+    if (cnt[e] > small_max) keys[a1[e]] = ((uint64_t)(0x7FFFFFFF - cnt[e]) << 32) | (uint32_t)e;
+  for (int i = n_big + t; i < n2; i += nt) keys[i] = ~0ull;   // padding, sorted last
   __syncthreads();
-  block_bitonic_sort(sortbuf, n2, [&](int x, int y) {
-    if (x >= E || y >= E) return x < y;
-    return cnt[x] > cnt[y] || (cnt[x] == cnt[y] && x < y);
-  });
-  for (int r = t; r < n_big; r += nt) a2[r] = sortbuf[r];
+  block_sort_keys(keys, n2);
+  for (int r = t; r < n_big; r += nt) a2[r] = (int)(keys[r] & 0xFFFFFF);
+  __syncthreads();
   // 128-row items: the large experts with a remainder of 1..128 rows, by rows (ties:
-  // heavier, then lower id), compacted and sorted the same way
+  // heavier, then lower id): keys (rows, INT_MAX - pairs, id), compacted and sorted
+  // the same way
   for (int e = t; e < E; e += nt) {
     const int m = cnt[e], rem = m % kXlRows;
     a1[e] = m > small_max && rem >= 1 && rem <= kXlRows / 2;
@@ -213,17 +240,14 @@ __device__ void build_worklists(const int32_t* cnt, int E, int small_max, int t1
   const int n2r = pow2_at_least(n_rem);
   for (int e = t; e < E; e += nt) {
     const int m = cnt[e], rem = m % kXlRows;
-    if (m > small_max && rem >= 1 && rem <= kXlRows / 2) sortbuf[a1[e]] = e;
+    if (m > small_max && rem >= 1 && rem <= kXlRows / 2)
+      keys[a1[e]] = ((uint64_t)rem << 56) | ((uint64_t)(0x7FFFFFFF - m) << 24) | (uint32_t)e;
   }
-  for (int i = n_rem + t; i < n2r; i += nt) sortbuf[i] = E;
+  for (int i = n_rem + t; i < n2r; i += nt) keys[i] = ~0ull;
   __syncthreads();
-  block_bitonic_sort(sortbuf, n2r, [&](int x, int y) {
-    if (x >= E || y >= E) return x < y;
-    const int mx = cnt[x], my = cnt[y], rx = mx % kXlRows, ry = my % kXlRows;
-    return rx < ry || (rx == ry && (mx > my || (mx == my && x < y)));
-  });
+  block_sort_keys(keys, n2r);
   for (int i = t; i < n_rem && i < large_cap; i += nt) {
-    const int e = sortbuf[i], m = cnt[e];
+    const int e = (int)(keys[i] & 0xFFFFFF), m = cnt[e];
     large_items[i] = make_int2(e, m - m % kXlRows);
   }
   // 256-row items: a1[r] = the first item of rank r; item i belongs to the last rank r
@@ -283,11 +307,11 @@ struct PlanArgs {
 
 // Single-block plan: all three phases in one launch (P <= kPlanChunk).
 __global__ __launch_bounds__(kPlanThreads) void k_plan_fused(PlanArgs a) {
-  extern __shared__ int32_t lds[];
+  extern __shared__ __attribute__((aligned(16))) int32_t lds[];
   const int E = a.E;
-  int32_t* cnt = lds;                         // [E]
-  int32_t* wcnt = cnt + E;                    // [kPlanWaves * E]
-  int32_t* off = wcnt + kPlanWaves * E;       // [E + 1]
+  int32_t* wcnt = lds;                        // [kPlanWaves * E]; later the sort keys
+  int32_t* cnt = wcnt + kPlanWaves * E;       // [E]
+  int32_t* off = cnt + E;                     // [E + 1]
   int32_t* a1 = off + E + 1;                  // [E]
   int32_t* a2 = a1 + E;                       // [E]
   int32_t* part = a2 + E;                     // [kPlanThreads]
@@ -317,14 +341,14 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan_fused(PlanArgs a) {
     }
     if (p >= n_valid) a.sorted_pairs[p] = -1;
   }
-  // wcnt (4 E words, zero again after local_ranks) is free: the sort buffer
+  // wcnt (4 E words at the start of LDS) is free: room for 2 E sort keys
   build_worklists(cnt, E, a.small_max, a.t13, a.t2, a.small_items, a.small_cap, a.large_items, a.large_cap, a.xl_items, a.xl_cap,
-                  a.hdr, a1, a2, part, wcnt);
+                  a.hdr, a1, a2, part, reinterpret_cast<uint64_t*>(wcnt));
 }
 
 // Multi-block phase 1.
 __global__ __launch_bounds__(kPlanThreads) void k_plan_local(PlanArgs a) {
-  extern __shared__ int32_t lds[];
+  extern __shared__ __attribute__((aligned(16))) int32_t lds[];
   const int E = a.E;
   int32_t* cnt = lds;
   int32_t* wcnt = cnt + E;
@@ -368,14 +392,14 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan_expert_scan(PlanArgs a) {
 // Multi-block phase 3 (one block of kScanThreads): expert offsets and work lists
 // from the per-expert totals.
 __global__ __launch_bounds__(kScanThreads) void k_plan_scan(PlanArgs a) {
-  extern __shared__ int32_t lds[];
+  extern __shared__ __attribute__((aligned(16))) int32_t lds[];
   const int E = a.E;
-  int32_t* cnt = lds;               // [E]
+  uint64_t* keys = reinterpret_cast<uint64_t*>(lds);   // [2 E] sort keys
+  int32_t* cnt = lds + 4 * E;       // [E]
   int32_t* off = cnt + E;           // [E + 1]
   int32_t* a1 = off + E + 1;        // [E]
   int32_t* a2 = a1 + E;             // [E]
   int32_t* part = a2 + E;           // [kScanThreads]
-  int32_t* sortbuf = part + kScanThreads;   // [2 E]
   const int t = threadIdx.x;
   for (int e = t; e < E; e += kScanThreads) {
     const int m = a.offsets[e];       // the expert's total, from the previous phase
@@ -391,7 +415,7 @@ __global__ __launch_bounds__(kScanThreads) void k_plan_scan(PlanArgs a) {
   __syncthreads();
   for (int e = t; e <= E; e += kScanThreads) a.offsets[e] = off[e];
   build_worklists(cnt, E, a.small_max, a.t13, a.t2, a.small_items, a.small_cap, a.large_items, a.large_cap, a.xl_items, a.xl_cap,
-                  a.hdr, a1, a2, part, sortbuf);
+                  a.hdr, a1, a2, part, keys);
 }
 
 // Multi-block phase 4.
@@ -519,7 +543,7 @@ hipError_t launch_plan(const moe_dims& d, const int32_t* ids, int32_t* offsets, 
   hipLaunchKernelGGL(k_plan_local, dim3(a.nb), dim3(kPlanThreads), lds_local, s, a);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const size_t lds_scan = sizeof(int32_t) * ((size_t)6 * d.E + 1 + kScanThreads);
+  const size_t lds_scan = sizeof(int32_t) * ((size_t)8 * d.E + 1 + kScanThreads);
   if (lds_scan > 65536) {
     err = hipFuncSetAttribute((const void*)k_plan_scan, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_scan);
     if (err != hipSuccess) return err;
