@@ -116,6 +116,13 @@ struct SmallLists {
 inline SmallLists small_lists(const int2* items, const int32_t* n_items, int64_t cap, int rows) {
   return SmallLists{{items, items}, {n_items, n_items}, (int)cap, 0, {rows, rows}};
 }
+// A list of items of more than 16 rows (one workgroup walks their tiles one after
+// another) as list 0, ahead of the single list of `rest`: those long workgroups take
+// the lowest rows y, which start first, instead of trailing the launch.
+inline SmallLists long_items_first(const int2* items, const int32_t* n_items, int64_t cap, int rows,
+                                   const SmallLists& rest) {
+  return SmallLists{{items, rest.items[0]}, {n_items, rest.n_items[0]}, (int)cap, rest.cap0, {rows, rest.rows[0]}};
+}
 hipError_t launch_w13_small(const moe_dims& d, const SmallLists& lists, const int32_t* offsets,
                             const int32_t* sorted_pairs, const uint8_t* x_q, const uint8_t* x_s,
                             const uint8_t* w13, const uint8_t* w13_s, uint8_t* h_q, uint8_t* h_s, hipStream_t s);

@@ -176,11 +176,8 @@ int ffn_enqueue(const moe_dims& d, const uint16_t* x, const float* topk_weights,
   if (bf16_rows(d)) {
     // bf16 activations: no quantization; every item list walked in 16-row tiles
     uint16_t* h = dbg && dbg->h_q ? reinterpret_cast<uint16_t*>(dbg->h_q) : reinterpret_cast<uint16_t*>(fw.h_q);
-    SmallLists sl = small_lists(pw.small_items, pw.hdr + 0, pw.small_cap, kSmallRows);
-    sl.items[1] = pw.large_items;
-    sl.n_items[1] = pw.hdr + 1;
-    sl.cap1 = (int)pw.large_cap;
-    sl.rows[1] = kLargeRows;
+    const SmallLists sl = long_items_first(pw.large_items, pw.hdr + 1, pw.large_cap, kLargeRows,
+                                           small_lists(pw.small_items, pw.hdr + 0, pw.small_cap, kSmallRows));
     const SmallLists sxl = small_lists(pw.xl_items, pw.hdr + 2, pw.xl_cap, kXlRows);
     record(dbg, MOE_EV_START, s);
     record(dbg, MOE_EV_QUANT_DONE, s);
@@ -242,14 +239,8 @@ int ffn_enqueue(const moe_dims& d, const uint16_t* x, const float* topk_weights,
   const bool any_xl = P > kXlRows / 2, any_l = P > small_max_of(d);
   const int t13 = tile_small_rows(d, true), t2 = tile_small_rows(d, false);
   auto lists_for = [&](int t, const int32_t* cut) {
-    SmallLists sl = small_lists(pw.small_items, pw.hdr + 0, pw.small_cap, kSmallRows);
-    if (any_l && t > 0) {
-      sl.items[1] = pw.large_items;
-      sl.n_items[1] = cut;
-      sl.cap1 = (int)pw.large_cap;
-      sl.rows[1] = kLargeRows;
-    }
-    return sl;
+    const SmallLists sl = small_lists(pw.small_items, pw.hdr + 0, pw.small_cap, kSmallRows);
+    return any_l && t > 0 ? long_items_first(pw.large_items, cut, pw.large_cap, kLargeRows, sl) : sl;
   };
   const SmallLists sl13 = lists_for(t13, pw.hdr + 3), sl2 = lists_for(t2, pw.hdr + 4);
   const SmallLists sxl = small_lists(pw.xl_items, pw.hdr + 2, pw.xl_cap, kXlRows);
