@@ -43,8 +43,14 @@ inline int64_t big_experts_bound(const moe_dims& d) {
   return big > d.E ? d.E : big;
 }
 inline int64_t large_items_bound(const moe_dims& d) { return big_experts_bound(d); }
+// Every 256-row item holds more than 128 rows (the full ones 256, an expert's last
+// one 129..256), so there are at most P / 129 of them; and at most P / 256 full ones
+// plus one last one per expert above small_max. The smaller bound sizes the list and
+// the grids (a launch whose workgroups all find no item still costs microseconds).
 inline int64_t xl_items_bound(const moe_dims& d) {
-  return (int64_t)d.T * d.K / kXlRows + big_experts_bound(d);
+  const int64_t P = (int64_t)d.T * d.K;
+  const int64_t by_rows = P / (kXlRows / 2 + 1), by_experts = P / kXlRows + big_experts_bound(d);
+  return by_rows < by_experts ? by_rows : by_experts;
 }
 
 // ---------------------------------------------------------------- plan workspace

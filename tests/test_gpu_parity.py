@@ -438,11 +438,11 @@ def _work_lists(p, T, K, E, small_max):
     small, 128-row and 256-row lists of {expert, first row} pairs, each region rounded
     up to 256 bytes and sized by the library's host-side bounds (written out here:
     min(P, E) small tiles, plus P / 16 when small_max > 16; min(P / (small_max + 1), E)
-    large experts; P / 256 + that 256-row items)."""
+    large experts; min(P / 129, P / 256 + that) 256-row items)."""
     P = T * K
     sc = min(P, E) + (P // 16 if small_max > 16 else 0)
     big = min(P // (small_max + 1), E)
-    lc, xc = big, P // 256 + big
+    lc = big
     al = lambda n: (n + 255) // 256 * 256
     o_small = 256
     o_large = o_small + al(8 * max(sc, 1))
