@@ -370,9 +370,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_xl(XlArgs a) {
     // SwiGLU + FP8 requantization. Lane (c, q) of routed-row fragment j holds h
     // columns 64wn + 16i + 4q .. +3 (i = 0..3: gate acc[i], up acc[4+i]) of tile row
     // 128wm + 16j + c. The two waves sharing a row exchange their amax in LDS (the
-    // routed-row buffers are free once every copy has landed).
+    // routed-row buffers are free once every copy has landed). The codes are staged
+    // as the tile's 128-byte rows of h (16-byte chunk k of row r at chunk k ^ (r % 8))
+    // and stored as whole cache lines, eight rows per instruction.
     __syncthreads();
     float* sRed = reinterpret_cast<float*>(&sB[0][0]);          // [2 halves][2 waves][kTok]
+    uint8_t* sH = &sB[1][0];                                      // [kTok][128 B]
 #pragma unroll
     for (int half = 0; half < 2; ++half) {    // routed-row fragments 4 half .. +3
       float hv[4][4][4];
@@ -405,15 +408,19 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_xl(XlArgs a) {
         const float m = fmaxf(red[row], red[kTok + row]);
         const int ex = e8m0_exponent(m);
         const float inv = exp2_neg(ex);
-        if (row < nrows) {
-          uint8_t* dst = a.h_q + (int64_t)(row0 + row) * a.I + nb * 128 + 64 * wn + q * 4;
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            *reinterpret_cast<uint32_t*>(dst + 16 * i) =
-                e4m3_pack4(hv[jj][i][0] * inv, hv[jj][i][1] * inv, hv[jj][i][2] * inv, hv[jj][i][3] * inv);
-          if (wn == 0 && q == 0) a.h_s[(int64_t)(row0 + row) * (a.I / 128) + nb] = (uint8_t)(ex + 127);
-        }
+        for (int i = 0; i < 4; ++i)
+          *reinterpret_cast<uint32_t*>(sH + row * 128 + (((4 * wn + i) ^ (row & 7)) << 4) + 4 * q) =
+              e4m3_pack4(hv[jj][i][0] * inv, hv[jj][i][1] * inv, hv[jj][i][2] * inv, hv[jj][i][3] * inv);
+        if (row < nrows && wn == 0 && q == 0) a.h_s[(int64_t)(row0 + row) * (a.I / 128) + nb] = (uint8_t)(ex + 127);
       }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {       // wave w: rows 64 w .. +63
+      const int r = 64 * wave + 8 * st + (lane >> 3), chunk = lane & 7;
+      const v4i v = *reinterpret_cast<const v4i*>(sH + r * 128 + ((chunk ^ (r & 7)) << 4));
+      if (r < nrows) *reinterpret_cast<v4i*>(a.h_q + (int64_t)(row0 + r) * a.I + nb * 128 + chunk * 16) = v;
     }
   } else {
 #pragma unroll
