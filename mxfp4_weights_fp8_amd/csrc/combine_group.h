@@ -29,6 +29,14 @@ __device__ __forceinline__ void combine_group(const uint16_t* __restrict__ o, co
   const int scales_per_row = groups_per_row / 4;   // one scale per 32 columns = 4 groups of 8
   const int64_t g = t * groups_per_row + c8;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  // the shared expert's row (same storage as the per-pair rows) is loaded with the
+  // first batch and added last
+  v4i sr = {0, 0, 0, 0};
+  int sex = 0;
+  if (so) {
+    sr = load16_nt(reinterpret_cast<const uint4*>(so) + g);
+    sex = (int)sos[t * scales_per_row + (c8 >> 2)] - 127;
+  }
   // j in order; batches of 8 pairs issue all their loads before the first add (a
   // dropped pair's row is loaded but not added: its slot was never written)
   for (int j0 = 0; j0 < K; j0 += 8) {
@@ -60,15 +68,12 @@ __device__ __forceinline__ void combine_group(const uint16_t* __restrict__ o, co
       }
     }
   }
-  if (so) {   // the shared expert's row, same storage as the per-pair rows, added last
-    const v4i r = load16_nt(reinterpret_cast<const uint4*>(so) + g);
-    const uint4 v = make_uint4((uint32_t)r.x, (uint32_t)r.y, (uint32_t)r.z, (uint32_t)r.w);
-    const int ex = (int)sos[t * scales_per_row + (c8 >> 2)] - 127;
-    const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+  if (so) {
+    const uint32_t u[4] = {(uint32_t)sr.x, (uint32_t)sr.y, (uint32_t)sr.z, (uint32_t)sr.w};
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      acc[2 * k] += __builtin_amdgcn_ldexpf(f16_lo(u[k]), ex);
-      acc[2 * k + 1] += __builtin_amdgcn_ldexpf(f16_hi(u[k]), ex);
+      acc[2 * k] += __builtin_amdgcn_ldexpf(f16_lo(u[k]), sex);
+      acc[2 * k + 1] += __builtin_amdgcn_ldexpf(f16_hi(u[k]), sex);
     }
   }
   uint4 r;
