@@ -93,6 +93,7 @@ struct XlArgs {
   int H, I, K;
   int gi, gn;              // XCD group: gi work items x gn column blocks
   int ngn;                 // column groups (column blocks / gn)
+  int P;                   // pairs (entries of sorted_pairs)
 };
 
 // acc += A (E2M1, 32 K values per lane) x B (E4M3) with E8M0 scales: byte 0 of sa,
@@ -156,20 +157,76 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_xl(XlArgs a) {
   const int KS = Kdim / 128;                            // K steps (a multiple of 4)
   const int wrow = Kdim / 2, srow = Kdim / 32, arow = Kdim;
 
-  // routed rows of the tile -> activation row (padding repeats the first row); W2
-  // also keeps each row's output slot
-  {
-    const int r = row0 + (tid < nrows ? tid : 0);
-    const int pair = a.sorted_pairs[r];
-    sTok[tid] = W13 ? pair / a.K : r;
-    if (!W13) sSlot[W13 ? 0 : tid] = pair;
-  }
-  __syncthreads();
-
   const v4i_s rw = rsrc4(a.w + (int64_t)e * N * wrow, (uint32_t)(N * wrow));
   const v4i_s rws = rsrc4(a.w_s + (int64_t)e * N * srow, (uint32_t)(N * srow));
   const v4i_s ra = rsrc4(a.act, a.act_bytes);
   const v4i_s ras = rsrc4(a.act_s, a.act_s_bytes);
+
+  // expert weight row of LDS row r (0..255): fragments of 16 rows
+  auto w_row = [&](int r) -> int {
+    const int f = r >> 4;
+    if (W13) return (f < 8 ? 0 : a.I) + nb * 128 + (f & 7) * 16 + (r & 15);
+    return nb * 256 + r;
+  };
+  // Copy plans (per wave). Weights (kernel-native layout: a fragment's codes of one
+  // K step are 1 KB in lane order): instruction i of a K step copies the block of LDS
+  // fragment 4*wave + i to LDS [fragment][1 KB] of the step's buffer; a wave's 64
+  // weight rows are consecutive expert rows. Routed rows: instruction i
+  // moves LDS rows 64*wave + 8i .. +7, lane l -> row +l/8, physical chunk l%8 holding
+  // logical chunk (l%8) ^ s(row), s(row) = (row / 2) % 8 = 4 (i % 2) + l / 16. Weight
+  // scales: instruction i moves rows 64*wave + 16i .. +15, lane l -> row +l/4, dword
+  // l%4 of the chunk. Lane offsets are loop-invariant registers; the K position goes
+  // in the scalar offset (the hardware range check covers the lane offset only, and
+  // a copy past the last step takes a size-0 resource, which masks every lane).
+  const int sw0 = ((lane & 7) ^ (lane >> 4)) << 4;
+  const int sw1 = ((lane & 7) ^ (4 | (lane >> 4))) << 4;
+  const int dA = w_row(64 * wave) * wrow + lane * 16;   // 64 consecutive expert rows per wave
+  const int dS = w_row(64 * wave + (lane >> 2)) * srow + (lane & 3) * 4;
+  int dW[4], dB[8], dSc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) dW[i] = dA + 16 * i * wrow;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) dSc[i] = dS + 16 * i * srow;
+
+  auto copy_w = [&](int step, int i) {    // weight fragment 4 wave + i of K step `step`
+    dma16(rsrc_sized(rw, step < KS), lds_addr(&sA[step & 3][(4 * wave + i) * 1024]), dW[i], step * 1024);
+  };
+  auto copy_t = [&](int step, int i) {    // routed rows of K step `step`, instruction i
+    dma16(rsrc_sized(ra, step < KS), lds_addr(&sB[step & 1][(64 * wave + 8 * i) * 128]), dB[i], step * 128);
+  };
+  auto copy_s = [&](int chunk, int i) {   // weight scales of K steps 4 chunk .. +3, instruction i
+    dma4(rsrc_sized(rws, 4 * chunk < KS), lds_addr(&sSa[chunk % 3][(64 * wave + 16 * i) * kChunkRow]), dSc[i],
+         chunk * kChunkRow);
+  };
+
+  // Prologue. The tile's sorted pairs come first, one dword copy per wave into
+  // routed-row buffer 1 (written by no copy before window 0); then scale chunk 0 and
+  // quarter 0 of chunk 1 and the weights of steps 0-2, which need only the expert
+  // and mostly come from HBM. Copies complete in issue order, so waiting until this
+  // wave's 17 later copies are the only ones in flight finds the pairs in LDS while
+  // the weights are still on their way.
+  int32_t* sPairs = reinterpret_cast<int32_t*>(&sB[1][0]);   // [kTok]
+  {
+    const int np = min(a.P - row0, kTok);   // entries past the list read as zeros
+    dma4(rsrc4(a.sorted_pairs + row0, (uint32_t)np * 4u), lds_addr(sPairs + 64 * wave), (64 * wave + lane) * 4, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) copy_s(0, i);
+  copy_s(1, 0);
+#pragma unroll
+  for (int st = 0; st < 3; ++st)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) copy_w(st, i);
+  wait_vmcnt<17>();
+  __syncthreads();
+  // routed rows of the tile -> activation row (padding repeats the first row); W2
+  // also keeps each row's output slot
+  {
+    const int pair = sPairs[tid < nrows ? tid : 0];
+    sTok[tid] = W13 ? pair / a.K : row0 + (tid < nrows ? tid : 0);
+    if (!W13) sSlot[W13 ? 0 : tid] = pair;
+  }
+  __syncthreads();
 
   // Activation scales: aligned rows by dword copies (instruction i of wave w covers
   // LDS dwords 64(4i + w) .. +63 of the table, row = dword / 17; the 17th dword of a
@@ -202,56 +259,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_xl(XlArgs a) {
     for (int i = 0; i < kMaxKS / 4; ++i) *reinterpret_cast<uint32_t*>(&sSb[tid * kSbRow + 4 * i]) = v[i];
   }
 
-  // expert weight row of LDS row r (0..255): fragments of 16 rows
-  auto w_row = [&](int r) -> int {
-    const int f = r >> 4;
-    if (W13) return (f < 8 ? 0 : a.I) + nb * 128 + (f & 7) * 16 + (r & 15);
-    return nb * 256 + r;
-  };
-  // Copy plans (per wave). Weights (kernel-native layout: a fragment's codes of one
-  // K step are 1 KB in lane order): instruction i of a K step copies the block of LDS
-  // fragment 4*wave + i to LDS [fragment][1 KB] of the step's buffer; a wave's 64
-  // weight rows are consecutive expert rows. Routed rows: instruction i
-  // moves LDS rows 64*wave + 8i .. +7, lane l -> row +l/8, physical chunk l%8 holding
-  // logical chunk (l%8) ^ s(row), s(row) = (row / 2) % 8 = 4 (i % 2) + l / 16. Weight
-  // scales: instruction i moves rows 64*wave + 16i .. +15, lane l -> row +l/4, dword
-  // l%4 of the chunk. Lane offsets are loop-invariant registers; the K position goes
-  // in the scalar offset (the hardware range check covers the lane offset only, and
-  // a copy past the last step takes a size-0 resource, which masks every lane).
-  const int sw0 = ((lane & 7) ^ (lane >> 4)) << 4;
-  const int sw1 = ((lane & 7) ^ (4 | (lane >> 4))) << 4;
-  const int dA = w_row(64 * wave) * wrow + lane * 16;   // 64 consecutive expert rows per wave
-  const int dS = w_row(64 * wave + (lane >> 2)) * srow + (lane & 3) * 4;
-  int dW[4], dB[8], dSc[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) dW[i] = dA + 16 * i * wrow;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     dB[i] = sTok[64 * wave + 8 * i + (lane >> 3)] * arow + ((i & 1) ? sw1 : sw0);
   }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) dSc[i] = dS + 16 * i * srow;
-
-  auto copy_w = [&](int step, int i) {    // weight fragment 4 wave + i of K step `step`
-    dma16(rsrc_sized(rw, step < KS), lds_addr(&sA[step & 3][(4 * wave + i) * 1024]), dW[i], step * 1024);
-  };
-  auto copy_t = [&](int step, int i) {    // routed rows of K step `step`, instruction i
-    dma16(rsrc_sized(ra, step < KS), lds_addr(&sB[step & 1][(64 * wave + 8 * i) * 128]), dB[i], step * 128);
-  };
-  auto copy_s = [&](int chunk, int i) {   // weight scales of K steps 4 chunk .. +3, instruction i
-    dma4(rsrc_sized(rws, 4 * chunk < KS), lds_addr(&sSa[chunk % 3][(64 * wave + 16 * i) * kChunkRow]), dSc[i],
-         chunk * kChunkRow);
-  };
-
-  // Prologue: scale chunk 0 and quarter 0 of chunk 1, weights of steps 0-2, routed
-  // rows of step 0; then (after M_{-1}) the column-7 part of window 0.
-#pragma unroll
-  for (int i = 0; i < 4; ++i) copy_s(0, i);
-  copy_s(1, 0);
-#pragma unroll
-  for (int st = 0; st < 3; ++st)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) copy_w(st, i);
+  // then the routed rows of step 0; (after M_{-1}) the column-7 part of window 0
 #pragma unroll
   for (int i = 0; i < 8; ++i) copy_t(0, i);
   wait_vmcnt<0>();
@@ -474,7 +486,7 @@ hipError_t launch_w13_xl(const moe_dims& d, const int2* items, const int32_t* n_
   const XcdGroups g = xcd_groups(d.I / 128, max_items, (double)kTok * d.H, 256.0 * (d.H / 2 + d.H / 32));
   XlArgs a{items, n_items, offsets, sorted_pairs, x_q, x_s, w13, w13_s, h_q, h_s, nullptr, nullptr,
            (uint32_t)((int64_t)d.T * d.H), (uint32_t)((int64_t)d.T * KS),
-           KS % 4 == 0 && (uintptr_t)x_s % 4 == 0, d.H, d.I, d.K, g.gi, g.gn, g.ngn};
+           KS % 4 == 0 && (uintptr_t)x_s % 4 == 0, d.H, d.I, d.K, g.gi, g.gn, g.ngn, d.T * d.K};
   hipLaunchKernelGGL(k_gemm_xl<true>, dim3((unsigned)g.grid), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
@@ -488,7 +500,7 @@ hipError_t launch_w2_xl(const moe_dims& d, const int2* items, const int32_t* n_i
   const XcdGroups g = xcd_groups(d.H / 256, max_items, (double)kTok * d.I, 256.0 * (d.I / 2 + d.I / 32));
   XlArgs a{items, n_items, offsets, sorted_pairs, h_q, h_s, w2, w2_s, nullptr, nullptr, o, os,
            (uint32_t)(P * d.I), (uint32_t)(P * KS), KS % 4 == 0 && (uintptr_t)h_s % 4 == 0, d.H, d.I, d.K,
-           g.gi, g.gn, g.ngn};
+           g.gi, g.gn, g.ngn, (int)P};
   hipLaunchKernelGGL(k_gemm_xl<false>, dim3((unsigned)g.grid), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
