@@ -5,6 +5,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 import mxfp4_weights_fp8_amd as moe
@@ -108,6 +109,48 @@ def test_workspace_sizes():
     assert moe.ffn_workspace_bytes(moe.make_dims(4, 200, 512, 8, 2)) == 0   # invalid dims -> 0
     small = moe.make_dims(7, 7168, 3072, 384, 8)
     assert 0 < moe.ffn_workspace_bytes(small) < ffn
+
+
+def _item_counts(cnt, small_max):
+    """Work items of per-expert pair counts, from their definition: experts above
+    small_max give one 256-row item per 256 rows (the last one when more than 128
+    remain) and one 128-row item for a remainder of 1..128 rows."""
+    xl = sum(m // 256 + (m % 256 > 128) for m in cnt if m > small_max)
+    large = sum(1 for m in cnt if m > small_max and 1 <= m % 256 <= 128)
+    return xl, large
+
+
+def test_plan_workspace_bounds_hold_and_size_the_layout():
+    """The plan workspace is the header and the three item lists, each sized by its
+    host-side bound (256-row items: min(P / 129, P / 256 + large experts), since every
+    such item holds more than 128 rows), then the planner scratch, every region
+    rounded up to 256 bytes. The bounds hold on random and extreme expert sizes."""
+    rng = np.random.default_rng(5)
+    for T, K, E, sm in [(7, 8, 384, 16), (256, 8, 384, 16), (32768, 8, 384, 16), (300, 1, 1, 16),
+                        (2048, 4, 4096, 1), (1000, 8, 64, 40), (129, 1, 1, 16)]:
+        P = T * K
+        big = min(P // (sm + 1), E)
+        xc = min(P // 129, P // 256 + big)
+        small = min(P, E) + (P // 16 if sm > 16 else 0)
+        nb = max(1, -(-P // 2048))
+        al = lambda n: -(-n // 256) * 256
+        want = al(64) + al(8 * max(small, 1)) + al(8 * max(big, 1)) + al(8 * max(xc, 1)) + al(4 * max(P, 1))
+        want += 2 * al(4 * nb * E)
+        assert moe.plan_workspace_bytes(moe.make_dims(T, 256, 256, E, K, small_max=sm)) == want, (T, K, E, sm)
+        # random splits of the P pairs over the experts, plus every pair on few experts
+        # with 129 rows each (the most 256-row items P pairs can make)
+        cases = [np.bincount(rng.integers(0, E, P), minlength=E) for _ in range(20)]
+        cases += [np.bincount(rng.zipf(1.3, P) % E, minlength=E)]
+        n129 = min(E, P // 129)
+        if n129:
+            c = np.zeros(E, np.int64)
+            c[:n129] = 129
+            c[0] += P - 129 * n129
+            cases.append(c)
+        for cnt in cases:
+            assert cnt.sum() == P
+            xl, large = _item_counts(cnt.tolist(), sm)
+            assert xl <= xc and large <= big, (T, K, E, sm, xl, xc, large, big)
 
 
 def test_host_checks_reject_before_enqueue():
