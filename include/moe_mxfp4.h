@@ -89,11 +89,11 @@ typedef struct moe_dims {
 
 /* moe_ffn at decode shapes (T*K <= 512): run W13 + SwiGLU/requant, W2 and the
  * top-k combine as ONE persistent launch in which each expert's W2 work starts
- * when its W13 work has signalled and each 256-column block of y is combined by
+ * when its W13 work has signalled and each 128-column block of y is combined by
  * the W2 unit that finishes it ("Pushing the Limits of Serving DeepSeek-V4-Pro",
  * section 4.3), instead of separate launches. Results are bitwise identical
- * either way. Measured on MI355X at the 7-token verify: 0.246 ms per step against
- * 0.224 ms with separate launches, so it is off by default. Ignored above 512
+ * either way. Measured on MI355X at the 7-token verify: 0.230 ms per step against
+ * 0.219 ms with separate launches, so it is off by default. Ignored above 512
  * pairs. */
 #define MOE_FLAG_DECODE_CHAIN 1
 

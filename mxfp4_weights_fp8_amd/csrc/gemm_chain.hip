@@ -9,7 +9,11 @@
 //
 // Work units, handed out in order by an atomic ticket:
 //   [0, n*U13)             W13 unit (item, 128 h columns), U13 = I/128
-//   [n*U13, n*(U13+U2))    W2 unit (item, 256 output columns), U2 = ceil(H/256)
+//   [n*U13, n*(U13+U2))    W2 unit (item, 128 output columns), U2 = ceil(H/128)
+// Four waves per workgroup, the split of the separate small-M kernels (each W13 wave
+// two gate and two up fragments, each W2 wave two fragments); measured on decode7
+// against eight waves of one gate/up pair and 256-column W2 units: 0.2300 vs 0.2381
+// ms per step (W2 units of two 128-column blocks in a row: 0.2359 ms).
 // n = the plan's items of every list (16-row, 128-row and 256-row items, all
 // walked in 16-row tiles: the chain runs for decode shapes, at most kFoldPairs
 // pairs). Items are heavy-first and units item-major, so the first W2 units
@@ -45,7 +49,7 @@ namespace {
 
 using namespace small;
 
-constexpr int kWaves = 8;
+constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 constexpr int kW2NF = 2;                       // fragments per wave in a W2 unit
 constexpr int kW2Cols = kWaves * 16 * kW2NF;   // output columns of a W2 unit
@@ -198,9 +202,9 @@ hipError_t launch_decode_chain(const moe_dims& d, const PlanWs& pw, const int32_
   a.H = d.H;
   a.I = d.I;
   a.K = d.K;
-  // LDS: the larger of a W13 unit's weight scales (per wave two runs of 16 rows x
-  // H/32) and a W2 unit's (per wave 32 rows x I/32)
-  const size_t lds13 = (size_t)kWaves * 2 * staged_bytes(16 * (d.H / 32));
+  // LDS: the larger of a W13 unit's weight scales (per wave two runs of 128/kWaves
+  // rows x H/32) and a W2 unit's (per wave 16 kW2NF rows x I/32)
+  const size_t lds13 = (size_t)kWaves * 2 * staged_bytes(128 / kWaves * (d.H / 32));
   const size_t lds2 = (size_t)kWaves * staged_bytes(16 * kW2NF * (d.I / 32));
   const size_t lds = lds13 > lds2 ? lds13 : lds2;
   int dev = 0, cus = 0, per_cu = 0;
