@@ -61,6 +61,53 @@ __device__ int block_exclusive_scan(int32_t* a, int n, int32_t* part) {
   return total;
 }
 
+// The same for two arrays at once (one pass, two barriers): exclusive scans of a[0..n)
+// and b[0..n); returns the total of a, the total of b in *total_b. part[] holds at
+// least 2 blockDim/64 entries.
+__device__ int block_exclusive_scan2(int32_t* a, int32_t* b, int n, int32_t* part, int* total_b) {
+  const int t = threadIdx.x, nt = blockDim.x, lane = t & 63, wave = t >> 6, nw = nt >> 6;
+  const int per = (n + nt - 1) / nt;
+  const int lo = min(n, t * per), hi = min(n, lo + per);
+  int sa = 0, sb = 0;
+  for (int i = lo; i < hi; ++i) {
+    sa += a[i];
+    sb += b[i];
+  }
+  int va = sa, vb = sb;                        // inclusive scans within the wave
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int ua = __shfl_up(va, off), ub = __shfl_up(vb, off);
+    if (lane >= off) {
+      va += ua;
+      vb += ub;
+    }
+  }
+  if (lane == 63) {
+    part[wave] = va;
+    part[nw + wave] = vb;
+  }
+  __syncthreads();
+  int base_a = 0, base_b = 0, tot_a = 0, tot_b = 0;
+  for (int w = 0; w < nw; ++w) {
+    const int pa = part[w], pb = part[nw + w];
+    base_a += w < wave ? pa : 0;
+    base_b += w < wave ? pb : 0;
+    tot_a += pa;
+    tot_b += pb;
+  }
+  int ra = base_a + va - sa, rb = base_b + vb - sb;
+  for (int i = lo; i < hi; ++i) {
+    const int xa = a[i], xb = b[i];
+    a[i] = ra;
+    b[i] = rb;
+    ra += xa;
+    rb += xb;
+  }
+  __syncthreads();
+  *total_b = tot_b;
+  return tot_a;
+}
+
 // Sum of v over the block (every thread gets it); part[] as for the scan.
 __device__ int block_sum(int v, int32_t* part) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
@@ -171,6 +218,11 @@ __device__ void local_ranks(const int32_t* __restrict__ ids, int begin, int end,
   }
 }
 
+// 16-row small-M tiles of an expert with m pairs (none above small_max).
+__device__ __forceinline__ int small_tiles(int m, int small_max) {
+  return (m >= 1 && m <= small_max) ? (m + kSmallRows - 1) / kSmallRows : 0;
+}
+
 // Work lists from per-expert counts cnt[E] (LDS): small-M tiles of kSmallRows rows
 // for experts with 1..small_max pairs (expert order); the rest in 256-row items (the
 // last one when more than 128 rows remain), heaviest expert first (ties: lower id
@@ -179,20 +231,15 @@ __device__ void local_ranks(const int32_t* __restrict__ ids, int begin, int end,
 // most t13 (t2) rows, which W13 (W2) walks as 16-row tiles, are a prefix whose
 // length goes to hdr[3] (hdr[4]). Both orders come from bitonic sorts of the
 // compacted experts, O(E log^2 E) work (a count of the experts ahead of each one,
-// O(E^2), took 3.7 ms at 4096 experts). a1, a2: E words, part: blockDim words,
-// keys: LDS for 2 E sort keys (8-byte aligned).
+// O(E^2), took 3.7 ms at 4096 experts). a1: E words holding on entry the exclusive
+// scan of small_tiles() (n_small in all), a2: E words, part: blockDim words, keys:
+// LDS for 2 E sort keys (8-byte aligned).
 __device__ void build_worklists(const int32_t* cnt, int E, int small_max, int t13, int t2,
                                 int2* __restrict__ small_items, int64_t small_cap, int2* __restrict__ large_items,
                                 int64_t large_cap, int2* __restrict__ xl_items, int64_t xl_cap,
-                                int32_t* __restrict__ hdr, int32_t* a1, int32_t* a2, int32_t* part,
+                                int32_t* __restrict__ hdr, int32_t* a1, int n_small, int32_t* a2, int32_t* part,
                                 uint64_t* keys) {
   const int t = threadIdx.x, nt = blockDim.x;
-  for (int e = t; e < E; e += nt) {
-    const int m = cnt[e];
-    a1[e] = (m >= 1 && m <= small_max) ? (m + kSmallRows - 1) / kSmallRows : 0;
-  }
-  __syncthreads();
-  const int n_small = block_exclusive_scan(a1, E, part);
   for (int e = t; e < E; e += nt) {
     const int m = cnt[e];
     if (m >= 1 && m <= small_max) {
@@ -321,9 +368,13 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan_fused(PlanArgs a) {
   for (int i = t; i < (kPlanWaves + 1) * E; i += kPlanThreads) lds[i] = 0;
   __syncthreads();
   local_ranks(a.ids, 0, a.P, E, a.nbits, rank, 0, key, cnt, wcnt);
-  for (int e = t; e < E; e += kPlanThreads) off[e] = cnt[e];
+  for (int e = t; e < E; e += kPlanThreads) {
+    off[e] = cnt[e];
+    a1[e] = small_tiles(cnt[e], a.small_max);
+  }
   __syncthreads();
-  const int n_valid = block_exclusive_scan(off, E, part);
+  int n_small;
+  const int n_valid = block_exclusive_scan2(off, a1, E, part, &n_small);
   if (t == 0) {
     off[E] = n_valid;
     a.status[0] = a.P - n_valid;
@@ -343,7 +394,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan_fused(PlanArgs a) {
   }
   // wcnt (4 E words at the start of LDS) is free: room for 2 E sort keys
   build_worklists(cnt, E, a.small_max, a.t13, a.t2, a.small_items, a.small_cap, a.large_items, a.large_cap, a.xl_items, a.xl_cap,
-                  a.hdr, a1, a2, part, reinterpret_cast<uint64_t*>(wcnt));
+                  a.hdr, a1, n_small, a2, part, reinterpret_cast<uint64_t*>(wcnt));
 }
 
 // Multi-block phase 1.
@@ -405,9 +456,11 @@ __global__ __launch_bounds__(kScanThreads) void k_plan_scan(PlanArgs a) {
     const int m = a.offsets[e];       // the expert's total, from the previous phase
     cnt[e] = m;
     off[e] = m;
+    a1[e] = small_tiles(m, a.small_max);
   }
   __syncthreads();
-  const int n_valid = block_exclusive_scan(off, E, part);
+  int n_small;
+  const int n_valid = block_exclusive_scan2(off, a1, E, part, &n_small);
   if (t == 0) {
     off[E] = n_valid;
     a.status[0] = a.P - n_valid;
@@ -415,7 +468,7 @@ __global__ __launch_bounds__(kScanThreads) void k_plan_scan(PlanArgs a) {
   __syncthreads();
   for (int e = t; e <= E; e += kScanThreads) a.offsets[e] = off[e];
   build_worklists(cnt, E, a.small_max, a.t13, a.t2, a.small_items, a.small_cap, a.large_items, a.large_cap, a.xl_items, a.xl_cap,
-                  a.hdr, a1, a2, part, keys);
+                  a.hdr, a1, n_small, a2, part, keys);
 }
 
 // Multi-block phase 4.
