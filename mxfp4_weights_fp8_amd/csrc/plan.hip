@@ -62,16 +62,17 @@ __device__ int block_exclusive_scan(int32_t* a, int n, int32_t* part) {
 }
 
 // The same for two arrays at once (one pass, two barriers): exclusive scans of a[0..n)
-// and b[0..n); returns the total of a, the total of b in *total_b. part[] holds at
-// least 2 blockDim/64 entries.
-__device__ int block_exclusive_scan2(int32_t* a, int32_t* b, int n, int32_t* part, int* total_b) {
+// and b[0..n); returns the total of a, the total of b in *total_b and the largest
+// element of a in *max_a. part[] holds at least 3 blockDim/64 entries.
+__device__ int block_exclusive_scan2(int32_t* a, int32_t* b, int n, int32_t* part, int* total_b, int* max_a) {
   const int t = threadIdx.x, nt = blockDim.x, lane = t & 63, wave = t >> 6, nw = nt >> 6;
   const int per = (n + nt - 1) / nt;
   const int lo = min(n, t * per), hi = min(n, lo + per);
-  int sa = 0, sb = 0;
+  int sa = 0, sb = 0, mx = 0;
   for (int i = lo; i < hi; ++i) {
     sa += a[i];
     sb += b[i];
+    mx = max(mx, a[i]);
   }
   int va = sa, vb = sb;                        // inclusive scans within the wave
 #pragma unroll
@@ -81,19 +82,22 @@ __device__ int block_exclusive_scan2(int32_t* a, int32_t* b, int n, int32_t* par
       va += ua;
       vb += ub;
     }
+    mx = max(mx, __shfl_xor(mx, off));
   }
   if (lane == 63) {
     part[wave] = va;
     part[nw + wave] = vb;
+    part[2 * nw + wave] = mx;
   }
   __syncthreads();
-  int base_a = 0, base_b = 0, tot_a = 0, tot_b = 0;
+  int base_a = 0, base_b = 0, tot_a = 0, tot_b = 0, max_all = 0;
   for (int w = 0; w < nw; ++w) {
     const int pa = part[w], pb = part[nw + w];
     base_a += w < wave ? pa : 0;
     base_b += w < wave ? pb : 0;
     tot_a += pa;
     tot_b += pb;
+    max_all = max(max_all, part[2 * nw + w]);
   }
   int ra = base_a + va - sa, rb = base_b + vb - sb;
   for (int i = lo; i < hi; ++i) {
@@ -105,6 +109,7 @@ __device__ int block_exclusive_scan2(int32_t* a, int32_t* b, int n, int32_t* par
   }
   __syncthreads();
   *total_b = tot_b;
+  *max_a = max_all;
   return tot_a;
 }
 
@@ -232,13 +237,14 @@ __device__ __forceinline__ int small_tiles(int m, int small_max) {
 // length goes to hdr[3] (hdr[4]). Both orders come from bitonic sorts of the
 // compacted experts, O(E log^2 E) work (a count of the experts ahead of each one,
 // O(E^2), took 3.7 ms at 4096 experts). a1: E words holding on entry the exclusive
-// scan of small_tiles() (n_small in all), a2: E words, part: blockDim words, keys:
-// LDS for 2 E sort keys (8-byte aligned).
+// scan of small_tiles() (n_small in all); any_big: some expert has more than
+// small_max pairs; a2: E words, part: blockDim words, keys: LDS for 2 E sort keys
+// (8-byte aligned).
 __device__ void build_worklists(const int32_t* cnt, int E, int small_max, int t13, int t2,
                                 int2* __restrict__ small_items, int64_t small_cap, int2* __restrict__ large_items,
                                 int64_t large_cap, int2* __restrict__ xl_items, int64_t xl_cap,
-                                int32_t* __restrict__ hdr, int32_t* a1, int n_small, int32_t* a2, int32_t* part,
-                                uint64_t* keys) {
+                                int32_t* __restrict__ hdr, int32_t* a1, int n_small, bool any_big, int32_t* a2,
+                                int32_t* part, uint64_t* keys) {
   const int t = threadIdx.x, nt = blockDim.x;
   for (int e = t; e < E; e += nt) {
     const int m = cnt[e];
@@ -249,9 +255,7 @@ __device__ void build_worklists(const int32_t* cnt, int E, int small_max, int t1
     }
   }
   // no expert above small_max (decode batches): empty large-M lists, done
-  int any_big = 0;
-  for (int e = t; e < E; e += nt) any_big |= cnt[e] > small_max;
-  if (!__syncthreads_or(any_big)) {
+  if (!any_big) {
     if (t == 0) {
       hdr[0] = n_small < small_cap ? n_small : (int)small_cap;
       hdr[1] = 0;
@@ -373,8 +377,8 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan_fused(PlanArgs a) {
     a1[e] = small_tiles(cnt[e], a.small_max);
   }
   __syncthreads();
-  int n_small;
-  const int n_valid = block_exclusive_scan2(off, a1, E, part, &n_small);
+  int n_small, max_cnt;
+  const int n_valid = block_exclusive_scan2(off, a1, E, part, &n_small, &max_cnt);
   if (t == 0) {
     off[E] = n_valid;
     a.status[0] = a.P - n_valid;
@@ -394,7 +398,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan_fused(PlanArgs a) {
   }
   // wcnt (4 E words at the start of LDS) is free: room for 2 E sort keys
   build_worklists(cnt, E, a.small_max, a.t13, a.t2, a.small_items, a.small_cap, a.large_items, a.large_cap, a.xl_items, a.xl_cap,
-                  a.hdr, a1, n_small, a2, part, reinterpret_cast<uint64_t*>(wcnt));
+                  a.hdr, a1, n_small, max_cnt > a.small_max, a2, part, reinterpret_cast<uint64_t*>(wcnt));
 }
 
 // Multi-block phase 1.
@@ -459,8 +463,8 @@ __global__ __launch_bounds__(kScanThreads) void k_plan_scan(PlanArgs a) {
     a1[e] = small_tiles(m, a.small_max);
   }
   __syncthreads();
-  int n_small;
-  const int n_valid = block_exclusive_scan2(off, a1, E, part, &n_small);
+  int n_small, max_cnt;
+  const int n_valid = block_exclusive_scan2(off, a1, E, part, &n_small, &max_cnt);
   if (t == 0) {
     off[E] = n_valid;
     a.status[0] = a.P - n_valid;
@@ -468,7 +472,7 @@ __global__ __launch_bounds__(kScanThreads) void k_plan_scan(PlanArgs a) {
   __syncthreads();
   for (int e = t; e <= E; e += kScanThreads) a.offsets[e] = off[e];
   build_worklists(cnt, E, a.small_max, a.t13, a.t2, a.small_items, a.small_cap, a.large_items, a.large_cap, a.xl_items, a.xl_cap,
-                  a.hdr, a1, n_small, a2, part, keys);
+                  a.hdr, a1, n_small, max_cnt > a.small_max, a2, part, keys);
 }
 
 // Multi-block phase 4.
