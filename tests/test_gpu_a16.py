@@ -33,6 +33,7 @@ def dev(gpu):
     (400, 1024, 256, 3, 2, 77),    # 128-row items
     (3, 16384, 256, 4, 2, 78),     # H at the small-M limit (scale runs of 8 KB per wave)
     (2, 256, 16384, 2, 1, 79),     # I at the small-M limit
+    (30, 512, 256, 48, 16, 82),    # top-16: two batches of 8 picks in the combine
 ])
 def test_a16_shapes(dev, T, H, I, E, K, seed):
     wl = scaled("tiny", T=T, H=H, I=I, E=E, K=K, seed=seed, weight_seed=seed, name=f"a16_{seed}")

@@ -46,6 +46,7 @@ def _inputs(wl, dev):
     (300, 512, 512, 1, 1, 105),    # a 256-row item and a remainder
     (400, 1024, 256, 3, 2, 106),   # 128-row items
     (700, 384, 384, 3, 1, 107),    # above 512 pairs (the wider work split), H of three 128-column blocks
+    (20, 256, 256, 40, 12, 108),   # top-12: a partial second batch of picks in the combine
 ])
 def test_nvfp4_shapes(dev, T, H, I, E, K, seed):
     inp = _inputs(scaled("tiny", T=T, H=H, I=I, E=E, K=K, seed=seed, weight_seed=seed, name=f"nv_{seed}"), dev)

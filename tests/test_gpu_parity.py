@@ -92,7 +92,8 @@ def test_quant_act_every_bf16_value(dev):
 # ----------------------------------------------------------------------------- planner
 
 @pytest.mark.parametrize("T,K,E,seed", [(1, 1, 1, 0), (7, 8, 384, 1), (64, 2, 8, 2), (256, 8, 384, 3),
-                                        (255, 3, 5, 4), (300, 8, 4096, 5), (4096, 8, 384, 6), (5000, 7, 64, 7)])
+                                        (255, 3, 5, 4), (300, 8, 4096, 5), (4096, 8, 384, 6), (5000, 7, 64, 7),
+                                        (50, 64, 100, 8), (3000, 16, 384, 9)])
 def test_plan_random(dev, T, K, E, seed):
     ids = np.random.default_rng(seed).integers(0, E, (T, K)).astype(np.int32)
     p = moe.plan(torch.from_numpy(ids).to(dev), E, 256, 256)
@@ -193,6 +194,12 @@ def test_tilings_agree_bit_for_bit(dev, wl):
     (300, 512, 128, 1, 1, 57, 0),
     (400, 1280, 256, 3, 2, 58, 0),
     (600, 1280, 384, 2, 1, 59, 0),
+    # top-k above 8: the combine adds picks in batches of 8 (K 16: two full
+    # batches; K 64, the largest the library takes: eight), the planner ranks
+    # 16 or 64 picks per token
+    (40, 256, 256, 64, 16, 64, 0),
+    (9, 256, 256, 80, 64, 65, 0),
+    (70, 512, 384, 40, 12, 66, 0),
 ])
 def test_ffn_shapes(dev, T, H, I, E, K, seed, small_max):
     wl = scaled("tiny", T=T, H=H, I=I, E=E, K=K, seed=seed, weight_seed=seed, name=f"s{seed}")
