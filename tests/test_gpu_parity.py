@@ -200,6 +200,9 @@ def test_tilings_agree_bit_for_bit(dev, wl):
     (40, 256, 256, 64, 16, 64, 0),
     (9, 256, 256, 80, 64, 65, 0),
     (70, 512, 384, 40, 12, 66, 0),
+    # 4096 experts, the most the library takes (multi-block plan, expert ids past
+    # 2^11 in every list and offset)
+    (600, 128, 128, 4096, 4, 67, 0),
 ])
 def test_ffn_shapes(dev, T, H, I, E, K, seed, small_max):
     wl = scaled("tiny", T=T, H=H, I=I, E=E, K=K, seed=seed, weight_seed=seed, name=f"s{seed}")
