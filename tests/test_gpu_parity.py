@@ -298,6 +298,7 @@ def test_ffn_bitwise_repeatable_whatever_the_workspace_holds(dev, full_weights, 
     dict(base="tiny", T=300, H=512, I=512, E=1, K=1, seed=83, weight_seed=83),           # 256-row + 128-row items
     dict(base="tiny", T=130, H=384, I=1152, E=3, K=2, seed=84, weight_seed=84),          # H/256 odd, I 9 x 128
     dict(base="tiny", T=3, H=16384, I=256, E=4, K=2, seed=85, weight_seed=85),           # H at the small-M limit
+    dict(base="tiny", T=24, H=512, I=256, E=48, K=16, seed=86, weight_seed=86),          # top-16, 384 pairs
 ])
 def test_decode_chain_matches_separate_launches(dev, wl):
     """MOE_FLAG_DECODE_CHAIN (one persistent launch of W13, W2 and the combine,
