@@ -27,6 +27,7 @@ def dev(gpu):
     (300, 512, 512, 3, 2, 0),      # 256-row and 128-row large-M items
     (7, 256, 256, 64, 8, 128),     # decode-sized: small-M tiles only, plus the dense shared expert
     (400, 1280, 384, 2, 1, 0),     # W2 with three K steps (few-K kernel)
+    (600, 256, 256, 16, 4, 0),     # 2400 pairs: the four-launch plan
 ])
 def test_graph_replay_matches_eager(dev, T, H, I, E, K, Is):
     base = scaled("tiny", T=T, H=H, I=I, E=E, K=K, Is=Is, seed=70, weight_seed=71, name="graph")
