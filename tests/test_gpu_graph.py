@@ -23,13 +23,15 @@ def dev(gpu):
     return gpu
 
 
-@pytest.mark.parametrize("T,H,I,E,K,Is", [
-    (300, 512, 512, 3, 2, 0),      # 256-row and 128-row large-M items
-    (7, 256, 256, 64, 8, 128),     # decode-sized: small-M tiles only, plus the dense shared expert
-    (400, 1280, 384, 2, 1, 0),     # W2 with three K steps (few-K kernel)
-    (600, 256, 256, 16, 4, 0),     # 2400 pairs: the four-launch plan
+@pytest.mark.parametrize("T,H,I,E,K,Is,flags", [
+    (300, 512, 512, 3, 2, 0, 0),      # 256-row and 128-row large-M items
+    (7, 256, 256, 64, 8, 128, 0),     # decode-sized: small-M tiles only, plus the dense shared expert
+    (400, 1280, 384, 2, 1, 0, 0),     # W2 with three K steps (few-K kernel)
+    (600, 256, 256, 16, 4, 0, 0),     # 2400 pairs: the four-launch plan
+    (300, 512, 512, 3, 2, 0, moe.FLAG_A16),           # bf16 activations
+    (7, 256, 256, 64, 8, 0, moe.FLAG_DECODE_CHAIN),   # the persistent chain (counters zeroed by a kernel)
 ])
-def test_graph_replay_matches_eager(dev, T, H, I, E, K, Is):
+def test_graph_replay_matches_eager(dev, T, H, I, E, K, Is, flags):
     base = scaled("tiny", T=T, H=H, I=I, E=E, K=K, Is=Is, seed=70, weight_seed=71, name="graph")
     first = make_inputs(base).to(dev)
     W = moe.pack_weights(first.weights)
@@ -37,20 +39,20 @@ def test_graph_replay_matches_eager(dev, T, H, I, E, K, Is):
     ids, x, tw = first.topk_ids.clone(), first.x.clone(), first.topk_weights.clone()
 
     # buffers the graph captures (allocated, and the path run once, before capture)
-    pbuf = moe.plan(ids, E, H, I, Is=Is)
+    pbuf = moe.plan(ids, E, H, I, Is=Is, flags=flags)
     ws = torch.empty(moe.ffn_workspace_bytes(pbuf.dims), dtype=torch.uint8, device=dev)
     y = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
-        moe.plan(ids, E, H, I, Is=Is, out=pbuf)
+        moe.plan(ids, E, H, I, Is=Is, flags=flags, out=pbuf)
         moe.ffn(x, tw, pbuf, W, shared=shared, ws=ws, y=y)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
 
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        moe.plan(ids, E, H, I, Is=Is, out=pbuf)
+        moe.plan(ids, E, H, I, Is=Is, flags=flags, out=pbuf)
         moe.ffn(x, tw, pbuf, W, shared=shared, ws=ws, y=y)
     torch.cuda.synchronize()
 
@@ -66,14 +68,14 @@ def test_graph_replay_matches_eager(dev, T, H, I, E, K, Is):
         pairs_graph = pbuf.sorted_pairs.clone()
         offsets_graph = pbuf.expert_offsets.clone()
         # eager run on the same inputs, fresh buffers
-        p2 = moe.plan(ids, E, H, I, Is=Is)
+        p2 = moe.plan(ids, E, H, I, Is=Is, flags=flags)
         y2 = moe.ffn(x, tw, p2, W, shared=shared)
         torch.cuda.synchronize()
         assert torch.equal(offsets_graph, p2.expert_offsets), f"replay {rep}: expert offsets differ"
         assert torch.equal(pairs_graph, p2.sorted_pairs), f"replay {rep}: plan differs"
         assert torch.equal(y_graph.view(torch.int16), y2.view(torch.int16)), f"replay {rep}: y differs"
         assert bool(torch.isfinite(y2.float()).all())
-        say(f"[graph {T}x{H} I{I} E{E} K{K} Is{Is}] replay {rep} equal to eager")
+        say(f"[graph {T}x{H} I{I} E{E} K{K} Is{Is} flags{flags}] replay {rep} equal to eager")
 
 
 def test_two_streams_match_sequential(dev):
