@@ -12,7 +12,7 @@ import torch
 
 import mxfp4_weights_fp8_amd as moe
 from gpu_helpers import say
-from synth import make_inputs, scaled
+from synth import make_expert_weights, make_inputs, scaled
 
 pytestmark = pytest.mark.gpu
 
@@ -30,10 +30,13 @@ def dev(gpu):
     (600, 256, 256, 16, 4, 0, 0),     # 2400 pairs: the four-launch plan
     (300, 512, 512, 3, 2, 0, moe.FLAG_A16),           # bf16 activations
     (7, 256, 256, 64, 8, 0, moe.FLAG_DECODE_CHAIN),   # the persistent chain (counters zeroed by a kernel)
+    (300, 512, 512, 3, 2, 0, moe.FLAG_NVFP4),         # NVFP4 weights
 ])
 def test_graph_replay_matches_eager(dev, T, H, I, E, K, Is, flags):
     base = scaled("tiny", T=T, H=H, I=I, E=E, K=K, Is=Is, seed=70, weight_seed=71, name="graph")
     first = make_inputs(base).to(dev)
+    if flags & moe.FLAG_NVFP4:
+        first.weights = make_expert_weights(base, dev, fmt="nvfp4")
     W = moe.pack_weights(first.weights)
     shared = first.shared
     ids, x, tw = first.topk_ids.clone(), first.x.clone(), first.topk_weights.clone()
